@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+@pytest.fixture(scope="session")
+def coracle():
+    from oracle import c_oracle
+    c_oracle.lib()
+    return c_oracle
+
+
+@pytest.fixture(scope="session")
+def noracle():
+    from oracle import np_oracle
+    return np_oracle

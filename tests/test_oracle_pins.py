@@ -1,0 +1,436 @@
+"""Pins of the CPU oracles against what the pages and mathematics fix (no GPU needed).
+
+Each test checks the oracle against something other than itself: IEEE/numpy conversions,
+closed forms of the Hadamard matrix, error bounds of uniform rounding, brute-force
+searches, textbook Lloyd-Max values, exact cases where quantization is lossless, and the
+second (NumPy) oracle written separately.
+"""
+import math
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+
+from int4_compressed_domain_amd import workloads as W
+
+ORACLES = ["c", "np"]
+
+
+@pytest.fixture(params=ORACLES)
+def orc(request, coracle, noracle):
+    return coracle if request.param == "c" else noracle
+
+
+def _sb(D, seed=0):
+    return W.sign_bits(D, seed)
+
+
+def _hadamard(D):
+    i = np.arange(D)
+    return np.array([[(-1) ** bin(a & b).count("1") for b in i] for a in i], dtype=np.float64)
+
+
+# ---- fp16 and rho ---------------------------------------------------------------------------
+
+def test_f16_conversion_matches_ieee(coracle):
+    """The C oracle's own fp16 rounding equals numpy's IEEE cast (RNE, subnormals)."""
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([
+        rng.standard_normal(3000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-5).astype(np.float32),     # subnormal range
+        (rng.standard_normal(500) * 3e4).astype(np.float32),
+        np.float32([0.0, -0.0, 65504.0, 65519.99, 5.96e-8, 2.98e-8, 2.99e-8, 6.1e-5]),
+        # exact ties between two fp16 values: 1 + (2k+1) * 2^-11
+        (1.0 + (2 * np.arange(50) + 1) * 2.0 ** -11).astype(np.float32),
+    ])
+    got = coracle.f32_to_f16_bits(vals)
+    with np.errstate(over="ignore"):
+        want = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("D", [2, 4, 8, 16, 32, 64, 128, 256, 512])
+def test_rho_is_correctly_rounded(orc, D):
+    """rho = fp32(1/sqrt(D)) within half an ulp of the exact value."""
+    getcontext().prec = 50
+    exact = Decimal(1) / Decimal(D).sqrt()
+    rho = np.float32(orc.rho_f32(D) if hasattr(orc, "rho_f32") else orc.rho32(D))
+    ulp = Decimal(float(np.spacing(rho)))
+    assert abs(Decimal(float(rho)) - exact) <= ulp / 2
+
+
+# ---- rotation -------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D", [4, 8, 16, 64, 128, 256])
+def test_rotation_columns_are_hadamard(orc, D):
+    """R e_j = rho * sigma_j * H[:, j] exactly (one nonzero input: no rounding but rho)."""
+    sb = _sb(D, 3)
+    sig = np.array([-1.0 if (sb[i // 32] >> (i % 32)) & 1 else 1.0 for i in range(D)])
+    H = _hadamard(D)
+    rho = float(np.float32(orc.rho_f32(D))) if hasattr(orc, "rho_f32") else float(orc.rho32(D))
+    cols = orc.rotate(np.eye(D, dtype=np.float32), sb).astype(np.float64)
+    want = (H * sig[None, :]).T * rho          # row j = R e_j
+    assert np.array_equal(cols, want)
+
+
+@pytest.mark.parametrize("D", [4, 16, 64, 256])
+def test_normalized_hadamard_is_involution(orc, D):
+    """(rho H)(rho H) = I exactly when rho is a power of two."""
+    zero = np.zeros(max(1, D // 32), np.uint32)
+    M = orc.rotate(np.eye(D, dtype=np.float32), zero).astype(np.float64)
+    assert np.array_equal(M @ M, np.eye(D))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rotation_preserves_dot_products(orc, D):
+    """|R(q).R(k) - q.k| <= 4 D 2^-24 |q||k| (the query is rotated into the cache basis)."""
+    rng = np.random.default_rng(D)
+    sb = _sb(D, 5)
+    q = rng.standard_normal((200, D)).astype(np.float32)
+    k = (rng.standard_normal((200, D)) * rng.lognormal(0, 1, D)).astype(np.float32)
+    rq = orc.rotate(q, sb).astype(np.float64)
+    rk = orc.rotate(k, sb).astype(np.float64)
+    lhs = np.abs(np.sum(rq * rk, 1) - np.sum(q.astype(np.float64) * k, 1))
+    bound = 4 * D * 2.0 ** -24 * np.linalg.norm(q, axis=1) * np.linalg.norm(k, axis=1)
+    assert np.all(lhs <= bound)
+
+
+def test_unrotate_inverts_rotate(orc):
+    D = 128
+    sb = _sb(D, 7)
+    x = np.random.default_rng(2).standard_normal((50, D)).astype(np.float32)
+    back = orc.unrotate_f32(orc.rotate(x, sb), sb)
+    assert np.max(np.abs(back - x)) <= 8 * 2.0 ** -24 * np.max(np.abs(x)) * math.sqrt(D)
+
+
+# ---- abs-max codec --------------------------------------------------------------------------
+
+def _brute_absmax(y, s):
+    """argmin over c in [-7, 7] of |y - c s| (exact fp64), ties to the even c. Entries whose
+    exact quotient y/s lies within 2^-20 of a half-integer are returned as None: there the
+    fp32 quotient the codec rounds may fall on either side, and both neighbours are valid."""
+    cs = np.arange(-7, 8)
+    out = []
+    for v in y:
+        qv = np.float64(v) / np.float64(s)
+        frac = abs(qv - math.floor(qv) - 0.5)
+        if frac < 2.0 ** -20 and abs(qv) < 7.5 and frac != 0.0:
+            out.append(None)
+            continue
+        err = np.abs(np.float64(v) - cs * np.float64(s))
+        best = np.flatnonzero(err == err.min())
+        out.append(cs[best[0]] if len(best) == 1 else [c for c in cs[best] if c % 2 == 0][0])
+    return out
+
+
+def _match(codes, brute):
+    return all(b is None or int(c) == int(b) for c, b in zip(codes, brute))
+
+
+def _absmax_groups(orc, y):
+    if hasattr(orc, "quant_absmax") and orc.__name__.endswith("c_oracle"):
+        u, s = orc.quant_absmax(y)
+        return u, np.uint16(s).view(np.float16)
+    u, s = orc.quant_absmax(y[None, :], group=y.shape[0])
+    return u[0], s[0, 0]
+
+
+def test_absmax_error_bound_and_brute_force(orc):
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        y = (rng.standard_normal(32) * rng.lognormal(0, 2)).astype(np.float32)
+        if trial % 5 == 0:
+            y[rng.integers(32)] *= 30.0
+        u, s16 = _absmax_groups(orc, y)
+        s = np.float64(np.float16(s16))
+        c = u.astype(np.int64) - 8
+        # scale rounds absmax/7 (fp32 division) to the nearest fp16
+        assert np.float16(s16) == np.float16(np.float32(np.max(np.abs(y))) / np.float32(7))
+        assert np.all(np.abs(y.astype(np.float64) - c * s) <= s / 2 * (1 + 2.0 ** -20))
+        assert _match(c, _brute_absmax(y, s))
+        assert np.all((u >= 1) & (u <= 15))
+
+
+def test_absmax_ties_go_to_even(orc):
+    """y/s = k + 1/2 exactly -> the even neighbour."""
+    y = np.float32([7.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5, -3.5, 4.5, 5.5, 6.5, -6.5] + [0.0] * 19)
+    u, s16 = _absmax_groups(orc, y)
+    assert float(np.float16(s16)) == 1.0
+    c = u.astype(int) - 8
+    assert list(c[:13]) == [7, 0, 2, 2, 0, -2, -2, 4, -4, 4, 6, 6, -6]
+
+
+def test_absmax_zero_group(orc):
+    u, s16 = _absmax_groups(orc, np.zeros(32, np.float32))
+    assert float(np.float16(s16)) == 0.0 and np.all(u == 8)
+
+
+def test_absmax_tiny_group_keeps_subnormal_scale(orc):
+    y = np.zeros(32, np.float32)
+    y[3] = 7 * 2.0 ** -24 * 5       # absmax/7 = 5 * 2^-24: an fp16 subnormal
+    y[4] = -7 * 2.0 ** -24 * 2
+    u, s16 = _absmax_groups(orc, y)
+    assert np.float16(s16).view(np.uint16) == 5
+    assert int(u[3]) - 8 == 7 and int(u[4]) - 8 == -3   # -14/5 = -2.8 -> -3
+
+
+# ---- LUT codec -------------------------------------------------------------------------------
+
+# Lloyd-Max 16-level quantizer for a unit Gaussian: positive output levels from the
+# textbook table (J. Max, "Quantizing for minimum distortion", IRE Trans. IT-6, 1960, N=16),
+# and its mean squared error 0.009497.
+MAX1960_LEVELS = [0.1284, 0.3881, 0.6568, 0.9424, 1.2562, 1.6181, 2.0690, 2.7326]
+
+
+def test_lloydmax_matches_textbook(orc):
+    m, mse = orc.lloydmax16()
+    assert np.allclose(m[8:], MAX1960_LEVELS, atol=2e-4)
+    assert np.allclose(m[:8], -np.array(MAX1960_LEVELS[::-1]), atol=2e-4)
+    assert abs(mse - 0.009497) < 1e-5
+    # Lloyd fixed point: each level is the centroid of its cell
+    from scipy import integrate
+    t = np.concatenate(([-np.inf], 0.5 * (m[1:] + m[:-1]), [np.inf]))
+    pdf = lambda x: np.exp(-x * x / 2) / math.sqrt(2 * math.pi)
+    for j in (0, 5, 8, 15):
+        num = integrate.quad(lambda x: x * pdf(x), t[j], t[j + 1])[0]
+        den = integrate.quad(pdf, t[j], t[j + 1])[0]
+        assert abs(num / den - m[j]) < 1e-9
+
+
+def _lut_of(orc):
+    lut = orc.lut16()
+    return lut.view(np.float16) if lut.dtype == np.uint16 else lut
+
+
+def test_lut_is_fp16_of_scaled_centroids(orc):
+    m, _ = orc.lloydmax16()
+    lut = _lut_of(orc)
+    assert np.array_equal(lut, (m / math.sqrt(32)).astype(np.float16))
+    assert np.array_equal(lut[8:].astype(np.float64), -lut[7::-1].astype(np.float64))
+
+
+def _lut_groups(orc, y):
+    if orc.__name__.endswith("c_oracle"):
+        u, n = orc.quant_lut(y)
+        return u, np.uint16(n).view(np.float16)
+    u, n = orc.quant_lut(y[None, :], group=y.shape[0])
+    return u[0], n[0, 0]
+
+
+def test_lut_codec_brute_force(orc):
+    """index = argmin_j |y/n - LUT_j| with ties to the upper index; n = fp16(||y||_2)."""
+    lut = _lut_of(orc).astype(np.float64)
+    rng = np.random.default_rng(21)
+    for trial in range(300):
+        y = (rng.standard_normal(32) * rng.lognormal(0, 1.5)).astype(np.float32)
+        u, n16 = _lut_groups(orc, y)
+        n = float(np.float16(n16))
+        ref_n = math.sqrt(float(np.sum(y.astype(np.float64) ** 2)))
+        assert abs(n - ref_n) <= ref_n * (2.0 ** -11 + 1e-6)
+        v = y.astype(np.float64) / n
+        mids = 0.5 * (lut[1:] + lut[:-1])
+        for i in range(32):
+            if np.min(np.abs(v[i] - mids)) < 2.0 ** -20 * max(1.0, abs(v[i])):
+                continue      # fp32 quotient may land on either side of the midpoint
+            err = np.abs(v[i] - lut)
+            best = np.flatnonzero(err == err.min())
+            assert u[i] == best[-1]
+
+
+def test_lut_ties_go_up(orc):
+    """A value exactly on a midpoint of two levels takes the upper level."""
+    lut = _lut_of(orc).astype(np.float32)
+    mids = (lut[:-1] + lut[1:]) * np.float32(0.5)
+    # make a group with norm exactly 1.0 that contains midpoint values
+    y = np.zeros(32, np.float32)
+    y[1:4] = mids[[2, 7, 12]]
+    y[0] = np.float32(math.sqrt(1.0 - float(np.sum(y[1:4].astype(np.float64) ** 2))))
+    u, n16 = _lut_groups(orc, y)
+    n = np.float32(np.float16(n16))
+    assert n == np.float32(1.0)
+    assert list(u[1:4]) == [3, 8, 13]
+
+
+def test_lut_zero_group(orc):
+    u, n16 = _lut_groups(orc, np.zeros(32, np.float32))
+    assert float(np.float16(n16)) == 0.0 and np.all(u == 8)
+
+
+# ---- exact agreement with plain attention ----------------------------------------------------
+
+def _exact_vectors(rng, n, D, sb, orc):
+    """x with R(x) = c exactly: c integer in [-7, 7], every group holding a +-7."""
+    c = rng.integers(-7, 8, size=(n, D)).astype(np.float64)
+    for g in range(D // 32):
+        c[np.arange(n), g * 32 + rng.integers(0, 32, n)] = rng.choice([-7.0, 7.0], n)
+    sig = np.array([-1.0 if (sb[i // 32] >> (i % 32)) & 1 else 1.0 for i in range(D)])
+    x = (c @ _hadamard(D)) / math.sqrt(D) * sig      # R^-1 c, exact for D = 4^k
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    return c, x.astype(np.float32)
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_lossless_case_equals_plain_attention(coracle, noracle, D):
+    """When R(k), R(v), R(q) are integers with a +-7 per group, quantization is lossless
+    and the oracle's decode equals softmax attention on the original vectors."""
+    rng = np.random.default_rng(D + 1)
+    sb = _sb(D, 9)
+    L, Hkv, Hq = 40, 2, 4
+    ck, k = _exact_vectors(rng, L * Hkv, D, sb, coracle)
+    cv, v = _exact_vectors(rng, L * Hkv, D, sb, coracle)
+    _, q = _exact_vectors(rng, Hq, D, sb, coracle)
+    k = k.reshape(L, Hkv, D)
+    v = v.reshape(L, Hkv, D)
+    bt = np.array([[3, 0, 2]], np.int32)
+    slots = W.slots_for(bt, 0, 0, L)
+    alpha = 1.0 / 16.0
+    for orc in (coracle, noracle):
+        pool = orc.new_pool(4, Hkv, D)
+        orc.append(pool, D, Hkv, k, v, slots, sb)
+        # codes are the integers, scales exactly 1
+        ku, ks, vu, vs = (coracle.fetch(pool, D, Hkv, 0, 5, 1))
+        assert np.all(ks == 0x3C00) and np.all(vs == 0x3C00)
+        out = orc.decode(pool, D, Hq, Hkv, sb, bt, np.array([L], np.int32), q[None], alpha)
+        for hq in range(Hq):
+            h = hq // (Hq // Hkv)
+            ref = coracle.attention_f64(q[hq].astype(np.float64), k[:, h].astype(np.float64),
+                                        v[:, h].astype(np.float64), alpha)
+            s = alpha * (k[:, h].astype(np.float64) @ q[hq].astype(np.float64))
+            w = np.exp(s - s.max())
+            plain = (w @ v[:, h].astype(np.float64)) / w.sum()
+            assert np.max(np.abs(ref - plain)) < 1e-12 * np.max(np.abs(plain))
+            assert np.max(np.abs(out[0, hq] - plain)) < 1e-12 * np.max(np.abs(plain))
+
+
+def test_codec_alone_lossless_at_d128(orc):
+    """D=128 has an irrational rho, so check the codec stage on pre-rotated integers."""
+    rng = np.random.default_rng(5)
+    for e in (-3, 0, 4):
+        c = rng.integers(-7, 8, size=32)
+        c[7] = 7
+        y = (c * 2.0 ** e).astype(np.float32)
+        u, s16 = _absmax_groups(orc, y)
+        assert float(np.float16(s16)) == 2.0 ** e
+        assert np.array_equal(u.astype(int) - 8, c)
+
+
+# ---- brute force on D = 8, N = 4 ------------------------------------------------------------
+
+def test_brute_force_d8_n4(coracle, noracle):
+    """Group 8 at D=8: codes by exhaustive search, attention by materialized softmax."""
+    D, N = 8, 4
+    rng = np.random.default_rng(8)
+    sb = np.array([0b10110010], np.uint32)
+    sig = np.array([-1.0 if (sb[0] >> i) & 1 else 1.0 for i in range(D)])
+    H = _hadamard(D)
+    for trial in range(2000):
+        k = rng.standard_normal((N, D)).astype(np.float32)
+        v = rng.standard_normal((N, D)).astype(np.float32)
+        q = rng.standard_normal(D).astype(np.float32)
+        if trial % 7 == 0:   # exact ties: y/s = k + 1/2
+            yk = np.float32(rng.integers(-6, 7, (N, D)) + 0.5)
+            yk[:, 0] = 7.0
+            k = ((yk.astype(np.float64) @ H) / math.sqrt(8) * sig).astype(np.float32)
+        ku_c, ks_c = coracle.encode(k, sb, 0, group=8)
+        vu_c, vs_c = coracle.encode(v, sb, 0, group=8)
+        ku_n, ks_n = noracle.encode(k, sb, 0, group=8)
+        assert np.array_equal(ku_c, ku_n) and np.array_equal(ks_c, ks_n.view(np.uint16))
+        yk = coracle.rotate(k, sb)
+        for t in range(N):
+            s = np.float16(ks_n[t, 0]).astype(np.float64)
+            want = _brute_absmax(yk[t], s) if s != 0 else [0] * D
+            assert _match(ku_c[t].astype(int) - 8, want)
+        K = (ku_c.astype(np.float64) - 8) * ks_n.astype(np.float64)
+        V = (vu_c.astype(np.float64) - 8) * vs_n_f(vs_c)
+        qr = coracle.rotate(q, sb).astype(np.float64)
+        got = coracle.attention_f64(qr, K, V, 0.35)
+        scores = [0.35 * sum(qr[i] * K[t, i] for i in range(D)) for t in range(N)]
+        ws = [math.exp(s - max(scores)) for s in scores]
+        want = [sum(ws[t] * V[t, i] for t in range(N)) / sum(ws) for i in range(D)]
+        assert np.allclose(got, want, rtol=0, atol=1e-13)
+
+
+def vs_n_f(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+# ---- split merge ------------------------------------------------------------------------------
+
+def test_split_softmax_merge_equals_direct(coracle):
+    """Partial (o', m, l) over any token split, merged with max-rescaling, equals the
+    direct softmax result (online normalizer, cited among the builds-on references)."""
+    rng = np.random.default_rng(4)
+    D, L = 64, 300
+    K = rng.standard_normal((L, D)) * 3
+    V = rng.standard_normal((L, D))
+    q = rng.standard_normal(D)
+    direct = coracle.attention_f64(q, K, V, 0.5)
+    for cuts in ([0, 300], [0, 1, 300], [0, 17, 130, 131, 299, 300], list(range(0, 301, 16)) + [300]):
+        cuts = sorted(set(cuts))
+        parts = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            s = 0.5 * K[a:b] @ q
+            m = s.max()
+            w = np.exp(s - m)
+            parts.append((w @ V[a:b], m, w.sum()))
+        M = max(p[1] for p in parts)
+        num = sum(p[0] * math.exp(p[1] - M) for p in parts)
+        den = sum(p[2] * math.exp(p[1] - M) for p in parts)
+        assert np.max(np.abs(num / den - direct)) < 1e-13
+
+
+# ---- the two oracles agree ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["single_head_1k", "llama8b_b16_8k", "gemma_d256_32k", "mixed_serving"])
+def test_c_and_numpy_oracles_agree(coracle, noracle, name):
+    w = W.WORKLOADS[name].scaled(context=45, batch=2, ragged_min=20, prefill=0)
+    D, Hkv, Hq = w.head_dim, w.kv_heads, w.q_heads
+    sb = W.sign_bits(D, 0)
+    lens = W.context_lens(w, 0)
+    bt, _, npages = W.page_tables(w, lens, 0)
+    pools = {}
+    for orc in (coracle, noracle):
+        pool = orc.new_pool(npages, Hkv, D)
+        for b in range(w.batch):
+            k, v, _, _ = W.seq_tokens(w, b, int(lens[b]), 0)
+            orc.append(pool, D, Hkv, k, v, W.slots_for(bt, b, 0, int(lens[b])), sb,
+                       w.k_codec, w.v_codec)
+        pools[orc] = pool
+    assert np.array_equal(pools[coracle], pools[noracle])
+    q, _ = W.queries(w, 0)
+    oc = coracle.decode(pools[coracle], D, Hq, Hkv, sb, bt, lens, q, w.attn_scale,
+                        k_codec=w.k_codec, v_codec=w.v_codec)
+    on = noracle.decode(pools[noracle], D, Hq, Hkv, sb, bt, lens, q, w.attn_scale,
+                        k_codec=w.k_codec, v_codec=w.v_codec)
+    assert np.max(np.abs(oc - on)) <= 1e-12 * max(1.0, np.max(np.abs(on)))
+
+
+def test_gqa_heads_share_their_kv_head(coracle):
+    """With r = Hq/Hkv, q head hq reads kv head hq // r: a decode with Hq = Hkv * r equals
+    r separate decodes with Hq = Hkv."""
+    D, Hkv, r, L = 64, 2, 3, 37
+    rng = np.random.default_rng(12)
+    sb = _sb(D, 1)
+    k = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    q = rng.standard_normal((1, Hkv * r, D)).astype(np.float32)
+    bt = np.array([[2, 0, 1]], np.int32)
+    pool = coracle.new_pool(3, Hkv, D)
+    coracle.append(pool, D, Hkv, k, v, W.slots_for(bt, 0, 0, L), sb)
+    cl = np.array([L], np.int32)
+    full = coracle.decode(pool, D, Hkv * r, Hkv, sb, bt, cl, q, 0.2)
+    for j in range(r):
+        sub = coracle.decode(pool, D, Hkv, Hkv, sb, bt, cl, q[:, [h * r + j for h in range(Hkv)]], 0.2)
+        for h in range(Hkv):
+            assert np.array_equal(full[0, h * r + j], sub[0, h])
+
+
+def test_memory_formula(coracle):
+    """Bytes per token of the pool = (K_bits + V_bits)/(2*16) of fp16 plus the scale
+    sidecar (mlxcel manual, cache-mode table note): 4+4 bits and one fp16 per 32 values."""
+    for D in (64, 128, 256):
+        per_token = coracle.block_bytes(D) / 16
+        fp16_per_token = 2 * D * 2
+        assert per_token / fp16_per_token == pytest.approx((4 + 4) / (2 * 16) + 2 * 16 / 32 / (2 * 16))
+    # 70B-like: 80 layers x 8 kv heads x 128 dims x 128K tokens in fp16 = 40 GiB (arXiv abstract)
+    assert 80 * 8 * 128 * 2 * 2 * 131072 / 2 ** 30 == pytest.approx(40.0)
