@@ -1,0 +1,269 @@
+"""Benchmark: one decode step of int4 compressed-domain attention on one MI355X.
+
+A step = the whole hot path over one batch: append the new token of every decoding
+sequence (plus the prefill chunk, for the mixed-serving workload) into the packed pool,
+then decode one query per sequence over its whole context, directly on the packed codes.
+Inputs are resident in HBM before the timed region. To measure HBM rather than the 256 MB
+Infinity Cache, the step cycles through several identical copies of the pool (>= 1 GiB
+in total), so each step reads a pool that was evicted since its last use.
+
+Prints one JSON line. Metric: effective KV GB/s (algorithmic packed K+V bytes + q + out,
+divided by the wall time of the step) and its fraction of the 8 TB/s HBM peak; decode
+microseconds per token at 128K context; roofline of the decode kernel (HIP events on the
+stream it runs on); the CPU oracle timed on the host; and the fp16
+dequantize-then-attend GPU baseline on the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective KV GB/s (fraction of HBM peak) + decode attn µs/token at 128K ctx"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--splits", type=int, default=0, help="context splits (0 = automatic)")
+    ap.add_argument("--min-pool-bytes", type=float, default=1.0 * 2 ** 30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baseline", action="store_true", help="skip the fp16 GPU baseline")
+    return ap.parse_args()
+
+
+def to_dev(arr, dtype, dev):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to(dev)
+
+
+class Setup:
+    """A workload resident on the GPU: filled pool (several copies), step inputs."""
+
+    def __init__(self, w, args, dev):
+        import torch
+        from int4_compressed_domain_amd import tq
+        from int4_compressed_domain_amd import workloads as W
+        self.w = w
+        D, Hkv = w.head_dim, w.kv_heads
+        self.sb = W.sign_bits(D, 0)
+        self.lens = W.context_lens(w, 0)
+        self.bt, self.prefill_pages, self.npages = W.page_tables(w, self.lens, 0)
+        self.sb_dev = torch.from_numpy(self.sb.view(np.int32)).to(dev)
+        self.layout = tq.make_layout(D, w.q_heads, Hkv, self.npages, self.sb_dev.data_ptr(),
+                                     w.k_codec, w.v_codec)
+        pool_bytes = self.npages * tq.tq_page_bytes(self.layout)
+        pool = torch.zeros(pool_bytes, dtype=torch.uint8, device=dev)
+        scales = W.channel_scales(w, 0)
+        self.scales = scales
+        # resident cache: every token but the last of each sequence
+        new_k, new_v, new_slots = [], [], []
+        t_fill = time.time()
+        for b in range(w.batch):
+            L = int(self.lens[b])
+            k32, v32, kst, vst = W.seq_tokens(w, b, L, 0, scales)
+            for t0 in range(0, L - 1, 16384):
+                t1 = min(L - 1, t0 + 16384)
+                tq.tq_kv_append(self.layout, pool, to_dev(kst[t0:t1], w.dtype, dev),
+                                to_dev(vst[t0:t1], w.dtype, dev),
+                                torch.from_numpy(W.slots_for(self.bt, b, t0, t1)).to(dev))
+            if L > 0:
+                new_k.append(kst[L - 1:L])
+                new_v.append(vst[L - 1:L])
+                new_slots.append(W.slots_for(self.bt, b, L - 1, L))
+        if w.prefill:
+            _, _, kst, vst = W.prefill_tokens(w, 0, scales)
+            new_k.append(kst)
+            new_v.append(vst)
+            pre = self.prefill_pages.astype(np.int64)
+            t = np.arange(w.prefill)
+            new_slots.append(pre[t // 16] * 16 + t % 16)
+        torch.cuda.synchronize()
+        log("filled %s: %d pages, %.1f MB pool, %.1f s" % (w.name, self.npages, pool_bytes / 1e6,
+                                                            time.time() - t_fill))
+        self.n_new = int(sum(len(s) for s in new_slots))
+        self.k_new = to_dev(np.concatenate(new_k), w.dtype, dev)
+        self.v_new = to_dev(np.concatenate(new_v), w.dtype, dev)
+        self.slots_new = torch.from_numpy(np.concatenate(new_slots).astype(np.int64)).to(dev)
+        ncopy = max(2, int(math.ceil(args.min_pool_bytes / max(pool_bytes, 1))))
+        self.pools = [pool] + [pool.clone() for _ in range(ncopy - 1)]
+        self.q32, qst = W.queries(w, 0)
+        self.q = to_dev(qst, w.dtype, dev)
+        self.bt_dev = torch.from_numpy(self.bt).to(dev)
+        self.lens_dev = torch.from_numpy(self.lens).to(dev)
+        self.max_ctx = int(self.lens.max())
+        self.splits = args.splits
+        ws = tq.tq_decode_workspace_size(self.layout, w.batch, self.max_ctx, self.splits)
+        self.ws = torch.zeros(max(ws, 4) // 4, dtype=torch.float32, device=dev)
+        self.out = torch.empty((w.batch, w.q_heads, D), dtype=torch.float32, device=dev)
+        self.alg_bytes = W.algorithmic_bytes(w, self.lens)
+        self.kv_bytes = int(np.sum(self.lens, dtype=np.int64)) * Hkv * 2 * (D // 2 + 2 * (D // 32))
+        log("pool copies: %d (%.2f GB)" % (ncopy, ncopy * pool_bytes / 1e9))
+
+    def append(self, i):
+        from int4_compressed_domain_amd import tq
+        tq.tq_kv_append(self.layout, self.pools[i % len(self.pools)], self.k_new, self.v_new,
+                        self.slots_new)
+
+    def decode(self, i):
+        from int4_compressed_domain_amd import tq
+        tq.tq_decode_attn(self.layout, self.pools[i % len(self.pools)], self.q, self.bt_dev,
+                          self.lens_dev, self.max_ctx, self.w.attn_scale, self.out, self.ws,
+                          num_splits=self.splits)
+
+
+def time_steps(S, steps, warmup):
+    """Wall-clock K steps between synchronizations; HIP events around each launch."""
+    import torch
+    for i in range(warmup):
+        S.append(i)
+        S.decode(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        S.append(warmup + i)
+        ev[i][1].record()
+        S.decode(warmup + i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    app = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3   # us
+    dec = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    return wall / steps * 1e3, app, dec
+
+
+def fp16_baseline(S, steps, warmup, dev):
+    """Dequantize to dense fp16 (original basis) then dense fp16 attention, same workload."""
+    import torch
+    from int4_compressed_domain_amd import tq
+    w = S.w
+    Lmax = S.max_ctx
+    k = torch.empty((w.batch, w.kv_heads, Lmax, w.head_dim), dtype=torch.float16, device=dev)
+    v = torch.empty_like(k)
+    out = torch.empty_like(S.out)
+    ws = torch.zeros(tq.tq_decode_workspace_size(S.layout, w.batch, Lmax, 0) // 4 + 1,
+                     dtype=torch.float32, device=dev)
+    res = {"dequant": [], "attend": []}
+    for i in range(warmup + steps):
+        pool = S.pools[i % len(S.pools)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        tq.tq_dequant_ref(S.layout, pool, S.bt_dev, S.lens_dev, Lmax, k, v, to_original_basis=1)
+        e[1].record()
+        tq.tq_dense_decode_attn(S.layout, k, v, S.q, S.lens_dev, Lmax, w.attn_scale, out, ws)
+        e[2].record()
+        if i >= warmup:
+            res["dequant"].append(e)
+    torch.cuda.synchronize()
+    dq = np.array([e[0].elapsed_time(e[1]) for e in res["dequant"]]) * 1e3
+    at = np.array([e[1].elapsed_time(e[2]) for e in res["dequant"]]) * 1e3
+    dense_bytes = 2 * k.numel() * 2
+    return {"dequant_us": float(np.median(dq)), "attend_us": float(np.median(at)),
+            "total_us": float(np.median(dq + at)), "dense_kv_bytes": int(dense_bytes),
+            "attend_GBps": dense_bytes / (np.median(at) * 1e-6) / 1e9}
+
+
+def cpu_baseline(w):
+    """The C oracle, as it stands, on the host cores: build its own pool (untimed), then time
+    its decode of the whole batch (every q head over every cached token)."""
+    from int4_compressed_domain_amd import workloads as W
+    from oracle import c_oracle
+    D, Hkv = w.head_dim, w.kv_heads
+    sb = W.sign_bits(D, 0)
+    lens = W.context_lens(w, 0)
+    bt, _, npages = W.page_tables(w, lens, 0)
+    # bounded sample: whole sequences, until ~2^27 token-heads of KV are covered
+    budget = 1 << 24
+    nseq = 0
+    while nseq < w.batch and int(np.sum(lens[:nseq + 1])) * Hkv <= budget:
+        nseq += 1
+    nseq = max(nseq, 1)
+    opool = c_oracle.new_pool(npages, Hkv, D)
+    scales = W.channel_scales(w, 0)
+    for b in range(nseq):
+        k32, v32, _, _ = W.seq_tokens(w, b, int(lens[b]), 0, scales)
+        c_oracle.append(opool, D, Hkv, k32, v32, W.slots_for(bt, b, 0, int(lens[b])), sb,
+                        w.k_codec, w.v_codec)
+    q32, _ = W.queries(w, 0)
+    pairs = np.array([(b, h) for b in range(nseq) for h in range(w.q_heads)], np.int32)
+    t0 = time.perf_counter()
+    c_oracle.decode(opool, D, w.q_heads, Hkv, sb, bt, lens, q32, w.attn_scale, pairs=pairs,
+                    k_codec=w.k_codec, v_codec=w.v_codec)
+    dt = time.perf_counter() - t0
+    kv = int(np.sum(lens[:nseq], dtype=np.int64)) * Hkv * 2 * (D // 2 + 2 * (D // 32))
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seconds": dt,
+            "sample": "C oracle decode (fp64) of %d of %d sequences x %d q heads, %d tokens each"
+                      % (nseq, w.batch, w.q_heads, int(lens[0]))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from int4_compressed_domain_amd import workloads as W
+    dev = "cuda:0"
+    name = args.workload or W.HEADLINE
+    w = W.WORKLOADS[name]
+    S = Setup(w, args, dev)
+    ms, app_us, dec_us = time_steps(S, args.steps, args.warmup)
+    dec_med = float(np.median(dec_us))
+    dec_mean = float(np.mean(dec_us))
+    value = S.alg_bytes / (ms * 1e-3) / 1e9
+    achieved = S.alg_bytes / (dec_mean * 1e-6) / 1e9
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": w.batch, "q_heads": w.q_heads,
+                   "kv_heads": w.kv_heads, "head_dim": w.head_dim, "context": w.context,
+                   "ragged_min": w.ragged_min, "prefill": w.prefill, "page": 16, "group": 32,
+                   "k_codec": ["absmax", "lloydmax"][w.k_codec], "v_codec": "absmax",
+                   "kv_input": w.dtype, "attn_scale": w.attn_scale, "splits": args.splits},
+        "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
+        "decode_us": round(dec_med, 3), "append_us": round(float(np.median(app_us)), 3),
+        "step_us": round(ms * 1e3, 3),
+        "us_per_token": round(ms * 1e3 / max(1, w.batch), 3),
+        "algorithmic_bytes": S.alg_bytes, "new_tokens_per_step": S.n_new,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "tq_decode_attn", "mean_us": round(dec_mean, 3)},
+    }
+    if not args.no_baseline:
+        base = fp16_baseline(S, min(args.steps, 20), 3, dev)
+        base["speedup_of_fused"] = round(base["total_us"] / dec_med, 2)
+        rec["fp16_dequant_then_attend"] = base
+    del S
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * tq.h -- C ABI of the MI355X (gfx950) int4 compressed-domain decode-attention library.
+ *
+ * What the library computes (sources are web pages, cited by title and section):
+ *  - On append, every key and value vector is rotated with a sign-randomized
+ *    Walsh-Hadamard transform, quantized to 4 bits per group of 32 coordinates with an
+ *    fp16 scale per group, and nibble-packed into a paged pool [Open-TQ-Metal, card
+ *    abstract: rotation + per-group abs-max + int4 nibble pack in one fused kernel;
+ *    "TurboQuant on AMD GPUs", section 4: Walsh-Hadamard rotation].
+ *  - Keys may instead use a 16-entry Gaussian Lloyd-Max table times the group's L2 norm,
+ *    values uniform abs-max ["TurboQuant on AMD GPUs", section 2, TQ4/4].
+ *  - Decode attention runs directly on the packed codes: the query is rotated into the
+ *    cache basis, scores and the weighted value sum are computed from codes and scales,
+ *    the softmax is online, and no dequantized K/V matrix is written [Open-TQ-Metal, arXiv
+ *    abstract]. A split over the context is merged in a second pass [online softmax
+ *    normalizer, cited among Open-TQ-Metal's references].
+ *  - The dequantize reference writes dense K/V, the "dequantize-then-attend" baseline the
+ *    arXiv abstract compares against; a dense fp16 decode attention completes it.
+ *
+ * Numerics (fixed so that codes are reproducible bit for bit):
+ *  - R = rho * H * diag(sigma), H the natural-order Sylvester Hadamard matrix
+ *    (H_ij = (-1)^popcount(i & j)), sigma_i = -1 iff bit i of sign_bits is set,
+ *    rho = fp32(1/sqrt(D)). fp32 butterfly with strides 1, 2, ..., D/2, then times rho.
+ *  - abs-max: s = fp16_rne(max|y|/7) (saturating at 65504); c = clamp(rint(y/s), -7, 7)
+ *    (c = 0 when s = 0); the stored 4-bit index is u = c + 8. Value = (u - 8) * s.
+ *  - Lloyd-Max (keys only): LUT_j = fp16_rne(m_j / sqrt(32)), m_j the 16 Lloyd-Max levels
+ *    of N(0,1) in increasing order; n = fp16_rne(sqrtf(sum of squares)) summed by the tree
+ *    t_i += t_{i+off}, off = 16, 8, 4, 2, 1; u = #{j in 1..15 : y/n >= (LUT_{j-1}+LUT_j)/2},
+ *    u = 8 when n = 0. Value = LUT_u * n.
+ *
+ * Pool format. A pool is one device buffer of num_pages * num_kv_heads * TQ_BLOCK_BYTES(D)
+ * bytes, [page][kv head][block]. A block holds 16 tokens of one KV head (G = D/32):
+ *     [K indices: 8*D B][V indices: 8*D B][K scales: 16*G fp16][V scales: 16*G fp16]
+ * Two 4-bit indices share a byte, the first in the low nibble.
+ *     K index of token t, dim d = 32g + 8j + e  ->  byte (16j + t)*4G + 4g + e/2, nibble e%2
+ *     V index of token t = 4j + e, dim d, c = d/2 = 16g + m
+ *                                            ->  byte 8D + (16j + m)*4G + 4g + e, nibble d%2
+ *     scale of token t, group g              ->  element t*G + g of its scale array
+ * These orders let one 64-lane wavefront load a block's K (or V) indices with one 16-byte
+ * load per lane, already in the operand order of the gfx950 matrix-core instructions.
+ * A slot is page * 16 + offset within the page.
+ *
+ * Conventions.
+ *  - Every buffer is allocated and owned by the caller; device pointers unless stated.
+ *    The library allocates nothing and keeps no mutable global state.
+ *  - Calls are asynchronous on the caller's stream (hipStream_t passed as void*, NULL =
+ *    default stream) and never synchronize.
+ *  - Arguments are checked on the host before any device work; failures return a
+ *    negative tq_status and launch nothing. A launch failure returns TQ_EDEVICE. Device
+ *    contents (slots, block tables, context lengths) are preconditions, not checked:
+ *    out-of-range values there are undefined behaviour.
+ *  - GPU support: head_dim in {64, 128, 256}, group_size 32, page_size 16,
+ *    1 <= num_q_heads / num_kv_heads <= 8 (TQ_EUNSUPPORTED otherwise).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = -1,        /* malformed argument: null pointer, negative size, bad enum */
+  TQ_EUNSUPPORTED = -2,  /* well-formed but outside what the GPU kernels implement */
+  TQ_ENOSPC = -3,        /* caller-provided workspace too small */
+  TQ_EDEVICE = -4        /* the HIP runtime reported an error */
+} tq_status;
+
+typedef enum { TQ_CODEC_ABSMAX = 0, TQ_CODEC_LLOYDMAX = 1 } tq_codec;
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+#define TQ_BLOCK_BYTES(D) (16 * (D) + 64 * ((D) / 32))
+
+typedef struct {
+  int32_t head_dim;          /* D: a power of two; 64, 128 or 256 on the GPU */
+  int32_t num_q_heads;       /* Hq */
+  int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0; q head hq uses kv head hq / (Hq/Hkv) */
+  int32_t group_size;        /* quantization group, must be 32 */
+  int32_t page_size;         /* tokens per page, must be 16 */
+  int32_t num_pages;         /* physical pages in the pool */
+  int32_t k_codec;           /* tq_codec for keys */
+  int32_t v_codec;           /* tq_codec for values (TQ_CODEC_ABSMAX only) */
+  const uint32_t* sign_bits; /* device, D/32 words; bit i of word i/32 set => sigma_i = -1 */
+} tq_layout;
+
+/* Human-readable name of a tq_status (static string, never NULL). */
+const char* tq_status_str(int status);
+
+/* Bytes of one physical page of the pool (all KV heads): num_kv_heads * TQ_BLOCK_BYTES(D).
+ * Returns 0 for an invalid layout. */
+size_t tq_page_bytes(const tq_layout* layout);
+
+/* Append: rotate, quantize and store n_tokens new K and V vectors.
+ *   pool          device, the layout's pool (written at the given slots only)
+ *   k, v          device, [n_tokens][num_kv_heads][head_dim] of in_dtype, row-major
+ *   slot_mapping  device int64 [n_tokens]: page * 16 + offset; a negative slot skips
+ *                 the token. Two tokens of one call must not share a slot.
+ * Writes exactly the indices and scales of the given slots; other bytes are untouched.
+ * [Open-TQ-Metal, card abstract: the fused quantize kernel] */
+int tq_kv_append(const tq_layout* layout, void* pool, const void* k, const void* v,
+                 int32_t in_dtype, int32_t n_tokens, const int64_t* slot_mapping, void* stream);
+
+/* Workspace bytes tq_decode_attn needs for this batch and maximum context length.
+ * num_splits: 0 picks the split count automatically (as tq_decode_attn does); > 0 asks
+ * for that many splits of the context (clamped to the number of pages). Returns 0 for
+ * invalid arguments. */
+size_t tq_decode_workspace_size(const tq_layout* layout, int32_t batch, int32_t max_context_len,
+                                int32_t num_splits);
+
+/* Decode attention on the compressed cache, one query per sequence.
+ *   q               device, [batch][num_q_heads][head_dim] of q_dtype (original basis)
+ *   block_table     device int32 [batch][max_pages_per_seq]: physical page of each
+ *                   16-token page of each sequence
+ *   context_lens    device int32 [batch]: tokens to attend (0 gives a zero output);
+ *                   each <= max_context_len <= 16 * max_pages_per_seq
+ *   max_context_len host, an upper bound of context_lens (sizes the launch)
+ *   attn_scale      softmax scale alpha (scores are alpha * q.k)
+ *   num_splits      0 = automatic; > 0 forces that many context splits (results agree
+ *                   across split counts up to rounding)
+ *   out             device fp32 [batch][num_q_heads][head_dim], original basis
+ *   workspace       device scratch of >= tq_decode_workspace_size(...) bytes (TQ_ENOSPC
+ *                   otherwise); contents on entry do not matter
+ * [Open-TQ-Metal, arXiv abstract: attention directly on the compressed representation] */
+int tq_decode_attn(const tq_layout* layout, const void* pool, const void* q, int32_t q_dtype,
+                   int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                   const int32_t* context_lens, int32_t max_context_len, float attn_scale,
+                   int32_t num_splits, float* out, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Dequantize reference: dense K and V, [batch][num_kv_heads][max_context_len][head_dim]
+ * of out_dtype (TQ_F32 or TQ_F16), rows at or past a sequence's length set to zero.
+ * to_original_basis = 0: values (u-8)*s or LUT_u*n in the rotated basis (exact products,
+ * rounded once to out_dtype); 1: times R^-1 = diag(sigma) * rho * H in fp32 (same stage
+ * order as the forward rotation), then rounded to out_dtype.
+ * [Open-TQ-Metal, arXiv abstract: the dequantize-then-attend baseline] */
+int tq_dequant_ref(const tq_layout* layout, const void* pool, int32_t batch,
+                   const int32_t* block_table, int32_t max_pages_per_seq,
+                   const int32_t* context_lens, int32_t max_context_len, int32_t to_original_basis,
+                   int32_t out_dtype, void* k_out, void* v_out, void* stream);
+
+/* Dense fp16 decode attention, the "attend" half of the baseline: K and V are fp16
+ * [batch][num_kv_heads][max_context_len][head_dim] (e.g. tq_dequant_ref output in the
+ * original basis), q as in tq_decode_attn but used unrotated; fp32 accumulation, same
+ * split/merge scheme; out fp32 [batch][num_q_heads][head_dim]. Workspace as for
+ * tq_decode_attn. Only head_dim, num_q_heads, num_kv_heads of the layout are used.
+ * [Open-TQ-Metal, arXiv abstract: dequantize-then-attend] */
+int tq_dense_decode_attn(const tq_layout* layout, const void* k, const void* v, const void* q,
+                         int32_t q_dtype, int32_t batch, const int32_t* context_lens,
+                         int32_t max_context_len, float attn_scale, int32_t num_splits,
+                         float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

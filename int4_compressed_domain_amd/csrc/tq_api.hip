@@ -1,0 +1,215 @@
+// Host side of the C ABI: argument validation (before any device work), launch geometry
+// (context split count), workspace sizing and kernel dispatch. Declarations and the
+// meaning of every argument are in include/tq.h.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Layout checks shared by every entry point. Non-power-of-two head dims are rejected, as
+// the mlxcel TurboQuant manual (head-dim limitation) does at cache initialisation.
+int check_layout(const tq_layout* L, bool need_pool_fields) {
+  if (!L) return TQ_EINVAL;
+  if (!is_pow2(L->head_dim)) return TQ_EINVAL;
+  if (L->num_q_heads <= 0 || L->num_kv_heads <= 0) return TQ_EINVAL;
+  if (L->num_q_heads % L->num_kv_heads != 0) return TQ_EINVAL;
+  if (L->head_dim != 64 && L->head_dim != 128 && L->head_dim != 256) return TQ_EUNSUPPORTED;
+  if (L->num_q_heads / L->num_kv_heads > 8) return TQ_EUNSUPPORTED;
+  if (!need_pool_fields) return TQ_OK;
+  if (L->group_size <= 0 || L->head_dim % L->group_size != 0) return TQ_EINVAL;
+  if (L->group_size != 32) return TQ_EUNSUPPORTED;
+  if (L->page_size <= 0) return TQ_EINVAL;
+  if (L->page_size != 16) return TQ_EUNSUPPORTED;
+  if (L->num_pages < 0) return TQ_EINVAL;
+  if (L->k_codec != TQ_CODEC_ABSMAX && L->k_codec != TQ_CODEC_LLOYDMAX) return TQ_EINVAL;
+  if (L->v_codec == TQ_CODEC_LLOYDMAX) return TQ_EUNSUPPORTED;  // the LUT codec is for keys
+  if (L->v_codec != TQ_CODEC_ABSMAX) return TQ_EINVAL;
+  if (!L->sign_bits) return TQ_EINVAL;
+  return TQ_OK;
+}
+
+bool valid_dtype(int d) { return d == TQ_F32 || d == TQ_BF16 || d == TQ_F16; }
+
+int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// Context split: enough (sequence, kv head, split) workgroups to give every compute unit
+// about three 4-wave workgroups, each split holding at least one page per wave.
+struct Split { int splits, pages_per_split; };
+
+Split choose_split(int B, int Hkv, int max_ctx, int requested) {
+  const int pages = (max_ctx + 15) / 16;
+  Split s{1, pages > 0 ? pages : 1};
+  if (pages == 0) return s;
+  int S;
+  if (requested > 0) {
+    S = requested < pages ? requested : pages;
+  } else {
+    const int64_t units = (int64_t)B * Hkv;
+    const int64_t target = 3LL * num_cus();
+    int64_t want = (target + units - 1) / units;
+    const int64_t cap = (pages + TQ_DECODE_WAVES - 1) / TQ_DECODE_WAVES;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    S = (int)want;
+  }
+  s.pages_per_split = (pages + S - 1) / S;
+  s.splits = (pages + s.pages_per_split - 1) / s.pages_per_split;
+  return s;
+}
+
+size_t workspace_bytes(int B, int Hq, int D, int splits) {
+  return (size_t)B * Hq * splits * ((size_t)D + 2) * sizeof(float);
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EDEVICE; }
+
+int check_decode_common(const tq_layout* L, const void* q, int q_dtype, int batch,
+                        const int32_t* context_lens, int max_context_len, float attn_scale,
+                        int num_splits, const float* out) {
+  if (batch < 0 || max_context_len < 0 || num_splits < 0) return TQ_EINVAL;
+  if (!valid_dtype(q_dtype)) return TQ_EINVAL;
+  if (!isfinite(attn_scale)) return TQ_EINVAL;
+  if (batch > 0 && (!q || !context_lens || !out)) return TQ_EINVAL;
+  if (batch > 65535) return TQ_EUNSUPPORTED;
+  (void)L;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_str(int status) {
+  switch (status) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_EINVAL: return "TQ_EINVAL: invalid argument";
+    case TQ_EUNSUPPORTED: return "TQ_EUNSUPPORTED: configuration not implemented on the GPU";
+    case TQ_ENOSPC: return "TQ_ENOSPC: workspace too small";
+    case TQ_EDEVICE: return "TQ_EDEVICE: HIP runtime error";
+    default: return "unknown tq_status";
+  }
+}
+
+size_t tq_page_bytes(const tq_layout* L) {
+  if (check_layout(L, true) != TQ_OK) return 0;
+  return (size_t)L->num_kv_heads * TQ_BLOCK_BYTES(L->head_dim);
+}
+
+int tq_kv_append(const tq_layout* L, void* pool, const void* k, const void* v, int32_t in_dtype,
+                 int32_t n_tokens, const int64_t* slot_mapping, void* stream) {
+  int rc = check_layout(L, true);
+  if (rc != TQ_OK) return rc;
+  if (n_tokens < 0 || !valid_dtype(in_dtype)) return TQ_EINVAL;
+  if (n_tokens == 0) return TQ_OK;
+  if (!pool || !k || !v || !slot_mapping) return TQ_EINVAL;
+  if ((int64_t)n_tokens * L->num_kv_heads * 2 > (int64_t)16 * 0x7fffffff) return TQ_EUNSUPPORTED;
+  LaunchAppend a{static_cast<uint8_t*>(pool), k, v, slot_mapping, L->sign_bits,
+                 L->head_dim, L->num_kv_heads, n_tokens, in_dtype, L->k_codec};
+  return from_hip(tq_launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t tq_decode_workspace_size(const tq_layout* L, int32_t batch, int32_t max_context_len,
+                                int32_t num_splits) {
+  if (check_layout(L, false) != TQ_OK || batch < 0 || max_context_len < 0 || num_splits < 0) return 0;
+  Split s = choose_split(batch, L->num_kv_heads, max_context_len, num_splits);
+  return workspace_bytes(batch, L->num_q_heads, L->head_dim, s.splits);
+}
+
+int tq_decode_attn(const tq_layout* L, const void* pool, const void* q, int32_t q_dtype,
+                   int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                   const int32_t* context_lens, int32_t max_context_len, float attn_scale,
+                   int32_t num_splits, float* out, void* workspace, size_t workspace_bytes_,
+                   void* stream) {
+  int rc = check_layout(L, true);
+  if (rc != TQ_OK) return rc;
+  rc = check_decode_common(L, q, q_dtype, batch, context_lens, max_context_len, attn_scale,
+                           num_splits, out);
+  if (rc != TQ_OK) return rc;
+  if (max_pages_per_seq < 0 || (int64_t)max_context_len > 16LL * max_pages_per_seq) return TQ_EINVAL;
+  if (batch == 0) return TQ_OK;
+  if (!pool || !block_table) return TQ_EINVAL;
+  Split s = choose_split(batch, L->num_kv_heads, max_context_len, num_splits);
+  const size_t need = workspace_bytes(batch, L->num_q_heads, L->head_dim, s.splits);
+  if (workspace_bytes_ < need) return TQ_ENOSPC;
+  if (!workspace) return TQ_EINVAL;
+  float* ws = static_cast<float*>(workspace);
+  LaunchDecode a{};
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.q = q;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.sign_bits = L->sign_bits;
+  a.out = out;
+  a.part_o = ws;
+  a.part_ml = ws + (size_t)batch * L->num_q_heads * s.splits * L->head_dim;
+  a.D = L->head_dim; a.Hq = L->num_q_heads; a.Hkv = L->num_kv_heads; a.B = batch;
+  a.max_pages = max_pages_per_seq; a.max_ctx = max_context_len;
+  a.q_dtype = q_dtype; a.k_codec = L->k_codec;
+  a.splits = s.splits; a.pages_per_split = s.pages_per_split;
+  a.attn_scale = attn_scale;
+  return from_hip(tq_launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int tq_dequant_ref(const tq_layout* L, const void* pool, int32_t batch, const int32_t* block_table,
+                   int32_t max_pages_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                   int32_t to_original_basis, int32_t out_dtype, void* k_out, void* v_out,
+                   void* stream) {
+  int rc = check_layout(L, true);
+  if (rc != TQ_OK) return rc;
+  if (batch < 0 || max_context_len < 0 || max_pages_per_seq < 0) return TQ_EINVAL;
+  if ((int64_t)max_context_len > 16LL * max_pages_per_seq) return TQ_EINVAL;
+  if (out_dtype != TQ_F32 && out_dtype != TQ_F16) return TQ_EINVAL;
+  if (to_original_basis != 0 && to_original_basis != 1) return TQ_EINVAL;
+  if ((int64_t)batch * max_context_len == 0) return TQ_OK;
+  if (!pool || !block_table || !context_lens || !k_out || !v_out) return TQ_EINVAL;
+  LaunchDequant a{static_cast<const uint8_t*>(pool), block_table, context_lens, L->sign_bits,
+                  k_out, v_out, L->head_dim, L->num_kv_heads, batch, max_pages_per_seq,
+                  max_context_len, to_original_basis, out_dtype, L->k_codec};
+  return from_hip(tq_launch_dequant(a, static_cast<hipStream_t>(stream)));
+}
+
+int tq_dense_decode_attn(const tq_layout* L, const void* k, const void* v, const void* q,
+                         int32_t q_dtype, int32_t batch, const int32_t* context_lens,
+                         int32_t max_context_len, float attn_scale, int32_t num_splits, float* out,
+                         void* workspace, size_t workspace_bytes_, void* stream) {
+  int rc = check_layout(L, false);
+  if (rc != TQ_OK) return rc;
+  rc = check_decode_common(L, q, q_dtype, batch, context_lens, max_context_len, attn_scale,
+                           num_splits, out);
+  if (rc != TQ_OK) return rc;
+  if (batch == 0) return TQ_OK;
+  if (!k || !v) return TQ_EINVAL;
+  Split s = choose_split(batch, L->num_kv_heads, max_context_len, num_splits);
+  const size_t need = workspace_bytes(batch, L->num_q_heads, L->head_dim, s.splits);
+  if (workspace_bytes_ < need) return TQ_ENOSPC;
+  if (!workspace) return TQ_EINVAL;
+  float* ws = static_cast<float*>(workspace);
+  LaunchDecode a{};
+  a.pool = static_cast<const uint8_t*>(k);
+  a.dense_v = v;
+  a.q = q;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.part_o = ws;
+  a.part_ml = ws + (size_t)batch * L->num_q_heads * s.splits * L->head_dim;
+  a.D = L->head_dim; a.Hq = L->num_q_heads; a.Hkv = L->num_kv_heads; a.B = batch;
+  a.max_ctx = max_context_len;
+  a.q_dtype = q_dtype;
+  a.splits = s.splits; a.pages_per_split = s.pages_per_split;
+  a.attn_scale = attn_scale;
+  return from_hip(tq_launch_dense_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

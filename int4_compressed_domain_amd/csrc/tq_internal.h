@@ -1,0 +1,48 @@
+// Internal launch descriptors shared by the host API (tq_api.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct LaunchAppend {
+  uint8_t* pool;
+  const void* k;
+  const void* v;
+  const int64_t* slots;
+  const uint32_t* sign_bits;
+  int D, Hkv, n_tokens, dtype, k_codec;
+};
+
+// Split-K decode: pass 1 writes, per (b, q head, split), the unnormalized weighted value
+// sum o' (rotated basis) and the running max m (log2 units) and sum l; pass 2 merges them.
+struct LaunchDecode {
+  const uint8_t* pool;       // compressed pool (pass 1), or dense fp16 K (dense path)
+  const void* dense_v;       // dense fp16 V (dense path only)
+  const void* q;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const uint32_t* sign_bits;
+  float* out;
+  float* part_o;             // [B][Hq][S][D]
+  float* part_ml;            // [B][Hq][S][2]
+  int D, Hq, Hkv, B, max_pages, max_ctx, q_dtype, k_codec;
+  int splits, pages_per_split;
+  float attn_scale;
+};
+
+hipError_t tq_launch_append(const LaunchAppend& a, hipStream_t st);
+hipError_t tq_launch_decode(const LaunchDecode& a, hipStream_t st);
+hipError_t tq_launch_dense_decode(const LaunchDecode& a, hipStream_t st);
+
+struct LaunchDequant {
+  const uint8_t* pool;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const uint32_t* sign_bits;
+  void* k_out;
+  void* v_out;
+  int D, Hkv, B, max_pages, max_ctx, original_basis, out_dtype, k_codec;
+};
+hipError_t tq_launch_dequant(const LaunchDequant& a, hipStream_t st);
+
+// Waves per pass-1 workgroup; each workgroup owns one (sequence, kv head, split).
+constexpr int TQ_DECODE_WAVES = 4;

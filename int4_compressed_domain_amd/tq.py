@@ -1,0 +1,134 @@
+"""Thin ctypes binding of libtq.so (include/tq.h). Argument marshalling only: every step of
+the path runs in the library's HIP kernels. Tensors are torch tensors; device pointers and
+the current HIP stream are passed through unchanged. Errors raise TQError.
+
+The binding never falls back to anything else: if libtq.so is missing, every call raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtq.so")
+
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_ENOSPC, TQ_EDEVICE = 0, -1, -2, -3, -4
+CODEC_ABSMAX, CODEC_LLOYDMAX = 0, 1
+F32, BF16, F16 = 0, 1, 2
+
+EXPORTS = ("tq_status_str", "tq_page_bytes", "tq_kv_append", "tq_decode_workspace_size",
+           "tq_decode_attn", "tq_dequant_ref", "tq_dense_decode_attn")
+
+
+class TQError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s" % (where, _lib().tq_status_str(status).decode()))
+
+
+class tq_layout(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("k_codec", ctypes.c_int32), ("v_codec", ctypes.c_int32),
+                ("sign_bits", ctypes.c_void_p)]
+
+
+_L = None
+
+
+def _lib():
+    global _L
+    if _L is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libtq.so is not built (run int4_compressed_domain_amd/build.py): "
+                              + LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        LP = ctypes.POINTER(tq_layout)
+        L.tq_status_str.argtypes = [ctypes.c_int]
+        L.tq_status_str.restype = ctypes.c_char_p
+        L.tq_page_bytes.argtypes = [LP]
+        L.tq_page_bytes.restype = sz
+        L.tq_kv_append.argtypes = [LP, P, P, P, i32, i32, P, P]
+        L.tq_decode_workspace_size.argtypes = [LP, i32, i32, i32]
+        L.tq_decode_workspace_size.restype = sz
+        L.tq_decode_attn.argtypes = [LP, P, P, i32, i32, P, i32, P, i32, f32, i32, P, P, sz, P]
+        L.tq_dequant_ref.argtypes = [LP, P, i32, P, i32, P, i32, i32, i32, P, P, P]
+        L.tq_dense_decode_attn.argtypes = [LP, P, P, P, i32, i32, P, i32, f32, i32, P, P, sz, P]
+        for name in ("tq_kv_append", "tq_decode_attn", "tq_dequant_ref", "tq_dense_decode_attn"):
+            getattr(L, name).restype = ctypes.c_int
+        _L = L
+    return _L
+
+
+def lib():
+    return _lib()
+
+
+def make_layout(head_dim, num_q_heads, num_kv_heads, num_pages, sign_bits_ptr, k_codec=0,
+                v_codec=0, group_size=32, page_size=16):
+    return tq_layout(head_dim, num_q_heads, num_kv_heads, group_size, page_size, num_pages,
+                     k_codec, v_codec, sign_bits_ptr)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t):
+    import torch
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}[t.dtype]
+
+
+def _check(rc, where):
+    if rc != TQ_OK:
+        raise TQError(rc, where)
+
+
+def tq_page_bytes(layout):
+    return _lib().tq_page_bytes(ctypes.byref(layout))
+
+
+def tq_kv_append(layout, pool, k, v, slot_mapping, stream=None):
+    n = k.shape[0] if k is not None else 0
+    _check(_lib().tq_kv_append(ctypes.byref(layout), _ptr(pool), _ptr(k), _ptr(v), _dtype_code(k),
+                               n, _ptr(slot_mapping), _stream(stream)), "tq_kv_append")
+
+
+def tq_decode_workspace_size(layout, batch, max_context_len, num_splits=0):
+    return _lib().tq_decode_workspace_size(ctypes.byref(layout), batch, max_context_len, num_splits)
+
+
+def tq_decode_attn(layout, pool, q, block_table, context_lens, max_context_len, attn_scale, out,
+                   workspace, num_splits=0, stream=None):
+    _check(_lib().tq_decode_attn(
+        ctypes.byref(layout), _ptr(pool), _ptr(q), _dtype_code(q), q.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(context_lens), max_context_len, attn_scale, num_splits,
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "tq_decode_attn")
+
+
+def tq_dequant_ref(layout, pool, block_table, context_lens, max_context_len, k_out, v_out,
+                   to_original_basis=1, stream=None):
+    _check(_lib().tq_dequant_ref(
+        ctypes.byref(layout), _ptr(pool), context_lens.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(context_lens), max_context_len, to_original_basis,
+        _dtype_code(k_out), _ptr(k_out), _ptr(v_out), _stream(stream)), "tq_dequant_ref")
+
+
+def tq_dense_decode_attn(layout, k, v, q, context_lens, max_context_len, attn_scale, out,
+                         workspace, num_splits=0, stream=None):
+    _check(_lib().tq_dense_decode_attn(
+        ctypes.byref(layout), _ptr(k), _ptr(v), _ptr(q), _dtype_code(q), q.shape[0],
+        _ptr(context_lens), max_context_len, attn_scale, num_splits, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "tq_dense_decode_attn")

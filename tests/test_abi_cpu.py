@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol of include/tq.h,
+and host-side validation rejects malformed arguments before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from int4_compressed_domain_amd import tq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(tq_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _header_functions()
+    assert set(names) == set(tq.EXPORTS), names
+    lib = tq.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(tq.lib().tq_status_str(s), bytes)
+
+
+def _layout(**kw):
+    args = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, num_pages=10, sign_bits_ptr=0x1000)
+    args.update(kw)
+    return tq.make_layout(**args)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _append(layout, n=1, dtype=tq.BF16, pool=FAKE, k=FAKE, v=FAKE, slots=FAKE):
+    return tq.lib().tq_kv_append(ctypes.byref(layout), pool, k, v, dtype, n, slots, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), tq.TQ_EINVAL),             # not a power of two: rejected
+    (dict(head_dim=0), tq.TQ_EINVAL),
+    (dict(head_dim=32), tq.TQ_EUNSUPPORTED),       # power of two outside 64/128/256
+    (dict(head_dim=512), tq.TQ_EUNSUPPORTED),
+    (dict(num_q_heads=30), tq.TQ_EINVAL),          # Hq % Hkv != 0
+    (dict(num_q_heads=0), tq.TQ_EINVAL),
+    (dict(num_q_heads=128), tq.TQ_EUNSUPPORTED),   # GQA ratio 16 > 8
+    (dict(group_size=24), tq.TQ_EINVAL),           # does not divide D
+    (dict(group_size=64), tq.TQ_EUNSUPPORTED),
+    (dict(page_size=32), tq.TQ_EUNSUPPORTED),
+    (dict(page_size=0), tq.TQ_EINVAL),
+    (dict(num_pages=-1), tq.TQ_EINVAL),
+    (dict(k_codec=5), tq.TQ_EINVAL),
+    (dict(v_codec=1), tq.TQ_EUNSUPPORTED),         # the LUT codec is for keys only
+    (dict(sign_bits_ptr=None), tq.TQ_EINVAL),
+])
+def test_layout_validation(kw, code):
+    assert _append(_layout(**kw)) == code
+
+
+def test_append_argument_validation():
+    L = _layout()
+    assert _append(L, n=-1) == tq.TQ_EINVAL
+    assert _append(L, dtype=9) == tq.TQ_EINVAL
+    assert _append(L, pool=None) == tq.TQ_EINVAL
+    assert _append(L, slots=None) == tq.TQ_EINVAL
+    assert _append(L, n=0, pool=None) == tq.TQ_OK     # nothing to do
+
+
+def _decode(L, batch=2, bt=FAKE, maxp=4, ctx=FAKE, maxctx=64, alpha=0.1, splits=0, out=FAKE,
+            ws=FAKE, wsb=1 << 30, q=FAKE, qd=tq.BF16, pool=FAKE):
+    return tq.lib().tq_decode_attn(ctypes.byref(L), pool, q, qd, batch, bt, maxp, ctx, maxctx,
+                                   alpha, splits, out, ws, wsb, None)
+
+
+def test_decode_argument_validation():
+    L = _layout()
+    assert _decode(L, batch=-1) == tq.TQ_EINVAL
+    assert _decode(L, maxctx=65, maxp=4) == tq.TQ_EINVAL        # more tokens than pages
+    assert _decode(L, splits=-2) == tq.TQ_EINVAL
+    assert _decode(L, qd=7) == tq.TQ_EINVAL
+    assert _decode(L, alpha=float("nan")) == tq.TQ_EINVAL
+    assert _decode(L, q=None) == tq.TQ_EINVAL
+    assert _decode(L, bt=None) == tq.TQ_EINVAL
+    assert _decode(L, wsb=16) == tq.TQ_ENOSPC
+    assert _decode(L, batch=0, q=None, out=None) == tq.TQ_OK
+
+
+def test_workspace_size_formula():
+    L = _layout()
+    for batch, ctx, splits in ((1, 131072, 5), (16, 8192, 1), (3, 100, 100)):
+        pages = -(-ctx // 16)
+        pps = -(-pages // min(splits, pages))
+        S = -(-pages // pps)
+        want = batch * 32 * S * (128 + 2) * 4
+        assert tq.tq_decode_workspace_size(L, batch, ctx, splits) == want
+    assert tq.tq_decode_workspace_size(_layout(head_dim=96), 1, 10, 0) == 0
+
+
+def test_page_bytes():
+    assert tq.tq_page_bytes(_layout()) == 8 * (16 * 128 + 64 * 4)
+    assert tq.tq_page_bytes(_layout(head_dim=256, num_q_heads=4, num_kv_heads=2)) == 2 * (16 * 256 + 64 * 8)
+    assert tq.tq_page_bytes(_layout(head_dim=100)) == 0
+
+
+def test_dequant_and_dense_validation():
+    L = _layout()
+    lib = tq.lib()
+    assert lib.tq_dequant_ref(ctypes.byref(L), FAKE, 1, FAKE, 4, FAKE, 64, 2, tq.F32, FAKE, FAKE, None) == tq.TQ_EINVAL
+    assert lib.tq_dequant_ref(ctypes.byref(L), FAKE, 1, FAKE, 4, FAKE, 64, 1, tq.BF16, FAKE, FAKE, None) == tq.TQ_EINVAL
+    assert lib.tq_dequant_ref(ctypes.byref(L), FAKE, 1, FAKE, 3, FAKE, 64, 1, tq.F32, FAKE, FAKE, None) == tq.TQ_EINVAL
+    assert lib.tq_dense_decode_attn(ctypes.byref(L), FAKE, None, FAKE, tq.BF16, 1, FAKE, 64, 0.1, 0, FAKE, FAKE, 1 << 30, None) == tq.TQ_EINVAL
+    assert lib.tq_dense_decode_attn(ctypes.byref(L), FAKE, FAKE, FAKE, tq.BF16, 1, FAKE, 64, 0.1, 0, FAKE, FAKE, 8, None) == tq.TQ_ENOSPC
+
+
+def test_lut_constant_matches_product_generator():
+    """The LUT table compiled into the kernels equals what the library's own generator
+    (independent of the oracle) derives from the Lloyd-Max iteration."""
+    from int4_compressed_domain_amd.csrc import gen_lloydmax
+    text = open(os.path.join(ROOT, "int4_compressed_domain_amd", "csrc", "tq_device.h")).read()
+    block = text[text.index("#define TQ_LUT16_BITS"):]
+    bits = [int(x, 16) for x in re.findall(r"0x([0-9a-f]{4})u", block)[:16]]
+    assert bits == gen_lloydmax.lut_bits()

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path through the C ABI against the C oracle on the same seeded inputs.
+
+* append: pools byte-identical (codes and fp16 scales) to the oracle's;
+* decode: per (sequence, q head) normwise relative error <= 2e-3 against the fp64 oracle;
+* dequantize reference: bit-identical to the oracle's fp32 dequantization;
+* dense fp16 baseline: against plain fp64 softmax attention of the same fp16 inputs.
+Small cases cover several pages with ragged tails; the full-size cases use the launch
+configuration the benchmark times and check sampled (sequence, head) outputs.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from int4_compressed_domain_amd import tq  # noqa: E402
+from int4_compressed_domain_amd import workloads as W  # noqa: E402
+from oracle import c_oracle  # noqa: E402
+
+from .gpu_util import ATTN_TOL, DEV, Case, attn_err, to_dev  # noqa: E402
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu_present():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tq.lib()
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check_case(c, pairs=None, num_splits=0, tol=ATTN_TOL):
+    out = c.decode_gpu(num_splits=num_splits)
+    if pairs is None:
+        ref = c.decode_oracle()
+        err = attn_err(out, ref)
+    else:
+        ref = c.decode_oracle(pairs)
+        got = np.stack([out[b, h] for b, h in pairs])
+        err = attn_err(got, ref)
+    assert np.all(np.isfinite(out)), "non-finite output"
+    _say("   max normwise err %.3e" % err.max())
+    assert err.max() <= tol, "attention error %.3e > %.1e" % (err.max(), tol)
+    return out
+
+
+SMALL = {
+    "single_head_1k": dict(context=1024, batch=1),
+    "llama8b_b16_8k": dict(context=700, batch=3),
+    "llama70b_b1_128k": dict(context=2000, batch=1),
+    "gemma_d256_32k": dict(context=900, batch=2),
+    "mixed_serving": dict(context=600, batch=5, ragged_min=17, prefill=100),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_workload_parity(name):
+    w = W.WORKLOADS[name].scaled(**SMALL[name])
+    _say("case", name, w)
+    c = Case(w)
+    c.fill()
+    if w.prefill:
+        k32, v32, kst, vst = W.prefill_tokens(w, c.seed, c.scales)
+        slots = c.prefill_pages.astype(np.int64).repeat(16)[:w.prefill] * 16 + np.arange(w.prefill) % 16
+        c.append_raw(k32, v32, kst, vst, slots)
+        torch.cuda.synchronize()
+    assert c.pool_equal(), "packed pool differs from the oracle"
+    _check_case(c)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("r", [1, 2, 4, 8])
+def test_head_dims_and_gqa(D, r):
+    base = W.WORKLOADS["llama8b_b16_8k"]
+    w = base.scaled(context=300, batch=2)
+    w = W.Workload("d%d_r%d" % (D, r), 2, 2 * r, 2, D, 300, "bf16", 1.0 / math.sqrt(D),
+                   dist="lognormal_spikes")
+    _say("case D=%d r=%d" % (D, r))
+    c = Case(w, seed=D + r)
+    c.fill()
+    assert c.pool_equal()
+    _check_case(c)
+
+
+@pytest.mark.parametrize("k_codec", [0, 1])
+def test_ragged_edge_lengths(k_codec):
+    lens = [0, 1, 15, 16, 17, 33, 48, 250]
+    w = W.Workload("edges", len(lens), 8, 2, 128, max(lens), "bf16", 0.125, k_codec=k_codec)
+    _say("case edge lengths, k_codec", k_codec)
+    c = Case(w, seed=5, lens=lens)
+    c.fill()
+    assert c.pool_equal()
+    out = _check_case(c)
+    assert np.all(out[0] == 0.0), "an empty sequence must give a zero output"
+
+
+@pytest.mark.parametrize("q_dtype", ["f32", "f16"])
+def test_query_dtypes(q_dtype):
+    w = W.WORKLOADS["llama8b_b16_8k"].scaled(context=200, batch=2)
+    _say("case q dtype", q_dtype)
+    c = Case(w, seed=3, q_dtype=q_dtype)
+    c.fill()
+    _check_case(c)
+
+
+def test_fp32_and_fp16_cache_inputs():
+    for dt in ("f32", "f16"):
+        w = W.Workload("in_" + dt, 2, 4, 2, 128, 130, "f32", 0.09)
+        c = Case(w, seed=9)
+        for b in range(w.batch):
+            k32, v32, _, _ = W.seq_tokens(w, b, int(c.lens[b]), c.seed, c.scales)
+            if dt == "f16":
+                k32, v32 = k32.astype(np.float16), v32.astype(np.float16)
+                c.w = W.Workload("in_f16", 2, 4, 2, 128, 130, "f16", 0.09)
+                c.append_raw(k32.astype(np.float32), v32.astype(np.float32), k32, v32,
+                             W.slots_for(c.bt, b, 0, int(c.lens[b])))
+                c.w = w
+            else:
+                c.append_raw(k32, v32, k32, v32, W.slots_for(c.bt, b, 0, int(c.lens[b])))
+        torch.cuda.synchronize()
+        assert c.pool_equal(), dt
+
+
+def test_split_count_invariance():
+    w = W.WORKLOADS["llama70b_b1_128k"].scaled(context=3000, batch=2)
+    _say("case split invariance")
+    c = Case(w, seed=11)
+    c.fill()
+    outs = [c.decode_gpu(num_splits=s) for s in (1, 2, 7, 0, 1000)]
+    for o in outs[1:]:
+        assert attn_err(o, outs[0]).max() < 1e-5
+    ref = c.decode_oracle()
+    for o in outs:
+        assert attn_err(o, ref).max() <= ATTN_TOL
+
+
+def test_negative_slots_and_untouched_bytes():
+    w = W.WORKLOADS["llama8b_b16_8k"].scaled(context=64, batch=1)
+    c = Case(w, seed=2)
+    c.pool.fill_(0xAB)
+    c.opool[:] = 0xAB
+    k32, v32, kst, vst = W.seq_tokens(w, 0, 40, c.seed, c.scales)
+    slots = W.slots_for(c.bt, 0, 0, 40)
+    slots[::3] = -1
+    c.append_raw(k32, v32, kst, vst, slots)
+    torch.cuda.synchronize()
+    assert c.pool_equal()
+
+
+@pytest.mark.parametrize("k_codec", [0, 1])
+@pytest.mark.parametrize("basis", [0, 1])
+def test_dequant_reference(k_codec, basis):
+    lens = [37, 0, 64]
+    w = W.Workload("dq", 3, 8, 2, 128, 64, "bf16", 0.1, k_codec=k_codec)
+    c = Case(w, seed=13, lens=lens)
+    c.fill()
+    Lmax = 64
+    for dt in (torch.float32, torch.float16):
+        ko = torch.full((3, 2, Lmax, 128), 7.0, dtype=dt, device=DEV)
+        vo = torch.full_like(ko, 7.0)
+        tq.tq_dequant_ref(c.layout, c.pool, c.bt_dev, c.lens_dev, Lmax, ko, vo, to_original_basis=basis)
+        torch.cuda.synchronize()
+        rk, rv = c_oracle.dequant(c.opool, 128, 2, c.sb, c.bt, c.lens, Lmax, basis, k_codec, 0)
+        if dt == torch.float16:
+            rk, rv = rk.astype(np.float16), rv.astype(np.float16)
+        assert np.array_equal(ko.cpu().numpy(), rk)
+        assert np.array_equal(vo.cpu().numpy(), rv)
+
+
+def test_dense_fp16_baseline():
+    w = W.WORKLOADS["gemma_d256_32k"].scaled(context=500, batch=2)
+    c = Case(w, seed=17, lens=[500, 333])
+    c.fill()
+    Lmax = 500
+    ko = torch.zeros((2, w.kv_heads, Lmax, w.head_dim), dtype=torch.float16, device=DEV)
+    vo = torch.zeros_like(ko)
+    tq.tq_dequant_ref(c.layout, c.pool, c.bt_dev, c.lens_dev, Lmax, ko, vo, to_original_basis=1)
+    ws = torch.empty(tq.tq_decode_workspace_size(c.layout, 2, Lmax, 0) // 4, dtype=torch.float32, device=DEV)
+    out = torch.zeros((2, w.q_heads, w.head_dim), dtype=torch.float32, device=DEV)
+    tq.tq_dense_decode_attn(c.layout, ko, vo, c.q_dev, c.lens_dev, Lmax, w.attn_scale, out, ws)
+    torch.cuda.synchronize()
+    K = ko.cpu().numpy().astype(np.float64)
+    V = vo.cpu().numpy().astype(np.float64)
+    ref = np.zeros((2, w.q_heads, w.head_dim))
+    alpha = float(np.float32(w.attn_scale))
+    for b in range(2):
+        for hq in range(w.q_heads):
+            h = hq // w.gqa
+            L = int(c.lens[b])
+            s = alpha * (K[b, h, :L] @ c.q32[b, hq].astype(np.float64))
+            p = np.exp(s - s.max())
+            ref[b, hq] = p @ V[b, h, :L] / p.sum()
+    assert attn_err(out.cpu().numpy(), ref).max() <= ATTN_TOL
+
+
+# ---- full-size workloads, in the benchmark's launch configuration --------------------------
+
+def _pairs(w, lens, n=12, seed=0):
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (w.batch - 1, w.q_heads - 1), (0, w.q_heads - 1)}
+    while len(pairs) < n:
+        pairs.add((int(rng.integers(w.batch)), int(rng.integers(w.q_heads))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", ["single_head_1k", "llama8b_b16_8k", "llama70b_b1_128k",
+                                  "gemma_d256_32k", "mixed_serving"])
+def test_full_size_workloads(name):
+    w = W.WORKLOADS[name]
+    _say("case full-size", name)
+    c = Case(w)
+    c.fill(chunk=8192)
+    if w.prefill:
+        k32, v32, kst, vst = W.prefill_tokens(w, c.seed, c.scales)
+        slots = c.prefill_pages.astype(np.int64).repeat(16)[:w.prefill] * 16 + np.arange(w.prefill) % 16
+        c.append_raw(k32, v32, kst, vst, slots)
+        torch.cuda.synchronize()
+    assert c.pool_equal(), "packed pool differs from the oracle"
+    _say("   pool bytes equal (%d B)" % c.pool.numel())
+    pairs = None if w.batch * w.q_heads <= 64 else _pairs(w, c.lens)
+    _check_case(c, pairs=pairs)
