@@ -50,7 +50,8 @@
  *    contents (slots, block tables, context lengths) are preconditions, not checked:
  *    out-of-range values there are undefined behaviour.
  *  - GPU support: head_dim in {64, 128, 256}, group_size 32, page_size 16,
- *    1 <= num_q_heads / num_kv_heads <= 8 (TQ_EUNSUPPORTED otherwise).
+ *    1 <= num_q_heads / num_kv_heads <= 8, batch * num_kv_heads <= 2^20
+ *    (TQ_EUNSUPPORTED otherwise).
  */
 #ifndef TQ_H
 #define TQ_H
@@ -74,6 +75,11 @@ typedef enum { TQ_CODEC_ABSMAX = 0, TQ_CODEC_LLOYDMAX = 1 } tq_codec;
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
 #define TQ_BLOCK_BYTES(D) (16 * (D) + 64 * ((D) / 32))
+
+/* The first TQ_DECODE_COUNTER_BYTES bytes of a decode workspace hold per-(sequence,
+ * kv head) arrival counters. They must be zero before the workspace is first used; every
+ * tq_decode_attn call leaves them zero again. */
+#define TQ_DECODE_COUNTER_BYTES ((size_t)4 << 20)
 
 typedef struct {
   int32_t head_dim;          /* D: a power of two; 64, 128 or 256 on the GPU */
@@ -119,11 +125,13 @@ size_t tq_decode_workspace_size(const tq_layout* layout, int32_t batch, int32_t 
  *                   each <= max_context_len <= 16 * max_pages_per_seq
  *   max_context_len host, an upper bound of context_lens (sizes the launch)
  *   attn_scale      softmax scale alpha (scores are alpha * q.k)
- *   num_splits      0 = automatic; > 0 forces that many context splits (results agree
- *                   across split counts up to rounding)
+ *   num_splits      0 = automatic; > 0 forces that many context splits, at most 128
+ *                   (results agree across split counts up to rounding)
  *   out             device fp32 [batch][num_q_heads][head_dim], original basis
  *   workspace       device scratch of >= tq_decode_workspace_size(...) bytes (TQ_ENOSPC
- *                   otherwise); contents on entry do not matter
+ *                   otherwise). Its first TQ_DECODE_COUNTER_BYTES must be zero before the
+ *                   first call (a zero-filled allocation); the rest is overwritten freely.
+ *                   Two calls that run at the same time must not share a workspace.
  * [Open-TQ-Metal, arXiv abstract: attention directly on the compressed representation] */
 int tq_decode_attn(const tq_layout* layout, const void* pool, const void* q, int32_t q_dtype,
                    int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,

@@ -20,6 +20,7 @@ SOURCES = {
     "append.hip": ["-ffp-contract=off"],
     "dequant.hip": ["-ffp-contract=off"],
     "decode.hip": [],
+    "dense.hip": [],
 }
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

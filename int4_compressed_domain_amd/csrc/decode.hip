@@ -1,84 +1,191 @@
-// Decode attention directly on the packed int4 cache.
+// Decode attention directly on the packed int4 cache, one fused kernel.
 // [Open-TQ-Metal, arXiv abstract: attention computed on the compressed representation,
-//  no intermediate dequantized K/V; the split merge follows the online softmax normalizer
-//  cited among its references.]
+//  no intermediate dequantized K/V matrix; the split merge follows the online softmax
+//  normalizer cited among its references.]
 //
-// Pass 1, one workgroup of 4 wavefronts per (sequence b, kv head h, context split s):
-//  prologue  the r = Hq/Hkv queries of kv head h are rotated into the cache basis with the
-//            same fp32 butterfly as the keys, scaled by alpha*log2(e) and a power of two,
-//            and split into fp16 hi + lo parts: B operand rows 0..7 hold hi of heads 0..7,
-//            rows 8..15 hold lo, so one 16-column MFMA carries ~22 bits of the query.
-//  loop      each wave takes every 4th page of the split. Per 16-token page:
-//            scores  S^T[t][row] = sum_g sK[t][g] * (K_g codes . q_g)  (4 x 16x16x32 MFMA
-//                    at D=128, one per 32-dim group, codes exact in fp16), hi + lo rows
-//                    added with a DPP lane rotate;
-//            softmax running max/sum per head (log2 domain);
-//            values  o'^T[d][row] += sum_t V codes[t][d] * P'[t][row], P' = p * sV (fp16
-//                    hi in rows 0..7, lo in rows 8..15), 2 x 16x16x16 MFMA per group.
-//  epilogue  the 4 waves merge through LDS; one partial (o', m, l) per split is written.
-// Pass 2, one wavefront per (b, q head): merge the splits, divide by the sum, and rotate
-//  back to the original basis (fp32 butterfly, times rho, times sigma).
+// Work unit u = (sequence b, kv head h); its pages are cut into S context splits, one
+// workgroup of NW wavefronts per (u, split). Workgroup order is XCD-aware: MI355X hands
+// consecutive workgroups to its 8 XCDs in turn, so all splits of unit u are placed on XCD
+// u mod 8 and the partials they exchange stay in that XCD's L2.
+//
+//  prologue  the r = Hq/Hkv queries of head h are rotated into the cache basis with the same
+//            fp32 butterfly as the keys, scaled by alpha*log2(e) and a power of two, and split
+//            into fp16 hi + lo parts: B-operand columns 0..7 hold hi of heads 0..7, columns
+//            8..15 hold lo, so one 16-column MFMA carries ~22 bits of each query.
+//  page loop each wave takes every NW-th page of the split, loading the next page while it
+//            computes the current one. Per 16-token page:
+//            scores  the K operand is the index bits themselves: (w & 0x000F000F) is the fp16
+//                    subnormal u * 2^-24 (exact), so one AND unpacks two indices; the offset
+//                    u = c + 8 is removed exactly by starting the MFMA accumulator at -beta,
+//                    beta = 8 * 2^-24 * (sum of the 32 query values of the group). One
+//                    16x16x32 MFMA per 32-dim group, then times the group's fp16 scale;
+//            softmax running max/sum per head in the log2 domain, rescaling only when the
+//                    max grows;
+//            values  V indices become exact fp16 c via 1024 + n magic; P' = p * s_V in fp16
+//                    hi (columns 0..7) + lo (8..15); two 16x16x16 MFMAs per group.
+//  epilogue  the NW waves merge through LDS. With one split the workgroup finishes the head;
+//            otherwise it stores its partial (o', m, l), and the last workgroup of the unit
+//            to arrive (atomic counter, reset afterwards) merges all splits. The result is
+//            rotated back (fp32 butterfly, times rho, times sigma) and written.
 #include "tq_device.h"
 #include "tq_internal.h"
 
 namespace {
 
-template <int G>
-__device__ __forceinline__ void load_dwords(const uint8_t* __restrict__ p, uint32_t (&w)[G]) {
-  if constexpr (G == 2) {
-    u32x2 a = *reinterpret_cast<const u32x2*>(p);
-    w[0] = a[0]; w[1] = a[1];
-  } else {
-#pragma unroll
-    for (int i = 0; i < G / 4; i++) {
-      u32x4 a = reinterpret_cast<const u32x4*>(p)[i];
-      w[4 * i] = a[0]; w[4 * i + 1] = a[1]; w[4 * i + 2] = a[2]; w[4 * i + 3] = a[3];
-    }
-  }
+// Subnormal-form K operand: dword of indices of dims e = 0..7 (nibble position e) -> 8
+// halves in k-slot order [e0 e4 e1 e5 e2 e6 e3 e7], values u*2^-24 for e0 e4 e2 e6 and
+// 16u*2^-24 for e1 e5 e3 e7 (the matching query values are divided by 16).
+__device__ __forceinline__ f16x8 unpack_k_sub(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  u32x4 r = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+  return __builtin_bit_cast(f16x8, r);
 }
 
-// 4 tokens x G fp16 scales (8G bytes, 16-byte aligned for G >= 2).
-template <int G>
-__device__ __forceinline__ void load_scales(const uint8_t* __restrict__ p, f16 (&s)[4 * G]) {
-  uint32_t w[2 * G];
-  if constexpr (G == 2) {
-    u32x4 a = *reinterpret_cast<const u32x4*>(p);
-    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
-  } else {
+// V operand: dword = 4 tokens (bytes) of one dim pair (even dim low nibble). Returns the
+// exact signed codes of the even dim and of the odd dim, k-slot order tokens [0 2 1 3].
+__device__ __forceinline__ void unpack_v(uint32_t w, uint32_t m0, uint32_t m1, uint32_t mg,
+                                         f16x4& ev, f16x4& od) {
+  const f16x2 off0 = {(f16)1032.0f, (f16)1032.0f};
+  const f16x2 sc1 = {(f16)0.0625f, (f16)0.0625f};
+  const f16x2 off1 = {(f16)72.0f, (f16)72.0f};
+  const uint32_t w8 = w >> 8;
+  const f16x2 e02 = as_h2(and_or(w, m0, mg)) - off0;
+  const f16x2 e13 = as_h2(and_or(w8, m0, mg)) - off0;
+  const f16x2 o02 = as_h2(and_or(w, m1, mg)) * sc1 - off1;
+  const f16x2 o13 = as_h2(and_or(w8, m1, mg)) * sc1 - off1;
+  ev = f16x4{e02[0], e02[1], e13[0], e13[1]};
+  od = f16x4{o02[0], o02[1], o13[0], o13[1]};
+}
+
+template <int D>
+struct Cfg {
+  static constexpr int G = D / 32;
+  static constexpr int BB = TQ_BLOCK_BYTES(D);
+  static constexpr int KB = 4 * G;                    // index bytes per lane per page (K or V)
+  static constexpr int DMAK = KB >= 16 ? 16 : 4;      // LDS-DMA size for index loads
+  static constexpr int NK = KB / DMAK;                // DMAs per index region
+  static constexpr int NSC = (16 * G + 63) / 64;      // dword DMAs for the scale region
+  static constexpr int NDMA = 2 * NK + NSC;            // vector-memory ops per page
+  static constexpr int SLOT = 128 * KB + 64 * G;      // LDS bytes of one staged page
+  static constexpr int NSLOT = 3;                     // ring slots per wave (2 pages in flight)
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+// Buffer loads that write LDS directly (lane i's `n` bytes land at lds + i * n). Issued from
+// inline asm so that the only waits for them are the explicit vmcnt waits of the page ring;
+// M0 (the LDS base) is set inside the same statement and used by nothing else here.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               ::"v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               ::"v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory");
+}
+
+// Stage one page (one kv head's block) into an LDS slot:
+//   [K indices: NK chunks of 64 lanes x DMAK][V indices: same][scales: 16G dwords]
+// The buffer descriptor spans exactly this block, so no lane can touch memory outside it.
+template <int D>
+__device__ __forceinline__ void stage_page(const uint8_t* blk, uint8_t* slot, int lane) {
+  using C = Cfg<D>;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
+  const uint32_t lo = (uint32_t)lane * C::KB;  // this lane's byte offset inside an index region
+  const uint32_t base = lds_addr(slot);
 #pragma unroll
-    for (int i = 0; i < G / 2; i++) {
-      u32x4 a = reinterpret_cast<const u32x4*>(p)[i];
-      w[4 * i] = a[0]; w[4 * i + 1] = a[1]; w[4 * i + 2] = a[2]; w[4 * i + 3] = a[3];
+  for (int c = 0; c < C::NK; c++) {
+    if constexpr (C::DMAK == 16) {
+      dma16(r, lo + c * 16, 0u, base + c * 1024);
+      dma16(r, lo + c * 16, 8u * D, base + 64 * C::KB + c * 1024);
+    } else {
+      dma4(r, lo + c * 4, 0u, base + c * 256);
+      dma4(r, lo + c * 4, 8u * D, base + 64 * C::KB + c * 256);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 2 * G; i++) {
-    f16x2 h = as_h2(w[i]);
-    s[2 * i] = h[0];
-    s[2 * i + 1] = h[1];
-  }
+  for (int c = 0; c < C::NSC; c++)
+    if (c * 64 + lane < 16 * C::G) dma4(r, 4 * (c * 64 + lane), 16u * D, base + 128 * C::KB + 256 * c);
 }
 
-template <int D, typename TQ, int KCODEC>
-__global__ __launch_bounds__(64 * TQ_DECODE_WAVES) void decode_pass1(LaunchDecode a) {
-  constexpr int G = D / 32, BB = TQ_BLOCK_BYTES(D), NW = TQ_DECODE_WAVES, NT = 64 * NW;
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+// Block-table entry as a wave-uniform (scalar) value. A scalar load through the scalar
+// cache; the wait sits in the same statement so the result is complete when it is used.
+__device__ __forceinline__ const uint8_t* page_base(const int32_t* bt, int p, const uint8_t* hbase,
+                                                    int64_t pstride) {
+  const int pu = __builtin_amdgcn_readfirstlane(p);
+  const int32_t* ptr = bt + pu;
+  int page;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(page) : "s"(ptr) : "memory");
+  return hbase + (int64_t)page * pstride;
+}
+
+// s_waitcnt vmcnt(n) with n a multiple of the per-page DMA count: n = k * NDMA, k = pages
+// issued after the one about to be read. The compiler does not track LDS-DMA writes.
+template <int NDMA>
+__device__ __forceinline__ void wait_pages_in_flight(int k) {
+  if (k >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NDMA) : "memory");
+  else if (k == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int D, typename TQ, int KCODEC, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
+  using C = Cfg<D>;
+  constexpr int G = C::G, BB = C::BB, NT = 64 * NW;
+  constexpr bool KSUB = (KCODEC == TQ_CODEC_ABSMAX);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar page loads
+  const int jq = lane >> 4, hr = lane & 15;
+
+  // ---- XCD-aware placement: unit u on XCD u mod 8 -----------------------------------------
+  const int U = a.B * a.Hkv;
+  const int n8 = (U + 7) >> 3;
+  const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
+  const int u = xcd + 8 * (kk % n8), s = kk / n8;
+  if (u >= U) return;
+  const int b = u / a.Hkv, h = u - b * a.Hkv;
   const int r = a.Hq / a.Hkv;
   const int L = a.context_lens[b];
   const int npages = (L + 15) >> 4;
-  const int p0 = s * a.pages_per_split;
-  if (p0 >= npages) return;  // pass 2 reads only the splits that hold pages
-  const int p1 = min(p0 + a.pages_per_split, npages);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int jq = lane >> 4, hr = lane & 15;
+  const int pps = a.pages_per_split;
+  const int ns = (npages + pps - 1) / pps;
+  float* outp = a.out + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
+  if (npages == 0) {  // empty sequence: zero output, written by split 0
+    if (s == 0)
+      for (int i = tid; i < r * D; i += NT) outp[i] = 0.0f;
+    return;
+  }
+  if (s >= ns) return;
+  const int p0 = s * pps, p1 = min(p0 + pps, npages);
 
-  __shared__ float qs[8 * D];
-  __shared__ f16x8 bq[G * 64];
+  // page ring (per wave) -- reused after the page loop for the per-wave partial results
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NW][C::NSLOT][C::SLOT];
+  __shared__ float qs[8 * D];                  // rotation workspace / output staging
+  __shared__ f16x8 bq[G * 64];                 // query B operands per (group, lane)
+  __shared__ float cb[G * 16];                 // -beta per (group, column)
   __shared__ float red[NW];
-  __shared__ float mo[NW][8][D];
-  __shared__ float mml[NW][8][2];
+  __shared__ float mml[NW][8][2];              // per-wave (m, l), then per-wave weights
+  __shared__ float wsh[8][TQ_MAX_SPLITS];      // split weights of the final merge
+  __shared__ float lsh[8][TQ_MAX_SPLITS];      // split sums l of the final merge
+  __shared__ int last_flag;
+  static_assert(NW * 8 * D * 4 <= NW * C::NSLOT * C::SLOT, "merge area must fit the ring");
+  float (*mo)[8][D] = reinterpret_cast<float (*)[8][D]>(&ring[0][0][0]);
 
-  // ---- prologue: rotate and split the queries ------------------------------------------
+  // ---- start streaming the first pages before the query prologue ---------------------------
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  const uint8_t* hbase = a.pool + (int64_t)h * BB;
+  const int64_t pstride = (int64_t)a.Hkv * BB;
+#pragma unroll
+  for (int k = 0; k < C::NSLOT - 1; k++) {
+    const int pp = p0 + wv + k * NW;
+    if (pp < p1) stage_page<D>(page_base(bt, pp, hbase, pstride), ring[wv][k], lane);
+  }
+
+  // ---- prologue: rotate, scale and split the queries ----------------------------------------
   const TQ* qb = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
   for (int i = tid; i < 8 * D; i += NT) {
     const int hd = i / D, d = i % D;
@@ -116,7 +223,9 @@ __global__ __launch_bounds__(64 * TQ_DECODE_WAVES) void decode_pass1(LaunchDecod
   for (int w = 1; w < NW; w++) mx = fmaxf(mx, red[w]);
   int sh = 0;
   if (mx > 0.0f) sh = min(60, max(-60, 14 - ilogbf(mx)));
-  const float up = ldexpf(1.0f, sh), down = ldexpf(1.0f, -sh);
+  const float up = ldexpf(1.0f, sh);
+  // scores come out in units of 2^-sh (times 2^24 for the subnormal K form)
+  const float down = ldexpf(1.0f, KSUB ? 24 - sh : -sh);
   for (int idx = tid; idx < G * 64; idx += NT) {
     const int g = idx >> 6, l = idx & 63, j = l >> 4, c = l & 15, hd = c & 7;
     f16x8 v;
@@ -124,17 +233,36 @@ __global__ __launch_bounds__(64 * TQ_DECODE_WAVES) void decode_pass1(LaunchDecod
     for (int k = 0; k < 8; k++) {
       const float x = (hd < r) ? qs[hd * D + 32 * g + 8 * j + kslot_dim<KCODEC>(k)] * up : 0.0f;
       const f16 hi = (f16)x;
-      v[k] = (c < 8) ? hi : (f16)(x - (float)hi);
+      f16 part = (c < 8) ? hi : (f16)(x - (float)hi);
+      if (KSUB && (k & 2)) part = part * (f16)0.0625f;  // odd nibble positions carry 16u
+      v[k] = part;
     }
     bq[idx] = v;
   }
-  __syncthreads();
-  f16x8 bop[G];
+  if (KSUB) {
+    // beta = 8 * 2^-24 * (sum over the group of the query part that column c holds); one
+    // lane per (group, column, 8-dim chunk), chunks summed with two lane exchanges
+    for (int idx = tid; idx < G * 64; idx += NT) {
+      const int g = idx >> 6, c = (idx >> 2) & 15, q4 = idx & 3, hd = c & 7;
+      float sum = 0.0f;
+      if (hd < r)
 #pragma unroll
-  for (int g = 0; g < G; g++) bop[g] = bq[g * 64 + lane];
-
+        for (int k = 0; k < 8; k++) {
+          const float x = qs[hd * D + 32 * g + 8 * q4 + k] * up;
+          const f16 hi = (f16)x;
+          sum += (c < 8) ? (float)hi : (float)(f16)(x - (float)hi);
+        }
+      sum += __shfl_xor(sum, 1, 64);
+      sum += __shfl_xor(sum, 2, 64);
+      if (q4 == 0) cb[g * 16 + c] = -sum * 4.76837158203125e-07f;  // 8 * 2^-24
+    }
+  }
+  __syncthreads();
+  float cinit[G];
+#pragma unroll
+  for (int g = 0; g < G; g++) cinit[g] = KSUB ? cb[g * 16 + hr] : 0.0f;
   uint32_t tlo[4] = {0, 0, 0, 0}, thi[4] = {0, 0, 0, 0};
-  if constexpr (KCODEC == TQ_CODEC_LLOYDMAX) {
+  if constexpr (!KSUB) {
     const uint16_t lb[16] = TQ_LUT16_BITS;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
@@ -142,314 +270,261 @@ __global__ __launch_bounds__(64 * TQ_DECODE_WAVES) void decode_pass1(LaunchDecod
       thi[i >> 2] |= (uint32_t)(lb[i] >> 8) << (8 * (i & 3));
     }
   }
+  // constants of the V unpack, kept in VGPRs for v_and_or_b32
+  uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = 0x64006400u;
+  asm("" : "+v"(m0), "+v"(m1), "+v"(mg));
+  const float lofac = (hr >= 8) ? 1.0f : 0.0f;
 
-  // ---- main loop over pages --------------------------------------------------------------
+  // ---- page loop ------------------------------------------------------------------------
   f32x4 acc[2 * G];
 #pragma unroll
   for (int t = 0; t < 2 * G; t++) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
-  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int p = p0 + wv; p < p1; p += NW) {
-    const uint8_t* blk = a.pool + ((int64_t)bt[p] * a.Hkv + h) * BB;
+  auto page = [&](const uint8_t* slot, int p, bool masked) {
     uint32_t kw[G], vw[G];
-    load_dwords<G>(blk + lane * 4 * G, kw);
-    load_dwords<G>(blk + 8 * D + lane * 4 * G, vw);
-    f16 ks[4 * G], vs[4 * G];
-    load_scales<G>(blk + 16 * D + 8 * G * jq, ks);
-    load_scales<G>(blk + 16 * D + 32 * G + 8 * G * jq, vs);
+#pragma unroll
+    for (int c = 0; c < C::NK; c++) {
+      if constexpr (C::DMAK == 16) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(slot + c * 1024 + lane * 16);
+        const u32x4 y = *reinterpret_cast<const u32x4*>(slot + 64 * C::KB + c * 1024 + lane * 16);
+        kw[4 * c] = x[0]; kw[4 * c + 1] = x[1]; kw[4 * c + 2] = x[2]; kw[4 * c + 3] = x[3];
+        vw[4 * c] = y[0]; vw[4 * c + 1] = y[1]; vw[4 * c + 2] = y[2]; vw[4 * c + 3] = y[3];
+      } else {
+        kw[c] = *reinterpret_cast<const uint32_t*>(slot + c * 256 + lane * 4);
+        vw[c] = *reinterpret_cast<const uint32_t*>(slot + 64 * C::KB + c * 256 + lane * 4);
+      }
+    }
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(slot + 128 * C::KB);
+    uint32_t kst[2 * G], vst[2 * G];  // fp16 pairs: tokens 4jq..4jq+3, groups 0..G-1
+#pragma unroll
+    for (int i = 0; i < 2 * G; i += 4) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(&sw[2 * G * jq + i]);
+      kst[i] = x[0]; kst[i + 1] = x[1]; kst[i + 2] = x[2]; kst[i + 3] = x[3];
+    }
+    auto ksc = [&](int e, int g) { return (float)as_h2(kst[(e * G + g) >> 1])[(e * G + g) & 1]; };
+    auto vsc = [&](int e, int g) { return (float)as_h2(vst[(e * G + g) >> 1])[(e * G + g) & 1]; };
 
     float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < G; g++) {
       f16x8 A;
-      if constexpr (KCODEC == TQ_CODEC_LLOYDMAX) A = unpack_k_lut(kw[g], tlo, thi);
-      else A = unpack_k_absmax(kw[g]);
-      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bop[g], zero4, 0, 0, 0);
+      if constexpr (KSUB) A = unpack_k_sub(kw[g]);
+      else A = unpack_k_lut(kw[g], tlo, thi);
+      const f32x4 ci = {cinit[g], cinit[g], cinit[g], cinit[g]};
+      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bq[g * 64 + lane], ci, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; e++) sc[e] += (float)ks[e * G + g] * c[e];
+      for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(ksc(e, g), c[e], sc[e]);
     }
     const int tb = p * 16 + 4 * jq;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       sc[e] = (sc[e] + dpp_ror8(sc[e])) * down;
-      if (tb + e >= L) sc[e] = -INFINITY;
+      if (masked && tb + e >= L) sc[e] = -INFINITY;
     }
     float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     cm = fmaxf(cm, xor_shfl(cm, 16));
     cm = fmaxf(cm, xor_shfl(cm, 32));
-    if (cm > m_run) {
-      const float f = exp2f(m_run - cm);
+    if (__any(cm > m_run)) {
+      const float mn = fmaxf(m_run, cm);
+      const float f = __builtin_amdgcn_exp2f(m_run - mn);  // 2^-inf = 0
       l_run *= f;
 #pragma unroll
       for (int t = 0; t < 2 * G; t++) acc[t] *= f;
-      m_run = cm;
+      m_run = mn;
     }
     float pr[4];
 #pragma unroll
-    for (int e = 0; e < 4; e++) pr[e] = exp2f(sc[e] - m_run);
+    for (int e = 0; e < 4; e++) pr[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
 #pragma unroll
-    for (int g = 0; g < G; g++) {
-      f16x4 P;
+    for (int i = 0; i < 2 * G; i += 4) {
+      const u32x4 y = *reinterpret_cast<const u32x4*>(&sw[8 * G + 2 * G * jq + i]);
+      vst[i] = y[0]; vst[i + 1] = y[1]; vst[i + 2] = y[2]; vst[i + 3] = y[3];
+    }
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
-        const int e = (k >> 1) | ((k & 1) << 1);  // k-slot order: tokens 0, 2, 1, 3
-        const float x = (tb + e < L) ? pr[e] * (float)vs[e * G + g] : 0.0f;
-        const f16 hi = (f16)x;
-        P[k] = (hr < 8) ? hi : (f16)(x - (float)hi);
+    for (int g = 0; g < G; g++) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        x[e] = __builtin_fmaf(pr[e], vsc(e, g), 0.0f);  // one v_fma_mix with the fp16 scale
+        if (masked && tb + e >= L) x[e] = 0.0f;
       }
-      const uint32_t w = vw[g];
-      const f16x2 e0 = nib_p0p4(w), e1 = nib_p0p4(w >> 8);
-      const f16x2 o0 = nib_p1p5(w), o1 = nib_p1p5(w >> 8);
-      const f16x4 Ae = {e0[0], e0[1], e1[0], e1[1]};
-      const f16x4 Ao = {o0[0], o0[1], o1[0], o1[1]};
+      // k-slot order of tokens: 0 2 1 3
+      const f16x2 h02 = {(f16)x[0], (f16)x[2]};
+      const f16x2 h13 = {(f16)x[1], (f16)x[3]};
+      const f16x2 l02 = {(f16)(x[0] - lofac * (float)h02[0]), (f16)(x[2] - lofac * (float)h02[1])};
+      const f16x2 l13 = {(f16)(x[1] - lofac * (float)h13[0]), (f16)(x[3] - lofac * (float)h13[1])};
+      const f16x4 P = {l02[0], l02[1], l13[0], l13[1]};
+      f16x4 Ae, Ao;
+      unpack_v(vw[g], m0, m1, mg, Ae, Ao);
       acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ae, P, acc[2 * g], 0, 0, 0);
       acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ao, P, acc[2 * g + 1], 0, 0, 0);
     }
+  };
+
+  int it = 0;
+#pragma unroll 1
+  for (int p = p0 + wv; p < p1; p += NW, it++) {
+    const int pf = p + (C::NSLOT - 1) * NW;
+    if (pf < p1) stage_page<D>(page_base(bt, pf, hbase, pstride), ring[wv][(it + C::NSLOT - 1) % C::NSLOT], lane);
+    const int younger = min(C::NSLOT - 1, (p1 - 1 - p) / NW);
+    wait_pages_in_flight<C::NDMA>(younger);
+    page(ring[wv][it % C::NSLOT], p, true);
   }
 
-  // ---- epilogue: per-wave results, then merge the waves of this workgroup ------------------
+  // ---- epilogue: merge the waves of this workgroup -----------------------------------------
   l_run += xor_shfl(l_run, 16);
   l_run += xor_shfl(l_run, 32);
 #pragma unroll
   for (int t = 0; t < 2 * G; t++)
 #pragma unroll
     for (int i = 0; i < 4; i++) acc[t][i] += dpp_ror8(acc[t][i]);
+  __syncthreads();  // every wave is done with its ring: reuse it as the merge area
   if (hr < 8) {
 #pragma unroll
-    for (int g = 0; g < G; g++)
-#pragma unroll
-      for (int par = 0; par < 2; par++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) mo[wv][hr][32 * g + 8 * jq + 2 * i + par] = acc[2 * g + par][i];
+    for (int g = 0; g < G; g++) {
+      // dims 32g + 8jq + 0..7: even dims from acc[2g], odd from acc[2g+1]
+      float* dst = &mo[wv][hr][32 * g + 8 * jq];
+      const f32x4 lo4 = {acc[2 * g][0], acc[2 * g + 1][0], acc[2 * g][1], acc[2 * g + 1][1]};
+      const f32x4 hi4 = {acc[2 * g][2], acc[2 * g + 1][2], acc[2 * g][3], acc[2 * g + 1][3]};
+      *reinterpret_cast<f32x4*>(dst) = lo4;
+      *reinterpret_cast<f32x4*>(dst + 4) = hi4;
+    }
     if (jq == 0) {
       mml[wv][hr][0] = m_run;
       mml[wv][hr][1] = l_run;
     }
   }
   __syncthreads();
+  if (tid < r) {  // per head: wave weights 2^(m_w - M) (into mml[w][hd][0]) and the sum l
+    const int hd = tid;
+    float M = -INFINITY;
+    for (int w = 0; w < NW; w++) M = fmaxf(M, mml[w][hd][0]);
+    float l = 0.0f;
+    for (int w = 0; w < NW; w++) {
+      const float f = (mml[w][hd][0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mml[w][hd][0] - M);
+      l += f * mml[w][hd][1];
+      mml[w][hd][0] = f;
+    }
+    red[hd] = M;
+    wsh[hd][0] = l;
+  }
+  __syncthreads();
   const int S = a.splits;
+  const int64_t prow = ((int64_t)u * S + s) * r;  // partial rows of this (unit, split)
   for (int i = tid; i < r * D; i += NT) {
     const int hd = i / D, d = i % D;
-    float M = -INFINITY;
+    float o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; w++) M = fmaxf(M, mml[w][hd][0]);
-    float o = 0.0f, l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; w++) {
-      const float mw = mml[w][hd][0];
-      if (mw != -INFINITY) {
-        const float f = exp2f(mw - M);
-        o += f * mo[w][hd][d];
-        l += f * mml[w][hd][1];
+    for (int w = 0; w < NW; w++) o += mml[w][hd][0] * mo[w][hd][d];
+    if (ns == 1) {
+      qs[hd * D + d] = o / wsh[hd][0];
+    } else {
+      __hip_atomic_store(&a.part_o[(prow + hd) * D + d], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0) {
+        __hip_atomic_store(&a.part_ml[2 * (prow + hd)], red[hd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.part_ml[2 * (prow + hd) + 1], wsh[hd][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    const int64_t row = ((int64_t)b * a.Hq + (int64_t)h * r + hd) * S + s;
-    a.part_o[row * D + d] = o;
-    if (d == 0) {
-      a.part_ml[2 * row] = M;
-      a.part_ml[2 * row + 1] = l;
-    }
   }
-}
-
-}  // namespace
-
-namespace {
-// Pass 2 (also used by the dense baseline with unrotate = false).
-template <int D, bool UNROTATE>
-__global__ __launch_bounds__(64) void decode_pass2(LaunchDecode a) {
-  constexpr int PL = D / 64;
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int L = a.context_lens[b];
-  const int npages = (L + 15) >> 4;
-  const int ns = (npages + a.pages_per_split - 1) / a.pages_per_split;
-  const int64_t row0 = ((int64_t)b * a.Hq + hq) * a.splits;
-  __shared__ float buf[D];
-  float M = -INFINITY;
-  for (int s = 0; s < ns; s++) M = fmaxf(M, a.part_ml[2 * (row0 + s)]);
-  float lsum = 0.0f, v[PL];
-#pragma unroll
-  for (int k = 0; k < PL; k++) v[k] = 0.0f;
-  for (int s = 0; s < ns; s++) {
-    const float m = a.part_ml[2 * (row0 + s)];
-    if (m == -INFINITY) continue;
-    const float f = exp2f(m - M);
-    lsum += f * a.part_ml[2 * (row0 + s) + 1];
-#pragma unroll
-    for (int k = 0; k < PL; k++) v[k] += f * a.part_o[(row0 + s) * D + lane + 64 * k];
-  }
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-#pragma unroll
-  for (int k = 0; k < PL; k++) buf[lane + 64 * k] = v[k] * inv;
-  if constexpr (UNROTATE) {
-    for (int st = 1; st < D; st <<= 1) {
-      __syncthreads();
-      for (int pi = lane; pi < D / 2; pi += 64) {
-        const int lo = (pi / st) * 2 * st + (pi % st), hi = lo + st;
-        const float x0 = buf[lo], x1 = buf[hi];
-        buf[lo] = x0 + x1;
-        buf[hi] = x0 - x1;
-      }
+  if (ns > 1) {
+    // Publish this split without a cache write-back: the partials were stored coherently at
+    // device scope (sc1), vmcnt(0) waits for them, then the arrival counter is bumped.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      last_flag = (__hip_atomic_fetch_add(&a.counters[u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns - 1);
+    __syncthreads();
+    if (!last_flag) return;
+    // the last workgroup of unit u merges every split (coherent sc1 loads)
+    const int64_t row0 = (int64_t)u * S * r;
+    // descriptor over this unit's partials only (<= TQ_MAX_SPLITS * 8 * D floats)
+    __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, (short)0, S * r * D * 4, 0x00020000);
+    for (int i = tid; i < ns * r; i += NT) {  // (m, l) of every split and head
+      const int t = i / r, hd = i % r;
+      wsh[hd][t] = __hip_atomic_load(&a.part_ml[2 * (row0 + (int64_t)t * r + hd)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lsh[hd][t] = __hip_atomic_load(&a.part_ml[2 * (row0 + (int64_t)t * r + hd) + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    const float rho = tq_rho(D);
+    for (int hd = wv; hd < r; hd += NW) {  // one wave per head: weights 2^(m_s - M) / L
+      float M = -INFINITY;
+      for (int t = lane; t < ns; t += 64) M = fmaxf(M, wsh[hd][t]);
 #pragma unroll
-    for (int k = 0; k < PL; k++) {
-      const int d = lane + 64 * k;
-      float x = buf[d] * rho;
-      if ((a.sign_bits[d >> 5] >> (d & 31)) & 1u) x = -x;
-      buf[d] = x;
+      for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+      float lsum = 0.0f;
+      for (int t = lane; t < ns; t += 64) {
+        const float m = wsh[hd][t];
+        const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+        wsh[hd][t] = f;
+        lsum += f * lsh[hd][t];
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o, 64);
+      const float inv = 1.0f / lsum;
+      for (int t = lane; t < ns; t += 64) wsh[hd][t] *= inv;
+    }
+    __syncthreads();
+    // weighted sum over splits: thread = (split group, head, 4 dims); 16-byte sc1 loads
+    constexpr int D4 = D / 4;
+    const int ngrp = max(1, NT / (r * D4));
+    float* accm = &mo[0][0][0];  // [ngrp][r][D] partial sums (16 * NT bytes)
+    for (int i = tid; i < ngrp * r * D4; i += NT) {
+      const int grp = i / (r * D4), hd = (i / D4) % r, d4 = i % D4;
+      f32x4 o4 = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int t = grp; t < ns; t += ngrp) {
+        const int off = ((t * r + hd) * D + 4 * d4) * 4;
+        const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 16));
+        o4 += wsh[hd][t] * v;
+      }
+      *reinterpret_cast<f32x4*>(&accm[(grp * r + hd) * D + 4 * d4]) = o4;
+    }
+    __syncthreads();
+    for (int i = tid; i < r * D; i += NT) {
+      float o = 0.0f;
+      for (int g2 = 0; g2 < ngrp; g2++) o += accm[g2 * r * D + i];
+      qs[i] = o;
+    }
+    if (tid == 0) __hip_atomic_store(&a.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // ---- back to the original basis: fp32 butterfly, times rho, times sigma --------------------
+  for (int st = 1; st < D; st <<= 1) {
+    __syncthreads();
+    for (int pi = tid; pi < r * (D / 2); pi += NT) {
+      const int hd = pi / (D / 2), k = pi % (D / 2);
+      const int lo = (k / st) * 2 * st + (k % st), hi = lo + st;
+      const float x0 = qs[hd * D + lo], x1 = qs[hd * D + hi];
+      qs[hd * D + lo] = x0 + x1;
+      qs[hd * D + hi] = x0 - x1;
     }
   }
   __syncthreads();
-  float* o = a.out + ((int64_t)b * a.Hq + hq) * D;
-#pragma unroll
-  for (int k = 0; k < PL; k++) o[lane + 64 * k] = buf[lane + 64 * k];
-}
-}  // namespace
-
-namespace {
-
-// Dense fp16 decode attention, the "attend" half of the dequantize-then-attend baseline
-// [Open-TQ-Metal, arXiv abstract]. K, V fp16 [B][Hkv][max_ctx][D] in the original basis;
-// q is used unrotated. Plain VALU fp32 arithmetic on 64-token tiles staged in LDS; the
-// partial (o', m, l) format is that of the compressed pass 1, merged by pass 2.
-template <int D, typename TQ>
-__global__ __launch_bounds__(256) void dense_pass1(LaunchDecode a) {
-  constexpr int TT = 64, PD = D + 8, DPT = D / 32;
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int r = a.Hq / a.Hkv;
-  const int L = a.context_lens[b];
-  const int npages = (L + 15) >> 4;
-  const int p0 = s * a.pages_per_split;
-  if (p0 >= npages) return;
-  const int t0 = p0 * 16, t1 = min(min(p0 + a.pages_per_split, npages) * 16, L);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  __shared__ float qf[8][D];
-  __shared__ f16 kt[TT][PD];
-  __shared__ f16 vt[TT][PD];
-  __shared__ float pt[8][TT];
-  __shared__ float mrow[8], lrow[8], frow[8];
-
-  const TQ* qb = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
-  const float qmul = a.attn_scale * TQ_LOG2E;
-  for (int i = tid; i < 8 * D; i += 256) {
-    const int hd = i / D, d = i % D;
-    qf[hd][d] = hd < r ? widen(qb[hd * D + d]) * qmul : 0.0f;
-  }
-  if (tid < 8) { mrow[tid] = -INFINITY; lrow[tid] = 0.0f; frow[tid] = 1.0f; }
-  const f16* kb = static_cast<const f16*>(static_cast<const void*>(a.pool)) +
-                  ((int64_t)b * a.Hkv + h) * (int64_t)a.max_ctx * D;
-  const f16* vb = static_cast<const f16*>(a.dense_v) + ((int64_t)b * a.Hkv + h) * (int64_t)a.max_ctx * D;
-  const int phd = tid >> 5, pd0 = tid & 31;   // PV mapping: head phd, dims pd0 + 32 k
-  float o[DPT];
-#pragma unroll
-  for (int k = 0; k < DPT; k++) o[k] = 0.0f;
-
-  for (int t = t0; t < t1; t += TT) {
-    const int n = min(TT, t1 - t);
-    __syncthreads();
-    for (int i = tid; i < TT * (D / 8); i += 256) {
-      const int row = i / (D / 8), c8 = i % (D / 8);
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (row < n) {
-        kv = reinterpret_cast<const u32x4*>(kb + (int64_t)(t + row) * D)[c8];
-        vv = reinterpret_cast<const u32x4*>(vb + (int64_t)(t + row) * D)[c8];
-      }
-      *reinterpret_cast<u32x4*>(&kt[row][8 * c8]) = kv;
-      *reinterpret_cast<u32x4*>(&vt[row][8 * c8]) = vv;
-    }
-    __syncthreads();
-    for (int hd = wv; hd < r; hd += 4) {
-      float sc = -INFINITY;
-      if (lane < n) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int d = 0; d < D; d++) acc += qf[hd][d] * (float)kt[lane][d];
-        sc = acc;
-      }
-      float cm = sc;
-#pragma unroll
-      for (int o2 = 32; o2 >= 1; o2 >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o2, 64));
-      const float m_old = mrow[hd];
-      const float m_new = fmaxf(m_old, cm);
-      const float p = exp2f(sc - m_new);
-      float ps = p;
-#pragma unroll
-      for (int o2 = 32; o2 >= 1; o2 >>= 1) ps += __shfl_xor(ps, o2, 64);
-      pt[hd][lane] = p;
-      if (lane == 0) {
-        const float f = exp2f(m_old - m_new);
-        frow[hd] = f;
-        lrow[hd] = lrow[hd] * f + ps;
-        mrow[hd] = m_new;
-      }
-    }
-    __syncthreads();
-    if (phd < r) {
-      const float f = frow[phd];
-#pragma unroll
-      for (int k = 0; k < DPT; k++) o[k] *= f;
-      for (int tt = 0; tt < n; tt++) {
-        const float p = pt[phd][tt];
-#pragma unroll
-        for (int k = 0; k < DPT; k++) o[k] += p * (float)vt[tt][pd0 + 32 * k];
-      }
-    }
-  }
-  __syncthreads();
-  if (phd < r) {
-    const int64_t row = ((int64_t)b * a.Hq + (int64_t)h * r + phd) * a.splits + s;
-#pragma unroll
-    for (int k = 0; k < DPT; k++) a.part_o[row * D + pd0 + 32 * k] = o[k];
-    if (pd0 == 0) {
-      a.part_ml[2 * row] = mrow[phd];
-      a.part_ml[2 * row + 1] = lrow[phd];
-    }
+  for (int i = tid; i < r * D; i += NT) {
+    const int d = i % D;
+    const float x = qs[i] * rho;
+    outp[i] = ((a.sign_bits[d >> 5] >> (d & 31)) & 1u) ? -x : x;
   }
 }
 
-template <int D, typename TQ>
-hipError_t launch_dense_dq(const LaunchDecode& a, hipStream_t st) {
-  hipLaunchKernelGGL((dense_pass1<D, TQ>), dim3(a.splits, a.Hkv, a.B), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_pass2<D, false>), dim3(a.Hq, a.B), dim3(64), 0, st, a);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_dense_d(const LaunchDecode& a, hipStream_t st) {
-  switch (a.q_dtype) {
-    case TQ_F32: return launch_dense_dq<D, float>(a, st);
-    case TQ_BF16: return launch_dense_dq<D, uint16_t>(a, st);
-    default: return launch_dense_dq<D, f16>(a, st);
-  }
-}
-
-template <int D, typename TQ>
+template <int D, typename TQ, int NW>
 hipError_t launch_dq(const LaunchDecode& a, hipStream_t st) {
-  dim3 g1(a.splits, a.Hkv, a.B), b1(64 * TQ_DECODE_WAVES);
+  const int U = a.B * a.Hkv;
+  const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * a.splits);
   if (a.k_codec == TQ_CODEC_LLOYDMAX)
-    hipLaunchKernelGGL((decode_pass1<D, TQ, TQ_CODEC_LLOYDMAX>), g1, b1, 0, st, a);
+    hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_LLOYDMAX, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_pass1<D, TQ, TQ_CODEC_ABSMAX>), g1, b1, 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_pass2<D, true>), dim3(a.Hq, a.B), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_ABSMAX, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const LaunchDecode& a, hipStream_t st) {
+  constexpr int NW = tq_decode_waves(D);
   switch (a.q_dtype) {
-    case TQ_F32: return launch_dq<D, float>(a, st);
-    case TQ_BF16: return launch_dq<D, uint16_t>(a, st);
-    default: return launch_dq<D, f16>(a, st);
+    case TQ_F32: return launch_dq<D, float, NW>(a, st);
+    case TQ_BF16: return launch_dq<D, uint16_t, NW>(a, st);
+    default: return launch_dq<D, f16, NW>(a, st);
   }
 }
 
@@ -460,13 +535,5 @@ hipError_t tq_launch_decode(const LaunchDecode& a, hipStream_t st) {
     case 64: return launch_d<64>(a, st);
     case 128: return launch_d<128>(a, st);
     default: return launch_d<256>(a, st);
-  }
-}
-
-hipError_t tq_launch_dense_decode(const LaunchDecode& a, hipStream_t st) {
-  switch (a.D) {
-    case 64: return launch_dense_d<64>(a, st);
-    case 128: return launch_dense_d<128>(a, st);
-    default: return launch_dense_d<256>(a, st);
   }
 }

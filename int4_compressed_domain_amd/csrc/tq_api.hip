@@ -44,33 +44,53 @@ int num_cus() {
   return n;
 }
 
-// Context split: enough (sequence, kv head, split) workgroups to give every compute unit
-// about three 4-wave workgroups, each split holding at least one page per wave.
+// Context split of the fused decode: about one 16-wave workgroup (two 8-wave ones at
+// D = 256) per compute unit in total, at least one page per wave, at most TQ_MAX_SPLITS.
 struct Split { int splits, pages_per_split; };
 
-Split choose_split(int B, int Hkv, int max_ctx, int requested) {
-  const int pages = (max_ctx + 15) / 16;
+Split make_split(int pages, int S) {
   Split s{1, pages > 0 ? pages : 1};
   if (pages == 0) return s;
-  int S;
-  if (requested > 0) {
-    S = requested < pages ? requested : pages;
-  } else {
-    const int64_t units = (int64_t)B * Hkv;
-    const int64_t target = 3LL * num_cus();
-    int64_t want = (target + units - 1) / units;
-    const int64_t cap = (pages + TQ_DECODE_WAVES - 1) / TQ_DECODE_WAVES;
-    if (want > cap) want = cap;
-    if (want < 1) want = 1;
-    S = (int)want;
-  }
+  if (S > pages) S = pages;
+  if (S < 1) S = 1;
   s.pages_per_split = (pages + S - 1) / S;
   s.splits = (pages + s.pages_per_split - 1) / s.pages_per_split;
   return s;
 }
 
-size_t workspace_bytes(int B, int Hq, int D, int splits) {
+Split choose_split(int B, int Hkv, int D, int max_ctx, int requested) {
+  const int pages = (max_ctx + 15) / 16;
+  if (requested > 0) return make_split(pages, requested < TQ_MAX_SPLITS ? requested : TQ_MAX_SPLITS);
+  const int nw = tq_decode_waves(D);
+  const int64_t units = (int64_t)B * Hkv;
+  const int64_t target = (int64_t)num_cus() * (D >= 256 ? 2 : 1);
+  int64_t want = (target + units - 1) / units;
+  const int64_t cap = (pages + nw - 1) / nw;
+  if (want > cap) want = cap;
+  if (want > TQ_MAX_SPLITS) want = TQ_MAX_SPLITS;
+  return make_split(pages, (int)want);
+}
+
+// The dense baseline uses 4-wave workgroups, about three per compute unit.
+Split choose_split_dense(int B, int Hkv, int max_ctx, int requested) {
+  const int pages = (max_ctx + 15) / 16;
+  if (requested > 0) return make_split(pages, requested);
+  const int64_t units = (int64_t)B * Hkv;
+  int64_t want = (3LL * num_cus() + units - 1) / units;
+  const int64_t cap = (pages + TQ_DECODE_WAVES - 1) / TQ_DECODE_WAVES;
+  if (want > cap) want = cap;
+  return make_split(pages, (int)want);
+}
+
+size_t partial_bytes(int B, int Hq, int D, int splits) {
   return (size_t)B * Hq * splits * ((size_t)D + 2) * sizeof(float);
+}
+
+size_t workspace_bytes(const tq_layout* L, int B, int max_ctx, int requested) {
+  const Split f = choose_split(B, L->num_kv_heads, L->head_dim, max_ctx, requested);
+  const Split d = choose_split_dense(B, L->num_kv_heads, max_ctx, requested);
+  const int S = f.splits > d.splits ? f.splits : d.splits;
+  return TQ_DECODE_COUNTER_BYTES + partial_bytes(B, L->num_q_heads, L->head_dim, S);
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EDEVICE; }
@@ -82,7 +102,7 @@ int check_decode_common(const tq_layout* L, const void* q, int q_dtype, int batc
   if (!valid_dtype(q_dtype)) return TQ_EINVAL;
   if (!isfinite(attn_scale)) return TQ_EINVAL;
   if (batch > 0 && (!q || !context_lens || !out)) return TQ_EINVAL;
-  if (batch > 65535) return TQ_EUNSUPPORTED;
+  if ((int64_t)batch * L->num_kv_heads > TQ_MAX_UNITS) return TQ_EUNSUPPORTED;
   (void)L;
   return TQ_OK;
 }
@@ -123,8 +143,7 @@ int tq_kv_append(const tq_layout* L, void* pool, const void* k, const void* v, i
 size_t tq_decode_workspace_size(const tq_layout* L, int32_t batch, int32_t max_context_len,
                                 int32_t num_splits) {
   if (check_layout(L, false) != TQ_OK || batch < 0 || max_context_len < 0 || num_splits < 0) return 0;
-  Split s = choose_split(batch, L->num_kv_heads, max_context_len, num_splits);
-  return workspace_bytes(batch, L->num_q_heads, L->head_dim, s.splits);
+  return workspace_bytes(L, batch, max_context_len, num_splits);
 }
 
 int tq_decode_attn(const tq_layout* L, const void* pool, const void* q, int32_t q_dtype,
@@ -140,12 +159,12 @@ int tq_decode_attn(const tq_layout* L, const void* pool, const void* q, int32_t 
   if (max_pages_per_seq < 0 || (int64_t)max_context_len > 16LL * max_pages_per_seq) return TQ_EINVAL;
   if (batch == 0) return TQ_OK;
   if (!pool || !block_table) return TQ_EINVAL;
-  Split s = choose_split(batch, L->num_kv_heads, max_context_len, num_splits);
-  const size_t need = workspace_bytes(batch, L->num_q_heads, L->head_dim, s.splits);
-  if (workspace_bytes_ < need) return TQ_ENOSPC;
+  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, max_context_len, num_splits);
+  if (workspace_bytes_ < workspace_bytes(L, batch, max_context_len, num_splits)) return TQ_ENOSPC;
   if (!workspace) return TQ_EINVAL;
-  float* ws = static_cast<float*>(workspace);
+  float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + TQ_DECODE_COUNTER_BYTES);
   LaunchDecode a{};
+  a.counters = static_cast<int*>(workspace);
   a.pool = static_cast<const uint8_t*>(pool);
   a.q = q;
   a.block_table = block_table;
@@ -191,11 +210,10 @@ int tq_dense_decode_attn(const tq_layout* L, const void* k, const void* v, const
   if (rc != TQ_OK) return rc;
   if (batch == 0) return TQ_OK;
   if (!k || !v) return TQ_EINVAL;
-  Split s = choose_split(batch, L->num_kv_heads, max_context_len, num_splits);
-  const size_t need = workspace_bytes(batch, L->num_q_heads, L->head_dim, s.splits);
-  if (workspace_bytes_ < need) return TQ_ENOSPC;
+  Split s = choose_split_dense(batch, L->num_kv_heads, max_context_len, num_splits);
+  if (workspace_bytes_ < workspace_bytes(L, batch, max_context_len, num_splits)) return TQ_ENOSPC;
   if (!workspace) return TQ_EINVAL;
-  float* ws = static_cast<float*>(workspace);
+  float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + TQ_DECODE_COUNTER_BYTES);
   LaunchDecode a{};
   a.pool = static_cast<const uint8_t*>(k);
   a.dense_v = v;

@@ -76,6 +76,14 @@ __device__ __forceinline__ float dpp_ror8(float x) {
 
 __device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// (a & m) | o in one VALU instruction. gfx9 VOP3 encodings take at most one literal or
+// SGPR, so the two constants are passed in VGPRs (the caller keeps them in registers).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
 // ---- nibble -> fp16 operand unpack ----------------------------------------------------
 // fp16 0x6400 | n is the exact value 1024 + n for n < 1024; 0x6400 | (n << 4) is
 // 1024 + 16 n. Subtracting (or scaling) these back is exact in fp16.

@@ -22,8 +22,9 @@ struct LaunchDecode {
   const int32_t* context_lens;
   const uint32_t* sign_bits;
   float* out;
-  float* part_o;             // [B][Hq][S][D]
+  float* part_o;             // [B][Hq][S][D] (= [unit][split][r][D])
   float* part_ml;            // [B][Hq][S][2]
+  int* counters;             // per unit (b * Hkv + h) arrival counters, zero between calls
   int D, Hq, Hkv, B, max_pages, max_ctx, q_dtype, k_codec;
   int splits, pages_per_split;
   float attn_scale;
@@ -44,5 +45,9 @@ struct LaunchDequant {
 };
 hipError_t tq_launch_dequant(const LaunchDequant& a, hipStream_t st);
 
-// Waves per pass-1 workgroup; each workgroup owns one (sequence, kv head, split).
-constexpr int TQ_DECODE_WAVES = 4;
+// Wavefronts per fused-decode workgroup; each workgroup owns one (sequence, kv head,
+// context split). 16 waves fill a CU when the kernel fits in 128 registers per lane.
+constexpr int tq_decode_waves(int D) { return D >= 256 ? 8 : 16; }
+constexpr int TQ_DECODE_WAVES = 4;   // dense baseline workgroups
+constexpr int TQ_MAX_SPLITS = 128;   // context splits per (sequence, kv head)
+constexpr int TQ_MAX_UNITS = 1 << 20;  // sequences x kv heads per call

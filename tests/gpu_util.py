@@ -104,7 +104,7 @@ class Case:
         w = self.w
         max_ctx = int(self.lens.max()) if max_ctx is None else max_ctx
         ws_bytes = tq.tq_decode_workspace_size(self.layout, w.batch, max_ctx, num_splits)
-        ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device=DEV)
+        ws = torch.zeros(max(ws_bytes, 4) // 4, dtype=torch.float32, device=DEV)
         out = torch.full((w.batch, w.q_heads, w.head_dim), float("nan"), dtype=torch.float32, device=DEV)
         tq.tq_decode_attn(self.layout, self.pool, self.q_dev, self.bt_dev, self.lens_dev, max_ctx,
                           w.attn_scale, out, ws, num_splits=num_splits)

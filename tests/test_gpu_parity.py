@@ -182,7 +182,7 @@ def test_dense_fp16_baseline():
     ko = torch.zeros((2, w.kv_heads, Lmax, w.head_dim), dtype=torch.float16, device=DEV)
     vo = torch.zeros_like(ko)
     tq.tq_dequant_ref(c.layout, c.pool, c.bt_dev, c.lens_dev, Lmax, ko, vo, to_original_basis=1)
-    ws = torch.empty(tq.tq_decode_workspace_size(c.layout, 2, Lmax, 0) // 4, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, 2, Lmax, 0) // 4, dtype=torch.float32, device=DEV)
     out = torch.zeros((2, w.q_heads, w.head_dim), dtype=torch.float32, device=DEV)
     tq.tq_dense_decode_attn(c.layout, ko, vo, c.q_dev, c.lens_dev, Lmax, w.attn_scale, out, ws)
     torch.cuda.synchronize()
@@ -226,3 +226,62 @@ def test_full_size_workloads(name):
     _say("   pool bytes equal (%d B)" % c.pool.numel())
     pairs = None if w.batch * w.q_heads <= 64 else _pairs(w, c.lens)
     _check_case(c, pairs=pairs)
+
+
+def test_workspace_reuse_across_calls():
+    """The split-arrival counters in the workspace return to zero after every call, so one
+    zero-filled workspace serves calls of any batch size and split count in sequence."""
+    w = W.WORKLOADS["llama70b_b1_128k"].scaled(context=2500, batch=3)
+    c = Case(w, seed=21)
+    c.fill()
+    ref = c.decode_oracle()
+    ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, 3, 2500, 40) // 4 + 16, dtype=torch.float32, device=DEV)
+    for it, (nb, splits) in enumerate([(3, 0), (1, 7), (3, 40), (2, 0), (3, 3), (3, 0)]):
+        out = torch.full((nb, w.q_heads, w.head_dim), float("nan"), dtype=torch.float32, device=DEV)
+        tq.tq_decode_attn(c.layout, c.pool, c.q_dev[:nb], c.bt_dev[:nb], c.lens_dev[:nb], int(c.lens[:nb].max()),
+                          w.attn_scale, out, ws, num_splits=splits)
+        torch.cuda.synchronize()
+        assert attn_err(out.cpu().numpy(), ref[:nb]).max() <= ATTN_TOL, (it, nb, splits)
+    assert int(ws[:(4 << 20) // 4].view(torch.int32).abs().sum().item()) == 0, "counters not reset"
+
+
+def test_graph_replay_matches_eager():
+    """append + decode captured in a HIP graph, replayed several times with eager work and
+    synchronizations in between; every replay must equal the eager result bit for bit."""
+    w = W.WORKLOADS["llama8b_b16_8k"].scaled(context=900, batch=4)
+    c = Case(w, seed=23, lens=[900, 899, 450, 17])
+    c.fill()
+    L = c.lens.copy()
+    ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, w.batch, int(L.max()), 0) // 4, dtype=torch.float32, device=DEV)
+    out = torch.zeros((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=DEV)
+    # the step re-appends the last token of every sequence, then decodes
+    k32, v32, kst, vst, sl = [], [], [], [], []
+    for b in range(w.batch):
+        kk, vv, ks_, vs_ = W.seq_tokens(w, b, int(L[b]), c.seed, c.scales)
+        k32.append(kk[-1:]); v32.append(vv[-1:]); kst.append(ks_[-1:]); vst.append(vs_[-1:])
+        sl.append(W.slots_for(c.bt, b, int(L[b]) - 1, int(L[b])))
+    kd, vd = to_dev(np.concatenate(kst), w.dtype), to_dev(np.concatenate(vst), w.dtype)
+    sd = torch.from_numpy(np.concatenate(sl)).to(DEV)
+
+    def step():
+        tq.tq_kv_append(c.layout, c.pool, kd, vd, sd)
+        tq.tq_decode_attn(c.layout, c.pool, c.q_dev, c.bt_dev, c.lens_dev, int(L.max()), w.attn_scale, out, ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert attn_err(eager.cpu().numpy(), c.decode_oracle()).max() <= ATTN_TOL
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), "replay %d differs" % rep
+        step()                      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
