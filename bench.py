@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--min-pool-bytes", type=float, default=1.0 * 2 ** 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true", help="skip the fp16 GPU baseline")
+    ap.add_argument("--profile", type=int, default=0,
+                    help="run this many eager steps (append + decode) and exit: for profilers")
     return ap.parse_args()
 
 
@@ -262,6 +264,13 @@ def main():
     name = args.workload or W.HEADLINE
     w = W.WORKLOADS[name]
     S = Setup(w, args, dev)
+    if args.profile:
+        for i in range(args.profile):
+            S.append(i)
+            S.decode(i)
+        torch.cuda.synchronize()
+        log("profile mode: %d eager steps done" % args.profile)
+        return
     K, ms, ev_ms, dec_mean, app_mean = time_steps(S, args.steps, args.warmup)
     value = S.alg_bytes / (ms * 1e-3) / 1e9
     achieved = S.alg_bytes / (dec_mean * 1e-6) / 1e9

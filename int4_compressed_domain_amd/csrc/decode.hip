@@ -112,17 +112,6 @@ __device__ __forceinline__ void stage_page(const uint8_t* blk, uint8_t* slot, in
     if (c * 64 + lane < 16 * C::G) dma4(r, 4 * (c * 64 + lane), 16u * D, base + 128 * C::KB + 256 * c);
 }
 
-// Block-table entry as a wave-uniform (scalar) value. A scalar load through the scalar
-// cache; the wait sits in the same statement so the result is complete when it is used.
-__device__ __forceinline__ const uint8_t* page_base(const int32_t* bt, int p, const uint8_t* hbase,
-                                                    int64_t pstride) {
-  const int pu = __builtin_amdgcn_readfirstlane(p);
-  const int32_t* ptr = bt + pu;
-  int page;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(page) : "s"(ptr) : "memory");
-  return hbase + (int64_t)page * pstride;
-}
-
 // s_waitcnt vmcnt(n) with n a multiple of the per-page DMA count: n = k * NDMA, k = pages
 // issued after the one about to be read. The compiler does not track LDS-DMA writes.
 template <int NDMA>
@@ -172,18 +161,18 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   __shared__ float wsh[8][TQ_MAX_SPLITS];      // split weights of the final merge
   __shared__ float lsh[8][TQ_MAX_SPLITS];      // split sums l of the final merge
   __shared__ int last_flag;
+  __shared__ int pid[TQ_MAX_SPLIT_PAGES];      // physical page of every page of this split
   static_assert(NW * 8 * D * 4 <= NW * C::NSLOT * C::SLOT, "merge area must fit the ring");
   float (*mo)[8][D] = reinterpret_cast<float (*)[8][D]>(&ring[0][0][0]);
 
-  // ---- start streaming the first pages before the query prologue ---------------------------
+  // ---- page ids of this split and the queries, loaded together -------------------------------
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const uint8_t* hbase = a.pool + (int64_t)h * BB;
   const int64_t pstride = (int64_t)a.Hkv * BB;
-#pragma unroll
-  for (int k = 0; k < C::NSLOT - 1; k++) {
-    const int pp = p0 + wv + k * NW;
-    if (pp < p1) stage_page<D>(page_base(bt, pp, hbase, pstride), ring[wv][k], lane);
-  }
+  for (int i = tid; i < p1 - p0; i += NT) pid[i] = bt[p0 + i];
+  auto page_ptr = [&](int p) {  // wave-uniform address of page p's block for head h
+    return hbase + (int64_t)__builtin_amdgcn_readfirstlane(pid[p - p0]) * pstride;
+  };
 
   // ---- prologue: rotate, scale and split the queries ----------------------------------------
   const TQ* qb = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
@@ -196,8 +185,15 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
     qs[i] = x;
   }
+  __syncthreads();
+  // start streaming this wave's first pages; they land while the queries are rotated
+#pragma unroll
+  for (int k = 0; k < C::NSLOT - 1; k++) {
+    const int pp = p0 + wv + k * NW;
+    if (pp < p1) stage_page<D>(page_ptr(pp), ring[wv][k], lane);
+  }
   for (int st = 1; st < D; st <<= 1) {
-    __syncthreads();
+    if (st > 1) __syncthreads();
     for (int pi = tid; pi < 4 * D; pi += NT) {
       const int hd = pi / (D / 2), k = pi % (D / 2);
       const int lo = (k / st) * 2 * st + (k % st), hi = lo + st;
@@ -323,8 +319,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       if (masked && tb + e >= L) sc[e] = -INFINITY;
     }
     float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    cm = fmaxf(cm, xor_shfl(cm, 16));
-    cm = fmaxf(cm, xor_shfl(cm, 32));
+    cm = max_xor16(cm);
+    cm = max_xor32(cm);
     if (__any(cm > m_run)) {
       const float mn = fmaxf(m_run, cm);
       const float f = __builtin_amdgcn_exp2f(m_run - mn);  // 2^-inf = 0
@@ -368,15 +364,15 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll 1
   for (int p = p0 + wv; p < p1; p += NW, it++) {
     const int pf = p + (C::NSLOT - 1) * NW;
-    if (pf < p1) stage_page<D>(page_base(bt, pf, hbase, pstride), ring[wv][(it + C::NSLOT - 1) % C::NSLOT], lane);
+    if (pf < p1) stage_page<D>(page_ptr(pf), ring[wv][(it + C::NSLOT - 1) % C::NSLOT], lane);
     const int younger = min(C::NSLOT - 1, (p1 - 1 - p) / NW);
     wait_pages_in_flight<C::NDMA>(younger);
     page(ring[wv][it % C::NSLOT], p, true);
   }
 
   // ---- epilogue: merge the waves of this workgroup -----------------------------------------
-  l_run += xor_shfl(l_run, 16);
-  l_run += xor_shfl(l_run, 32);
+  l_run = sum_xor16(l_run);
+  l_run = sum_xor32(l_run);
 #pragma unroll
   for (int t = 0; t < 2 * G; t++)
 #pragma unroll
@@ -473,10 +469,16 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     for (int i = tid; i < ngrp * r * D4; i += NT) {
       const int grp = i / (r * D4), hd = (i / D4) % r, d4 = i % D4;
       f32x4 o4 = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int t = grp; t < ns; t += ngrp) {
-        const int off = ((t * r + hd) * D + 4 * d4) * 4;
-        const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 16));
-        o4 += wsh[hd][t] * v;
+      for (int t0 = grp; t0 < ns; t0 += 8 * ngrp) {  // 8 loads in flight per thread
+        f32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          const int t = min(t0 + k * ngrp, ns - 1);
+          v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, ((t * r + hd) * D + 4 * d4) * 4, 0, 16));
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+          if (t0 + k * ngrp < ns) o4 += wsh[hd][t0 + k * ngrp] * v[k];
       }
       *reinterpret_cast<f32x4*>(&accm[(grp * r + hd) * D + 4 * d4]) = o4;
     }

@@ -60,13 +60,18 @@ Split make_split(int pages, int S) {
 
 Split choose_split(int B, int Hkv, int D, int max_ctx, int requested) {
   const int pages = (max_ctx + 15) / 16;
-  if (requested > 0) return make_split(pages, requested < TQ_MAX_SPLITS ? requested : TQ_MAX_SPLITS);
+  const int min_s = (pages + TQ_MAX_SPLIT_PAGES - 1) / TQ_MAX_SPLIT_PAGES;  // page ids fit LDS
+  if (requested > 0) {
+    int S = requested < TQ_MAX_SPLITS ? requested : TQ_MAX_SPLITS;
+    return make_split(pages, S > min_s ? S : min_s);
+  }
   const int nw = tq_decode_waves(D);
   const int64_t units = (int64_t)B * Hkv;
   const int64_t target = (int64_t)num_cus() * (D >= 256 ? 2 : 1);
   int64_t want = (target + units - 1) / units;
   const int64_t cap = (pages + nw - 1) / nw;
   if (want > cap) want = cap;
+  if (want < min_s) want = min_s;
   if (want > TQ_MAX_SPLITS) want = TQ_MAX_SPLITS;
   return make_split(pages, (int)want);
 }
@@ -157,6 +162,7 @@ int tq_decode_attn(const tq_layout* L, const void* pool, const void* q, int32_t 
                            num_splits, out);
   if (rc != TQ_OK) return rc;
   if (max_pages_per_seq < 0 || (int64_t)max_context_len > 16LL * max_pages_per_seq) return TQ_EINVAL;
+  if ((int64_t)max_context_len > 16LL * TQ_MAX_SPLITS * TQ_MAX_SPLIT_PAGES) return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
   if (!pool || !block_table) return TQ_EINVAL;
   Split s = choose_split(batch, L->num_kv_heads, L->head_dim, max_context_len, num_splits);

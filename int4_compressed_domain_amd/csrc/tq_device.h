@@ -76,6 +76,26 @@ __device__ __forceinline__ float dpp_ror8(float x) {
 
 __device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// Butterfly exchanges across 16-lane rows (lane ^ 16) and wave halves (lane ^ 32) with the
+// gfx950 permlane swaps: both outputs of a self-swap hold {x[l], x[l ^ 16|32]} in some
+// order, so their max / sum is the reduction over the pair.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // (a & m) | o in one VALU instruction. gfx9 VOP3 encodings take at most one literal or
 // SGPR, so the two constants are passed in VGPRs (the caller keeps them in registers).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {

@@ -50,4 +50,5 @@ hipError_t tq_launch_dequant(const LaunchDequant& a, hipStream_t st);
 constexpr int tq_decode_waves(int D) { return D >= 256 ? 8 : 16; }
 constexpr int TQ_DECODE_WAVES = 4;   // dense baseline workgroups
 constexpr int TQ_MAX_SPLITS = 128;   // context splits per (sequence, kv head)
+constexpr int TQ_MAX_SPLIT_PAGES = 2048;  // pages per split (their ids are staged in LDS)
 constexpr int TQ_MAX_UNITS = 1 << 20;  // sequences x kv heads per call
