@@ -41,22 +41,6 @@ __device__ __forceinline__ f16x8 unpack_k_sub(uint32_t w) {
   return __builtin_bit_cast(f16x8, r);
 }
 
-// V operand: dword = 4 tokens (bytes) of one dim pair (even dim low nibble). Returns the
-// exact signed codes of the even dim and of the odd dim, k-slot order tokens [0 2 1 3].
-__device__ __forceinline__ void unpack_v(uint32_t w, uint32_t m0, uint32_t m1, uint32_t mg,
-                                         f16x4& ev, f16x4& od) {
-  const f16x2 off0 = {(f16)1032.0f, (f16)1032.0f};
-  const f16x2 sc1 = {(f16)0.0625f, (f16)0.0625f};
-  const f16x2 off1 = {(f16)72.0f, (f16)72.0f};
-  const uint32_t w8 = w >> 8;
-  const f16x2 e02 = as_h2(and_or(w, m0, mg)) - off0;
-  const f16x2 e13 = as_h2(and_or(w8, m0, mg)) - off0;
-  const f16x2 o02 = as_h2(and_or(w, m1, mg)) * sc1 - off1;
-  const f16x2 o13 = as_h2(and_or(w8, m1, mg)) * sc1 - off1;
-  ev = f16x4{e02[0], e02[1], e13[0], e13[1]};
-  od = f16x4{o02[0], o02[1], o13[0], o13[1]};
-}
-
 template <int D>
 struct Cfg {
   static constexpr int G = D / 32;
@@ -266,18 +250,25 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       thi[i >> 2] |= (uint32_t)(lb[i] >> 8) << (8 * (i & 3));
     }
   }
-  // constants of the V unpack, kept in VGPRs for v_and_or_b32
-  uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = 0x64006400u;
-  asm("" : "+v"(m0), "+v"(m1), "+v"(mg));
-  const float lofac = (hr >= 8) ? 1.0f : 0.0f;
+  // V operands are subnormal fp16 too: (w & 0x000F000F) = u * 2^-24 (even dims) and
+  // (w & 0x00F000F0) = 16u * 2^-24 (odd dims). The offset u = c + 8 is removed page by page
+  // by a second MFMA whose A operand is the constant -8 * 2^-24 (-128 * 2^-24 for odd dims):
+  // it adds -8 * 2^-24 * sum_t P'_t to every row, so the accumulator always holds the signed
+  // sum and never the offset-biased one.
+  u32x2 ce2 = {0x80088008u, 0x80088008u}, co2 = {0x80808080u, 0x80808080u};
+  asm("" : "+v"(ce2), "+v"(co2));  // keep the constant operands in VGPRs
+  const f16x4 ceven = __builtin_bit_cast(f16x4, ce2), codd = __builtin_bit_cast(f16x4, co2);
+  const int ltail = L & 15;
+  const int ptail = ltail ? npages - 1 : -1;  // the sequence's partial last page, if any
 
   // ---- page loop ------------------------------------------------------------------------
   f32x4 acc[2 * G];
 #pragma unroll
   for (int t = 0; t < 2 * G; t++) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  // m_run: running max of the raw scores (units of 2^(sh - 24)); nmd = -m_run * down
+  float m_run = -INFINITY, nmd = INFINITY, l_run = 0.0f;
 
-  auto page = [&](const uint8_t* slot, int p, bool masked) {
+  auto page = [&](const uint8_t* slot, int p) {
     uint32_t kw[G], vw[G];
 #pragma unroll
     for (int c = 0; c < C::NK; c++) {
@@ -297,6 +288,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     for (int i = 0; i < 2 * G; i += 4) {
       const u32x4 x = *reinterpret_cast<const u32x4*>(&sw[2 * G * jq + i]);
       kst[i] = x[0]; kst[i + 1] = x[1]; kst[i + 2] = x[2]; kst[i + 3] = x[3];
+      const u32x4 y = *reinterpret_cast<const u32x4*>(&sw[8 * G + 2 * G * jq + i]);
+      vst[i] = y[0]; vst[i + 1] = y[1]; vst[i + 2] = y[2]; vst[i + 3] = y[3];
     }
     auto ksc = [&](int e, int g) { return (float)as_h2(kst[(e * G + g) >> 1])[(e * G + g) & 1]; };
     auto vsc = [&](int e, int g) { return (float)as_h2(vst[(e * G + g) >> 1])[(e * G + g) & 1]; };
@@ -312,51 +305,47 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
       for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(ksc(e, g), c[e], sc[e]);
     }
-    const int tb = p * 16 + 4 * jq;
+    // hi + lo query parts (columns hr and hr ^ 8): both lanes end with the same full score
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
-      sc[e] = (sc[e] + dpp_ror8(sc[e])) * down;
-      if (masked && tb + e >= L) sc[e] = -INFINITY;
+    for (int e = 0; e < 4; e++) sc[e] += dpp_ror8(sc[e]);
+    if (p == ptail) {  // wave-uniform: only the partial last page is masked
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        if (4 * jq + e >= ltail) {
+          sc[e] = -INFINITY;
+#pragma unroll
+          for (int g = 0; g < G; g += 2) vst[(e * G + g) >> 1] = 0u;  // slot may hold garbage
+        }
     }
-    float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    float cm = vmax3(sc[0], sc[1], vmax(sc[2], sc[3]));
     cm = max_xor16(cm);
     cm = max_xor32(cm);
     if (__any(cm > m_run)) {
       const float mn = fmaxf(m_run, cm);
-      const float f = __builtin_amdgcn_exp2f(m_run - mn);  // 2^-inf = 0
+      const float f = __builtin_amdgcn_exp2f((m_run - mn) * down);  // 2^-inf = 0
       l_run *= f;
 #pragma unroll
       for (int t = 0; t < 2 * G; t++) acc[t] *= f;
       m_run = mn;
+      nmd = -mn * down;
     }
     float pr[4];
 #pragma unroll
-    for (int e = 0; e < 4; e++) pr[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
+    for (int e = 0; e < 4; e++) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], down, nmd));
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
 #pragma unroll
-    for (int i = 0; i < 2 * G; i += 4) {
-      const u32x4 y = *reinterpret_cast<const u32x4*>(&sw[8 * G + 2 * G * jq + i]);
-      vst[i] = y[0]; vst[i + 1] = y[1]; vst[i + 2] = y[2]; vst[i + 3] = y[3];
-    }
-#pragma unroll
     for (int g = 0; g < G; g++) {
-      float x[4];
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        x[e] = __builtin_fmaf(pr[e], vsc(e, g), 0.0f);  // one v_fma_mix with the fp16 scale
-        if (masked && tb + e >= L) x[e] = 0.0f;
-      }
-      // k-slot order of tokens: 0 2 1 3
-      const f16x2 h02 = {(f16)x[0], (f16)x[2]};
-      const f16x2 h13 = {(f16)x[1], (f16)x[3]};
-      const f16x2 l02 = {(f16)(x[0] - lofac * (float)h02[0]), (f16)(x[2] - lofac * (float)h02[1])};
-      const f16x2 l13 = {(f16)(x[1] - lofac * (float)h13[0]), (f16)(x[3] - lofac * (float)h13[1])};
-      const f16x4 P = {l02[0], l02[1], l13[0], l13[1]};
-      f16x4 Ae, Ao;
-      unpack_v(vw[g], m0, m1, mg, Ae, Ao);
+      // P' = p * s_V rounded once to fp16, k-slot token order 0 2 1 3
+      const f16x4 P = {(f16)__builtin_fmaf(pr[0], vsc(0, g), 0.0f), (f16)__builtin_fmaf(pr[2], vsc(2, g), 0.0f),
+                       (f16)__builtin_fmaf(pr[1], vsc(1, g), 0.0f), (f16)__builtin_fmaf(pr[3], vsc(3, g), 0.0f)};
+      const uint32_t w = vw[g], w8 = w >> 8;
+      const f16x4 Ae = __builtin_bit_cast(f16x4, u32x2{w & 0x000F000Fu, w8 & 0x000F000Fu});
+      const f16x4 Ao = __builtin_bit_cast(f16x4, u32x2{w & 0x00F000F0u, w8 & 0x00F000F0u});
       acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ae, P, acc[2 * g], 0, 0, 0);
+      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16f16(ceven, P, acc[2 * g], 0, 0, 0);
       acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ao, P, acc[2 * g + 1], 0, 0, 0);
+      acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(codd, P, acc[2 * g + 1], 0, 0, 0);
     }
   };
 
@@ -367,16 +356,19 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     if (pf < p1) stage_page<D>(page_ptr(pf), ring[wv][(it + C::NSLOT - 1) % C::NSLOT], lane);
     const int younger = min(C::NSLOT - 1, (p1 - 1 - p) / NW);
     wait_pages_in_flight<C::NDMA>(younger);
-    page(ring[wv][it % C::NSLOT], p, true);
+    page(ring[wv][it % C::NSLOT], p);
   }
 
   // ---- epilogue: merge the waves of this workgroup -----------------------------------------
   l_run = sum_xor16(l_run);
   l_run = sum_xor32(l_run);
+  m_run *= down;  // to the log2 domain of the merges below
+  // back from the subnormal operand units: even dims carry 2^-24, odd dims 2^-20
 #pragma unroll
-  for (int t = 0; t < 2 * G; t++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) acc[t][i] += dpp_ror8(acc[t][i]);
+  for (int g = 0; g < G; g++) {
+    acc[2 * g] *= 16777216.0f;
+    acc[2 * g + 1] *= 1048576.0f;
+  }
   __syncthreads();  // every wave is done with its ring: reuse it as the merge area
   if (hr < 8) {
 #pragma unroll

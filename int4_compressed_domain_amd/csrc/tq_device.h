@@ -71,7 +71,20 @@ __device__ __forceinline__ f16 f16_sat(float x) {
 // ---- lane exchange -------------------------------------------------------------------
 // DPP row rotate right by 8 lanes inside each row of 16: lane i reads lane (i+8) mod 16.
 __device__ __forceinline__ float dpp_ror8(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, true));
+}
+
+// max of floats without the canonicalizing v_max x,x that fmaxf adds under IEEE mode
+// (the inputs here are never signaling NaNs).
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 __device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
@@ -81,11 +94,11 @@ __device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x,
 // order, so their max / sum is the reduction over the pair.
 __device__ __forceinline__ float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

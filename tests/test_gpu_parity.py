@@ -134,8 +134,11 @@ def test_split_count_invariance():
     c = Case(w, seed=11)
     c.fill()
     outs = [c.decode_gpu(num_splits=s) for s in (1, 2, 7, 0, 1000)]
+    # P' = p * s_V is rounded to fp16 relative to the running max at the time its page is
+    # processed, which depends on the split count: results agree to about one fp16 unit
+    # roundoff (2^-11), not bit for bit.
     for o in outs[1:]:
-        assert attn_err(o, outs[0]).max() < 1e-5
+        assert attn_err(o, outs[0]).max() < 2.0 ** -11
     ref = c.decode_oracle()
     for o in outs:
         assert attn_err(o, ref).max() <= ATTN_TOL
