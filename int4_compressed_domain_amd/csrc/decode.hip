@@ -105,14 +105,88 @@ __device__ __forceinline__ void wait_pages_in_flight(int k) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Value of lane ^ st (st = 1, 2, 4, 8: inside a row of 16 lanes) by DPP, no LDS round trip.
+template <int ST>
+__device__ __forceinline__ float dpp_xor(float x, int lane) {
+  const int v = __float_as_int(x);
+  if constexpr (ST == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, true));  // quad_perm 1 0 3 2
+  else if constexpr (ST == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, true));  // quad_perm 2 3 0 1
+  else if constexpr (ST == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, true));  // row_ror 8
+  else {  // ST == 4 (row_ror n: lane i reads lane i - n mod 16): i + 4 is row_ror 12, i - 4 row_ror 4
+    const int from_up = __builtin_amdgcn_mov_dpp(v, 0x12C, 0xf, 0xf, true);
+    const int from_dn = __builtin_amdgcn_mov_dpp(v, 0x124, 0xf, 0xf, true);
+    return __int_as_float((lane & 4) ? from_dn : from_up);
+  }
+}
+
+// One butterfly stage across lanes: lane with bit st clear keeps x + partner, the other
+// partner - x (its own value is the upper element of the pair).
+template <int ST>
+__device__ __forceinline__ float bfly(float x, int lane) {
+  float y;
+  if constexpr (ST < 16) y = dpp_xor<ST>(x, lane);
+  else y = __shfl_xor(x, ST, 64);
+  return (lane & ST) ? y - x : x + y;
+}
+
+// In-wave Walsh-Hadamard butterflies: lane holds V = D/64 values, value k at dim lane + 64k.
+// Stages commute, so the in-register strides (64, 128) go first, then lane strides 1..32.
+template <int V>
+__device__ __forceinline__ void wave_fwht(float (&x)[V], int lane) {
+#pragma unroll
+  for (int st = 1; st < V; st <<= 1)
+#pragma unroll
+    for (int k = 0; k < V; k++)
+      if (!(k & st)) {
+        const float x0 = x[k], x1 = x[k + st];
+        x[k] = x0 + x1;
+        x[k + st] = x0 - x1;
+      }
+#pragma unroll
+  for (int k = 0; k < V; k++) {
+    float y = x[k];
+    y = bfly<1>(y, lane);
+    y = bfly<2>(y, lane);
+    y = bfly<4>(y, lane);
+    y = bfly<8>(y, lane);
+    y = bfly<16>(y, lane);
+    y = bfly<32>(y, lane);
+    x[k] = y;
+  }
+}
+
+// Max over the 64 lanes of a wave (rotations inside rows, then row and half swaps).
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, true)));
+  return max_xor32(max_xor16(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, true));
+  return sum_xor32(sum_xor16(x));
+}
+
+// k-slot of the score MFMA's B operand that holds dim offset e (0..7) of an 8-dim chunk
+// (inverse of kslot_dim).
+template <int KCODEC>
+__device__ __forceinline__ int dim_kslot(int e) {
+  if constexpr (KCODEC == TQ_CODEC_ABSMAX) return ((e & 3) << 1) | (e >> 2);
+  else return (e >> 1) | ((e & 1) << 2);
+}
+
 template <int D, typename TQ, int KCODEC, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   using C = Cfg<D>;
-  constexpr int G = C::G, BB = C::BB, NT = 64 * NW;
+  constexpr int G = C::G, BB = C::BB, NT = 64 * NW, V = D / 64;
   constexpr bool KSUB = (KCODEC == TQ_CODEC_ABSMAX);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar page loads
-  const int jq = lane >> 4, hr = lane & 15;
+  const int jq = lane >> 4, hr = lane & 15, hl = hr & 7;
 
   // ---- XCD-aware placement: unit u on XCD u mod 8 -----------------------------------------
   const int U = a.B * a.Hkv;
@@ -135,21 +209,20 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   if (s >= ns) return;
   const int p0 = s * pps, p1 = min(p0 + pps, npages);
 
-  // page ring (per wave) -- reused after the page loop for the per-wave partial results
+  // page ring (per wave) -- reused after the page loop as the merge area
   __shared__ __attribute__((aligned(16))) uint8_t ring[NW][C::NSLOT][C::SLOT];
-  __shared__ float qs[8 * D];                  // rotation workspace / output staging
-  __shared__ f16x8 bq[G * 64];                 // query B operands per (group, lane)
-  __shared__ float cb[G * 16];                 // -beta per (group, column)
-  __shared__ float red[NW];
+  __shared__ __attribute__((aligned(16))) f16 bqs[G][64][8];  // score B operands (lane, k-slot)
+  __shared__ float qdown[8];                   // per head: raw score units -> log2 units
   __shared__ float mml[NW][8][2];              // per-wave (m, l), then per-wave weights
+  __shared__ float hml[8][2];                  // per head: max M and sum l of the workgroup
   __shared__ float wsh[8][TQ_MAX_SPLITS];      // split weights of the final merge
-  __shared__ float lsh[8][TQ_MAX_SPLITS];      // split sums l of the final merge
   __shared__ int last_flag;
   __shared__ int pid[TQ_MAX_SPLIT_PAGES];      // physical page of every page of this split
   static_assert(NW * 8 * D * 4 <= NW * C::NSLOT * C::SLOT, "merge area must fit the ring");
+  static_assert(NW >= 8, "one wave per query head in the rotations");
   float (*mo)[8][D] = reinterpret_cast<float (*)[8][D]>(&ring[0][0][0]);
 
-  // ---- page ids of this split and the queries, loaded together -------------------------------
+  // ---- page ids of this split and this wave's query head, loaded together ------------------
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const uint8_t* hbase = a.pool + (int64_t)h * BB;
   const int64_t pstride = (int64_t)a.Hkv * BB;
@@ -157,90 +230,76 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   auto page_ptr = [&](int p) {  // wave-uniform address of page p's block for head h
     return hbase + (int64_t)__builtin_amdgcn_readfirstlane(pid[p - p0]) * pstride;
   };
-
-  // ---- prologue: rotate, scale and split the queries ----------------------------------------
   const TQ* qb = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
-  for (int i = tid; i < 8 * D; i += NT) {
-    const int hd = i / D, d = i % D;
-    float x = 0.0f;
-    if (hd < r) {
-      x = widen(qb[hd * D + d]);
-      if ((a.sign_bits[d >> 5] >> (d & 31)) & 1u) x = -x;
+  float qv[V];
+  if (wv < r) {  // wave w rotates query head w: sign flip now, butterflies below
+#pragma unroll
+    for (int k = 0; k < V; k++) {
+      const int d = lane + 64 * k;
+      const float x = widen(qb[wv * D + d]);
+      qv[k] = ((a.sign_bits[d >> 5] >> (d & 31)) & 1u) ? -x : x;
     }
-    qs[i] = x;
   }
   __syncthreads();
-  // start streaming this wave's first pages; they land while the queries are rotated
+  // start streaming this wave's first pages; they land while the queries are prepared
 #pragma unroll
   for (int k = 0; k < C::NSLOT - 1; k++) {
     const int pp = p0 + wv + k * NW;
     if (pp < p1) stage_page<D>(page_ptr(pp), ring[wv][k], lane);
   }
-  for (int st = 1; st < D; st <<= 1) {
-    if (st > 1) __syncthreads();
-    for (int pi = tid; pi < 4 * D; pi += NT) {
-      const int hd = pi / (D / 2), k = pi % (D / 2);
-      const int lo = (k / st) * 2 * st + (k % st), hi = lo + st;
-      const float x0 = qs[hd * D + lo], x1 = qs[hd * D + hi];
-      qs[hd * D + lo] = x0 + x1;
-      qs[hd * D + hi] = x0 - x1;
-    }
-  }
-  __syncthreads();
+
+  // ---- prologue: rotate, scale, power-of-two prescale per head ----------------------------
+  // Wave w (< r) holds query head w: after the butterflies and scaling it writes the fp16
+  // hi part (column w) and lo part (column w + 8) of every dim straight into the B-operand
+  // layout: lane 16j + c, k-slot s holds dim 32g + 8j + kslot_dim(s) of group g.
   const float rho = tq_rho(D), qmul = a.attn_scale * TQ_LOG2E;
-  float mx = 0.0f;
-  for (int i = tid; i < 8 * D; i += NT) {
-    const float v = (qs[i] * rho) * qmul;
-    qs[i] = v;
-    mx = fmaxf(mx, fabsf(v));
-  }
+  if (wv < r) {
+    wave_fwht<V>(qv, lane);
+    float mx = 0.0f;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  if (lane == 0) red[wv] = mx;
-  __syncthreads();
-  mx = red[0];
+    for (int k = 0; k < V; k++) {
+      qv[k] = (qv[k] * rho) * qmul;
+      mx = fmaxf(mx, fabsf(qv[k]));
+    }
+    mx = wave_max(mx);
+    int sh = 0;
+    if (mx > 0.0f) sh = min(60, max(-60, 14 - ilogbf(mx)));
+    const float up = ldexpf(1.0f, sh);
 #pragma unroll
-  for (int w = 1; w < NW; w++) mx = fmaxf(mx, red[w]);
-  int sh = 0;
-  if (mx > 0.0f) sh = min(60, max(-60, 14 - ilogbf(mx)));
-  const float up = ldexpf(1.0f, sh);
-  // scores come out in units of 2^-sh (times 2^24 for the subnormal K form)
-  const float down = ldexpf(1.0f, KSUB ? 24 - sh : -sh);
-  for (int idx = tid; idx < G * 64; idx += NT) {
-    const int g = idx >> 6, l = idx & 63, j = l >> 4, c = l & 15, hd = c & 7;
-    f16x8 v;
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const float x = (hd < r) ? qs[hd * D + 32 * g + 8 * j + kslot_dim<KCODEC>(k)] * up : 0.0f;
+    for (int k = 0; k < V; k++) {
+      const int d = lane + 64 * k, g = d >> 5, j = (d >> 3) & 3, sl = dim_kslot<KCODEC>(d & 7);
+      const float x = qv[k] * up;
       const f16 hi = (f16)x;
-      f16 part = (c < 8) ? hi : (f16)(x - (float)hi);
-      if (KSUB && (k & 2)) part = part * (f16)0.0625f;  // odd nibble positions carry 16u
-      v[k] = part;
+      f16 lo = (f16)(x - (float)hi), hs = hi;
+      if (KSUB && (sl & 2)) {  // odd nibble positions carry 16u
+        hs = hi * (f16)0.0625f;
+        lo = lo * (f16)0.0625f;
+      }
+      bqs[g][16 * j + wv][sl] = hs;
+      bqs[g][16 * j + wv + 8][sl] = lo;
     }
-    bq[idx] = v;
-  }
-  if (KSUB) {
-    // beta = 8 * 2^-24 * (sum over the group of the query part that column c holds); one
-    // lane per (group, column, 8-dim chunk), chunks summed with two lane exchanges
-    for (int idx = tid; idx < G * 64; idx += NT) {
-      const int g = idx >> 6, c = (idx >> 2) & 15, q4 = idx & 3, hd = c & 7;
-      float sum = 0.0f;
-      if (hd < r)
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const float x = qs[hd * D + 32 * g + 8 * q4 + k] * up;
-          const f16 hi = (f16)x;
-          sum += (c < 8) ? (float)hi : (float)(f16)(x - (float)hi);
-        }
-      sum += __shfl_xor(sum, 1, 64);
-      sum += __shfl_xor(sum, 2, 64);
-      if (q4 == 0) cb[g * 16 + c] = -sum * 4.76837158203125e-07f;  // 8 * 2^-24
-    }
+    // scores come out in units of 2^-sh (times 2^24 for the subnormal K form)
+    if (lane == 0) qdown[wv] = ldexpf(1.0f, KSUB ? 24 - sh : -sh);
   }
   __syncthreads();
+  const bool live = hl < r;
+  const float down = live ? qdown[hl] : 1.0f;
+  f16x8 bq[G];
   float cinit[G];
+  // beta = 8 * 2^-24 * (sum of the column's query parts over the group), from one MFMA:
+  // A = 8 * 2^-24 in every k-slot (128 * 2^-24 where the B values were divided by 16)
+  const f16x8 abeta = __builtin_bit_cast(f16x8, u32x4{0x00080008u, 0x00800080u, 0x00080008u, 0x00800080u});
 #pragma unroll
-  for (int g = 0; g < G; g++) cinit[g] = KSUB ? cb[g * 16 + hr] : 0.0f;
+  for (int g = 0; g < G; g++) {
+    bq[g] = *reinterpret_cast<const f16x8*>(&bqs[g][lane][0]);
+    if (!live) bq[g] = f16x8{};
+    if constexpr (KSUB) {
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      cinit[g] = -__builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, bq[g], z, 0, 0, 0)[0];
+    } else {
+      cinit[g] = 0.0f;
+    }
+  }
   uint32_t tlo[4] = {0, 0, 0, 0}, thi[4] = {0, 0, 0, 0};
   if constexpr (!KSUB) {
     const uint16_t lb[16] = TQ_LUT16_BITS;
@@ -265,7 +324,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   f32x4 acc[2 * G];
 #pragma unroll
   for (int t = 0; t < 2 * G; t++) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // m_run: running max of the raw scores (units of 2^(sh - 24)); nmd = -m_run * down
+  // m_run: running max of the raw scores; nmd = -m_run * down
   float m_run = -INFINITY, nmd = INFINITY, l_run = 0.0f;
 
   auto page = [&](const uint8_t* slot, int p) {
@@ -301,7 +360,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       if constexpr (KSUB) A = unpack_k_sub(kw[g]);
       else A = unpack_k_lut(kw[g], tlo, thi);
       const f32x4 ci = {cinit[g], cinit[g], cinit[g], cinit[g]};
-      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bq[g * 64 + lane], ci, 0, 0, 0);
+      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bq[g], ci, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(ksc(e, g), c[e], sc[e]);
     }
@@ -396,28 +455,45 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       l += f * mml[w][hd][1];
       mml[w][hd][0] = f;
     }
-    red[hd] = M;
-    wsh[hd][0] = l;
+    hml[hd][0] = M;
+    hml[hd][1] = l;
   }
   __syncthreads();
+  // fin: [ngf][r][D] partial sums of the result (rotated basis), summed by the rotation below
+  float* fin = &mo[0][0][0];
+  int ngf = 1;
   const int S = a.splits;
   const int64_t prow = ((int64_t)u * S + s) * r;  // partial rows of this (unit, split)
-  for (int i = tid; i < r * D; i += NT) {
-    const int hd = i / D, d = i % D;
-    float o = 0.0f;
+  if (ns == 1) {
+    float ov[(8 * D + NT - 1) / NT];
 #pragma unroll
-    for (int w = 0; w < NW; w++) o += mml[w][hd][0] * mo[w][hd][d];
-    if (ns == 1) {
-      qs[hd * D + d] = o / wsh[hd][0];
-    } else {
+    for (int j = 0; j < (8 * D + NT - 1) / NT; j++) {
+      const int i = tid + j * NT;
+      float o = 0.0f;
+      if (i < r * D) {
+        const int hd = i / D, d = i % D;
+#pragma unroll
+        for (int w = 0; w < NW; w++) o += mml[w][hd][0] * mo[w][hd][d];
+        o /= hml[hd][1];
+      }
+      ov[j] = o;
+    }
+    __syncthreads();  // fin aliases mo
+#pragma unroll
+    for (int j = 0; j < (8 * D + NT - 1) / NT; j++)
+      if (tid + j * NT < r * D) fin[tid + j * NT] = ov[j];
+  } else {
+    for (int i = tid; i < r * D; i += NT) {
+      const int hd = i / D, d = i % D;
+      float o = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; w++) o += mml[w][hd][0] * mo[w][hd][d];
       __hip_atomic_store(&a.part_o[(prow + hd) * D + d], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (d == 0) {
-        __hip_atomic_store(&a.part_ml[2 * (prow + hd)], red[hd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.part_ml[2 * (prow + hd) + 1], wsh[hd][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.part_ml[2 * (prow + hd)], hml[hd][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.part_ml[2 * (prow + hd) + 1], hml[hd][1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-  }
-  if (ns > 1) {
     // Publish this split without a cache write-back: the partials were stored coherently at
     // device scope (sc1), vmcnt(0) waits for them, then the arrival counter is bumped.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -426,43 +502,62 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       last_flag = (__hip_atomic_fetch_add(&a.counters[u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns - 1);
     __syncthreads();
     if (!last_flag) return;
-    // the last workgroup of unit u merges every split (coherent sc1 loads)
+    if (tid == 0) __hip_atomic_store(&a.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---- the last workgroup of unit u merges every split (coherent sc1 loads) ----------
+    // thread = (split group grp, head hd, 4 dims d4); split group grp takes splits
+    // grp, grp + ngrp, ...; the first 8 of them are loaded before the weights are known
     const int64_t row0 = (int64_t)u * S * r;
-    // descriptor over this unit's partials only (<= TQ_MAX_SPLITS * 8 * D floats)
     __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, (short)0, S * r * D * 4, 0x00020000);
-    for (int i = tid; i < ns * r; i += NT) {  // (m, l) of every split and head
-      const int t = i / r, hd = i % r;
-      wsh[hd][t] = __hip_atomic_load(&a.part_ml[2 * (row0 + (int64_t)t * r + hd)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      lsh[hd][t] = __hip_atomic_load(&a.part_ml[2 * (row0 + (int64_t)t * r + hd) + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    for (int hd = wv; hd < r; hd += NW) {  // one wave per head: weights 2^(m_s - M) / L
-      float M = -INFINITY;
-      for (int t = lane; t < ns; t += 64) M = fmaxf(M, wsh[hd][t]);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-      float lsum = 0.0f;
-      for (int t = lane; t < ns; t += 64) {
-        const float m = wsh[hd][t];
-        const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-        wsh[hd][t] = f;
-        lsum += f * lsh[hd][t];
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o, 64);
-      const float inv = 1.0f / lsum;
-      for (int t = lane; t < ns; t += 64) wsh[hd][t] *= inv;
-    }
-    __syncthreads();
-    // weighted sum over splits: thread = (split group, head, 4 dims); 16-byte sc1 loads
     constexpr int D4 = D / 4;
     const int ngrp = max(1, NT / (r * D4));
-    float* accm = &mo[0][0][0];  // [ngrp][r][D] partial sums (16 * NT bytes)
-    for (int i = tid; i < ngrp * r * D4; i += NT) {
-      const int grp = i / (r * D4), hd = (i / D4) % r, d4 = i % D4;
-      f32x4 o4 = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int t0 = grp; t0 < ns; t0 += 8 * ngrp) {  // 8 loads in flight per thread
-        f32x4 v[8];
+    ngf = ngrp;
+    const bool act = tid < ngrp * r * D4;
+    const int grp = tid / (r * D4), hd = (tid / D4) % r, d4 = tid % D4;
+    f32x4 v[8];
+    if (act) {
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const int t = min(grp + k * ngrp, ns - 1);
+        v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, ((t * r + hd) * D + 4 * d4) * 4, 0, 16));
+      }
+    }
+    // wave hd (< r) turns the (m, l) of every split of head hd into merge weights
+    // 2^(m_t - M) / sum_t 2^(m_t - M) l_t (lanes over splits), while the partials load
+    if (wv < r) {
+      constexpr int TPL = TQ_MAX_SPLITS / 64;  // splits per lane
+      float m[TPL], l[TPL];
+#pragma unroll
+      for (int q = 0; q < TPL; q++) {
+        const int t = lane + 64 * q;
+        m[q] = -INFINITY;
+        l[q] = 0.0f;
+        if (t < ns) {
+          m[q] = __hip_atomic_load(&a.part_ml[2 * (row0 + (int64_t)t * r + wv)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          l[q] = __hip_atomic_load(&a.part_ml[2 * (row0 + (int64_t)t * r + wv) + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      float M = m[0];
+#pragma unroll
+      for (int q = 1; q < TPL; q++) M = fmaxf(M, m[q]);
+      M = wave_max(M);
+      float lsum = 0.0f;
+#pragma unroll
+      for (int q = 0; q < TPL; q++) {
+        m[q] = (m[q] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[q] - M);
+        lsum += m[q] * l[q];
+      }
+      const float inv = 1.0f / wave_sum(lsum);
+#pragma unroll
+      for (int q = 0; q < TPL; q++)
+        if (lane + 64 * q < ns) wsh[wv][lane + 64 * q] = m[q] * inv;
+    }
+    __syncthreads();
+    f32x4 o4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (act) {
+#pragma unroll
+      for (int k = 0; k < 8; k++)
+        if (grp + k * ngrp < ns) o4 += wsh[hd][grp + k * ngrp] * v[k];
+      for (int t0 = grp + 8 * ngrp; t0 < ns; t0 += 8 * ngrp) {  // more than 8 splits per group
 #pragma unroll
         for (int k = 0; k < 8; k++) {
           const int t = min(t0 + k * ngrp, ns - 1);
@@ -472,32 +567,27 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
         for (int k = 0; k < 8; k++)
           if (t0 + k * ngrp < ns) o4 += wsh[hd][t0 + k * ngrp] * v[k];
       }
-      *reinterpret_cast<f32x4*>(&accm[(grp * r + hd) * D + 4 * d4]) = o4;
     }
-    __syncthreads();
-    for (int i = tid; i < r * D; i += NT) {
-      float o = 0.0f;
-      for (int g2 = 0; g2 < ngrp; g2++) o += accm[g2 * r * D + i];
-      qs[i] = o;
-    }
-    if (tid == 0) __hip_atomic_store(&a.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // ---- back to the original basis: fp32 butterfly, times rho, times sigma --------------------
-  for (int st = 1; st < D; st <<= 1) {
-    __syncthreads();
-    for (int pi = tid; pi < r * (D / 2); pi += NT) {
-      const int hd = pi / (D / 2), k = pi % (D / 2);
-      const int lo = (k / st) * 2 * st + (k % st), hi = lo + st;
-      const float x0 = qs[hd * D + lo], x1 = qs[hd * D + hi];
-      qs[hd * D + lo] = x0 + x1;
-      qs[hd * D + hi] = x0 - x1;
-    }
+    __syncthreads();  // fin aliases mo
+    if (act) *reinterpret_cast<f32x4*>(&fin[(grp * r + hd) * D + 4 * d4]) = o4;
   }
   __syncthreads();
-  for (int i = tid; i < r * D; i += NT) {
-    const int d = i % D;
-    const float x = qs[i] * rho;
-    outp[i] = ((a.sign_bits[d >> 5] >> (d & 31)) & 1u) ? -x : x;
+  // ---- back to the original basis: wave w takes head w (fp32 butterflies, rho, sigma) -------
+  if (wv < r) {
+    float x[V];
+#pragma unroll
+    for (int k = 0; k < V; k++) {
+      float o = 0.0f;
+      for (int g2 = 0; g2 < ngf; g2++) o += fin[(g2 * r + wv) * D + lane + 64 * k];
+      x[k] = o;
+    }
+    wave_fwht<V>(x, lane);
+#pragma unroll
+    for (int k = 0; k < V; k++) {
+      const int d = lane + 64 * k;
+      const float y = x[k] * rho;
+      outp[wv * D + d] = ((a.sign_bits[d >> 5] >> (d & 31)) & 1u) ? -y : y;
+    }
   }
 }
 
