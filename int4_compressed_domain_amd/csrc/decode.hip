@@ -51,7 +51,6 @@ struct Cfg {
   static constexpr int NSC = (16 * G + 63) / 64;      // dword DMAs for the scale region
   static constexpr int NDMA = 2 * NK + NSC;            // vector-memory ops per page
   static constexpr int SLOT = 128 * KB + 64 * G;      // LDS bytes of one staged page
-  static constexpr int NSLOT = 3;                     // ring slots per wave (2 pages in flight)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -98,11 +97,14 @@ __device__ __forceinline__ void stage_page(const uint8_t* blk, uint8_t* slot, in
 
 // s_waitcnt vmcnt(n) with n a multiple of the per-page DMA count: n = k * NDMA, k = pages
 // issued after the one about to be read. The compiler does not track LDS-DMA writes.
-template <int NDMA>
+template <int NDMA, int K>
 __device__ __forceinline__ void wait_pages_in_flight(int k) {
-  if (k >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NDMA) : "memory");
-  else if (k == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (K == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (k >= K) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K * NDMA) : "memory");
+    else wait_pages_in_flight<NDMA, K - 1>(k);
+  }
 }
 
 // Value of lane ^ st (st = 1, 2, 4, 8: inside a row of 16 lanes) by DPP, no LDS round trip.
@@ -183,6 +185,9 @@ template <int D, typename TQ, int KCODEC, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   using C = Cfg<D>;
   constexpr int G = C::G, BB = C::BB, NT = 64 * NW, V = D / 64;
+  // ring slots per wave: as many as ~144 KB of LDS holds, at most 8 (NSLOT - 1 pages in flight)
+  constexpr int NSLOT = (147456 / (NW * C::SLOT)) < 8 ? (147456 / (NW * C::SLOT)) : 8;
+  static_assert(NSLOT >= 3, "ring too small");
   constexpr bool KSUB = (KCODEC == TQ_CODEC_ABSMAX);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar page loads
@@ -210,17 +215,20 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int p0 = s * pps, p1 = min(p0 + pps, npages);
 
   // page ring (per wave) -- reused after the page loop as the merge area
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NW][C::NSLOT][C::SLOT];
-  __shared__ __attribute__((aligned(16))) f16 bqs[G][64][8];  // score B operands (lane, k-slot)
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT][NW][C::SLOT];
   __shared__ float qdown[8];                   // per head: raw score units -> log2 units
   __shared__ float mml[NW][8][2];              // per-wave (m, l), then per-wave weights
   __shared__ float hml[8][2];                  // per head: max M and sum l of the workgroup
-  __shared__ float wsh[8][TQ_MAX_SPLITS];      // split weights of the final merge
   __shared__ int last_flag;
   __shared__ int pid[TQ_MAX_SPLIT_PAGES];      // physical page of every page of this split
-  static_assert(NW * 8 * D * 4 <= NW * C::NSLOT * C::SLOT, "merge area must fit the ring");
   static_assert(NW >= 8, "one wave per query head in the rotations");
+  // Aliases of the ring: the query operands live in the last slot of every wave until the
+  // page loop starts; after the loop, the per-wave results and the final-merge weights.
+  static_assert(G * 64 * 8 * 2 <= NW * C::SLOT, "query operands must fit one ring slot row");
+  static_assert(NW * 8 * D * 4 + 8 * TQ_MAX_SPLITS * 4 <= NSLOT * NW * C::SLOT, "merge area must fit the ring");
+  f16 (*bqs)[64][8] = reinterpret_cast<f16 (*)[64][8]>(&ring[NSLOT - 1][0][0]);
   float (*mo)[8][D] = reinterpret_cast<float (*)[8][D]>(&ring[0][0][0]);
+  float (*wsh)[TQ_MAX_SPLITS] = reinterpret_cast<float (*)[TQ_MAX_SPLITS]>(&ring[0][0][0] + NW * 8 * D * 4);
 
   // ---- page ids of this split and this wave's query head, loaded together ------------------
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
@@ -242,11 +250,15 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   }
   __syncthreads();
   // start streaming this wave's first pages; they land while the queries are prepared
+  // (the rotating waves issue theirs after the rotation, which stays off the busy queue)
+  auto stage_first = [&]() {
 #pragma unroll
-  for (int k = 0; k < C::NSLOT - 1; k++) {
-    const int pp = p0 + wv + k * NW;
-    if (pp < p1) stage_page<D>(page_ptr(pp), ring[wv][k], lane);
-  }
+    for (int k = 0; k < NSLOT - 2; k++) {
+      const int pp = p0 + wv + k * NW;
+      if (pp < p1) stage_page<D>(page_ptr(pp), ring[k][wv], lane);
+    }
+  };
+  if (wv >= r) stage_first();
 
   // ---- prologue: rotate, scale, power-of-two prescale per head ----------------------------
   // Wave w (< r) holds query head w: after the butterflies and scaling it writes the fp16
@@ -280,6 +292,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
     // scores come out in units of 2^-sh (times 2^24 for the subnormal K form)
     if (lane == 0) qdown[wv] = ldexpf(1.0f, KSUB ? 24 - sh : -sh);
+    stage_first();
   }
   __syncthreads();
   const bool live = hl < r;
@@ -300,6 +313,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       cinit[g] = 0.0f;
     }
   }
+  __syncthreads();  // every wave holds its operands: the last ring slot is free again
   uint32_t tlo[4] = {0, 0, 0, 0}, thi[4] = {0, 0, 0, 0};
   if constexpr (!KSUB) {
     const uint16_t lb[16] = TQ_LUT16_BITS;
@@ -310,50 +324,50 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
   }
   // V operands are subnormal fp16 too: (w & 0x000F000F) = u * 2^-24 (even dims) and
-  // (w & 0x00F000F0) = 16u * 2^-24 (odd dims). The offset u = c + 8 is removed page by page
+  // (w & 0x00F000F0) = 16u * 2^-24 (odd dims). The offset u = c + 8 is removed pair by pair
   // by a second MFMA whose A operand is the constant -8 * 2^-24 (-128 * 2^-24 for odd dims):
   // it adds -8 * 2^-24 * sum_t P'_t to every row, so the accumulator always holds the signed
   // sum and never the offset-biased one.
-  u32x2 ce2 = {0x80088008u, 0x80088008u}, co2 = {0x80808080u, 0x80808080u};
-  asm("" : "+v"(ce2), "+v"(co2));  // keep the constant operands in VGPRs
-  const f16x4 ceven = __builtin_bit_cast(f16x4, ce2), codd = __builtin_bit_cast(f16x4, co2);
+  u32x4 ce4 = {0x80088008u, 0x80088008u, 0x80088008u, 0x80088008u};
+  u32x4 co4 = {0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+  asm("" : "+v"(ce4), "+v"(co4));  // keep the constant operands in VGPRs
+  const f16x8 ceven = __builtin_bit_cast(f16x8, ce4), codd = __builtin_bit_cast(f16x8, co4);
   const int ltail = L & 15;
   const int ptail = ltail ? npages - 1 : -1;  // the sequence's partial last page, if any
+  const bool hiLane = hr < 8;                 // lanes 0..7 of a row keep page A, 8..15 page B
 
-  // ---- page loop ------------------------------------------------------------------------
+  // ---- page loop: two pages per step ----------------------------------------------------
+  // Wave wv takes pages p0 + wv + NW n, n = 0, 1, ...; step i handles n = 2i (page A) and
+  // 2i + 1 (page B). Scores of both pages come from the MFMAs in every lane; then lanes with
+  // hr < 8 finish page A and lanes with hr >= 8 page B (same head hr & 7), so the softmax and
+  // P' work is not duplicated, and one K = 32 MFMA per group accumulates both pages.
   f32x4 acc[2 * G];
 #pragma unroll
   for (int t = 0; t < 2 * G; t++) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // m_run: running max of the raw scores; nmd = -m_run * down
+  // m_run: running max of the raw scores (shared by lanes hr and hr ^ 8); nmd = -m_run * down
   float m_run = -INFINITY, nmd = INFINITY, l_run = 0.0f;
+  const int npw = (p1 - p0 - wv + NW - 1) / NW;  // pages of this wave
 
-  auto page = [&](const uint8_t* slot, int p) {
-    uint32_t kw[G], vw[G];
+  auto scores = [&](const uint8_t* slot, float (&sc)[4]) {
+    uint32_t kw[G];
 #pragma unroll
     for (int c = 0; c < C::NK; c++) {
       if constexpr (C::DMAK == 16) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(slot + c * 1024 + lane * 16);
-        const u32x4 y = *reinterpret_cast<const u32x4*>(slot + 64 * C::KB + c * 1024 + lane * 16);
         kw[4 * c] = x[0]; kw[4 * c + 1] = x[1]; kw[4 * c + 2] = x[2]; kw[4 * c + 3] = x[3];
-        vw[4 * c] = y[0]; vw[4 * c + 1] = y[1]; vw[4 * c + 2] = y[2]; vw[4 * c + 3] = y[3];
       } else {
         kw[c] = *reinterpret_cast<const uint32_t*>(slot + c * 256 + lane * 4);
-        vw[c] = *reinterpret_cast<const uint32_t*>(slot + 64 * C::KB + c * 256 + lane * 4);
       }
     }
     const uint32_t* sw = reinterpret_cast<const uint32_t*>(slot + 128 * C::KB);
-    uint32_t kst[2 * G], vst[2 * G];  // fp16 pairs: tokens 4jq..4jq+3, groups 0..G-1
+    uint32_t kst[2 * G];  // fp16 pairs: tokens 4jq..4jq+3, groups 0..G-1
 #pragma unroll
     for (int i = 0; i < 2 * G; i += 4) {
       const u32x4 x = *reinterpret_cast<const u32x4*>(&sw[2 * G * jq + i]);
       kst[i] = x[0]; kst[i + 1] = x[1]; kst[i + 2] = x[2]; kst[i + 3] = x[3];
-      const u32x4 y = *reinterpret_cast<const u32x4*>(&sw[8 * G + 2 * G * jq + i]);
-      vst[i] = y[0]; vst[i + 1] = y[1]; vst[i + 2] = y[2]; vst[i + 3] = y[3];
     }
-    auto ksc = [&](int e, int g) { return (float)as_h2(kst[(e * G + g) >> 1])[(e * G + g) & 1]; };
-    auto vsc = [&](int e, int g) { return (float)as_h2(vst[(e * G + g) >> 1])[(e * G + g) & 1]; };
-
-    float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int e = 0; e < 4; e++) sc[e] = 0.0f;
 #pragma unroll
     for (int g = 0; g < G; g++) {
       f16x8 A;
@@ -362,15 +376,37 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       const f32x4 ci = {cinit[g], cinit[g], cinit[g], cinit[g]};
       const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bq[g], ci, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(ksc(e, g), c[e], sc[e]);
+      for (int e = 0; e < 4; e++)
+        sc[e] = __builtin_fmaf((float)as_h2(kst[(e * G + g) >> 1])[(e * G + g) & 1], c[e], sc[e]);
     }
-    // hi + lo query parts (columns hr and hr ^ 8): both lanes end with the same full score
+  };
+
+  auto step = [&](const uint8_t* slotA, const uint8_t* slotB, int pa, int pb) {
+    float sA[4], sB[4];
+    scores(slotA, sA);
+    scores(slotB, sB);
+    // own page's hi (or lo) part plus the partner lane's part of the same page
+    float sc[4];
 #pragma unroll
-    for (int e = 0; e < 4; e++) sc[e] += dpp_ror8(sc[e]);
-    if (p == ptail) {  // wave-uniform: only the partial last page is masked
+    for (int e = 0; e < 4; e++) {
+      const float own = hiLane ? sA[e] : sB[e];
+      const float sup = hiLane ? sB[e] : sA[e];
+      sc[e] = own + dpp_ror8(sup);
+    }
+    const uint8_t* mine = hiLane ? slotA : slotB;
+    const uint32_t* swm = reinterpret_cast<const uint32_t*>(mine + 128 * C::KB);
+    uint32_t vst[2 * G];  // V scales of this lane's page
+#pragma unroll
+    for (int i = 0; i < 2 * G; i += 4) {
+      const u32x4 y = *reinterpret_cast<const u32x4*>(&swm[8 * G + 2 * G * jq + i]);
+      vst[i] = y[0]; vst[i + 1] = y[1]; vst[i + 2] = y[2]; vst[i + 3] = y[3];
+    }
+    if (pa == ptail || pb == ptail || pb >= p1) {  // wave-uniform: a partial or missing page
+      const int pm = hiLane ? pa : pb;
+      const int lim = (pm >= p1) ? 0 : (pm == ptail ? ltail : 16);
 #pragma unroll
       for (int e = 0; e < 4; e++)
-        if (4 * jq + e >= ltail) {
+        if (4 * jq + e >= lim) {
           sc[e] = -INFINITY;
 #pragma unroll
           for (int g = 0; g < G; g += 2) vst[(e * G + g) >> 1] = 0u;  // slot may hold garbage
@@ -379,6 +415,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     float cm = vmax3(sc[0], sc[1], vmax(sc[2], sc[3]));
     cm = max_xor16(cm);
     cm = max_xor32(cm);
+    cm = vmax(cm, dpp_ror8(cm));
     if (__any(cm > m_run)) {
       const float mn = fmaxf(m_run, cm);
       const float f = __builtin_amdgcn_exp2f((m_run - mn) * down);  // 2^-inf = 0
@@ -393,34 +430,58 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     for (int e = 0; e < 4; e++) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], down, nmd));
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
+    uint32_t vwA[G], vwB[G];
+#pragma unroll
+    for (int c = 0; c < C::NK; c++) {
+      if constexpr (C::DMAK == 16) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(slotA + 64 * C::KB + c * 1024 + lane * 16);
+        const u32x4 y = *reinterpret_cast<const u32x4*>(slotB + 64 * C::KB + c * 1024 + lane * 16);
+        vwA[4 * c] = x[0]; vwA[4 * c + 1] = x[1]; vwA[4 * c + 2] = x[2]; vwA[4 * c + 3] = x[3];
+        vwB[4 * c] = y[0]; vwB[4 * c + 1] = y[1]; vwB[4 * c + 2] = y[2]; vwB[4 * c + 3] = y[3];
+      } else {
+        vwA[c] = *reinterpret_cast<const uint32_t*>(slotA + 64 * C::KB + c * 256 + lane * 4);
+        vwB[c] = *reinterpret_cast<const uint32_t*>(slotB + 64 * C::KB + c * 256 + lane * 4);
+      }
+    }
+    auto vsc = [&](int e, int g) { return (float)as_h2(vst[(e * G + g) >> 1])[(e * G + g) & 1]; };
 #pragma unroll
     for (int g = 0; g < G; g++) {
-      // P' = p * s_V rounded once to fp16, k-slot token order 0 2 1 3
-      const f16x4 P = {(f16)__builtin_fmaf(pr[0], vsc(0, g), 0.0f), (f16)__builtin_fmaf(pr[2], vsc(2, g), 0.0f),
-                       (f16)__builtin_fmaf(pr[1], vsc(1, g), 0.0f), (f16)__builtin_fmaf(pr[3], vsc(3, g), 0.0f)};
-      const uint32_t w = vw[g], w8 = w >> 8;
-      const f16x4 Ae = __builtin_bit_cast(f16x4, u32x2{w & 0x000F000Fu, w8 & 0x000F000Fu});
-      const f16x4 Ao = __builtin_bit_cast(f16x4, u32x2{w & 0x00F000F0u, w8 & 0x00F000F0u});
-      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ae, P, acc[2 * g], 0, 0, 0);
-      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16f16(ceven, P, acc[2 * g], 0, 0, 0);
-      acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ao, P, acc[2 * g + 1], 0, 0, 0);
-      acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(codd, P, acc[2 * g + 1], 0, 0, 0);
+      // P' = p * s_V of this lane's page, rounded once to fp16, k-slot token order 0 2 1 3;
+      // k-slots 0..3 of the operand are page A, 4..7 page B (from the partner lane)
+      const f16x4 own = {(f16)__builtin_fmaf(pr[0], vsc(0, g), 0.0f), (f16)__builtin_fmaf(pr[2], vsc(2, g), 0.0f),
+                         (f16)__builtin_fmaf(pr[1], vsc(1, g), 0.0f), (f16)__builtin_fmaf(pr[3], vsc(3, g), 0.0f)};
+      const u32x2 o2 = __builtin_bit_cast(u32x2, own);
+      const uint32_t x0 = __builtin_amdgcn_mov_dpp(o2[0], 0x128, 0xf, 0xf, true);
+      const uint32_t x1 = __builtin_amdgcn_mov_dpp(o2[1], 0x128, 0xf, 0xf, true);
+      const f16x8 P = __builtin_bit_cast(f16x8, u32x4{o2[0], o2[1], x0, x1});
+      const uint32_t a = vwA[g], a8 = a >> 8, bw = vwB[g], b8 = bw >> 8;
+      const f16x8 Ae = __builtin_bit_cast(f16x8, u32x4{a & 0x000F000Fu, a8 & 0x000F000Fu, bw & 0x000F000Fu, b8 & 0x000F000Fu});
+      const f16x8 Ao = __builtin_bit_cast(f16x8, u32x4{a & 0x00F000F0u, a8 & 0x00F000F0u, bw & 0x00F000F0u, b8 & 0x00F000F0u});
+      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, P, acc[2 * g], 0, 0, 0);
+      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ceven, P, acc[2 * g], 0, 0, 0);
+      acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, P, acc[2 * g + 1], 0, 0, 0);
+      acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codd, P, acc[2 * g + 1], 0, 0, 0);
     }
   };
 
-  int it = 0;
 #pragma unroll 1
-  for (int p = p0 + wv; p < p1; p += NW, it++) {
-    const int pf = p + (C::NSLOT - 1) * NW;
-    if (pf < p1) stage_page<D>(page_ptr(pf), ring[wv][(it + C::NSLOT - 1) % C::NSLOT], lane);
-    const int younger = min(C::NSLOT - 1, (p1 - 1 - p) / NW);
-    wait_pages_in_flight<C::NDMA>(younger);
-    page(ring[wv][it % C::NSLOT], p);
+  for (int na = 0; na < npw; na += 2) {
+    // keep NSLOT - 2 pages in flight beyond the pair being computed
+#pragma unroll
+    for (int k = NSLOT - 2; k < NSLOT; k++) {
+      const int n = na + k;
+      if (n < npw) stage_page<D>(page_ptr(p0 + wv + NW * n), ring[n % NSLOT][wv], lane);
+    }
+    const int younger = max(0, min(NSLOT - 2, npw - 2 - na));  // pages issued after page na + 1
+    wait_pages_in_flight<C::NDMA, NSLOT - 2>(younger);
+    const int pa = p0 + wv + NW * na;
+    step(ring[na % NSLOT][wv], ring[(na + 1) % NSLOT][wv], pa, pa + NW);
   }
 
   // ---- epilogue: merge the waves of this workgroup -----------------------------------------
   l_run = sum_xor16(l_run);
   l_run = sum_xor32(l_run);
+  l_run += dpp_ror8(l_run);  // lanes hr and hr ^ 8 summed the two pages of each step
   m_run *= down;  // to the log2 domain of the merges below
   // back from the subnormal operand units: even dims carry 2^-24, odd dims 2^-20
 #pragma unroll
