@@ -79,7 +79,7 @@ __device__ __forceinline__ void stage_page(const uint8_t* blk, uint8_t* slot, in
   using C = Cfg<D>;
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
   const uint32_t lo = (uint32_t)lane * C::KB;  // this lane's byte offset inside an index region
-  const uint32_t base = lds_addr(slot);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(slot));  // M0 is scalar
 #pragma unroll
   for (int c = 0; c < C::NK; c++) {
     if constexpr (C::DMAK == 16) {
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // (the rotating waves issue theirs after the rotation, which stays off the busy queue)
   auto stage_first = [&]() {
 #pragma unroll
-    for (int k = 0; k < NSLOT - 2; k++) {
+    for (int k = 0; k < 2; k++) {
       const int pp = p0 + wv + k * NW;
       if (pp < p1) stage_page<D>(page_ptr(pp), ring[k][wv], lane);
     }
@@ -296,21 +296,41 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   }
   __syncthreads();
   const bool live = hl < r;
+  const bool hiLane = hr < 8;  // lanes 0..7 of a row finish page A of each step, 8..15 page B
   const float down = live ? qdown[hl] : 1.0f;
-  f16x8 bq[G];
+  // Score operands. With CHAIN (G <= 4) every lane holds the hi and the lo part of its own
+  // head, each twice: once live in the lanes that finish page A (hr < 8) and zero in the
+  // others, once the other way round. Four MFMAs chained on one accumulator (page A hi, A lo,
+  // B hi, B lo) then leave in every lane the full score of its own page, and the K-scale
+  // multiply runs once per lane instead of once per page and part. Without CHAIN (D = 256,
+  // where those registers are not available) column hr holds the hi part (hr < 8) or the lo
+  // part (hr >= 8) and the two are added across lanes afterwards.
+  constexpr bool CHAIN = G <= 4;
+  constexpr int NB = CHAIN ? 4 : 1;
+  f16x8 bq[NB][G];
   float cinit[G];
   // beta = 8 * 2^-24 * (sum of the column's query parts over the group), from one MFMA:
   // A = 8 * 2^-24 in every k-slot (128 * 2^-24 where the B values were divided by 16)
   const f16x8 abeta = __builtin_bit_cast(f16x8, u32x4{0x00080008u, 0x00800080u, 0x00080008u, 0x00800080u});
+  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int g = 0; g < G; g++) {
-    bq[g] = *reinterpret_cast<const f16x8*>(&bqs[g][lane][0]);
-    if (!live) bq[g] = f16x8{};
-    if constexpr (KSUB) {
-      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      cinit[g] = -__builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, bq[g], z, 0, 0, 0)[0];
-    } else {
+    if constexpr (CHAIN) {
+      f16x8 qh = *reinterpret_cast<const f16x8*>(&bqs[g][16 * jq + hl][0]);
+      f16x8 ql = *reinterpret_cast<const f16x8*>(&bqs[g][16 * jq + hl + 8][0]);
+      if (!live) qh = ql = f16x8{};
       cinit[g] = 0.0f;
+      if constexpr (KSUB)
+        cinit[g] = -(__builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, qh, zero4, 0, 0, 0)[0] +
+                     __builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, ql, zero4, 0, 0, 0)[0]);
+      bq[0][g] = hiLane ? qh : f16x8{};
+      bq[1][g] = hiLane ? ql : f16x8{};
+      bq[2][g] = hiLane ? f16x8{} : qh;
+      bq[3][g] = hiLane ? f16x8{} : ql;
+    } else {
+      bq[0][g] = *reinterpret_cast<const f16x8*>(&bqs[g][lane][0]);
+      if (!live) bq[0][g] = f16x8{};
+      cinit[g] = KSUB ? -__builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, bq[0][g], zero4, 0, 0, 0)[0] : 0.0f;
     }
   }
   __syncthreads();  // every wave holds its operands: the last ring slot is free again
@@ -334,7 +354,6 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const f16x8 ceven = __builtin_bit_cast(f16x8, ce4), codd = __builtin_bit_cast(f16x8, co4);
   const int ltail = L & 15;
   const int ptail = ltail ? npages - 1 : -1;  // the sequence's partial last page, if any
-  const bool hiLane = hr < 8;                 // lanes 0..7 of a row keep page A, 8..15 page B
 
   // ---- page loop: two pages per step ----------------------------------------------------
   // Wave wv takes pages p0 + wv + NW n, n = 0, 1, ...; step i handles n = 2i (page A) and
@@ -348,59 +367,84 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   float m_run = -INFINITY, nmd = INFINITY, l_run = 0.0f;
   const int npw = (p1 - p0 - wv + NW - 1) / NW;  // pages of this wave
 
-  auto scores = [&](const uint8_t* slot, float (&sc)[4]) {
-    uint32_t kw[G];
+  auto load_idx = [&](const uint8_t* slot, uint32_t (&w)[G], int region) {  // region 0: K, 1: V
 #pragma unroll
     for (int c = 0; c < C::NK; c++) {
       if constexpr (C::DMAK == 16) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(slot + c * 1024 + lane * 16);
-        kw[4 * c] = x[0]; kw[4 * c + 1] = x[1]; kw[4 * c + 2] = x[2]; kw[4 * c + 3] = x[3];
+        const u32x4 x = *reinterpret_cast<const u32x4*>(slot + region * 64 * C::KB + c * 1024 + lane * 16);
+        w[4 * c] = x[0]; w[4 * c + 1] = x[1]; w[4 * c + 2] = x[2]; w[4 * c + 3] = x[3];
       } else {
-        kw[c] = *reinterpret_cast<const uint32_t*>(slot + c * 256 + lane * 4);
+        w[c] = *reinterpret_cast<const uint32_t*>(slot + region * 64 * C::KB + c * 256 + lane * 4);
       }
     }
+  };
+  auto load_scales = [&](const uint8_t* slot, uint32_t (&st)[2 * G], int region) {  // 0: K, 1: V
     const uint32_t* sw = reinterpret_cast<const uint32_t*>(slot + 128 * C::KB);
-    uint32_t kst[2 * G];  // fp16 pairs: tokens 4jq..4jq+3, groups 0..G-1
 #pragma unroll
-    for (int i = 0; i < 2 * G; i += 4) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(&sw[2 * G * jq + i]);
-      kst[i] = x[0]; kst[i + 1] = x[1]; kst[i + 2] = x[2]; kst[i + 3] = x[3];
+    for (int i = 0; i < 2 * G; i += 4) {  // fp16 pairs: tokens 4jq..4jq+3, groups 0..G-1
+      const u32x4 x = *reinterpret_cast<const u32x4*>(&sw[region * 8 * G + 2 * G * jq + i]);
+      st[i] = x[0]; st[i + 1] = x[1]; st[i + 2] = x[2]; st[i + 3] = x[3];
     }
+  };
+  auto kop = [&](uint32_t w) -> f16x8 {
+    if constexpr (KSUB) return unpack_k_sub(w);
+    else return unpack_k_lut(w, tlo, thi);
+  };
+  auto scale_of = [](const uint32_t (&st)[2 * G], int e, int g) {
+    return (float)as_h2(st[(e * G + g) >> 1])[(e * G + g) & 1];
+  };
+  // one page's partial scores in every lane (column hr: hi or lo part), no CHAIN
+  auto scores = [&](const uint8_t* slot, float (&sc)[4]) {
+    uint32_t kw[G], kst[2 * G];
+    load_idx(slot, kw, 0);
+    load_scales(slot, kst, 0);
 #pragma unroll
     for (int e = 0; e < 4; e++) sc[e] = 0.0f;
 #pragma unroll
     for (int g = 0; g < G; g++) {
-      f16x8 A;
-      if constexpr (KSUB) A = unpack_k_sub(kw[g]);
-      else A = unpack_k_lut(kw[g], tlo, thi);
       const f32x4 ci = {cinit[g], cinit[g], cinit[g], cinit[g]};
-      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bq[g], ci, 0, 0, 0);
+      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop(kw[g]), bq[0][g], ci, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; e++)
-        sc[e] = __builtin_fmaf((float)as_h2(kst[(e * G + g) >> 1])[(e * G + g) & 1], c[e], sc[e]);
+      for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(scale_of(kst, e, g), c[e], sc[e]);
     }
   };
 
   auto step = [&](const uint8_t* slotA, const uint8_t* slotB, int pa, int pb) {
-    float sA[4], sB[4];
-    scores(slotA, sA);
-    scores(slotB, sB);
-    // own page's hi (or lo) part plus the partner lane's part of the same page
     float sc[4];
+    if constexpr (CHAIN) {
+      // full scores of this lane's page: page A hi, A lo, B hi, B lo on one accumulator
+      const uint8_t* own = hiLane ? slotA : slotB;
+      uint32_t kwA[G], kwB[G], kst[2 * G];
+      load_idx(slotA, kwA, 0);
+      load_idx(slotB, kwB, 0);
+      load_scales(own, kst, 0);
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const float own = hiLane ? sA[e] : sB[e];
-      const float sup = hiLane ? sB[e] : sA[e];
-      sc[e] = own + dpp_ror8(sup);
+      for (int e = 0; e < 4; e++) sc[e] = 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; g++) {
+        const f16x8 KA = kop(kwA[g]), KB = kop(kwB[g]);
+        f32x4 c = {cinit[g], cinit[g], cinit[g], cinit[g]};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA, bq[0][g], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA, bq[1][g], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB, bq[2][g], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB, bq[3][g], c, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(scale_of(kst, e, g), c[e], sc[e]);
+      }
+    } else {
+      float sA[4], sB[4];
+      scores(slotA, sA);
+      scores(slotB, sB);
+      // own page's hi (or lo) part plus the partner lane's part of the same page
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float own = hiLane ? sA[e] : sB[e];
+        const float sup = hiLane ? sB[e] : sA[e];
+        sc[e] = own + dpp_ror8(sup);
+      }
     }
-    const uint8_t* mine = hiLane ? slotA : slotB;
-    const uint32_t* swm = reinterpret_cast<const uint32_t*>(mine + 128 * C::KB);
     uint32_t vst[2 * G];  // V scales of this lane's page
-#pragma unroll
-    for (int i = 0; i < 2 * G; i += 4) {
-      const u32x4 y = *reinterpret_cast<const u32x4*>(&swm[8 * G + 2 * G * jq + i]);
-      vst[i] = y[0]; vst[i + 1] = y[1]; vst[i + 2] = y[2]; vst[i + 3] = y[3];
-    }
+    load_scales(hiLane ? slotA : slotB, vst, 1);
     if (pa == ptail || pb == ptail || pb >= p1) {  // wave-uniform: a partial or missing page
       const int pm = hiLane ? pa : pb;
       const int lim = (pm >= p1) ? 0 : (pm == ptail ? ltail : 16);
@@ -431,18 +475,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
     uint32_t vwA[G], vwB[G];
-#pragma unroll
-    for (int c = 0; c < C::NK; c++) {
-      if constexpr (C::DMAK == 16) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(slotA + 64 * C::KB + c * 1024 + lane * 16);
-        const u32x4 y = *reinterpret_cast<const u32x4*>(slotB + 64 * C::KB + c * 1024 + lane * 16);
-        vwA[4 * c] = x[0]; vwA[4 * c + 1] = x[1]; vwA[4 * c + 2] = x[2]; vwA[4 * c + 3] = x[3];
-        vwB[4 * c] = y[0]; vwB[4 * c + 1] = y[1]; vwB[4 * c + 2] = y[2]; vwB[4 * c + 3] = y[3];
-      } else {
-        vwA[c] = *reinterpret_cast<const uint32_t*>(slotA + 64 * C::KB + c * 256 + lane * 4);
-        vwB[c] = *reinterpret_cast<const uint32_t*>(slotB + 64 * C::KB + c * 256 + lane * 4);
-      }
-    }
+    load_idx(slotA, vwA, 1);
+    load_idx(slotB, vwB, 1);
     auto vsc = [&](int e, int g) { return (float)as_h2(vst[(e * G + g) >> 1])[(e * G + g) & 1]; };
 #pragma unroll
     for (int g = 0; g < G; g++) {
@@ -464,15 +498,20 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
   };
 
+  // Pages are issued in order; nis = next page number to issue. The ring fills up over the
+  // first steps (at most 4 issues per step) instead of in one burst that would stall the
+  // prologue behind a full memory queue.
+  int nis = min(npw, 2);
 #pragma unroll 1
   for (int na = 0; na < npw; na += 2) {
-    // keep NSLOT - 2 pages in flight beyond the pair being computed
+    const int nmax = min(npw, na + NSLOT);  // the slots of pages < na are free again
 #pragma unroll
-    for (int k = NSLOT - 2; k < NSLOT; k++) {
-      const int n = na + k;
-      if (n < npw) stage_page<D>(page_ptr(p0 + wv + NW * n), ring[n % NSLOT][wv], lane);
-    }
-    const int younger = max(0, min(NSLOT - 2, npw - 2 - na));  // pages issued after page na + 1
+    for (int k = 0; k < 4; k++)
+      if (nis < nmax) {
+        stage_page<D>(page_ptr(p0 + wv + NW * nis), ring[nis % NSLOT][wv], lane);
+        nis++;
+      }
+    const int younger = max(0, min(NSLOT - 2, nis - na - 2));  // pages issued after page na + 1
     wait_pages_in_flight<C::NDMA, NSLOT - 2>(younger);
     const int pa = p0 + wv + NW * na;
     step(ring[na % NSLOT][wv], ring[(na + 1) % NSLOT][wv], pa, pa + NW);
@@ -566,7 +605,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     if (tid == 0) __hip_atomic_store(&a.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // ---- the last workgroup of unit u merges every split (coherent sc1 loads) ----------
     // thread = (split group grp, head hd, 4 dims d4); split group grp takes splits
-    // grp, grp + ngrp, ...; the first 8 of them are loaded before the weights are known
+    // grp, grp + ngrp, ...; the first NLD of them are loaded before the weights are known
     const int64_t row0 = (int64_t)u * S * r;
     __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, (short)0, S * r * D * 4, 0x00020000);
     constexpr int D4 = D / 4;
@@ -574,10 +613,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     ngf = ngrp;
     const bool act = tid < ngrp * r * D4;
     const int grp = tid / (r * D4), hd = (tid / D4) % r, d4 = tid % D4;
-    f32x4 v[8];
+    constexpr int NLD = 16;  // split loads in flight per thread
+    f32x4 v[NLD];
     if (act) {
 #pragma unroll
-      for (int k = 0; k < 8; k++) {
+      for (int k = 0; k < NLD; k++) {
         const int t = min(grp + k * ngrp, ns - 1);
         v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, ((t * r + hd) * D + 4 * d4) * 4, 0, 16));
       }
@@ -616,16 +656,16 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     f32x4 o4 = {0.0f, 0.0f, 0.0f, 0.0f};
     if (act) {
 #pragma unroll
-      for (int k = 0; k < 8; k++)
+      for (int k = 0; k < NLD; k++)
         if (grp + k * ngrp < ns) o4 += wsh[hd][grp + k * ngrp] * v[k];
-      for (int t0 = grp + 8 * ngrp; t0 < ns; t0 += 8 * ngrp) {  // more than 8 splits per group
+      for (int t0 = grp + NLD * ngrp; t0 < ns; t0 += NLD * ngrp) {  // more splits per group
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
+        for (int k = 0; k < NLD; k++) {
           const int t = min(t0 + k * ngrp, ns - 1);
           v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, ((t * r + hd) * D + 4 * d4) * 4, 0, 16));
         }
 #pragma unroll
-        for (int k = 0; k < 8; k++)
+        for (int k = 0; k < NLD; k++)
           if (t0 + k * ngrp < ns) o4 += wsh[hd][t0 + k * ngrp] * v[k];
       }
     }
