@@ -75,11 +75,10 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
 //   [K indices: NK chunks of 64 lanes x DMAK][V indices: same][scales: 16G dwords]
 // The buffer descriptor spans exactly this block, so no lane can touch memory outside it.
 template <int D>
-__device__ __forceinline__ void stage_page(const uint8_t* blk, uint8_t* slot, int lane) {
+__device__ __forceinline__ void stage_page(const uint8_t* blk, uint32_t base, int lane) {
   using C = Cfg<D>;
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
   const uint32_t lo = (uint32_t)lane * C::KB;  // this lane's byte offset inside an index region
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(slot));  // M0 is scalar
 #pragma unroll
   for (int c = 0; c < C::NK; c++) {
     if constexpr (C::DMAK == 16) {
@@ -220,7 +219,6 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   __shared__ float mml[NW][8][2];              // per-wave (m, l), then per-wave weights
   __shared__ float hml[8][2];                  // per head: max M and sum l of the workgroup
   __shared__ int last_flag;
-  __shared__ int pid[TQ_MAX_SPLIT_PAGES];      // physical page of every page of this split
   static_assert(NW >= 8, "one wave per query head in the rotations");
   // Aliases of the ring: the query operands live in the last slot of every wave until the
   // page loop starts; after the loop, the per-wave results and the final-merge weights.
@@ -234,10 +232,29 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const uint8_t* hbase = a.pool + (int64_t)h * BB;
   const int64_t pstride = (int64_t)a.Hkv * BB;
-  for (int i = tid; i < p1 - p0; i += NT) pid[i] = bt[p0 + i];
-  auto page_ptr = [&](int p) {  // wave-uniform address of page p's block for head h
-    return hbase + (int64_t)__builtin_amdgcn_readfirstlane(pid[p - p0]) * pstride;
+  // this wave's pages p0 + wv + NW n, n < npw: physical page ids held across the lanes
+  // (page n in lane n % 64 of register n / 64), read back with v_readlane when issued
+  const int npw = (p1 - p0 - wv + NW - 1) / NW;  // pages of this wave
+  constexpr int PPL = (TQ_MAX_SPLIT_PAGES / NW + 63) / 64;
+  int vpid[PPL];
+#pragma unroll
+  for (int k = 0; k < PPL; k++) vpid[k] = (lane + 64 * k < npw) ? bt[p0 + wv + NW * (lane + 64 * k)] : 0;
+  // consume the loads here, before any page is in flight: otherwise the compiler waits for
+  // them (vmcnt(0), i.e. for every in-flight page too) where they are first read in the loop
+#pragma unroll
+  for (int k = 0; k < PPL; k++) asm volatile("" ::"v"(vpid[k]));
+  auto page_blk = [&](int n) {  // wave-uniform address of page n's block for head h
+    int id = vpid[0];
+    if constexpr (PPL > 1) {
+#pragma unroll
+      for (int k = 1; k < PPL; k++)
+        if ((n >> 6) == k) id = vpid[k];
+    }
+    return hbase + (int64_t)__builtin_amdgcn_readlane(id, n & 63) * pstride;
   };
+  // LDS byte address of ring slot k of this wave
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ring[0][0][0]));
+  auto slot_lds = [&](int k) { return ring_lds + (uint32_t)((k * NW + wv) * C::SLOT); };
   const TQ* qb = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
   float qv[V];
   if (wv < r) {  // wave w rotates query head w: sign flip now, butterflies below
@@ -255,7 +272,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int k = 0; k < 2; k++) {
       const int pp = p0 + wv + k * NW;
-      if (pp < p1) stage_page<D>(page_ptr(pp), ring[k][wv], lane);
+      if (pp < p1) stage_page<D>(page_blk(k), slot_lds(k), lane);
     }
   };
   if (wv >= r) stage_first();
@@ -305,7 +322,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // multiply runs once per lane instead of once per page and part. Without CHAIN (D = 256,
   // where those registers are not available) column hr holds the hi part (hr < 8) or the lo
   // part (hr >= 8) and the two are added across lanes afterwards.
-  constexpr bool CHAIN = G <= 4;
+  constexpr bool CHAIN = (G <= 4) && (NW <= 8);
   constexpr int NB = CHAIN ? 4 : 1;
   f16x8 bq[NB][G];
   float cinit[G];
@@ -365,7 +382,6 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   for (int t = 0; t < 2 * G; t++) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // m_run: running max of the raw scores (shared by lanes hr and hr ^ 8); nmd = -m_run * down
   float m_run = -INFINITY, nmd = INFINITY, l_run = 0.0f;
-  const int npw = (p1 - p0 - wv + NW - 1) / NW;  // pages of this wave
 
   auto load_idx = [&](const uint8_t* slot, uint32_t (&w)[G], int region) {  // region 0: K, 1: V
 #pragma unroll
@@ -508,7 +524,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int k = 0; k < 4; k++)
       if (nis < nmax) {
-        stage_page<D>(page_ptr(p0 + wv + NW * nis), ring[nis % NSLOT][wv], lane);
+        stage_page<D>(page_blk(nis), slot_lds(nis % NSLOT), lane);
         nis++;
       }
     const int younger = max(0, min(NSLOT - 2, nis - na - 2));  // pages issued after page na + 1

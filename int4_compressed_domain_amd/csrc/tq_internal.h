@@ -47,7 +47,7 @@ hipError_t tq_launch_dequant(const LaunchDequant& a, hipStream_t st);
 
 // Wavefronts per fused-decode workgroup; each workgroup owns one (sequence, kv head,
 // context split). 16 waves fill a CU when the kernel fits in 128 registers per lane.
-constexpr int tq_decode_waves(int D) { return D > 0 ? 8 : 8; }
+constexpr int tq_decode_waves(int D) { return D > 128 ? 8 : 16; }
 constexpr int TQ_DECODE_WAVES = 4;   // dense baseline workgroups
 constexpr int TQ_MAX_SPLITS = 128;   // context splits per (sequence, kv head)
 constexpr int TQ_MAX_SPLIT_PAGES = 2048;  // pages per split (their ids are staged in LDS)
