@@ -315,16 +315,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const bool live = hl < r;
   const bool hiLane = hr < 8;  // lanes 0..7 of a row finish page A of each step, 8..15 page B
   const float down = live ? qdown[hl] : 1.0f;
-  // Score operands. With CHAIN (G <= 4) every lane holds the hi and the lo part of its own
-  // head, each twice: once live in the lanes that finish page A (hr < 8) and zero in the
-  // others, once the other way round. Four MFMAs chained on one accumulator (page A hi, A lo,
-  // B hi, B lo) then leave in every lane the full score of its own page, and the K-scale
-  // multiply runs once per lane instead of once per page and part. Without CHAIN (D = 256,
-  // where those registers are not available) column hr holds the hi part (hr < 8) or the lo
-  // part (hr >= 8) and the two are added across lanes afterwards.
-  constexpr bool CHAIN = (G <= 4) && (NW <= 8);
-  constexpr int NB = CHAIN ? 4 : 1;
-  f16x8 bq[NB][G];
+  // Score operands: column hr holds the hi part (hr < 8) or the lo part (hr >= 8) of the
+  // query values of head hr & 7; the two partial scores are added across lanes afterwards.
+  f16x8 bq[G];
   float cinit[G];
   // beta = 8 * 2^-24 * (sum of the column's query parts over the group), from one MFMA:
   // A = 8 * 2^-24 in every k-slot (128 * 2^-24 where the B values were divided by 16)
@@ -332,23 +325,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int g = 0; g < G; g++) {
-    if constexpr (CHAIN) {
-      f16x8 qh = *reinterpret_cast<const f16x8*>(&bqs[g][16 * jq + hl][0]);
-      f16x8 ql = *reinterpret_cast<const f16x8*>(&bqs[g][16 * jq + hl + 8][0]);
-      if (!live) qh = ql = f16x8{};
-      cinit[g] = 0.0f;
-      if constexpr (KSUB)
-        cinit[g] = -(__builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, qh, zero4, 0, 0, 0)[0] +
-                     __builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, ql, zero4, 0, 0, 0)[0]);
-      bq[0][g] = hiLane ? qh : f16x8{};
-      bq[1][g] = hiLane ? ql : f16x8{};
-      bq[2][g] = hiLane ? f16x8{} : qh;
-      bq[3][g] = hiLane ? f16x8{} : ql;
-    } else {
-      bq[0][g] = *reinterpret_cast<const f16x8*>(&bqs[g][lane][0]);
-      if (!live) bq[0][g] = f16x8{};
-      cinit[g] = KSUB ? -__builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, bq[0][g], zero4, 0, 0, 0)[0] : 0.0f;
-    }
+    bq[g] = *reinterpret_cast<const f16x8*>(&bqs[g][lane][0]);
+    if (!live) bq[g] = f16x8{};
+    cinit[g] = KSUB ? -__builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, bq[g], zero4, 0, 0, 0)[0] : 0.0f;
   }
   __syncthreads();  // every wave holds its operands: the last ring slot is free again
   uint32_t tlo[4] = {0, 0, 0, 0}, thi[4] = {0, 0, 0, 0};
@@ -409,7 +388,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   auto scale_of = [](const uint32_t (&st)[2 * G], int e, int g) {
     return (float)as_h2(st[(e * G + g) >> 1])[(e * G + g) & 1];
   };
-  // one page's partial scores in every lane (column hr: hi or lo part), no CHAIN
+  // one page's partial scores in every lane (column hr: hi or lo part)
   auto scores = [&](const uint8_t* slot, float (&sc)[4]) {
     uint32_t kw[G], kst[2 * G];
     load_idx(slot, kw, 0);
@@ -419,7 +398,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int g = 0; g < G; g++) {
       const f32x4 ci = {cinit[g], cinit[g], cinit[g], cinit[g]};
-      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop(kw[g]), bq[0][g], ci, 0, 0, 0);
+      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop(kw[g]), bq[g], ci, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(scale_of(kst, e, g), c[e], sc[e]);
     }
@@ -427,37 +406,15 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 
   auto step = [&](const uint8_t* slotA, const uint8_t* slotB, int pa, int pb) {
     float sc[4];
-    if constexpr (CHAIN) {
-      // full scores of this lane's page: page A hi, A lo, B hi, B lo on one accumulator
-      const uint8_t* own = hiLane ? slotA : slotB;
-      uint32_t kwA[G], kwB[G], kst[2 * G];
-      load_idx(slotA, kwA, 0);
-      load_idx(slotB, kwB, 0);
-      load_scales(own, kst, 0);
+    float sA[4], sB[4];
+    scores(slotA, sA);
+    scores(slotB, sB);
+    // own page's hi (or lo) part plus the partner lane's part of the same page
 #pragma unroll
-      for (int e = 0; e < 4; e++) sc[e] = 0.0f;
-#pragma unroll
-      for (int g = 0; g < G; g++) {
-        const f16x8 KA = kop(kwA[g]), KB = kop(kwB[g]);
-        f32x4 c = {cinit[g], cinit[g], cinit[g], cinit[g]};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA, bq[0][g], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA, bq[1][g], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB, bq[2][g], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB, bq[3][g], c, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(scale_of(kst, e, g), c[e], sc[e]);
-      }
-    } else {
-      float sA[4], sB[4];
-      scores(slotA, sA);
-      scores(slotB, sB);
-      // own page's hi (or lo) part plus the partner lane's part of the same page
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const float own = hiLane ? sA[e] : sB[e];
-        const float sup = hiLane ? sB[e] : sA[e];
-        sc[e] = own + dpp_ror8(sup);
-      }
+    for (int e = 0; e < 4; e++) {
+      const float own = hiLane ? sA[e] : sB[e];
+      const float sup = hiLane ? sB[e] : sA[e];
+      sc[e] = own + dpp_ror8(sup);
     }
     uint32_t vst[2 * G];  // V scales of this lane's page
     load_scales(hiLane ? slotA : slotB, vst, 1);
