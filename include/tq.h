@@ -139,6 +139,26 @@ int tq_decode_attn(const tq_layout* layout, const void* pool, const void* q, int
                    int32_t num_splits, float* out, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Append the newest token of every sequence, then decode: the same result as
+ *   tq_kv_append(k_last, v_last, slots = position context_lens[b] - 1 of each sequence)
+ *   followed by tq_decode_attn(...), in one launch. The token of sequence b is the last one
+ *   it attends to (position context_lens[b] - 1, in the page block_table[b][(len - 1) / 16]);
+ *   sequences with context_lens[b] == 0 append nothing.
+ *   pool            device, written at those slots (and read as in tq_decode_attn)
+ *   k_last, v_last  device, [batch][num_kv_heads][head_dim] of in_dtype (TQ_F32, TQ_BF16,
+ *                   TQ_F16), row-major
+ *   other arguments, workspace and errors as tq_decode_attn.
+ * The decode of a step reads that page anyway: the new token is quantized by the same
+ * kernel and used from on-chip memory, which saves the separate append launch.
+ * [Open-TQ-Metal, card abstract: quantize on append; arXiv abstract: attention directly on
+ *  the compressed representation] */
+int tq_append_decode_attn(const tq_layout* layout, void* pool, const void* k_last,
+                          const void* v_last, int32_t in_dtype, const void* q, int32_t q_dtype,
+                          int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, float attn_scale,
+                          int32_t num_splits, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Dequantize reference: dense K and V, [batch][num_kv_heads][max_context_len][head_dim]
  * of out_dtype (TQ_F32 or TQ_F16), rows at or past a sequence's length set to zero.
  * to_original_basis = 0: values (u-8)*s or LUT_u*n in the rotated basis (exact products,

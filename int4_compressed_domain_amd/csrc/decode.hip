@@ -27,7 +27,7 @@
 //            otherwise it stores its partial (o', m, l), and the last workgroup of the unit
 //            to arrive (atomic counter, reset afterwards) merges all splits. The result is
 //            rotated back (fp32 butterfly, times rho, times sigma) and written.
-#include "tq_device.h"
+#include "tq_codec.h"
 #include "tq_internal.h"
 
 namespace {
@@ -215,6 +215,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 
   // page ring (per wave) -- reused after the page loop as the merge area
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT][NW][C::SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t tokblk[BB];  // the appended token's codes
   __shared__ float qdown[8];                   // per head: raw score units -> log2 units
   __shared__ float mml[NW][8][2];              // per-wave (m, l), then per-wave weights
   __shared__ float hml[8][2];                  // per head: max M and sum l of the workgroup
@@ -255,6 +256,27 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // LDS byte address of ring slot k of this wave
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ring[0][0][0]));
   auto slot_lds = [&](int k) { return ring_lds + (uint32_t)((k * NW + wv) * C::SLOT); };
+  // Fused append: the split holding the sequence's last page also appends its last token
+  // (position L - 1) for head h. Wave wc quantizes it into tokblk (the block layout, only
+  // that token's bytes valid); wave wl, which owns the last page, patches its staged copy
+  // before computing it; wave wc stores the token to the pool after the page loop.
+  constexpr int E = CodecCfg<D>::E;
+  const bool app = (a.knew != nullptr) && (s == ns - 1);
+  const int plast = npages - 1, tnew = (L - 1) & 15;
+  const int wc = NW - 1, wl = (plast - p0) % NW;
+  float ynew[E];
+  uint32_t swnew = 0;
+  if (app && wv == wc && lane < 32) {
+    swnew = lane_signs<D>(a.sign_bits, lane & 15);
+    const int64_t off = ((int64_t)b * a.Hkv + h) * D + (lane & 15) * E;
+    const void* src = (lane < 16) ? a.knew : a.vnew;
+    if (a.new_dtype == TQ_F32) load_widen<float, E>(static_cast<const float*>(src) + off, ynew);
+    else if (a.new_dtype == TQ_BF16) load_widen<uint16_t, E>(static_cast<const uint16_t*>(src) + off, ynew);
+    else load_widen<f16, E>(static_cast<const f16*>(src) + off, ynew);
+#pragma unroll
+    for (int e = 0; e < E; e++) asm volatile("" ::"v"(ynew[e]));  // before any page load
+    asm volatile("" ::"v"(swnew));
+  }
   const TQ* qb = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
   float qv[V];
   if (wv < r) {  // wave w rotates query head w: sign flip now, butterflies below
@@ -310,6 +332,13 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     // scores come out in units of 2^-sh (times 2^24 for the subnormal K form)
     if (lane == 0) qdown[wv] = ldexpf(1.0f, KSUB ? 24 - sh : -sh);
     stage_first();
+  }
+  if (app && wv == wc && lane < 32) {
+    uint32_t un[E];
+    f16 scn;
+    if (lane >= 16 || KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, swnew, lane & 15, un, scn);
+    else codec_vector<D, TQ_CODEC_LLOYDMAX>(ynew, swnew, lane & 15, un, scn);
+    place_vector<D>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
   }
   __syncthreads();
   const bool live = hl < r;
@@ -471,6 +500,29 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
   };
 
+  // Copy the appended token's bytes (indices and scales of token tnew) from tokblk into a
+  // block: the pool (to_lds = false), or the staged LDS copy of the last page, whose index
+  // regions are stored chunk by chunk as the page loads wrote them (see stage_page).
+  auto copy_token = [&](uint8_t* dst, bool to_lds) {
+    constexpr int G_ = D / 32, KB = C::KB, DM = C::DMAK;
+    auto at = [&](int o) {
+      if (!to_lds || o >= 128 * KB) return o;
+      const int reg = o / (64 * KB), w = o % (64 * KB), l = w / KB, wb = w % KB;
+      return reg * 64 * KB + (wb / DM) * (64 * DM) + l * DM + (wb % DM);
+    };
+    for (int i = lane; i < 4 * G_; i += 64) {  // K index dwords: chunk q = 4g + j
+      const int off = (16 * (i & 3) + tnew) * 4 * G_ + 4 * (i >> 2);
+      *reinterpret_cast<uint32_t*>(dst + at(off)) = *reinterpret_cast<const uint32_t*>(tokblk + off);
+    }
+    for (int c = lane; c < D / 2; c += 64) {  // V index bytes: dim pair c = 16g + m
+      const int off = 8 * D + (16 * (tnew >> 2) + (c & 15)) * 4 * G_ + 4 * (c >> 4) + (tnew & 3);
+      dst[at(off)] = tokblk[off];
+    }
+    if (lane < 2 * G_) {  // K scales then V scales
+      const int off = 16 * D + (lane >= G_ ? 32 * G_ : 0) + 2 * (tnew * G_ + (lane % G_));
+      *reinterpret_cast<f16*>(dst + at(off)) = *reinterpret_cast<const f16*>(tokblk + off);
+    }
+  };
   // Pages are issued in order; nis = next page number to issue. The ring fills up over the
   // first steps (at most 4 issues per step) instead of in one burst that would stall the
   // prologue behind a full memory queue.
@@ -487,8 +539,15 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     const int younger = max(0, min(NSLOT - 2, nis - na - 2));  // pages issued after page na + 1
     wait_pages_in_flight<C::NDMA, NSLOT - 2>(younger);
     const int pa = p0 + wv + NW * na;
+    if (app && wv == wl && (pa == plast || pa + NW == plast)) {  // wave-uniform
+      copy_token(ring[(pa == plast ? na : na + 1) % NSLOT][wv], true);
+      asm volatile("" ::: "memory");
+    }
     step(ring[na % NSLOT][wv], ring[(na + 1) % NSLOT][wv], pa, pa + NW);
   }
+
+  if (app && wv == wc)  // the appended token goes to the pool too, for later calls
+    copy_token(const_cast<uint8_t*>(a.pool) + ((int64_t)__builtin_amdgcn_readfirstlane(bt[plast]) * a.Hkv + h) * BB, false);
 
   // ---- epilogue: merge the waves of this workgroup -----------------------------------------
   l_run = sum_xor16(l_run);

@@ -151,11 +151,12 @@ size_t tq_decode_workspace_size(const tq_layout* L, int32_t batch, int32_t max_c
   return workspace_bytes(L, batch, max_context_len, num_splits);
 }
 
-int tq_decode_attn(const tq_layout* L, const void* pool, const void* q, int32_t q_dtype,
-                   int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
-                   const int32_t* context_lens, int32_t max_context_len, float attn_scale,
-                   int32_t num_splits, float* out, void* workspace, size_t workspace_bytes_,
-                   void* stream) {
+static int decode_impl(const tq_layout* L, const void* pool, const void* knew, const void* vnew,
+                       int32_t new_dtype, const void* q, int32_t q_dtype, int32_t batch,
+                       const int32_t* block_table, int32_t max_pages_per_seq,
+                       const int32_t* context_lens, int32_t max_context_len, float attn_scale,
+                       int32_t num_splits, float* out, void* workspace, size_t workspace_bytes_,
+                       void* stream) {
   int rc = check_layout(L, true);
   if (rc != TQ_OK) return rc;
   rc = check_decode_common(L, q, q_dtype, batch, context_lens, max_context_len, attn_scale,
@@ -184,7 +185,31 @@ int tq_decode_attn(const tq_layout* L, const void* pool, const void* q, int32_t 
   a.q_dtype = q_dtype; a.k_codec = L->k_codec;
   a.splits = s.splits; a.pages_per_split = s.pages_per_split;
   a.attn_scale = attn_scale;
+  a.knew = knew; a.vnew = vnew; a.new_dtype = new_dtype;
   return from_hip(tq_launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int tq_decode_attn(const tq_layout* L, const void* pool, const void* q, int32_t q_dtype,
+                   int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                   const int32_t* context_lens, int32_t max_context_len, float attn_scale,
+                   int32_t num_splits, float* out, void* workspace, size_t workspace_bytes_,
+                   void* stream) {
+  return decode_impl(L, pool, nullptr, nullptr, 0, q, q_dtype, batch, block_table,
+                     max_pages_per_seq, context_lens, max_context_len, attn_scale, num_splits, out,
+                     workspace, workspace_bytes_, stream);
+}
+
+int tq_append_decode_attn(const tq_layout* L, void* pool, const void* k_last, const void* v_last,
+                          int32_t in_dtype, const void* q, int32_t q_dtype, int32_t batch,
+                          const int32_t* block_table, int32_t max_pages_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, float attn_scale,
+                          int32_t num_splits, float* out, void* workspace, size_t workspace_bytes_,
+                          void* stream) {
+  if (in_dtype != TQ_F32 && in_dtype != TQ_BF16 && in_dtype != TQ_F16) return TQ_EINVAL;
+  if (batch > 0 && (!k_last || !v_last)) return TQ_EINVAL;
+  return decode_impl(L, pool, k_last, v_last, in_dtype, q, q_dtype, batch, block_table,
+                     max_pages_per_seq, context_lens, max_context_len, attn_scale, num_splits, out,
+                     workspace, workspace_bytes_, stream);
 }
 
 int tq_dequant_ref(const tq_layout* L, const void* pool, int32_t batch, const int32_t* block_table,

@@ -28,6 +28,9 @@ struct LaunchDecode {
   int D, Hq, Hkv, B, max_pages, max_ctx, q_dtype, k_codec;
   int splits, pages_per_split;
   float attn_scale;
+  const void* knew;          // optional: K and V of each sequence's last token,
+  const void* vnew;          //   [B][Hkv][D] of new_dtype, appended before attending
+  int new_dtype;
 };
 
 hipError_t tq_launch_append(const LaunchAppend& a, hipStream_t st);

@@ -15,7 +15,7 @@ CODEC_ABSMAX, CODEC_LLOYDMAX = 0, 1
 F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("tq_status_str", "tq_page_bytes", "tq_kv_append", "tq_decode_workspace_size",
-           "tq_decode_attn", "tq_dequant_ref", "tq_dense_decode_attn")
+           "tq_decode_attn", "tq_append_decode_attn", "tq_dequant_ref", "tq_dense_decode_attn")
 
 
 class TQError(RuntimeError):
@@ -52,6 +52,10 @@ def _lib():
         L.tq_decode_workspace_size.argtypes = [LP, i32, i32, i32]
         L.tq_decode_workspace_size.restype = sz
         L.tq_decode_attn.argtypes = [LP, P, P, i32, i32, P, i32, P, i32, f32, i32, P, P, sz, P]
+        if hasattr(L, "tq_append_decode_attn"):  # (absent from older builds of the library)
+            L.tq_append_decode_attn.argtypes = [LP, P, P, P, i32, P, i32, i32, P, i32, P, i32, f32,
+                                                i32, P, P, sz, P]
+            L.tq_append_decode_attn.restype = ctypes.c_int
         L.tq_dequant_ref.argtypes = [LP, P, i32, P, i32, P, i32, i32, i32, P, P, P]
         L.tq_dense_decode_attn.argtypes = [LP, P, P, P, i32, i32, P, i32, f32, i32, P, P, sz, P]
         for name in ("tq_kv_append", "tq_decode_attn", "tq_dequant_ref", "tq_dense_decode_attn"):
@@ -116,6 +120,16 @@ def tq_decode_attn(layout, pool, q, block_table, context_lens, max_context_len, 
         block_table.shape[1], _ptr(context_lens), max_context_len, attn_scale, num_splits,
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)), "tq_decode_attn")
+
+
+def tq_append_decode_attn(layout, pool, k_last, v_last, q, block_table, context_lens,
+                          max_context_len, attn_scale, out, workspace, num_splits=0, stream=None):
+    """Append each sequence's newest token (k_last, v_last: [batch][Hkv][D]), then decode."""
+    _check(_lib().tq_append_decode_attn(
+        ctypes.byref(layout), _ptr(pool), _ptr(k_last), _ptr(v_last), _dtype_code(k_last),
+        _ptr(q), _dtype_code(q), q.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(context_lens), max_context_len, attn_scale, num_splits, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "tq_append_decode_attn")
 
 
 def tq_dequant_ref(layout, pool, block_table, context_lens, max_context_len, k_out, v_out,

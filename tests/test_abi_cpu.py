@@ -91,6 +91,24 @@ def test_decode_argument_validation():
     assert _decode(L, batch=0, q=None, out=None) == tq.TQ_OK
 
 
+def _append_decode(L, batch=2, kl=FAKE, vl=FAKE, kd=tq.BF16, bt=FAKE, maxp=4, ctx=FAKE, maxctx=64,
+                   alpha=0.1, splits=0, out=FAKE, ws=FAKE, wsb=1 << 30, q=FAKE, qd=tq.BF16, pool=FAKE):
+    return tq.lib().tq_append_decode_attn(ctypes.byref(L), pool, kl, vl, kd, q, qd, batch, bt, maxp,
+                                          ctx, maxctx, alpha, splits, out, ws, wsb, None)
+
+
+def test_append_decode_argument_validation():
+    L = _layout()
+    assert _append_decode(L, kd=5) == tq.TQ_EINVAL              # bad k/v dtype
+    assert _append_decode(L, kl=None) == tq.TQ_EINVAL
+    assert _append_decode(L, vl=None) == tq.TQ_EINVAL
+    assert _append_decode(L, maxctx=65, maxp=4) == tq.TQ_EINVAL
+    assert _append_decode(L, qd=7) == tq.TQ_EINVAL
+    assert _append_decode(L, wsb=16) == tq.TQ_ENOSPC
+    assert _append_decode(L, pool=None) == tq.TQ_EINVAL
+    assert _append_decode(L, batch=0, kl=None, vl=None, q=None, out=None) == tq.TQ_OK
+
+
 def test_workspace_size_formula():
     L = _layout()
     for batch, ctx, splits in ((1, 131072, 5), (16, 8192, 1), (3, 100, 100)):

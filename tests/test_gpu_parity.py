@@ -231,6 +231,56 @@ def test_full_size_workloads(name):
     _check_case(c, pairs=pairs)
 
 
+@pytest.mark.parametrize("D,r,k_codec,dtype", [(128, 8, 0, "bf16"), (128, 4, 1, "bf16"),
+                                               (64, 2, 0, "f32"), (256, 2, 0, "bf16")])
+def test_append_decode_equals_append_then_decode(D, r, k_codec, dtype):
+    """The fused entry point writes the same pool bytes as tq_kv_append of each sequence's
+    last token and returns the same output, bit for bit, as tq_decode_attn afterwards."""
+    lens = [0, 1, 15, 16, 17, 33, 250, 1000]
+    w = W.Workload("appdec", len(lens), 2 * r, 2, D, max(lens), dtype, 0.125, k_codec=k_codec)
+    _say("case append+decode D", D, "r", r, "k_codec", k_codec, dtype)
+    fused = Case(w, seed=31, lens=lens)
+    split = Case(w, seed=31, lens=lens, oracle=False)
+    for c in (fused, split):  # every token but the last
+        for b, L in enumerate(c.lens):
+            if L > 1:
+                c.append_seq(b, 0, int(L) - 1)
+    k_last = np.zeros((w.batch, w.kv_heads, D), np.float32)
+    v_last = np.zeros_like(k_last)
+    kst = np.zeros(k_last.shape, np.float32 if dtype == "f32" else np.uint16)
+    vst = np.zeros_like(kst)
+    slots = np.full(w.batch, -1, np.int64)
+    for b, L in enumerate(fused.lens):
+        if L > 0:
+            k32, v32, ks_, vs_ = W.seq_tokens(w, b, int(L), fused.seed, fused.scales)
+            k_last[b], v_last[b], kst[b], vst[b] = k32[-1], v32[-1], ks_[-1], vs_[-1]
+            slots[b] = W.slots_for(fused.bt, b, int(L) - 1, int(L))[0]
+    maxc = int(max(lens))
+    outs = []
+    for c, use_fused in ((fused, True), (split, False)):
+        ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, w.batch, maxc, 0) // 4, dtype=torch.float32, device=DEV)
+        out = torch.full((w.batch, w.q_heads, D), float("nan"), dtype=torch.float32, device=DEV)
+        if use_fused:
+            tq.tq_append_decode_attn(c.layout, c.pool, to_dev(kst, dtype), to_dev(vst, dtype), c.q_dev,
+                                     c.bt_dev, c.lens_dev, maxc, w.attn_scale, out, ws)
+        else:
+            tq.tq_kv_append(c.layout, c.pool, to_dev(kst, dtype), to_dev(vst, dtype),
+                            torch.from_numpy(slots).to(DEV))
+            tq.tq_decode_attn(c.layout, c.pool, c.q_dev, c.bt_dev, c.lens_dev, maxc, w.attn_scale, out, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    keep = slots >= 0
+    c_oracle.append(fused.opool, D, w.kv_heads, k_last[keep], v_last[keep], slots[keep], fused.sb,
+                    w.k_codec, w.v_codec)
+    assert np.array_equal(fused.pool.cpu().numpy(), split.pool.cpu().numpy())
+    assert fused.pool_equal()
+    assert np.array_equal(outs[0], outs[1])
+    err = attn_err(outs[0], fused.decode_oracle())
+    _say("   max normwise err %.3e" % err.max())
+    assert err.max() <= ATTN_TOL
+    assert np.all(outs[0][0] == 0.0)
+
+
 def test_workspace_reuse_across_calls():
     """The split-arrival counters in the workspace return to zero after every call, so one
     zero-filled workspace serves calls of any batch size and split count in sequence."""
