@@ -1,8 +1,10 @@
 """Benchmark: one decode step of int4 compressed-domain attention on one MI355X.
 
-A step = the whole hot path over one batch: append the new token of every decoding
-sequence (plus the prefill chunk, for the mixed-serving workload) into the packed pool,
-then decode one query per sequence over its whole context, directly on the packed codes.
+A step = the whole hot path over one batch: the prefill chunk of the mixed-serving
+workload is appended to the packed pool (tq_kv_append), then one launch
+(tq_append_decode_attn) rotates, quantizes and writes the new token of every decoding
+sequence and decodes one query per sequence over its whole context, directly on the
+packed codes.
 Inputs are resident in HBM before the timed region. To measure HBM rather than the 256 MB
 Infinity Cache, the step cycles through several identical copies of the pool (>= 1 GiB
 in total), so each step reads a pool that was evicted since its last use.
@@ -38,7 +40,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--splits", type=int, default=0, help="context splits (0 = automatic)")
@@ -46,7 +48,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true", help="skip the fp16 GPU baseline")
     ap.add_argument("--profile", type=int, default=0,
-                    help="run this many eager steps (append + decode) and exit: for profilers")
+                    help="run this many eager steps and exit: for profilers")
     return ap.parse_args()
 
 
@@ -77,7 +79,10 @@ class Setup:
         scales = W.channel_scales(w, 0)
         self.scales = scales
         # resident cache: every token but the last of each sequence
-        new_k, new_v, new_slots = [], [], []
+        # newest token of each sequence, in its storage type (zeros for an empty sequence)
+        sdt = np.uint16 if w.dtype == "bf16" else np.float32
+        k_last = np.zeros((w.batch, Hkv, D), sdt)
+        v_last = np.zeros((w.batch, Hkv, D), sdt)
         t_fill = time.time()
         for b in range(w.batch):
             L = int(self.lens[b])
@@ -88,23 +93,20 @@ class Setup:
                                 to_dev(vst[t0:t1], w.dtype, dev),
                                 torch.from_numpy(W.slots_for(self.bt, b, t0, t1)).to(dev))
             if L > 0:
-                new_k.append(kst[L - 1:L])
-                new_v.append(vst[L - 1:L])
-                new_slots.append(W.slots_for(self.bt, b, L - 1, L))
+                k_last[b], v_last[b] = kst[L - 1], vst[L - 1]
+        self.k_pre = None
         if w.prefill:
             _, _, kst, vst = W.prefill_tokens(w, 0, scales)
-            new_k.append(kst)
-            new_v.append(vst)
             pre = self.prefill_pages.astype(np.int64)
             t = np.arange(w.prefill)
-            new_slots.append(pre[t // 16] * 16 + t % 16)
+            self.k_pre, self.v_pre = to_dev(kst, w.dtype, dev), to_dev(vst, w.dtype, dev)
+            self.slots_pre = torch.from_numpy(pre[t // 16] * 16 + t % 16).to(dev)
         torch.cuda.synchronize()
         log("filled %s: %d pages, %.1f MB pool, %.1f s" % (w.name, self.npages, pool_bytes / 1e6,
                                                             time.time() - t_fill))
-        self.n_new = int(sum(len(s) for s in new_slots))
-        self.k_new = to_dev(np.concatenate(new_k), w.dtype, dev)
-        self.v_new = to_dev(np.concatenate(new_v), w.dtype, dev)
-        self.slots_new = torch.from_numpy(np.concatenate(new_slots).astype(np.int64)).to(dev)
+        self.n_new = int(np.count_nonzero(self.lens)) + w.prefill
+        self.k_last = to_dev(k_last, w.dtype, dev)
+        self.v_last = to_dev(v_last, w.dtype, dev)
         ncopy = max(2, int(math.ceil(args.min_pool_bytes / max(pool_bytes, 1))))
         self.pools = [pool] + [pool.clone() for _ in range(ncopy - 1)]
         self.q32, qst = W.queries(w, 0)
@@ -120,16 +122,23 @@ class Setup:
         self.kv_bytes = int(np.sum(self.lens, dtype=np.int64)) * Hkv * 2 * (D // 2 + 2 * (D // 32))
         log("pool copies: %d (%.2f GB)" % (ncopy, ncopy * pool_bytes / 1e9))
 
-    def append(self, i):
+    def prefill(self, i):
+        """The prefill chunk's append (mixed serving only)."""
         from int4_compressed_domain_amd import tq
-        tq.tq_kv_append(self.layout, self.pools[i % len(self.pools)], self.k_new, self.v_new,
-                        self.slots_new)
+        if self.k_pre is not None:
+            tq.tq_kv_append(self.layout, self.pools[i % len(self.pools)], self.k_pre, self.v_pre,
+                            self.slots_pre)
 
     def decode(self, i):
+        """One launch: append every decoding sequence's newest token, then attend."""
         from int4_compressed_domain_amd import tq
-        tq.tq_decode_attn(self.layout, self.pools[i % len(self.pools)], self.q, self.bt_dev,
-                          self.lens_dev, self.max_ctx, self.w.attn_scale, self.out, self.ws,
-                          num_splits=self.splits)
+        tq.tq_append_decode_attn(self.layout, self.pools[i % len(self.pools)], self.k_last,
+                                 self.v_last, self.q, self.bt_dev, self.lens_dev, self.max_ctx,
+                                 self.w.attn_scale, self.out, self.ws, num_splits=self.splits)
+
+    def step(self, i):
+        self.prefill(i)
+        self.decode(i)
 
 
 def _graph(fn, n):
@@ -160,34 +169,36 @@ def _time_replays(g, reps):
 
 
 def time_steps(S, steps, warmup):
-    """Each step = append + decode on the next pool copy. The steps of one pass over the
-    copies are captured in a HIP graph; K = reps * copies steps are timed between
-    synchronizations. Decode-only and append-only graphs give each kernel's mean time."""
+    """Each step = (prefill append) + fused append/decode on the next pool copy. The steps
+    of one pass over the copies are captured in a HIP graph; K = reps * copies steps are
+    timed between synchronizations. A decode-only graph gives the fused kernel's mean
+    time, a prefill-only graph the prefill append's (mixed serving)."""
     import torch
     n = len(S.pools)
     for i in range(warmup):
-        S.append(i)
-        S.decode(i)
+        S.step(i)
     torch.cuda.synchronize()
     eager = S.out.clone()
-    g_step = _graph(lambda i: (S.append(i), S.decode(i)), n)
-    g_dec = _graph(S.decode, n)
-    g_app = _graph(S.append, n)
+    graphs = [_graph(S.step, n), _graph(S.decode, n)]
+    if S.k_pre is not None:
+        graphs.append(_graph(S.prefill, n))
     reps = max(1, -(-steps // n))
-    for g in (g_step, g_dec, g_app):
+    for g in graphs[:2]:
         g.replay()
-    torch.cuda.synchronize()
-    if not torch.equal(S.out, eager):
-        raise RuntimeError("graph replay output differs from the eager decode")
-    for g in (g_step, g_dec, g_app):  # untimed replays: clocks and caches settle
-        for _ in range(3):
-            g.replay()
-    torch.cuda.synchronize()
-    ev_ms, wall = _time_replays(g_step, reps)
-    dec_ms, _ = _time_replays(g_dec, reps)
-    app_ms, _ = _time_replays(g_app, reps)
+        torch.cuda.synchronize()
+        if not torch.equal(S.out, eager):
+            raise RuntimeError("graph replay output differs from the eager step")
+    for g in graphs:  # untimed replays, ~0.3 s each: clocks ramp up and settle
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            for _ in range(20):
+                g.replay()
+            torch.cuda.synchronize()
+    ev_ms, wall = _time_replays(graphs[0], reps)
+    dec_ms, _ = _time_replays(graphs[1], reps)
+    pre_ms = _time_replays(graphs[2], reps)[0] if len(graphs) > 2 else 0.0
     K = reps * n
-    return K, wall / K * 1e3, ev_ms / K, dec_ms / K * 1e3, app_ms / K * 1e3
+    return K, wall / K * 1e3, ev_ms / K, dec_ms / K * 1e3, pre_ms / K * 1e3
 
 
 def fp16_baseline(S, steps, warmup, dev):
@@ -222,7 +233,7 @@ def fp16_baseline(S, steps, warmup, dev):
 
 
 KERNEL_SOURCES = ("int4_compressed_domain_amd/csrc/decode.hip", "int4_compressed_domain_amd/csrc/tq_device.h",
-                  "int4_compressed_domain_amd/csrc/tq_internal.h")
+                  "int4_compressed_domain_amd/csrc/tq_internal.h", "int4_compressed_domain_amd/csrc/tq_codec.h")
 
 
 def kernel_source_hash():
@@ -303,12 +314,11 @@ def main():
     S = Setup(w, args, dev)
     if args.profile:
         for i in range(args.profile):
-            S.append(i)
-            S.decode(i)
+            S.step(i)
         torch.cuda.synchronize()
         log("profile mode: %d eager steps done" % args.profile)
         return
-    K, ms, ev_ms, dec_mean, app_mean = time_steps(S, args.steps, args.warmup)
+    K, ms, ev_ms, dec_mean, pre_mean = time_steps(S, args.steps, args.warmup)
     value = S.alg_bytes / (ms * 1e-3) / 1e9
     achieved = S.alg_bytes / (dec_mean * 1e-6) / 1e9
     rec = {
@@ -322,7 +332,7 @@ def main():
                    "k_codec": ["absmax", "lloydmax"][w.k_codec], "v_codec": "absmax",
                    "kv_input": w.dtype, "attn_scale": w.attn_scale, "splits": args.splits},
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
-        "decode_us": round(dec_mean, 3), "append_us": round(app_mean, 3),
+        "decode_us": round(dec_mean, 3), "prefill_append_us": round(pre_mean, 3),
         "step_us": round(ms * 1e3, 3), "step_us_events": round(ev_ms * 1e3, 3),
         "us_per_token": round(ms * 1e3 / max(1, w.batch), 3),
         "algorithmic_bytes": S.alg_bytes, "new_tokens_per_step": S.n_new,

@@ -110,7 +110,9 @@ size_t tq_page_bytes(const tq_layout* layout);
 int tq_kv_append(const tq_layout* layout, void* pool, const void* k, const void* v,
                  int32_t in_dtype, int32_t n_tokens, const int64_t* slot_mapping, void* stream);
 
-/* Workspace bytes tq_decode_attn needs for this batch and maximum context length.
+/* Workspace bytes tq_decode_attn needs for this batch and maximum context length:
+ * TQ_DECODE_COUNTER_BYTES of counters, the split partials (batch * num_q_heads * splits *
+ * (head_dim + 2) floats) and the workgroup order (batch * num_kv_heads int32).
  * num_splits: 0 picks the split count automatically (as tq_decode_attn does); > 0 asks
  * for that many splits of the context (clamped to the number of pages). Returns 0 for
  * invalid arguments. */
@@ -132,6 +134,9 @@ size_t tq_decode_workspace_size(const tq_layout* layout, int32_t batch, int32_t 
  *                   otherwise). Its first TQ_DECODE_COUNTER_BYTES must be zero before the
  *                   first call (a zero-filled allocation); the rest is overwritten freely.
  *                   Two calls that run at the same time must not share a workspace.
+ * When the grid is larger than the GPU holds at once (batch * num_kv_heads * splits above
+ * the compute-unit count) and batch <= 256, a one-workgroup kernel first ranks the
+ * sequences by context_lens and the decode workgroups take them longest first.
  * [Open-TQ-Metal, arXiv abstract: attention directly on the compressed representation] */
 int tq_decode_attn(const tq_layout* layout, const void* pool, const void* q, int32_t q_dtype,
                    int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
@@ -141,7 +146,7 @@ int tq_decode_attn(const tq_layout* layout, const void* pool, const void* q, int
 
 /* Append the newest token of every sequence, then decode: the same result as
  *   tq_kv_append(k_last, v_last, slots = position context_lens[b] - 1 of each sequence)
- *   followed by tq_decode_attn(...), in one launch. The token of sequence b is the last one
+ *   followed by tq_decode_attn(...), in one decode launch. The token of sequence b is the last one
  *   it attends to (position context_lens[b] - 1, in the page block_table[b][(len - 1) / 16]);
  *   sequences with context_lens[b] == 0 append nothing.
  *   pool            device, written at those slots (and read as in tq_decode_attn)

@@ -106,20 +106,6 @@ __device__ __forceinline__ void wait_pages_in_flight(int k) {
   }
 }
 
-// Value of lane ^ st (st = 1, 2, 4, 8: inside a row of 16 lanes) by DPP, no LDS round trip.
-template <int ST>
-__device__ __forceinline__ float dpp_xor(float x, int lane) {
-  const int v = __float_as_int(x);
-  if constexpr (ST == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, true));  // quad_perm 1 0 3 2
-  else if constexpr (ST == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, true));  // quad_perm 2 3 0 1
-  else if constexpr (ST == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, true));  // row_ror 8
-  else {  // ST == 4 (row_ror n: lane i reads lane i - n mod 16): i + 4 is row_ror 12, i - 4 row_ror 4
-    const int from_up = __builtin_amdgcn_mov_dpp(v, 0x12C, 0xf, 0xf, true);
-    const int from_dn = __builtin_amdgcn_mov_dpp(v, 0x124, 0xf, 0xf, true);
-    return __int_as_float((lane & 4) ? from_dn : from_up);
-  }
-}
-
 // One butterfly stage across lanes: lane with bit st clear keeps x + partner, the other
 // partner - x (its own value is the upper element of the pair).
 template <int ST>
@@ -196,8 +182,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int U = a.B * a.Hkv;
   const int n8 = (U + 7) >> 3;
   const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
-  const int u = xcd + 8 * (kk % n8), s = kk / n8;
+  int u = xcd + 8 * (kk % n8);
+  const int s = kk / n8;
   if (u >= U) return;
+  if (a.order) u = a.order[u];  // longest-first order (see lpt_order_kernel)
   const int b = u / a.Hkv, h = u - b * a.Hkv;
   const int r = a.Hq / a.Hkv;
   const int L = a.context_lens[b];
@@ -220,6 +208,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   __shared__ float mml[NW][8][2];              // per-wave (m, l), then per-wave weights
   __shared__ float hml[8][2];                  // per head: max M and sum l of the workgroup
   __shared__ int last_flag;
+  __shared__ int lead_n;                       // furthest page-loop step reached by a wave
   static_assert(NW >= 8, "one wave per query head in the rotations");
   // Aliases of the ring: the query operands live in the last slot of every wave until the
   // page loop starts; after the loop, the per-wave results and the final-merge weights.
@@ -297,6 +286,13 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       if (pp < p1) stage_page<D>(page_blk(k), slot_lds(k), lane);
     }
   };
+  if (app && wv == wc && lane < 32) {  // quantize the appended token before this wave's
+    uint32_t un[E];                     // first page loads, which may wait for queue space
+    f16 scn;
+    if (lane >= 16 || KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, swnew, lane & 15, un, scn);
+    else codec_vector<D, TQ_CODEC_LLOYDMAX>(ynew, swnew, lane & 15, un, scn);
+    place_vector<D>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
+  }
   if (wv >= r) stage_first();
 
   // ---- prologue: rotate, scale, power-of-two prescale per head ----------------------------
@@ -333,13 +329,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     if (lane == 0) qdown[wv] = ldexpf(1.0f, KSUB ? 24 - sh : -sh);
     stage_first();
   }
-  if (app && wv == wc && lane < 32) {
-    uint32_t un[E];
-    f16 scn;
-    if (lane >= 16 || KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, swnew, lane & 15, un, scn);
-    else codec_vector<D, TQ_CODEC_LLOYDMAX>(ynew, swnew, lane & 15, un, scn);
-    place_vector<D>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
-  }
+  if (tid == 0) lead_n = 0;
   __syncthreads();
   const bool live = hl < r;
   const bool hiLane = hr < 8;  // lanes 0..7 of a row finish page A of each step, 8..15 page B
@@ -527,8 +517,20 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // first steps (at most 4 issues per step) instead of in one burst that would stall the
   // prologue behind a full memory queue.
   int nis = min(npw, 2);
+  const bool balance = npw >= 32;
 #pragma unroll 1
   for (int na = 0; na < npw; na += 2) {
+    // Keep the waves abreast on long loops. The hardware lets the oldest waves issue first,
+    // so the youngest ones otherwise finish last, alone on their SIMDs and with too few
+    // pages in flight. A wave that lags the furthest one takes issue priority.
+    if (balance) {
+      int lead = 0;
+      if (lane == 0) lead = atomicMax(&lead_n, na);
+      const int lag = __builtin_amdgcn_readfirstlane(lead) - na;
+      if (lag >= 4) __builtin_amdgcn_s_setprio(3);
+      else if (lag >= 2) __builtin_amdgcn_s_setprio(2);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     const int nmax = min(npw, na + NSLOT);  // the slots of pages < na are free again
 #pragma unroll
     for (int k = 0; k < 4; k++)
@@ -546,6 +548,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     step(ring[na % NSLOT][wv], ring[(na + 1) % NSLOT][wv], pa, pa + NW);
   }
 
+  __builtin_amdgcn_s_setprio(0);
   if (app && wv == wc)  // the appended token goes to the pool too, for later calls
     copy_token(const_cast<uint8_t*>(a.pool) + ((int64_t)__builtin_amdgcn_readfirstlane(bt[plast]) * a.Hkv + h) * BB, false);
 
@@ -724,8 +727,36 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   }
 }
 
+// Longest-first order of the units (b, h), for grids larger than the chip holds at once,
+// where a long sequence whose workgroups start last would finish alone: position p takes
+// head p % Hkv of the sequence ranked p / Hkv by context length (longest first, ties by
+// index). Positions keep the XCD placement of the decode grid.
+__global__ __launch_bounds__(256) void lpt_order_kernel(const int32_t* __restrict__ lens, int B,
+                                                        int Hkv, int32_t* __restrict__ order) {
+  __shared__ int lens_s[TQ_LPT_MAX_BATCH];
+  __shared__ int seq_of_rank[TQ_LPT_MAX_BATCH];
+  const int t = threadIdx.x;
+  if (t < B) lens_s[t] = lens[t];
+  __syncthreads();
+  if (t < B) {
+    const int lt = lens_s[t];
+    int rank = 0;
+    for (int j = 0; j < B; j++) {
+      const int lj = lens_s[j];
+      rank += (lj > lt || (lj == lt && j < t)) ? 1 : 0;
+    }
+    seq_of_rank[rank] = t;
+  }
+  __syncthreads();
+  for (int p = t; p < B * Hkv; p += 256) order[p] = seq_of_rank[p / Hkv] * Hkv + p % Hkv;
+}
+
 template <int D, typename TQ, int NW>
 hipError_t launch_dq(const LaunchDecode& a, hipStream_t st) {
+  if (a.order) {
+    if (a.B > TQ_LPT_MAX_BATCH) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lpt_order_kernel, dim3(1), dim3(256), 0, st, a.context_lens, a.B, a.Hkv, a.order);
+  }
   const int U = a.B * a.Hkv;
   const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * a.splits);
   if (a.k_codec == TQ_CODEC_LLOYDMAX)

@@ -95,7 +95,8 @@ size_t workspace_bytes(const tq_layout* L, int B, int max_ctx, int requested) {
   const Split f = choose_split(B, L->num_kv_heads, L->head_dim, max_ctx, requested);
   const Split d = choose_split_dense(B, L->num_kv_heads, max_ctx, requested);
   const int S = f.splits > d.splits ? f.splits : d.splits;
-  return TQ_DECODE_COUNTER_BYTES + partial_bytes(B, L->num_q_heads, L->head_dim, S);
+  return TQ_DECODE_COUNTER_BYTES + partial_bytes(B, L->num_q_heads, L->head_dim, S) +
+         (size_t)B * L->num_kv_heads * sizeof(int32_t);  // + the workgroup order
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EDEVICE; }
@@ -186,6 +187,11 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   a.splits = s.splits; a.pages_per_split = s.pages_per_split;
   a.attn_scale = attn_scale;
   a.knew = knew; a.vnew = vnew; a.new_dtype = new_dtype;
+  // longest-first order pays when the workgroups do not all fit on the chip at once
+  const int64_t resident = (int64_t)num_cus() * (L->head_dim >= 256 ? 2 : 1);
+  if (batch > 1 && batch <= TQ_LPT_MAX_BATCH && (int64_t)batch * L->num_kv_heads * s.splits > resident)
+    a.order = reinterpret_cast<int32_t*>(
+        a.part_ml + (size_t)batch * L->num_q_heads * s.splits * 2);
   return from_hip(tq_launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -5,8 +5,8 @@
 //
 // Work split: 16 lanes per vector, each lane holding E = D/16 consecutive coordinates.
 // The butterfly runs stride 1..E/2 inside a lane and stride E..D/2 across lanes (lane
-// xor), in ascending order, so every fp32 add/sub pairs the same operands as the plain
-// definition. No multiply may fuse into an add here (contraction is switched off in these
+// xor by DPP, so the 16 lanes must be one aligned row), in ascending order, so every fp32
+// add/sub pairs the same operands as the plain definition. No multiply may fuse into an add here (contraction is switched off in these
 // functions), so codes are bit-identical to a sequential implementation.
 #pragma once
 #include "tq_device.h"
@@ -53,7 +53,7 @@ __device__ __forceinline__ void codec_vector(float (&y)[D / 16], uint32_t sw, in
     const bool upper = (lane16 & m) != 0;
 #pragma unroll
     for (int e = 0; e < E; e++) {
-      float o = __shfl_xor(y[e], m, 16);
+      float o = lane_xor16(y[e], m, lane16);
       y[e] = upper ? (o - y[e]) : (y[e] + o);
     }
   }
@@ -67,7 +67,7 @@ __device__ __forceinline__ void codec_vector(float (&y)[D / 16], uint32_t sw, in
 #pragma unroll
     for (int e = 0; e < E; e++) a = fmaxf(a, fabsf(y[e]));
 #pragma unroll
-    for (int m = 1; m < LPG; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, 16));
+    for (int m = 1; m < LPG; m <<= 1) a = fmaxf(a, lane_xor16(a, m, lane16));
     scale = f16_sat(a / 7.0f);
     const float sf = (float)scale;
 #pragma unroll
@@ -85,7 +85,7 @@ __device__ __forceinline__ void codec_vector(float (&y)[D / 16], uint32_t sw, in
     for (int off = 16; off >= 1; off >>= 1) {
       if (off >= E) {
 #pragma unroll
-        for (int e = 0; e < E; e++) t[e] = t[e] + __shfl_xor(t[e], off / E, 16);
+        for (int e = 0; e < E; e++) t[e] = t[e] + lane_xor16(t[e], off / E, lane16);
       } else {
 #pragma unroll
         for (int e = 0; e < E; e++)

@@ -74,6 +74,30 @@ __device__ __forceinline__ float dpp_ror8(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, true));
 }
 
+// Value of lane ^ st (st = 1, 2, 4, 8: inside a row of 16 lanes) by DPP, no LDS round trip.
+template <int ST>
+__device__ __forceinline__ float dpp_xor(float x, int lane) {
+  const int v = __float_as_int(x);
+  if constexpr (ST == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, true));  // quad_perm 1 0 3 2
+  else if constexpr (ST == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, true));  // quad_perm 2 3 0 1
+  else if constexpr (ST == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, true));  // row_ror 8
+  else {  // ST == 4 (row_ror n: lane i reads lane i - n mod 16): i + 4 is row_ror 12, i - 4 row_ror 4
+    const int from_up = __builtin_amdgcn_mov_dpp(v, 0x12C, 0xf, 0xf, true);
+    const int from_dn = __builtin_amdgcn_mov_dpp(v, 0x124, 0xf, 0xf, true);
+    return __int_as_float((lane & 4) ? from_dn : from_up);
+  }
+}
+
+// lane ^ m for a run-time-constant m in {1, 2, 4, 8} (folds once loops are unrolled)
+__device__ __forceinline__ float lane_xor16(float x, int m, int lane) {
+  switch (m) {
+    case 1: return dpp_xor<1>(x, lane);
+    case 2: return dpp_xor<2>(x, lane);
+    case 4: return dpp_xor<4>(x, lane);
+    default: return dpp_xor<8>(x, lane);
+  }
+}
+
 // max of floats without the canonicalizing v_max x,x that fmaxf adds under IEEE mode
 // (the inputs here are never signaling NaNs).
 __device__ __forceinline__ float vmax3(float a, float b, float c) {

@@ -31,6 +31,7 @@ struct LaunchDecode {
   const void* knew;          // optional: K and V of each sequence's last token,
   const void* vnew;          //   [B][Hkv][D] of new_dtype, appended before attending
   int new_dtype;
+  int32_t* order;            // optional [B * Hkv]: the unit that workgroup position u takes
 };
 
 hipError_t tq_launch_append(const LaunchAppend& a, hipStream_t st);
@@ -54,4 +55,5 @@ constexpr int tq_decode_waves(int D) { return D > 128 ? 8 : 16; }
 constexpr int TQ_DECODE_WAVES = 4;   // dense baseline workgroups
 constexpr int TQ_MAX_SPLITS = 128;   // context splits per (sequence, kv head)
 constexpr int TQ_MAX_SPLIT_PAGES = 2048;  // pages per split (their ids are staged in LDS)
+constexpr int TQ_LPT_MAX_BATCH = 256;    // longest-first workgroup order up to this batch
 constexpr int TQ_MAX_UNITS = 1 << 20;  // sequences x kv heads per call

@@ -101,6 +101,36 @@ def test_ragged_edge_lengths(k_codec):
     assert np.all(out[0] == 0.0), "an empty sequence must give a zero output"
 
 
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_many_ragged_sequences(num_splits):
+    """More workgroups than the chip holds at once (40 sequences x 8 kv heads): workgroups
+    take sequences longest first. Ties, empty and one-token sequences included."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 400, 40)
+    lens[[3, 9, 20]] = 0
+    lens[[4, 5, 6]] = 257          # ties
+    lens[7] = 1
+    lens[8] = 512
+    w = W.Workload("many", len(lens), 16, 8, 128, int(lens.max()), "bf16", 0.125,
+                   k_codec=1, ragged_min=1)
+    _say("case many ragged sequences, splits", num_splits)
+    c = Case(w, seed=8, lens=lens)
+    c.fill()
+    out = _check_case(c, num_splits=num_splits)
+    assert np.all(out[[3, 9, 20]] == 0.0)
+
+
+def test_batch_beyond_longest_first_limit():
+    """Batch 300 (past the longest-first limit): plain workgroup order."""
+    rng = np.random.default_rng(78)
+    lens = rng.integers(0, 40, 300)
+    w = W.Workload("wide", len(lens), 4, 2, 64, int(lens.max()), "f32", 0.125, ragged_min=1)
+    _say("case batch 300")
+    c = Case(w, seed=9, lens=lens)
+    c.fill()
+    _check_case(c)
+
+
 @pytest.mark.parametrize("q_dtype", ["f32", "f16"])
 def test_query_dtypes(q_dtype):
     w = W.WORKLOADS["llama8b_b16_8k"].scaled(context=200, batch=2)
