@@ -209,14 +209,18 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   __shared__ float hml[8][2];                  // per head: max M and sum l of the workgroup
   __shared__ int last_flag;
   __shared__ int lead_n;                       // furthest page-loop step reached by a wave
+  __shared__ uint32_t sgn_s[D / 32];           // sigma bits, read once for the final un-rotation
   static_assert(NW >= 8, "one wave per query head in the rotations");
   // Aliases of the ring: the query operands live in the last slot of every wave until the
   // page loop starts; after the loop, the per-wave results and the final-merge weights.
   static_assert(G * 64 * 8 * 2 <= NW * C::SLOT, "query operands must fit one ring slot row");
-  static_assert(NW * 8 * D * 4 + 8 * TQ_MAX_SPLITS * 4 <= NSLOT * NW * C::SLOT, "merge area must fit the ring");
+  // per-wave results: rows of D + 4 floats, so the 8 heads' rows written by one store
+  // instruction start in different LDS banks
+  constexpr int MOW = D + 4;
+  static_assert(NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4 <= NSLOT * NW * C::SLOT, "merge area must fit the ring");
   f16 (*bqs)[64][8] = reinterpret_cast<f16 (*)[64][8]>(&ring[NSLOT - 1][0][0]);
-  float (*mo)[8][D] = reinterpret_cast<float (*)[8][D]>(&ring[0][0][0]);
-  float (*wsh)[TQ_MAX_SPLITS] = reinterpret_cast<float (*)[TQ_MAX_SPLITS]>(&ring[0][0][0] + NW * 8 * D * 4);
+  float (*mo)[8][MOW] = reinterpret_cast<float (*)[8][MOW]>(&ring[0][0][0]);
+  float (*wsh)[TQ_MAX_SPLITS] = reinterpret_cast<float (*)[TQ_MAX_SPLITS]>(&ring[0][0][0] + NW * 8 * MOW * 4);
 
   // ---- page ids of this split and this wave's query head, loaded together ------------------
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
@@ -266,6 +270,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     for (int e = 0; e < E; e++) asm volatile("" ::"v"(ynew[e]));  // before any page load
     asm volatile("" ::"v"(swnew));
   }
+  if (tid < D / 32) sgn_s[tid] = a.sign_bits[tid];
   const TQ* qb = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
   float qv[V];
   if (wv < r) {  // wave w rotates query head w: sign flip now, butterflies below
@@ -722,7 +727,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     for (int k = 0; k < V; k++) {
       const int d = lane + 64 * k;
       const float y = x[k] * rho;
-      outp[wv * D + d] = ((a.sign_bits[d >> 5] >> (d & 31)) & 1u) ? -y : y;
+      outp[wv * D + d] = ((sgn_s[d >> 5] >> (d & 31)) & 1u) ? -y : y;
     }
   }
 }
