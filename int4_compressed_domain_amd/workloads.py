@@ -6,7 +6,7 @@ CPU oracle can take their inputs from it. Every array comes from numpy's PCG64
 (``default_rng``) with a seed derived from (seed, purpose, sequence), so a sequence's
 tokens do not depend on how the caller chunks the generation.
 
-Five workloads, named by what they are:
+Six workloads, named by what they are:
 
   single_head_1k     1 head, D=128, 1024 cached tokens, fp32, N(0,1) with 4 outlier
                      channels x20 on K and V (q not scaled)
@@ -19,6 +19,9 @@ Five workloads, named by what they are:
   mixed_serving      prefill chunk of 2048 tokens appended to 128 fresh pages, then a
                      decode batch of 64 with contexts uniform in [1024, 32768]; 32 q / 8 kv
                      heads, D=128, keys by the LUT codec, values by abs-max
+  llama70b_b1_128k_k16v4
+                     the 128K workload with keys kept in fp16 and values in 4 bits (the
+                     asymmetric mode)
 
 Each step of a workload appends one new token per decoding sequence (its last token;
 the other L_b - 1 tokens are the resident cache) plus, for mixed_serving, the 2048-token
@@ -33,6 +36,7 @@ PAGE = 16
 
 CODEC_ABSMAX = 0
 CODEC_LUT = 1
+CODEC_FP16 = 2   # keys only: kept in fp16 (values stay 4-bit)
 
 
 @dataclass(frozen=True)
@@ -76,6 +80,9 @@ WORKLOADS = {
     "mixed_serving": Workload("mixed_serving", 64, 32, 8, 128, 32768, "bf16",
                               1.0 / math.sqrt(128), k_codec=CODEC_LUT, ragged_min=1024,
                               prefill=2048),
+    "llama70b_b1_128k_k16v4": Workload("llama70b_b1_128k_k16v4", 1, 64, 8, 128, 131072, "bf16",
+                                       1.0 / math.sqrt(128), k_codec=CODEC_FP16,
+                                       dist="lognormal_spikes"),
 }
 
 HEADLINE = "llama70b_b1_128k"
@@ -180,8 +187,12 @@ def slots_for(bt, b, t0, t1):
 
 def algorithmic_bytes(w: Workload, lens):
     """Packed K+V indices and fp16 scales read by one decode: sum_b L_b * Hkv * 2 *
-    (D/2 + 2*D/32), plus the query and the fp32 output."""
+    (D/2 + 2*D/32) (fp16 keys: L_b * Hkv * (2D + D/2 + 2*D/32)), plus the query and the
+    fp32 output."""
     D = w.head_dim
-    per_tok = w.kv_heads * 2 * (D // 2 + 2 * (D // 32))
+    if w.k_codec == CODEC_FP16:
+        per_tok = w.kv_heads * (2 * D + D // 2 + 2 * (D // 32))
+    else:
+        per_tok = w.kv_heads * 2 * (D // 2 + 2 * (D // 32))
     qbytes = w.batch * w.q_heads * D * (4 if w.dtype == "f32" else 2)
     return int(np.sum(lens, dtype=np.int64)) * per_tok + qbytes + w.batch * w.q_heads * D * 4

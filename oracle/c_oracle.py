@@ -56,6 +56,11 @@ def lib():
         L.or_attention_f64.argtypes = [P, P, P, i64, i32, f64, P]
         L.or_decode.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, P, P, ctypes.c_float, P, i32, P]
         L.or_dequant.argtypes = [P, i32, i32, i32, i32, P, P, i32, P, i32, i32, i32, P, P]
+        L.or_block_bytes_kc.argtypes = [i32, i32]
+        L.or_block_bytes_kc.restype = i64
+        L.or_keys_f16.argtypes = [P, i64, P]
+        L.or_place_kf16.argtypes = [P, i32, i32, i64, P, P, P, P]
+        L.or_fetch_kf16.argtypes = [P, i32, i32, i64, i32, i32, P, P, P]
         _lib = L
     return _lib
 
@@ -143,12 +148,35 @@ def encode(x, sign_bits, codec=0, group=32):
     return u.reshape(x.shape[:-1] + (D,)), s.reshape(x.shape[:-1] + (D // group,))
 
 
-def block_bytes(D):
-    return int(lib().or_block_bytes(D))
+KF16 = 2  # k_codec of the fp16-key mode
 
 
-def new_pool(num_pages, Hkv, D):
-    return np.zeros(num_pages * Hkv * block_bytes(D), np.uint8)
+def block_bytes(D, k_codec=0):
+    return int(lib().or_block_bytes_kc(D, k_codec))
+
+
+def new_pool(num_pages, Hkv, D, k_codec=0):
+    return np.zeros(num_pages * Hkv * block_bytes(D, k_codec), np.uint8)
+
+
+def keys_f16(k):
+    """fp16 bits (round to nearest even, overflow saturated) of fp32 keys, any shape."""
+    k = _c(k, np.float32)
+    out = np.empty(k.shape, np.uint16)
+    lib().or_keys_f16(_p(k), k.size, _p(out))
+    return out
+
+
+def place_kf16(pool, D, Hkv, slots, kh, vu, vs):
+    slots = _c(slots, np.int64)
+    lib().or_place_kf16(_p(pool), D, Hkv, slots.shape[0], _p(slots), _p(_c(kh, np.uint16)),
+                        _p(_c(vu, np.uint8)), _p(_c(vs, np.uint16)))
+
+
+def fetch_kf16(pool, D, Hkv, page, t, h):
+    kh, vu, vs = np.empty(D, np.uint16), np.empty(D, np.uint8), np.empty(D // 32, np.uint16)
+    lib().or_fetch_kf16(_p(pool), D, Hkv, page, t, h, _p(kh), _p(vu), _p(vs))
+    return kh, vu, vs
 
 
 def place(pool, D, Hkv, slots, ku, ks, vu, vs):

@@ -10,7 +10,10 @@ sharing any code with it, so that the two can be compared byte for byte:
   * LUT int4 for keys ["TurboQuant on AMD GPUs", section 2: rotation + LUT] - Lloyd-Max
     N(0,1) centroids / sqrt(32) in fp16 times the fp16 group L2 norm;
   * attention in fp64 on the dequantized rotated values [Open-TQ-Metal, arXiv abstract],
-    then the fp64 inverse rotation.
+    then the fp64 inverse rotation;
+  * fp16 keys (k_codec 2) [mlxcel "TurboQuant KV cache" manual, cache-mode table: keys in
+    fp16, values in the 4-bit rotated form] - fp16(k) of the original key, saturated; the
+    scores use the query as given (no rotation), the values are as above.
 
 numpy's float32 arithmetic is IEEE single precision and its float16 casts round to
 nearest even with subnormals, which is what the readings ask for.
@@ -185,7 +188,12 @@ def dequant_values(u, s16, codec=0, lut=None, group=GROUP):
 # V index of (t = 4j + e, d): column c = d//2 = 16g + m, byte 8D + (16j + m)*4G + 4g + e,
 #   high nibble iff d odd.
 
-def block_bytes(D):
+KF16 = 2
+
+
+def block_bytes(D, k_codec=0):
+    if k_codec == KF16:
+        return 41 * D          # [K fp16 32D][V indices 8D][V scales 16 x G fp16]
     return 16 * D + 64 * (D // 32)
 
 
@@ -207,8 +215,53 @@ def _v_index(D):
     return 8 * D + (16 * j + m) * 4 * G + 4 * g + e, np.broadcast_to(d % 2, (PAGE, D))
 
 
-def new_pool(num_pages, Hkv, D):
-    return np.zeros(num_pages * Hkv * block_bytes(D), np.uint8)
+def _kf16_index(D):
+    """fp16-key block: byte of K (t, d = 32g + 8j + e) is 1024g + 16(16j + t) + 2e."""
+    d = np.arange(D)
+    t = np.arange(PAGE)[:, None]
+    g, j, e = d // 32, (d % 32) // 8, d % 8
+    return 1024 * g + 16 * (16 * j + t) + 2 * e
+
+
+def new_pool(num_pages, Hkv, D, k_codec=0):
+    return np.zeros(num_pages * Hkv * block_bytes(D, k_codec), np.uint8)
+
+
+def place_kf16(pool, D, Hkv, slots, kh, vu, vs):
+    """fp16-key pool: kh [n, Hkv, D] fp16 keys, V indices and scales as in place()."""
+    G = D // 32
+    bb = block_bytes(D, KF16)
+    kb = _kf16_index(D)
+    vb, vh = _v_index(D)
+    vb = vb + 24 * D           # the V region starts at 32D instead of 8D
+    blocks = pool.reshape(-1, Hkv, bb)
+    for i, slot in enumerate(np.asarray(slots, np.int64)):
+        if slot < 0:
+            continue
+        page, t = divmod(int(slot), PAGE)
+        for h in range(Hkv):
+            blk = blocks[page, h]
+            kbytes = np.asarray(kh[i, h], np.float16).view(np.uint8)
+            blk[kb[t]] = kbytes[0::2]
+            blk[kb[t] + 1] = kbytes[1::2]
+            u = np.asarray(vu[i, h], np.uint8)
+            lo_sel, hi_sel = vh[t] == 0, vh[t] == 1
+            blk[vb[t][lo_sel]] = (blk[vb[t][lo_sel]] & 0xF0) | u[lo_sel]
+            blk[vb[t][hi_sel]] = (blk[vb[t][hi_sel]] & 0x0F) | (u[hi_sel] << 4)
+            blk[40 * D + 2 * G * t:40 * D + 2 * G * (t + 1)] = np.asarray(vs[i, h], np.float16).view(np.uint8)
+
+
+def fetch_block_kf16(pool, D, Hkv, page, h):
+    """fp16 keys [16, D], V indices [16, D] and V scales [16, G] of one fp16-key block."""
+    G = D // 32
+    blk = pool.reshape(-1, Hkv, block_bytes(D, KF16))[page, h]
+    kb = _kf16_index(D)
+    vb, vh = _v_index(D)
+    vb = vb + 24 * D
+    k = (blk[kb].astype(np.uint16) | (blk[kb + 1].astype(np.uint16) << 8)).view(np.float16)
+    vu = np.where(vh == 1, blk[vb] >> 4, blk[vb] & 0x0F).astype(np.uint8)
+    vs = blk[40 * D:40 * D + 32 * G].copy().view(np.float16).reshape(PAGE, G)
+    return k, vu, vs
 
 
 def place(pool, D, Hkv, slots, ku, ks, vu, vs):
@@ -236,8 +289,11 @@ def place(pool, D, Hkv, slots, ku, ks, vu, vs):
 
 
 def append(pool, D, Hkv, k, v, slots, sign_bits, k_codec=0, v_codec=0):
-    ku, ks = encode(k, sign_bits, k_codec)
     vu, vs = encode(v, sign_bits, v_codec)
+    if k_codec == KF16:
+        place_kf16(pool, D, Hkv, slots, to_f16_sat(np.asarray(k, F32)), vu, vs)
+        return
+    ku, ks = encode(k, sign_bits, k_codec)
     place(pool, D, Hkv, slots, ku, ks, vu, vs)
 
 
@@ -255,13 +311,18 @@ def fetch_block(pool, D, Hkv, page, h):
 
 
 def gather(pool, D, Hkv, block_table, L, b, h, k_codec=0, v_codec=0):
-    """Dequantized K, V (fp64, rotated basis) of the first L tokens of sequence b, head h."""
+    """Dequantized K, V (fp64; rotated basis, fp16 keys as stored) of the first L tokens of
+    sequence b, head h."""
     npg = -(-L // PAGE)
     ks_, vs_ = [], []
     lut = lut16()
     for p in range(npg):
-        ku, ks, vu, vs = fetch_block(pool, D, Hkv, int(block_table[b][p]), h)
-        ks_.append(dequant_values(ku, ks, k_codec, lut))
+        if k_codec == KF16:
+            k16, vu, vs = fetch_block_kf16(pool, D, Hkv, int(block_table[b][p]), h)
+            ks_.append(k16.astype(np.float64))
+        else:
+            ku, ks, vu, vs = fetch_block(pool, D, Hkv, int(block_table[b][p]), h)
+            ks_.append(dequant_values(ku, ks, k_codec, lut))
         vs_.append(dequant_values(vu, vs, v_codec, lut))
     if npg == 0:
         return np.zeros((0, D)), np.zeros((0, D))
@@ -287,7 +348,10 @@ def decode(pool, D, Hq, Hkv, sign_bits, block_table, context_lens, q, alpha, k_c
         for h in range(Hkv):
             K, V = gather(pool, D, Hkv, block_table, int(context_lens[b]), b, h, k_codec, v_codec)
             for hq in range(h * r, (h + 1) * r):
-                qr = rotate(q[b, hq], sign_bits).astype(np.float64)
+                if k_codec == KF16:   # fp16 keys stay in the original basis
+                    qr = q[b, hq].astype(np.float64)
+                else:
+                    qr = rotate(q[b, hq], sign_bits).astype(np.float64)
                 o1 = attention_f64(qr, K, V, float(np.float32(alpha)))
                 out[b, hq] = unrotate_f64(o1, sign_bits)
     return out

@@ -27,6 +27,11 @@
  *  - Attention in fp64: scores alpha*q'.k^, softmax, weighted sum of v^ in the rotated
  *    basis, then the fp64 inverse rotation rho*sigma.*(H o').
  *  - Pool placement: see the header comment of each placement function below.
+ *  - fp16 keys (mlxcel "TurboQuant KV cache" manual, cache-mode table and recommended
+ *    mode: keys stay fp16, only values take the 4-bit rotated form): k_codec 2 stores
+ *    fp16_rne(k) of the original key, saturating at 65504, with no rotation; scores are
+ *    alpha * q.k in the original basis (the query is not rotated for them); values,
+ *    the weighted sum and the inverse rotation are as in the 4-bit mode.
  *
  * Build: gcc -O2 -fPIC -shared -ffp-contract=off -fno-fast-math -fopenmp (no -march).
  */
@@ -301,6 +306,62 @@ void or_place(uint8_t* pool, int D, int Hkv, int64_t n, const int64_t* slots,
   }
 }
 
+/* fp16-key blocks (k_codec 2): [K fp16 32D bytes][V indices 8D bytes][V scales 16*G fp16].
+ *  - K value of (token t, dim d), d = 32g + 8j + e: byte 1024g + 16(16j + t) + 2e
+ *    (for each group, the 16 tokens x 32 dims as four 8-dim chunks per token);
+ *  - V byte and V scale as in the 4-bit block, shifted to start at 32D and 40D. */
+#define OR_KF16 2
+
+int64_t or_block_bytes_kc(int D, int k_codec) {
+  return k_codec == OR_KF16 ? 41 * (int64_t)D : or_block_bytes(D);
+}
+static int64_t kf16_off(int t, int d) {
+  int g = d / 32, j = (d % 32) / 8, e = d % 8;
+  return 1024 * (int64_t)g + 16 * (int64_t)(16 * j + t) + 2 * e;
+}
+static int64_t kf16_v_byte(int t, int d, int D) { return v_byte(t, d, D) + 24 * (int64_t)D; }
+static int64_t kf16_vs_off(int t, int k, int D) { return 40 * (int64_t)D + 2 * (t * (D / 32) + k); }
+
+/* Keys to fp16 bits: round to nearest even (or_f64_to_f16), overflow saturated. */
+void or_keys_f16(const float* k, int64_t n, uint16_t* kh) {
+  for (int64_t i = 0; i < n; i++) kh[i] = f16_saturate(or_f64_to_f16((double)k[i]));
+}
+
+/* Store n tokens x Hkv heads into an fp16-key pool: kh [n][Hkv][D] fp16 bits, V indices
+ * and scales as for or_place. Negative slots are skipped. */
+void or_place_kf16(uint8_t* pool, int D, int Hkv, int64_t n, const int64_t* slots,
+                   const uint16_t* kh, const uint8_t* vu, const uint16_t* vs) {
+  int G = D / 32;
+  int64_t bb = or_block_bytes_kc(D, OR_KF16);
+  for (int64_t i = 0; i < n; i++) {
+    if (slots[i] < 0) continue;
+    int64_t page = slots[i] / OR_PAGE;
+    int t = (int)(slots[i] % OR_PAGE);
+    for (int h = 0; h < Hkv; h++) {
+      uint8_t* blk = pool + (page * Hkv + h) * bb;
+      const uint16_t* kx = kh + (i * Hkv + h) * D;
+      const uint8_t* vx = vu + (i * Hkv + h) * D;
+      for (int d = 0; d < D; d++) {
+        put16(blk + kf16_off(t, d), kx[d]);
+        put_nibble(blk + kf16_v_byte(t, d, D), d & 1, vx[d]);
+      }
+      for (int k = 0; k < G; k++) put16(blk + kf16_vs_off(t, k, D), vs[(i * Hkv + h) * G + k]);
+    }
+  }
+}
+
+/* Read back one token of an fp16-key pool: K fp16 bits, V indices and scales. */
+void or_fetch_kf16(const uint8_t* pool, int D, int Hkv, int64_t page, int t, int h,
+                   uint16_t* kh, uint8_t* vu, uint16_t* vs) {
+  int G = D / 32;
+  const uint8_t* blk = pool + (page * Hkv + h) * or_block_bytes_kc(D, OR_KF16);
+  for (int d = 0; d < D; d++) {
+    kh[d] = get16(blk + kf16_off(t, d));
+    vu[d] = get_nibble(blk + kf16_v_byte(t, d, D), d & 1);
+  }
+  for (int k = 0; k < G; k++) vs[k] = get16(blk + kf16_vs_off(t, k, D));
+}
+
 /* Append [one fused step per the Open-TQ-Metal card abstract]: encode K and V of n tokens
  * ([n][Hkv][D] fp32) and store them at their slots. */
 void or_append(uint8_t* pool, int D, int Hkv, int k_codec, int v_codec, const uint32_t* sign_bits,
@@ -309,11 +370,16 @@ void or_append(uint8_t* pool, int D, int Hkv, int k_codec, int v_codec, const ui
   int64_t nv = n * Hkv;
   uint8_t* ku = malloc(nv * D);
   uint8_t* vu = malloc(nv * D);
-  uint16_t* ks = malloc(nv * G * 2);
+  uint16_t* ks = malloc(nv * (k_codec == OR_KF16 ? D : G) * 2);
   uint16_t* vs = malloc(nv * G * 2);
-  or_encode(k, nv, D, OR_GROUP, sign_bits, k_codec, ku, ks);
   or_encode(v, nv, D, OR_GROUP, sign_bits, v_codec, vu, vs);
-  or_place(pool, D, Hkv, n, slots, ku, ks, vu, vs);
+  if (k_codec == OR_KF16) {  /* keys kept in fp16, original basis */
+    or_keys_f16(k, nv * D, ks);
+    or_place_kf16(pool, D, Hkv, n, slots, ks, vu, vs);
+  } else {
+    or_encode(k, nv, D, OR_GROUP, sign_bits, k_codec, ku, ks);
+    or_place(pool, D, Hkv, n, slots, ku, ks, vu, vs);
+  }
   free(ku); free(vu); free(ks); free(vs);
 }
 
@@ -357,7 +423,8 @@ void or_attention_f64(const double* q, const double* K, const double* V, int64_t
 /* Decode attention for a list of (b, hq) pairs, reading the pool through the block table.
  * q is fp32 [B][Hq][D] (already widened from its storage type); alpha is the fp32 scale the
  * caller passes, widened exactly to fp64. The query is rotated with
- * the same fp32 rotation as the keys; kv head = hq / (Hq/Hkv) [GQA, contiguous groups].
+ * the same fp32 rotation as the keys (not at all for fp16 keys, which stay in the original
+ * basis); kv head = hq / (Hq/Hkv) [GQA, contiguous groups].
  * out: fp64 [n_pairs][D], original basis. A sequence of length 0 gives zeros. */
 void or_decode(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec, int v_codec,
                const uint32_t* sign_bits, const int32_t* block_table, int max_pages,
@@ -372,19 +439,27 @@ void or_decode(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec, int v_c
     int64_t L = context_lens[b];
     float qr[512];
     double qd[512], o1[512];
-    or_rotate(q + ((int64_t)b * Hq + hq) * D, qr, D, sign_bits);
-    for (int i = 0; i < D; i++) qd[i] = (double)qr[i];
+    const float* qx = q + ((int64_t)b * Hq + hq) * D;
+    if (k_codec == OR_KF16) {  /* fp16 keys are in the original basis: q as given */
+      for (int i = 0; i < D; i++) qd[i] = (double)qx[i];
+    } else {
+      or_rotate(qx, qr, D, sign_bits);
+      for (int i = 0; i < D; i++) qd[i] = (double)qr[i];
+    }
     double* K = malloc(sizeof(double) * (L > 0 ? L : 1) * D);
     double* V = malloc(sizeof(double) * (L > 0 ? L : 1) * D);
     uint8_t ku[512], vu[512];
-    uint16_t ks[16], vs[16];
+    uint16_t ks[16], vs[16], kh[512];
     for (int64_t t = 0; t < L; t++) {
       int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
-      or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
-      for (int d = 0; d < D; d++) {
-        K[t * D + d] = dequant1(k_codec, ku[d], ks[d / 32], lut);
-        V[t * D + d] = dequant1(v_codec, vu[d], vs[d / 32], lut);
+      if (k_codec == OR_KF16) {
+        or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
+        for (int d = 0; d < D; d++) K[t * D + d] = or_f16_to_f64(kh[d]);
+      } else {
+        or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+        for (int d = 0; d < D; d++) K[t * D + d] = dequant1(k_codec, ku[d], ks[d / 32], lut);
       }
+      for (int d = 0; d < D; d++) V[t * D + d] = dequant1(v_codec, vu[d], vs[d / 32], lut);
     }
     (void)G;
     or_attention_f64(qd, K, V, L, D, (double)alpha, o1);
@@ -407,15 +482,21 @@ void or_dequant(const uint8_t* pool, int D, int Hkv, int k_codec, int v_codec,
         float* vr = vout + (((int64_t)b * Hkv + h) * Lmax + t) * D;
         if (t >= context_lens[b]) { memset(kr, 0, 4 * D); memset(vr, 0, 4 * D); continue; }
         uint8_t ku[512], vu[512];
-        uint16_t ks[16], vs[16];
+        uint16_t ks[16], vs[16], kh[512];
         int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
-        or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
         float ky[512], vy[512];
-        for (int d = 0; d < D; d++) {
-          ky[d] = (float)dequant1(k_codec, ku[d], ks[d / 32], lut);
-          vy[d] = (float)dequant1(v_codec, vu[d], vs[d / 32], lut);
+        if (k_codec == OR_KF16) {
+          or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
+          for (int d = 0; d < D; d++) ky[d] = (float)or_f16_to_f64(kh[d]);
+        } else {
+          or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+          for (int d = 0; d < D; d++) ky[d] = (float)dequant1(k_codec, ku[d], ks[d / 32], lut);
         }
-        if (basis == 0) { memcpy(kr, ky, 4 * D); memcpy(vr, vy, 4 * D); }
-        else { or_unrotate_f32(ky, kr, D, sign_bits); or_unrotate_f32(vy, vr, D, sign_bits); }
+        for (int d = 0; d < D; d++) vy[d] = (float)dequant1(v_codec, vu[d], vs[d / 32], lut);
+        /* fp16 keys have no rotated form: they are returned as stored in both bases */
+        if (basis == 0 || k_codec == OR_KF16) memcpy(kr, ky, 4 * D);
+        else or_unrotate_f32(ky, kr, D, sign_bits);
+        if (basis == 0) memcpy(vr, vy, 4 * D);
+        else or_unrotate_f32(vy, vr, D, sign_bits);
       }
 }

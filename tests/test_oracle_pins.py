@@ -302,6 +302,58 @@ def test_lossless_case_equals_plain_attention(coracle, noracle, D):
             assert np.max(np.abs(out[0, hq] - plain)) < 1e-12 * np.max(np.abs(plain))
 
 
+def _keys_f16(orc, k):
+    return orc.keys_f16(k) if hasattr(orc, "keys_f16") else orc.to_f16_sat(k).view(np.uint16)
+
+
+def test_fp16_keys_are_ieee_rne_with_saturation(orc):
+    """fp16-key mode: stored keys are IEEE binary16 round-to-nearest-even of the fp32 key
+    (numpy's cast), with overflow clamped to +-65504; subnormals and signed zeros kept."""
+    rng = np.random.default_rng(31)
+    k = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-9, 6, 4000),
+                        [70000.0, -1e9, 65504.0, 65520.0, 65519.99, 6e-8, -3e-8, 0.0, -0.0]]).astype(np.float32)
+    got = _keys_f16(orc, k)
+    with np.errstate(over="ignore"):
+        want = k.astype(np.float16)
+    want = np.where(np.isinf(want), np.copysign(np.float16(65504.0), want), want).astype(np.float16)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_fp16_keys_lossless_values_equal_plain_attention(coracle, noracle, D):
+    """fp16 keys + 4-bit values: with fp16-representable keys and values whose rotation is
+    lossless for the abs-max codec, decode equals plain softmax attention on the original
+    q, k, v (the scores use the query as given)."""
+    rng = np.random.default_rng(D + 7)
+    sb = _sb(D, 4)
+    L, Hkv, Hq = 37, 2, 6
+    k = (rng.standard_normal((L, Hkv, D)) * 3.0).astype(np.float16).astype(np.float32)
+    _, v = _exact_vectors(rng, L * Hkv, D, sb, coracle)
+    v = v.reshape(L, Hkv, D)
+    q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+    bt = np.array([[1, 3, 0]], np.int32)
+    slots = W.slots_for(bt, 0, 0, L)
+    alpha = 0.0625
+    for orc in (coracle, noracle):
+        pool = orc.new_pool(4, Hkv, D, 2)
+        orc.append(pool, D, Hkv, k, v, slots, sb, 2, 0)
+        out = orc.decode(pool, D, Hq, Hkv, sb, bt, np.array([L], np.int32), q, alpha, k_codec=2)
+        for hq in range(Hq):
+            h = hq // (Hq // Hkv)
+            s = alpha * (k[:, h].astype(np.float64) @ q[0, hq].astype(np.float64))
+            w = np.exp(s - s.max())
+            plain = (w @ v[:, h].astype(np.float64)) / w.sum()
+            assert np.max(np.abs(out[0, hq] - plain)) < 1e-12 * np.max(np.abs(plain))
+
+
+def test_fp16_key_memory_formula(coracle):
+    """fp16 keys + 4-bit values: bytes per token = (16 + 4)/(2*16) of fp16 plus the value
+    scale sidecar (one fp16 per 32 values), the mlxcel manual's memory formula."""
+    for D in (64, 128, 256):
+        per_token = coracle.block_bytes(D, 2) / 16
+        assert per_token / (2 * D * 2) == pytest.approx((16 + 4) / (2 * 16) + 16 / 32 / (2 * 16))
+
+
 def test_codec_alone_lossless_at_d128(orc):
     """D=128 has an irrational rho, so check the codec stage on pre-rotated integers."""
     rng = np.random.default_rng(5)
@@ -381,7 +433,8 @@ def test_split_softmax_merge_equals_direct(coracle):
 
 # ---- the two oracles agree ---------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["single_head_1k", "llama8b_b16_8k", "gemma_d256_32k", "mixed_serving"])
+@pytest.mark.parametrize("name", ["single_head_1k", "llama8b_b16_8k", "gemma_d256_32k", "mixed_serving",
+                                  "llama70b_b1_128k_k16v4"])
 def test_c_and_numpy_oracles_agree(coracle, noracle, name):
     w = W.WORKLOADS[name].scaled(context=45, batch=2, ragged_min=20, prefill=0)
     D, Hkv, Hq = w.head_dim, w.kv_heads, w.q_heads
@@ -390,7 +443,7 @@ def test_c_and_numpy_oracles_agree(coracle, noracle, name):
     bt, _, npages = W.page_tables(w, lens, 0)
     pools = {}
     for orc in (coracle, noracle):
-        pool = orc.new_pool(npages, Hkv, D)
+        pool = orc.new_pool(npages, Hkv, D, w.k_codec)
         for b in range(w.batch):
             k, v, _, _ = W.seq_tokens(w, b, int(lens[b]), 0)
             orc.append(pool, D, Hkv, k, v, W.slots_for(bt, b, 0, int(lens[b])), sb,
