@@ -280,7 +280,7 @@ def cpu_baseline(w):
     while nseq < w.batch and int(np.sum(lens[:nseq + 1])) * Hkv <= budget:
         nseq += 1
     nseq = max(nseq, 1)
-    opool = c_oracle.new_pool(npages, Hkv, D)
+    opool = c_oracle.new_pool(npages, Hkv, D, w.k_codec)
     scales = W.channel_scales(w, 0)
     for b in range(nseq):
         k32, v32, _, _ = W.seq_tokens(w, b, int(lens[b]), 0, scales)

@@ -9,6 +9,9 @@
  *    "TurboQuant on AMD GPUs", section 4: Walsh-Hadamard rotation].
  *  - Keys may instead use a 16-entry Gaussian Lloyd-Max table times the group's L2 norm,
  *    values uniform abs-max ["TurboQuant on AMD GPUs", section 2, TQ4/4].
+ *  - Or keys stay in fp16 and only values take the 4-bit rotated form: the asymmetric
+ *    mode the mlxcel "TurboQuant KV cache" manual recommends by default (cache-mode table,
+ *    fp16+turbo4). Keys are then stored unrotated and scored against the query as given.
  *  - Decode attention runs directly on the packed codes: the query is rotated into the
  *    cache basis, scores and the weighted value sum are computed from codes and scales,
  *    the softmax is online, and no dequantized K/V matrix is written [Open-TQ-Metal, arXiv
@@ -27,6 +30,7 @@
  *    of N(0,1) in increasing order; n = fp16_rne(sqrtf(sum of squares)) summed by the tree
  *    t_i += t_{i+off}, off = 16, 8, 4, 2, 1; u = #{j in 1..15 : y/n >= (LUT_{j-1}+LUT_j)/2},
  *    u = 8 when n = 0. Value = LUT_u * n.
+ *  - fp16 keys: k16 = fp16_rne(k) of the original key (saturating at 65504), no rotation.
  *
  * Pool format. A pool is one device buffer of num_pages * num_kv_heads * TQ_BLOCK_BYTES(D)
  * bytes, [page][kv head][block]. A block holds 16 tokens of one KV head (G = D/32):
@@ -38,6 +42,11 @@
  *     scale of token t, group g              ->  element t*G + g of its scale array
  * These orders let one 64-lane wavefront load a block's K (or V) indices with one 16-byte
  * load per lane, already in the operand order of the gfx950 matrix-core instructions.
+ * With fp16 keys (k_codec TQ_CODEC_FP16) a block is TQ_BLOCK_BYTES_KF16(D) bytes:
+ *     [K fp16: 32*D B][V indices: 8*D B][V scales: 16*G fp16]
+ *     K of token t, dim d = 32g + 8j + e     ->  byte 1024g + 16(16j + t) + 2e
+ *     V indices and scales as above, their regions starting at 32*D and 40*D
+ * (each group's 16 tokens x 32 dims are one 1 KB run, again one 16-byte load per lane).
  * A slot is page * 16 + offset within the page.
  *
  * Conventions.
@@ -50,8 +59,8 @@
  *    contents (slots, block tables, context lengths) are preconditions, not checked:
  *    out-of-range values there are undefined behaviour.
  *  - GPU support: head_dim in {64, 128, 256}, group_size 32, page_size 16,
- *    1 <= num_q_heads / num_kv_heads <= 8, batch * num_kv_heads <= 2^20
- *    (TQ_EUNSUPPORTED otherwise).
+ *    1 <= num_q_heads / num_kv_heads <= 8, batch * num_kv_heads <= 2^20; decode with fp16
+ *    keys at head_dim 64 and 128 (TQ_EUNSUPPORTED otherwise).
  */
 #ifndef TQ_H
 #define TQ_H
@@ -71,10 +80,11 @@ typedef enum {
   TQ_EDEVICE = -4        /* the HIP runtime reported an error */
 } tq_status;
 
-typedef enum { TQ_CODEC_ABSMAX = 0, TQ_CODEC_LLOYDMAX = 1 } tq_codec;
+typedef enum { TQ_CODEC_ABSMAX = 0, TQ_CODEC_LLOYDMAX = 1, TQ_CODEC_FP16 = 2 } tq_codec;
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
 #define TQ_BLOCK_BYTES(D) (16 * (D) + 64 * ((D) / 32))
+#define TQ_BLOCK_BYTES_KF16(D) (41 * (D))
 
 /* The first TQ_DECODE_COUNTER_BYTES bytes of a decode workspace hold per-(sequence,
  * kv head) arrival counters. They must be zero before the workspace is first used; every
@@ -88,7 +98,7 @@ typedef struct {
   int32_t group_size;        /* quantization group, must be 32 */
   int32_t page_size;         /* tokens per page, must be 16 */
   int32_t num_pages;         /* physical pages in the pool */
-  int32_t k_codec;           /* tq_codec for keys */
+  int32_t k_codec;           /* tq_codec for keys: ABSMAX, LLOYDMAX or FP16 */
   int32_t v_codec;           /* tq_codec for values (TQ_CODEC_ABSMAX only) */
   const uint32_t* sign_bits; /* device, D/32 words; bit i of word i/32 set => sigma_i = -1 */
 } tq_layout;
@@ -96,8 +106,8 @@ typedef struct {
 /* Human-readable name of a tq_status (static string, never NULL). */
 const char* tq_status_str(int status);
 
-/* Bytes of one physical page of the pool (all KV heads): num_kv_heads * TQ_BLOCK_BYTES(D).
- * Returns 0 for an invalid layout. */
+/* Bytes of one physical page of the pool (all KV heads): num_kv_heads * TQ_BLOCK_BYTES(D)
+ * (TQ_BLOCK_BYTES_KF16(D) with fp16 keys). Returns 0 for an invalid layout. */
 size_t tq_page_bytes(const tq_layout* layout);
 
 /* Append: rotate, quantize and store n_tokens new K and V vectors.
@@ -168,7 +178,8 @@ int tq_append_decode_attn(const tq_layout* layout, void* pool, const void* k_las
  * of out_dtype (TQ_F32 or TQ_F16), rows at or past a sequence's length set to zero.
  * to_original_basis = 0: values (u-8)*s or LUT_u*n in the rotated basis (exact products,
  * rounded once to out_dtype); 1: times R^-1 = diag(sigma) * rho * H in fp32 (same stage
- * order as the forward rotation), then rounded to out_dtype.
+ * order as the forward rotation), then rounded to out_dtype. fp16 keys have no rotated
+ * form: they are written as stored in both cases.
  * [Open-TQ-Metal, arXiv abstract: the dequantize-then-attend baseline] */
 int tq_dequant_ref(const tq_layout* layout, const void* pool, int32_t batch,
                    const int32_t* block_table, int32_t max_pages_per_seq,

@@ -15,7 +15,8 @@ __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
                                                      const uint32_t* __restrict__ sign_bits,
                                                      int n_tokens, int Hkv) {
   constexpr int E = D / 16;
-  constexpr int BB = TQ_BLOCK_BYTES(D);
+  constexpr int BB = tq_block_bytes(D, KCODEC);
+  constexpr bool KF16 = KCODEC == TQ_CODEC_FP16;
   const int lane = threadIdx.x & 15;
   const int64_t vec = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   if (vec >= (int64_t)n_tokens * Hkv * 2) return;  // whole 16-lane groups exit together
@@ -28,12 +29,17 @@ __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
 
   float y[E];
   load_widen<TIn, E>((is_v ? vin : kin) + th * D + lane * E, y);
+  uint8_t* blk = pool + ((slot >> 4) * (int64_t)Hkv + h) * BB;
+  if (KF16 && !is_v) {  // fp16 keys: stored as given, no rotation [16-lane group uniform]
+    place_key_f16<D>(blk, (int)(slot & 15), lane, y);
+    return;
+  }
   uint32_t u[E];
   f16 scale;
   const uint32_t sw = lane_signs<D>(sign_bits, lane);
-  if (is_v || KCODEC == TQ_CODEC_ABSMAX) codec_vector<D, TQ_CODEC_ABSMAX>(y, sw, lane, u, scale);
+  if (is_v || KCODEC != TQ_CODEC_LLOYDMAX) codec_vector<D, TQ_CODEC_ABSMAX>(y, sw, lane, u, scale);
   else codec_vector<D, TQ_CODEC_LLOYDMAX>(y, sw, lane, u, scale);
-  place_vector<D>(pool + ((slot >> 4) * (int64_t)Hkv + h) * BB, (int)(slot & 15), lane, is_v != 0, u, scale);
+  place_vector<D, KF16>(blk, (int)(slot & 15), lane, is_v != 0, u, scale);
 }
 
 template <int D, typename T>
@@ -44,6 +50,9 @@ hipError_t launch_d(const LaunchAppend& a, hipStream_t st) {
   const T* v = static_cast<const T*>(a.v);
   if (a.k_codec == TQ_CODEC_LLOYDMAX)
     hipLaunchKernelGGL((append_kernel<D, T, TQ_CODEC_LLOYDMAX>), grid, dim3(256), 0, st, a.pool, k, v,
+                       a.slots, a.sign_bits, a.n_tokens, a.Hkv);
+  else if (a.k_codec == TQ_CODEC_FP16)
+    hipLaunchKernelGGL((append_kernel<D, T, TQ_CODEC_FP16>), grid, dim3(256), 0, st, a.pool, k, v,
                        a.slots, a.sign_bits, a.n_tokens, a.Hkv);
   else
     hipLaunchKernelGGL((append_kernel<D, T, TQ_CODEC_ABSMAX>), grid, dim3(256), 0, st, a.pool, k, v,

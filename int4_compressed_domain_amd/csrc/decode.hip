@@ -41,16 +41,24 @@ __device__ __forceinline__ f16x8 unpack_k_sub(uint32_t w) {
   return __builtin_bit_cast(f16x8, r);
 }
 
-template <int D>
+// Geometry of a block and of its staged copy in LDS: [K][V indices][scales].
+template <int D, int KC>
 struct Cfg {
+  static constexpr bool KF16 = KC == TQ_CODEC_FP16;   // fp16 keys
   static constexpr int G = D / 32;
-  static constexpr int BB = TQ_BLOCK_BYTES(D);
+  static constexpr int BB = tq_block_bytes(D, KC);
   static constexpr int KB = 4 * G;                    // index bytes per lane per page (K or V)
   static constexpr int DMAK = KB >= 16 ? 16 : 4;      // LDS-DMA size for index loads
   static constexpr int NK = KB / DMAK;                // DMAs per index region
-  static constexpr int NSC = (16 * G + 63) / 64;      // dword DMAs for the scale region
-  static constexpr int NDMA = 2 * NK + NSC;            // vector-memory ops per page
-  static constexpr int SLOT = 128 * KB + 64 * G;      // LDS bytes of one staged page
+  static constexpr int KREG = KF16 ? 32 * D : 64 * KB;  // staged K bytes (fp16: G runs of 1 KB)
+  static constexpr int VOFF = KREG;                   // staged V indices
+  static constexpr int SOFF = VOFF + 64 * KB;         // staged scales
+  static constexpr int SCB = KF16 ? 32 * G : 64 * G;  // scale bytes (fp16 keys: V scales only)
+  static constexpr int NSC = (SCB / 4 + 63) / 64;     // dword DMAs for the scales
+  static constexpr int NDMA = (KF16 ? G : NK) + NK + NSC;  // vector-memory ops per page
+  static constexpr int SLOT = SOFF + SCB;             // LDS bytes of one staged page
+  static constexpr int BV = KF16 ? 32 * D : 8 * D;    // block offsets of the V indices
+  static constexpr int BS = KF16 ? 40 * D : 16 * D;   //   and of the scales
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -74,24 +82,28 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
 // Stage one page (one kv head's block) into an LDS slot:
 //   [K indices: NK chunks of 64 lanes x DMAK][V indices: same][scales: 16G dwords]
 // The buffer descriptor spans exactly this block, so no lane can touch memory outside it.
-template <int D>
+template <int D, int KC>
 __device__ __forceinline__ void stage_page(const uint8_t* blk, uint32_t base, int lane) {
-  using C = Cfg<D>;
+  using C = Cfg<D, KC>;
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
   const uint32_t lo = (uint32_t)lane * C::KB;  // this lane's byte offset inside an index region
+  if constexpr (C::KF16) {  // fp16 keys: group g's 1 KB run, 16 bytes per lane
+#pragma unroll
+    for (int g = 0; g < C::G; g++) dma16(r, (uint32_t)lane * 16, 1024u * g, base + 1024 * g);
+  }
 #pragma unroll
   for (int c = 0; c < C::NK; c++) {
     if constexpr (C::DMAK == 16) {
-      dma16(r, lo + c * 16, 0u, base + c * 1024);
-      dma16(r, lo + c * 16, 8u * D, base + 64 * C::KB + c * 1024);
+      if constexpr (!C::KF16) dma16(r, lo + c * 16, 0u, base + c * 1024);
+      dma16(r, lo + c * 16, (uint32_t)C::BV, base + C::VOFF + c * 1024);
     } else {
-      dma4(r, lo + c * 4, 0u, base + c * 256);
-      dma4(r, lo + c * 4, 8u * D, base + 64 * C::KB + c * 256);
+      if constexpr (!C::KF16) dma4(r, lo + c * 4, 0u, base + c * 256);
+      dma4(r, lo + c * 4, (uint32_t)C::BV, base + C::VOFF + c * 256);
     }
   }
 #pragma unroll
   for (int c = 0; c < C::NSC; c++)
-    if (c * 64 + lane < 16 * C::G) dma4(r, 4 * (c * 64 + lane), 16u * D, base + 128 * C::KB + 256 * c);
+    if (c * 64 + lane < C::SCB / 4) dma4(r, 4 * (c * 64 + lane), (uint32_t)C::BS, base + C::SOFF + 256 * c);
 }
 
 // s_waitcnt vmcnt(n) with n a multiple of the per-page DMA count: n = k * NDMA, k = pages
@@ -163,13 +175,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int KCODEC>
 __device__ __forceinline__ int dim_kslot(int e) {
   if constexpr (KCODEC == TQ_CODEC_ABSMAX) return ((e & 3) << 1) | (e >> 2);
+  else if constexpr (KCODEC == TQ_CODEC_FP16) return e;  // fp16 keys: dims in order
   else return (e >> 1) | ((e & 1) << 2);
 }
 
 template <int D, typename TQ, int KCODEC, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
-  using C = Cfg<D>;
+  using C = Cfg<D, KCODEC>;
   constexpr int G = C::G, BB = C::BB, NT = 64 * NW, V = D / 64;
+  constexpr bool KF16 = C::KF16;
   // ring slots per wave: as many as ~144 KB of LDS holds, at most 8 (NSLOT - 1 pages in flight)
   constexpr int NSLOT = (147456 / (NW * C::SLOT)) < 8 ? (147456 / (NW * C::SLOT)) : 8;
   static_assert(NSLOT >= 3, "ring too small");
@@ -278,7 +292,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     for (int k = 0; k < V; k++) {
       const int d = lane + 64 * k;
       const float x = widen(qb[wv * D + d]);
-      qv[k] = ((a.sign_bits[d >> 5] >> (d & 31)) & 1u) ? -x : x;
+      // fp16 keys are in the original basis: the query scores them unrotated
+      qv[k] = (!KF16 && ((a.sign_bits[d >> 5] >> (d & 31)) & 1u)) ? -x : x;
     }
   }
   __syncthreads();
@@ -288,15 +303,19 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int k = 0; k < 2; k++) {
       const int pp = p0 + wv + k * NW;
-      if (pp < p1) stage_page<D>(page_blk(k), slot_lds(k), lane);
+      if (pp < p1) stage_page<D, KCODEC>(page_blk(k), slot_lds(k), lane);
     }
   };
   if (app && wv == wc && lane < 32) {  // quantize the appended token before this wave's
     uint32_t un[E];                     // first page loads, which may wait for queue space
     f16 scn;
-    if (lane >= 16 || KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, swnew, lane & 15, un, scn);
-    else codec_vector<D, TQ_CODEC_LLOYDMAX>(ynew, swnew, lane & 15, un, scn);
-    place_vector<D>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
+    if (KF16 && lane < 16) {
+      place_key_f16<D>(tokblk, tnew, lane, ynew);  // fp16 key, no rotation
+    } else {
+      if (lane >= 16 || KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, swnew, lane & 15, un, scn);
+      else codec_vector<D, TQ_CODEC_LLOYDMAX>(ynew, swnew, lane & 15, un, scn);
+      place_vector<D, KF16>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
+    }
   }
   if (wv >= r) stage_first();
 
@@ -306,11 +325,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // layout: lane 16j + c, k-slot s holds dim 32g + 8j + kslot_dim(s) of group g.
   const float rho = tq_rho(D), qmul = a.attn_scale * TQ_LOG2E;
   if (wv < r) {
-    wave_fwht<V>(qv, lane);
+    if constexpr (!KF16) wave_fwht<V>(qv, lane);
     float mx = 0.0f;
 #pragma unroll
     for (int k = 0; k < V; k++) {
-      qv[k] = (qv[k] * rho) * qmul;
+      qv[k] = KF16 ? qv[k] * qmul : (qv[k] * rho) * qmul;
       mx = fmaxf(mx, fabsf(qv[k]));
     }
     mx = wave_max(mx);
@@ -355,7 +374,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   }
   __syncthreads();  // every wave holds its operands: the last ring slot is free again
   uint32_t tlo[4] = {0, 0, 0, 0}, thi[4] = {0, 0, 0, 0};
-  if constexpr (!KSUB) {
+  if constexpr (KCODEC == TQ_CODEC_LLOYDMAX) {
     const uint16_t lb[16] = TQ_LUT16_BITS;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
@@ -390,18 +409,19 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int c = 0; c < C::NK; c++) {
       if constexpr (C::DMAK == 16) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(slot + region * 64 * C::KB + c * 1024 + lane * 16);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(slot + (region ? C::VOFF : 0) + c * 1024 + lane * 16);
         w[4 * c] = x[0]; w[4 * c + 1] = x[1]; w[4 * c + 2] = x[2]; w[4 * c + 3] = x[3];
       } else {
-        w[c] = *reinterpret_cast<const uint32_t*>(slot + region * 64 * C::KB + c * 256 + lane * 4);
+        w[c] = *reinterpret_cast<const uint32_t*>(slot + (region ? C::VOFF : 0) + c * 256 + lane * 4);
       }
     }
   };
   auto load_scales = [&](const uint8_t* slot, uint32_t (&st)[2 * G], int region) {  // 0: K, 1: V
-    const uint32_t* sw = reinterpret_cast<const uint32_t*>(slot + 128 * C::KB);
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(slot + C::SOFF);
+    const int roff = KF16 ? 0 : region * 8 * G;  // fp16 keys: only V scales are staged
 #pragma unroll
     for (int i = 0; i < 2 * G; i += 4) {  // fp16 pairs: tokens 4jq..4jq+3, groups 0..G-1
-      const u32x4 x = *reinterpret_cast<const u32x4*>(&sw[region * 8 * G + 2 * G * jq + i]);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(&sw[roff + 2 * G * jq + i]);
       st[i] = x[0]; st[i + 1] = x[1]; st[i + 2] = x[2]; st[i + 3] = x[3];
     }
   };
@@ -414,6 +434,16 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   };
   // one page's partial scores in every lane (column hr: hi or lo part)
   auto scores = [&](const uint8_t* slot, float (&sc)[4]) {
+    if constexpr (KF16) {  // fp16 keys are the A operand as staged; one accumulator
+      f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int g = 0; g < G; g++)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const f16x8*>(slot + 1024 * g + lane * 16),
+                                                    bq[g], c, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; e++) sc[e] = c[e];
+      return;
+    }
     uint32_t kw[G], kst[2 * G];
     load_idx(slot, kw, 0);
     load_scales(slot, kst, 0);
@@ -500,21 +530,36 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // regions are stored chunk by chunk as the page loads wrote them (see stage_page).
   auto copy_token = [&](uint8_t* dst, bool to_lds) {
     constexpr int G_ = D / 32, KB = C::KB, DM = C::DMAK;
-    auto at = [&](int o) {
-      if (!to_lds || o >= 128 * KB) return o;
-      const int reg = o / (64 * KB), w = o % (64 * KB), l = w / KB, wb = w % KB;
-      return reg * 64 * KB + (wb / DM) * (64 * DM) + l * DM + (wb % DM);
+    // staged position of a 4-bit index byte w of an index region (page loads write each
+    // region chunk by chunk: chunk w / DM of every lane, lane after lane)
+    auto staged = [&](int w) {
+      const int l = w / KB, wb = w % KB;
+      return (wb / DM) * (64 * DM) + l * DM + (wb % DM);
     };
-    for (int i = lane; i < 4 * G_; i += 64) {  // K index dwords: chunk q = 4g + j
-      const int off = (16 * (i & 3) + tnew) * 4 * G_ + 4 * (i >> 2);
-      *reinterpret_cast<uint32_t*>(dst + at(off)) = *reinterpret_cast<const uint32_t*>(tokblk + off);
+    auto at = [&](int o) {  // block offset -> offset in dst
+      if (!to_lds) return o;
+      if (o < C::BV) return KF16 ? o : staged(o);  // keys (fp16 keys are staged as stored)
+      if (o < C::BS) return C::VOFF + staged(o - C::BV);
+      return C::SOFF + (o - C::BS);
+    };
+    if constexpr (KF16) {
+      for (int i = lane; i < 4 * G_; i += 64) {  // fp16 key: 8-dim run (g, j) = (i / 4, i % 4)
+        const int off = 1024 * (i >> 2) + 16 * (16 * (i & 3) + tnew);
+        *reinterpret_cast<u32x4*>(dst + at(off)) = *reinterpret_cast<const u32x4*>(tokblk + off);
+      }
+    } else {
+      for (int i = lane; i < 4 * G_; i += 64) {  // K index dwords: chunk q = 4g + j
+        const int off = (16 * (i & 3) + tnew) * 4 * G_ + 4 * (i >> 2);
+        *reinterpret_cast<uint32_t*>(dst + at(off)) = *reinterpret_cast<const uint32_t*>(tokblk + off);
+      }
     }
     for (int c = lane; c < D / 2; c += 64) {  // V index bytes: dim pair c = 16g + m
-      const int off = 8 * D + (16 * (tnew >> 2) + (c & 15)) * 4 * G_ + 4 * (c >> 4) + (tnew & 3);
+      const int off = C::BV + (16 * (tnew >> 2) + (c & 15)) * 4 * G_ + 4 * (c >> 4) + (tnew & 3);
       dst[at(off)] = tokblk[off];
     }
-    if (lane < 2 * G_) {  // K scales then V scales
-      const int off = 16 * D + (lane >= G_ ? 32 * G_ : 0) + 2 * (tnew * G_ + (lane % G_));
+    constexpr int NSCL = KF16 ? G_ : 2 * G_;  // scales of the token: (K then) V
+    if (lane < NSCL) {
+      const int off = C::BS + (lane >= G_ ? 32 * G_ : 0) + 2 * (tnew * G_ + (lane % G_));
       *reinterpret_cast<f16*>(dst + at(off)) = *reinterpret_cast<const f16*>(tokblk + off);
     }
   };
@@ -540,7 +585,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int k = 0; k < 4; k++)
       if (nis < nmax) {
-        stage_page<D>(page_blk(nis), slot_lds(nis % NSLOT), lane);
+        stage_page<D, KCODEC>(page_blk(nis), slot_lds(nis % NSLOT), lane);
         nis++;
       }
     const int younger = max(0, min(NSLOT - 2, nis - na - 2));  // pages issued after page na + 1
@@ -764,10 +809,19 @@ hipError_t launch_dq(const LaunchDecode& a, hipStream_t st) {
   }
   const int U = a.B * a.Hkv;
   const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * a.splits);
-  if (a.k_codec == TQ_CODEC_LLOYDMAX)
+  if (a.k_codec == TQ_CODEC_FP16) {
+    // fp16 keys: 8 waves; a staged page does not fit three times per wave at D = 256
+    if constexpr (D <= 128) {
+      constexpr int NWF = tq_decode_waves(D, TQ_CODEC_FP16);
+      hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_FP16, NWF>), dim3(grid), dim3(64 * NWF), 0, st, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (a.k_codec == TQ_CODEC_LLOYDMAX) {
     hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_LLOYDMAX, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
-  else
+  } else {
     hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_ABSMAX, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -3,7 +3,8 @@
 // 16 lanes per (sequence, kv head, token) vector, E = D/16 coordinates per lane; values
 // (u-8)*s or LUT_u*n are exact in fp32. The original-basis variant applies the fp32
 // inverse rotation diag(sigma)*rho*H with the forward rotation's stage order.
-// Compiled with -ffp-contract=off.
+// fp16 keys are copied as stored (they have no rotated form). Compiled with
+// -ffp-contract=off.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -11,7 +12,10 @@ namespace {
 
 template <int D, typename TOut>
 __global__ __launch_bounds__(256) void dequant_kernel(LaunchDequant a) {
-  constexpr int E = D / 16, G = D / 32, BB = TQ_BLOCK_BYTES(D);
+  constexpr int E = D / 16, G = D / 32;
+  const bool kf16 = a.k_codec == TQ_CODEC_FP16;
+  const int BB = tq_block_bytes(D, a.k_codec);
+  const int vbase = kf16 ? 32 * D : 8 * D;
   const int lane = threadIdx.x & 15;
   const int64_t vec = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int64_t per_b = (int64_t)a.Hkv * a.max_ctx;
@@ -30,7 +34,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(LaunchDequant a) {
     const uint8_t* blk = a.pool + (page * a.Hkv + h) * BB;
     const int tt = t & 15;
     uint32_t u[E];
-    if (!is_v) {
+    if (!is_v && kf16) {  // fp16 key, dims lane*E + e: byte 1024g + 16(16j + t) + 2(d % 8)
+#pragma unroll
+      for (int e = 0; e < E; e++) {
+        const int d = lane * E + e;
+        y[e] = (float)*reinterpret_cast<const f16*>(blk + 1024 * (d >> 5) + 16 * (16 * ((d >> 3) & 3) + tt) + 2 * (d & 7));
+      }
+    } else if (!is_v) {
       if constexpr (E >= 8) {
 #pragma unroll
         for (int c = 0; c < E / 8; c++) {
@@ -49,14 +59,17 @@ __global__ __launch_bounds__(256) void dequant_kernel(LaunchDequant a) {
 #pragma unroll
       for (int k = 0; k < E / 2; k++) {
         const int c = lane * (E / 2) + k;
-        const uint32_t byte = blk[8 * D + (16 * (tt >> 2) + (c & 15)) * 4 * G + 4 * (c >> 4) + (tt & 3)];
+        const uint32_t byte = blk[vbase + (16 * (tt >> 2) + (c & 15)) * 4 * G + 4 * (c >> 4) + (tt & 3)];
         u[2 * k] = byte & 15u;
         u[2 * k + 1] = byte >> 4;
       }
     }
     const int g = (lane * E) / 32;
-    const float sc = (float)*reinterpret_cast<const f16*>(blk + 16 * D + (is_v ? 32 * G : 0) + 2 * (tt * G + g));
-    if (!is_v && a.k_codec == TQ_CODEC_LLOYDMAX) {
+    const int sbase = kf16 ? 40 * D : 16 * D + (is_v ? 32 * G : 0);
+    const float sc = (float)*reinterpret_cast<const f16*>(blk + sbase + 2 * (tt * G + g));
+    if (!is_v && kf16) {
+      // y holds the key already
+    } else if (!is_v && a.k_codec == TQ_CODEC_LLOYDMAX) {
       const uint16_t lb[16] = TQ_LUT16_BITS;
 #pragma unroll
       for (int e = 0; e < E; e++) y[e] = (float)__builtin_bit_cast(f16, lb[u[e]]) * sc;
@@ -64,7 +77,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(LaunchDequant a) {
 #pragma unroll
       for (int e = 0; e < E; e++) y[e] = (float)((int)u[e] - 8) * sc;
     }
-    if (a.original_basis) {
+    if (a.original_basis && (is_v || !kf16)) {
 #pragma unroll
       for (int s = 1; s < E; s <<= 1)
 #pragma unroll

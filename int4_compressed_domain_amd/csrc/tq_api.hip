@@ -27,7 +27,8 @@ int check_layout(const tq_layout* L, bool need_pool_fields) {
   if (L->page_size <= 0) return TQ_EINVAL;
   if (L->page_size != 16) return TQ_EUNSUPPORTED;
   if (L->num_pages < 0) return TQ_EINVAL;
-  if (L->k_codec != TQ_CODEC_ABSMAX && L->k_codec != TQ_CODEC_LLOYDMAX) return TQ_EINVAL;
+  if (L->k_codec != TQ_CODEC_ABSMAX && L->k_codec != TQ_CODEC_LLOYDMAX && L->k_codec != TQ_CODEC_FP16)
+    return TQ_EINVAL;
   if (L->v_codec == TQ_CODEC_LLOYDMAX) return TQ_EUNSUPPORTED;  // the LUT codec is for keys
   if (L->v_codec != TQ_CODEC_ABSMAX) return TQ_EINVAL;
   if (!L->sign_bits) return TQ_EINVAL;
@@ -58,14 +59,14 @@ Split make_split(int pages, int S) {
   return s;
 }
 
-Split choose_split(int B, int Hkv, int D, int max_ctx, int requested) {
+Split choose_split(int B, int Hkv, int D, int k_codec, int max_ctx, int requested) {
   const int pages = (max_ctx + 15) / 16;
   const int min_s = (pages + TQ_MAX_SPLIT_PAGES - 1) / TQ_MAX_SPLIT_PAGES;  // page ids fit LDS
   if (requested > 0) {
     int S = requested < TQ_MAX_SPLITS ? requested : TQ_MAX_SPLITS;
     return make_split(pages, S > min_s ? S : min_s);
   }
-  const int nw = tq_decode_waves(D);
+  const int nw = tq_decode_waves(D, k_codec);
   const int64_t units = (int64_t)B * Hkv;
   const int64_t target = (int64_t)num_cus() * (D >= 256 ? 2 : 1);
   int64_t want = (target + units - 1) / units;
@@ -92,7 +93,7 @@ size_t partial_bytes(int B, int Hq, int D, int splits) {
 }
 
 size_t workspace_bytes(const tq_layout* L, int B, int max_ctx, int requested) {
-  const Split f = choose_split(B, L->num_kv_heads, L->head_dim, max_ctx, requested);
+  const Split f = choose_split(B, L->num_kv_heads, L->head_dim, L->k_codec, max_ctx, requested);
   const Split d = choose_split_dense(B, L->num_kv_heads, max_ctx, requested);
   const int S = f.splits > d.splits ? f.splits : d.splits;
   return TQ_DECODE_COUNTER_BYTES + partial_bytes(B, L->num_q_heads, L->head_dim, S) +
@@ -130,7 +131,7 @@ const char* tq_status_str(int status) {
 
 size_t tq_page_bytes(const tq_layout* L) {
   if (check_layout(L, true) != TQ_OK) return 0;
-  return (size_t)L->num_kv_heads * TQ_BLOCK_BYTES(L->head_dim);
+  return (size_t)L->num_kv_heads * tq_block_bytes(L->head_dim, L->k_codec);
 }
 
 int tq_kv_append(const tq_layout* L, void* pool, const void* k, const void* v, int32_t in_dtype,
@@ -165,9 +166,10 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   if (rc != TQ_OK) return rc;
   if (max_pages_per_seq < 0 || (int64_t)max_context_len > 16LL * max_pages_per_seq) return TQ_EINVAL;
   if ((int64_t)max_context_len > 16LL * TQ_MAX_SPLITS * TQ_MAX_SPLIT_PAGES) return TQ_EUNSUPPORTED;
+  if (L->k_codec == TQ_CODEC_FP16 && L->head_dim > 128) return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
   if (!pool || !block_table) return TQ_EINVAL;
-  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, max_context_len, num_splits);
+  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits);
   if (workspace_bytes_ < workspace_bytes(L, batch, max_context_len, num_splits)) return TQ_ENOSPC;
   if (!workspace) return TQ_EINVAL;
   float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + TQ_DECODE_COUNTER_BYTES);

@@ -115,11 +115,13 @@ __device__ __forceinline__ void codec_vector(float (&y)[D / 16], uint32_t sw, in
 }
 
 // Write one lane's indices and (from the group's first lane) the scale of token t into a
-// block (pool memory, or a copy of the block in LDS; see the pool format in tq.h).
-template <int D>
+// block (pool memory, or a copy of the block in LDS; see the pool format in tq.h). KF16:
+// the fp16-key block, whose value regions start at 32D (indices) and 40D (scales).
+template <int D, bool KF16 = false>
 __device__ __forceinline__ void place_vector(uint8_t* blk, int t, int lane16, bool is_v,
                                              const uint32_t (&u)[D / 16], f16 scale) {
   constexpr int E = CodecCfg<D>::E, G = CodecCfg<D>::G, LPG = CodecCfg<D>::LPG;
+  constexpr int VBASE = KF16 ? 32 * D : 8 * D;
   if (!is_v) {
     // K: dims 8q..8q+7 (q = chunk index, g = q/4, j = q%4) -> one dword at (16j+t)*4G + 4g
     if constexpr (E >= 8) {
@@ -141,12 +143,37 @@ __device__ __forceinline__ void place_vector(uint8_t* blk, int t, int lane16, bo
 #pragma unroll
     for (int k = 0; k < E / 2; k++) {
       const int c = lane16 * (E / 2) + k;
-      blk[8 * D + (16 * (t >> 2) + (c & 15)) * 4 * G + 4 * (c >> 4) + (t & 3)] =
+      blk[VBASE + (16 * (t >> 2) + (c & 15)) * 4 * G + 4 * (c >> 4) + (t & 3)] =
           (uint8_t)(u[2 * k] | (u[2 * k + 1] << 4));
     }
   }
   if ((lane16 % LPG) == 0) {
     const int g = (lane16 * E) / 32;
-    *reinterpret_cast<f16*>(blk + 16 * D + (is_v ? 32 * G : 0) + 2 * (t * G + g)) = scale;
+    const int sbase = KF16 ? 40 * D : 16 * D + (is_v ? 32 * G : 0);
+    *reinterpret_cast<f16*>(blk + sbase + 2 * (t * G + g)) = scale;
+  }
+}
+
+// fp16 keys: this lane's E coordinates of the (unrotated) key of token t, rounded to fp16
+// (nearest even, overflow saturated), into an fp16-key block: dims 32g + 8j + 0..7 of
+// token t are the 16 bytes at 1024g + 16(16j + t).
+template <int D>
+__device__ __forceinline__ void place_key_f16(uint8_t* blk, int t, int lane16, const float (&y)[D / 16]) {
+  constexpr int E = CodecCfg<D>::E;
+#pragma unroll
+  for (int c = 0; c < (E >= 8 ? E / 8 : 1); c++) {
+    const int d0 = lane16 * E + 8 * c;
+    uint8_t* dst = blk + 1024 * (d0 >> 5) + 16 * (16 * ((d0 >> 3) & 3) + t) + 2 * (d0 & 7);
+    if constexpr (E >= 8) {
+      f16x8 h;
+#pragma unroll
+      for (int e = 0; e < 8; e++) h[e] = f16_sat(y[8 * c + e]);
+      *reinterpret_cast<f16x8*>(dst) = h;
+    } else {  // E == 4: half of an 8-dim run
+      f16x4 h;
+#pragma unroll
+      for (int e = 0; e < 4; e++) h[e] = f16_sat(y[e]);
+      *reinterpret_cast<f16x4*>(dst) = h;
+    }
   }
 }

@@ -51,7 +51,14 @@ hipError_t tq_launch_dequant(const LaunchDequant& a, hipStream_t st);
 
 // Wavefronts per fused-decode workgroup; each workgroup owns one (sequence, kv head,
 // context split). 16 waves fill a CU when the kernel fits in 128 registers per lane.
-constexpr int tq_decode_waves(int D) { return D > 128 ? 8 : 16; }
+// fp16 keys: 8 waves (a staged page is 41*D bytes, three per wave fit the LDS ring).
+constexpr int tq_decode_waves(int D, int k_codec = TQ_CODEC_ABSMAX) {
+  return (D > 128 || k_codec == TQ_CODEC_FP16) ? 8 : 16;
+}
+// Bytes of one block (16 tokens of one kv head).
+constexpr int tq_block_bytes(int D, int k_codec) {
+  return k_codec == TQ_CODEC_FP16 ? TQ_BLOCK_BYTES_KF16(D) : TQ_BLOCK_BYTES(D);
+}
 constexpr int TQ_DECODE_WAVES = 4;   // dense baseline workgroups
 constexpr int TQ_MAX_SPLITS = 128;   // context splits per (sequence, kv head)
 constexpr int TQ_MAX_SPLIT_PAGES = 2048;  // pages per split (their ids are staged in LDS)

@@ -124,6 +124,18 @@ def test_page_bytes():
     assert tq.tq_page_bytes(_layout()) == 8 * (16 * 128 + 64 * 4)
     assert tq.tq_page_bytes(_layout(head_dim=256, num_q_heads=4, num_kv_heads=2)) == 2 * (16 * 256 + 64 * 8)
     assert tq.tq_page_bytes(_layout(head_dim=100)) == 0
+    # fp16 keys: [K fp16 32D][V indices 8D][V scales 16 x D/32 fp16]
+    assert tq.tq_page_bytes(_layout(k_codec=tq.CODEC_FP16)) == 8 * (32 * 128 + 8 * 128 + 32 * 4)
+    assert tq.tq_page_bytes(_layout(head_dim=64, k_codec=tq.CODEC_FP16)) == 8 * 41 * 64
+
+
+def test_fp16_keys_decode_limits():
+    """fp16 keys decode at head_dim 64 and 128; 256 is rejected before any launch."""
+    L = _layout(head_dim=256, num_q_heads=16, num_kv_heads=8, k_codec=tq.CODEC_FP16)
+    assert _decode(L) == tq.TQ_EUNSUPPORTED
+    assert _append_decode(L) == tq.TQ_EUNSUPPORTED
+    assert _append(L, pool=None) == tq.TQ_EINVAL     # appending itself is supported
+    assert _decode(_layout(k_codec=tq.CODEC_FP16), q=None) == tq.TQ_EINVAL
 
 
 def test_dequant_and_dense_validation():

@@ -89,7 +89,22 @@ def test_head_dims_and_gqa(D, r):
     _check_case(c)
 
 
-@pytest.mark.parametrize("k_codec", [0, 1])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("r", [1, 4, 8])
+def test_fp16_keys(D, r):
+    """fp16 keys + 4-bit values: pool bytes equal the oracle's (keys as fp16 of the input,
+    values rotated and quantized), attention within the tolerance, across split counts."""
+    w = W.Workload("k16_d%d_r%d" % (D, r), 3, 2 * r, 2, D, 700, "bf16", 1.0 / math.sqrt(D),
+                   k_codec=2, dist="lognormal_spikes")
+    _say("case fp16 keys D=%d r=%d" % (D, r))
+    c = Case(w, seed=40 + D + r, lens=[700, 33, 260])
+    c.fill()
+    assert c.pool_equal()
+    for splits in (0, 1, 5):
+        _check_case(c, num_splits=splits)
+
+
+@pytest.mark.parametrize("k_codec", [0, 1, 2])
 def test_ragged_edge_lengths(k_codec):
     lens = [0, 1, 15, 16, 17, 33, 48, 250]
     w = W.Workload("edges", len(lens), 8, 2, 128, max(lens), "bf16", 0.125, k_codec=k_codec)
@@ -187,7 +202,7 @@ def test_negative_slots_and_untouched_bytes():
     assert c.pool_equal()
 
 
-@pytest.mark.parametrize("k_codec", [0, 1])
+@pytest.mark.parametrize("k_codec", [0, 1, 2])
 @pytest.mark.parametrize("basis", [0, 1])
 def test_dequant_reference(k_codec, basis):
     lens = [37, 0, 64]
@@ -244,7 +259,7 @@ def _pairs(w, lens, n=12, seed=0):
 
 
 @pytest.mark.parametrize("name", ["single_head_1k", "llama8b_b16_8k", "llama70b_b1_128k",
-                                  "gemma_d256_32k", "mixed_serving"])
+                                  "gemma_d256_32k", "mixed_serving", "llama70b_b1_128k_k16v4"])
 def test_full_size_workloads(name):
     w = W.WORKLOADS[name]
     _say("case full-size", name)
@@ -262,7 +277,8 @@ def test_full_size_workloads(name):
 
 
 @pytest.mark.parametrize("D,r,k_codec,dtype", [(128, 8, 0, "bf16"), (128, 4, 1, "bf16"),
-                                               (64, 2, 0, "f32"), (256, 2, 0, "bf16")])
+                                               (64, 2, 0, "f32"), (256, 2, 0, "bf16"),
+                                               (128, 8, 2, "bf16"), (64, 4, 2, "f32")])
 def test_append_decode_equals_append_then_decode(D, r, k_codec, dtype):
     """The fused entry point writes the same pool bytes as tq_kv_append of each sequence's
     last token and returns the same output, bit for bit, as tq_decode_attn afterwards."""
