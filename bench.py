@@ -329,7 +329,7 @@ def main():
         "config": {"workload": name, "batch": w.batch, "q_heads": w.q_heads,
                    "kv_heads": w.kv_heads, "head_dim": w.head_dim, "context": w.context,
                    "ragged_min": w.ragged_min, "prefill": w.prefill, "page": 16, "group": 32,
-                   "k_codec": ["absmax", "lloydmax"][w.k_codec], "v_codec": "absmax",
+                   "k_codec": ["absmax", "lloydmax", "fp16"][w.k_codec], "v_codec": "absmax",
                    "kv_input": w.dtype, "attn_scale": w.attn_scale, "splits": args.splits},
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
         "decode_us": round(dec_mean, 3), "prefill_append_us": round(pre_mean, 3),
