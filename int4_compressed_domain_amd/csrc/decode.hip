@@ -630,18 +630,22 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
   }
   __syncthreads();
-  if (tid < r) {  // per head: wave weights 2^(m_w - M) (into mml[w][hd][0]) and the sum l
-    const int hd = tid;
-    float M = -INFINITY;
-    for (int w = 0; w < NW; w++) M = fmaxf(M, mml[w][hd][0]);
-    float l = 0.0f;
-    for (int w = 0; w < NW; w++) {
-      const float f = (mml[w][hd][0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mml[w][hd][0] - M);
-      l += f * mml[w][hd][1];
-      mml[w][hd][0] = f;
+  if (tid < 128) {  // per head, one row of 16 lanes (lane = wave): weights 2^(m_w - M)
+    const int hd = tid >> 4, w = tid & 15;   // into mml[w][hd][0], and the sum l
+    const bool on = hd < r && w < NW;
+    const float mw = on ? mml[w][hd][0] : -INFINITY;
+    float M = mw;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, lane_xor16(M, o, lane));
+    const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+    float l = on ? f * mml[w][hd][1] : 0.0f;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) l += lane_xor16(l, o, lane);
+    if (on) mml[w][hd][0] = f;
+    if (on && w == 0) {
+      hml[hd][0] = M;
+      hml[hd][1] = l;
     }
-    hml[hd][0] = M;
-    hml[hd][1] = l;
   }
   __syncthreads();
   // fin: [ngf][r][D] partial sums of the result (rotated basis), summed by the rotation below
