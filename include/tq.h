@@ -174,6 +174,28 @@ int tq_append_decode_attn(const tq_layout* layout, void* pool, const void* k_las
                           int32_t num_splits, float* out, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Decode attention with sparse values: as tq_decode_attn, except that the values of a
+ * 16-token page (of one kv head) are neither loaded nor used when every weight of it, for
+ * every q head of the kv head, is below v_threshold (mlxcel "TurboQuant KV cache" manual,
+ * sparse-V threshold: value dequantization is skipped where the attention weight is below
+ * it, 1e-6 by default). The weight compared is exp(score - running max) when the page is
+ * scored, which bounds the token's final softmax weight from above; so the result differs
+ * from tq_decode_attn only by dropped terms w_t * v_t with every w_t < v_threshold (the
+ * softmax normalizer still counts every token). Which pages are dropped depends on the
+ * split count; v_threshold = 0 drops none and gives tq_decode_attn's result bit for bit.
+ *   v_threshold     in [0, 1), TQ_EINVAL otherwise
+ *   v_pages_skipped optional device uint64: the number of (page, kv head) value blocks
+ *                   skipped is added to it (NULL: not counted)
+ *   other arguments, workspace and errors as tq_decode_attn.
+ * [mlxcel manual, sparse-V dequant threshold; Open-TQ-Metal, arXiv abstract] */
+int tq_decode_attn_sparse_v(const tq_layout* layout, const void* pool, const void* q,
+                            int32_t q_dtype, int32_t batch, const int32_t* block_table,
+                            int32_t max_pages_per_seq, const int32_t* context_lens,
+                            int32_t max_context_len, float attn_scale, float v_threshold,
+                            int32_t num_splits, float* out, void* workspace,
+                            size_t workspace_bytes, unsigned long long* v_pages_skipped,
+                            void* stream);
+
 /* Dequantize reference: dense K and V, [batch][num_kv_heads][max_context_len][head_dim]
  * of out_dtype (TQ_F32 or TQ_F16), rows at or past a sequence's length set to zero.
  * to_original_basis = 0: values (u-8)*s or LUT_u*n in the rotated basis (exact products,

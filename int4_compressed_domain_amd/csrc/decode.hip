@@ -106,6 +106,66 @@ __device__ __forceinline__ void stage_page(const uint8_t* blk, uint32_t base, in
     if (c * 64 + lane < C::SCB / 4) dma4(r, 4 * (c * 64 + lane), (uint32_t)C::BS, base + C::SOFF + 256 * c);
 }
 
+// Sparse values: the key part of a page ([K][K scales]) and its value part ([V indices][V
+// scales]) staged separately, into the same slot layout as stage_page.
+template <int D, int KC>
+struct SplitDma {
+  using C = Cfg<D, KC>;
+  static constexpr int NSK = C::KF16 ? 0 : (8 * C::G + 63) / 64;  // dword DMAs, K scales
+  static constexpr int NSV = (8 * C::G + 63) / 64;                // dword DMAs, V scales
+  static constexpr int NK_OPS = (C::KF16 ? C::G : C::NK) + NSK;
+  static constexpr int NV_OPS = C::NK + NSV;
+};
+
+template <int D, int KC>
+__device__ __forceinline__ void stage_k(const uint8_t* blk, uint32_t base, int lane) {
+  using C = Cfg<D, KC>;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
+  if constexpr (C::KF16) {
+#pragma unroll
+    for (int g = 0; g < C::G; g++) dma16(r, (uint32_t)lane * 16, 1024u * g, base + 1024 * g);
+  } else {
+    const uint32_t lo = (uint32_t)lane * C::KB;
+#pragma unroll
+    for (int c = 0; c < C::NK; c++) {
+      if constexpr (C::DMAK == 16) dma16(r, lo + c * 16, 0u, base + c * 1024);
+      else dma4(r, lo + c * 4, 0u, base + c * 256);
+    }
+#pragma unroll
+    for (int c = 0; c < SplitDma<D, KC>::NSK; c++)
+      if (c * 64 + lane < 8 * C::G) dma4(r, 4 * (c * 64 + lane), (uint32_t)C::BS, base + C::SOFF + 256 * c);
+  }
+}
+
+template <int D, int KC>
+__device__ __forceinline__ void stage_v(const uint8_t* blk, uint32_t base, int lane) {
+  using C = Cfg<D, KC>;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
+  const uint32_t lo = (uint32_t)lane * C::KB;
+#pragma unroll
+  for (int c = 0; c < C::NK; c++) {
+    if constexpr (C::DMAK == 16) dma16(r, lo + c * 16, (uint32_t)C::BV, base + C::VOFF + c * 1024);
+    else dma4(r, lo + c * 4, (uint32_t)C::BV, base + C::VOFF + c * 256);
+  }
+  constexpr int VS = C::KF16 ? 0 : 32 * C::G;  // V scales after the K scales (4-bit keys)
+#pragma unroll
+  for (int c = 0; c < SplitDma<D, KC>::NSV; c++)
+    if (c * 64 + lane < 8 * C::G)
+      dma4(r, 4 * (c * 64 + lane), (uint32_t)(C::BS + VS), base + C::SOFF + VS + 256 * c);
+}
+
+// s_waitcnt vmcnt(n * per), n = 0..4 (wave-uniform): every load but the last n*per done.
+template <int PER>
+__device__ __forceinline__ void wait_all_but(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PER) : "memory"); break;
+  }
+}
+
 // s_waitcnt vmcnt(n) with n a multiple of the per-page DMA count: n = k * NDMA, k = pages
 // issued after the one about to be read. The compiler does not track LDS-DMA writes.
 template <int NDMA, int K>
@@ -179,7 +239,7 @@ __device__ __forceinline__ int dim_kslot(int e) {
   else return (e >> 1) | ((e & 1) << 2);
 }
 
-template <int D, typename TQ, int KCODEC, int NW>
+template <int D, typename TQ, int KCODEC, int NW, bool SPV>
 __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   using C = Cfg<D, KCODEC>;
   constexpr int G = C::G, BB = C::BB, NT = 64 * NW, V = D / 64;
@@ -223,6 +283,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   __shared__ float hml[8][2];                  // per head: max M and sum l of the workgroup
   __shared__ int last_flag;
   __shared__ int lead_n;                       // furthest page-loop step reached by a wave
+  __shared__ float smax[8];                    // sparse values: per head, the largest raw score
+                                               // any wave of the workgroup has seen
   __shared__ uint32_t sgn_s[D / 32];           // sigma bits, read once for the final un-rotation
   static_assert(NW >= 8, "one wave per query head in the rotations");
   // Aliases of the ring: the query operands live in the last slot of every wave until the
@@ -268,7 +330,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // that token's bytes valid); wave wl, which owns the last page, patches its staged copy
   // before computing it; wave wc stores the token to the pool after the page loop.
   constexpr int E = CodecCfg<D>::E;
-  const bool app = (a.knew != nullptr) && (s == ns - 1);
+  const bool app = !SPV && (a.knew != nullptr) && (s == ns - 1);
   const int plast = npages - 1, tnew = (L - 1) & 15;
   const int wc = NW - 1, wl = (plast - p0) % NW;
   float ynew[E];
@@ -303,7 +365,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int k = 0; k < 2; k++) {
       const int pp = p0 + wv + k * NW;
-      if (pp < p1) stage_page<D, KCODEC>(page_blk(k), slot_lds(k), lane);
+      if (pp < p1) {
+        if constexpr (SPV) stage_k<D, KCODEC>(page_blk(k), slot_lds(k), lane);
+        else stage_page<D, KCODEC>(page_blk(k), slot_lds(k), lane);
+      }
     }
   };
   if (app && wv == wc && lane < 32) {  // quantize the appended token before this wave's
@@ -354,6 +419,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     stage_first();
   }
   if (tid == 0) lead_n = 0;
+  if (tid < 8) smax[tid] = -INFINITY;
   __syncthreads();
   const bool live = hl < r;
   const bool hiLane = hr < 8;  // lanes 0..7 of a row finish page A of each step, 8..15 page B
@@ -525,6 +591,118 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
   };
 
+  // ---- sparse values: a page's values are loaded only when some weight of it can reach
+  // the threshold. p is relative to the running max when the page is scored, and the final
+  // weight exp(s - m_final) / l is never larger (m_final >= m, l >= 1), so a skipped page's
+  // tokens all have final weights below the threshold. The values of a step's pages are
+  // folded in at the next step, before that step may raise the running max: the order of
+  // the accumulator updates is the same as in the dense loop.
+  float ppr[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // previous step: this lane's p
+  int pneed = 0;                            // bit 0: page A's values loaded, bit 1: page B's
+  int ppa = 0, pna = 0;                     // previous step: page A, and its wave page number
+  int nskip = 0;                            // pages of this wave whose values were skipped
+  auto pv_prev = [&]() {
+    const uint8_t* sA = ring[pna % NSLOT][wv];
+    const uint8_t* sB = ring[(pna + 1) % NSLOT][wv];
+    uint32_t vst[2 * G];
+    if ((hiLane ? (pneed & 1) : (pneed & 2)) != 0) {
+      load_scales(hiLane ? sA : sB, vst, 1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2 * G; i++) vst[i] = 0u;
+    }
+    const int pb = ppa + NW;
+    if (ppa == ptail || pb == ptail || pb >= p1) {  // wave-uniform: a partial or missing page
+      const int pm = hiLane ? ppa : pb;
+      const int lim = (pm >= p1) ? 0 : (pm == ptail ? ltail : 16);
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        if (4 * jq + e >= lim) {
+#pragma unroll
+          for (int g = 0; g < G; g += 2) vst[(e * G + g) >> 1] = 0u;  // slot may hold garbage
+        }
+    }
+    uint32_t vwA[G], vwB[G];
+#pragma unroll
+    for (int g = 0; g < G; g++) vwA[g] = vwB[g] = 0u;
+    if (pneed & 1) load_idx(sA, vwA, 1);
+    if (pneed & 2) load_idx(sB, vwB, 1);
+    auto vsc = [&](int e, int g) { return (float)as_h2(vst[(e * G + g) >> 1])[(e * G + g) & 1]; };
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+      const f16x4 own = {(f16)__builtin_fmaf(ppr[0], vsc(0, g), 0.0f), (f16)__builtin_fmaf(ppr[2], vsc(2, g), 0.0f),
+                         (f16)__builtin_fmaf(ppr[1], vsc(1, g), 0.0f), (f16)__builtin_fmaf(ppr[3], vsc(3, g), 0.0f)};
+      const u32x2 o2 = __builtin_bit_cast(u32x2, own);
+      const uint32_t x0 = __builtin_amdgcn_mov_dpp(o2[0], 0x128, 0xf, 0xf, true);
+      const uint32_t x1 = __builtin_amdgcn_mov_dpp(o2[1], 0x128, 0xf, 0xf, true);
+      const f16x8 P = __builtin_bit_cast(f16x8, u32x4{o2[0], o2[1], x0, x1});
+      const uint32_t a0 = vwA[g], a8 = a0 >> 8, bw = vwB[g], b8 = bw >> 8;
+      const f16x8 Ae = __builtin_bit_cast(f16x8, u32x4{a0 & 0x000F000Fu, a8 & 0x000F000Fu, bw & 0x000F000Fu, b8 & 0x000F000Fu});
+      const f16x8 Ao = __builtin_bit_cast(f16x8, u32x4{a0 & 0x00F000F0u, a8 & 0x00F000F0u, bw & 0x00F000F0u, b8 & 0x00F000F0u});
+      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, P, acc[2 * g], 0, 0, 0);
+      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ceven, P, acc[2 * g], 0, 0, 0);
+      acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, P, acc[2 * g + 1], 0, 0, 0);
+      acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codd, P, acc[2 * g + 1], 0, 0, 0);
+    }
+  };
+  const float vthr = a.v_thr;
+  auto sstep = [&](int na_, const uint8_t* slotA, const uint8_t* slotB, int pa, int pb) {
+    float sc[4], sA[4], sB[4];
+    scores(slotA, sA);
+    scores(slotB, sB);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float own = hiLane ? sA[e] : sB[e];
+      const float sup = hiLane ? sB[e] : sA[e];
+      sc[e] = own + dpp_ror8(sup);
+    }
+    if (pa == ptail || pb == ptail || pb >= p1) {  // wave-uniform: a partial or missing page
+      const int pm = hiLane ? pa : pb;
+      const int lim = (pm >= p1) ? 0 : (pm == ptail ? ltail : 16);
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        if (4 * jq + e >= lim) sc[e] = -INFINITY;
+    }
+    float cm = vmax3(sc[0], sc[1], vmax(sc[2], sc[3]));
+    cm = max_xor16(cm);
+    cm = max_xor32(cm);
+    cm = vmax(cm, dpp_ror8(cm));
+    if (pneed) pv_prev();  // the previous pages, at the running max they were weighted with
+    if (__any(cm > m_run)) {
+      const float mn = fmaxf(m_run, cm);
+      const float f = __builtin_amdgcn_exp2f((m_run - mn) * down);
+      l_run *= f;
+#pragma unroll
+      for (int t = 0; t < 2 * G; t++) acc[t] *= f;
+      m_run = mn;
+      nmd = -mn * down;
+    }
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], down, nmd));
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    // The skip test uses the largest score any wave of the workgroup has seen for the head
+    // (still at most the final maximum, so the bound on the final weight holds) and live
+    // heads only (the padding columns hl >= r carry no query).
+    if (jq == 0 && hr < 8) __hip_atomic_fetch_max(&smax[hl], cm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const float nsh = -fmaxf(smax[hl], cm) * down;
+    float pmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; e++) pmax = fmaxf(pmax, __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], down, nsh)));
+    if (!live) pmax = 0.0f;
+    const bool needA = __any(hiLane && pmax >= vthr);
+    const bool needB = pb < p1 && __any(!hiLane && pmax >= vthr);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the previous pages' values are read
+    if (needA) stage_v<D, KCODEC>(page_blk(na_), slot_lds(na_ % NSLOT), lane);
+    if (needB) stage_v<D, KCODEC>(page_blk(na_ + 1), slot_lds((na_ + 1) % NSLOT), lane);
+    nskip += (needA ? 0 : 1) + ((needB || pb >= p1) ? 0 : 1);
+    pneed = (needA ? 1 : 0) | (needB ? 2 : 0);
+    ppa = pa;
+    pna = na_;
+#pragma unroll
+    for (int e = 0; e < 4; e++) ppr[e] = pr[e];
+  };
+
   // Copy the appended token's bytes (indices and scales of token tnew) from tokblk into a
   // block: the pool (to_lds = false), or the staged LDS copy of the last page, whose index
   // regions are stored chunk by chunk as the page loads wrote them (see stage_page).
@@ -568,6 +746,36 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // prologue behind a full memory queue.
   int nis = min(npw, 2);
   const bool balance = npw >= 32;
+  if constexpr (SPV) {
+#pragma unroll 1
+    for (int na = 0; na < npw; na += 2) {
+      if (balance) {
+        int lead = 0;
+        if (lane == 0) lead = atomicMax(&lead_n, na);
+        const int lag = __builtin_amdgcn_readfirstlane(lead) - na;
+        if (lag >= 4) __builtin_amdgcn_s_setprio(3);
+        else if (lag >= 2) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+      const int nmax = min(npw, na + NSLOT);
+      int nk = 0;
+#pragma unroll
+      for (int k = 0; k < 4; k++)
+        if (nis < nmax) {
+          stage_k<D, KCODEC>(page_blk(nis), slot_lds(nis % NSLOT), lane);
+          nis++;
+          nk++;
+        }
+      // wait for this step's keys (page na + 1 may have been issued just now, when the ring
+      // has 3 slots) and for everything issued before this step (the previous step's values)
+      wait_all_but<SplitDma<D, KCODEC>::NK_OPS>(max(0, min(nk, nis - na - 2)));
+      const int pa = p0 + wv + NW * na;
+      sstep(na, ring[na % NSLOT][wv], ring[(na + 1) % NSLOT][wv], pa, pa + NW);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (pneed) pv_prev();
+    if (a.v_skipped && lane == 0 && nskip > 0) atomicAdd(a.v_skipped, (unsigned long long)nskip);
+  } else {
 #pragma unroll 1
   for (int na = 0; na < npw; na += 2) {
     // Keep the waves abreast on long loops. The hardware lets the oldest waves issue first,
@@ -596,6 +804,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       asm volatile("" ::: "memory");
     }
     step(ring[na % NSLOT][wv], ring[(na + 1) % NSLOT][wv], pa, pa + NW);
+  }
   }
 
   __builtin_amdgcn_s_setprio(0);
@@ -805,6 +1014,24 @@ __global__ __launch_bounds__(256) void lpt_order_kernel(const int32_t* __restric
   for (int p = t; p < B * Hkv; p += 256) order[p] = seq_of_rank[p / Hkv] * Hkv + p % Hkv;
 }
 
+template <int D, typename TQ, int NW, bool SPV>
+hipError_t launch_dqs(const LaunchDecode& a, hipStream_t st, unsigned grid) {
+  if (a.k_codec == TQ_CODEC_FP16) {
+    // fp16 keys: 8 waves; a staged page does not fit three times per wave at D = 256
+    if constexpr (D <= 128) {
+      constexpr int NWF = tq_decode_waves(D, TQ_CODEC_FP16);
+      hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_FP16, NWF, SPV>), dim3(grid), dim3(64 * NWF), 0, st, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (a.k_codec == TQ_CODEC_LLOYDMAX) {
+    hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_LLOYDMAX, NW, SPV>), dim3(grid), dim3(64 * NW), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_ABSMAX, NW, SPV>), dim3(grid), dim3(64 * NW), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
 template <int D, typename TQ, int NW>
 hipError_t launch_dq(const LaunchDecode& a, hipStream_t st) {
   if (a.order) {
@@ -813,20 +1040,8 @@ hipError_t launch_dq(const LaunchDecode& a, hipStream_t st) {
   }
   const int U = a.B * a.Hkv;
   const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * a.splits);
-  if (a.k_codec == TQ_CODEC_FP16) {
-    // fp16 keys: 8 waves; a staged page does not fit three times per wave at D = 256
-    if constexpr (D <= 128) {
-      constexpr int NWF = tq_decode_waves(D, TQ_CODEC_FP16);
-      hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_FP16, NWF>), dim3(grid), dim3(64 * NWF), 0, st, a);
-    } else {
-      return hipErrorInvalidValue;
-    }
-  } else if (a.k_codec == TQ_CODEC_LLOYDMAX) {
-    hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_LLOYDMAX, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
-  } else {
-    hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_ABSMAX, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
-  }
-  return hipGetLastError();
+  if (a.sparse_v) return launch_dqs<D, TQ, NW, true>(a, st, grid);
+  return launch_dqs<D, TQ, NW, false>(a, st, grid);
 }
 
 template <int D>

@@ -158,7 +158,8 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
                        const int32_t* block_table, int32_t max_pages_per_seq,
                        const int32_t* context_lens, int32_t max_context_len, float attn_scale,
                        int32_t num_splits, float* out, void* workspace, size_t workspace_bytes_,
-                       void* stream) {
+                       void* stream, int sparse_v = 0, float v_thr = 0.0f,
+                       unsigned long long* v_skipped = nullptr) {
   int rc = check_layout(L, true);
   if (rc != TQ_OK) return rc;
   rc = check_decode_common(L, q, q_dtype, batch, context_lens, max_context_len, attn_scale,
@@ -189,6 +190,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   a.splits = s.splits; a.pages_per_split = s.pages_per_split;
   a.attn_scale = attn_scale;
   a.knew = knew; a.vnew = vnew; a.new_dtype = new_dtype;
+  a.sparse_v = sparse_v; a.v_thr = v_thr; a.v_skipped = v_skipped;
   // longest-first order pays when the workgroups do not all fit on the chip at once
   const int64_t resident = (int64_t)num_cus() * (L->head_dim >= 256 ? 2 : 1);
   if (batch > 1 && batch <= TQ_LPT_MAX_BATCH && (int64_t)batch * L->num_kv_heads * s.splits > resident)
@@ -218,6 +220,18 @@ int tq_append_decode_attn(const tq_layout* L, void* pool, const void* k_last, co
   return decode_impl(L, pool, k_last, v_last, in_dtype, q, q_dtype, batch, block_table,
                      max_pages_per_seq, context_lens, max_context_len, attn_scale, num_splits, out,
                      workspace, workspace_bytes_, stream);
+}
+
+int tq_decode_attn_sparse_v(const tq_layout* L, const void* pool, const void* q, int32_t q_dtype,
+                            int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len, float attn_scale,
+                            float v_threshold, int32_t num_splits, float* out, void* workspace,
+                            size_t workspace_bytes_, unsigned long long* v_pages_skipped,
+                            void* stream) {
+  if (!(v_threshold >= 0.0f && v_threshold < 1.0f)) return TQ_EINVAL;
+  return decode_impl(L, pool, nullptr, nullptr, 0, q, q_dtype, batch, block_table,
+                     max_pages_per_seq, context_lens, max_context_len, attn_scale, num_splits, out,
+                     workspace, workspace_bytes_, stream, 1, v_threshold, v_pages_skipped);
 }
 
 int tq_dequant_ref(const tq_layout* L, const void* pool, int32_t batch, const int32_t* block_table,

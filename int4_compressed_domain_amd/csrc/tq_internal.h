@@ -32,6 +32,9 @@ struct LaunchDecode {
   const void* vnew;          //   [B][Hkv][D] of new_dtype, appended before attending
   int new_dtype;
   int32_t* order;            // optional [B * Hkv]: the unit that workgroup position u takes
+  int sparse_v;              // 1: values loaded only where a weight can reach v_thr
+  float v_thr;               // sparse values: weight threshold
+  unsigned long long* v_skipped;  // optional: pages whose values were skipped (added to)
 };
 
 hipError_t tq_launch_append(const LaunchAppend& a, hipStream_t st);

@@ -15,7 +15,8 @@ CODEC_ABSMAX, CODEC_LLOYDMAX, CODEC_FP16 = 0, 1, 2
 F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("tq_status_str", "tq_page_bytes", "tq_kv_append", "tq_decode_workspace_size",
-           "tq_decode_attn", "tq_append_decode_attn", "tq_dequant_ref", "tq_dense_decode_attn")
+           "tq_decode_attn", "tq_append_decode_attn", "tq_decode_attn_sparse_v", "tq_dequant_ref",
+           "tq_dense_decode_attn")
 
 
 class TQError(RuntimeError):
@@ -56,6 +57,10 @@ def _lib():
             L.tq_append_decode_attn.argtypes = [LP, P, P, P, i32, P, i32, i32, P, i32, P, i32, f32,
                                                 i32, P, P, sz, P]
             L.tq_append_decode_attn.restype = ctypes.c_int
+        if hasattr(L, "tq_decode_attn_sparse_v"):  # (absent from older builds of the library)
+            L.tq_decode_attn_sparse_v.argtypes = [LP, P, P, i32, i32, P, i32, P, i32, f32, f32, i32,
+                                                  P, P, sz, P, P]
+            L.tq_decode_attn_sparse_v.restype = ctypes.c_int
         L.tq_dequant_ref.argtypes = [LP, P, i32, P, i32, P, i32, i32, i32, P, P, P]
         L.tq_dense_decode_attn.argtypes = [LP, P, P, P, i32, i32, P, i32, f32, i32, P, P, sz, P]
         for name in ("tq_kv_append", "tq_decode_attn", "tq_dequant_ref", "tq_dense_decode_attn"):
@@ -130,6 +135,18 @@ def tq_append_decode_attn(layout, pool, k_last, v_last, q, block_table, context_
         _ptr(q), _dtype_code(q), q.shape[0], _ptr(block_table), block_table.shape[1],
         _ptr(context_lens), max_context_len, attn_scale, num_splits, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)), "tq_append_decode_attn")
+
+
+def tq_decode_attn_sparse_v(layout, pool, q, block_table, context_lens, max_context_len,
+                            attn_scale, v_threshold, out, workspace, num_splits=0,
+                            v_pages_skipped=None, stream=None):
+    """tq_decode_attn that skips the values of pages whose weights are all below v_threshold;
+    v_pages_skipped: optional int64 device tensor of one element, added to."""
+    _check(_lib().tq_decode_attn_sparse_v(
+        ctypes.byref(layout), _ptr(pool), _ptr(q), _dtype_code(q), q.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(context_lens), max_context_len, attn_scale, v_threshold,
+        num_splits, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(v_pages_skipped), _stream(stream)), "tq_decode_attn_sparse_v")
 
 
 def tq_dequant_ref(layout, pool, block_table, context_lens, max_context_len, k_out, v_out,

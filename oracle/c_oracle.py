@@ -61,6 +61,8 @@ def lib():
         L.or_keys_f16.argtypes = [P, i64, P]
         L.or_place_kf16.argtypes = [P, i32, i32, i64, P, P, P, P]
         L.or_fetch_kf16.argtypes = [P, i32, i32, i64, i32, i32, P, P, P]
+        L.or_decode_sparse_v.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, P, P, ctypes.c_float,
+                                         f64, P, i32, P, P]
         _lib = L
     return _lib
 
@@ -238,3 +240,25 @@ def dequant(pool, D, Hkv, sign_bits, block_table, context_lens, Lmax, basis, k_c
     lib().or_dequant(_p(pool), D, Hkv, k_codec, v_codec, _p(_c(sign_bits, np.uint32)), _p(bt),
                      bt.shape[1], _p(cl), B, Lmax, basis, _p(ko), _p(vo))
     return ko, vo
+
+
+def decode_sparse_v(pool, D, Hq, Hkv, sign_bits, block_table, context_lens, q, alpha, thr,
+                    pairs=None, k_codec=0, v_codec=0):
+    """Exact-weight sparse values: (out_sparse, bound) per (b, hq) pair (default: all), out
+    fp64 original basis; see or_decode_sparse_v."""
+    q = _c(q, np.float32)
+    B = q.shape[0]
+    bt = _c(block_table, np.int32)
+    cl = _c(context_lens, np.int32)
+    full = pairs is None
+    if full:
+        pairs = np.array([(b, h) for b in range(B) for h in range(Hq)], np.int32)
+    pairs = _c(pairs, np.int32).reshape(-1, 2)
+    out = np.empty((pairs.shape[0], D), np.float64)
+    bound = np.empty(pairs.shape[0], np.float64)
+    lib().or_decode_sparse_v(_p(pool), D, Hq, Hkv, k_codec, v_codec, _p(_c(sign_bits, np.uint32)),
+                             _p(bt), bt.shape[1], _p(cl), _p(q), float(alpha), float(thr), _p(pairs),
+                             pairs.shape[0], _p(out), _p(bound))
+    if full:
+        return out.reshape(B, Hq, D), bound.reshape(B, Hq)
+    return out, bound

@@ -468,6 +468,76 @@ void or_decode(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec, int v_c
   }
 }
 
+/* Sparse values [mlxcel "TurboQuant KV cache" manual, sparse-V threshold: value
+ * dequantization is skipped where the attention weight is below the threshold]. For each
+ * (b, hq) pair: the exact fp64 softmax weights w_t over all L tokens (as or_decode);
+ * out_sparse = R^-1 sum_{t: w_t >= thr} w_t v_t (the terms below the threshold dropped, the
+ * normalizer unchanged), and bound = sum_{t: w_t < thr} w_t * max_i |(R^-1 v_t)_i|, which
+ * bounds (max norm) the difference from the exact output made by dropping any subset of the
+ * terms below the threshold. */
+void or_decode_sparse_v(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec, int v_codec,
+                        const uint32_t* sign_bits, const int32_t* block_table, int max_pages,
+                        const int32_t* context_lens, const float* q, float alpha, double thr,
+                        const int32_t* pairs, int n_pairs, double* out_sparse, double* bound) {
+  uint16_t lut[16];
+  or_lut16(lut);
+  int r = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int p = 0; p < n_pairs; p++) {
+    int b = pairs[2 * p], hq = pairs[2 * p + 1], h = hq / r;
+    int64_t L = context_lens[b];
+    float qr[512];
+    double qd[512], acc[512], vt[512], ut[512];
+    const float* qx = q + ((int64_t)b * Hq + hq) * D;
+    if (k_codec == OR_KF16) {
+      for (int i = 0; i < D; i++) qd[i] = (double)qx[i];
+    } else {
+      or_rotate(qx, qr, D, sign_bits);
+      for (int i = 0; i < D; i++) qd[i] = (double)qr[i];
+    }
+    double* sc = malloc(sizeof(double) * (L > 0 ? L : 1));
+    uint8_t ku[512], vu[512];
+    uint16_t ks[16], vs[16], kh[512];
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < L; t++) {  /* scores */
+      int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
+      double dot = 0.0;
+      if (k_codec == OR_KF16) {
+        or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
+        for (int d = 0; d < D; d++) dot += qd[d] * or_f16_to_f64(kh[d]);
+      } else {
+        or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+        for (int d = 0; d < D; d++) dot += qd[d] * dequant1(k_codec, ku[d], ks[d / 32], lut);
+      }
+      sc[t] = (double)alpha * dot;
+      if (sc[t] > mx) mx = sc[t];
+    }
+    double l = 0.0;
+    for (int64_t t = 0; t < L; t++) l += exp(sc[t] - mx);
+    for (int i = 0; i < D; i++) acc[i] = 0.0;
+    double bnd = 0.0;
+    for (int64_t t = 0; t < L; t++) {  /* weighted values, kept or bounded */
+      int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
+      if (k_codec == OR_KF16) or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
+      else or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+      for (int d = 0; d < D; d++) vt[d] = dequant1(v_codec, vu[d], vs[d / 32], lut);
+      double w = exp(sc[t] - mx) / l;
+      if (w >= thr) {
+        for (int d = 0; d < D; d++) acc[d] += w * vt[d];
+      } else {
+        unrotate_f64(vt, ut, D, sign_bits);
+        double m = 0.0;
+        for (int d = 0; d < D; d++) m = fmax(m, fabs(ut[d]));
+        bnd += w * m;
+      }
+    }
+    if (L > 0) unrotate_f64(acc, out_sparse + (int64_t)p * D, D, sign_bits);
+    else for (int d = 0; d < D; d++) out_sparse[(int64_t)p * D + d] = 0.0;
+    bound[p] = bnd;
+    free(sc);
+  }
+}
+
 /* Dense dequantized K and V, [B][Hkv][Lmax][D] fp32, rows past a sequence's length zero.
  * basis 0: rotated (exact c*s products); basis 1: original, via or_unrotate_f32. */
 void or_dequant(const uint8_t* pool, int D, int Hkv, int k_codec, int v_codec,

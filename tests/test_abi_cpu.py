@@ -109,6 +109,22 @@ def test_append_decode_argument_validation():
     assert _append_decode(L, batch=0, kl=None, vl=None, q=None, out=None) == tq.TQ_OK
 
 
+def _sparse(L, thr=1e-6, batch=2, bt=FAKE, maxp=4, ctx=FAKE, maxctx=64, out=FAKE, ws=FAKE,
+            wsb=1 << 30, q=FAKE, skipped=None):
+    return tq.lib().tq_decode_attn_sparse_v(ctypes.byref(L), FAKE, q, tq.BF16, batch, bt, maxp, ctx,
+                                            maxctx, 0.1, thr, 0, out, ws, wsb, skipped, None)
+
+
+def test_sparse_v_argument_validation():
+    L = _layout()
+    assert _sparse(L, thr=-1e-6) == tq.TQ_EINVAL
+    assert _sparse(L, thr=1.0) == tq.TQ_EINVAL
+    assert _sparse(L, thr=float("nan")) == tq.TQ_EINVAL
+    assert _sparse(L, q=None) == tq.TQ_EINVAL
+    assert _sparse(L, wsb=16) == tq.TQ_ENOSPC
+    assert _sparse(L, batch=0, q=None, out=None) == tq.TQ_OK
+
+
 def test_workspace_size_formula():
     L = _layout()
     for batch, ctx, splits in ((1, 131072, 5), (16, 8192, 1), (3, 100, 100)):

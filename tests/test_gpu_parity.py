@@ -104,6 +104,50 @@ def test_fp16_keys(D, r):
         _check_case(c, num_splits=splits)
 
 
+def _sparse_gpu(c, thr, num_splits=0):
+    w = c.w
+    max_ctx = int(c.lens.max())
+    ws = torch.zeros(max(tq.tq_decode_workspace_size(c.layout, w.batch, max_ctx, num_splits), 4) // 4,
+                     dtype=torch.float32, device=DEV)
+    out = torch.full((w.batch, w.q_heads, w.head_dim), float("nan"), dtype=torch.float32, device=DEV)
+    skipped = torch.zeros(1, dtype=torch.int64, device=DEV)
+    tq.tq_decode_attn_sparse_v(c.layout, c.pool, c.q_dev, c.bt_dev, c.lens_dev, max_ctx, w.attn_scale,
+                               thr, out, ws, num_splits=num_splits, v_pages_skipped=skipped)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), int(skipped.item())
+
+
+@pytest.mark.parametrize("name,k_codec", [("llama70b_b1_128k", 0), ("gemma_d256_32k", 0),
+                                          ("mixed_serving", 1), ("llama70b_b1_128k", 2)])
+def test_sparse_values(name, k_codec):
+    """Sparse values: threshold 0 reproduces the dense decode bit for bit; at 1e-6 the
+    result stays within the tolerance plus the oracle's bound on the dropped terms
+    (sum of w_t |v_t| over weights below the threshold), for several split counts, and
+    spiky attention lets most value pages be skipped."""
+    base = W.WORKLOADS[name]
+    w = W.Workload(name + "_sv", 3, base.q_heads, base.kv_heads, base.head_dim, 3000, base.dtype,
+                   base.attn_scale, k_codec=k_codec, dist="lognormal_spikes")
+    _say("case sparse values", name, "k_codec", k_codec)
+    c = Case(w, seed=23, lens=[3000, 1234, 77])
+    c.fill()
+    dense = c.decode_gpu()
+    out0, sk0 = _sparse_gpu(c, 0.0)
+    assert sk0 == 0 and np.array_equal(out0, dense)
+    exact = c.decode_oracle()
+    _, bound = c_oracle.decode_sparse_v(c.opool, w.head_dim, w.q_heads, w.kv_heads, c.sb, c.bt,
+                                        c.lens, c.q32, w.attn_scale, 1e-6, k_codec=w.k_codec,
+                                        v_codec=w.v_codec)
+    total = int(np.sum((c.lens + 15) // 16)) * w.kv_heads
+    for splits in (0, 1, 3):
+        out, sk = _sparse_gpu(c, 1e-6, splits)
+        err = np.max(np.abs(out - exact), axis=2)
+        lim = ATTN_TOL * np.max(np.abs(exact), axis=2) + bound
+        _say("   splits %d: skipped %d of %d value pages, max err %.3e" % (splits, sk, total, err.max()))
+        assert np.all(np.isfinite(out)) and np.all(err <= lim)
+        if splits == 1:
+            assert sk > 0, "spiky attention should let value pages be skipped"
+
+
 @pytest.mark.parametrize("k_codec", [0, 1, 2])
 def test_ragged_edge_lengths(k_codec):
     lens = [0, 1, 15, 16, 17, 33, 48, 250]

@@ -354,6 +354,43 @@ def test_fp16_key_memory_formula(coracle):
         assert per_token / (2 * D * 2) == pytest.approx((16 + 4) / (2 * 16) + 16 / 32 / (2 * 16))
 
 
+def test_sparse_values_against_plain_softmax(coracle):
+    """Sparse values [mlxcel manual, sparse-V threshold]: with lossless k, v, q the oracle's
+    kept-terms output and drop bound equal a plain softmax computed here, for thresholds
+    from 0 (nothing dropped: the ordinary decode) to above every weight (all dropped)."""
+    D, L, Hkv, Hq = 64, 45, 1, 2
+    rng = np.random.default_rng(61)
+    sb = _sb(D, 2)
+    _, k = _exact_vectors(rng, L, D, sb, coracle)
+    _, v = _exact_vectors(rng, L, D, sb, coracle)
+    _, q = _exact_vectors(rng, Hq, D, sb, coracle)
+    k[5] *= 2.0    # a few dominant keys make most weights tiny
+    k[30] *= 2.0
+    k, v = k.reshape(L, 1, D), v.reshape(L, 1, D)
+    bt = np.array([[2, 0, 1]], np.int32)
+    pool = coracle.new_pool(3, Hkv, D)
+    coracle.append(pool, D, Hkv, k, v, W.slots_for(bt, 0, 0, L), sb)
+    cl = np.array([L], np.int32)
+    alpha = 0.02   # spreads the weights: each threshold below drops a different set
+    dense = coracle.decode(pool, D, Hq, Hkv, sb, bt, cl, q[None], alpha)
+    for thr in (0.0, 1e-6, 1e-3, 0.05, 2.0):
+        out, bound = coracle.decode_sparse_v(pool, D, Hq, Hkv, sb, bt, cl, q[None], alpha, thr)
+        for hq in range(Hq):
+            s_ = float(np.float32(alpha)) * (k[:, 0].astype(np.float64) @ q[hq].astype(np.float64))
+            w = np.exp(s_ - s_.max())
+            w /= w.sum()
+            keep = w >= thr
+            want = (w[keep] @ v[keep, 0].astype(np.float64)) if keep.any() else np.zeros(D)
+            want_bound = np.sum(w[~keep] * np.max(np.abs(v[~keep, 0].astype(np.float64)), axis=1))
+            assert np.max(np.abs(out[0, hq] - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+            assert bound[0, hq] == pytest.approx(want_bound, rel=1e-12, abs=1e-300)
+            # the bound covers dropping any subset of the terms below the threshold
+            assert np.max(np.abs(dense[0, hq] - out[0, hq])) <= bound[0, hq] * (1 + 1e-12) + 1e-12
+        if thr == 0.0:
+            assert np.all(bound == 0.0)
+            assert np.max(np.abs(out - dense)) <= 1e-12 * np.max(np.abs(dense))
+
+
 def test_codec_alone_lossless_at_d128(orc):
     """D=128 has an irrational rho, so check the codec stage on pre-rotated integers."""
     rng = np.random.default_rng(5)
