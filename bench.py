@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--min-pool-bytes", type=float, default=1.0 * 2 ** 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true", help="skip the fp16 GPU baseline")
+    ap.add_argument("--sparse-v", type=float, default=None, metavar="THR",
+                    help="decode with sparse values at this weight threshold (the step is then the "
+                         "new tokens' append + tq_decode_attn_sparse_v)")
     ap.add_argument("--profile", type=int, default=0,
                     help="run this many eager steps and exit: for profilers")
     return ap.parse_args()
@@ -107,6 +110,11 @@ class Setup:
         self.n_new = int(np.count_nonzero(self.lens)) + w.prefill
         self.k_last = to_dev(k_last, w.dtype, dev)
         self.v_last = to_dev(v_last, w.dtype, dev)
+        last = np.array([W.slots_for(self.bt, b, int(L) - 1, int(L))[0] if L > 0 else -1
+                         for b, L in enumerate(self.lens)], np.int64)
+        self.slots_last = torch.from_numpy(last).to(dev)
+        self.sparse_v = args.sparse_v
+        self.v_skipped = torch.zeros(1, dtype=torch.int64, device=dev)
         ncopy = max(2, int(math.ceil(args.min_pool_bytes / max(pool_bytes, 1))))
         self.pools = [pool] + [pool.clone() for _ in range(ncopy - 1)]
         self.q32, qst = W.queries(w, 0)
@@ -119,6 +127,7 @@ class Setup:
         self.ws = torch.zeros(max(ws, 4) // 4, dtype=torch.float32, device=dev)
         self.out = torch.empty((w.batch, w.q_heads, D), dtype=torch.float32, device=dev)
         self.alg_bytes = W.algorithmic_bytes(w, self.lens)
+        self.kv_bytes_all = W.algorithmic_bytes(w, self.lens) - W.algorithmic_bytes(w, 0 * self.lens)
         self.kv_bytes = int(np.sum(self.lens, dtype=np.int64)) * Hkv * 2 * (D // 2 + 2 * (D // 32))
         log("pool copies: %d (%.2f GB)" % (ncopy, ncopy * pool_bytes / 1e9))
 
@@ -130,11 +139,19 @@ class Setup:
                             self.slots_pre)
 
     def decode(self, i):
-        """One launch: append every decoding sequence's newest token, then attend."""
+        """One launch: append every decoding sequence's newest token, then attend (sparse
+        values: the append, then the sparse decode)."""
         from int4_compressed_domain_amd import tq
-        tq.tq_append_decode_attn(self.layout, self.pools[i % len(self.pools)], self.k_last,
-                                 self.v_last, self.q, self.bt_dev, self.lens_dev, self.max_ctx,
-                                 self.w.attn_scale, self.out, self.ws, num_splits=self.splits)
+        pool = self.pools[i % len(self.pools)]
+        if self.sparse_v is not None:
+            tq.tq_kv_append(self.layout, pool, self.k_last, self.v_last, self.slots_last)
+            tq.tq_decode_attn_sparse_v(self.layout, pool, self.q, self.bt_dev, self.lens_dev,
+                                       self.max_ctx, self.w.attn_scale, self.sparse_v, self.out,
+                                       self.ws, num_splits=self.splits, v_pages_skipped=self.v_skipped)
+            return
+        tq.tq_append_decode_attn(self.layout, pool, self.k_last, self.v_last, self.q, self.bt_dev,
+                                 self.lens_dev, self.max_ctx, self.w.attn_scale, self.out, self.ws,
+                                 num_splits=self.splits)
 
     def step(self, i):
         self.prefill(i)
@@ -340,6 +357,25 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(name),
                      "kernel": "decode_fused", "mean_us": round(dec_mean, 3)},
     }
+    if S.sparse_v is not None:
+        # one more decode, counted alone: the share of (page, kv head) value blocks skipped
+        S.v_skipped.zero_()
+        S.decode(0)
+        torch.cuda.synchronize()
+        pages = int(np.sum((S.lens + 15) // 16)) * w.kv_heads
+        frac = int(S.v_skipped.item()) / max(1, pages)
+        D = w.head_dim
+        kpart = D * 2 if w.k_codec == W.CODEC_FP16 else D // 2 + 2 * (D // 32)
+        vpart = D // 2 + 2 * (D // 32)
+        moved = int(np.sum(S.lens, dtype=np.int64)) * w.kv_heads * (kpart + vpart * (1.0 - frac))
+        moved += S.alg_bytes - S.kv_bytes_all
+        rec["config"]["sparse_v_threshold"] = S.sparse_v
+        rec["sparse_v"] = {"threshold": S.sparse_v, "value_pages_skipped_frac": round(frac, 4),
+                           "bytes_moved_est": int(moved)}
+        # the dominant kernel's rate on the bytes it actually moves (keys + values not skipped)
+        rec["roofline"].update({"achieved": round(moved / (dec_mean * 1e-6) / 1e9, 2),
+                                "frac": round(moved / (dec_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "traffic": None, "kernel": "decode_fused (sparse values)"})
     if not args.no_baseline:
         base = fp16_baseline(S, min(args.steps, 20), 3, dev)
         base["speedup_of_fused"] = round(base["total_us"] / dec_mean, 2)

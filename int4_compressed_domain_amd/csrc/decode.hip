@@ -646,6 +646,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
   };
   const float vthr = a.v_thr;
+  float msh = -INFINITY;  // after the first step: the workgroup's largest score for this head
   auto sstep = [&](int na_, const uint8_t* slotA, const uint8_t* slotB, int pa, int pb) {
     float sc[4], sA[4], sB[4];
     scores(slotA, sA);
@@ -681,11 +682,12 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int e = 0; e < 4; e++) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], down, nmd));
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    // The skip test uses the largest score any wave of the workgroup has seen for the head
-    // (still at most the final maximum, so the bound on the final weight holds) and live
-    // heads only (the padding columns hl >= r carry no query).
-    if (jq == 0 && hr < 8) __hip_atomic_fetch_max(&smax[hl], cm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const float nsh = -fmaxf(smax[hl], cm) * down;
+    // The skip test uses the larger of the wave's running max and the workgroup's maximum
+    // over every wave's first step (msh, still at most the final maximum, so the bound on
+    // the final weight holds), and live heads only (padding columns hl >= r carry no query).
+    if (na_ == 0 && jq == 0 && hr < 8)
+      __hip_atomic_fetch_max(&smax[hl], cm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const float nsh = -fmaxf(msh, m_run) * down;
     float pmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; e++) pmax = fmaxf(pmax, __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], down, nsh)));
@@ -747,8 +749,14 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   int nis = min(npw, 2);
   const bool balance = npw >= 32;
   if constexpr (SPV) {
+    // The first step runs alone: every wave then shares its maxima (an exact max, so the
+    // snapshot and the skip decisions after it do not depend on timing).
 #pragma unroll 1
     for (int na = 0; na < npw; na += 2) {
+      if (na == 2) {  // wave-uniform; waves without a second step meet the barrier below
+        __syncthreads();
+        msh = smax[hl];
+      }
       if (balance) {
         int lead = 0;
         if (lane == 0) lead = atomicMax(&lead_n, na);
@@ -772,6 +780,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       const int pa = p0 + wv + NW * na;
       sstep(na, ring[na % NSLOT][wv], ring[(na + 1) % NSLOT][wv], pa, pa + NW);
     }
+    if (npw <= 2) __syncthreads();  // the first-step barrier of waves that never reached it
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (pneed) pv_prev();
     if (a.v_skipped && lane == 0 && nskip > 0) atomicAdd(a.v_skipped, (unsigned long long)nskip);
