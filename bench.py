@@ -215,7 +215,39 @@ def time_steps(S, steps, warmup):
     dec_ms, _ = _time_replays(graphs[1], reps)
     pre_ms = _time_replays(graphs[2], reps)[0] if len(graphs) > 2 else 0.0
     K = reps * n
+    # spread: events around single replays of the decode graph (n launches each)
+    per = []
+    for _ in range(min(reps, 60)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graphs[1].replay()
+        e1.record()
+        per.append((e0, e1))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) for a, b in per]) / n * 1e3
+    S.decode_pct = [round(float(x), 3) for x in np.percentile(us, [10, 50, 90])]
     return K, wall / K * 1e3, ev_ms / K, dec_ms / K * 1e3, pre_ms / K * 1e3
+
+
+def stream_read_peak(dev, gib=2.0):
+    """Measured HBM read rate of the library's plain streaming-read probe over gib GiB (best
+    of 10 after 2 untimed): the practical read peak to set the decode's rate against."""
+    import torch
+    from int4_compressed_domain_amd import tq
+    x = torch.ones(int(gib * 2 ** 30) // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(1 << 19, dtype=torch.int32, device=dev)
+    best = float("inf")
+    for i in range(12):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tq.tq_stream_read_probe(x, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            best = min(best, e0.elapsed_time(e1))
+    del x, sink
+    torch.cuda.empty_cache()
+    return gib * 2 ** 30 / (best * 1e-3) / 1e9
 
 
 def fp16_baseline(S, steps, warmup, dev):
@@ -356,6 +388,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(name),
                      "kernel": "decode_fused", "mean_us": round(dec_mean, 3)},
+        "decode_us_p10_p50_p90": S.decode_pct,
     }
     if S.sparse_v is not None:
         # one more decode, counted alone: the share of (page, kv head) value blocks skipped
@@ -382,6 +415,9 @@ def main():
         rec["fp16_dequant_then_attend"] = base
     del S
     torch.cuda.empty_cache()
+    peak_meas = stream_read_peak(dev)
+    rec["roofline"]["measured_read_peak"] = round(peak_meas, 1)
+    rec["roofline"]["frac_of_measured_peak"] = round(rec["roofline"]["achieved"] / peak_meas, 4)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

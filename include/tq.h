@@ -196,6 +196,12 @@ int tq_decode_attn_sparse_v(const tq_layout* layout, const void* pool, const voi
                             size_t workspace_bytes, unsigned long long* v_pages_skipped,
                             void* stream);
 
+/* Measurement aid, not part of the method: reads bytes (a multiple of 16) of buf with a plain
+ * streaming kernel, so that the decode's HBM rate can be set against the read rate a simple
+ * kernel reaches on the same GPU. sink: device scratch of >= 8 * CUs * 256 * 4 bytes
+ * (TQ_ENOSPC otherwise; 2 MiB always suffices), overwritten with the words' XOR per thread. */
+int tq_stream_read_probe(const void* buf, size_t bytes, void* sink, size_t sink_bytes, void* stream);
+
 /* Dequantize reference: dense K and V, [batch][num_kv_heads][max_context_len][head_dim]
  * of out_dtype (TQ_F32 or TQ_F16), rows at or past a sequence's length set to zero.
  * to_original_basis = 0: values (u-8)*s or LUT_u*n in the rotated basis (exact products,

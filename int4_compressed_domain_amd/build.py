@@ -21,6 +21,7 @@ SOURCES = {
     "dequant.hip": ["-ffp-contract=off"],
     "decode.hip": [],
     "dense.hip": [],
+    "stream_read.hip": [],
 }
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -38,6 +38,7 @@ struct LaunchDecode {
 };
 
 hipError_t tq_launch_append(const LaunchAppend& a, hipStream_t st);
+hipError_t tq_launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t st);
 hipError_t tq_launch_decode(const LaunchDecode& a, hipStream_t st);
 hipError_t tq_launch_dense_decode(const LaunchDecode& a, hipStream_t st);
 

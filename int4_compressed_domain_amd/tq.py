@@ -16,7 +16,7 @@ F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("tq_status_str", "tq_page_bytes", "tq_kv_append", "tq_decode_workspace_size",
            "tq_decode_attn", "tq_append_decode_attn", "tq_decode_attn_sparse_v", "tq_dequant_ref",
-           "tq_dense_decode_attn")
+           "tq_dense_decode_attn", "tq_stream_read_probe")
 
 
 class TQError(RuntimeError):
@@ -62,6 +62,9 @@ def _lib():
                                                   P, P, sz, P, P]
             L.tq_decode_attn_sparse_v.restype = ctypes.c_int
         L.tq_dequant_ref.argtypes = [LP, P, i32, P, i32, P, i32, i32, i32, P, P, P]
+        if hasattr(L, "tq_stream_read_probe"):
+            L.tq_stream_read_probe.argtypes = [P, sz, P, sz, P]
+            L.tq_stream_read_probe.restype = ctypes.c_int
         L.tq_dense_decode_attn.argtypes = [LP, P, P, P, i32, i32, P, i32, f32, i32, P, P, sz, P]
         for name in ("tq_kv_append", "tq_decode_attn", "tq_dequant_ref", "tq_dense_decode_attn"):
             getattr(L, name).restype = ctypes.c_int
@@ -163,3 +166,10 @@ def tq_dense_decode_attn(layout, k, v, q, context_lens, max_context_len, attn_sc
         ctypes.byref(layout), _ptr(k), _ptr(v), _ptr(q), _dtype_code(q), q.shape[0],
         _ptr(context_lens), max_context_len, attn_scale, num_splits, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)), "tq_dense_decode_attn")
+
+
+def tq_stream_read_probe(buf, sink, stream=None):
+    """Read every byte of buf (a device tensor) with the plain streaming kernel."""
+    _check(_lib().tq_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                       sink.numel() * sink.element_size(), _stream(stream)),
+           "tq_stream_read_probe")

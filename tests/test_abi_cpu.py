@@ -125,6 +125,14 @@ def test_sparse_v_argument_validation():
     assert _sparse(L, batch=0, q=None, out=None) == tq.TQ_OK
 
 
+def test_stream_read_probe_validation():
+    probe = tq.lib().tq_stream_read_probe
+    assert probe(FAKE, 0, None, 0, None) == tq.TQ_OK          # nothing to read
+    assert probe(None, 64, FAKE, 1 << 21, None) == tq.TQ_EINVAL
+    assert probe(FAKE, 60, FAKE, 1 << 21, None) == tq.TQ_EINVAL  # not a multiple of 16
+    assert probe(FAKE, 64, FAKE, 16, None) == tq.TQ_ENOSPC      # sink too small
+
+
 def test_workspace_size_formula():
     L = _layout()
     for batch, ctx, splits in ((1, 131072, 5), (16, 8192, 1), (3, 100, 100)):
