@@ -63,6 +63,8 @@ def lib():
         L.or_fetch_kf16.argtypes = [P, i32, i32, i64, i32, i32, P, P, P]
         L.or_decode_sparse_v.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, P, P, ctypes.c_float,
                                          f64, P, i32, P, P]
+        L.or_decode_hotcold.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, P, P, P, P, i32, P,
+                                        ctypes.c_float, P, i32, P]
         _lib = L
     return _lib
 
@@ -262,3 +264,25 @@ def decode_sparse_v(pool, D, Hq, Hkv, sign_bits, block_table, context_lens, q, a
     if full:
         return out.reshape(B, Hq, D), bound.reshape(B, Hq)
     return out, bound
+
+
+def decode_hotcold(pool, D, Hq, Hkv, sign_bits, block_table, cold_lens, hot_k, hot_v, hot_lens, q,
+                   alpha, pairs=None, k_codec=0, v_codec=0):
+    """fp64 decode over cold (pool) + hot tokens; hot_k, hot_v: [B, Hkv, hot_cap, D] fp16 (or
+    their uint16 bits), original basis. Returns [B, Hq, D] (or [n_pairs, D])."""
+    q = _c(q, np.float32)
+    B = q.shape[0]
+    bt = _c(block_table, np.int32)
+    cl = _c(cold_lens, np.int32)
+    hl = _c(hot_lens, np.int32)
+    hk = np.ascontiguousarray(hot_k).view(np.uint16)
+    hv = np.ascontiguousarray(hot_v).view(np.uint16)
+    full = pairs is None
+    if full:
+        pairs = np.array([(b, h) for b in range(B) for h in range(Hq)], np.int32)
+    pairs = _c(pairs, np.int32).reshape(-1, 2)
+    out = np.empty((pairs.shape[0], D), np.float64)
+    lib().or_decode_hotcold(_p(pool), D, Hq, Hkv, k_codec, v_codec, _p(_c(sign_bits, np.uint32)), _p(bt),
+                            bt.shape[1], _p(cl), _p(hk), _p(hv), _p(hl), hk.shape[2], _p(q), float(alpha),
+                            _p(pairs), pairs.shape[0], _p(out))
+    return out.reshape(B, Hq, D) if full else out

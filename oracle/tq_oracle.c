@@ -538,6 +538,83 @@ void or_decode_sparse_v(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec
   }
 }
 
+/* Hot/cold cache [mlxcel "TurboQuant KV cache" manual, delegated cache: the most recent
+ * tokens are kept in fp16, the older ones in the packed form]. Sequence b attends to its
+ * cold tokens 0..cold_lens[b]-1 in the pool (as or_decode) and then to its hot tokens,
+ * hot_k / hot_v [B][Hkv][hot_cap][D] fp16 bits in the original basis, hot_lens[b] of them.
+ * One softmax over all of them, in fp64; out is in the original basis. */
+void or_decode_hotcold(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec, int v_codec,
+                       const uint32_t* sign_bits, const int32_t* block_table, int max_pages,
+                       const int32_t* cold_lens, const uint16_t* hot_k, const uint16_t* hot_v,
+                       const int32_t* hot_lens, int hot_cap, const float* q, float alpha,
+                       const int32_t* pairs, int n_pairs, double* out) {
+  uint16_t lut[16];
+  or_lut16(lut);
+  int r = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int p = 0; p < n_pairs; p++) {
+    int b = pairs[2 * p], hq = pairs[2 * p + 1], h = hq / r;
+    int64_t Lc = cold_lens[b], Lh = hot_lens[b], L = Lc + Lh;
+    const float* qx = q + ((int64_t)b * Hq + hq) * D;
+    float qr[512];
+    double qo[512], qc[512], accc[512], acch[512], tmp[512];
+    for (int i = 0; i < D; i++) qo[i] = (double)qx[i];
+    if (k_codec == OR_KF16) {
+      for (int i = 0; i < D; i++) qc[i] = qo[i];
+    } else {
+      or_rotate(qx, qr, D, sign_bits);
+      for (int i = 0; i < D; i++) qc[i] = (double)qr[i];
+    }
+    double* sc = malloc(sizeof(double) * (L > 0 ? L : 1));
+    uint8_t ku[512], vu[512];
+    uint16_t ks[16], vs[16], kh[512];
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < Lc; t++) {  /* cold scores */
+      int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
+      double dot = 0.0;
+      if (k_codec == OR_KF16) {
+        or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
+        for (int d = 0; d < D; d++) dot += qc[d] * or_f16_to_f64(kh[d]);
+      } else {
+        or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+        for (int d = 0; d < D; d++) dot += qc[d] * dequant1(k_codec, ku[d], ks[d / 32], lut);
+      }
+      sc[t] = (double)alpha * dot;
+    }
+    const uint16_t* hk = hot_k + (((int64_t)b * Hkv + h) * hot_cap) * D;
+    const uint16_t* hv = hot_v + (((int64_t)b * Hkv + h) * hot_cap) * D;
+    for (int64_t t = 0; t < Lh; t++) {  /* hot scores: original basis */
+      double dot = 0.0;
+      for (int d = 0; d < D; d++) dot += qo[d] * or_f16_to_f64(hk[t * D + d]);
+      sc[Lc + t] = (double)alpha * dot;
+    }
+    for (int64_t t = 0; t < L; t++) if (sc[t] > mx) mx = sc[t];
+    double l = 0.0;
+    for (int i = 0; i < D; i++) { accc[i] = 0.0; acch[i] = 0.0; }
+    for (int64_t t = 0; t < Lc; t++) {  /* cold values, rotated basis */
+      int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
+      if (k_codec == OR_KF16) or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
+      else or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+      double w = exp(sc[t] - mx);
+      l += w;
+      for (int d = 0; d < D; d++) accc[d] += w * dequant1(v_codec, vu[d], vs[d / 32], lut);
+    }
+    for (int64_t t = 0; t < Lh; t++) {  /* hot values, original basis */
+      double w = exp(sc[Lc + t] - mx);
+      l += w;
+      for (int d = 0; d < D; d++) acch[d] += w * or_f16_to_f64(hv[t * D + d]);
+    }
+    double* o = out + (int64_t)p * D;
+    if (L == 0) {
+      for (int d = 0; d < D; d++) o[d] = 0.0;
+    } else {
+      unrotate_f64(accc, tmp, D, sign_bits);
+      for (int d = 0; d < D; d++) o[d] = (tmp[d] + acch[d]) / l;
+    }
+    free(sc);
+  }
+}
+
 /* Dense dequantized K and V, [B][Hkv][Lmax][D] fp32, rows past a sequence's length zero.
  * basis 0: rotated (exact c*s products); basis 1: original, via or_unrotate_f32. */
 void or_dequant(const uint8_t* pool, int D, int Hkv, int k_codec, int v_codec,

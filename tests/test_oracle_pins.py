@@ -391,6 +391,51 @@ def test_sparse_values_against_plain_softmax(coracle):
             assert np.max(np.abs(out - dense)) <= 1e-12 * np.max(np.abs(dense))
 
 
+@pytest.mark.parametrize("k_codec", [0, 2])
+def test_hot_cold_equals_plain_attention(coracle, k_codec):
+    """Hot/cold cache [mlxcel manual, delegated cache]: the first tokens in the packed pool
+    (lossless keys and values), the rest in fp16 in the hot tail; decode equals plain
+    softmax attention over all tokens. Also: an empty hot tail gives the ordinary decode and
+    an empty cold part plain attention over the hot tokens."""
+    D, Hkv, Hq, L, Lc, cap = 64, 2, 4, 50, 33, 24
+    rng = np.random.default_rng(71 + k_codec)
+    sb = _sb(D, 6)
+    _, k = _exact_vectors(rng, L * Hkv, D, sb, coracle)
+    _, v = _exact_vectors(rng, L * Hkv, D, sb, coracle)
+    k = k.reshape(L, Hkv, D)
+    v = v.reshape(L, Hkv, D)
+    assert np.array_equal(k.astype(np.float16).astype(np.float32), k)   # fp16-exact too
+    assert np.array_equal(v.astype(np.float16).astype(np.float32), v)
+    _, q = _exact_vectors(rng, Hq, D, sb, coracle)    # R(q) exact: cold scores lose nothing
+    q = q[None]
+    bt = np.array([[3, 1, 0]], np.int32)
+    pool = coracle.new_pool(4, Hkv, D, k_codec)
+    coracle.append(pool, D, Hkv, k[:Lc], v[:Lc], W.slots_for(bt, 0, 0, Lc), sb, k_codec, 0)
+    hk = np.zeros((1, Hkv, cap, D), np.float16)
+    hv = np.zeros((1, Hkv, cap, D), np.float16)
+    hk[0, :, :L - Lc] = k[Lc:].transpose(1, 0, 2)
+    hv[0, :, :L - Lc] = v[Lc:].transpose(1, 0, 2)
+    alpha = 0.0625
+    def plain(kk, vv):
+        out = np.zeros((Hq, D))
+        for hq in range(Hq):
+            h = hq // (Hq // Hkv)
+            s_ = alpha * (kk[:, h].astype(np.float64) @ q[0, hq].astype(np.float64))
+            w = np.exp(s_ - s_.max())
+            out[hq] = (w @ vv[:, h].astype(np.float64)) / w.sum()
+        return out
+    cases = [(Lc, L - Lc, plain(k, v)),                 # cold + hot
+             (Lc, 0, None),                              # no hot tail: the ordinary decode
+             (0, L - Lc, plain(k[Lc:], v[Lc:]))]         # hot tokens only
+    for lc, lh, want in cases:
+        got = coracle.decode_hotcold(pool, D, Hq, Hkv, sb, bt, np.array([lc], np.int32), hk, hv,
+                                     np.array([lh], np.int32), q, alpha, k_codec=k_codec)
+        if want is None:
+            want = coracle.decode(pool, D, Hq, Hkv, sb, bt, np.array([lc], np.int32), q, alpha,
+                                  k_codec=k_codec)[0]
+        assert np.max(np.abs(got[0] - want)) <= 1e-12 * np.max(np.abs(want))
+
+
 def test_codec_alone_lossless_at_d128(orc):
     """D=128 has an irrational rho, so check the codec stage on pre-rotated integers."""
     rng = np.random.default_rng(5)
