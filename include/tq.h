@@ -121,8 +121,9 @@ int tq_kv_append(const tq_layout* layout, void* pool, const void* k, const void*
                  int32_t in_dtype, int32_t n_tokens, const int64_t* slot_mapping, void* stream);
 
 /* Workspace bytes tq_decode_attn needs for this batch and maximum context length:
- * TQ_DECODE_COUNTER_BYTES of counters, the split partials (batch * num_q_heads * splits *
- * (head_dim + 2) floats) and the workgroup order (batch * num_kv_heads int32).
+ * TQ_DECODE_COUNTER_BYTES of counters, the split partials (batch * num_q_heads * (splits + 1)
+ * * (head_dim + 2) floats: one row more for the fp16 tail of tq_decode_attn_hotcold) and the
+ * workgroup order (batch * num_kv_heads int32).
  * num_splits: 0 picks the split count automatically (as tq_decode_attn does); > 0 asks
  * for that many splits of the context (clamped to the number of pages). Returns 0 for
  * invalid arguments. */
@@ -195,6 +196,29 @@ int tq_decode_attn_sparse_v(const tq_layout* layout, const void* pool, const voi
                             int32_t num_splits, float* out, void* workspace,
                             size_t workspace_bytes, unsigned long long* v_pages_skipped,
                             void* stream);
+
+/* Decode attention over a hot/cold cache: the packed pool holds each sequence's older
+ * tokens and an fp16 tail its most recent ones [mlxcel "TurboQuant KV cache" manual,
+ * delegated cache: recent tokens in fp16, older ones in the 4-bit form]. Sequence b attends
+ * to its cold_lens[b] pool tokens and then to its hot_lens[b] tail tokens, one softmax over
+ * both; the tail is a split of its own whose partial joins the pool's splits in the merge.
+ *   cold_lens       device int32 [batch], as context_lens of tq_decode_attn (may be 0)
+ *   max_cold_len    host, an upper bound of cold_lens
+ *   hot_k, hot_v    device fp16 [batch][num_kv_heads][hot_cap][head_dim], original basis
+ *                   (not rotated); rows >= hot_lens[b] are not read
+ *   hot_lens        device int32 [batch], 0 <= hot_lens[b] <= hot_cap
+ *   hot_cap         1..1024 (TQ_EUNSUPPORTED otherwise)
+ *   other arguments, workspace (tq_decode_workspace_size(layout, batch, max_cold_len,
+ *   num_splits)) and errors as tq_decode_attn. A sequence with no tokens at all gets zeros.
+ * The caller writes new tokens into the tail as plain fp16 (nothing to quantize) and folds
+ * the oldest tail tokens into the pool with tq_kv_append when the tail is full. */
+int tq_decode_attn_hotcold(const tq_layout* layout, const void* pool, const void* q,
+                           int32_t q_dtype, int32_t batch, const int32_t* block_table,
+                           int32_t max_pages_per_seq, const int32_t* cold_lens,
+                           int32_t max_cold_len, const void* hot_k, const void* hot_v,
+                           const int32_t* hot_lens, int32_t hot_cap, float attn_scale,
+                           int32_t num_splits, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Measurement aid, not part of the method: reads bytes (a multiple of 16) of buf with a plain
  * streaming kernel, so that the decode's HBM rate can be set against the read rate a simple

@@ -265,15 +265,22 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int L = a.context_lens[b];
   const int npages = (L + 15) >> 4;
   const int pps = a.pages_per_split;
-  const int ns = (npages + pps - 1) / pps;
+  // Hot/cold: an fp16 tail of Lh recent tokens besides the pool's L; the workgroups of split
+  // index a.splits attend to it (hotwg) and publish it as one more partial, index ns_cold.
+  const int Lh = a.hot_k ? a.hot_lens[b] : 0;
+  const bool hotwg = a.hot_k != nullptr && s == a.splits;
+  const int ns_cold = (npages + pps - 1) / pps;
+  const int ns = ns_cold + (Lh > 0 ? 1 : 0);  // partials merged for this unit
   float* outp = a.out + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
-  if (npages == 0) {  // empty sequence: zero output, written by split 0
+  if (ns == 0) {  // empty sequence: zero output, written by split 0
     if (s == 0)
       for (int i = tid; i < r * D; i += NT) outp[i] = 0.0f;
     return;
   }
-  if (s >= ns) return;
-  const int p0 = s * pps, p1 = min(p0 + pps, npages);
+  if (hotwg ? Lh == 0 : s >= ns_cold) return;
+  const int srow = hotwg ? ns_cold : s;  // this workgroup's partial row
+  // (a hot workgroup has no pages: p0 >= p1, so it streams nothing)
+  const int p0 = hotwg ? npages : s * pps, p1 = hotwg ? npages : min(p0 + pps, npages);
 
   // page ring (per wave) -- reused after the page loop as the merge area
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT][NW][C::SLOT];
@@ -294,6 +301,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // instruction start in different LDS banks
   constexpr int MOW = D + 4;
   static_assert(NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4 <= NSLOT * NW * C::SLOT, "merge area must fit the ring");
+  static_assert(NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4 + 8 * (D + TQ_MAX_HOT) * 4 <= NSLOT * NW * C::SLOT,
+                "the fp16 tail's scratch must fit the ring");
   f16 (*bqs)[64][8] = reinterpret_cast<f16 (*)[64][8]>(&ring[NSLOT - 1][0][0]);
   float (*mo)[8][MOW] = reinterpret_cast<float (*)[8][MOW]>(&ring[0][0][0]);
   float (*wsh)[TQ_MAX_SPLITS] = reinterpret_cast<float (*)[TQ_MAX_SPLITS]>(&ring[0][0][0] + NW * 8 * MOW * 4);
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // that token's bytes valid); wave wl, which owns the last page, patches its staged copy
   // before computing it; wave wc stores the token to the pool after the page loop.
   constexpr int E = CodecCfg<D>::E;
-  const bool app = !SPV && (a.knew != nullptr) && (s == ns - 1);
+  const bool app = !SPV && !hotwg && (a.knew != nullptr) && (s == ns_cold - 1);
   const int plast = npages - 1, tnew = (L - 1) & 15;
   const int wc = NW - 1, wl = (plast - p0) % NW;
   float ynew[E];
@@ -866,11 +875,79 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
   }
   __syncthreads();
+  int nwsum = NW;  // waves whose results are summed below
+  if (hotwg) {
+    // The fp16 tail [mlxcel manual, delegated cache]: scores with the query as given,
+    // p = 2^(s - M) in the log2 domain as the pages' scores, values summed in the original
+    // basis and rotated into the cache basis (sign flip, butterflies, rho), then handed on
+    // as one wave's result with weight 1 and (M, l).
+    float* qs = reinterpret_cast<float*>(&ring[0][0][0] + NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4);
+    float* ps = qs + 8 * D;  // [8][hot_cap] scores, then weights; qs then holds the sums
+    const TQ* qh = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
+    const f16* hk = static_cast<const f16*>(a.hot_k) + ((int64_t)b * a.Hkv + h) * a.hot_cap * D;
+    const f16* hv = static_cast<const f16*>(a.hot_v) + ((int64_t)b * a.Hkv + h) * a.hot_cap * D;
+    const float qmul2 = a.attn_scale * TQ_LOG2E;
+    for (int i = tid; i < r * D; i += NT) qs[i] = widen(qh[i]) * qmul2;
+    __syncthreads();
+    for (int i = tid; i < Lh * r; i += NT) {
+      const int t = i / r, hd = i - t * r;
+      const f16* kr = hk + (int64_t)t * D;
+      float dot = 0.0f;
+      for (int d = 0; d < D; d += 8) {
+        const f16x8 k8 = *reinterpret_cast<const f16x8*>(kr + d);
+#pragma unroll
+        for (int e = 0; e < 8; e++) dot = __builtin_fmaf(qs[hd * D + d + e], (float)k8[e], dot);
+      }
+      ps[hd * a.hot_cap + t] = dot;
+    }
+    __syncthreads();
+    if (wv < r) {  // wave hd: M, p and l of head hd
+      float* pr = ps + wv * a.hot_cap;
+      float M = -INFINITY;
+      for (int t = lane; t < Lh; t += 64) M = fmaxf(M, pr[t]);
+      M = wave_max(M);
+      float l = 0.0f;
+      for (int t = lane; t < Lh; t += 64) {
+        const float p = __builtin_amdgcn_exp2f(pr[t] - M);
+        pr[t] = p;
+        l += p;
+      }
+      l = wave_sum(l);
+      if (lane == 0) {
+        hml[wv][0] = M;
+        hml[wv][1] = l;
+        mml[0][wv][0] = 1.0f;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < r * D; i += NT) {
+      const int hd = i / D, d = i - hd * D;
+      const float* pr = ps + hd * a.hot_cap;
+      float o = 0.0f;
+      for (int t = 0; t < Lh; t++) o = __builtin_fmaf(pr[t], (float)hv[(int64_t)t * D + d], o);
+      qs[i] = o;
+    }
+    __syncthreads();
+    if (wv < r) {
+      float x[V];
+#pragma unroll
+      for (int k = 0; k < V; k++) {
+        const int d = lane + 64 * k;
+        const float o = qs[wv * D + d];
+        x[k] = ((sgn_s[d >> 5] >> (d & 31)) & 1u) ? -o : o;
+      }
+      wave_fwht<V>(x, lane);
+#pragma unroll
+      for (int k = 0; k < V; k++) mo[0][wv][lane + 64 * k] = x[k] * rho;
+    }
+    nwsum = 1;
+    __syncthreads();
+  }
   // fin: [ngf][r][D] partial sums of the result (rotated basis), summed by the rotation below
   float* fin = &mo[0][0][0];
   int ngf = 1;
-  const int S = a.splits;
-  const int64_t prow = ((int64_t)u * S + s) * r;  // partial rows of this (unit, split)
+  const int S = a.splits + (a.hot_k ? 1 : 0);  // partial rows per unit
+  const int64_t prow = ((int64_t)u * S + srow) * r;  // partial rows of this (unit, split)
   if (ns == 1) {
     float ov[(8 * D + NT - 1) / NT];
 #pragma unroll
@@ -880,7 +957,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       if (i < r * D) {
         const int hd = i / D, d = i % D;
 #pragma unroll
-        for (int w = 0; w < NW; w++) o += mml[w][hd][0] * mo[w][hd][d];
+        for (int w = 0; w < NW; w++)
+          if (w < nwsum) o += mml[w][hd][0] * mo[w][hd][d];
         o /= hml[hd][1];
       }
       ov[j] = o;
@@ -894,7 +972,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       const int hd = i / D, d = i % D;
       float o = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; w++) o += mml[w][hd][0] * mo[w][hd][d];
+      for (int w = 0; w < NW; w++)
+        if (w < nwsum) o += mml[w][hd][0] * mo[w][hd][d];
       __hip_atomic_store(&a.part_o[(prow + hd) * D + d], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (d == 0) {
         __hip_atomic_store(&a.part_ml[2 * (prow + hd)], hml[hd][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1048,7 +1127,7 @@ hipError_t launch_dq(const LaunchDecode& a, hipStream_t st) {
     hipLaunchKernelGGL(lpt_order_kernel, dim3(1), dim3(256), 0, st, a.context_lens, a.B, a.Hkv, a.order);
   }
   const int U = a.B * a.Hkv;
-  const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * a.splits);
+  const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * (a.splits + (a.hot_k ? 1 : 0)));
   if (a.sparse_v) return launch_dqs<D, TQ, NW, true>(a, st, grid);
   return launch_dqs<D, TQ, NW, false>(a, st, grid);
 }

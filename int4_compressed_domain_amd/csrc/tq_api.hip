@@ -96,7 +96,7 @@ size_t workspace_bytes(const tq_layout* L, int B, int max_ctx, int requested) {
   const Split f = choose_split(B, L->num_kv_heads, L->head_dim, L->k_codec, max_ctx, requested);
   const Split d = choose_split_dense(B, L->num_kv_heads, max_ctx, requested);
   const int S = f.splits > d.splits ? f.splits : d.splits;
-  return TQ_DECODE_COUNTER_BYTES + partial_bytes(B, L->num_q_heads, L->head_dim, S) +
+  return TQ_DECODE_COUNTER_BYTES + partial_bytes(B, L->num_q_heads, L->head_dim, S + 1) +  // + the fp16 tail row
          (size_t)B * L->num_kv_heads * sizeof(int32_t);  // + the workgroup order
 }
 
@@ -159,7 +159,9 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
                        const int32_t* context_lens, int32_t max_context_len, float attn_scale,
                        int32_t num_splits, float* out, void* workspace, size_t workspace_bytes_,
                        void* stream, int sparse_v = 0, float v_thr = 0.0f,
-                       unsigned long long* v_skipped = nullptr) {
+                       unsigned long long* v_skipped = nullptr, const void* hot_k = nullptr,
+                       const void* hot_v = nullptr, const int32_t* hot_lens = nullptr,
+                       int hot_cap = 0) {
   int rc = check_layout(L, true);
   if (rc != TQ_OK) return rc;
   rc = check_decode_common(L, q, q_dtype, batch, context_lens, max_context_len, attn_scale,
@@ -182,8 +184,9 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   a.context_lens = context_lens;
   a.sign_bits = L->sign_bits;
   a.out = out;
+  const int rows = s.splits + (hot_k ? 1 : 0);  // partial rows per unit
   a.part_o = ws;
-  a.part_ml = ws + (size_t)batch * L->num_q_heads * s.splits * L->head_dim;
+  a.part_ml = ws + (size_t)batch * L->num_q_heads * rows * L->head_dim;
   a.D = L->head_dim; a.Hq = L->num_q_heads; a.Hkv = L->num_kv_heads; a.B = batch;
   a.max_pages = max_pages_per_seq; a.max_ctx = max_context_len;
   a.q_dtype = q_dtype; a.k_codec = L->k_codec;
@@ -191,11 +194,12 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   a.attn_scale = attn_scale;
   a.knew = knew; a.vnew = vnew; a.new_dtype = new_dtype;
   a.sparse_v = sparse_v; a.v_thr = v_thr; a.v_skipped = v_skipped;
+  a.hot_k = hot_k; a.hot_v = hot_v; a.hot_lens = hot_lens; a.hot_cap = hot_cap;
   // longest-first order pays when the workgroups do not all fit on the chip at once
   const int64_t resident = (int64_t)num_cus() * (L->head_dim >= 256 ? 2 : 1);
   if (batch > 1 && batch <= TQ_LPT_MAX_BATCH && (int64_t)batch * L->num_kv_heads * s.splits > resident)
     a.order = reinterpret_cast<int32_t*>(
-        a.part_ml + (size_t)batch * L->num_q_heads * s.splits * 2);
+        a.part_ml + (size_t)batch * L->num_q_heads * rows * 2);
   return from_hip(tq_launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -232,6 +236,20 @@ int tq_decode_attn_sparse_v(const tq_layout* L, const void* pool, const void* q,
   return decode_impl(L, pool, nullptr, nullptr, 0, q, q_dtype, batch, block_table,
                      max_pages_per_seq, context_lens, max_context_len, attn_scale, num_splits, out,
                      workspace, workspace_bytes_, stream, 1, v_threshold, v_pages_skipped);
+}
+
+int tq_decode_attn_hotcold(const tq_layout* L, const void* pool, const void* q, int32_t q_dtype,
+                           int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                           const int32_t* cold_lens, int32_t max_cold_len, const void* hot_k,
+                           const void* hot_v, const int32_t* hot_lens, int32_t hot_cap,
+                           float attn_scale, int32_t num_splits, float* out, void* workspace,
+                           size_t workspace_bytes_, void* stream) {
+  if (hot_cap < 1 || hot_cap > TQ_MAX_HOT) return TQ_EUNSUPPORTED;
+  if (batch > 0 && (!hot_k || !hot_v || !hot_lens)) return TQ_EINVAL;
+  return decode_impl(L, pool, nullptr, nullptr, 0, q, q_dtype, batch, block_table,
+                     max_pages_per_seq, cold_lens, max_cold_len, attn_scale, num_splits, out,
+                     workspace, workspace_bytes_, stream, 0, 0.0f, nullptr, hot_k, hot_v, hot_lens,
+                     hot_cap);
 }
 
 int tq_stream_read_probe(const void* buf, size_t bytes, void* sink, size_t sink_bytes, void* stream) {

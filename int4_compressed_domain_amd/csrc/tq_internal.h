@@ -35,6 +35,10 @@ struct LaunchDecode {
   int sparse_v;              // 1: values loaded only where a weight can reach v_thr
   float v_thr;               // sparse values: weight threshold
   unsigned long long* v_skipped;  // optional: pages whose values were skipped (added to)
+  const void* hot_k;         // optional fp16 tail [B][Hkv][hot_cap][D] (original basis),
+  const void* hot_v;         //   hot_lens[b] tokens attended after the pool's context_lens[b]
+  const int32_t* hot_lens;
+  int hot_cap;
 };
 
 hipError_t tq_launch_append(const LaunchAppend& a, hipStream_t st);
@@ -67,4 +71,5 @@ constexpr int TQ_DECODE_WAVES = 4;   // dense baseline workgroups
 constexpr int TQ_MAX_SPLITS = 128;   // context splits per (sequence, kv head)
 constexpr int TQ_MAX_SPLIT_PAGES = 2048;  // pages per split (their ids are staged in LDS)
 constexpr int TQ_LPT_MAX_BATCH = 256;    // longest-first workgroup order up to this batch
+constexpr int TQ_MAX_HOT = 1024;         // fp16 tail tokens per (sequence, kv head)
 constexpr int TQ_MAX_UNITS = 1 << 20;  // sequences x kv heads per call

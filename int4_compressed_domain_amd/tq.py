@@ -16,7 +16,7 @@ F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("tq_status_str", "tq_page_bytes", "tq_kv_append", "tq_decode_workspace_size",
            "tq_decode_attn", "tq_append_decode_attn", "tq_decode_attn_sparse_v", "tq_dequant_ref",
-           "tq_dense_decode_attn", "tq_stream_read_probe")
+           "tq_dense_decode_attn", "tq_decode_attn_hotcold", "tq_stream_read_probe")
 
 
 class TQError(RuntimeError):
@@ -62,6 +62,10 @@ def _lib():
                                                   P, P, sz, P, P]
             L.tq_decode_attn_sparse_v.restype = ctypes.c_int
         L.tq_dequant_ref.argtypes = [LP, P, i32, P, i32, P, i32, i32, i32, P, P, P]
+        if hasattr(L, "tq_decode_attn_hotcold"):
+            L.tq_decode_attn_hotcold.argtypes = [LP, P, P, i32, i32, P, i32, P, i32, P, P, P, i32, f32,
+                                                 i32, P, P, sz, P]
+            L.tq_decode_attn_hotcold.restype = ctypes.c_int
         if hasattr(L, "tq_stream_read_probe"):
             L.tq_stream_read_probe.argtypes = [P, sz, P, sz, P]
             L.tq_stream_read_probe.restype = ctypes.c_int
@@ -173,3 +177,13 @@ def tq_stream_read_probe(buf, sink, stream=None):
     _check(_lib().tq_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                        sink.numel() * sink.element_size(), _stream(stream)),
            "tq_stream_read_probe")
+
+
+def tq_decode_attn_hotcold(layout, pool, q, block_table, cold_lens, max_cold_len, hot_k, hot_v,
+                           hot_lens, attn_scale, out, workspace, num_splits=0, stream=None):
+    """Decode over the pool's cold tokens and an fp16 tail (hot_k, hot_v: [B][Hkv][cap][D])."""
+    _check(_lib().tq_decode_attn_hotcold(
+        ctypes.byref(layout), _ptr(pool), _ptr(q), _dtype_code(q), q.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(cold_lens), max_cold_len, _ptr(hot_k), _ptr(hot_v), _ptr(hot_lens),
+        hot_k.shape[2], attn_scale, num_splits, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "tq_decode_attn_hotcold")

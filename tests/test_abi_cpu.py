@@ -133,13 +133,26 @@ def test_stream_read_probe_validation():
     assert probe(FAKE, 64, FAKE, 16, None) == tq.TQ_ENOSPC      # sink too small
 
 
+def test_hotcold_argument_validation():
+    L = _layout()
+    def hc(cap=16, hk=FAKE, hv=FAKE, hl=FAKE, batch=2, q=FAKE):
+        return tq.lib().tq_decode_attn_hotcold(ctypes.byref(L), FAKE, q, tq.BF16, batch, FAKE, 4, FAKE,
+                                               64, hk, hv, hl, cap, 0.1, 0, FAKE, FAKE, 1 << 30, None)
+    assert hc(cap=0) == tq.TQ_EUNSUPPORTED
+    assert hc(cap=1025) == tq.TQ_EUNSUPPORTED
+    assert hc(hk=None) == tq.TQ_EINVAL
+    assert hc(hl=None) == tq.TQ_EINVAL
+    assert hc(q=None) == tq.TQ_EINVAL
+    assert hc(batch=0, hk=None, hv=None, hl=None, q=None) == tq.TQ_OK
+
+
 def test_workspace_size_formula():
     L = _layout()
     for batch, ctx, splits in ((1, 131072, 5), (16, 8192, 1), (3, 100, 100)):
         pages = -(-ctx // 16)
         pps = -(-pages // min(splits, pages))
         S = -(-pages // pps)
-        want = (4 << 20) + batch * 32 * S * (128 + 2) * 4 + batch * 8 * 4  # counters + partials + order
+        want = (4 << 20) + batch * 32 * (S + 1) * (128 + 2) * 4 + batch * 8 * 4  # counters + partials + order
         assert tq.tq_decode_workspace_size(L, batch, ctx, splits) == want
     assert tq.tq_decode_workspace_size(_layout(head_dim=96), 1, 10, 0) == 0
 

@@ -148,6 +148,48 @@ def test_sparse_values(name, k_codec):
             assert sk > 0, "spiky attention should let value pages be skipped"
 
 
+@pytest.mark.parametrize("D,r,k_codec", [(128, 8, 0), (128, 4, 1), (128, 8, 2), (64, 2, 2),
+                                         (256, 2, 0)])
+def test_hot_cold(D, r, k_codec):
+    """Hot/cold cache: older tokens in the pool, the most recent in an fp16 tail, one softmax;
+    against the oracle for several split counts, with empty pools, empty and full tails, and
+    a sequence with no tokens at all."""
+    cold = [0, 1, 40, 300, 1000, 0]
+    hot = [5, 0, 64, 17, 1, 0]
+    cap = 64
+    w = W.Workload("hc_d%d_r%d_k%d" % (D, r, k_codec), len(cold), 2 * r, 2, D, max(cold), "bf16",
+                   1.0 / math.sqrt(D), k_codec=k_codec, dist="lognormal_spikes")
+    _say("case hot/cold D", D, "r", r, "k_codec", k_codec)
+    c = Case(w, seed=90 + D + r + k_codec, lens=cold)
+    c.fill()
+    hk = np.zeros((w.batch, w.kv_heads, cap, D), np.float16)
+    hv = np.zeros_like(hk)
+    for b in range(w.batch):
+        k32, v32, _, _ = W.seq_tokens(w, b, cold[b] + hot[b], c.seed, c.scales)
+        hk[b, :, :hot[b]] = k32[cold[b]:].transpose(1, 0, 2).astype(np.float16)
+        hv[b, :, :hot[b]] = v32[cold[b]:].transpose(1, 0, 2).astype(np.float16)
+    hl = np.array(hot, np.int32)
+    ref = c_oracle.decode_hotcold(c.opool, D, w.q_heads, w.kv_heads, c.sb, c.bt, c.lens, hk, hv, hl,
+                                  c.q32, w.attn_scale, k_codec=w.k_codec, v_codec=w.v_codec)
+    hk_d = torch.from_numpy(hk).to(DEV)
+    hv_d = torch.from_numpy(hv).to(DEV)
+    hl_d = torch.from_numpy(hl).to(DEV)
+    maxc = int(max(cold))
+    for splits in (0, 1, 3):
+        ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, w.batch, maxc, splits) // 4,
+                         dtype=torch.float32, device=DEV)
+        out = torch.full((w.batch, w.q_heads, D), float("nan"), dtype=torch.float32, device=DEV)
+        tq.tq_decode_attn_hotcold(c.layout, c.pool, c.q_dev, c.bt_dev, c.lens_dev, maxc, hk_d, hv_d,
+                                  hl_d, w.attn_scale, out, ws, num_splits=splits)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        err = attn_err(o, ref)
+        _say("   splits %d: max normwise err %.3e" % (splits, err.max()))
+        assert np.all(np.isfinite(o)) and err.max() <= ATTN_TOL
+        assert np.all(o[-1] == 0.0)
+        assert int(ws[:(4 << 20) // 4].view(torch.int32).abs().sum().item()) == 0, "counters not reset"
+
+
 @pytest.mark.parametrize("k_codec", [0, 1, 2])
 def test_ragged_edge_lengths(k_codec):
     lens = [0, 1, 15, 16, 17, 33, 48, 250]
