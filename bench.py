@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--min-pool-bytes", type=float, default=1.0 * 2 ** 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true", help="skip the fp16 GPU baseline")
+    ap.add_argument("--hot", type=int, default=0, metavar="N",
+                    help="hot/cold cache: the last N tokens of each sequence in an fp16 tail, the "
+                         "rest in the pool; the step is one tq_decode_attn_hotcold")
     ap.add_argument("--sparse-v", type=float, default=None, metavar="THR",
                     help="decode with sparse values at this weight threshold (the step is then the "
                          "new tokens' append + tq_decode_attn_sparse_v)")
@@ -87,11 +90,22 @@ class Setup:
         k_last = np.zeros((w.batch, Hkv, D), sdt)
         v_last = np.zeros((w.batch, Hkv, D), sdt)
         t_fill = time.time()
+        self.hot = getattr(args, "hot", 0)
+        if self.hot:  # hot/cold: the pool holds the first L - hot tokens, the tail the rest
+            self.cold_lens = np.maximum(self.lens - self.hot, 0).astype(np.int32)
+            self.hot_lens = (self.lens - self.cold_lens).astype(np.int32)
+            hk = np.zeros((w.batch, Hkv, self.hot, D), np.float16)
+            hv = np.zeros_like(hk)
         for b in range(w.batch):
             L = int(self.lens[b])
             k32, v32, kst, vst = W.seq_tokens(w, b, L, 0, scales)
-            for t0 in range(0, L - 1, 16384):
-                t1 = min(L - 1, t0 + 16384)
+            nres = int(self.cold_lens[b]) + 1 if self.hot else L   # tokens appended, plus one
+            if self.hot:
+                c0 = int(self.cold_lens[b])
+                hk[b, :, :L - c0] = k32[c0:].transpose(1, 0, 2).astype(np.float16)
+                hv[b, :, :L - c0] = v32[c0:].transpose(1, 0, 2).astype(np.float16)
+            for t0 in range(0, nres - 1, 16384):
+                t1 = min(nres - 1, t0 + 16384)
                 tq.tq_kv_append(self.layout, pool, to_dev(kst[t0:t1], w.dtype, dev),
                                 to_dev(vst[t0:t1], w.dtype, dev),
                                 torch.from_numpy(W.slots_for(self.bt, b, t0, t1)).to(dev))
@@ -110,6 +124,12 @@ class Setup:
         self.n_new = int(np.count_nonzero(self.lens)) + w.prefill
         self.k_last = to_dev(k_last, w.dtype, dev)
         self.v_last = to_dev(v_last, w.dtype, dev)
+        if self.hot:
+            self.hk = torch.from_numpy(hk).to(dev)
+            self.hv = torch.from_numpy(hv).to(dev)
+            self.cold_dev = torch.from_numpy(self.cold_lens).to(dev)
+            self.hot_dev = torch.from_numpy(self.hot_lens).to(dev)
+            self.max_cold = int(self.cold_lens.max())
         last = np.array([W.slots_for(self.bt, b, int(L) - 1, int(L))[0] if L > 0 else -1
                          for b, L in enumerate(self.lens)], np.int64)
         self.slots_last = torch.from_numpy(last).to(dev)
@@ -127,6 +147,9 @@ class Setup:
         self.ws = torch.zeros(max(ws, 4) // 4, dtype=torch.float32, device=dev)
         self.out = torch.empty((w.batch, w.q_heads, D), dtype=torch.float32, device=dev)
         self.alg_bytes = W.algorithmic_bytes(w, self.lens)
+        if self.hot:  # cold tokens packed, hot tokens fp16 K and V (4D bytes per token and head)
+            self.alg_bytes = (W.algorithmic_bytes(w, self.cold_lens)
+                              + int(np.sum(self.hot_lens, dtype=np.int64)) * Hkv * 4 * D)
         self.kv_bytes_all = W.algorithmic_bytes(w, self.lens) - W.algorithmic_bytes(w, 0 * self.lens)
         self.kv_bytes = int(np.sum(self.lens, dtype=np.int64)) * Hkv * 2 * (D // 2 + 2 * (D // 32))
         log("pool copies: %d (%.2f GB)" % (ncopy, ncopy * pool_bytes / 1e9))
@@ -143,6 +166,11 @@ class Setup:
         values: the append, then the sparse decode)."""
         from int4_compressed_domain_amd import tq
         pool = self.pools[i % len(self.pools)]
+        if self.hot:
+            tq.tq_decode_attn_hotcold(self.layout, pool, self.q, self.bt_dev, self.cold_dev,
+                                      self.max_cold, self.hk, self.hv, self.hot_dev,
+                                      self.w.attn_scale, self.out, self.ws, num_splits=self.splits)
+            return
         if self.sparse_v is not None:
             tq.tq_kv_append(self.layout, pool, self.k_last, self.v_last, self.slots_last)
             tq.tq_decode_attn_sparse_v(self.layout, pool, self.q, self.bt_dev, self.lens_dev,
@@ -390,6 +418,9 @@ def main():
                      "kernel": "decode_fused", "mean_us": round(dec_mean, 3)},
         "decode_us_p10_p50_p90": S.decode_pct,
     }
+    if S.hot:
+        rec["config"]["hot_tail"] = S.hot
+        rec["roofline"].update({"traffic": None, "kernel": "decode_fused (hot/cold)"})
     if S.sparse_v is not None:
         # one more decode, counted alone: the share of (page, kv head) value blocks skipped
         S.v_skipped.zero_()
@@ -402,14 +433,14 @@ def main():
         vpart = D // 2 + 2 * (D // 32)
         moved = int(np.sum(S.lens, dtype=np.int64)) * w.kv_heads * (kpart + vpart * (1.0 - frac))
         moved += S.alg_bytes - S.kv_bytes_all
-        rec["config"]["sparse_v_threshold"] = S.sparse_v
+        rec["config"]["sparse_v_threshold"] = S.sparse_v  # (value pages skipped below)
         rec["sparse_v"] = {"threshold": S.sparse_v, "value_pages_skipped_frac": round(frac, 4),
                            "bytes_moved_est": int(moved)}
         # the dominant kernel's rate on the bytes it actually moves (keys + values not skipped)
         rec["roofline"].update({"achieved": round(moved / (dec_mean * 1e-6) / 1e9, 2),
                                 "frac": round(moved / (dec_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                 "traffic": None, "kernel": "decode_fused (sparse values)"})
-    if not args.no_baseline:
+    if not args.no_baseline and not S.hot:
         base = fp16_baseline(S, min(args.steps, 20), 3, dev)
         base["speedup_of_fused"] = round(base["total_us"] / dec_mean, 2)
         rec["fp16_dequant_then_attend"] = base

@@ -257,7 +257,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int n8 = (U + 7) >> 3;
   const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
   int u = xcd + 8 * (kk % n8);
-  const int s = kk / n8;
+  // with an fp16 tail, its workgroups (split index a.splits) come first in the grid, so they
+  // start in the first wave of workgroups even when the grid is larger than one
+  const int s = a.hot_k ? (kk < n8 ? a.splits : kk / n8 - 1) : kk / n8;
   if (u >= U) return;
   if (a.order) u = a.order[u];  // longest-first order (see lpt_order_kernel)
   const int b = u / a.Hkv, h = u - b * a.Hkv;
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int pps = a.pages_per_split;
   // Hot/cold: an fp16 tail of Lh recent tokens besides the pool's L; the workgroups of split
   // index a.splits attend to it (hotwg) and publish it as one more partial, index ns_cold.
-  const int Lh = a.hot_k ? a.hot_lens[b] : 0;
+  const int Lh = a.hot_k ? min(max(a.hot_lens[b], 0), a.hot_cap) : 0;
   const bool hotwg = a.hot_k != nullptr && s == a.splits;
   const int ns_cold = (npages + pps - 1) / pps;
   const int ns = ns_cold + (Lh > 0 ? 1 : 0);  // partials merged for this unit
@@ -882,23 +884,33 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     // basis and rotated into the cache basis (sign flip, butterflies, rho), then handed on
     // as one wave's result with weight 1 and (M, l).
     float* qs = reinterpret_cast<float*>(&ring[0][0][0] + NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4);
-    float* ps = qs + 8 * D;  // [8][hot_cap] scores, then weights; qs then holds the sums
+    float* ps = qs + 8 * D;  // [8][hot_cap] scores, then weights
     const TQ* qh = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
     const f16* hk = static_cast<const f16*>(a.hot_k) + ((int64_t)b * a.Hkv + h) * a.hot_cap * D;
     const f16* hv = static_cast<const f16*>(a.hot_v) + ((int64_t)b * a.Hkv + h) * a.hot_cap * D;
     const float qmul2 = a.attn_scale * TQ_LOG2E;
-    for (int i = tid; i < r * D; i += NT) qs[i] = widen(qh[i]) * qmul2;
+    for (int i = tid; i < 8 * D; i += NT) qs[i] = i < r * D ? widen(qh[i]) * qmul2 : 0.0f;
     __syncthreads();
-    for (int i = tid; i < Lh * r; i += NT) {
-      const int t = i / r, hd = i - t * r;
+    // scores: one token per thread, every head; all lanes read the same query word (broadcast)
+    for (int t = tid; t < Lh; t += NT) {
       const f16* kr = hk + (int64_t)t * D;
-      float dot = 0.0f;
-      for (int d = 0; d < D; d += 8) {
-        const f16x8 k8 = *reinterpret_cast<const f16x8*>(kr + d);
+      float dot[8] = {};
+      for (int d0 = 0; d0 < D; d0 += 32) {
+        f16x8 k8[4];
 #pragma unroll
-        for (int e = 0; e < 8; e++) dot = __builtin_fmaf(qs[hd * D + d + e], (float)k8[e], dot);
+        for (int c = 0; c < 4; c++) k8[c] = *reinterpret_cast<const f16x8*>(kr + d0 + 8 * c);
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float kx = (float)k8[c][e];
+#pragma unroll
+            for (int hd = 0; hd < 8; hd++) dot[hd] = __builtin_fmaf(qs[hd * D + d0 + 8 * c + e], kx, dot[hd]);
+          }
       }
-      ps[hd * a.hot_cap + t] = dot;
+#pragma unroll
+      for (int hd = 0; hd < 8; hd++)
+        if (hd < r) ps[hd * a.hot_cap + t] = dot[hd];
     }
     __syncthreads();
     if (wv < r) {  // wave hd: M, p and l of head hd
@@ -920,20 +932,54 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       }
     }
     __syncthreads();
-    for (int i = tid; i < r * D; i += NT) {
-      const int hd = i / D, d = i - hd * D;
-      const float* pr = ps + hd * a.hot_cap;
-      float o = 0.0f;
-      for (int t = 0; t < Lh; t++) o = __builtin_fmaf(pr[t], (float)hv[(int64_t)t * D + d], o);
-      qs[i] = o;
+    // values: a lane holds 4 consecutive dims (chunk c) of one of TPW consecutive tokens (j);
+    // wave wv takes the token rows wv, wv + NW, ... of TPW tokens each, HB of them per batch
+    {
+      constexpr int CH = D / 4, TPW = 64 / CH > 1 ? 64 / CH : 1, HB = 8;
+      const int c = lane % CH, j = lane / CH;
+      float acc[8][4] = {};
+      const int nrow = (Lh + TPW - 1) / TPW;
+      for (int n0 = wv; n0 < nrow; n0 += NW * HB) {
+        f16x4 v4[HB];
+#pragma unroll
+        for (int k = 0; k < HB; k++) {
+          const int t = (n0 + k * NW) * TPW + j;
+          if (t < Lh) v4[k] = *reinterpret_cast<const f16x4*>(hv + (int64_t)t * D + 4 * c);
+        }
+#pragma unroll
+        for (int k = 0; k < HB; k++) {
+          const int t = (n0 + k * NW) * TPW + j;
+          if (t < Lh) {
+#pragma unroll
+            for (int hd = 0; hd < 8; hd++) {
+              const float p = hd < r ? ps[hd * a.hot_cap + t] : 0.0f;
+#pragma unroll
+              for (int e = 0; e < 4; e++) acc[hd][e] = __builtin_fmaf(p, (float)v4[k][e], acc[hd][e]);
+            }
+          }
+        }
+      }
+      // the TPW token lanes of each chunk, then the waves (through mo, original basis)
+#pragma unroll
+      for (int m = CH; m < 64; m <<= 1)
+#pragma unroll
+        for (int hd = 0; hd < 8; hd++)
+#pragma unroll
+          for (int e = 0; e < 4; e++) acc[hd][e] += xor_shfl(acc[hd][e], m);
+      if (j == 0) {
+#pragma unroll
+        for (int hd = 0; hd < 8; hd++)
+          if (hd < r) *reinterpret_cast<f32x4*>(&mo[wv][hd][4 * c]) = f32x4{acc[hd][0], acc[hd][1], acc[hd][2], acc[hd][3]};
+      }
     }
     __syncthreads();
-    if (wv < r) {
+    if (wv < r) {  // wave hd: sum over the waves, then into the cache basis
       float x[V];
 #pragma unroll
       for (int k = 0; k < V; k++) {
         const int d = lane + 64 * k;
-        const float o = qs[wv * D + d];
+        float o = 0.0f;
+        for (int w = 0; w < NW; w++) o += mo[w][wv][d];
         x[k] = ((sgn_s[d >> 5] >> (d & 31)) & 1u) ? -o : o;
       }
       wave_fwht<V>(x, lane);

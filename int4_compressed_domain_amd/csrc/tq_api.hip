@@ -59,7 +59,9 @@ Split make_split(int pages, int S) {
   return s;
 }
 
-Split choose_split(int B, int Hkv, int D, int k_codec, int max_ctx, int requested) {
+// hot: an fp16 tail adds one workgroup per (sequence, kv head); the pool's splits give it
+// room so that the whole grid still fits the target.
+Split choose_split(int B, int Hkv, int D, int k_codec, int max_ctx, int requested, bool hot = false) {
   const int pages = (max_ctx + 15) / 16;
   const int min_s = (pages + TQ_MAX_SPLIT_PAGES - 1) / TQ_MAX_SPLIT_PAGES;  // page ids fit LDS
   if (requested > 0) {
@@ -70,6 +72,7 @@ Split choose_split(int B, int Hkv, int D, int k_codec, int max_ctx, int requeste
   const int64_t units = (int64_t)B * Hkv;
   const int64_t target = (int64_t)num_cus() * (D >= 256 ? 2 : 1);
   int64_t want = (target + units - 1) / units;
+  if (hot && want > 1) want--;
   const int64_t cap = (pages + nw - 1) / nw;
   if (want > cap) want = cap;
   if (want < min_s) want = min_s;
@@ -172,7 +175,8 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   if (L->k_codec == TQ_CODEC_FP16 && L->head_dim > 128) return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
   if (!pool || !block_table) return TQ_EINVAL;
-  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits);
+  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits,
+                         hot_k != nullptr);
   if (workspace_bytes_ < workspace_bytes(L, batch, max_context_len, num_splits)) return TQ_ENOSPC;
   if (!workspace) return TQ_EINVAL;
   float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + TQ_DECODE_COUNTER_BYTES);

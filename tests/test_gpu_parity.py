@@ -148,19 +148,11 @@ def test_sparse_values(name, k_codec):
             assert sk > 0, "spiky attention should let value pages be skipped"
 
 
-@pytest.mark.parametrize("D,r,k_codec", [(128, 8, 0), (128, 4, 1), (128, 8, 2), (64, 2, 2),
-                                         (256, 2, 0)])
-def test_hot_cold(D, r, k_codec):
-    """Hot/cold cache: older tokens in the pool, the most recent in an fp16 tail, one softmax;
-    against the oracle for several split counts, with empty pools, empty and full tails, and
-    a sequence with no tokens at all."""
-    cold = [0, 1, 40, 300, 1000, 0]
-    hot = [5, 0, 64, 17, 1, 0]
-    cap = 64
-    w = W.Workload("hc_d%d_r%d_k%d" % (D, r, k_codec), len(cold), 2 * r, 2, D, max(cold), "bf16",
+def _hot_cold_case(D, r, k_codec, cold, hot, cap, splits_list, seed):
+    w = W.Workload("hc_d%d_r%d_k%d" % (D, r, k_codec), len(cold), 2 * r, 2, D, max(max(cold), 1), "bf16",
                    1.0 / math.sqrt(D), k_codec=k_codec, dist="lognormal_spikes")
-    _say("case hot/cold D", D, "r", r, "k_codec", k_codec)
-    c = Case(w, seed=90 + D + r + k_codec, lens=cold)
+    _say("case hot/cold D", D, "r", r, "k_codec", k_codec, "tail capacity", cap)
+    c = Case(w, seed=seed, lens=cold)
     c.fill()
     hk = np.zeros((w.batch, w.kv_heads, cap, D), np.float16)
     hv = np.zeros_like(hk)
@@ -175,7 +167,8 @@ def test_hot_cold(D, r, k_codec):
     hv_d = torch.from_numpy(hv).to(DEV)
     hl_d = torch.from_numpy(hl).to(DEV)
     maxc = int(max(cold))
-    for splits in (0, 1, 3):
+    outs = []
+    for splits in splits_list:
         ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, w.batch, maxc, splits) // 4,
                          dtype=torch.float32, device=DEV)
         out = torch.full((w.batch, w.q_heads, D), float("nan"), dtype=torch.float32, device=DEV)
@@ -186,8 +179,28 @@ def test_hot_cold(D, r, k_codec):
         err = attn_err(o, ref)
         _say("   splits %d: max normwise err %.3e" % (splits, err.max()))
         assert np.all(np.isfinite(o)) and err.max() <= ATTN_TOL
-        assert np.all(o[-1] == 0.0)
         assert int(ws[:(4 << 20) // 4].view(torch.int32).abs().sum().item()) == 0, "counters not reset"
+        outs.append(o)
+    return outs
+
+
+@pytest.mark.parametrize("D,r,k_codec", [(128, 8, 0), (128, 4, 1), (128, 8, 2), (64, 2, 2),
+                                         (256, 2, 0)])
+def test_hot_cold(D, r, k_codec):
+    """Hot/cold cache: older tokens in the pool, the most recent in an fp16 tail, one softmax;
+    against the oracle for several split counts, with empty pools, empty and full tails, and
+    a sequence with no tokens at all."""
+    outs = _hot_cold_case(D, r, k_codec, [0, 1, 40, 300, 1000, 0], [5, 0, 64, 17, 1, 0], 64,
+                          (0, 1, 3), 90 + D + r + k_codec)
+    for o in outs:
+        assert np.all(o[-1] == 0.0)
+
+
+@pytest.mark.parametrize("D,r", [(64, 8), (128, 8), (256, 4)])
+def test_hot_cold_long_tail(D, r):
+    """Tails of up to the largest capacity (1024 tokens), longer than one batch of the value
+    loop, with ragged ends; a tail-only sequence (no pool tokens) among them."""
+    _hot_cold_case(D, r, 0, [0, 700, 33, 129], [1024, 1023, 517, 64], 1024, (0, 2), 300 + D)
 
 
 @pytest.mark.parametrize("k_codec", [0, 1, 2])
