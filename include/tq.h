@@ -121,9 +121,8 @@ int tq_kv_append(const tq_layout* layout, void* pool, const void* k, const void*
                  int32_t in_dtype, int32_t n_tokens, const int64_t* slot_mapping, void* stream);
 
 /* Workspace bytes tq_decode_attn needs for this batch and maximum context length:
- * TQ_DECODE_COUNTER_BYTES of counters, the split partials (batch * num_q_heads * (splits + 1)
- * * (head_dim + 2) floats: one row more for the fp16 tail of tq_decode_attn_hotcold) and the
- * workgroup order (batch * num_kv_heads int32).
+ * TQ_DECODE_COUNTER_BYTES of counters, the split partials (batch * num_q_heads * splits
+ * * (head_dim + 2) floats) and the workgroup order (batch * num_kv_heads int32).
  * num_splits: 0 picks the split count automatically (as tq_decode_attn does); > 0 asks
  * for that many splits of the context (clamped to the number of pages). Returns 0 for
  * invalid arguments. */
@@ -201,7 +200,8 @@ int tq_decode_attn_sparse_v(const tq_layout* layout, const void* pool, const voi
  * tokens and an fp16 tail its most recent ones [mlxcel "TurboQuant KV cache" manual,
  * delegated cache: recent tokens in fp16, older ones in the 4-bit form]. Sequence b attends
  * to its cold_lens[b] pool tokens and then to its hot_lens[b] tail tokens, one softmax over
- * both; the tail is a split of its own whose partial joins the pool's splits in the merge.
+ * both. Each split of the pool also takes an equal slice of the tail and joins it to its
+ * partial, so the tail adds no workgroups and its work is spread over the splits.
  *   cold_lens       device int32 [batch], as context_lens of tq_decode_attn (may be 0)
  *   max_cold_len    host, an upper bound of cold_lens
  *   hot_k, hot_v    device fp16 [batch][num_kv_heads][hot_cap][head_dim], original basis

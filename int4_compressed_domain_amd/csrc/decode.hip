@@ -257,9 +257,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int n8 = (U + 7) >> 3;
   const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
   int u = xcd + 8 * (kk % n8);
-  // with an fp16 tail, its workgroups (split index a.splits) come first in the grid, so they
-  // start in the first wave of workgroups even when the grid is larger than one
-  const int s = a.hot_k ? (kk < n8 ? a.splits : kk / n8 - 1) : kk / n8;
+  const int s = kk / n8;
   if (u >= U) return;
   if (a.order) u = a.order[u];  // longest-first order (see lpt_order_kernel)
   const int b = u / a.Hkv, h = u - b * a.Hkv;
@@ -267,22 +265,21 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int L = a.context_lens[b];
   const int npages = (L + 15) >> 4;
   const int pps = a.pages_per_split;
-  // Hot/cold: an fp16 tail of Lh recent tokens besides the pool's L; the workgroups of split
-  // index a.splits attend to it (hotwg) and publish it as one more partial, index ns_cold.
+  // Hot/cold: an fp16 tail of Lh recent tokens besides the pool's L. Every split of the
+  // unit takes an equal slice [t0, t1) of it after its pages; a unit with a tail and no
+  // pool tokens has one split, holding the whole tail.
   const int Lh = a.hot_k ? min(max(a.hot_lens[b], 0), a.hot_cap) : 0;
-  const bool hotwg = a.hot_k != nullptr && s == a.splits;
   const int ns_cold = (npages + pps - 1) / pps;
-  const int ns = ns_cold + (Lh > 0 ? 1 : 0);  // partials merged for this unit
+  const int ns = ns_cold > 0 ? ns_cold : (Lh > 0 ? 1 : 0);  // partials merged for this unit
   float* outp = a.out + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
   if (ns == 0) {  // empty sequence: zero output, written by split 0
     if (s == 0)
       for (int i = tid; i < r * D; i += NT) outp[i] = 0.0f;
     return;
   }
-  if (hotwg ? Lh == 0 : s >= ns_cold) return;
-  const int srow = hotwg ? ns_cold : s;  // this workgroup's partial row
-  // (a hot workgroup has no pages: p0 >= p1, so it streams nothing)
-  const int p0 = hotwg ? npages : s * pps, p1 = hotwg ? npages : min(p0 + pps, npages);
+  if (s >= ns) return;
+  const int p0 = s * pps, p1 = min(p0 + pps, npages);
+  const int t0 = (int)((int64_t)Lh * s / ns), tsl = (int)((int64_t)Lh * (s + 1) / ns) - t0;
 
   // page ring (per wave) -- reused after the page loop as the merge area
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT][NW][C::SLOT];
@@ -303,7 +300,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // instruction start in different LDS banks
   constexpr int MOW = D + 4;
   static_assert(NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4 <= NSLOT * NW * C::SLOT, "merge area must fit the ring");
-  static_assert(NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4 + 8 * (D + TQ_MAX_HOT) * 4 <= NSLOT * NW * C::SLOT,
+  static_assert(NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4 + 8 * (2 * D + TQ_MAX_HOT) * 4 <= NSLOT * NW * C::SLOT,
                 "the fp16 tail's scratch must fit the ring");
   f16 (*bqs)[64][8] = reinterpret_cast<f16 (*)[64][8]>(&ring[NSLOT - 1][0][0]);
   float (*mo)[8][MOW] = reinterpret_cast<float (*)[8][MOW]>(&ring[0][0][0]);
@@ -341,7 +338,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // that token's bytes valid); wave wl, which owns the last page, patches its staged copy
   // before computing it; wave wc stores the token to the pool after the page loop.
   constexpr int E = CodecCfg<D>::E;
-  const bool app = !SPV && !hotwg && (a.knew != nullptr) && (s == ns_cold - 1);
+  const bool app = !SPV && (a.knew != nullptr) && (s == ns_cold - 1);
   const int plast = npages - 1, tnew = (L - 1) & 15;
   const int wc = NW - 1, wl = (plast - p0) % NW;
   float ynew[E];
@@ -878,88 +875,129 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   }
   __syncthreads();
   int nwsum = NW;  // waves whose results are summed below
-  if (hotwg) {
-    // The fp16 tail [mlxcel manual, delegated cache]: scores with the query as given,
-    // p = 2^(s - M) in the log2 domain as the pages' scores, values summed in the original
-    // basis and rotated into the cache basis (sign flip, butterflies, rho), then handed on
-    // as one wave's result with weight 1 and (M, l).
+  if (!SPV && tsl > 0) {
+    // This split's slice of the fp16 tail [mlxcel manual, delegated cache]: scores with the
+    // query as given, p = 2^(s - M_t) in the log2 domain as the pages' scores, values summed
+    // in the original basis and rotated into the cache basis (sign flip, butterflies, rho),
+    // then joined to the pages' result of this workgroup by the usual max/rescale rule.
     float* qs = reinterpret_cast<float*>(&ring[0][0][0] + NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4);
-    float* ps = qs + 8 * D;  // [8][hot_cap] scores, then weights
+    float* ps = qs + 8 * D;           // [8][TQ_MAX_HOT] scores, then weights
+    float* pw = ps + 8 * TQ_MAX_HOT;  // [8][D] the pages' part: sum over waves of f_w o_w
     const TQ* qh = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
-    const f16* hk = static_cast<const f16*>(a.hot_k) + ((int64_t)b * a.Hkv + h) * a.hot_cap * D;
-    const f16* hv = static_cast<const f16*>(a.hot_v) + ((int64_t)b * a.Hkv + h) * a.hot_cap * D;
+    const f16* hk = static_cast<const f16*>(a.hot_k) + (((int64_t)b * a.Hkv + h) * a.hot_cap + t0) * D;
+    const f16* hv = static_cast<const f16*>(a.hot_v) + (((int64_t)b * a.Hkv + h) * a.hot_cap + t0) * D;
     const float qmul2 = a.attn_scale * TQ_LOG2E;
-    for (int i = tid; i < 8 * D; i += NT) qs[i] = i < r * D ? widen(qh[i]) * qmul2 : 0.0f;
+    // Scores: 8 lanes per token, lane sg holding dims [sg D/8, (sg+1) D/8) (KP loads of 8),
+    // wave wv taking tokens tb + (lane / 8), tb = 8 wv, 8 wv + 8 NW, ...
+    // Values: a lane holds 4 consecutive dims (chunk c) of one of TPW consecutive tokens (j);
+    // wave wv takes the token rows wv, wv + NW, ... of TPW tokens each, HB of them per batch.
+    // The first keys and values are loaded before anything else, so that their latency
+    // overlaps the folding of the pages' result.
+    constexpr int KP = D / 64, CH = D / 4, TPW = 64 / CH > 1 ? 64 / CH : 1, HB = 8;
+    const int tt = lane >> 3, sg = lane & 7;
+    const int c = lane % CH, j = lane / CH;
+    f16x8 kp[KP];
+    f16x4 v4[HB];
+    auto load_k = [&](int tb) {
+      const int t = tb + tt;
+      if (t < tsl) {
+#pragma unroll
+        for (int i = 0; i < KP; i++)
+          kp[i] = *reinterpret_cast<const f16x8*>(hk + (int64_t)t * D + sg * (D / 8) + 8 * i);
+      }
+    };
+    auto load_v = [&](int n0) {
+#pragma unroll
+      for (int k = 0; k < HB; k++) {
+        const int t = (n0 + k * NW) * TPW + j;
+        if (t < tsl) v4[k] = *reinterpret_cast<const f16x4*>(hv + (int64_t)t * D + 4 * c);
+      }
+    };
+    // (the query first: the loads complete in order, so its wait would cover the others)
+    constexpr int QPT = (8 * D + NT - 1) / NT;
+    float qx[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; k++) {
+      const int i = tid + k * NT;
+      qx[k] = (i < 8 * D && i < r * D) ? widen(qh[i]) * qmul2 : 0.0f;
+    }
+    load_k(8 * wv);
+    load_v(wv);
+#pragma unroll
+    for (int k = 0; k < QPT; k++) {
+      const int i = tid + k * NT;
+      if (i < 8 * D) {
+        const int hd = i / D, d = i - hd * D;
+        float o = 0.0f;
+        if (hd < r) {
+#pragma unroll
+          for (int w = 0; w < NW; w++) o += mml[w][hd][0] * mo[w][hd][d];
+        }
+        pw[i] = o;
+        qs[i] = qx[k];
+      }
+    }
     __syncthreads();
-    // scores: one token per thread, every head; all lanes read the same query word (broadcast)
-    for (int t = tid; t < Lh; t += NT) {
-      const f16* kr = hk + (int64_t)t * D;
+    for (int tb = 8 * wv; tb < tsl; tb += 8 * NW) {
+      if (tb != 8 * wv) load_k(tb);
       float dot[8] = {};
-      for (int d0 = 0; d0 < D; d0 += 32) {
-        f16x8 k8[4];
 #pragma unroll
-        for (int c = 0; c < 4; c++) k8[c] = *reinterpret_cast<const f16x8*>(kr + d0 + 8 * c);
+      for (int i = 0; i < KP; i++)
 #pragma unroll
-        for (int c = 0; c < 4; c++)
+        for (int e = 0; e < 8; e++) {
+          const float kx = (float)kp[i][e];
+          const int d = sg * (D / 8) + 8 * i + e;
 #pragma unroll
-          for (int e = 0; e < 8; e++) {
-            const float kx = (float)k8[c][e];
-#pragma unroll
-            for (int hd = 0; hd < 8; hd++) dot[hd] = __builtin_fmaf(qs[hd * D + d0 + 8 * c + e], kx, dot[hd]);
-          }
-      }
-#pragma unroll
-      for (int hd = 0; hd < 8; hd++)
-        if (hd < r) ps[hd * a.hot_cap + t] = dot[hd];
-    }
-    __syncthreads();
-    if (wv < r) {  // wave hd: M, p and l of head hd
-      float* pr = ps + wv * a.hot_cap;
-      float M = -INFINITY;
-      for (int t = lane; t < Lh; t += 64) M = fmaxf(M, pr[t]);
-      M = wave_max(M);
-      float l = 0.0f;
-      for (int t = lane; t < Lh; t += 64) {
-        const float p = __builtin_amdgcn_exp2f(pr[t] - M);
-        pr[t] = p;
-        l += p;
-      }
-      l = wave_sum(l);
-      if (lane == 0) {
-        hml[wv][0] = M;
-        hml[wv][1] = l;
-        mml[0][wv][0] = 1.0f;
-      }
-    }
-    __syncthreads();
-    // values: a lane holds 4 consecutive dims (chunk c) of one of TPW consecutive tokens (j);
-    // wave wv takes the token rows wv, wv + NW, ... of TPW tokens each, HB of them per batch
-    {
-      constexpr int CH = D / 4, TPW = 64 / CH > 1 ? 64 / CH : 1, HB = 8;
-      const int c = lane % CH, j = lane / CH;
-      float acc[8][4] = {};
-      const int nrow = (Lh + TPW - 1) / TPW;
-      for (int n0 = wv; n0 < nrow; n0 += NW * HB) {
-        f16x4 v4[HB];
-#pragma unroll
-        for (int k = 0; k < HB; k++) {
-          const int t = (n0 + k * NW) * TPW + j;
-          if (t < Lh) v4[k] = *reinterpret_cast<const f16x4*>(hv + (int64_t)t * D + 4 * c);
+          for (int hd = 0; hd < 8; hd++) dot[hd] = __builtin_fmaf(qs[hd * D + d], kx, dot[hd]);
         }
 #pragma unroll
+      for (int hd = 0; hd < 8; hd++) {
+        dot[hd] += lane_xor16(dot[hd], 1, lane);
+        dot[hd] += lane_xor16(dot[hd], 2, lane);
+        dot[hd] += lane_xor16(dot[hd], 4, lane);
+      }
+      const int t = tb + tt;
+      if (t < tsl && sg < r) {
+        float v = dot[0];
+#pragma unroll
+        for (int hd = 1; hd < 8; hd++) v = sg == hd ? dot[hd] : v;
+        ps[sg * TQ_MAX_HOT + t] = v;
+      }
+    }
+    __syncthreads();
+    float Mt = -INFINITY, lt = 0.0f;  // wave hd: the slice's max and sum for head hd
+    if (wv < r) {
+      float* pr = ps + wv * TQ_MAX_HOT;
+      for (int t = lane; t < tsl; t += 64) Mt = fmaxf(Mt, pr[t]);
+      Mt = wave_max(Mt);
+      for (int t = lane; t < tsl; t += 64) {
+        const float p = __builtin_amdgcn_exp2f(pr[t] - Mt);
+        pr[t] = p;
+        lt += p;
+      }
+      lt = wave_sum(lt);
+    }
+    __syncthreads();
+    {
+      float acc[8][4] = {};
+      const int nrow = (tsl + TPW - 1) / TPW;
+      for (int n0 = wv; n0 < nrow; n0 += NW * HB) {
+        if (n0 != wv) load_v(n0);
+#pragma unroll
         for (int k = 0; k < HB; k++) {
           const int t = (n0 + k * NW) * TPW + j;
-          if (t < Lh) {
+          if (t < tsl) {
 #pragma unroll
             for (int hd = 0; hd < 8; hd++) {
-              const float p = hd < r ? ps[hd * a.hot_cap + t] : 0.0f;
+              const float p = hd < r ? ps[hd * TQ_MAX_HOT + t] : 0.0f;
 #pragma unroll
               for (int e = 0; e < 4; e++) acc[hd][e] = __builtin_fmaf(p, (float)v4[k][e], acc[hd][e]);
             }
           }
         }
       }
-      // the TPW token lanes of each chunk, then the waves (through mo, original basis)
+      // the TPW token lanes of each chunk, then the waves (through mo, whose page results
+      // are folded into pw above)
 #pragma unroll
       for (int m = CH; m < 64; m <<= 1)
 #pragma unroll
@@ -973,7 +1011,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       }
     }
     __syncthreads();
-    if (wv < r) {  // wave hd: sum over the waves, then into the cache basis
+    if (wv < r) {  // wave hd: the slice into the cache basis, joined to the pages' part
       float x[V];
 #pragma unroll
       for (int k = 0; k < V; k++) {
@@ -983,8 +1021,20 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
         x[k] = ((sgn_s[d >> 5] >> (d & 31)) & 1u) ? -o : o;
       }
       wave_fwht<V>(x, lane);
+      const float Mp = hml[wv][0], lp = hml[wv][1];
+      const float M = fmaxf(Mp, Mt);
+      const float cp = (Mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(Mp - M);
+      const float ct = __builtin_amdgcn_exp2f(Mt - M);
 #pragma unroll
-      for (int k = 0; k < V; k++) mo[0][wv][lane + 64 * k] = x[k] * rho;
+      for (int k = 0; k < V; k++) {
+        const int d = lane + 64 * k;
+        mo[0][wv][d] = cp * pw[wv * D + d] + ct * (x[k] * rho);
+      }
+      if (lane == 0) {
+        hml[wv][0] = M;
+        hml[wv][1] = cp * lp + ct * lt;
+        mml[0][wv][0] = 1.0f;
+      }
     }
     nwsum = 1;
     __syncthreads();
@@ -992,8 +1042,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // fin: [ngf][r][D] partial sums of the result (rotated basis), summed by the rotation below
   float* fin = &mo[0][0][0];
   int ngf = 1;
-  const int S = a.splits + (a.hot_k ? 1 : 0);  // partial rows per unit
-  const int64_t prow = ((int64_t)u * S + srow) * r;  // partial rows of this (unit, split)
+  const int S = a.splits;  // partial rows per unit
+  const int64_t prow = ((int64_t)u * S + s) * r;  // partial rows of this (unit, split)
   if (ns == 1) {
     float ov[(8 * D + NT - 1) / NT];
 #pragma unroll
@@ -1173,7 +1223,7 @@ hipError_t launch_dq(const LaunchDecode& a, hipStream_t st) {
     hipLaunchKernelGGL(lpt_order_kernel, dim3(1), dim3(256), 0, st, a.context_lens, a.B, a.Hkv, a.order);
   }
   const int U = a.B * a.Hkv;
-  const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * (a.splits + (a.hot_k ? 1 : 0)));
+  const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * a.splits);
   if (a.sparse_v) return launch_dqs<D, TQ, NW, true>(a, st, grid);
   return launch_dqs<D, TQ, NW, false>(a, st, grid);
 }

@@ -59,9 +59,7 @@ Split make_split(int pages, int S) {
   return s;
 }
 
-// hot: an fp16 tail adds one workgroup per (sequence, kv head); the pool's splits give it
-// room so that the whole grid still fits the target.
-Split choose_split(int B, int Hkv, int D, int k_codec, int max_ctx, int requested, bool hot = false) {
+Split choose_split(int B, int Hkv, int D, int k_codec, int max_ctx, int requested) {
   const int pages = (max_ctx + 15) / 16;
   const int min_s = (pages + TQ_MAX_SPLIT_PAGES - 1) / TQ_MAX_SPLIT_PAGES;  // page ids fit LDS
   if (requested > 0) {
@@ -72,7 +70,6 @@ Split choose_split(int B, int Hkv, int D, int k_codec, int max_ctx, int requeste
   const int64_t units = (int64_t)B * Hkv;
   const int64_t target = (int64_t)num_cus() * (D >= 256 ? 2 : 1);
   int64_t want = (target + units - 1) / units;
-  if (hot && want > 1) want--;
   const int64_t cap = (pages + nw - 1) / nw;
   if (want > cap) want = cap;
   if (want < min_s) want = min_s;
@@ -99,7 +96,7 @@ size_t workspace_bytes(const tq_layout* L, int B, int max_ctx, int requested) {
   const Split f = choose_split(B, L->num_kv_heads, L->head_dim, L->k_codec, max_ctx, requested);
   const Split d = choose_split_dense(B, L->num_kv_heads, max_ctx, requested);
   const int S = f.splits > d.splits ? f.splits : d.splits;
-  return TQ_DECODE_COUNTER_BYTES + partial_bytes(B, L->num_q_heads, L->head_dim, S + 1) +  // + the fp16 tail row
+  return TQ_DECODE_COUNTER_BYTES + partial_bytes(B, L->num_q_heads, L->head_dim, S) +
          (size_t)B * L->num_kv_heads * sizeof(int32_t);  // + the workgroup order
 }
 
@@ -175,8 +172,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   if (L->k_codec == TQ_CODEC_FP16 && L->head_dim > 128) return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
   if (!pool || !block_table) return TQ_EINVAL;
-  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits,
-                         hot_k != nullptr);
+  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits);
   if (workspace_bytes_ < workspace_bytes(L, batch, max_context_len, num_splits)) return TQ_ENOSPC;
   if (!workspace) return TQ_EINVAL;
   float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + TQ_DECODE_COUNTER_BYTES);
@@ -188,7 +184,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   a.context_lens = context_lens;
   a.sign_bits = L->sign_bits;
   a.out = out;
-  const int rows = s.splits + (hot_k ? 1 : 0);  // partial rows per unit
+  const int rows = s.splits;  // partial rows per unit
   a.part_o = ws;
   a.part_ml = ws + (size_t)batch * L->num_q_heads * rows * L->head_dim;
   a.D = L->head_dim; a.Hq = L->num_q_heads; a.Hkv = L->num_kv_heads; a.B = batch;

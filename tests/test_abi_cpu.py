@@ -152,7 +152,7 @@ def test_workspace_size_formula():
         pages = -(-ctx // 16)
         pps = -(-pages // min(splits, pages))
         S = -(-pages // pps)
-        want = (4 << 20) + batch * 32 * (S + 1) * (128 + 2) * 4 + batch * 8 * 4  # counters + partials + order
+        want = (4 << 20) + batch * 32 * S * (128 + 2) * 4 + batch * 8 * 4  # counters + partials + order
         assert tq.tq_decode_workspace_size(L, batch, ctx, splits) == want
     assert tq.tq_decode_workspace_size(_layout(head_dim=96), 1, 10, 0) == 0
 
