@@ -37,6 +37,9 @@ PAGE = 16
 CODEC_ABSMAX = 0
 CODEC_LUT = 1
 CODEC_FP16 = 2   # keys only: kept in fp16 (values stay 4-bit)
+CODEC_ABSMAX3 = 3  # values only: 3-bit abs-max
+CODEC_ABSMAX2 = 4  # values only: 2-bit abs-max
+VALUE_BITS = {CODEC_ABSMAX: 4, CODEC_ABSMAX3: 3, CODEC_ABSMAX2: 2}
 
 
 @dataclass(frozen=True)
@@ -83,6 +86,14 @@ WORKLOADS = {
     "llama70b_b1_128k_k16v4": Workload("llama70b_b1_128k_k16v4", 1, 64, 8, 128, 131072, "bf16",
                                        1.0 / math.sqrt(128), k_codec=CODEC_FP16,
                                        dist="lognormal_spikes"),
+    # fp16 keys + 3-bit values (the mlxcel manual's fp16+turbo3 mode)
+    "llama70b_b1_128k_k16v3": Workload("llama70b_b1_128k_k16v3", 1, 64, 8, 128, 131072, "bf16",
+                                       1.0 / math.sqrt(128), k_codec=CODEC_FP16,
+                                       v_codec=CODEC_ABSMAX3, dist="lognormal_spikes"),
+    # 4-bit keys + 2-bit values
+    "llama70b_b1_128k_k4v2": Workload("llama70b_b1_128k_k4v2", 1, 64, 8, 128, 131072, "bf16",
+                                      1.0 / math.sqrt(128), v_codec=CODEC_ABSMAX2,
+                                      dist="lognormal_spikes"),
 }
 
 HEADLINE = "llama70b_b1_128k"
@@ -186,13 +197,12 @@ def slots_for(bt, b, t0, t1):
 
 
 def algorithmic_bytes(w: Workload, lens):
-    """Packed K+V indices and fp16 scales read by one decode: sum_b L_b * Hkv * 2 *
-    (D/2 + 2*D/32) (fp16 keys: L_b * Hkv * (2D + D/2 + 2*D/32)), plus the query and the
-    fp32 output."""
+    """Packed K+V indices and fp16 scales read by one decode: sum_b L_b * Hkv * (keys:
+    D/2 + 2*D/32, or 2D for fp16 keys; values: b*D/8 + 2*D/32 for b-bit values), plus the
+    query and the fp32 output."""
     D = w.head_dim
-    if w.k_codec == CODEC_FP16:
-        per_tok = w.kv_heads * (2 * D + D // 2 + 2 * (D // 32))
-    else:
-        per_tok = w.kv_heads * 2 * (D // 2 + 2 * (D // 32))
+    kbytes = 2 * D if w.k_codec == CODEC_FP16 else D // 2 + 2 * (D // 32)
+    vbytes = VALUE_BITS[w.v_codec] * D // 8 + 2 * (D // 32)
+    per_tok = w.kv_heads * (kbytes + vbytes)
     qbytes = w.batch * w.q_heads * D * (4 if w.dtype == "f32" else 2)
     return int(np.sum(lens, dtype=np.int64)) * per_tok + qbytes + w.batch * w.q_heads * D * 4

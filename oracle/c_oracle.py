@@ -61,6 +61,11 @@ def lib():
         L.or_keys_f16.argtypes = [P, i64, P]
         L.or_place_kf16.argtypes = [P, i32, i32, i64, P, P, P, P]
         L.or_fetch_kf16.argtypes = [P, i32, i32, i64, i32, i32, P, P, P]
+        L.or_quant_absmax_q.argtypes = [P, i32, i32, P, P]
+        L.or_block_bytes_kv.argtypes = [i32, i32, i32]
+        L.or_block_bytes_kv.restype = i64
+        L.or_place_kv.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, P, P, P]
+        L.or_fetch_kv.argtypes = [P, i32, i32, i32, i32, i64, i32, i32, P, P, P, P, P]
         L.or_decode_sparse_v.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, P, P, ctypes.c_float,
                                          f64, P, i32, P, P]
         L.or_decode_hotcold.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, P, P, P, P, i32, P,
@@ -109,12 +114,15 @@ def unrotate_f32(y, sign_bits):
     return out.reshape(y.shape)
 
 
-def quant_absmax(y):
-    """One group of rotated fp32 values -> (indices u in 0..15, fp16 scale bits)."""
+def quant_absmax(y, qmax=7):
+    """One group of rotated fp32 values -> (indices u in 1..2*qmax+1, fp16 scale bits)."""
     y = _c(y, np.float32)
     u = np.empty(y.shape[0], np.uint8)
     s = np.zeros(1, np.uint16)
-    lib().or_quant_absmax(_p(y), y.shape[0], _p(u), _p(s))
+    if qmax == 7:
+        lib().or_quant_absmax(_p(y), y.shape[0], _p(u), _p(s))
+    else:
+        lib().or_quant_absmax_q(_p(y), y.shape[0], qmax, _p(u), _p(s))
     return u, int(s[0])
 
 
@@ -155,12 +163,37 @@ def encode(x, sign_bits, codec=0, group=32):
 KF16 = 2  # k_codec of the fp16-key mode
 
 
-def block_bytes(D, k_codec=0):
-    return int(lib().or_block_bytes_kc(D, k_codec))
+ABSMAX3, ABSMAX2 = 3, 4  # v_codec of the 3-bit and 2-bit value modes
 
 
-def new_pool(num_pages, Hkv, D, k_codec=0):
-    return np.zeros(num_pages * Hkv * block_bytes(D, k_codec), np.uint8)
+def block_bytes(D, k_codec=0, v_codec=0):
+    return int(lib().or_block_bytes_kv(D, k_codec, v_codec))
+
+
+def new_pool(num_pages, Hkv, D, k_codec=0, v_codec=0):
+    return np.zeros(num_pages * Hkv * block_bytes(D, k_codec, v_codec), np.uint8)
+
+
+def place_kv(pool, D, Hkv, slots, vu, vs, ku=None, ks=None, kh=None, k_codec=0, v_codec=0):
+    """Store encoded tokens in a pool of any (k_codec, v_codec); keys as ku/ks (indices and
+    scales) or kh (fp16 bits, k_codec 2)."""
+    slots = _c(slots, np.int64)
+    lib().or_place_kv(_p(pool), D, Hkv, k_codec, v_codec, slots.shape[0], _p(slots),
+                      None if ku is None else _p(_c(ku, np.uint8)),
+                      None if ks is None else _p(_c(ks, np.uint16)),
+                      None if kh is None else _p(_c(kh, np.uint16)),
+                      _p(_c(vu, np.uint8)), _p(_c(vs, np.uint16)))
+
+
+def fetch_kv(pool, D, Hkv, page, t, h, k_codec=0, v_codec=0):
+    """-> (ku, ks, kh, vu, vs) of one token; the key arrays of the other key form are zero."""
+    G = D // 32
+    ku, vu = np.zeros(D, np.uint8), np.zeros(D, np.uint8)
+    ks, vs = np.zeros(G, np.uint16), np.zeros(G, np.uint16)
+    kh = np.zeros(D, np.uint16)
+    lib().or_fetch_kv(_p(pool), D, Hkv, k_codec, v_codec, page, t, h, _p(ku), _p(ks), _p(kh),
+                      _p(vu), _p(vs))
+    return ku, ks, kh, vu, vs
 
 
 def keys_f16(k):

@@ -13,7 +13,11 @@ sharing any code with it, so that the two can be compared byte for byte:
     then the fp64 inverse rotation;
   * fp16 keys (k_codec 2) [mlxcel "TurboQuant KV cache" manual, cache-mode table: keys in
     fp16, values in the 4-bit rotated form] - fp16(k) of the original key, saturated; the
-    scores use the query as given (no rotation), the values are as above.
+    scores use the query as given (no rotation), the values are as above;
+  * 3-bit and 2-bit values (v_codec 3 and 4) [mlxcel manual, cache-mode table: fp16+turbo3;
+    "TurboQuant on AMD GPUs", section 2: 2-bit is possible] - abs-max with the largest
+    level 3 or 1 instead of 7, index u = c + 4 or c + 2, packed as the block comment
+    below describes.
 
 numpy's float32 arithmetic is IEEE single precision and its float16 casts round to
 nearest even with subnormals, which is what the readings ask for.
@@ -90,19 +94,23 @@ def to_f16_sat(x):
     return np.where(np.isinf(h), np.copysign(np.float16(65504.0), h), h).astype(np.float16)
 
 
-def quant_absmax(y, group=GROUP):
-    """y [..., D] rotated fp32 -> (u [..., D] uint8 in 1..15, scales [..., D/group] fp16)."""
+QMAX = {0: 7, 3: 3, 4: 1}    # largest abs-max level per codec (4, 3, 2 bits)
+VBITS = {0: 4, 1: 4, 3: 3, 4: 2}
+
+
+def quant_absmax(y, group=GROUP, qmax=7):
+    """y [..., D] rotated fp32 -> (u [..., D] uint8 in 1..2*qmax+1, scales [..., D/group] fp16)."""
     y = np.asarray(y, F32)
     D = y.shape[-1]
     yg = y.reshape(y.shape[:-1] + (D // group, group))
     a = np.max(np.abs(yg), axis=-1)
-    s16 = to_f16_sat(a / F32(7.0))
+    s16 = to_f16_sat(a / F32(qmax))
     sf = s16.astype(F32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         c = np.rint(yg / np.where(sf == 0, F32(1.0), sf))
-    c = np.clip(c, -7, 7)
+    c = np.clip(c, -qmax, qmax)
     c = np.where(sf == 0, 0, c)
-    u = (c + 8).astype(np.uint8).reshape(y.shape)
+    u = (c + qmax + 1).astype(np.uint8).reshape(y.shape)
     return u, s16
 
 
@@ -167,7 +175,7 @@ def quant_lut(y, lut=None, group=GROUP):
 
 def encode(x, sign_bits, codec=0, group=GROUP):
     y = rotate(x, sign_bits)
-    return quant_absmax(y, group) if codec == 0 else quant_lut(y, group=group)
+    return quant_lut(y, group=group) if codec == 1 else quant_absmax(y, group, QMAX[codec])
 
 
 def dequant_values(u, s16, codec=0, lut=None, group=GROUP):
@@ -175,8 +183,8 @@ def dequant_values(u, s16, codec=0, lut=None, group=GROUP):
     u = np.asarray(u)
     D = u.shape[-1]
     s = np.repeat(np.asarray(s16, np.float16).astype(np.float64), group, axis=-1)
-    if codec == 0:
-        return (u.astype(np.float64) - 8.0) * s
+    if codec != 1:
+        return (u.astype(np.float64) - float(QMAX[codec] + 1)) * s
     lut = lut16() if lut is None else lut
     return lut.astype(np.float64)[u] * s
 
@@ -191,10 +199,58 @@ def dequant_values(u, s16, codec=0, lut=None, group=GROUP):
 KF16 = 2
 
 
-def block_bytes(D, k_codec=0):
+def block_bytes(D, k_codec=0, v_codec=0):
+    vb = 2 * VBITS[v_codec] * D  # V index bytes of 16 tokens
     if k_codec == KF16:
-        return 41 * D          # [K fp16 32D][V indices 8D][V scales 16 x G fp16]
-    return 16 * D + 64 * (D // 32)
+        return 32 * D + vb + D   # [K fp16 32D][V indices][V scales 16 x G fp16]
+    return 8 * D + vb + 2 * D    # [K indices 8D][V indices][K scales][V scales]
+
+
+# 3-bit and 2-bit value indices. The 16 tokens' 4-bit V region would be 64 rows of G
+# little-endian dwords (row 16j + m, dword g: tokens 4j..4j+3 at bytes 0..3, dims
+# 32g + 2m (low nibble) and 32g + 2m + 1 (high nibble)). With b bits, the two low bits of
+# each nibble of dwords g = 2i, 2i + 1 of a row share one dword X[row][i] (dword 2i in
+# bits 0-1 of every nibble, 2i + 1 in bits 2-3); for b = 3 the third bits of all rows
+# follow as dwords Z, where dword g of row r lands in Z[(r*G + g) // 4] at bit
+# (r*G + g) % 4 of every nibble.
+def _nibble_rows(D):
+    """(row, dword g, nibble n) of every (t, d) in the 4-bit V layout, each [16, D]."""
+    d = np.arange(D)
+    t = np.arange(PAGE)[:, None]
+    c = d // 2
+    g, m = c // 16, c % 16
+    row = 16 * (t // 4) + m
+    n = 2 * (t % 4) + d % 2
+    return np.broadcast_to(row, (PAGE, D)), np.broadcast_to(g, (PAGE, D)), n
+
+
+def _vpack(u, D, bits):
+    """u [16, D] indices -> the V region bytes for b = 3 or 2."""
+    G = D // 32
+    row, g, n = _nibble_rows(D)
+    u = np.asarray(u, np.uint32)
+    X = np.zeros((64, G // 2 if G >= 2 else 1), np.uint32)
+    np.bitwise_or.at(X, (row, g // 2), (u & 3) << (4 * n + 2 * (g % 2)).astype(np.uint32))
+    out = [X.reshape(-1)]
+    if bits == 3:
+        z = row * G + g
+        Z = np.zeros(16 * G, np.uint32)
+        np.bitwise_or.at(Z, z // 4, ((u >> 2) & 1) << (4 * n + z % 4).astype(np.uint32))
+        out.append(Z)
+    return np.concatenate(out).astype("<u4").view(np.uint8)
+
+
+def _vunpack(reg, D, bits):
+    G = D // 32
+    row, g, n = _nibble_rows(D)
+    w = np.asarray(reg, np.uint8).copy().view("<u4").astype(np.uint32)
+    X = w[:32 * G].reshape(64, -1)
+    u = (X[row, g // 2] >> (4 * n + 2 * (g % 2)).astype(np.uint32)) & 3
+    if bits == 3:
+        z = row * G + g
+        Z = w[32 * G:]
+        u = u | (((Z[z // 4] >> (4 * n + z % 4).astype(np.uint32)) & 1) << 2)
+    return u.astype(np.uint8)
 
 
 def _k_index(D):
@@ -223,17 +279,41 @@ def _kf16_index(D):
     return 1024 * g + 16 * (16 * j + t) + 2 * e
 
 
-def new_pool(num_pages, Hkv, D, k_codec=0):
-    return np.zeros(num_pages * Hkv * block_bytes(D, k_codec), np.uint8)
+def new_pool(num_pages, Hkv, D, k_codec=0, v_codec=0):
+    return np.zeros(num_pages * Hkv * block_bytes(D, k_codec, v_codec), np.uint8)
 
 
-def place_kf16(pool, D, Hkv, slots, kh, vu, vs):
+def _put_v(blk, base, D, v_codec, t, u):
+    """Write token t's value indices into the V region at blk[base:]."""
+    bits = VBITS[v_codec]
+    if bits == 4:
+        vb, vh = _v_index(D)
+        vb = vb - 8 * D + base
+        lo_sel, hi_sel = vh[t] == 0, vh[t] == 1
+        blk[vb[t][lo_sel]] = (blk[vb[t][lo_sel]] & 0xF0) | u[lo_sel]
+        blk[vb[t][hi_sel]] = (blk[vb[t][hi_sel]] & 0x0F) | (u[hi_sel] << 4)
+        return
+    nb = 2 * bits * D
+    cur = _vunpack(blk[base:base + nb], D, bits)
+    cur[t] = u
+    blk[base:base + nb] = _vpack(cur, D, bits)
+
+
+def _get_v(blk, base, D, v_codec):
+    bits = VBITS[v_codec]
+    if bits == 4:
+        vb, vh = _v_index(D)
+        vb = vb - 8 * D + base
+        return np.where(vh == 1, blk[vb] >> 4, blk[vb] & 0x0F).astype(np.uint8)
+    return _vunpack(blk[base:base + 2 * bits * D], D, bits)
+
+
+def place_kf16(pool, D, Hkv, slots, kh, vu, vs, v_codec=0):
     """fp16-key pool: kh [n, Hkv, D] fp16 keys, V indices and scales as in place()."""
     G = D // 32
-    bb = block_bytes(D, KF16)
+    bb = block_bytes(D, KF16, v_codec)
     kb = _kf16_index(D)
-    vb, vh = _v_index(D)
-    vb = vb + 24 * D           # the V region starts at 32D instead of 8D
+    vsoff = 32 * D + 2 * VBITS[v_codec] * D
     blocks = pool.reshape(-1, Hkv, bb)
     for i, slot in enumerate(np.asarray(slots, np.int64)):
         if slot < 0:
@@ -244,32 +324,28 @@ def place_kf16(pool, D, Hkv, slots, kh, vu, vs):
             kbytes = np.asarray(kh[i, h], np.float16).view(np.uint8)
             blk[kb[t]] = kbytes[0::2]
             blk[kb[t] + 1] = kbytes[1::2]
-            u = np.asarray(vu[i, h], np.uint8)
-            lo_sel, hi_sel = vh[t] == 0, vh[t] == 1
-            blk[vb[t][lo_sel]] = (blk[vb[t][lo_sel]] & 0xF0) | u[lo_sel]
-            blk[vb[t][hi_sel]] = (blk[vb[t][hi_sel]] & 0x0F) | (u[hi_sel] << 4)
-            blk[40 * D + 2 * G * t:40 * D + 2 * G * (t + 1)] = np.asarray(vs[i, h], np.float16).view(np.uint8)
+            _put_v(blk, 32 * D, D, v_codec, t, np.asarray(vu[i, h], np.uint8))
+            blk[vsoff + 2 * G * t:vsoff + 2 * G * (t + 1)] = np.asarray(vs[i, h], np.float16).view(np.uint8)
 
 
-def fetch_block_kf16(pool, D, Hkv, page, h):
+def fetch_block_kf16(pool, D, Hkv, page, h, v_codec=0):
     """fp16 keys [16, D], V indices [16, D] and V scales [16, G] of one fp16-key block."""
     G = D // 32
-    blk = pool.reshape(-1, Hkv, block_bytes(D, KF16))[page, h]
+    blk = pool.reshape(-1, Hkv, block_bytes(D, KF16, v_codec))[page, h]
     kb = _kf16_index(D)
-    vb, vh = _v_index(D)
-    vb = vb + 24 * D
+    vsoff = 32 * D + 2 * VBITS[v_codec] * D
     k = (blk[kb].astype(np.uint16) | (blk[kb + 1].astype(np.uint16) << 8)).view(np.float16)
-    vu = np.where(vh == 1, blk[vb] >> 4, blk[vb] & 0x0F).astype(np.uint8)
-    vs = blk[40 * D:40 * D + 32 * G].copy().view(np.float16).reshape(PAGE, G)
+    vu = _get_v(blk, 32 * D, D, v_codec)
+    vs = blk[vsoff:vsoff + 32 * G].copy().view(np.float16).reshape(PAGE, G)
     return k, vu, vs
 
 
-def place(pool, D, Hkv, slots, ku, ks, vu, vs):
+def place(pool, D, Hkv, slots, ku, ks, vu, vs, v_codec=0):
     """Write encoded tokens ([n, Hkv, D] indices, [n, Hkv, G] scales) at their slots."""
     G = D // 32
-    bb = block_bytes(D)
+    bb = block_bytes(D, 0, v_codec)
     kb, kh = _k_index(D)
-    vb, vh = _v_index(D)
+    ksoff = 8 * D + 2 * VBITS[v_codec] * D
     blocks = pool.reshape(-1, Hkv, bb)
     for i, slot in enumerate(np.asarray(slots, np.int64)):
         if slot < 0:
@@ -277,36 +353,36 @@ def place(pool, D, Hkv, slots, ku, ks, vu, vs):
         page, t = divmod(int(slot), PAGE)
         for h in range(Hkv):
             blk = blocks[page, h]
-            for idx, hi, u in ((kb[t], kh[t], ku[i, h]), (vb[t], vh[t], vu[i, h])):
-                u = np.asarray(u, np.uint8)
-                lo_sel, hi_sel = hi == 0, hi == 1     # one nibble per byte per pass
-                blk[idx[lo_sel]] = (blk[idx[lo_sel]] & 0xF0) | u[lo_sel]
-                blk[idx[hi_sel]] = (blk[idx[hi_sel]] & 0x0F) | (u[hi_sel] << 4)
+            u = np.asarray(ku[i, h], np.uint8)
+            lo_sel, hi_sel = kh[t] == 0, kh[t] == 1     # one nibble per byte per pass
+            blk[kb[t][lo_sel]] = (blk[kb[t][lo_sel]] & 0xF0) | u[lo_sel]
+            blk[kb[t][hi_sel]] = (blk[kb[t][hi_sel]] & 0x0F) | (u[hi_sel] << 4)
+            _put_v(blk, 8 * D, D, v_codec, t, np.asarray(vu[i, h], np.uint8))
             kscale = np.asarray(ks[i, h], np.float16).view(np.uint8)
             vscale = np.asarray(vs[i, h], np.float16).view(np.uint8)
-            blk[16 * D + 2 * G * t:16 * D + 2 * G * (t + 1)] = kscale
-            blk[16 * D + 32 * G + 2 * G * t:16 * D + 32 * G + 2 * G * (t + 1)] = vscale
+            blk[ksoff + 2 * G * t:ksoff + 2 * G * (t + 1)] = kscale
+            blk[ksoff + D + 2 * G * t:ksoff + D + 2 * G * (t + 1)] = vscale
 
 
 def append(pool, D, Hkv, k, v, slots, sign_bits, k_codec=0, v_codec=0):
     vu, vs = encode(v, sign_bits, v_codec)
     if k_codec == KF16:
-        place_kf16(pool, D, Hkv, slots, to_f16_sat(np.asarray(k, F32)), vu, vs)
+        place_kf16(pool, D, Hkv, slots, to_f16_sat(np.asarray(k, F32)), vu, vs, v_codec)
         return
     ku, ks = encode(k, sign_bits, k_codec)
-    place(pool, D, Hkv, slots, ku, ks, vu, vs)
+    place(pool, D, Hkv, slots, ku, ks, vu, vs, v_codec)
 
 
-def fetch_block(pool, D, Hkv, page, h):
+def fetch_block(pool, D, Hkv, page, h, v_codec=0):
     """Indices and scales of the 16 tokens of one block, natural order."""
     G = D // 32
-    blk = pool.reshape(-1, Hkv, block_bytes(D))[page, h]
+    blk = pool.reshape(-1, Hkv, block_bytes(D, 0, v_codec))[page, h]
     kb, kh = _k_index(D)
-    vb, vh = _v_index(D)
+    ksoff = 8 * D + 2 * VBITS[v_codec] * D
     ku = np.where(kh == 1, blk[kb] >> 4, blk[kb] & 0x0F).astype(np.uint8)
-    vu = np.where(vh == 1, blk[vb] >> 4, blk[vb] & 0x0F).astype(np.uint8)
-    ks = blk[16 * D:16 * D + 32 * G].copy().view(np.float16).reshape(PAGE, G)
-    vs = blk[16 * D + 32 * G:16 * D + 64 * G].copy().view(np.float16).reshape(PAGE, G)
+    vu = _get_v(blk, 8 * D, D, v_codec)
+    ks = blk[ksoff:ksoff + 32 * G].copy().view(np.float16).reshape(PAGE, G)
+    vs = blk[ksoff + D:ksoff + D + 32 * G].copy().view(np.float16).reshape(PAGE, G)
     return ku, ks, vu, vs
 
 
@@ -318,10 +394,10 @@ def gather(pool, D, Hkv, block_table, L, b, h, k_codec=0, v_codec=0):
     lut = lut16()
     for p in range(npg):
         if k_codec == KF16:
-            k16, vu, vs = fetch_block_kf16(pool, D, Hkv, int(block_table[b][p]), h)
+            k16, vu, vs = fetch_block_kf16(pool, D, Hkv, int(block_table[b][p]), h, v_codec)
             ks_.append(k16.astype(np.float64))
         else:
-            ku, ks, vu, vs = fetch_block(pool, D, Hkv, int(block_table[b][p]), h)
+            ku, ks, vu, vs = fetch_block(pool, D, Hkv, int(block_table[b][p]), h, v_codec)
             ks_.append(dequant_values(ku, ks, k_codec, lut))
         vs_.append(dequant_values(vu, vs, v_codec, lut))
     if npg == 0:

@@ -32,6 +32,12 @@
  *    fp16_rne(k) of the original key, saturating at 65504, with no rotation; scores are
  *    alpha * q.k in the original basis (the query is not rotated for them); values,
  *    the weighted sum and the inverse rotation are as in the 4-bit mode.
+ *  - 3-bit and 2-bit values (mlxcel manual, cache-mode table: fp16+turbo3 keeps keys in
+ *    fp16 and stores values with 3 bits; TurboQuant on AMD GPUs section 2: 2 bits are
+ *    possible): v_codec 3 and 4 are the abs-max codec with the largest level qmax = 3
+ *    and 1 instead of 7: s = fp16_rne(absmax/qmax), c = clamp(rint(y/s), -qmax, qmax),
+ *    stored index u = c + qmax + 1 (3 and 2 bits). Their packing: see the placement
+ *    functions below.
  *
  * Build: gcc -O2 -fPIC -shared -ffp-contract=off -fno-fast-math -fopenmp (no -march).
  */
@@ -140,22 +146,33 @@ static void unrotate_f64(const double* y, double* x, int D, const uint32_t* sign
 /* ------------------------------------------------------------------------------------- */
 /* Uniform abs-max int4 for one group of g rotated values [Open-TQ-Metal card abstract:
  * per-group abs-max + int4; TurboQuant on AMD GPUs section 2: uniform V]. */
-void or_quant_absmax(const float* y, int g, uint8_t* u, uint16_t* scale) {
+void or_quant_absmax_q(const float* y, int g, int qmax, uint8_t* u, uint16_t* scale) {
   float a = 0.0f;
   for (int i = 0; i < g; i++) { float t = fabsf(y[i]); if (t > a) a = t; }
-  float s32 = a / 7.0f;
+  float s32 = a / (float)qmax;
   uint16_t s16 = f16_saturate(or_f64_to_f16((double)s32));
   float sf = (float)or_f16_to_f64(s16);
+  float lim = (float)qmax;
   for (int i = 0; i < g; i++) {
     int c = 0;
     if (sf != 0.0f) {
       float r = rintf(y[i] / sf);
-      c = r > 7.0f ? 7 : (r < -7.0f ? -7 : (int)r);
+      c = r > lim ? qmax : (r < -lim ? -qmax : (int)r);
     }
-    u[i] = (uint8_t)(c + 8);
+    u[i] = (uint8_t)(c + qmax + 1);
   }
   *scale = s16;
 }
+
+void or_quant_absmax(const float* y, int g, uint8_t* u, uint16_t* scale) {
+  or_quant_absmax_q(y, g, 7, u, scale);
+}
+
+/* Largest level of the abs-max codecs: v_codec 0 (4 bits), 3 (3 bits), 4 (2 bits). */
+#define OR_ABSMAX3 3
+#define OR_ABSMAX2 4
+static int qmax_of(int codec) { return codec == OR_ABSMAX3 ? 3 : (codec == OR_ABSMAX2 ? 1 : 7); }
+static int vbits_of(int codec) { return codec == OR_ABSMAX3 ? 3 : (codec == OR_ABSMAX2 ? 2 : 4); }
 
 /* Lloyd-Max quantizer with 16 levels for N(0,1), by Lloyd's iteration in fp64
  * [TurboQuant on AMD GPUs section 2: keys use a LUT quantizer after the rotation]. */
@@ -229,13 +246,13 @@ void or_quant_lut(const float* y, int g, const uint16_t* lut, uint8_t* u, uint16
 /* Value of one stored index under each codec. */
 static double dequant1(int codec, uint8_t u, uint16_t s16, const uint16_t* lut) {
   double s = or_f16_to_f64(s16);
-  if (codec == 0) return (double)((int)u - 8) * s;
-  return or_f16_to_f64(lut[u]) * s;
+  if (codec == 1) return or_f16_to_f64(lut[u]) * s;
+  return (double)((int)u - qmax_of(codec) - 1) * s;
 }
 
 /* Encode n vectors of length D (fp32 input) with group size g: rotate, then quantize each
  * group. Outputs natural-order indices u[n][D] and scales[n][D/g]. codec 0 = abs-max,
- * 1 = LUT. */
+ * 1 = LUT, 3 = 3-bit abs-max, 4 = 2-bit abs-max. */
 void or_encode(const float* x, int64_t n, int D, int g, const uint32_t* sign_bits, int codec,
                uint8_t* u, uint16_t* scales) {
   uint16_t lut[16];
@@ -245,8 +262,8 @@ void or_encode(const float* x, int64_t n, int D, int g, const uint32_t* sign_bit
     float y[512];
     or_rotate(x + v * D, y, D, sign_bits);
     for (int k = 0; k < D / g; k++) {
-      if (codec == 0) or_quant_absmax(y + k * g, g, u + v * D + k * g, scales + v * (D / g) + k);
-      else or_quant_lut(y + k * g, g, lut, u + v * D + k * g, scales + v * (D / g) + k);
+      if (codec == 1) or_quant_lut(y + k * g, g, lut, u + v * D + k * g, scales + v * (D / g) + k);
+      else or_quant_absmax_q(y + k * g, g, qmax_of(codec), u + v * D + k * g, scales + v * (D / g) + k);
     }
   }
 }
@@ -362,6 +379,109 @@ void or_fetch_kf16(const uint8_t* pool, int D, int Hkv, int64_t page, int t, int
   for (int k = 0; k < G; k++) vs[k] = get16(blk + kf16_vs_off(t, k, D));
 }
 
+/* Blocks in general, by key codec and value codec:
+ *   4-bit keys: [K indices 8D][V indices][K scales 16*G fp16][V scales 16*G fp16]
+ *   fp16 keys:  [K fp16 32D][V indices][V scales 16*G fp16]
+ * with 2*b*D bytes of V indices for b-bit values (b = 4, 3, 2). K bytes as above.
+ * b = 4: the V byte of (t, d) as in the 4-bit block. b = 3 or 2: the 4-bit position of
+ * (t, d) -- row l = 16j + m, dword g of the row, nibble n = 2e + d%2, where t = 4j + e
+ * and d/2 = 16g + m -- decides where the bits of its index go: bits 0-1 to X dword
+ * l*G/2 + g/2 at bit 4n + 2*(g%2); for b = 3 bit 2 to Z dword (l*G + g)/4 at bit
+ * 4n + (l*G + g)%4, the 16*G Z dwords following the 32*G X dwords. Dwords are
+ * little-endian. Every byte of the V region then holds bits of one token only. */
+int64_t or_block_bytes_kv(int D, int k_codec, int v_codec) {
+  int64_t kpart = k_codec == OR_KF16 ? 32 * (int64_t)D : 8 * (int64_t)D;
+  int64_t scales = k_codec == OR_KF16 ? (int64_t)D : 2 * (int64_t)D;
+  return kpart + 2 * (int64_t)vbits_of(v_codec) * D + scales;
+}
+static int64_t vbase_of(int D, int k_codec) { return k_codec == OR_KF16 ? 32 * (int64_t)D : 8 * (int64_t)D; }
+static int64_t kv_ks_off(int t, int k, int D, int v_codec) {
+  return 8 * (int64_t)D + 2 * (int64_t)vbits_of(v_codec) * D + 2 * (t * (D / 32) + k);
+}
+static int64_t kv_vs_off(int t, int k, int D, int k_codec, int v_codec) {
+  return vbase_of(D, k_codec) + 2 * (int64_t)vbits_of(v_codec) * D + (k_codec == OR_KF16 ? 0 : D) +
+         2 * (t * (D / 32) + k);
+}
+/* bit offsets, inside the V region, of the low two bits (xb) and of bit 2 (zb) of the
+ * b-bit index of (t, d), b = 3 or 2 */
+static void vbit_pos(int t, int d, int D, int64_t* xb, int64_t* zb) {
+  int G = D / 32, c = d / 2, g = c / 16, m = c % 16, j = t / 4, e = t % 4;
+  int l = 16 * j + m, n = 2 * e + (d & 1);
+  *xb = 32 * ((int64_t)l * (G / 2) + g / 2) + 4 * n + 2 * (g % 2);
+  int64_t zi = ((int64_t)l * G + g) / 4, zs = ((int64_t)l * G + g) % 4;
+  *zb = 32 * (32 * (int64_t)G + zi) + 4 * n + zs;
+}
+static void put_bit(uint8_t* reg, int64_t bit, int v) {
+  uint8_t* p = reg + bit / 8;
+  *p = v ? (uint8_t)(*p | (1u << (bit % 8))) : (uint8_t)(*p & ~(1u << (bit % 8)));
+}
+static int get_bit(const uint8_t* reg, int64_t bit) { return (reg[bit / 8] >> (bit % 8)) & 1; }
+static void put_v(uint8_t* blk, int t, int d, int D, int k_codec, int v_codec, uint8_t u) {
+  uint8_t* reg = blk + vbase_of(D, k_codec);
+  int b = vbits_of(v_codec);
+  if (b == 4) { put_nibble(reg + (v_byte(t, d, D) - 8 * (int64_t)D), d & 1, u); return; }
+  int64_t xb, zb;
+  vbit_pos(t, d, D, &xb, &zb);
+  put_bit(reg, xb, u & 1);
+  put_bit(reg, xb + 1, (u >> 1) & 1);
+  if (b == 3) put_bit(reg, zb, (u >> 2) & 1);
+}
+static uint8_t get_v(const uint8_t* blk, int t, int d, int D, int k_codec, int v_codec) {
+  const uint8_t* reg = blk + vbase_of(D, k_codec);
+  int b = vbits_of(v_codec);
+  if (b == 4) return get_nibble(reg + (v_byte(t, d, D) - 8 * (int64_t)D), d & 1);
+  int64_t xb, zb;
+  vbit_pos(t, d, D, &xb, &zb);
+  int u = get_bit(reg, xb) | (get_bit(reg, xb + 1) << 1);
+  if (b == 3) u |= get_bit(reg, zb) << 2;
+  return (uint8_t)u;
+}
+
+/* Store n tokens x Hkv heads into a pool of any (k_codec, v_codec): keys as indices ku and
+ * scales ks (4-bit keys) or fp16 bits kh (fp16 keys), values as indices vu, scales vs.
+ * Negative slots are skipped. */
+void or_place_kv(uint8_t* pool, int D, int Hkv, int k_codec, int v_codec, int64_t n,
+                 const int64_t* slots, const uint8_t* ku, const uint16_t* ks, const uint16_t* kh,
+                 const uint8_t* vu, const uint16_t* vs) {
+  int G = D / 32;
+  int64_t bb = or_block_bytes_kv(D, k_codec, v_codec);
+  for (int64_t i = 0; i < n; i++) {
+    if (slots[i] < 0) continue;
+    int64_t page = slots[i] / OR_PAGE;
+    int t = (int)(slots[i] % OR_PAGE);
+    for (int h = 0; h < Hkv; h++) {
+      uint8_t* blk = pool + (page * Hkv + h) * bb;
+      int64_t row = i * Hkv + h;
+      for (int d = 0; d < D; d++) {
+        if (k_codec == OR_KF16) put16(blk + kf16_off(t, d), kh[row * D + d]);
+        else put_nibble(blk + k_byte(t, d, D), (d % 8) & 1, ku[row * D + d]);
+        put_v(blk, t, d, D, k_codec, v_codec, vu[row * D + d]);
+      }
+      for (int k = 0; k < G; k++) {
+        if (k_codec != OR_KF16) put16(blk + kv_ks_off(t, k, D, v_codec), ks[row * G + k]);
+        put16(blk + kv_vs_off(t, k, D, k_codec, v_codec), vs[row * G + k]);
+      }
+    }
+  }
+}
+
+/* Read back one token of a pool of any (k_codec, v_codec): key indices and scales (4-bit
+ * keys) or key fp16 bits (fp16 keys), value indices and scales. */
+void or_fetch_kv(const uint8_t* pool, int D, int Hkv, int k_codec, int v_codec, int64_t page,
+                 int t, int h, uint8_t* ku, uint16_t* ks, uint16_t* kh, uint8_t* vu, uint16_t* vs) {
+  int G = D / 32;
+  const uint8_t* blk = pool + (page * Hkv + h) * or_block_bytes_kv(D, k_codec, v_codec);
+  for (int d = 0; d < D; d++) {
+    if (k_codec == OR_KF16) kh[d] = get16(blk + kf16_off(t, d));
+    else ku[d] = get_nibble(blk + k_byte(t, d, D), (d % 8) & 1);
+    vu[d] = get_v(blk, t, d, D, k_codec, v_codec);
+  }
+  for (int k = 0; k < G; k++) {
+    if (k_codec != OR_KF16) ks[k] = get16(blk + kv_ks_off(t, k, D, v_codec));
+    vs[k] = get16(blk + kv_vs_off(t, k, D, k_codec, v_codec));
+  }
+}
+
 /* Append [one fused step per the Open-TQ-Metal card abstract]: encode K and V of n tokens
  * ([n][Hkv][D] fp32) and store them at their slots. */
 void or_append(uint8_t* pool, int D, int Hkv, int k_codec, int v_codec, const uint32_t* sign_bits,
@@ -375,10 +495,10 @@ void or_append(uint8_t* pool, int D, int Hkv, int k_codec, int v_codec, const ui
   or_encode(v, nv, D, OR_GROUP, sign_bits, v_codec, vu, vs);
   if (k_codec == OR_KF16) {  /* keys kept in fp16, original basis */
     or_keys_f16(k, nv * D, ks);
-    or_place_kf16(pool, D, Hkv, n, slots, ks, vu, vs);
+    or_place_kv(pool, D, Hkv, k_codec, v_codec, n, slots, NULL, NULL, ks, vu, vs);
   } else {
     or_encode(k, nv, D, OR_GROUP, sign_bits, k_codec, ku, ks);
-    or_place(pool, D, Hkv, n, slots, ku, ks, vu, vs);
+    or_place_kv(pool, D, Hkv, k_codec, v_codec, n, slots, ku, ks, NULL, vu, vs);
   }
   free(ku); free(vu); free(ks); free(vs);
 }
@@ -452,11 +572,10 @@ void or_decode(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec, int v_c
     uint16_t ks[16], vs[16], kh[512];
     for (int64_t t = 0; t < L; t++) {
       int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
+      or_fetch_kv(pool, D, Hkv, k_codec, v_codec, page, (int)(t % OR_PAGE), h, ku, ks, kh, vu, vs);
       if (k_codec == OR_KF16) {
-        or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
         for (int d = 0; d < D; d++) K[t * D + d] = or_f16_to_f64(kh[d]);
       } else {
-        or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
         for (int d = 0; d < D; d++) K[t * D + d] = dequant1(k_codec, ku[d], ks[d / 32], lut);
       }
       for (int d = 0; d < D; d++) V[t * D + d] = dequant1(v_codec, vu[d], vs[d / 32], lut);
@@ -503,10 +622,10 @@ void or_decode_sparse_v(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec
       int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
       double dot = 0.0;
       if (k_codec == OR_KF16) {
-        or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
+        or_fetch_kv(pool, D, Hkv, k_codec, v_codec, page, (int)(t % OR_PAGE), h, ku, ks, kh, vu, vs);
         for (int d = 0; d < D; d++) dot += qd[d] * or_f16_to_f64(kh[d]);
       } else {
-        or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+        or_fetch_kv(pool, D, Hkv, k_codec, v_codec, page, (int)(t % OR_PAGE), h, ku, ks, kh, vu, vs);
         for (int d = 0; d < D; d++) dot += qd[d] * dequant1(k_codec, ku[d], ks[d / 32], lut);
       }
       sc[t] = (double)alpha * dot;
@@ -518,8 +637,7 @@ void or_decode_sparse_v(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec
     double bnd = 0.0;
     for (int64_t t = 0; t < L; t++) {  /* weighted values, kept or bounded */
       int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
-      if (k_codec == OR_KF16) or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
-      else or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+      or_fetch_kv(pool, D, Hkv, k_codec, v_codec, page, (int)(t % OR_PAGE), h, ku, ks, kh, vu, vs);
       for (int d = 0; d < D; d++) vt[d] = dequant1(v_codec, vu[d], vs[d / 32], lut);
       double w = exp(sc[t] - mx) / l;
       if (w >= thr) {
@@ -573,10 +691,10 @@ void or_decode_hotcold(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec,
       int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
       double dot = 0.0;
       if (k_codec == OR_KF16) {
-        or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
+        or_fetch_kv(pool, D, Hkv, k_codec, v_codec, page, (int)(t % OR_PAGE), h, ku, ks, kh, vu, vs);
         for (int d = 0; d < D; d++) dot += qc[d] * or_f16_to_f64(kh[d]);
       } else {
-        or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+        or_fetch_kv(pool, D, Hkv, k_codec, v_codec, page, (int)(t % OR_PAGE), h, ku, ks, kh, vu, vs);
         for (int d = 0; d < D; d++) dot += qc[d] * dequant1(k_codec, ku[d], ks[d / 32], lut);
       }
       sc[t] = (double)alpha * dot;
@@ -593,8 +711,7 @@ void or_decode_hotcold(const uint8_t* pool, int D, int Hq, int Hkv, int k_codec,
     for (int i = 0; i < D; i++) { accc[i] = 0.0; acch[i] = 0.0; }
     for (int64_t t = 0; t < Lc; t++) {  /* cold values, rotated basis */
       int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
-      if (k_codec == OR_KF16) or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
-      else or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+      or_fetch_kv(pool, D, Hkv, k_codec, v_codec, page, (int)(t % OR_PAGE), h, ku, ks, kh, vu, vs);
       double w = exp(sc[t] - mx);
       l += w;
       for (int d = 0; d < D; d++) accc[d] += w * dequant1(v_codec, vu[d], vs[d / 32], lut);
@@ -633,10 +750,10 @@ void or_dequant(const uint8_t* pool, int D, int Hkv, int k_codec, int v_codec,
         int64_t page = block_table[(int64_t)b * max_pages + t / OR_PAGE];
         float ky[512], vy[512];
         if (k_codec == OR_KF16) {
-          or_fetch_kf16(pool, D, Hkv, page, (int)(t % OR_PAGE), h, kh, vu, vs);
+          or_fetch_kv(pool, D, Hkv, k_codec, v_codec, page, (int)(t % OR_PAGE), h, ku, ks, kh, vu, vs);
           for (int d = 0; d < D; d++) ky[d] = (float)or_f16_to_f64(kh[d]);
         } else {
-          or_fetch(pool, D, Hkv, page, (int)(t % OR_PAGE), h, ku, ks, vu, vs);
+          or_fetch_kv(pool, D, Hkv, k_codec, v_codec, page, (int)(t % OR_PAGE), h, ku, ks, kh, vu, vs);
           for (int d = 0; d < D; d++) ky[d] = (float)dequant1(k_codec, ku[d], ks[d / 32], lut);
         }
         for (int d = 0; d < D; d++) vy[d] = (float)dequant1(v_codec, vu[d], vs[d / 32], lut);

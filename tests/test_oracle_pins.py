@@ -105,16 +105,16 @@ def test_unrotate_inverts_rotate(orc):
 
 # ---- abs-max codec --------------------------------------------------------------------------
 
-def _brute_absmax(y, s):
-    """argmin over c in [-7, 7] of |y - c s| (exact fp64), ties to the even c. Entries whose
-    exact quotient y/s lies within 2^-20 of a half-integer are returned as None: there the
-    fp32 quotient the codec rounds may fall on either side, and both neighbours are valid."""
-    cs = np.arange(-7, 8)
+def _brute_absmax(y, s, qmax=7):
+    """argmin over c in [-qmax, qmax] of |y - c s| (exact fp64), ties to the even c. Entries
+    whose exact quotient y/s lies within 2^-20 of a half-integer are returned as None: there
+    the fp32 quotient the codec rounds may fall on either side, and both neighbours are valid."""
+    cs = np.arange(-qmax, qmax + 1)
     out = []
     for v in y:
         qv = np.float64(v) / np.float64(s)
         frac = abs(qv - math.floor(qv) - 0.5)
-        if frac < 2.0 ** -20 and abs(qv) < 7.5 and frac != 0.0:
+        if frac < 2.0 ** -20 and abs(qv) < qmax + 0.5 and frac != 0.0:
             out.append(None)
             continue
         err = np.abs(np.float64(v) - cs * np.float64(s))
@@ -127,11 +127,11 @@ def _match(codes, brute):
     return all(b is None or int(c) == int(b) for c, b in zip(codes, brute))
 
 
-def _absmax_groups(orc, y):
+def _absmax_groups(orc, y, qmax=7):
     if hasattr(orc, "quant_absmax") and orc.__name__.endswith("c_oracle"):
-        u, s = orc.quant_absmax(y)
+        u, s = orc.quant_absmax(y, qmax)
         return u, np.uint16(s).view(np.float16)
-    u, s = orc.quant_absmax(y[None, :], group=y.shape[0])
+    u, s = orc.quant_absmax(y[None, :], group=y.shape[0], qmax=qmax)
     return u[0], s[0, 0]
 
 
@@ -149,6 +149,27 @@ def test_absmax_error_bound_and_brute_force(orc):
         assert np.all(np.abs(y.astype(np.float64) - c * s) <= s / 2 * (1 + 2.0 ** -20))
         assert _match(c, _brute_absmax(y, s))
         assert np.all((u >= 1) & (u <= 15))
+
+
+@pytest.mark.parametrize("qmax", [3, 1])
+def test_low_bit_absmax_error_bound_and_brute_force(orc, qmax):
+    """3-bit (qmax 3) and 2-bit (qmax 1) abs-max: the scale is fp16(absmax/qmax), every
+    code is the nearest level (brute force, ties to even), the error is at most s/2, and
+    the stored index u = c + qmax + 1 fills 1..2 qmax + 1."""
+    rng = np.random.default_rng(12 + qmax)
+    for trial in range(300):
+        y = (rng.standard_normal(32) * rng.lognormal(0, 2)).astype(np.float32)
+        if trial % 5 == 0:
+            y[rng.integers(32)] *= 30.0
+        u, s16 = _absmax_groups(orc, y, qmax)
+        s = np.float64(np.float16(s16))
+        c = u.astype(np.int64) - (qmax + 1)
+        assert np.float16(s16) == np.float16(np.float32(np.max(np.abs(y))) / np.float32(qmax))
+        assert np.all(np.abs(y.astype(np.float64) - c * s) <= s / 2 * (1 + 2.0 ** -20))
+        assert _match(c, _brute_absmax(y, s, qmax))
+        assert np.all((u >= 1) & (u <= 2 * qmax + 1))
+    u, s16 = _absmax_groups(orc, np.zeros(32, np.float32), qmax)
+    assert float(np.float16(s16)) == 0.0 and np.all(u == qmax + 1)
 
 
 def test_absmax_ties_go_to_even(orc):
@@ -354,6 +375,121 @@ def test_fp16_key_memory_formula(coracle):
         assert per_token / (2 * D * 2) == pytest.approx((16 + 4) / (2 * 16) + 16 / 32 / (2 * 16))
 
 
+def _exact_low_bit(rng, n, D, sb, qmax):
+    """x with R(x) = c exactly: c integer in [-qmax, qmax], every group holding a +-qmax."""
+    c = rng.integers(-qmax, qmax + 1, size=(n, D)).astype(np.float64)
+    for g in range(D // 32):
+        c[np.arange(n), g * 32 + rng.integers(0, 32, n)] = rng.choice([-float(qmax), float(qmax)], n)
+    sig = np.array([-1.0 if (sb[i // 32] >> (i % 32)) & 1 else 1.0 for i in range(D)])
+    x = (c @ _hadamard(D)) / math.sqrt(D) * sig
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    return c, x.astype(np.float32)
+
+
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("k_codec,v_codec", [(0, 3), (0, 4), (2, 3), (2, 4)])
+def test_low_bit_values_lossless_equal_plain_attention(coracle, noracle, D, k_codec, v_codec):
+    """3-bit and 2-bit values: with values whose rotation is an integer vector with a
+    +-qmax in every group (lossless for the codec) and lossless keys (4-bit integers or
+    fp16-representable), decode equals plain softmax attention on the original q, k, v;
+    this passes through the packed value layout of a pool."""
+    qmax = 3 if v_codec == 3 else 1
+    rng = np.random.default_rng(D + 10 * v_codec + k_codec)
+    sb = _sb(D, 5)
+    L, Hkv, Hq = 53, 2, 4
+    if k_codec == 0:
+        _, k = _exact_vectors(rng, L * Hkv, D, sb, coracle)
+        k = k.reshape(L, Hkv, D)
+        _, q = _exact_vectors(rng, Hq, D, sb, coracle)
+        q = q[None]
+    else:
+        k = (rng.standard_normal((L, Hkv, D)) * 3.0).astype(np.float16).astype(np.float32)
+        q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+    _, v = _exact_low_bit(rng, L * Hkv, D, sb, qmax)
+    v = v.reshape(L, Hkv, D)
+    bt = np.array([[2, 0, 3, 1]], np.int32)
+    slots = W.slots_for(bt, 0, 0, L)
+    alpha = 0.0625
+    for orc in (coracle, noracle):
+        pool = orc.new_pool(4, Hkv, D, k_codec, v_codec)
+        orc.append(pool, D, Hkv, k, v, slots, sb, k_codec, v_codec)
+        out = orc.decode(pool, D, Hq, Hkv, sb, bt, np.array([L], np.int32), q, alpha,
+                         k_codec=k_codec, v_codec=v_codec)
+        for hq in range(Hq):
+            h = hq // (Hq // Hkv)
+            s = alpha * (k[:, h].astype(np.float64) @ q[0, hq].astype(np.float64))
+            w = np.exp(s - s.max())
+            plain = (w @ v[:, h].astype(np.float64)) / w.sum()
+            assert np.max(np.abs(out[0, hq] - plain)) < 1e-12 * np.max(np.abs(plain))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("k_codec,v_codec", [(0, 3), (0, 4), (2, 3), (2, 4)])
+def test_low_bit_value_packing(coracle, noracle, D, k_codec, v_codec):
+    """The b-bit value region of a block: random codes of 16 tokens read back unchanged;
+    every bit of the region belongs to exactly one (token, dim) (a token of all-ones codes
+    sets 16 D b bits in total over the 16 tokens, none twice, and nothing outside the
+    region); every byte of the region holds bits of one token only (appends of different
+    tokens never share a byte); both oracles write the same bytes."""
+    bits = 3 if v_codec == 3 else 2
+    G, Hkv = D // 32, 1
+    rng = np.random.default_rng(D + bits)
+    vu = rng.integers(1, 2 ** bits, size=(16, Hkv, D)).astype(np.uint8)
+    vs = rng.integers(0x3000, 0x4000, size=(16, Hkv, G)).astype(np.uint16)
+    kh = rng.integers(0, 0x7C00, size=(16, Hkv, D)).astype(np.uint16)
+    ku = rng.integers(0, 16, size=(16, Hkv, D)).astype(np.uint8)
+    ks = rng.integers(0x3000, 0x4000, size=(16, Hkv, G)).astype(np.uint16)
+    slots = np.arange(16, dtype=np.int64)
+    pool = coracle.new_pool(1, Hkv, D, k_codec, v_codec)
+    kw = dict(kh=kh) if k_codec == 2 else dict(ku=ku, ks=ks)
+    coracle.place_kv(pool, D, Hkv, slots, vu, vs, k_codec=k_codec, v_codec=v_codec, **kw)
+    for t in range(16):
+        gku, gks, gkh, gvu, gvs = coracle.fetch_kv(pool, D, Hkv, 0, t, 0, k_codec, v_codec)
+        assert np.array_equal(gvu, vu[t, 0]) and np.array_equal(gvs, vs[t, 0])
+        if k_codec == 2:
+            assert np.array_equal(gkh, kh[t, 0])
+        else:
+            assert np.array_equal(gku, ku[t, 0]) and np.array_equal(gks, ks[t, 0])
+    npool = noracle.new_pool(1, Hkv, D, k_codec, v_codec)
+    if k_codec == 2:
+        noracle.place_kf16(npool, D, Hkv, slots, kh.view(np.float16), vu, vs.view(np.float16), v_codec)
+    else:
+        noracle.place(npool, D, Hkv, slots, ku, ks.view(np.float16), vu, vs.view(np.float16), v_codec)
+    assert np.array_equal(pool, npool)
+    vbase = 32 * D if k_codec == 2 else 8 * D
+    vlen = 2 * bits * D
+    ones = np.full((1, Hkv, D), 2 ** bits - 1, np.uint8)
+    zero_s = np.zeros((1, Hkv, G), np.uint16)
+    owner = np.full(vlen, -1)
+    total = np.zeros(vlen, np.uint8)
+    for t in range(16):
+        p = coracle.new_pool(1, Hkv, D, k_codec, v_codec)
+        kw1 = dict(kh=np.zeros((1, Hkv, D), np.uint16)) if k_codec == 2 else \
+            dict(ku=np.zeros((1, Hkv, D), np.uint8), ks=zero_s)
+        coracle.place_kv(p, D, Hkv, np.array([t], np.int64), ones, zero_s, k_codec=k_codec,
+                         v_codec=v_codec, **kw1)
+        reg = p[vbase:vbase + vlen]
+        assert not np.any(np.delete(p, np.arange(vbase, vbase + vlen)))
+        assert not np.any(total & reg), "a bit written by two tokens"
+        total |= reg
+        nz = np.flatnonzero(reg)
+        assert np.all(owner[nz] == -1), "a byte shared by two tokens"
+        owner[nz] = t
+    assert np.all(total == 0xFF), "every bit of the region is used"
+    assert np.unpackbits(total).sum() == 16 * D * bits
+
+
+def test_low_bit_memory_formula(coracle):
+    """Bytes per token against fp16 K and V: (K bits + V bits) / (2 * 16) plus one fp16
+    scale per 32 values of each quantized side (the mlxcel manual's formula), for fp16
+    keys with 3-bit values (its fp16+turbo3 mode) and 4-bit keys with 2- or 3-bit values."""
+    for D in (64, 128, 256):
+        for k_codec, kbits, v_codec, vbits in ((2, 16, 3, 3), (2, 16, 4, 2), (0, 4, 3, 3), (0, 4, 4, 2)):
+            per_token = coracle.block_bytes(D, k_codec, v_codec) / 16
+            side = (16 / 32) * ((1 if k_codec == 0 else 0) + 1) / (2 * 16)
+            assert per_token / (2 * D * 2) == pytest.approx((kbits + vbits) / (2 * 16) + side)
+
+
 def test_sparse_values_against_plain_softmax(coracle):
     """Sparse values [mlxcel manual, sparse-V threshold]: with lossless k, v, q the oracle's
     kept-terms output and drop bound equal a plain softmax computed here, for thresholds
@@ -516,7 +652,8 @@ def test_split_softmax_merge_equals_direct(coracle):
 # ---- the two oracles agree ---------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["single_head_1k", "llama8b_b16_8k", "gemma_d256_32k", "mixed_serving",
-                                  "llama70b_b1_128k_k16v4"])
+                                  "llama70b_b1_128k_k16v4", "llama70b_b1_128k_k16v3",
+                                  "llama70b_b1_128k_k4v2"])
 def test_c_and_numpy_oracles_agree(coracle, noracle, name):
     w = W.WORKLOADS[name].scaled(context=45, batch=2, ragged_min=20, prefill=0)
     D, Hkv, Hq = w.head_dim, w.kv_heads, w.q_heads
@@ -525,7 +662,7 @@ def test_c_and_numpy_oracles_agree(coracle, noracle, name):
     bt, _, npages = W.page_tables(w, lens, 0)
     pools = {}
     for orc in (coracle, noracle):
-        pool = orc.new_pool(npages, Hkv, D, w.k_codec)
+        pool = orc.new_pool(npages, Hkv, D, w.k_codec, w.v_codec)
         for b in range(w.batch):
             k, v, _, _ = W.seq_tokens(w, b, int(lens[b]), 0)
             orc.append(pool, D, Hkv, k, v, W.slots_for(bt, b, 0, int(lens[b])), sb,
