@@ -12,6 +12,9 @@
  *  - Or keys stay in fp16 and only values take the 4-bit rotated form: the asymmetric
  *    mode the mlxcel "TurboQuant KV cache" manual recommends by default (cache-mode table,
  *    fp16+turbo4). Keys are then stored unrotated and scored against the query as given.
+ *  - Values may also take 3 or 2 bits (the same rotation, abs-max with fewer levels): the
+ *    manual's fp16+turbo3 mode is fp16 keys with 3-bit values; "TurboQuant on AMD GPUs",
+ *    section 2, notes that 2 bits are possible.
  *  - Decode attention runs directly on the packed codes: the query is rotated into the
  *    cache basis, scores and the weighted value sum are computed from codes and scales,
  *    the softmax is online, and no dequantized K/V matrix is written [Open-TQ-Metal, arXiv
@@ -31,6 +34,9 @@
  *    t_i += t_{i+off}, off = 16, 8, 4, 2, 1; u = #{j in 1..15 : y/n >= (LUT_{j-1}+LUT_j)/2},
  *    u = 8 when n = 0. Value = LUT_u * n.
  *  - fp16 keys: k16 = fp16_rne(k) of the original key (saturating at 65504), no rotation.
+ *  - 3-bit and 2-bit values (v_codec TQ_CODEC_ABSMAX3, TQ_CODEC_ABSMAX2): abs-max with the
+ *    largest level Q = 3 or 1 in place of 7: s = fp16_rne(max|y|/Q), c = clamp(rint(y/s),
+ *    -Q, Q), stored index u = c + Q + 1. Value = (u - Q - 1) * s.
  *
  * Pool format. A pool is one device buffer of num_pages * num_kv_heads * TQ_BLOCK_BYTES(D)
  * bytes, [page][kv head][block]. A block holds 16 tokens of one KV head (G = D/32):
@@ -47,6 +53,15 @@
  *     K of token t, dim d = 32g + 8j + e     ->  byte 1024g + 16(16j + t) + 2e
  *     V indices and scales as above, their regions starting at 32*D and 40*D
  * (each group's 16 tokens x 32 dims are one 1 KB run, again one 16-byte load per lane).
+ * With b-bit values (b = 3 or 2) the V index region takes 2*b*D bytes instead of 8*D and
+ * the scale regions follow it (block bytes: TQ_BLOCK_BYTES_KV). Its dwords are derived
+ * from the 4-bit V region's, read as 64 rows of G little-endian dwords (row 16j + m,
+ * dword g = the indices of dim pair m of group g of tokens 4j..4j+3, byte e = token
+ * 4j + e, low nibble the even dim): the two low bits of each nibble of dwords g = 2i and
+ * 2i + 1 of row l form X dword l*G/2 + i (dword 2i in bits 0-1 of every nibble, 2i + 1 in
+ * bits 2-3); for b = 3 the third bits follow as 16*G Z dwords, bit 2 of each nibble of
+ * dword g of row l going to bit (l*G + g) % 4 of that nibble in Z dword (l*G + g) / 4.
+ * Every byte then holds bits of one token only.
  * A slot is page * 16 + offset within the page.
  *
  * Conventions.
@@ -60,7 +75,8 @@
  *    out-of-range values there are undefined behaviour.
  *  - GPU support: head_dim in {64, 128, 256}, group_size 32, page_size 16,
  *    1 <= num_q_heads / num_kv_heads <= 8, batch * num_kv_heads <= 2^20; decode with fp16
- *    keys at head_dim 64 and 128 (TQ_EUNSUPPORTED otherwise).
+ *    keys at head_dim 64 and 128; sparse values with 4-bit values only (TQ_EUNSUPPORTED
+ *    otherwise).
  */
 #ifndef TQ_H
 #define TQ_H
@@ -80,11 +96,21 @@ typedef enum {
   TQ_EDEVICE = -4        /* the HIP runtime reported an error */
 } tq_status;
 
-typedef enum { TQ_CODEC_ABSMAX = 0, TQ_CODEC_LLOYDMAX = 1, TQ_CODEC_FP16 = 2 } tq_codec;
+typedef enum {
+  TQ_CODEC_ABSMAX = 0,    /* 4-bit abs-max (keys or values) */
+  TQ_CODEC_LLOYDMAX = 1,  /* 4-bit Lloyd-Max table times the group norm (keys) */
+  TQ_CODEC_FP16 = 2,      /* fp16, not rotated (keys) */
+  TQ_CODEC_ABSMAX3 = 3,   /* 3-bit abs-max (values) */
+  TQ_CODEC_ABSMAX2 = 4    /* 2-bit abs-max (values) */
+} tq_codec;
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
 #define TQ_BLOCK_BYTES(D) (16 * (D) + 64 * ((D) / 32))
 #define TQ_BLOCK_BYTES_KF16(D) (41 * (D))
+/* any (k_codec, v_codec): keys 8*D (4-bit) or 32*D (fp16), values 2*b*D, scales D or 2*D */
+#define TQ_VALUE_BITS(VC) ((VC) == TQ_CODEC_ABSMAX3 ? 3 : ((VC) == TQ_CODEC_ABSMAX2 ? 2 : 4))
+#define TQ_BLOCK_BYTES_KV(D, KC, VC)                                                  \
+  (((KC) == TQ_CODEC_FP16 ? 33 * (D) : 10 * (D)) + 2 * TQ_VALUE_BITS(VC) * (D))
 
 /* The first TQ_DECODE_COUNTER_BYTES bytes of a decode workspace hold per-(sequence,
  * kv head) arrival counters. They must be zero before the workspace is first used; every
@@ -99,15 +125,15 @@ typedef struct {
   int32_t page_size;         /* tokens per page, must be 16 */
   int32_t num_pages;         /* physical pages in the pool */
   int32_t k_codec;           /* tq_codec for keys: ABSMAX, LLOYDMAX or FP16 */
-  int32_t v_codec;           /* tq_codec for values (TQ_CODEC_ABSMAX only) */
+  int32_t v_codec;           /* tq_codec for values: ABSMAX, ABSMAX3 or ABSMAX2 */
   const uint32_t* sign_bits; /* device, D/32 words; bit i of word i/32 set => sigma_i = -1 */
 } tq_layout;
 
 /* Human-readable name of a tq_status (static string, never NULL). */
 const char* tq_status_str(int status);
 
-/* Bytes of one physical page of the pool (all KV heads): num_kv_heads * TQ_BLOCK_BYTES(D)
- * (TQ_BLOCK_BYTES_KF16(D) with fp16 keys). Returns 0 for an invalid layout. */
+/* Bytes of one physical page of the pool (all KV heads):
+ * num_kv_heads * TQ_BLOCK_BYTES_KV(D, k_codec, v_codec). Returns 0 for an invalid layout. */
 size_t tq_page_bytes(const tq_layout* layout);
 
 /* Append: rotate, quantize and store n_tokens new K and V vectors.

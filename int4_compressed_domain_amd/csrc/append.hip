@@ -7,7 +7,7 @@
 
 namespace {
 
-template <int D, typename TIn, int KCODEC>
+template <int D, typename TIn, int KCODEC, int VCODEC>
 __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
                                                      const TIn* __restrict__ kin,
                                                      const TIn* __restrict__ vin,
@@ -15,7 +15,8 @@ __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
                                                      const uint32_t* __restrict__ sign_bits,
                                                      int n_tokens, int Hkv) {
   constexpr int E = D / 16;
-  constexpr int BB = tq_block_bytes(D, KCODEC);
+  constexpr int BB = tq_block_bytes(D, KCODEC, VCODEC);
+  constexpr int VB = tq_value_bits(VCODEC);
   constexpr bool KF16 = KCODEC == TQ_CODEC_FP16;
   const int lane = threadIdx.x & 15;
   const int64_t vec = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -37,27 +38,37 @@ __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
   uint32_t u[E];
   f16 scale;
   const uint32_t sw = lane_signs<D>(sign_bits, lane);
-  if (is_v || KCODEC != TQ_CODEC_LLOYDMAX) codec_vector<D, TQ_CODEC_ABSMAX>(y, sw, lane, u, scale);
-  else codec_vector<D, TQ_CODEC_LLOYDMAX>(y, sw, lane, u, scale);
-  place_vector<D, KF16>(blk, (int)(slot & 15), lane, is_v != 0, u, scale);
+  if (is_v) codec_vector<D, VCODEC>(y, sw, lane, u, scale);
+  else if (KCODEC == TQ_CODEC_LLOYDMAX) codec_vector<D, TQ_CODEC_LLOYDMAX>(y, sw, lane, u, scale);
+  else codec_vector<D, TQ_CODEC_ABSMAX>(y, sw, lane, u, scale);
+  place_vector<D, KF16, VB>(blk, (int)(slot & 15), lane, is_v != 0, u, scale);
 }
 
-template <int D, typename T>
-hipError_t launch_d(const LaunchAppend& a, hipStream_t st) {
+template <int D, typename T, int VC>
+hipError_t launch_v(const LaunchAppend& a, hipStream_t st) {
   const int64_t nvec = (int64_t)a.n_tokens * a.Hkv * 2;
   dim3 grid((unsigned)((nvec + 15) / 16));
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
   if (a.k_codec == TQ_CODEC_LLOYDMAX)
-    hipLaunchKernelGGL((append_kernel<D, T, TQ_CODEC_LLOYDMAX>), grid, dim3(256), 0, st, a.pool, k, v,
+    hipLaunchKernelGGL((append_kernel<D, T, TQ_CODEC_LLOYDMAX, VC>), grid, dim3(256), 0, st, a.pool, k, v,
                        a.slots, a.sign_bits, a.n_tokens, a.Hkv);
   else if (a.k_codec == TQ_CODEC_FP16)
-    hipLaunchKernelGGL((append_kernel<D, T, TQ_CODEC_FP16>), grid, dim3(256), 0, st, a.pool, k, v,
+    hipLaunchKernelGGL((append_kernel<D, T, TQ_CODEC_FP16, VC>), grid, dim3(256), 0, st, a.pool, k, v,
                        a.slots, a.sign_bits, a.n_tokens, a.Hkv);
   else
-    hipLaunchKernelGGL((append_kernel<D, T, TQ_CODEC_ABSMAX>), grid, dim3(256), 0, st, a.pool, k, v,
+    hipLaunchKernelGGL((append_kernel<D, T, TQ_CODEC_ABSMAX, VC>), grid, dim3(256), 0, st, a.pool, k, v,
                        a.slots, a.sign_bits, a.n_tokens, a.Hkv);
   return hipGetLastError();
+}
+
+template <int D, typename T>
+hipError_t launch_d(const LaunchAppend& a, hipStream_t st) {
+  switch (a.v_codec) {
+    case TQ_CODEC_ABSMAX3: return launch_v<D, T, TQ_CODEC_ABSMAX3>(a, st);
+    case TQ_CODEC_ABSMAX2: return launch_v<D, T, TQ_CODEC_ABSMAX2>(a, st);
+    default: return launch_v<D, T, TQ_CODEC_ABSMAX>(a, st);
+  }
 }
 
 template <int D>

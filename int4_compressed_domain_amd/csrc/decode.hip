@@ -41,24 +41,29 @@ __device__ __forceinline__ f16x8 unpack_k_sub(uint32_t w) {
   return __builtin_bit_cast(f16x8, r);
 }
 
-// Geometry of a block and of its staged copy in LDS: [K][V indices][scales].
-template <int D, int KC>
+// Geometry of a block and of its staged copy in LDS: [K][V indices][scales]. VB: bits per
+// value index; 4-bit values are staged chunk by chunk like the keys, packed 3- and 2-bit
+// values as one contiguous copy of their region.
+template <int D, int KC, int VB = 4>
 struct Cfg {
   static constexpr bool KF16 = KC == TQ_CODEC_FP16;   // fp16 keys
   static constexpr int G = D / 32;
-  static constexpr int BB = tq_block_bytes(D, KC);
+  static constexpr int VC = VB == 4 ? TQ_CODEC_ABSMAX : (VB == 3 ? TQ_CODEC_ABSMAX3 : TQ_CODEC_ABSMAX2);
+  static constexpr int BB = tq_block_bytes(D, KC, VC);
   static constexpr int KB = 4 * G;                    // index bytes per lane per page (K or V)
   static constexpr int DMAK = KB >= 16 ? 16 : 4;      // LDS-DMA size for index loads
   static constexpr int NK = KB / DMAK;                // DMAs per index region
+  static constexpr int VR = 2 * VB * D;               // V index bytes of a block
+  static constexpr int NVP = (VR + 1023) / 1024;      // 16-byte DMAs for packed values
   static constexpr int KREG = KF16 ? 32 * D : 64 * KB;  // staged K bytes (fp16: G runs of 1 KB)
   static constexpr int VOFF = KREG;                   // staged V indices
-  static constexpr int SOFF = VOFF + 64 * KB;         // staged scales
+  static constexpr int SOFF = VOFF + (VB == 4 ? 64 * KB : VR);  // staged scales
   static constexpr int SCB = KF16 ? 32 * G : 64 * G;  // scale bytes (fp16 keys: V scales only)
   static constexpr int NSC = (SCB / 4 + 63) / 64;     // dword DMAs for the scales
-  static constexpr int NDMA = (KF16 ? G : NK) + NK + NSC;  // vector-memory ops per page
+  static constexpr int NDMA = (KF16 ? G : NK) + (VB == 4 ? NK : NVP) + NSC;  // vector-memory ops per page
   static constexpr int SLOT = SOFF + SCB;             // LDS bytes of one staged page
   static constexpr int BV = KF16 ? 32 * D : 8 * D;    // block offsets of the V indices
-  static constexpr int BS = KF16 ? 40 * D : 16 * D;   //   and of the scales
+  static constexpr int BS = BV + VR;                  //   and of the scales
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -82,9 +87,9 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
 // Stage one page (one kv head's block) into an LDS slot:
 //   [K indices: NK chunks of 64 lanes x DMAK][V indices: same][scales: 16G dwords]
 // The buffer descriptor spans exactly this block, so no lane can touch memory outside it.
-template <int D, int KC>
+template <int D, int KC, int VB = 4>
 __device__ __forceinline__ void stage_page(const uint8_t* blk, uint32_t base, int lane) {
-  using C = Cfg<D, KC>;
+  using C = Cfg<D, KC, VB>;
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
   const uint32_t lo = (uint32_t)lane * C::KB;  // this lane's byte offset inside an index region
   if constexpr (C::KF16) {  // fp16 keys: group g's 1 KB run, 16 bytes per lane
@@ -95,11 +100,17 @@ __device__ __forceinline__ void stage_page(const uint8_t* blk, uint32_t base, in
   for (int c = 0; c < C::NK; c++) {
     if constexpr (C::DMAK == 16) {
       if constexpr (!C::KF16) dma16(r, lo + c * 16, 0u, base + c * 1024);
-      dma16(r, lo + c * 16, (uint32_t)C::BV, base + C::VOFF + c * 1024);
+      if constexpr (VB == 4) dma16(r, lo + c * 16, (uint32_t)C::BV, base + C::VOFF + c * 1024);
     } else {
       if constexpr (!C::KF16) dma4(r, lo + c * 4, 0u, base + c * 256);
-      dma4(r, lo + c * 4, (uint32_t)C::BV, base + C::VOFF + c * 256);
+      if constexpr (VB == 4) dma4(r, lo + c * 4, (uint32_t)C::BV, base + C::VOFF + c * 256);
     }
+  }
+  if constexpr (VB < 4) {  // packed values: the region as is, 1 KB per DMA (lane 0 always active)
+#pragma unroll
+    for (int c = 0; c < C::NVP; c++)
+      if (c * 64 + lane < C::VR / 16)
+        dma16(r, (uint32_t)(c * 64 + lane) * 16, (uint32_t)C::BV, base + C::VOFF + c * 1024);
   }
 #pragma unroll
   for (int c = 0; c < C::NSC; c++)
@@ -239,9 +250,17 @@ __device__ __forceinline__ int dim_kslot(int e) {
   else return (e >> 1) | ((e & 1) << 2);
 }
 
-template <int D, typename TQ, int KCODEC, int NW, bool SPV>
+// One query element of dtype dt (fp32, bf16 or fp16), widened exactly.
+__device__ __forceinline__ float load_q(const void* q, int dt, int64_t i) {
+  if (dt == TQ_F32) return static_cast<const float*>(q)[i];
+  if (dt == TQ_BF16) return widen(static_cast<const uint16_t*>(q)[i]);
+  return widen(static_cast<const f16*>(q)[i]);
+}
+
+template <int D, int KCODEC, int VB, int NW, bool SPV>
 __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
-  using C = Cfg<D, KCODEC>;
+  using C = Cfg<D, KCODEC, VB>;
+  static_assert(!SPV || VB == 4, "sparse values: 4-bit values only");
   constexpr int G = C::G, BB = C::BB, NT = 64 * NW, V = D / 64;
   constexpr bool KF16 = C::KF16;
   // ring slots per wave: as many as ~144 KB of LDS holds, at most 8 (NSLOT - 1 pages in flight)
@@ -355,13 +374,13 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     asm volatile("" ::"v"(swnew));
   }
   if (tid < D / 32) sgn_s[tid] = a.sign_bits[tid];
-  const TQ* qb = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
+  const int64_t qb = ((int64_t)b * a.Hq + (int64_t)h * r) * D;  // this unit's query elements
   float qv[V];
   if (wv < r) {  // wave w rotates query head w: sign flip now, butterflies below
 #pragma unroll
     for (int k = 0; k < V; k++) {
       const int d = lane + 64 * k;
-      const float x = widen(qb[wv * D + d]);
+      const float x = load_q(a.q, a.q_dtype, qb + wv * D + d);
       // fp16 keys are in the original basis: the query scores them unrotated
       qv[k] = (!KF16 && ((a.sign_bits[d >> 5] >> (d & 31)) & 1u)) ? -x : x;
     }
@@ -375,7 +394,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       const int pp = p0 + wv + k * NW;
       if (pp < p1) {
         if constexpr (SPV) stage_k<D, KCODEC>(page_blk(k), slot_lds(k), lane);
-        else stage_page<D, KCODEC>(page_blk(k), slot_lds(k), lane);
+        else stage_page<D, KCODEC, VB>(page_blk(k), slot_lds(k), lane);
       }
     }
   };
@@ -385,9 +404,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     if (KF16 && lane < 16) {
       place_key_f16<D>(tokblk, tnew, lane, ynew);  // fp16 key, no rotation
     } else {
-      if (lane >= 16 || KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, swnew, lane & 15, un, scn);
+      if (lane >= 16) codec_vector<D, C::VC>(ynew, swnew, lane & 15, un, scn);
+      else if (KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, swnew, lane & 15, un, scn);
       else codec_vector<D, TQ_CODEC_LLOYDMAX>(ynew, swnew, lane & 15, un, scn);
-      place_vector<D, KF16>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
+      place_vector<D, KF16, VB>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
     }
   }
   if (wv >= r) stage_first();
@@ -461,8 +481,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // by a second MFMA whose A operand is the constant -8 * 2^-24 (-128 * 2^-24 for odd dims):
   // it adds -8 * 2^-24 * sum_t P'_t to every row, so the accumulator always holds the signed
   // sum and never the offset-biased one.
-  u32x4 ce4 = {0x80088008u, 0x80088008u, 0x80088008u, 0x80088008u};
-  u32x4 co4 = {0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+  // (3- and 2-bit values: offsets 4 and 2, so -4 or -2 * 2^-24 and -64 or -32 * 2^-24)
+  constexpr uint32_t CEV = VB == 4 ? 0x80088008u : (VB == 3 ? 0x80048004u : 0x80028002u);
+  constexpr uint32_t COD = VB == 4 ? 0x80808080u : (VB == 3 ? 0x80408040u : 0x80208020u);
+  u32x4 ce4 = {CEV, CEV, CEV, CEV};
+  u32x4 co4 = {COD, COD, COD, COD};
   asm("" : "+v"(ce4), "+v"(co4));  // keep the constant operands in VGPRs
   const f16x8 ceven = __builtin_bit_cast(f16x8, ce4), codd = __builtin_bit_cast(f16x8, co4);
   const int ltail = L & 15;
@@ -480,6 +503,45 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   float m_run = -INFINITY, nmd = INFINITY, l_run = 0.0f;
 
   auto load_idx = [&](const uint8_t* slot, uint32_t (&w)[G], int region) {  // region 0: K, 1: V
+    if constexpr (VB < 4) {
+      if (region) {
+        // packed values back to the 4-bit layout's dwords w[g] (indices in the low 3 or 2
+        // bits of each nibble): X dword g/2 of this lane's row, shifted by 2*(g%2), and for
+        // 3 bits Z dword (lane*G + g)/4, shifted by (lane*G + g)%4, into bit 2
+        const uint8_t* vr = slot + C::VOFF;
+        uint32_t X[G >= 2 ? G / 2 : 1];
+        if constexpr (G == 2) {
+          X[0] = *reinterpret_cast<const uint32_t*>(vr + lane * 4);
+        } else if constexpr (G == 4) {
+          const u32x2 x2 = *reinterpret_cast<const u32x2*>(vr + lane * 8);
+          X[0] = x2[0]; X[1] = x2[1];
+        } else {
+          const u32x4 x4 = *reinterpret_cast<const u32x4*>(vr + lane * 16);
+          X[0] = x4[0]; X[1] = x4[1]; X[2] = x4[2]; X[3] = x4[3];
+        }
+#pragma unroll
+        for (int g = 0; g < G; g++) w[g] = (X[g >> 1] >> (2 * (g & 1))) & 0x33333333u;
+        if constexpr (VB == 3) {
+          const uint8_t* zr = vr + 128 * G;
+          if constexpr (G == 2) {
+            const uint32_t z = *reinterpret_cast<const uint32_t*>(zr + (lane >> 1) * 4) >> (2 * (lane & 1));
+#pragma unroll
+            for (int g = 0; g < G; g++) w[g] |= ((z >> g) & 0x11111111u) << 2;
+          } else {
+            uint32_t Z[G / 4];
+            if constexpr (G == 4) {
+              Z[0] = *reinterpret_cast<const uint32_t*>(zr + lane * 4);
+            } else {
+              const u32x2 z2 = *reinterpret_cast<const u32x2*>(zr + lane * 8);
+              Z[0] = z2[0]; Z[1] = z2[1];
+            }
+#pragma unroll
+            for (int g = 0; g < G; g++) w[g] |= ((Z[g >> 2] >> (g & 3)) & 0x11111111u) << 2;
+          }
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int c = 0; c < C::NK; c++) {
       if constexpr (C::DMAK == 16) {
@@ -727,7 +789,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     auto at = [&](int o) {  // block offset -> offset in dst
       if (!to_lds) return o;
       if (o < C::BV) return KF16 ? o : staged(o);  // keys (fp16 keys are staged as stored)
-      if (o < C::BS) return C::VOFF + staged(o - C::BV);
+      if (o < C::BS) return VB == 4 ? C::VOFF + staged(o - C::BV) : C::VOFF + (o - C::BV);
       return C::SOFF + (o - C::BS);
     };
     if constexpr (KF16) {
@@ -741,9 +803,24 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
         *reinterpret_cast<uint32_t*>(dst + at(off)) = *reinterpret_cast<const uint32_t*>(tokblk + off);
       }
     }
-    for (int c = lane; c < D / 2; c += 64) {  // V index bytes: dim pair c = 16g + m
-      const int off = C::BV + (16 * (tnew >> 2) + (c & 15)) * 4 * G_ + 4 * (c >> 4) + (tnew & 3);
-      dst[at(off)] = tokblk[off];
+    if constexpr (VB == 4) {
+      for (int c = lane; c < D / 2; c += 64) {  // V index bytes: dim pair c = 16g + m
+        const int off = C::BV + (16 * (tnew >> 2) + (c & 15)) * 4 * G_ + 4 * (c >> 4) + (tnew & 3);
+        dst[at(off)] = tokblk[off];
+      }
+    } else {  // packed values: byte tnew % 4 of the X dwords of rows 16j..16j+15 (and of Z)
+      constexpr int XD = G_ >= 2 ? G_ / 2 : 1;
+      const int j = tnew >> 2, e = tnew & 3;
+      for (int i = lane; i < 16 * XD; i += 64) {
+        const int off = C::BV + 4 * (16 * j * XD + i) + e;
+        dst[at(off)] = tokblk[off];
+      }
+      if constexpr (VB == 3) {
+        for (int i = lane; i < 4 * G_; i += 64) {  // Z dwords (l*G + g)/4 of those rows
+          const int off = C::BV + 128 * G_ + 4 * (4 * j * G_ + i) + e;
+          dst[at(off)] = tokblk[off];
+        }
+      }
     }
     constexpr int NSCL = KF16 ? G_ : 2 * G_;  // scales of the token: (K then) V
     if (lane < NSCL) {
@@ -810,7 +887,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int k = 0; k < 4; k++)
       if (nis < nmax) {
-        stage_page<D, KCODEC>(page_blk(nis), slot_lds(nis % NSLOT), lane);
+        stage_page<D, KCODEC, VB>(page_blk(nis), slot_lds(nis % NSLOT), lane);
         nis++;
       }
     const int younger = max(0, min(NSLOT - 2, nis - na - 2));  // pages issued after page na + 1
@@ -883,7 +960,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     float* qs = reinterpret_cast<float*>(&ring[0][0][0] + NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4);
     float* ps = qs + 8 * D;           // [8][TQ_MAX_HOT] scores, then weights
     float* pw = ps + 8 * TQ_MAX_HOT;  // [8][D] the pages' part: sum over waves of f_w o_w
-    const TQ* qh = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
+    const int64_t qh = ((int64_t)b * a.Hq + (int64_t)h * r) * D;
     const f16* hk = static_cast<const f16*>(a.hot_k) + (((int64_t)b * a.Hkv + h) * a.hot_cap + t0) * D;
     const f16* hv = static_cast<const f16*>(a.hot_v) + (((int64_t)b * a.Hkv + h) * a.hot_cap + t0) * D;
     const float qmul2 = a.attn_scale * TQ_LOG2E;
@@ -919,7 +996,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int k = 0; k < QPT; k++) {
       const int i = tid + k * NT;
-      qx[k] = (i < 8 * D && i < r * D) ? widen(qh[i]) * qmul2 : 0.0f;
+      qx[k] = (i < 8 * D && i < r * D) ? load_q(a.q, a.q_dtype, qh + i) * qmul2 : 0.0f;
     }
     load_k(8 * wv);
     load_v(wv);
@@ -1198,44 +1275,41 @@ __global__ __launch_bounds__(256) void lpt_order_kernel(const int32_t* __restric
   for (int p = t; p < B * Hkv; p += 256) order[p] = seq_of_rank[p / Hkv] * Hkv + p % Hkv;
 }
 
-template <int D, typename TQ, int NW, bool SPV>
+template <int D, int VB, int NW, bool SPV>
 hipError_t launch_dqs(const LaunchDecode& a, hipStream_t st, unsigned grid) {
   if (a.k_codec == TQ_CODEC_FP16) {
     // fp16 keys: 8 waves; a staged page does not fit three times per wave at D = 256
     if constexpr (D <= 128) {
       constexpr int NWF = tq_decode_waves(D, TQ_CODEC_FP16);
-      hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_FP16, NWF, SPV>), dim3(grid), dim3(64 * NWF), 0, st, a);
+      hipLaunchKernelGGL((decode_fused<D, TQ_CODEC_FP16, VB, NWF, SPV>), dim3(grid), dim3(64 * NWF), 0, st, a);
     } else {
       return hipErrorInvalidValue;
     }
   } else if (a.k_codec == TQ_CODEC_LLOYDMAX) {
-    hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_LLOYDMAX, NW, SPV>), dim3(grid), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((decode_fused<D, TQ_CODEC_LLOYDMAX, VB, NW, SPV>), dim3(grid), dim3(64 * NW), 0, st, a);
   } else {
-    hipLaunchKernelGGL((decode_fused<D, TQ, TQ_CODEC_ABSMAX, NW, SPV>), dim3(grid), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((decode_fused<D, TQ_CODEC_ABSMAX, VB, NW, SPV>), dim3(grid), dim3(64 * NW), 0, st, a);
   }
   return hipGetLastError();
 }
 
-template <int D, typename TQ, int NW>
-hipError_t launch_dq(const LaunchDecode& a, hipStream_t st) {
+template <int D>
+hipError_t launch_d(const LaunchDecode& a, hipStream_t st) {
+  constexpr int NW = tq_decode_waves(D);
   if (a.order) {
     if (a.B > TQ_LPT_MAX_BATCH) return hipErrorInvalidValue;
     hipLaunchKernelGGL(lpt_order_kernel, dim3(1), dim3(256), 0, st, a.context_lens, a.B, a.Hkv, a.order);
   }
   const int U = a.B * a.Hkv;
   const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * a.splits);
-  if (a.sparse_v) return launch_dqs<D, TQ, NW, true>(a, st, grid);
-  return launch_dqs<D, TQ, NW, false>(a, st, grid);
-}
-
-template <int D>
-hipError_t launch_d(const LaunchDecode& a, hipStream_t st) {
-  constexpr int NW = tq_decode_waves(D);
-  switch (a.q_dtype) {
-    case TQ_F32: return launch_dq<D, float, NW>(a, st);
-    case TQ_BF16: return launch_dq<D, uint16_t, NW>(a, st);
-    default: return launch_dq<D, f16, NW>(a, st);
+  const int vb = tq_value_bits(a.v_codec);
+  if (a.sparse_v) {
+    if (vb != 4) return hipErrorInvalidValue;
+    return launch_dqs<D, 4, NW, true>(a, st, grid);
   }
+  if (vb == 3) return launch_dqs<D, 3, NW, false>(a, st, grid);
+  if (vb == 2) return launch_dqs<D, 2, NW, false>(a, st, grid);
+  return launch_dqs<D, 4, NW, false>(a, st, grid);
 }
 
 }  // namespace

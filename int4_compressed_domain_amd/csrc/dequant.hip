@@ -14,7 +14,9 @@ template <int D, typename TOut>
 __global__ __launch_bounds__(256) void dequant_kernel(LaunchDequant a) {
   constexpr int E = D / 16, G = D / 32;
   const bool kf16 = a.k_codec == TQ_CODEC_FP16;
-  const int BB = tq_block_bytes(D, a.k_codec);
+  const int BB = tq_block_bytes(D, a.k_codec, a.v_codec);
+  const int VB = tq_value_bits(a.v_codec);
+  const int QM = VB == 4 ? 7 : (VB == 3 ? 3 : 1);  // largest abs-max level of the values
   const int vbase = kf16 ? 32 * D : 8 * D;
   const int lane = threadIdx.x & 15;
   const int64_t vec = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(LaunchDequant a) {
 #pragma unroll
         for (int e = 0; e < 4; e++) u[e] = (w >> (4 * e)) & 15u;
       }
-    } else {
+    } else if (VB == 4) {
 #pragma unroll
       for (int k = 0; k < E / 2; k++) {
         const int c = lane * (E / 2) + k;
@@ -63,9 +65,30 @@ __global__ __launch_bounds__(256) void dequant_kernel(LaunchDequant a) {
         u[2 * k] = byte & 15u;
         u[2 * k + 1] = byte >> 4;
       }
+    } else {
+      // packed b-bit values: dim pair c = 16g + m of token tt = 4j + e is row l = 16j + m,
+      // dword g of the 4-bit layout; its low bits are in byte e of X dword l*G/2 + g/2
+      // (nibble bits 2*(g%2)), its third bits (b = 3) in byte e of Z dword (l*G + g)/4
+      // (nibble bit (l*G + g)%4)
+      constexpr int XD = G >= 2 ? G / 2 : 1;
+#pragma unroll
+      for (int k = 0; k < E / 2; k++) {
+        const int c = lane * (E / 2) + k, gg = c >> 4;
+        const int l = 16 * (tt >> 2) + (c & 15), e = tt & 3;
+        const uint32_t xb = blk[vbase + 4 * (l * XD + (gg >> 1)) + e] >> (2 * (gg & 1));
+        uint32_t lo = xb & 3u, hi = (xb >> 4) & 3u;
+        if (VB == 3) {
+          const int z = l * G + gg;
+          const uint32_t zb = blk[vbase + 128 * G + 4 * (z >> 2) + e] >> (z & 3);
+          lo |= (zb & 1u) << 2;
+          hi |= ((zb >> 4) & 1u) << 2;
+        }
+        u[2 * k] = lo;
+        u[2 * k + 1] = hi;
+      }
     }
     const int g = (lane * E) / 32;
-    const int sbase = kf16 ? 40 * D : 16 * D + (is_v ? 32 * G : 0);
+    const int sbase = (kf16 ? 32 * D : 8 * D) + 2 * VB * D + ((is_v && !kf16) ? D : 0);
     const float sc = (float)*reinterpret_cast<const f16*>(blk + sbase + 2 * (tt * G + g));
     if (!is_v && kf16) {
       // y holds the key already
@@ -74,8 +97,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(LaunchDequant a) {
 #pragma unroll
       for (int e = 0; e < E; e++) y[e] = (float)__builtin_bit_cast(f16, lb[u[e]]) * sc;
     } else {
+      const int off = is_v ? QM + 1 : 8;
 #pragma unroll
-      for (int e = 0; e < E; e++) y[e] = (float)((int)u[e] - 8) * sc;
+      for (int e = 0; e < E; e++) y[e] = (float)((int)u[e] - off) * sc;
     }
     if (a.original_basis && (is_v || !kf16)) {
 #pragma unroll

@@ -29,8 +29,10 @@ int check_layout(const tq_layout* L, bool need_pool_fields) {
   if (L->num_pages < 0) return TQ_EINVAL;
   if (L->k_codec != TQ_CODEC_ABSMAX && L->k_codec != TQ_CODEC_LLOYDMAX && L->k_codec != TQ_CODEC_FP16)
     return TQ_EINVAL;
-  if (L->v_codec == TQ_CODEC_LLOYDMAX) return TQ_EUNSUPPORTED;  // the LUT codec is for keys
-  if (L->v_codec != TQ_CODEC_ABSMAX) return TQ_EINVAL;
+  if (L->v_codec == TQ_CODEC_LLOYDMAX || L->v_codec == TQ_CODEC_FP16)
+    return TQ_EUNSUPPORTED;  // the LUT codec and fp16 are for keys
+  if (L->v_codec != TQ_CODEC_ABSMAX && L->v_codec != TQ_CODEC_ABSMAX3 && L->v_codec != TQ_CODEC_ABSMAX2)
+    return TQ_EINVAL;
   if (!L->sign_bits) return TQ_EINVAL;
   return TQ_OK;
 }
@@ -131,7 +133,7 @@ const char* tq_status_str(int status) {
 
 size_t tq_page_bytes(const tq_layout* L) {
   if (check_layout(L, true) != TQ_OK) return 0;
-  return (size_t)L->num_kv_heads * tq_block_bytes(L->head_dim, L->k_codec);
+  return (size_t)L->num_kv_heads * tq_block_bytes(L->head_dim, L->k_codec, L->v_codec);
 }
 
 int tq_kv_append(const tq_layout* L, void* pool, const void* k, const void* v, int32_t in_dtype,
@@ -143,7 +145,7 @@ int tq_kv_append(const tq_layout* L, void* pool, const void* k, const void* v, i
   if (!pool || !k || !v || !slot_mapping) return TQ_EINVAL;
   if ((int64_t)n_tokens * L->num_kv_heads * 2 > (int64_t)16 * 0x7fffffff) return TQ_EUNSUPPORTED;
   LaunchAppend a{static_cast<uint8_t*>(pool), k, v, slot_mapping, L->sign_bits,
-                 L->head_dim, L->num_kv_heads, n_tokens, in_dtype, L->k_codec};
+                 L->head_dim, L->num_kv_heads, n_tokens, in_dtype, L->k_codec, L->v_codec};
   return from_hip(tq_launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -170,6 +172,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   if (max_pages_per_seq < 0 || (int64_t)max_context_len > 16LL * max_pages_per_seq) return TQ_EINVAL;
   if ((int64_t)max_context_len > 16LL * TQ_MAX_SPLITS * TQ_MAX_SPLIT_PAGES) return TQ_EUNSUPPORTED;
   if (L->k_codec == TQ_CODEC_FP16 && L->head_dim > 128) return TQ_EUNSUPPORTED;
+  if (sparse_v && L->v_codec != TQ_CODEC_ABSMAX) return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
   if (!pool || !block_table) return TQ_EINVAL;
   Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits);
@@ -189,7 +192,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   a.part_ml = ws + (size_t)batch * L->num_q_heads * rows * L->head_dim;
   a.D = L->head_dim; a.Hq = L->num_q_heads; a.Hkv = L->num_kv_heads; a.B = batch;
   a.max_pages = max_pages_per_seq; a.max_ctx = max_context_len;
-  a.q_dtype = q_dtype; a.k_codec = L->k_codec;
+  a.q_dtype = q_dtype; a.k_codec = L->k_codec; a.v_codec = L->v_codec;
   a.splits = s.splits; a.pages_per_split = s.pages_per_split;
   a.attn_scale = attn_scale;
   a.knew = knew; a.vnew = vnew; a.new_dtype = new_dtype;
@@ -275,7 +278,7 @@ int tq_dequant_ref(const tq_layout* L, const void* pool, int32_t batch, const in
   if (!pool || !block_table || !context_lens || !k_out || !v_out) return TQ_EINVAL;
   LaunchDequant a{static_cast<const uint8_t*>(pool), block_table, context_lens, L->sign_bits,
                   k_out, v_out, L->head_dim, L->num_kv_heads, batch, max_pages_per_seq,
-                  max_context_len, to_original_basis, out_dtype, L->k_codec};
+                  max_context_len, to_original_basis, out_dtype, L->k_codec, L->v_codec};
   return from_hip(tq_launch_dequant(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -9,7 +9,7 @@ struct LaunchAppend {
   const void* v;
   const int64_t* slots;
   const uint32_t* sign_bits;
-  int D, Hkv, n_tokens, dtype, k_codec;
+  int D, Hkv, n_tokens, dtype, k_codec, v_codec;
 };
 
 // Split-K decode: pass 1 writes, per (b, q head, split), the unnormalized weighted value
@@ -25,7 +25,7 @@ struct LaunchDecode {
   float* part_o;             // [B][Hq][S][D] (= [unit][split][r][D])
   float* part_ml;            // [B][Hq][S][2]
   int* counters;             // per unit (b * Hkv + h) arrival counters, zero between calls
-  int D, Hq, Hkv, B, max_pages, max_ctx, q_dtype, k_codec;
+  int D, Hq, Hkv, B, max_pages, max_ctx, q_dtype, k_codec, v_codec;
   int splits, pages_per_split;
   float attn_scale;
   const void* knew;          // optional: K and V of each sequence's last token,
@@ -53,7 +53,7 @@ struct LaunchDequant {
   const uint32_t* sign_bits;
   void* k_out;
   void* v_out;
-  int D, Hkv, B, max_pages, max_ctx, original_basis, out_dtype, k_codec;
+  int D, Hkv, B, max_pages, max_ctx, original_basis, out_dtype, k_codec, v_codec;
 };
 hipError_t tq_launch_dequant(const LaunchDequant& a, hipStream_t st);
 
@@ -63,9 +63,11 @@ hipError_t tq_launch_dequant(const LaunchDequant& a, hipStream_t st);
 constexpr int tq_decode_waves(int D, int k_codec = TQ_CODEC_ABSMAX) {
   return (D > 128 || k_codec == TQ_CODEC_FP16) ? 8 : 16;
 }
+// Bits per value index of a value codec.
+constexpr int tq_value_bits(int v_codec) { return TQ_VALUE_BITS(v_codec); }
 // Bytes of one block (16 tokens of one kv head).
-constexpr int tq_block_bytes(int D, int k_codec) {
-  return k_codec == TQ_CODEC_FP16 ? TQ_BLOCK_BYTES_KF16(D) : TQ_BLOCK_BYTES(D);
+constexpr int tq_block_bytes(int D, int k_codec, int v_codec = TQ_CODEC_ABSMAX) {
+  return TQ_BLOCK_BYTES_KV(D, k_codec, v_codec);
 }
 constexpr int TQ_DECODE_WAVES = 4;   // dense baseline workgroups
 constexpr int TQ_MAX_SPLITS = 128;   // context splits per (sequence, kv head)

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtq.so")
 
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_ENOSPC, TQ_EDEVICE = 0, -1, -2, -3, -4
-CODEC_ABSMAX, CODEC_LLOYDMAX, CODEC_FP16 = 0, 1, 2
+CODEC_ABSMAX, CODEC_LLOYDMAX, CODEC_FP16, CODEC_ABSMAX3, CODEC_ABSMAX2 = 0, 1, 2, 3, 4
 F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("tq_status_str", "tq_page_bytes", "tq_kv_append", "tq_decode_workspace_size",

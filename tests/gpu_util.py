@@ -51,9 +51,9 @@ class Case:
         self.layout = tq.make_layout(D, w.q_heads, Hkv, self.npages, self.sb_dev.data_ptr(),
                                      w.k_codec, w.v_codec)
         self.page_bytes = tq.tq_page_bytes(self.layout)
-        assert self.page_bytes == Hkv * c_oracle.block_bytes(D, w.k_codec)
+        assert self.page_bytes == Hkv * c_oracle.block_bytes(D, w.k_codec, w.v_codec)
         self.pool = torch.zeros(self.npages * self.page_bytes, dtype=torch.uint8, device=DEV)
-        self.opool = c_oracle.new_pool(self.npages, Hkv, D, w.k_codec) if oracle else None
+        self.opool = c_oracle.new_pool(self.npages, Hkv, D, w.k_codec, w.v_codec) if oracle else None
         self.scales = W.channel_scales(w, seed)
         self.q_dtype = q_dtype or w.dtype
         q32, qst = W.queries(w, seed)

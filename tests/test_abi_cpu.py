@@ -57,6 +57,9 @@ def _append(layout, n=1, dtype=tq.BF16, pool=FAKE, k=FAKE, v=FAKE, slots=FAKE):
     (dict(num_pages=-1), tq.TQ_EINVAL),
     (dict(k_codec=5), tq.TQ_EINVAL),
     (dict(v_codec=1), tq.TQ_EUNSUPPORTED),         # the LUT codec is for keys only
+    (dict(v_codec=2), tq.TQ_EUNSUPPORTED),         # and so is fp16
+    (dict(v_codec=5), tq.TQ_EINVAL),
+    (dict(k_codec=3), tq.TQ_EINVAL),               # 3- and 2-bit codecs are for values
     (dict(sign_bits_ptr=None), tq.TQ_EINVAL),
 ])
 def test_layout_validation(kw, code):
@@ -123,6 +126,9 @@ def test_sparse_v_argument_validation():
     assert _sparse(L, q=None) == tq.TQ_EINVAL
     assert _sparse(L, wsb=16) == tq.TQ_ENOSPC
     assert _sparse(L, batch=0, q=None, out=None) == tq.TQ_OK
+    # sparse values are implemented for 4-bit values only
+    assert _sparse(_layout(v_codec=tq.CODEC_ABSMAX3)) == tq.TQ_EUNSUPPORTED
+    assert _sparse(_layout(v_codec=tq.CODEC_ABSMAX2)) == tq.TQ_EUNSUPPORTED
 
 
 def test_stream_read_probe_validation():
@@ -164,6 +170,13 @@ def test_page_bytes():
     # fp16 keys: [K fp16 32D][V indices 8D][V scales 16 x D/32 fp16]
     assert tq.tq_page_bytes(_layout(k_codec=tq.CODEC_FP16)) == 8 * (32 * 128 + 8 * 128 + 32 * 4)
     assert tq.tq_page_bytes(_layout(head_dim=64, k_codec=tq.CODEC_FP16)) == 8 * 41 * 64
+    # b-bit values: 2*b*D bytes of value indices instead of 8*D
+    for D in (64, 128, 256):
+        for vc, b in ((tq.CODEC_ABSMAX3, 3), (tq.CODEC_ABSMAX2, 2)):
+            L = _layout(head_dim=D, num_q_heads=8, num_kv_heads=8, v_codec=vc)
+            assert tq.tq_page_bytes(L) == 8 * (8 * D + 2 * b * D + 2 * D)
+            L = _layout(head_dim=D, num_q_heads=8, num_kv_heads=8, v_codec=vc, k_codec=tq.CODEC_FP16)
+            assert tq.tq_page_bytes(L) == 8 * (32 * D + 2 * b * D + D)
 
 
 def test_fp16_keys_decode_limits():

@@ -104,6 +104,28 @@ def test_fp16_keys(D, r):
         _check_case(c, num_splits=splits)
 
 
+V3, V2 = W.CODEC_ABSMAX3, W.CODEC_ABSMAX2
+
+
+@pytest.mark.parametrize("D,r,k_codec,v_codec", [(64, 4, 0, V3), (128, 8, 0, V3), (128, 8, 2, V3),
+                                                 (256, 2, 0, V3), (128, 4, 1, V2), (128, 8, 0, V2),
+                                                 (64, 2, 2, V2), (256, 4, 1, V2)])
+def test_low_bit_values(D, r, k_codec, v_codec):
+    """3-bit and 2-bit values with each key codec: packed pool bytes equal the oracle's
+    (appends of many tokens into shared pages), attention within the tolerance for edge
+    lengths and several split counts."""
+    lens = [700, 0, 1, 15, 16, 17, 260]
+    w = W.Workload("v%d_d%d_r%d_k%d" % (v_codec, D, r, k_codec), len(lens), 2 * r, 2, D, max(lens), "bf16",
+                   1.0 / math.sqrt(D), k_codec=k_codec, v_codec=v_codec, dist="lognormal_spikes")
+    _say("case low-bit values D=%d r=%d k_codec=%d v_codec=%d" % (D, r, k_codec, v_codec))
+    c = Case(w, seed=60 + D + r + k_codec + v_codec, lens=lens)
+    c.fill(chunk=300)
+    assert c.pool_equal(), "packed pool differs from the oracle"
+    for splits in (0, 1, 5):
+        out = _check_case(c, num_splits=splits)
+        assert np.all(out[1] == 0.0)
+
+
 def _sparse_gpu(c, thr, num_splits=0):
     w = c.w
     max_ctx = int(c.lens.max())
@@ -148,9 +170,9 @@ def test_sparse_values(name, k_codec):
             assert sk > 0, "spiky attention should let value pages be skipped"
 
 
-def _hot_cold_case(D, r, k_codec, cold, hot, cap, splits_list, seed):
+def _hot_cold_case(D, r, k_codec, cold, hot, cap, splits_list, seed, v_codec=0):
     w = W.Workload("hc_d%d_r%d_k%d" % (D, r, k_codec), len(cold), 2 * r, 2, D, max(max(cold), 1), "bf16",
-                   1.0 / math.sqrt(D), k_codec=k_codec, dist="lognormal_spikes")
+                   1.0 / math.sqrt(D), k_codec=k_codec, v_codec=v_codec, dist="lognormal_spikes")
     _say("case hot/cold D", D, "r", r, "k_codec", k_codec, "tail capacity", cap)
     c = Case(w, seed=seed, lens=cold)
     c.fill()
@@ -184,14 +206,14 @@ def _hot_cold_case(D, r, k_codec, cold, hot, cap, splits_list, seed):
     return outs
 
 
-@pytest.mark.parametrize("D,r,k_codec", [(128, 8, 0), (128, 4, 1), (128, 8, 2), (64, 2, 2),
-                                         (256, 2, 0)])
-def test_hot_cold(D, r, k_codec):
+@pytest.mark.parametrize("D,r,k_codec,v_codec", [(128, 8, 0, 0), (128, 4, 1, 0), (128, 8, 2, 0),
+                                                 (64, 2, 2, 0), (256, 2, 0, 0), (128, 8, 2, V3)])
+def test_hot_cold(D, r, k_codec, v_codec):
     """Hot/cold cache: older tokens in the pool, the most recent in an fp16 tail, one softmax;
     against the oracle for several split counts, with empty pools, empty and full tails, and
     a sequence with no tokens at all."""
     outs = _hot_cold_case(D, r, k_codec, [0, 1, 40, 300, 1000, 0], [5, 0, 64, 17, 1, 0], 64,
-                          (0, 1, 3), 90 + D + r + k_codec)
+                          (0, 1, 3), 90 + D + r + k_codec, v_codec)
     for o in outs:
         assert np.all(o[-1] == 0.0)
 
@@ -301,11 +323,11 @@ def test_negative_slots_and_untouched_bytes():
     assert c.pool_equal()
 
 
-@pytest.mark.parametrize("k_codec", [0, 1, 2])
+@pytest.mark.parametrize("k_codec,v_codec", [(0, 0), (1, 0), (2, 0), (0, V3), (2, V3), (1, V2)])
 @pytest.mark.parametrize("basis", [0, 1])
-def test_dequant_reference(k_codec, basis):
+def test_dequant_reference(k_codec, v_codec, basis):
     lens = [37, 0, 64]
-    w = W.Workload("dq", 3, 8, 2, 128, 64, "bf16", 0.1, k_codec=k_codec)
+    w = W.Workload("dq", 3, 8, 2, 128, 64, "bf16", 0.1, k_codec=k_codec, v_codec=v_codec)
     c = Case(w, seed=13, lens=lens)
     c.fill()
     Lmax = 64
@@ -314,7 +336,7 @@ def test_dequant_reference(k_codec, basis):
         vo = torch.full_like(ko, 7.0)
         tq.tq_dequant_ref(c.layout, c.pool, c.bt_dev, c.lens_dev, Lmax, ko, vo, to_original_basis=basis)
         torch.cuda.synchronize()
-        rk, rv = c_oracle.dequant(c.opool, 128, 2, c.sb, c.bt, c.lens, Lmax, basis, k_codec, 0)
+        rk, rv = c_oracle.dequant(c.opool, 128, 2, c.sb, c.bt, c.lens, Lmax, basis, k_codec, v_codec)
         if dt == torch.float16:
             rk, rv = rk.astype(np.float16), rv.astype(np.float16)
         assert np.array_equal(ko.cpu().numpy(), rk)
@@ -358,7 +380,8 @@ def _pairs(w, lens, n=12, seed=0):
 
 
 @pytest.mark.parametrize("name", ["single_head_1k", "llama8b_b16_8k", "llama70b_b1_128k",
-                                  "gemma_d256_32k", "mixed_serving", "llama70b_b1_128k_k16v4"])
+                                  "gemma_d256_32k", "mixed_serving", "llama70b_b1_128k_k16v4",
+                                  "llama70b_b1_128k_k16v3", "llama70b_b1_128k_k4v2"])
 def test_full_size_workloads(name):
     w = W.WORKLOADS[name]
     _say("case full-size", name)
@@ -375,15 +398,19 @@ def test_full_size_workloads(name):
     _check_case(c, pairs=pairs)
 
 
-@pytest.mark.parametrize("D,r,k_codec,dtype", [(128, 8, 0, "bf16"), (128, 4, 1, "bf16"),
-                                               (64, 2, 0, "f32"), (256, 2, 0, "bf16"),
-                                               (128, 8, 2, "bf16"), (64, 4, 2, "f32")])
-def test_append_decode_equals_append_then_decode(D, r, k_codec, dtype):
+@pytest.mark.parametrize("D,r,k_codec,dtype,v_codec", [(128, 8, 0, "bf16", 0), (128, 4, 1, "bf16", 0),
+                                                       (64, 2, 0, "f32", 0), (256, 2, 0, "bf16", 0),
+                                                       (128, 8, 2, "bf16", 0), (64, 4, 2, "f32", 0),
+                                                       (128, 8, 2, "bf16", V3), (128, 8, 0, "bf16", V2),
+                                                       (64, 4, 2, "f32", V3), (256, 2, 0, "bf16", V3),
+                                                       (64, 2, 1, "bf16", V2)])
+def test_append_decode_equals_append_then_decode(D, r, k_codec, dtype, v_codec):
     """The fused entry point writes the same pool bytes as tq_kv_append of each sequence's
     last token and returns the same output, bit for bit, as tq_decode_attn afterwards."""
     lens = [0, 1, 15, 16, 17, 33, 250, 1000]
-    w = W.Workload("appdec", len(lens), 2 * r, 2, D, max(lens), dtype, 0.125, k_codec=k_codec)
-    _say("case append+decode D", D, "r", r, "k_codec", k_codec, dtype)
+    w = W.Workload("appdec", len(lens), 2 * r, 2, D, max(lens), dtype, 0.125, k_codec=k_codec,
+                   v_codec=v_codec)
+    _say("case append+decode D", D, "r", r, "k_codec", k_codec, dtype, "v_codec", v_codec)
     fused = Case(w, seed=31, lens=lens)
     split = Case(w, seed=31, lens=lens, oracle=False)
     for c in (fused, split):  # every token but the last
