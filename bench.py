@@ -357,7 +357,7 @@ def cpu_baseline(w):
     while nseq < w.batch and int(np.sum(lens[:nseq + 1])) * Hkv <= budget:
         nseq += 1
     nseq = max(nseq, 1)
-    opool = c_oracle.new_pool(npages, Hkv, D, w.k_codec)
+    opool = c_oracle.new_pool(npages, Hkv, D, w.k_codec, w.v_codec)
     scales = W.channel_scales(w, 0)
     for b in range(nseq):
         k32, v32, _, _ = W.seq_tokens(w, b, int(lens[b]), 0, scales)
@@ -406,7 +406,7 @@ def main():
         "config": {"workload": name, "batch": w.batch, "q_heads": w.q_heads,
                    "kv_heads": w.kv_heads, "head_dim": w.head_dim, "context": w.context,
                    "ragged_min": w.ragged_min, "prefill": w.prefill, "page": 16, "group": 32,
-                   "k_codec": ["absmax", "lloydmax", "fp16"][w.k_codec], "v_codec": "absmax",
+                   "k_codec": ["absmax", "lloydmax", "fp16"][w.k_codec], "v_codec": {W.CODEC_ABSMAX: "absmax", W.CODEC_ABSMAX3: "absmax3", W.CODEC_ABSMAX2: "absmax2"}[w.v_codec],
                    "kv_input": w.dtype, "attn_scale": w.attn_scale, "splits": args.splits},
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
         "decode_us": round(dec_mean, 3), "prefill_append_us": round(pre_mean, 3),
