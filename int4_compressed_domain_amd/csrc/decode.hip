@@ -284,21 +284,27 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int L = a.context_lens[b];
   const int npages = (L + 15) >> 4;
   const int pps = a.pages_per_split;
-  // Hot/cold: an fp16 tail of Lh recent tokens besides the pool's L. Every split of the
-  // unit takes an equal slice [t0, t1) of it after its pages; a unit with a tail and no
-  // pool tokens has one split, holding the whole tail.
+  // Hot/cold: an fp16 tail of Lh recent tokens besides the pool's L. Either every split of
+  // the unit takes an equal slice [t0, t0 + tsl) of it after its pages (a unit with a tail
+  // and no pool tokens has one split, holding the whole tail), or (a.hot_wg, when the grid
+  // has room for it) one more workgroup per unit, split index a.splits, takes the whole
+  // tail and no pages and publishes partial row ns_cold.
   const int Lh = a.hot_k ? min(max(a.hot_lens[b], 0), a.hot_cap) : 0;
   const int ns_cold = (npages + pps - 1) / pps;
-  const int ns = ns_cold > 0 ? ns_cold : (Lh > 0 ? 1 : 0);  // partials merged for this unit
+  const bool hotwg = a.hot_wg && s == a.splits;
+  const int ns = a.hot_wg ? ns_cold + (Lh > 0 ? 1 : 0)
+                          : (ns_cold > 0 ? ns_cold : (Lh > 0 ? 1 : 0));  // partials merged for this unit
   float* outp = a.out + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
   if (ns == 0) {  // empty sequence: zero output, written by split 0
     if (s == 0)
       for (int i = tid; i < r * D; i += NT) outp[i] = 0.0f;
     return;
   }
-  if (s >= ns) return;
-  const int p0 = s * pps, p1 = min(p0 + pps, npages);
-  const int t0 = (int)((int64_t)Lh * s / ns), tsl = (int)((int64_t)Lh * (s + 1) / ns) - t0;
+  if (hotwg ? Lh == 0 : s >= (a.hot_wg ? ns_cold : ns)) return;
+  const int srow = hotwg ? ns_cold : s;  // this workgroup's partial row
+  const int p0 = hotwg ? 0 : s * pps, p1 = hotwg ? 0 : min(p0 + pps, npages);
+  const int t0 = a.hot_wg ? 0 : (int)((int64_t)Lh * s / ns);
+  const int tsl = a.hot_wg ? (hotwg ? Lh : 0) : (int)((int64_t)Lh * (s + 1) / ns) - t0;
 
   // page ring (per wave) -- reused after the page loop as the merge area
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT][NW][C::SLOT];
@@ -357,7 +363,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // that token's bytes valid); wave wl, which owns the last page, patches its staged copy
   // before computing it; wave wc stores the token to the pool after the page loop.
   constexpr int E = CodecCfg<D>::E;
-  const bool app = !SPV && (a.knew != nullptr) && (s == ns_cold - 1);
+  const bool app = !SPV && !hotwg && (a.knew != nullptr) && (s == ns_cold - 1);
   const int plast = npages - 1, tnew = (L - 1) & 15;
   const int wc = NW - 1, wl = (plast - p0) % NW;
   float ynew[E];
@@ -1016,13 +1022,16 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
     __syncthreads();
     for (int tb = 8 * wv; tb < tsl; tb += 8 * NW) {
-      if (tb != 8 * wv) load_k(tb);
+      f16x8 kc[KP];  // this pass's keys; the next pass's are loaded meanwhile
+#pragma unroll
+      for (int i = 0; i < KP; i++) kc[i] = kp[i];
+      if (tb + 8 * NW < tsl) load_k(tb + 8 * NW);
       float dot[8] = {};
 #pragma unroll
       for (int i = 0; i < KP; i++)
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          const float kx = (float)kp[i][e];
+          const float kx = (float)kc[i][e];
           const int d = sg * (D / 8) + 8 * i + e;
 #pragma unroll
           for (int hd = 0; hd < 8; hd++) dot[hd] = __builtin_fmaf(qs[hd * D + d], kx, dot[hd]);
@@ -1059,7 +1068,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       float acc[8][4] = {};
       const int nrow = (tsl + TPW - 1) / TPW;
       for (int n0 = wv; n0 < nrow; n0 += NW * HB) {
-        if (n0 != wv) load_v(n0);
+        f16x4 vc[HB];  // this batch's values; the next batch's are loaded meanwhile
+#pragma unroll
+        for (int k = 0; k < HB; k++) vc[k] = v4[k];
+        if (n0 + NW * HB < nrow) load_v(n0 + NW * HB);
 #pragma unroll
         for (int k = 0; k < HB; k++) {
           const int t = (n0 + k * NW) * TPW + j;
@@ -1068,7 +1080,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
             for (int hd = 0; hd < 8; hd++) {
               const float p = hd < r ? ps[hd * TQ_MAX_HOT + t] : 0.0f;
 #pragma unroll
-              for (int e = 0; e < 4; e++) acc[hd][e] = __builtin_fmaf(p, (float)v4[k][e], acc[hd][e]);
+              for (int e = 0; e < 4; e++) acc[hd][e] = __builtin_fmaf(p, (float)vc[k][e], acc[hd][e]);
             }
           }
         }
@@ -1119,8 +1131,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // fin: [ngf][r][D] partial sums of the result (rotated basis), summed by the rotation below
   float* fin = &mo[0][0][0];
   int ngf = 1;
-  const int S = a.splits;  // partial rows per unit
-  const int64_t prow = ((int64_t)u * S + s) * r;  // partial rows of this (unit, split)
+  const int S = a.splits + a.hot_wg;  // partial rows per unit
+  const int64_t prow = ((int64_t)u * S + srow) * r;  // partial rows of this (unit, split)
   if (ns == 1) {
     float ov[(8 * D + NT - 1) / NT];
 #pragma unroll
@@ -1301,7 +1313,7 @@ hipError_t launch_d(const LaunchDecode& a, hipStream_t st) {
     hipLaunchKernelGGL(lpt_order_kernel, dim3(1), dim3(256), 0, st, a.context_lens, a.B, a.Hkv, a.order);
   }
   const int U = a.B * a.Hkv;
-  const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * a.splits);
+  const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * (a.splits + a.hot_wg));
   const int vb = tq_value_bits(a.v_codec);
   if (a.sparse_v) {
     if (vb != 4) return hipErrorInvalidValue;

@@ -176,6 +176,19 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   if (batch == 0) return TQ_OK;
   if (!pool || !block_table) return TQ_EINVAL;
   Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits);
+  const int64_t resident = (int64_t)num_cus() * (L->head_dim >= 256 ? 2 : 1);
+  // fp16 tail: with automatic splits, at least 8 of them per unit, a grid that fits the chip
+  // and a tail of at most 256 tokens, one split is given up for a workgroup per unit that
+  // takes the whole tail and runs beside the pool's (its cost then hides behind theirs; a
+  // longer tail on one compute unit would outlast them); otherwise every split takes a
+  // slice of the tail after its pages.
+  int hot_wg = 0;
+  if (hot_k && num_splits == 0 && hot_cap <= 256 && s.splits >= 8 &&
+      (int64_t)batch * L->num_kv_heads * s.splits <= resident &&
+      (int64_t)(s.splits - 1) * TQ_MAX_SPLIT_PAGES >= (max_context_len + 15) / 16) {
+    s = make_split((max_context_len + 15) / 16, s.splits - 1);
+    hot_wg = 1;
+  }
   if (workspace_bytes_ < workspace_bytes(L, batch, max_context_len, num_splits)) return TQ_ENOSPC;
   if (!workspace) return TQ_EINVAL;
   float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + TQ_DECODE_COUNTER_BYTES);
@@ -187,7 +200,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   a.context_lens = context_lens;
   a.sign_bits = L->sign_bits;
   a.out = out;
-  const int rows = s.splits;  // partial rows per unit
+  const int rows = s.splits + hot_wg;  // partial rows per unit
   a.part_o = ws;
   a.part_ml = ws + (size_t)batch * L->num_q_heads * rows * L->head_dim;
   a.D = L->head_dim; a.Hq = L->num_q_heads; a.Hkv = L->num_kv_heads; a.B = batch;
@@ -197,9 +210,8 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   a.attn_scale = attn_scale;
   a.knew = knew; a.vnew = vnew; a.new_dtype = new_dtype;
   a.sparse_v = sparse_v; a.v_thr = v_thr; a.v_skipped = v_skipped;
-  a.hot_k = hot_k; a.hot_v = hot_v; a.hot_lens = hot_lens; a.hot_cap = hot_cap;
+  a.hot_k = hot_k; a.hot_v = hot_v; a.hot_lens = hot_lens; a.hot_cap = hot_cap; a.hot_wg = hot_wg;
   // longest-first order pays when the workgroups do not all fit on the chip at once
-  const int64_t resident = (int64_t)num_cus() * (L->head_dim >= 256 ? 2 : 1);
   if (batch > 1 && batch <= TQ_LPT_MAX_BATCH && (int64_t)batch * L->num_kv_heads * s.splits > resident)
     a.order = reinterpret_cast<int32_t*>(
         a.part_ml + (size_t)batch * L->num_q_heads * rows * 2);

@@ -39,6 +39,7 @@ struct LaunchDecode {
   const void* hot_v;         //   hot_lens[b] tokens attended after the pool's context_lens[b]
   const int32_t* hot_lens;
   int hot_cap;
+  int hot_wg;                // 1: split index `splits` of each unit takes the whole tail
 };
 
 hipError_t tq_launch_append(const LaunchAppend& a, hipStream_t st);

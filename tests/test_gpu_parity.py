@@ -170,8 +170,8 @@ def test_sparse_values(name, k_codec):
             assert sk > 0, "spiky attention should let value pages be skipped"
 
 
-def _hot_cold_case(D, r, k_codec, cold, hot, cap, splits_list, seed, v_codec=0):
-    w = W.Workload("hc_d%d_r%d_k%d" % (D, r, k_codec), len(cold), 2 * r, 2, D, max(max(cold), 1), "bf16",
+def _hot_cold_case(D, r, k_codec, cold, hot, cap, splits_list, seed, v_codec=0, kv=2):
+    w = W.Workload("hc_d%d_r%d_k%d" % (D, r, k_codec), len(cold), kv * r, kv, D, max(max(cold), 1), "bf16",
                    1.0 / math.sqrt(D), k_codec=k_codec, v_codec=v_codec, dist="lognormal_spikes")
     _say("case hot/cold D", D, "r", r, "k_codec", k_codec, "tail capacity", cap)
     c = Case(w, seed=seed, lens=cold)
@@ -216,6 +216,17 @@ def test_hot_cold(D, r, k_codec, v_codec):
                           (0, 1, 3), 90 + D + r + k_codec, v_codec)
     for o in outs:
         assert np.all(o[-1] == 0.0)
+
+
+@pytest.mark.parametrize("D,kv", [(128, 2), (256, 4), (64, 1)])
+def test_hot_cold_tail_workgroup(D, kv):
+    """Few long sequences with automatic splits: the tail gets a workgroup of its own per
+    (sequence, kv head) beside the pool's splits (one split fewer); checked against the
+    oracle with long, short and empty tails and pools."""
+    cold = [8000, 0, 6000, 100]
+    hot = [200, 256, 0, 17]
+    w_outs = _hot_cold_case(D, 4, 0, cold, hot, 256, (0,), 400 + D, kv=kv)
+    assert np.all(np.isfinite(w_outs[0]))
 
 
 @pytest.mark.parametrize("D,r", [(64, 8), (128, 8), (256, 4)])
