@@ -204,12 +204,16 @@ int tq_append_decode_attn(const tq_layout* layout, void* pool, const void* k_las
  * 16-token page (of one kv head) are neither loaded nor used when every weight of it, for
  * every q head of the kv head, is below v_threshold (mlxcel "TurboQuant KV cache" manual,
  * sparse-V threshold: value dequantization is skipped where the attention weight is below
- * it, 1e-6 by default). The weight compared is exp(score - running max) when the page is
- * scored, which bounds the token's final softmax weight from above; so the result differs
- * from tq_decode_attn only by dropped terms w_t * v_t with every w_t < v_threshold (the
- * softmax normalizer still counts every token). Which pages are dropped depends on the
- * split count; v_threshold = 0 drops none and gives tq_decode_attn's result bit for bit.
- *   v_threshold     in [0, 1), TQ_EINVAL otherwise
+ * it, 1e-6 by default). Each context split first reads the keys of all its pages, then
+ * the keys and values of the pages it keeps. The weight compared is exp(score - M), M the
+ * largest score of the split, which bounds the token's final softmax weight from above; so
+ * the result differs from tq_decode_attn only by dropped terms w_t * v_t with every
+ * w_t < v_threshold (the softmax normalizer still counts every token). Which pages are
+ * dropped depends on the split count; v_threshold = 0 drops none and is tq_decode_attn,
+ * bit for bit. Keys are read twice for kept pages: this pays where attention is peaky.
+ * The split count is at least the context's pages / (32 * waves per workgroup), which
+ * tq_decode_workspace_size includes.
+ *   v_threshold     in [0, 1), TQ_EINVAL otherwise; 4-bit values only (TQ_EUNSUPPORTED)
  *   v_pages_skipped optional device uint64: the number of (page, kv head) value blocks
  *                   skipped is added to it (NULL: not counted)
  *   other arguments, workspace and errors as tq_decode_attn.

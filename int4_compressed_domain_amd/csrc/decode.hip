@@ -64,6 +64,10 @@ struct Cfg {
   static constexpr int SLOT = SOFF + SCB;             // LDS bytes of one staged page
   static constexpr int BV = KF16 ? 32 * D : 8 * D;    // block offsets of the V indices
   static constexpr int BS = BV + VR;                  //   and of the scales
+  // sparse values, first pass: a page's keys alone ([K indices][K scales], KH bytes) fit
+  // half a slot with 4-bit keys, so that pass streams two pages per slot
+  static constexpr int KH = KREG + 32 * G;
+  static constexpr bool HS = !KF16 && KH <= SLOT / 2 && (SLOT / 2) % 16 == 0;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -117,16 +121,31 @@ __device__ __forceinline__ void stage_page(const uint8_t* blk, uint32_t base, in
     if (c * 64 + lane < C::SCB / 4) dma4(r, 4 * (c * 64 + lane), (uint32_t)C::BS, base + C::SOFF + 256 * c);
 }
 
-// Sparse values: the key part of a page ([K][K scales]) and its value part ([V indices][V
-// scales]) staged separately, into the same slot layout as stage_page.
+// Sparse values, first pass: the key part of a page ([K][K scales]) alone, into the same slot
+// layout as stage_page.
 template <int D, int KC>
 struct SplitDma {
   using C = Cfg<D, KC>;
   static constexpr int NSK = C::KF16 ? 0 : (8 * C::G + 63) / 64;  // dword DMAs, K scales
-  static constexpr int NSV = (8 * C::G + 63) / 64;                // dword DMAs, V scales
   static constexpr int NK_OPS = (C::KF16 ? C::G : C::NK) + NSK;
-  static constexpr int NV_OPS = C::NK + NSV;
 };
+
+// The same, compact: K scales right after the K indices (a half slot, see Cfg::HS).
+template <int D, int KC>
+__device__ __forceinline__ void stage_kc(const uint8_t* blk, uint32_t base, int lane) {
+  using C = Cfg<D, KC>;
+  static_assert(C::HS, "compact key staging needs 4-bit keys");
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
+  const uint32_t lo = (uint32_t)lane * C::KB;
+#pragma unroll
+  for (int c = 0; c < C::NK; c++) {
+    if constexpr (C::DMAK == 16) dma16(r, lo + c * 16, 0u, base + c * 1024);
+    else dma4(r, lo + c * 4, 0u, base + c * 256);
+  }
+#pragma unroll
+  for (int c = 0; c < SplitDma<D, KC>::NSK; c++)
+    if (c * 64 + lane < 8 * C::G) dma4(r, 4 * (c * 64 + lane), (uint32_t)C::BS, base + C::KREG + 256 * c);
+}
 
 template <int D, int KC>
 __device__ __forceinline__ void stage_k(const uint8_t* blk, uint32_t base, int lane) {
@@ -146,23 +165,6 @@ __device__ __forceinline__ void stage_k(const uint8_t* blk, uint32_t base, int l
     for (int c = 0; c < SplitDma<D, KC>::NSK; c++)
       if (c * 64 + lane < 8 * C::G) dma4(r, 4 * (c * 64 + lane), (uint32_t)C::BS, base + C::SOFF + 256 * c);
   }
-}
-
-template <int D, int KC>
-__device__ __forceinline__ void stage_v(const uint8_t* blk, uint32_t base, int lane) {
-  using C = Cfg<D, KC>;
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
-  const uint32_t lo = (uint32_t)lane * C::KB;
-#pragma unroll
-  for (int c = 0; c < C::NK; c++) {
-    if constexpr (C::DMAK == 16) dma16(r, lo + c * 16, (uint32_t)C::BV, base + C::VOFF + c * 1024);
-    else dma4(r, lo + c * 4, (uint32_t)C::BV, base + C::VOFF + c * 256);
-  }
-  constexpr int VS = C::KF16 ? 0 : 32 * C::G;  // V scales after the K scales (4-bit keys)
-#pragma unroll
-  for (int c = 0; c < SplitDma<D, KC>::NSV; c++)
-    if (c * 64 + lane < 8 * C::G)
-      dma4(r, 4 * (c * 64 + lane), (uint32_t)(C::BS + VS), base + C::SOFF + VS + 256 * c);
 }
 
 // s_waitcnt vmcnt(n * per), n = 0..4 (wave-uniform): every load but the last n*per done.
@@ -314,8 +316,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   __shared__ float hml[8][2];                  // per head: max M and sum l of the workgroup
   __shared__ int last_flag;
   __shared__ int lead_n;                       // furthest page-loop step reached by a wave
-  __shared__ float smax[8];                    // sparse values: per head, the largest raw score
-                                               // any wave of the workgroup has seen
+  __shared__ int wskip;                        // sparse values: pages skipped by the workgroup
   __shared__ uint32_t sgn_s[D / 32];           // sigma bits, read once for the final un-rotation
   static_assert(NW >= 8, "one wave per query head in the rotations");
   // Aliases of the ring: the query operands live in the last slot of every wave until the
@@ -394,12 +395,26 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   __syncthreads();
   // start streaming this wave's first pages; they land while the queries are prepared
   // (the rotating waves issue theirs after the rotation, which stays off the busy queue)
+  // sparse values, first pass: NR ring entries per wave, half slots with 4-bit keys
+  constexpr int NR = C::HS ? 2 * NSLOT : NSLOT;
+  auto k_lds = [&](int n) {  // LDS byte address of the first pass's entry for page n
+    if constexpr (C::HS) return slot_lds((n % NR) >> 1) + (uint32_t)(((n % NR) & 1) * (C::SLOT / 2));
+    else return slot_lds(n % NSLOT);
+  };
+  auto k_slot = [&](int n) -> const uint8_t* {
+    if constexpr (C::HS) return &ring[(n % NR) >> 1][wv][((n % NR) & 1) * (C::SLOT / 2)];
+    else return ring[n % NSLOT][wv];
+  };
+  auto stage_keys = [&](int n) {
+    if constexpr (C::HS) stage_kc<D, KCODEC>(page_blk(n), k_lds(n), lane);
+    else stage_k<D, KCODEC>(page_blk(n), k_lds(n), lane);
+  };
   auto stage_first = [&]() {
 #pragma unroll
     for (int k = 0; k < 2; k++) {
       const int pp = p0 + wv + k * NW;
       if (pp < p1) {
-        if constexpr (SPV) stage_k<D, KCODEC>(page_blk(k), slot_lds(k), lane);
+        if constexpr (SPV) stage_keys(k);
         else stage_page<D, KCODEC, VB>(page_blk(k), slot_lds(k), lane);
       }
     }
@@ -416,7 +431,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       place_vector<D, KF16, VB>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
     }
   }
-  if (wv >= r) stage_first();
+  stage_first();  // (the query operands go to the last slot, which these loads do not use)
 
   // ---- prologue: rotate, scale, power-of-two prescale per head ----------------------------
   // Wave w (< r) holds query head w: after the butterflies and scaling it writes the fp16
@@ -450,10 +465,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
     // scores come out in units of 2^-sh (times 2^24 for the subnormal K form)
     if (lane == 0) qdown[wv] = ldexpf(1.0f, KSUB ? 24 - sh : -sh);
-    stage_first();
   }
-  if (tid == 0) lead_n = 0;
-  if (tid < 8) smax[tid] = -INFINITY;
+  if (tid == 0) {
+    lead_n = 0;
+    wskip = 0;
+  }
   __syncthreads();
   const bool live = hl < r;
   const bool hiLane = hr < 8;  // lanes 0..7 of a row finish page A of each step, 8..15 page B
@@ -558,8 +574,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       }
     }
   };
-  auto load_scales = [&](const uint8_t* slot, uint32_t (&st)[2 * G], int region) {  // 0: K, 1: V
-    const uint32_t* sw = reinterpret_cast<const uint32_t*>(slot + C::SOFF);
+  auto load_scales = [&](const uint8_t* slot, uint32_t (&st)[2 * G], int region,
+                         int soff = C::SOFF) {  // region 0: K, 1: V
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(slot + soff);
     const int roff = KF16 ? 0 : region * 8 * G;  // fp16 keys: only V scales are staged
 #pragma unroll
     for (int i = 0; i < 2 * G; i += 4) {  // fp16 pairs: tokens 4jq..4jq+3, groups 0..G-1
@@ -575,7 +592,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     return (float)as_h2(st[(e * G + g) >> 1])[(e * G + g) & 1];
   };
   // one page's partial scores in every lane (column hr: hi or lo part)
-  auto scores = [&](const uint8_t* slot, float (&sc)[4]) {
+  auto scores = [&](const uint8_t* slot, float (&sc)[4], int kso = C::SOFF) {  // kso: K scales
     if constexpr (KF16) {  // fp16 keys are the A operand as staged; one accumulator
       f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -588,7 +605,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
     uint32_t kw[G], kst[2 * G];
     load_idx(slot, kw, 0);
-    load_scales(slot, kst, 0);
+    load_scales(slot, kst, 0, kso);
 #pragma unroll
     for (int e = 0; e < 4; e++) sc[e] = 0.0f;
 #pragma unroll
@@ -667,66 +684,20 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     }
   };
 
-  // ---- sparse values: a page's values are loaded only when some weight of it can reach
-  // the threshold. p is relative to the running max when the page is scored, and the final
-  // weight exp(s - m_final) / l is never larger (m_final >= m, l >= 1), so a skipped page's
-  // tokens all have final weights below the threshold. The values of a step's pages are
-  // folded in at the next step, before that step may raise the running max: the order of
-  // the accumulator updates is the same as in the dense loop.
-  float ppr[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // previous step: this lane's p
-  int pneed = 0;                            // bit 0: page A's values loaded, bit 1: page B's
-  int ppa = 0, pna = 0;                     // previous step: page A, and its wave page number
-  int nskip = 0;                            // pages of this wave whose values were skipped
-  auto pv_prev = [&]() {
-    const uint8_t* sA = ring[pna % NSLOT][wv];
-    const uint8_t* sB = ring[(pna + 1) % NSLOT][wv];
-    uint32_t vst[2 * G];
-    if ((hiLane ? (pneed & 1) : (pneed & 2)) != 0) {
-      load_scales(hiLane ? sA : sB, vst, 1);
-    } else {
+  // ---- sparse values, pass 1: keys only. The running max and sum of every token are kept
+  // as in the dense loop (no values), and each page's largest score per head goes to pmreg:
+  // entry 8n + h (wave page n, head h) in lane (8n + h) % 64 of register n / 8, which after
+  // the reductions below is lane 16 ((n / 2) % 4) + hr of the step that scores page n.
+  constexpr int NPM = TQ_SPARSE_PAGES_PER_WAVE / 8;  // registers of page maxima
+  float pmreg[NPM];
 #pragma unroll
-      for (int i = 0; i < 2 * G; i++) vst[i] = 0u;
-    }
-    const int pb = ppa + NW;
-    if (ppa == ptail || pb == ptail || pb >= p1) {  // wave-uniform: a partial or missing page
-      const int pm = hiLane ? ppa : pb;
-      const int lim = (pm >= p1) ? 0 : (pm == ptail ? ltail : 16);
-#pragma unroll
-      for (int e = 0; e < 4; e++)
-        if (4 * jq + e >= lim) {
-#pragma unroll
-          for (int g = 0; g < G; g += 2) vst[(e * G + g) >> 1] = 0u;  // slot may hold garbage
-        }
-    }
-    uint32_t vwA[G], vwB[G];
-#pragma unroll
-    for (int g = 0; g < G; g++) vwA[g] = vwB[g] = 0u;
-    if (pneed & 1) load_idx(sA, vwA, 1);
-    if (pneed & 2) load_idx(sB, vwB, 1);
-    auto vsc = [&](int e, int g) { return (float)as_h2(vst[(e * G + g) >> 1])[(e * G + g) & 1]; };
-#pragma unroll
-    for (int g = 0; g < G; g++) {
-      const f16x4 own = {(f16)__builtin_fmaf(ppr[0], vsc(0, g), 0.0f), (f16)__builtin_fmaf(ppr[2], vsc(2, g), 0.0f),
-                         (f16)__builtin_fmaf(ppr[1], vsc(1, g), 0.0f), (f16)__builtin_fmaf(ppr[3], vsc(3, g), 0.0f)};
-      const u32x2 o2 = __builtin_bit_cast(u32x2, own);
-      const uint32_t x0 = __builtin_amdgcn_mov_dpp(o2[0], 0x128, 0xf, 0xf, true);
-      const uint32_t x1 = __builtin_amdgcn_mov_dpp(o2[1], 0x128, 0xf, 0xf, true);
-      const f16x8 P = __builtin_bit_cast(f16x8, u32x4{o2[0], o2[1], x0, x1});
-      const uint32_t a0 = vwA[g], a8 = a0 >> 8, bw = vwB[g], b8 = bw >> 8;
-      const f16x8 Ae = __builtin_bit_cast(f16x8, u32x4{a0 & 0x000F000Fu, a8 & 0x000F000Fu, bw & 0x000F000Fu, b8 & 0x000F000Fu});
-      const f16x8 Ao = __builtin_bit_cast(f16x8, u32x4{a0 & 0x00F000F0u, a8 & 0x00F000F0u, bw & 0x00F000F0u, b8 & 0x00F000F0u});
-      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, P, acc[2 * g], 0, 0, 0);
-      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ceven, P, acc[2 * g], 0, 0, 0);
-      acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, P, acc[2 * g + 1], 0, 0, 0);
-      acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codd, P, acc[2 * g + 1], 0, 0, 0);
-    }
-  };
-  const float vthr = a.v_thr;
-  float msh = -INFINITY;  // after the first step: the workgroup's largest score for this head
-  auto sstep = [&](int na_, const uint8_t* slotA, const uint8_t* slotB, int pa, int pb) {
+  for (int k = 0; k < NPM; k++) pmreg[k] = -INFINITY;
+  int nskip = 0;  // pages of this wave whose values were skipped
+  auto kstep = [&](int na_, const uint8_t* slotA, const uint8_t* slotB, int pa, int pb) {
     float sc[4], sA[4], sB[4];
-    scores(slotA, sA);
-    scores(slotB, sB);
+    constexpr int kso = C::HS ? C::KREG : C::SOFF;  // where the first pass put the K scales
+    scores(slotA, sA, kso);
+    scores(slotB, sB, kso);
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       const float own = hiLane ? sA[e] : sB[e];
@@ -740,45 +711,22 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       for (int e = 0; e < 4; e++)
         if (4 * jq + e >= lim) sc[e] = -INFINITY;
     }
-    float cm = vmax3(sc[0], sc[1], vmax(sc[2], sc[3]));
-    cm = max_xor16(cm);
-    cm = max_xor32(cm);
-    cm = vmax(cm, dpp_ror8(cm));
-    if (pneed) pv_prev();  // the previous pages, at the running max they were weighted with
+    float pmx = vmax3(sc[0], sc[1], vmax(sc[2], sc[3]));
+    pmx = max_xor16(pmx);
+    pmx = max_xor32(pmx);  // this lane's page (A if hiLane), head hl: its largest score
+    const int kreg = na_ >> 3, kq = (na_ >> 1) & 3;
+#pragma unroll
+    for (int k = 0; k < NPM; k++)
+      if (k == kreg && jq == kq) pmreg[k] = pmx;
+    const float cm = vmax(pmx, dpp_ror8(pmx));  // both pages
     if (__any(cm > m_run)) {
       const float mn = fmaxf(m_run, cm);
-      const float f = __builtin_amdgcn_exp2f((m_run - mn) * down);
-      l_run *= f;
-#pragma unroll
-      for (int t = 0; t < 2 * G; t++) acc[t] *= f;
+      l_run *= __builtin_amdgcn_exp2f((m_run - mn) * down);  // 2^-inf = 0
       m_run = mn;
       nmd = -mn * down;
     }
-    float pr[4];
 #pragma unroll
-    for (int e = 0; e < 4; e++) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], down, nmd));
-    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    // The skip test uses the larger of the wave's running max and the workgroup's maximum
-    // over every wave's first step (msh, still at most the final maximum, so the bound on
-    // the final weight holds), and live heads only (padding columns hl >= r carry no query).
-    if (na_ == 0 && jq == 0 && hr < 8)
-      __hip_atomic_fetch_max(&smax[hl], cm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const float nsh = -fmaxf(msh, m_run) * down;
-    float pmax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; e++) pmax = fmaxf(pmax, __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], down, nsh)));
-    if (!live) pmax = 0.0f;
-    const bool needA = __any(hiLane && pmax >= vthr);
-    const bool needB = pb < p1 && __any(!hiLane && pmax >= vthr);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the previous pages' values are read
-    if (needA) stage_v<D, KCODEC>(page_blk(na_), slot_lds(na_ % NSLOT), lane);
-    if (needB) stage_v<D, KCODEC>(page_blk(na_ + 1), slot_lds((na_ + 1) % NSLOT), lane);
-    nskip += (needA ? 0 : 1) + ((needB || pb >= p1) ? 0 : 1);
-    pneed = (needA ? 1 : 0) | (needB ? 2 : 0);
-    ppa = pa;
-    pna = na_;
-#pragma unroll
-    for (int e = 0; e < 4; e++) ppr[e] = pr[e];
+    for (int e = 0; e < 4; e++) l_run += __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], down, nmd));
   };
 
   // Copy the appended token's bytes (indices and scales of token tnew) from tokblk into a
@@ -840,41 +788,80 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   int nis = min(npw, 2);
   const bool balance = npw >= 32;
   if constexpr (SPV) {
-    // The first step runs alone: every wave then shares its maxima (an exact max, so the
-    // snapshot and the skip decisions after it do not depend on timing).
+    // Sparse values [mlxcel manual, sparse-V threshold]. Pass 1 streams the keys of every
+    // page of this wave (exact running max and sum, page maxima). The workgroup's maximum
+    // per head M (over every wave: deterministic) then decides: a page is kept if some
+    // live head has 2^((max score - M) * down) >= v_thr; every other token's final weight,
+    // exp(s - m_final) / l with m_final >= M and l >= 1, is below v_thr too. Pass 2 streams
+    // keys and values of the kept pages through the dense step with the maximum fixed at M,
+    // and the sum over every token comes from pass 1. (At most 32 pages per wave: the split
+    // count is chosen for it.)
 #pragma unroll 1
     for (int na = 0; na < npw; na += 2) {
-      if (na == 2) {  // wave-uniform; waves without a second step meet the barrier below
-        __syncthreads();
-        msh = smax[hl];
-      }
-      if (balance) {
-        int lead = 0;
-        if (lane == 0) lead = atomicMax(&lead_n, na);
-        const int lag = __builtin_amdgcn_readfirstlane(lead) - na;
-        if (lag >= 4) __builtin_amdgcn_s_setprio(3);
-        else if (lag >= 2) __builtin_amdgcn_s_setprio(2);
-        else __builtin_amdgcn_s_setprio(0);
-      }
-      const int nmax = min(npw, na + NSLOT);
-      int nk = 0;
+      const int nmax = min(npw, na + NR);
 #pragma unroll
       for (int k = 0; k < 4; k++)
         if (nis < nmax) {
-          stage_k<D, KCODEC>(page_blk(nis), slot_lds(nis % NSLOT), lane);
+          stage_keys(nis);
           nis++;
-          nk++;
         }
-      // wait for this step's keys (page na + 1 may have been issued just now, when the ring
-      // has 3 slots) and for everything issued before this step (the previous step's values)
-      wait_all_but<SplitDma<D, KCODEC>::NK_OPS>(max(0, min(nk, nis - na - 2)));
+      wait_pages_in_flight<SplitDma<D, KCODEC>::NK_OPS, NR - 2>(max(0, min(NR - 2, nis - na - 2)));
       const int pa = p0 + wv + NW * na;
-      sstep(na, ring[na % NSLOT][wv], ring[(na + 1) % NSLOT][wv], pa, pa + NW);
+      kstep(na, k_slot(na), k_slot(na + 1), pa, pa + NW);
     }
-    if (npw <= 2) __syncthreads();  // the first-step barrier of waves that never reached it
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (pneed) pv_prev();
-    if (a.v_skipped && lane == 0 && nskip > 0) atomicAdd(a.v_skipped, (unsigned long long)nskip);
+    if (jq == 0 && hr < 8) mml[wv][hr][0] = m_run;
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; w++) M = fmaxf(M, mml[w][hl][0]);
+    __syncthreads();  // (mml is written again in the epilogue)
+    const float l_all = (m_run == -INFINITY) ? 0.0f : l_run * __builtin_amdgcn_exp2f((m_run - M) * down);
+    m_run = M;
+    nmd = -M * down;
+    // keep mask: bit n = page n of this wave
+    const float l2t = __builtin_amdgcn_logf(a.v_thr);  // log2 of the threshold
+    uint32_t keep = 0;
+#pragma unroll
+    for (int k = 0; k < NPM; k++) {
+      const int n = 8 * k + (lane >> 3);
+      const bool hit = live && n < npw && (pmreg[k] - M) * down >= l2t;
+      const uint64_t bal = __ballot(hit);
+#pragma unroll
+      for (int q = 0; q < 8; q++)
+        if ((bal >> (8 * q)) & 0xffu) keep |= 1u << (8 * k + q);
+    }
+    keep = __builtin_amdgcn_readfirstlane(keep);
+    const int nk = __builtin_popcount(keep);
+    nskip = npw - nk;
+    int klist = 0;  // lane i: the wave page number of the i-th kept page
+    {
+      uint32_t m = keep;
+      for (int i = 0; m != 0u; i++) {
+        const int n = __builtin_ctz(m);
+        m &= m - 1u;
+        if (lane == i) klist = n;
+      }
+    }
+    auto kn = [&](int i) { return __builtin_amdgcn_readlane(klist, i); };
+    int nis2 = 0;
+#pragma unroll 1
+    for (int i = 0; i < nk; i += 2) {
+      const int nmax = min(nk, i + NSLOT);
+#pragma unroll
+      for (int k = 0; k < 4; k++)
+        if (nis2 < nmax) {
+          stage_page<D, KCODEC, VB>(page_blk(kn(nis2)), slot_lds(nis2 % NSLOT), lane);
+          nis2++;
+        }
+      wait_pages_in_flight<C::NDMA, NSLOT - 2>(max(0, min(NSLOT - 2, nis2 - i - 2)));
+      const int pa = p0 + wv + NW * kn(i);
+      const int pb = (i + 1 < nk) ? p0 + wv + NW * kn(i + 1) : p1;  // p1: no page B
+      step(ring[i % NSLOT][wv], ring[(i + 1) % NSLOT][wv], pa, pb);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    l_run = l_all;
+    if (lane == 0 && nskip > 0) atomicAdd(&wskip, nskip);  // (one global add per workgroup below)
   } else {
 #pragma unroll 1
   for (int na = 0; na < npw; na += 2) {
@@ -923,6 +910,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     acc[2 * g + 1] *= 1048576.0f;
   }
   __syncthreads();  // every wave is done with its ring: reuse it as the merge area
+  if (SPV && tid == 0 && a.v_skipped && wskip > 0) atomicAdd(a.v_skipped, (unsigned long long)wskip);
   if (hr < 8) {
 #pragma unroll
     for (int g = 0; g < G; g++) {

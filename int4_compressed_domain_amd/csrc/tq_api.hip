@@ -61,14 +61,20 @@ Split make_split(int pages, int S) {
   return s;
 }
 
-Split choose_split(int B, int Hkv, int D, int k_codec, int max_ctx, int requested) {
+// sparse: the two-pass sparse-value loop keeps at most TQ_SPARSE_PAGES_PER_WAVE pages per
+// wave, which sets a smallest split count.
+Split choose_split(int B, int Hkv, int D, int k_codec, int max_ctx, int requested, bool sparse = false) {
   const int pages = (max_ctx + 15) / 16;
-  const int min_s = (pages + TQ_MAX_SPLIT_PAGES - 1) / TQ_MAX_SPLIT_PAGES;  // page ids fit LDS
+  const int nw = tq_decode_waves(D, k_codec);
+  int min_s = (pages + TQ_MAX_SPLIT_PAGES - 1) / TQ_MAX_SPLIT_PAGES;  // page ids fit LDS
+  if (sparse) {
+    const int per = TQ_SPARSE_PAGES_PER_WAVE * nw;
+    if ((pages + per - 1) / per > min_s) min_s = (pages + per - 1) / per;
+  }
   if (requested > 0) {
     int S = requested < TQ_MAX_SPLITS ? requested : TQ_MAX_SPLITS;
     return make_split(pages, S > min_s ? S : min_s);
   }
-  const int nw = tq_decode_waves(D, k_codec);
   const int64_t units = (int64_t)B * Hkv;
   const int64_t target = (int64_t)num_cus() * (D >= 256 ? 2 : 1);
   int64_t want = (target + units - 1) / units;
@@ -96,8 +102,10 @@ size_t partial_bytes(int B, int Hq, int D, int splits) {
 
 size_t workspace_bytes(const tq_layout* L, int B, int max_ctx, int requested) {
   const Split f = choose_split(B, L->num_kv_heads, L->head_dim, L->k_codec, max_ctx, requested);
+  const Split sp = choose_split(B, L->num_kv_heads, L->head_dim, L->k_codec, max_ctx, requested, true);
   const Split d = choose_split_dense(B, L->num_kv_heads, max_ctx, requested);
-  const int S = f.splits > d.splits ? f.splits : d.splits;
+  int S = f.splits > d.splits ? f.splits : d.splits;
+  if (sp.splits > S) S = sp.splits;
   return TQ_DECODE_COUNTER_BYTES + partial_bytes(B, L->num_q_heads, L->head_dim, S) +
          (size_t)B * L->num_kv_heads * sizeof(int32_t);  // + the workgroup order
 }
@@ -173,9 +181,13 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   if ((int64_t)max_context_len > 16LL * TQ_MAX_SPLITS * TQ_MAX_SPLIT_PAGES) return TQ_EUNSUPPORTED;
   if (L->k_codec == TQ_CODEC_FP16 && L->head_dim > 128) return TQ_EUNSUPPORTED;
   if (sparse_v && L->v_codec != TQ_CODEC_ABSMAX) return TQ_EUNSUPPORTED;
+  if (sparse_v && (int64_t)max_context_len >
+                      16LL * TQ_MAX_SPLITS * TQ_SPARSE_PAGES_PER_WAVE * tq_decode_waves(L->head_dim, L->k_codec))
+    return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
   if (!pool || !block_table) return TQ_EINVAL;
-  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits);
+  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits,
+                         sparse_v != 0);
   const int64_t resident = (int64_t)num_cus() * (L->head_dim >= 256 ? 2 : 1);
   // fp16 tail: with automatic splits, at least 8 of them per unit, a grid that fits the chip
   // and a tail of at most 256 tokens, one split is given up for a workgroup per unit that
@@ -248,9 +260,12 @@ int tq_decode_attn_sparse_v(const tq_layout* L, const void* pool, const void* q,
                             size_t workspace_bytes_, unsigned long long* v_pages_skipped,
                             void* stream) {
   if (!(v_threshold >= 0.0f && v_threshold < 1.0f)) return TQ_EINVAL;
+  if (check_layout(L, true) == TQ_OK && L->v_codec != TQ_CODEC_ABSMAX) return TQ_EUNSUPPORTED;
+  // a zero threshold drops nothing: the dense decode, bit for bit
   return decode_impl(L, pool, nullptr, nullptr, 0, q, q_dtype, batch, block_table,
                      max_pages_per_seq, context_lens, max_context_len, attn_scale, num_splits, out,
-                     workspace, workspace_bytes_, stream, 1, v_threshold, v_pages_skipped);
+                     workspace, workspace_bytes_, stream, v_threshold > 0.0f ? 1 : 0, v_threshold,
+                     v_pages_skipped);
 }
 
 int tq_decode_attn_hotcold(const tq_layout* L, const void* pool, const void* q, int32_t q_dtype,

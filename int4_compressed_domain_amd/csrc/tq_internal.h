@@ -74,5 +74,6 @@ constexpr int TQ_DECODE_WAVES = 4;   // dense baseline workgroups
 constexpr int TQ_MAX_SPLITS = 128;   // context splits per (sequence, kv head)
 constexpr int TQ_MAX_SPLIT_PAGES = 2048;  // pages per split (their ids are staged in LDS)
 constexpr int TQ_LPT_MAX_BATCH = 256;    // longest-first workgroup order up to this batch
+constexpr int TQ_SPARSE_PAGES_PER_WAVE = 32;  // sparse values: page maxima kept per wave
 constexpr int TQ_MAX_HOT = 1024;         // fp16 tail tokens per (sequence, kv head)
 constexpr int TQ_MAX_UNITS = 1 << 20;  // sequences x kv heads per call
