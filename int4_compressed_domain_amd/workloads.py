@@ -196,13 +196,19 @@ def slots_for(bt, b, t0, t1):
     return bt[b, t // PAGE].astype(np.int64) * PAGE + t % PAGE
 
 
+def kv_bytes_per_token(w: Workload):
+    """Packed K+V bytes of one token over all kv heads: keys D/2 + 2*D/32 (fp16 keys: 2D),
+    values b*D/8 + 2*D/32 for b-bit values, per kv head."""
+    D = w.head_dim
+    kbytes = 2 * D if w.k_codec == CODEC_FP16 else D // 2 + 2 * (D // 32)
+    vbytes = VALUE_BITS[w.v_codec] * D // 8 + 2 * (D // 32)
+    return w.kv_heads * (kbytes + vbytes)
+
+
 def algorithmic_bytes(w: Workload, lens):
     """Packed K+V indices and fp16 scales read by one decode: sum_b L_b * Hkv * (keys:
     D/2 + 2*D/32, or 2D for fp16 keys; values: b*D/8 + 2*D/32 for b-bit values), plus the
     query and the fp32 output."""
-    D = w.head_dim
-    kbytes = 2 * D if w.k_codec == CODEC_FP16 else D // 2 + 2 * (D // 32)
-    vbytes = VALUE_BITS[w.v_codec] * D // 8 + 2 * (D // 32)
-    per_tok = w.kv_heads * (kbytes + vbytes)
+    per_tok = kv_bytes_per_token(w)
     qbytes = w.batch * w.q_heads * D * (4 if w.dtype == "f32" else 2)
     return int(np.sum(lens, dtype=np.int64)) * per_tok + qbytes + w.batch * w.q_heads * D * 4
