@@ -209,6 +209,7 @@ def algorithmic_bytes(w: Workload, lens):
     """Packed K+V indices and fp16 scales read by one decode: sum_b L_b * Hkv * (keys:
     D/2 + 2*D/32, or 2D for fp16 keys; values: b*D/8 + 2*D/32 for b-bit values), plus the
     query and the fp32 output."""
+    D = w.head_dim
     per_tok = kv_bytes_per_token(w)
     qbytes = w.batch * w.q_heads * D * (4 if w.dtype == "f32" else 2)
     return int(np.sum(lens, dtype=np.int64)) * per_tok + qbytes + w.batch * w.q_heads * D * 4

@@ -208,3 +208,16 @@ def test_lut_constant_matches_product_generator():
     block = text[text.index("#define TQ_LUT16_BITS"):]
     bits = [int(x, 16) for x in re.findall(r"0x([0-9a-f]{4})u", block)[:16]]
     assert bits == gen_lloydmax.lut_bits()
+
+
+def test_algorithmic_bytes_of_the_measured_workloads():
+    """Bytes one decode must read (packed K+V, query, fp32 output), as the benchmark counts
+    them: 144 B per token and kv head at D = 128 with 4-bit keys and values, 328 with fp16
+    keys, 312 with fp16 keys and 3-bit values, 112 with 2-bit values."""
+    from int4_compressed_domain_amd import workloads as W
+    extra = 64 * 128 * 2 + 64 * 128 * 4  # bf16 query + fp32 output
+    for name, per in (("llama70b_b1_128k", 144), ("llama70b_b1_128k_k16v4", 328),
+                      ("llama70b_b1_128k_k16v3", 312), ("llama70b_b1_128k_k4v2", 112)):
+        w = W.WORKLOADS[name]
+        assert W.algorithmic_bytes(w, W.context_lens(w, 0)) == 131072 * 8 * per + extra
+    assert W.algorithmic_bytes(W.WORKLOADS["llama70b_b1_128k"], W.context_lens(W.WORKLOADS["llama70b_b1_128k"], 0)) == 151044096
