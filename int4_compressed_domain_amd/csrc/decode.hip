@@ -1,4 +1,4 @@
-// Decode attention directly on the packed int4 cache, one fused kernel.
+// Decode attention directly on the packed cache, one fused kernel.
 // [Open-TQ-Metal, arXiv abstract: attention computed on the compressed representation,
 //  no intermediate dequantized K/V matrix; the split merge follows the online softmax
 //  normalizer cited among its references.]
@@ -9,24 +9,32 @@
 // u mod 8 and the partials they exchange stay in that XCD's L2.
 //
 //  prologue  the r = Hq/Hkv queries of head h are rotated into the cache basis with the same
-//            fp32 butterfly as the keys, scaled by alpha*log2(e) and a power of two, and split
-//            into fp16 hi + lo parts: B-operand columns 0..7 hold hi of heads 0..7, columns
-//            8..15 hold lo, so one 16-column MFMA carries ~22 bits of each query.
-//  page loop each wave takes every NW-th page of the split, loading the next page while it
-//            computes the current one. Per 16-token page:
+//            fp32 butterfly as the keys (fp16 keys: not rotated), scaled by alpha*log2(e)
+//            and a power of two, and split into fp16 hi + lo parts: B-operand columns 0..7
+//            hold hi of heads 0..7, columns 8..15 hold lo, so one 16-column MFMA carries
+//            ~22 bits of each query. Each wave's first two pages are already loading.
+//  page loop each wave takes every NW-th page of the split, two pages per step, streaming
+//            later pages into its LDS ring (LDS-DMA) while it computes. Per 16-token page:
 //            scores  the K operand is the index bits themselves: (w & 0x000F000F) is the fp16
 //                    subnormal u * 2^-24 (exact), so one AND unpacks two indices; the offset
 //                    u = c + 8 is removed exactly by starting the MFMA accumulator at -beta,
 //                    beta = 8 * 2^-24 * (sum of the 32 query values of the group). One
-//                    16x16x32 MFMA per 32-dim group, then times the group's fp16 scale;
+//                    16x16x32 MFMA per 32-dim group, then times the group's fp16 scale (LUT
+//                    keys: the index picks a table value first; fp16 keys: the staged keys
+//                    are the A operand);
 //            softmax running max/sum per head in the log2 domain, rescaling only when the
 //                    max grows;
-//            values  V indices become exact fp16 c via 1024 + n magic; P' = p * s_V in fp16
-//                    hi (columns 0..7) + lo (8..15); two 16x16x16 MFMAs per group.
-//  epilogue  the NW waves merge through LDS. With one split the workgroup finishes the head;
-//            otherwise it stores its partial (o', m, l), and the last workgroup of the unit
-//            to arrive (atomic counter, reset afterwards) merges all splits. The result is
-//            rotated back (fp32 butterfly, times rho, times sigma) and written.
+//            values  the V indices are subnormal A operands too (3- and 2-bit values are
+//                    first rebuilt into the 4-bit layout); P' = p * s_V rounded once to
+//                    fp16 is the B operand, one 16x16x32 MFMA per group and dim parity for
+//                    both pages, and a second one with a constant A removes the offset.
+//  epilogue  the NW waves merge through LDS (an fp16 tail's slice joins here); with one
+//            split the workgroup finishes the head, otherwise it stores its partial
+//            (o', m, l), and the last workgroup of the unit to arrive (atomic counter, reset
+//            afterwards) merges all splits. The result is rotated back (fp32 butterfly,
+//            times rho, times sigma) and written.
+// Variants: the fused append of each sequence's newest token (knew/vnew), sparse values in
+// two passes (SPV), an fp16 tail (hot_k/hot_v).
 #include "tq_codec.h"
 #include "tq_internal.h"
 

@@ -1,7 +1,8 @@
 // Dequantize reference: dense K and V from the packed pool, the first half of the
 // dequantize-then-attend baseline [Open-TQ-Metal, arXiv abstract].
 // 16 lanes per (sequence, kv head, token) vector, E = D/16 coordinates per lane; values
-// (u-8)*s or LUT_u*n are exact in fp32. The original-basis variant applies the fp32
+// (u - 8)*s (4-bit), (u - 4)*s or (u - 2)*s (3- and 2-bit values) or LUT_u*n are exact in
+// fp32. The original-basis variant applies the fp32
 // inverse rotation diag(sigma)*rho*H with the forward rotation's stage order.
 // fp16 keys are copied as stored (they have no rotated form). Compiled with
 // -ffp-contract=off.
