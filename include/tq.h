@@ -161,7 +161,8 @@ size_t tq_decode_workspace_size(const tq_layout* layout, int32_t batch, int32_t 
  *                   16-token page of each sequence
  *   context_lens    device int32 [batch]: tokens to attend (0 gives a zero output);
  *                   each <= max_context_len <= 16 * max_pages_per_seq
- *   max_context_len host, an upper bound of context_lens (sizes the launch)
+ *   max_context_len host, an upper bound of context_lens (sizes the launch); when it is
+ *                   0, pool and block_table are not read and may be NULL
  *   attn_scale      softmax scale alpha (scores are alpha * q.k)
  *   num_splits      0 = automatic; > 0 forces that many context splits, at most 128
  *                   (results agree across split counts up to rounding)

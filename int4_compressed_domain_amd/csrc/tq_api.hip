@@ -185,7 +185,9 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
                       16LL * TQ_MAX_SPLITS * TQ_SPARSE_PAGES_PER_WAVE * tq_decode_waves(L->head_dim, L->k_codec))
     return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
-  if (!pool || !block_table) return TQ_EINVAL;
+  // with every context empty nothing is read from the pool or the block table (the outputs
+  // are zeros, plus a tail's attention for tq_decode_attn_hotcold): they may be NULL then
+  if (max_context_len > 0 && (!pool || !block_table)) return TQ_EINVAL;
   Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits,
                          sparse_v != 0);
   const int64_t resident = (int64_t)num_cus() * (L->head_dim >= 256 ? 2 : 1);

@@ -521,3 +521,46 @@ def test_graph_replay_matches_eager():
         step()                      # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
+
+
+def _random_config(i):
+    rng = np.random.default_rng(1000 + i)
+    D = int(rng.choice([64, 128, 256]))
+    k_codec = int(rng.choice([0, 1, 2] if D <= 128 else [0, 1]))
+    v_codec = int(rng.choice([W.CODEC_ABSMAX, W.CODEC_ABSMAX3, W.CODEC_ABSMAX2]))
+    r = int(rng.choice([1, 2, 3, 4, 8]))
+    kv = int(rng.choice([1, 2, 3]))
+    batch = int(rng.integers(1, 5))
+    lens = [int(x) for x in rng.integers(0, 600, batch)]
+    if i % 4 == 1:
+        lens[-1] = 0
+    if i % 4 == 2:
+        lens[0] = 16 * int(rng.integers(1, 30))
+    q_dtype = str(rng.choice(["bf16", "f32", "f16"]))
+    splits = int(rng.choice([0, 0, 1, 2, 7]))
+    hot = int(rng.choice([0, 0, 1, 40])) if i % 3 == 0 else 0
+    return D, k_codec, v_codec, r, kv, batch, lens, q_dtype, splits, hot
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_configurations(i):
+    """Seeded random combinations of head dim, key and value codecs, GQA ratio, kv heads,
+    ragged lengths, query dtype, split count and (every third case) an fp16 tail: pool bytes
+    equal to the oracle's and attention within the tolerance."""
+    D, k_codec, v_codec, r, kv, batch, lens, q_dtype, splits, hot = _random_config(i)
+    _say("case random %d: D %d k %d v %d r %d kv %d lens %s q %s splits %d hot %d"
+         % (i, D, k_codec, v_codec, r, kv, lens, q_dtype, splits, hot))
+    if hot:
+        hl = [min(hot, 1 + (b * 7) % (hot + 1)) for b in range(batch)]
+        _hot_cold_case(D, r, k_codec, [max(L, 1) if b % 2 else L for b, L in enumerate(lens)], hl,
+                       max(hot, 1), (splits,), 2000 + i, v_codec=v_codec, kv=kv)
+        return
+    w = W.Workload("rnd%d" % i, batch, kv * r, kv, D, max(max(lens), 1), "bf16", 1.0 / math.sqrt(D),
+                   k_codec=k_codec, v_codec=v_codec, dist="lognormal_spikes")
+    c = Case(w, seed=3000 + i, lens=lens, q_dtype=q_dtype)
+    c.fill(chunk=257)
+    assert c.pool_equal(), "packed pool differs from the oracle"
+    out = _check_case(c, num_splits=splits)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(out[b] == 0.0)
