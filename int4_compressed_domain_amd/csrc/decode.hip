@@ -266,6 +266,16 @@ __device__ __forceinline__ float load_q(const void* q, int dt, int64_t i) {
   if (dt == TQ_BF16) return widen(static_cast<const uint16_t*>(q)[i]);
   return widen(static_cast<const f16*>(q)[i]);
 }
+// The same in two steps: the element's bits (fp32, or 16 bits zero-extended), then widened.
+__device__ __forceinline__ uint32_t load_q_bits(const void* q, int dt, int64_t i) {
+  if (dt == TQ_F32) return static_cast<const uint32_t*>(q)[i];
+  return static_cast<const uint16_t*>(q)[i];
+}
+__device__ __forceinline__ float widen_q_bits(uint32_t x, int dt) {
+  if (dt == TQ_F32) return __uint_as_float(x);
+  if (dt == TQ_BF16) return __uint_as_float(x << 16);
+  return (float)__builtin_bit_cast(f16, (uint16_t)x);
+}
 
 template <int D, int KCODEC, int VB, int NW, bool SPV>
 __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
@@ -347,14 +357,19 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // this wave's pages p0 + wv + NW n, n < npw: physical page ids held across the lanes
   // (page n in lane n % 64 of register n / 64), read back with v_readlane when issued
   const int npw = (p1 - p0 - wv + NW - 1) / NW;  // pages of this wave
+  // The small loads of the prologue (query bits, sign bits, page ids, an appended token)
+  // are issued back to back and waited for together: one memory round trip.
+  const int64_t qb = ((int64_t)b * a.Hq + (int64_t)h * r) * D;  // this unit's query elements
+  uint32_t qraw[V];  // wave w < r: bits of query head w, dims lane + 64k (widened below)
+  if (wv < r) {
+#pragma unroll
+    for (int k = 0; k < V; k++) qraw[k] = load_q_bits(a.q, a.q_dtype, qb + wv * D + lane + 64 * k);
+  }
+  const uint32_t sgn_word = tid < D / 32 ? a.sign_bits[tid] : 0u;
   constexpr int PPL = (TQ_MAX_SPLIT_PAGES / NW + 63) / 64;
   int vpid[PPL];
 #pragma unroll
   for (int k = 0; k < PPL; k++) vpid[k] = (lane + 64 * k < npw) ? bt[p0 + wv + NW * (lane + 64 * k)] : 0;
-  // consume the loads here, before any page is in flight: otherwise the compiler waits for
-  // them (vmcnt(0), i.e. for every in-flight page too) where they are first read in the loop
-#pragma unroll
-  for (int k = 0; k < PPL; k++) asm volatile("" ::"v"(vpid[k]));
   auto page_blk = [&](int n) {  // wave-uniform address of page n's block for head h
     int id = vpid[0];
     if constexpr (PPL > 1) {
@@ -388,21 +403,23 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     for (int e = 0; e < E; e++) asm volatile("" ::"v"(ynew[e]));  // before any page load
     asm volatile("" ::"v"(swnew));
   }
-  if (tid < D / 32) sgn_s[tid] = a.sign_bits[tid];
-  const int64_t qb = ((int64_t)b * a.Hq + (int64_t)h * r) * D;  // this unit's query elements
+  // consume the page ids here, before any page is in flight: otherwise the compiler waits
+  // for them (vmcnt(0), i.e. for every in-flight page too) where they are first read
+#pragma unroll
+  for (int k = 0; k < PPL; k++) asm volatile("" ::"v"(vpid[k]));
+  if (tid < D / 32) sgn_s[tid] = sgn_word;
+  __syncthreads();
   float qv[V];
   if (wv < r) {  // wave w rotates query head w: sign flip now, butterflies below
 #pragma unroll
     for (int k = 0; k < V; k++) {
       const int d = lane + 64 * k;
-      const float x = load_q(a.q, a.q_dtype, qb + wv * D + d);
+      const float x = widen_q_bits(qraw[k], a.q_dtype);
       // fp16 keys are in the original basis: the query scores them unrotated
-      qv[k] = (!KF16 && ((a.sign_bits[d >> 5] >> (d & 31)) & 1u)) ? -x : x;
+      qv[k] = (!KF16 && ((sgn_s[d >> 5] >> (d & 31)) & 1u)) ? -x : x;
     }
   }
-  __syncthreads();
   // start streaming this wave's first pages; they land while the queries are prepared
-  // (the rotating waves issue theirs after the rotation, which stays off the busy queue)
   // sparse values, first pass: NR ring entries per wave, half slots with 4-bit keys
   constexpr int NR = C::HS ? 2 * NSLOT : NSLOT;
   auto k_lds = [&](int n) {  // LDS byte address of the first pass's entry for page n
