@@ -118,6 +118,7 @@ class Setup:
             t = np.arange(w.prefill)
             self.k_pre, self.v_pre = to_dev(kst, w.dtype, dev), to_dev(vst, w.dtype, dev)
             self.slots_pre = torch.from_numpy(pre[t // 16] * 16 + t % 16).to(dev)
+            self.pre_stream = torch.cuda.Stream()  # default priority, like every stream here
         torch.cuda.synchronize()
         log("filled %s: %d pages, %.1f MB pool, %.1f s" % (w.name, self.npages, pool_bytes / 1e6,
                                                             time.time() - t_fill))
@@ -182,8 +183,19 @@ class Setup:
                                  num_splits=self.splits)
 
     def step(self, i):
-        self.prefill(i)
-        self.decode(i)
+        """The prefill chunk's append and the decode. They touch different pages (the chunk
+        fills fresh ones), so the append runs on a second stream beside the decode and can
+        take the compute units the decode's shorter sequences leave idle."""
+        import torch
+        if self.k_pre is None:
+            self.decode(i)
+            return
+        cur = torch.cuda.current_stream()
+        self.pre_stream.wait_stream(cur)
+        self.decode(i)  # first, so that its workgroups (one per CU) take the CUs first
+        with torch.cuda.stream(self.pre_stream):
+            self.prefill(i)
+        cur.wait_stream(self.pre_stream)
 
 
 def _graph(fn, n):
