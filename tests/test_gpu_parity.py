@@ -564,3 +564,18 @@ def test_random_configurations(i):
     for b, L in enumerate(lens):
         if L == 0:
             assert np.all(out[b] == 0.0)
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 12345, 8 << 20])
+def test_stream_read_probe_reads_every_word_once(nbytes):
+    """The measurement probe (not part of the method): every thread stores the XOR of the
+    words it read, so the XOR over the sink equals the XOR over the whole buffer exactly
+    when each 16-byte element is read once."""
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2 ** 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(DEV)
+    sink = torch.zeros((2 << 20) // 4, dtype=torch.int32, device=DEV)
+    tq.tq_stream_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert int(got) == int(np.bitwise_xor.reduce(host))
