@@ -72,7 +72,12 @@
  *  - Arguments are checked on the host before any device work; failures return a
  *    negative tq_status and launch nothing. A launch failure returns TQ_EDEVICE. Device
  *    contents (slots, block tables, context lengths) are preconditions, not checked:
- *    out-of-range values there are undefined behaviour.
+ *    out-of-range values there are undefined behaviour, unless the environment variable
+ *    TQ_VALIDATE is 1. Then each call synchronizes its stream, copies these arrays to
+ *    the host and returns TQ_EINVAL, launching nothing, for page ids a sequence uses
+ *    outside [0, num_pages), lengths outside [0, max_context_len], tail lengths above
+ *    hot_cap, and slots outside the pool or given twice (a debugging aid: it costs a
+ *    synchronization and host copies per call).
  *  - GPU support: head_dim in {64, 128, 256}, group_size 32, page_size 16,
  *    1 <= num_q_heads / num_kv_heads <= 8, batch * num_kv_heads <= 2^20; decode with fp16
  *    keys at head_dim 64 and 128; sparse values with 4-bit values only (TQ_EUNSUPPORTED

@@ -4,6 +4,10 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <vector>
 
 #include "../../include/tq.h"
 #include "tq_internal.h"
@@ -112,6 +116,71 @@ size_t workspace_bytes(const tq_layout* L, int B, int max_ctx, int requested) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EDEVICE; }
 
+// ---- optional validation of device-side preconditions (TQ_VALIDATE=1) -------------------
+// Block tables, lengths and slots live in device memory and are normally trusted. With the
+// environment variable TQ_VALIDATE set to 1, a call first synchronizes its stream, copies
+// them to the host and rejects out-of-range values before launching anything.
+bool validating() {
+  const char* e = getenv("TQ_VALIDATE");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+template <typename T>
+int to_host(std::vector<T>& dst, const T* src, size_t n) {
+  dst.resize(n);
+  if (n == 0) return TQ_OK;
+  return from_hip(hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost));
+}
+
+// lengths in [0, max_ctx]; the page ids a sequence uses in [0, num_pages); tail lengths
+// (hot_lens, when given) in [0, hot_cap]
+int validate_tables(const tq_layout* L, int batch, const int32_t* block_table, int max_pages,
+                    const int32_t* lens_dev, int max_ctx, const int32_t* hot_lens, int hot_cap,
+                    hipStream_t st) {
+  if (hipStreamSynchronize(st) != hipSuccess) return TQ_EDEVICE;
+  std::vector<int32_t> lens, bt, hl;
+  int rc = to_host(lens, lens_dev, (size_t)batch);
+  if (rc != TQ_OK) return rc;
+  int32_t need = 0;
+  for (int b = 0; b < batch; b++) {
+    if (lens[b] < 0 || lens[b] > max_ctx) return TQ_EINVAL;
+    need = std::max(need, (lens[b] + 15) / 16);
+  }
+  if (need > 0) {
+    if (!block_table) return TQ_EINVAL;
+    rc = to_host(bt, block_table, (size_t)batch * max_pages);
+    if (rc != TQ_OK) return rc;
+    for (int b = 0; b < batch; b++)
+      for (int p = 0; p < (lens[b] + 15) / 16; p++) {
+        const int32_t id = bt[(size_t)b * max_pages + p];
+        if (id < 0 || id >= L->num_pages) return TQ_EINVAL;
+      }
+  }
+  if (hot_lens) {
+    rc = to_host(hl, hot_lens, (size_t)batch);
+    if (rc != TQ_OK) return rc;
+    for (int b = 0; b < batch; b++)
+      if (hl[b] < 0 || hl[b] > hot_cap) return TQ_EINVAL;
+  }
+  return TQ_OK;
+}
+
+// slots inside the pool (negative: skipped), no slot twice
+int validate_slots(const tq_layout* L, int n, const int64_t* slots, hipStream_t st) {
+  if (hipStreamSynchronize(st) != hipSuccess) return TQ_EDEVICE;
+  std::vector<int64_t> sl;
+  const int rc = to_host(sl, slots, (size_t)n);
+  if (rc != TQ_OK) return rc;
+  std::vector<int64_t> used;
+  for (int64_t x : sl) {
+    if (x < 0) continue;
+    if (x >= (int64_t)L->num_pages * 16) return TQ_EINVAL;
+    used.push_back(x);
+  }
+  std::sort(used.begin(), used.end());
+  return std::adjacent_find(used.begin(), used.end()) == used.end() ? TQ_OK : TQ_EINVAL;
+}
+
 int check_decode_common(const tq_layout* L, const void* q, int q_dtype, int batch,
                         const int32_t* context_lens, int max_context_len, float attn_scale,
                         int num_splits, const float* out) {
@@ -152,6 +221,10 @@ int tq_kv_append(const tq_layout* L, void* pool, const void* k, const void* v, i
   if (n_tokens == 0) return TQ_OK;
   if (!pool || !k || !v || !slot_mapping) return TQ_EINVAL;
   if ((int64_t)n_tokens * L->num_kv_heads * 2 > (int64_t)16 * 0x7fffffff) return TQ_EUNSUPPORTED;
+  if (validating()) {
+    rc = validate_slots(L, n_tokens, slot_mapping, static_cast<hipStream_t>(stream));
+    if (rc != TQ_OK) return rc;
+  }
   LaunchAppend a{static_cast<uint8_t*>(pool), k, v, slot_mapping, L->sign_bits,
                  L->head_dim, L->num_kv_heads, n_tokens, in_dtype, L->k_codec, L->v_codec};
   return from_hip(tq_launch_append(a, static_cast<hipStream_t>(stream)));
@@ -205,6 +278,11 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   }
   if (workspace_bytes_ < workspace_bytes(L, batch, max_context_len, num_splits)) return TQ_ENOSPC;
   if (!workspace) return TQ_EINVAL;
+  if (validating()) {
+    rc = validate_tables(L, batch, block_table, max_pages_per_seq, context_lens, max_context_len,
+                         hot_k ? hot_lens : nullptr, hot_cap, static_cast<hipStream_t>(stream));
+    if (rc != TQ_OK) return rc;
+  }
   float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + TQ_DECODE_COUNTER_BYTES);
   LaunchDecode a{};
   a.counters = static_cast<int*>(workspace);
@@ -305,6 +383,11 @@ int tq_dequant_ref(const tq_layout* L, const void* pool, int32_t batch, const in
   if (to_original_basis != 0 && to_original_basis != 1) return TQ_EINVAL;
   if ((int64_t)batch * max_context_len == 0) return TQ_OK;
   if (!pool || !block_table || !context_lens || !k_out || !v_out) return TQ_EINVAL;
+  if (validating()) {
+    rc = validate_tables(L, batch, block_table, max_pages_per_seq, context_lens, max_context_len,
+                         nullptr, 0, static_cast<hipStream_t>(stream));
+    if (rc != TQ_OK) return rc;
+  }
   LaunchDequant a{static_cast<const uint8_t*>(pool), block_table, context_lens, L->sign_bits,
                   k_out, v_out, L->head_dim, L->num_kv_heads, batch, max_pages_per_seq,
                   max_context_len, to_original_basis, out_dtype, L->k_codec, L->v_codec};

@@ -579,3 +579,47 @@ def test_stream_read_probe_reads_every_word_once(nbytes):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert int(got) == int(np.bitwise_xor.reduce(host))
+
+
+def test_validation_of_device_tables(monkeypatch):
+    """TQ_VALIDATE=1: the device-side preconditions are checked on the host before any
+    launch. A page id outside the pool, a length above max_context_len, a tail longer than
+    its capacity, and a slot outside the pool or given twice return TQ_EINVAL; valid
+    tables decode as usual."""
+    monkeypatch.setenv("TQ_VALIDATE", "1")
+    w = W.Workload("val", 2, 4, 2, 128, 40, "bf16", 0.1)
+    c = Case(w, seed=7, lens=[40, 17])
+    c.fill()
+    _check_case(c)  # valid tables: checked, then decoded
+    ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, 2, 40, 0) // 4, dtype=torch.float32, device=DEV)
+    out = torch.zeros((2, 4, 128), dtype=torch.float32, device=DEV)
+
+    def decode(bt, lens, maxc=40):
+        tq.tq_decode_attn(c.layout, c.pool, c.q_dev, torch.from_numpy(bt).to(DEV),
+                          torch.from_numpy(np.asarray(lens, np.int32)).to(DEV), maxc, 0.1, out, ws)
+
+    bt = c.bt.copy()
+    bt[1, 1] = c.npages  # page 1 of the 17-token sequence lies outside the pool
+    with pytest.raises(tq.TQError) as e:
+        decode(bt, c.lens)
+    assert e.value.status == tq.TQ_EINVAL
+    bt = c.bt.copy()
+    bt[1, 2] = -1  # not used by a 17-token sequence: accepted
+    decode(bt, c.lens)
+    with pytest.raises(tq.TQError) as e:
+        decode(c.bt, [41, 17])  # longer than max_context_len
+    assert e.value.status == tq.TQ_EINVAL
+    hk = torch.zeros((2, 2, 8, 128), dtype=torch.float16, device=DEV)
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_decode_attn_hotcold(c.layout, c.pool, c.q_dev, c.bt_dev, c.lens_dev, 40, hk, hk,
+                                  torch.tensor([3, 9], dtype=torch.int32, device=DEV), 0.1, out, ws)
+    assert e.value.status == tq.TQ_EINVAL  # a tail of 9 tokens in a capacity of 8
+    kv = torch.zeros((2, 2, 128), dtype=torch.bfloat16, device=DEV)
+    for slots in ([0, 0], [c.npages * 16, -1]):  # a slot twice; a slot outside the pool
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_kv_append(c.layout, c.pool, kv, kv, torch.tensor(slots, dtype=torch.int64, device=DEV))
+        assert e.value.status == tq.TQ_EINVAL
+    before = c.pool.clone()
+    tq.tq_kv_append(c.layout, c.pool, kv[:1], kv[:1], torch.tensor([-1], dtype=torch.int64, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(before, c.pool)
