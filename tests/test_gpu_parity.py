@@ -623,3 +623,25 @@ def test_validation_of_device_tables(monkeypatch):
     tq.tq_kv_append(c.layout, c.pool, kv[:1], kv[:1], torch.tensor([-1], dtype=torch.int64, device=DEV))
     torch.cuda.synchronize()
     assert torch.equal(before, c.pool)
+
+
+@pytest.mark.parametrize("D,k_codec", [(64, 0), (128, 1)])
+def test_sparse_values_full_waves(D, k_codec):
+    """Sparse values with one split over 8192 tokens (512 pages): each wave holds the most
+    pages the first pass keeps maxima for (32); D = 64 packs two key parts per ring slot
+    like D = 128. Within the tolerance plus the oracle's bound, value pages skipped."""
+    w = W.Workload("sv_full_d%d" % D, 2, 8, 2, D, 8192, "bf16", 1.0 / math.sqrt(D), k_codec=k_codec,
+                   dist="lognormal_spikes")
+    _say("case sparse values, full waves, D", D, "k_codec", k_codec)
+    c = Case(w, seed=29, lens=[8192, 5000])
+    c.fill()
+    exact = c.decode_oracle()
+    _, bound = c_oracle.decode_sparse_v(c.opool, D, w.q_heads, w.kv_heads, c.sb, c.bt, c.lens, c.q32,
+                                        w.attn_scale, 1e-6, k_codec=k_codec, v_codec=w.v_codec)
+    for splits in (1, 0):
+        out, sk = _sparse_gpu(c, 1e-6, splits)
+        err = np.max(np.abs(out - exact), axis=2)
+        lim = ATTN_TOL * np.max(np.abs(exact), axis=2) + bound
+        _say("   splits %d: skipped %d value pages, max err %.3e" % (splits, sk, err.max()))
+        assert np.all(np.isfinite(out)) and np.all(err <= lim)
+        assert sk > 0
