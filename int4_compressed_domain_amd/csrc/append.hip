@@ -7,6 +7,11 @@
 
 namespace {
 
+// Each 16-lane group takes VPT vectors (index vec = group * VPT + i; even vec: key, odd:
+// value, of token-head vec / 2): their slots and inputs are all loaded first, so one group
+// keeps several loads in flight and a large append needs few wavefronts.
+constexpr int VPT = 4;
+
 template <int D, typename TIn, int KCODEC, int VCODEC>
 __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
                                                      const TIn* __restrict__ kin,
@@ -19,35 +24,46 @@ __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
   constexpr int VB = tq_value_bits(VCODEC);
   constexpr bool KF16 = KCODEC == TQ_CODEC_FP16;
   const int lane = threadIdx.x & 15;
-  const int64_t vec = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  if (vec >= (int64_t)n_tokens * Hkv * 2) return;  // whole 16-lane groups exit together
-  const int is_v = (int)(vec & 1);
-  const int64_t th = vec >> 1;  // token * Hkv + head
-  const int64_t tok = th / Hkv;
-  const int h = (int)(th % Hkv);
-  const int64_t slot = slots[tok];
-  if (slot < 0) return;
-
-  float y[E];
-  load_widen<TIn, E>((is_v ? vin : kin) + th * D + lane * E, y);
-  uint8_t* blk = pool + ((slot >> 4) * (int64_t)Hkv + h) * BB;
-  if (KF16 && !is_v) {  // fp16 keys: stored as given, no rotation [16-lane group uniform]
-    place_key_f16<D>(blk, (int)(slot & 15), lane, y);
-    return;
+  const int64_t nvec = (int64_t)n_tokens * Hkv * 2;
+  const int64_t vec0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * VPT;
+  if (vec0 >= nvec) return;  // whole 16-lane groups exit together
+  int64_t slot[VPT];
+  float y[VPT][E];
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t vec = vec0 + i;
+    slot[i] = -1;
+    if (vec < nvec) {
+      const int64_t th = vec >> 1;  // token * Hkv + head
+      slot[i] = slots[th / Hkv];
+      load_widen<TIn, E>(((vec & 1) ? vin : kin) + th * D + lane * E, y[i]);
+    }
   }
-  uint32_t u[E];
-  f16 scale;
   const uint32_t sw = lane_signs<D>(sign_bits, lane);
-  if (is_v) codec_vector<D, VCODEC>(y, sw, lane, u, scale);
-  else if (KCODEC == TQ_CODEC_LLOYDMAX) codec_vector<D, TQ_CODEC_LLOYDMAX>(y, sw, lane, u, scale);
-  else codec_vector<D, TQ_CODEC_ABSMAX>(y, sw, lane, u, scale);
-  place_vector<D, KF16, VB>(blk, (int)(slot & 15), lane, is_v != 0, u, scale);
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    if (slot[i] < 0) continue;  // a skipped token, or past the end: the same for the group
+    const int64_t vec = vec0 + i;
+    const int is_v = (int)(vec & 1);
+    const int h = (int)((vec >> 1) % Hkv);
+    uint8_t* blk = pool + ((slot[i] >> 4) * (int64_t)Hkv + h) * BB;
+    if (KF16 && !is_v) {  // fp16 keys: stored as given, no rotation
+      place_key_f16<D>(blk, (int)(slot[i] & 15), lane, y[i]);
+      continue;
+    }
+    uint32_t u[E];
+    f16 scale;
+    if (is_v) codec_vector<D, VCODEC>(y[i], sw, lane, u, scale);
+    else if (KCODEC == TQ_CODEC_LLOYDMAX) codec_vector<D, TQ_CODEC_LLOYDMAX>(y[i], sw, lane, u, scale);
+    else codec_vector<D, TQ_CODEC_ABSMAX>(y[i], sw, lane, u, scale);
+    place_vector<D, KF16, VB>(blk, (int)(slot[i] & 15), lane, is_v != 0, u, scale);
+  }
 }
 
 template <int D, typename T, int VC>
 hipError_t launch_v(const LaunchAppend& a, hipStream_t st) {
   const int64_t nvec = (int64_t)a.n_tokens * a.Hkv * 2;
-  dim3 grid((unsigned)((nvec + 15) / 16));
+  dim3 grid((unsigned)((nvec + 16 * VPT - 1) / (16 * VPT)));
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
   if (a.k_codec == TQ_CODEC_LLOYDMAX)
