@@ -223,7 +223,7 @@ def test_hot_cold_tail_workgroup(D, kv):
     """Few long sequences with automatic splits: the tail gets a workgroup of its own per
     (sequence, kv head) beside the pool's splits (one split fewer); checked against the
     oracle with long, short and empty tails and pools."""
-    cold = [8000, 0, 6000, 100]
+    cold = [16384, 0, 9000, 100]
     hot = [200, 256, 0, 17]
     w_outs = _hot_cold_case(D, 4, 0, cold, hot, 256, (0,), 400 + D, kv=kv)
     assert np.all(np.isfinite(w_outs[0]))
