@@ -645,3 +645,73 @@ def test_sparse_values_full_waves(D, k_codec):
         _say("   splits %d: skipped %d value pages, max err %.3e" % (splits, sk, err.max()))
         assert np.all(np.isfinite(out)) and np.all(err <= lim)
         assert sk > 0
+
+
+@pytest.mark.parametrize("D,kv,k_codec,v_codec", [(256, 4, 0, 0), (128, 8, 2, V3), (64, 8, 1, 0)])
+def test_pool_beyond_4gib(D, kv, k_codec, v_codec):
+    """A pool of more than 4.5 GiB whose used pages all lie past the first 4.5 GiB, up to its
+    last page: append, fused append+decode, decode, sparse values and the dequantize
+    reference write and read the same bytes and results as the oracle's compact pool (same
+    pages, shifted ids), and the bytes below the used pages stay untouched."""
+    lens = [3000, 1037, 16]
+    w = W.Workload("big_d%d" % D, len(lens), 4 * kv, kv, D, max(lens), "bf16", 1.0 / math.sqrt(D),
+                   k_codec=k_codec, v_codec=v_codec, dist="lognormal_spikes")
+    _say("case pool beyond 4 GiB, D", D, "kv", kv, "k_codec", k_codec, "v_codec", v_codec)
+    c = Case(w, seed=41, lens=lens)
+    pb = c.page_bytes
+    base = -(-(9 << 29) // pb)  # first used page starts at or past 4.5 GiB
+    total = base + c.npages
+    big = torch.zeros(total * pb, dtype=torch.uint8, device=DEV)
+    lay = tq.make_layout(D, w.q_heads, kv, total, c.sb_dev.data_ptr(), k_codec, v_codec)
+    bt_big = torch.from_numpy(c.bt.astype(np.int64) + base).to(torch.int32).to(DEV)
+    k_last = np.zeros((w.batch, kv, D), np.float32)
+    v_last = np.zeros_like(k_last)
+    kst, vst = np.zeros(k_last.shape, np.uint16), np.zeros(k_last.shape, np.uint16)
+    for b, L in enumerate(lens):  # every token but the last of each sequence
+        k32, v32, ks_, vs_ = W.seq_tokens(w, b, L, c.seed, c.scales)
+        slots = W.slots_for(c.bt, b, 0, L - 1)
+        tq.tq_kv_append(lay, big, to_dev(ks_[:L - 1], "bf16"), to_dev(vs_[:L - 1], "bf16"),
+                        torch.from_numpy(slots + base * 16).to(DEV))
+        c_oracle.append(c.opool, D, kv, k32[:L - 1], v32[:L - 1], slots, c.sb, k_codec, v_codec)
+        k_last[b], v_last[b], kst[b], vst[b] = k32[-1], v32[-1], ks_[-1], vs_[-1]
+        c_oracle.append(c.opool, D, kv, k32[-1:], v32[-1:], W.slots_for(c.bt, b, L - 1, L), c.sb,
+                        k_codec, v_codec)
+    maxc = max(lens)
+    ws = torch.zeros(tq.tq_decode_workspace_size(lay, w.batch, maxc, 0) // 4, dtype=torch.float32,
+                     device=DEV)
+    out = torch.full((w.batch, w.q_heads, D), float("nan"), dtype=torch.float32, device=DEV)
+    tq.tq_append_decode_attn(lay, big, to_dev(kst, "bf16"), to_dev(vst, "bf16"), c.q_dev, bt_big,
+                             c.lens_dev, maxc, w.attn_scale, out, ws)
+    out2 = torch.full_like(out, float("nan"))
+    tq.tq_decode_attn(lay, big, c.q_dev, bt_big, c.lens_dev, maxc, w.attn_scale, out2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(big[base * pb:].cpu().numpy(), c.opool), "pool bytes differ"
+    low = big[:base * pb].view(torch.int32)
+    assert int(low.max().item()) == 0 and int(low.min().item()) == 0, "bytes below the pages written"
+    del low
+    o = out.cpu().numpy()
+    assert np.array_equal(o, out2.cpu().numpy())
+    exact = c.decode_oracle()
+    err = attn_err(o, exact)
+    _say("   decode: max normwise err %.3e" % err.max())
+    assert np.all(np.isfinite(o)) and err.max() <= ATTN_TOL
+    if v_codec == 0:
+        _, bound = c_oracle.decode_sparse_v(c.opool, D, w.q_heads, kv, c.sb, c.bt, c.lens, c.q32,
+                                            w.attn_scale, 1e-6, k_codec=k_codec, v_codec=v_codec)
+        so = torch.full_like(out, float("nan"))
+        skipped = torch.zeros(1, dtype=torch.int64, device=DEV)
+        tq.tq_decode_attn_sparse_v(lay, big, c.q_dev, bt_big, c.lens_dev, maxc, w.attn_scale, 1e-6,
+                                   so, ws, v_pages_skipped=skipped)
+        torch.cuda.synchronize()
+        so = so.cpu().numpy()
+        lim = ATTN_TOL * np.max(np.abs(exact), axis=2) + bound
+        _say("   sparse values: skipped %d value pages" % int(skipped.item()))
+        assert np.all(np.isfinite(so)) and np.all(np.max(np.abs(so - exact), axis=2) <= lim)
+    ko = torch.full((w.batch, kv, maxc, D), 7.0, dtype=torch.float32, device=DEV)
+    vo = torch.full_like(ko, 7.0)
+    tq.tq_dequant_ref(lay, big, bt_big, c.lens_dev, maxc, ko, vo, to_original_basis=1)
+    torch.cuda.synchronize()
+    rk, rv = c_oracle.dequant(c.opool, D, kv, c.sb, c.bt, c.lens, maxc, 1, k_codec, v_codec)
+    assert np.array_equal(ko.cpu().numpy(), rk) and np.array_equal(vo.cpu().numpy(), rv)
+    del big, ko, vo
+    torch.cuda.empty_cache()
