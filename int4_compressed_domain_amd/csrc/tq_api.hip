@@ -52,7 +52,8 @@ int num_cus() {
 }
 
 // Context split of the fused decode: about one 16-wave workgroup (two 8-wave ones at
-// D = 256) per compute unit in total, at least one page per wave, at most TQ_MAX_SPLITS.
+// D = 256) per compute unit in total, at least four pages per wave where the context has
+// them, at most TQ_MAX_SPLITS.
 struct Split { int splits, pages_per_split; };
 
 Split make_split(int pages, int S) {
