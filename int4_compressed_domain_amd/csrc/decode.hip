@@ -340,15 +340,26 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // Aliases of the ring: the query operands live in the last slot of every wave until the
   // page loop starts; after the loop, the per-wave results and the final-merge weights.
   static_assert(G * 64 * 8 * 2 <= NW * C::SLOT, "query operands must fit one ring slot row");
-  // per-wave results: rows of D + 4 floats, so the 8 heads' rows written by one store
-  // instruction start in different LDS banks
-  constexpr int MOW = D + 4;
-  static_assert(NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4 <= NSLOT * NW * C::SLOT, "merge area must fit the ring");
-  static_assert(NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4 + 8 * (2 * D + TQ_MAX_HOT) * 4 <= NSLOT * NW * C::SLOT,
+  // per-wave results: 8 rows of MOW floats (one per head) in the wave's own ring slots, RPS
+  // rows per slot, so that a wave writes them as soon as its page loop ends, while other
+  // waves still stream pages through their slots. Rows are padded to D + 4 floats (the rows
+  // of one slot then start in different LDS banks) where the ring has room for it.
+  constexpr int RING = NSLOT * NW * C::SLOT, SCR = 8 * TQ_MAX_SPLITS * 4 + 8 * (2 * D + TQ_MAX_HOT) * 4;
+  constexpr int RPSP = C::SLOT / ((D + 4) * 4) < 8 ? C::SLOT / ((D + 4) * 4) : 8;
+  constexpr bool PAD = RPSP > 0 && ((8 + RPSP - 1) / RPSP) * NW * C::SLOT + SCR <= RING;
+  constexpr int MOW = PAD ? D + 4 : D;
+  constexpr int RPS = C::SLOT / (MOW * 4) < 8 ? C::SLOT / (MOW * 4) : 8;
+  constexpr int NRS = RPS > 0 ? (8 + RPS - 1) / RPS : NSLOT + 1;  // slot rows holding them
+  static_assert(NRS <= NSLOT, "a wave's results must fit its ring slots");
+  constexpr int MEND = NRS * NW * C::SLOT;  // ring bytes below the end of the results
+  static_assert(MEND + 8 * TQ_MAX_SPLITS * 4 <= NSLOT * NW * C::SLOT, "merge area must fit the ring");
+  static_assert(MEND + 8 * TQ_MAX_SPLITS * 4 + 8 * (2 * D + TQ_MAX_HOT) * 4 <= NSLOT * NW * C::SLOT,
                 "the fp16 tail's scratch must fit the ring");
   f16 (*bqs)[64][8] = reinterpret_cast<f16 (*)[64][8]>(&ring[NSLOT - 1][0][0]);
-  float (*mo)[8][MOW] = reinterpret_cast<float (*)[8][MOW]>(&ring[0][0][0]);
-  float (*wsh)[TQ_MAX_SPLITS] = reinterpret_cast<float (*)[TQ_MAX_SPLITS]>(&ring[0][0][0] + NW * 8 * MOW * 4);
+  auto mo = [&](int w, int hd) -> float* {  // row of head hd in wave w's results
+    return reinterpret_cast<float*>(&ring[hd / RPS][w][(hd % RPS) * MOW * 4]);
+  };
+  float (*wsh)[TQ_MAX_SPLITS] = reinterpret_cast<float (*)[TQ_MAX_SPLITS]>(&ring[0][0][0] + MEND);
 
   // ---- page ids of this split and this wave's query head, loaded together ------------------
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
@@ -392,6 +403,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int wc = NW - 1, wl = (plast - p0) % NW;
   float ynew[E];
   uint32_t swnew = 0;
+  int pid_last = 0;  // wave wc: physical id of the last page, for the token's store to the pool
+  if (app && wv == wc) pid_last = bt[plast];
   if (app && wv == wc && lane < 32) {
     swnew = lane_signs<D>(a.sign_bits, lane & 15);
     const int64_t off = ((int64_t)b * a.Hkv + h) * D + (lane & 15) * E;
@@ -403,6 +416,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     for (int e = 0; e < E; e++) asm volatile("" ::"v"(ynew[e]));  // before any page load
     asm volatile("" ::"v"(swnew));
   }
+  if (app && wv == wc) asm volatile("" ::"v"(pid_last));
   // consume the page ids here, before any page is in flight: otherwise the compiler waits
   // for them (vmcnt(0), i.e. for every in-flight page too) where they are first read
 #pragma unroll
@@ -921,7 +935,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 
   __builtin_amdgcn_s_setprio(0);
   if (app && wv == wc)  // the appended token goes to the pool too, for later calls
-    copy_token(const_cast<uint8_t*>(a.pool) + ((int64_t)__builtin_amdgcn_readfirstlane(bt[plast]) * a.Hkv + h) * BB, false);
+    copy_token(const_cast<uint8_t*>(a.pool) + ((int64_t)__builtin_amdgcn_readfirstlane(pid_last) * a.Hkv + h) * BB, false);
 
   // ---- epilogue: merge the waves of this workgroup -----------------------------------------
   l_run = sum_xor16(l_run);
@@ -934,13 +948,13 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     acc[2 * g] *= 16777216.0f;
     acc[2 * g + 1] *= 1048576.0f;
   }
-  __syncthreads();  // every wave is done with its ring: reuse it as the merge area
-  if (SPV && tid == 0 && a.v_skipped && wskip > 0) atomicAdd(a.v_skipped, (unsigned long long)wskip);
+  // This wave's page loop is over, so its ring slots are free: its results go there now,
+  // while the other waves may still be streaming pages through theirs.
   if (hr < 8) {
 #pragma unroll
     for (int g = 0; g < G; g++) {
       // dims 32g + 8jq + 0..7: even dims from acc[2g], odd from acc[2g+1]
-      float* dst = &mo[wv][hr][32 * g + 8 * jq];
+      float* dst = mo(wv, hr) + 32 * g + 8 * jq;
       const f32x4 lo4 = {acc[2 * g][0], acc[2 * g + 1][0], acc[2 * g][1], acc[2 * g + 1][1]};
       const f32x4 hi4 = {acc[2 * g][2], acc[2 * g + 1][2], acc[2 * g][3], acc[2 * g + 1][3]};
       *reinterpret_cast<f32x4*>(dst) = lo4;
@@ -951,7 +965,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       mml[wv][hr][1] = l_run;
     }
   }
-  __syncthreads();
+  __syncthreads();  // every wave's results are in
+  if (SPV && tid == 0 && a.v_skipped && wskip > 0) atomicAdd(a.v_skipped, (unsigned long long)wskip);
   if (tid < 128) {  // per head, one row of 16 lanes (lane = wave): weights 2^(m_w - M)
     const int hd = tid >> 4, w = tid & 15;   // into mml[w][hd][0], and the sum l
     const bool on = hd < r && w < NW;
@@ -976,7 +991,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     // query as given, p = 2^(s - M_t) in the log2 domain as the pages' scores, values summed
     // in the original basis and rotated into the cache basis (sign flip, butterflies, rho),
     // then joined to the pages' result of this workgroup by the usual max/rescale rule.
-    float* qs = reinterpret_cast<float*>(&ring[0][0][0] + NW * 8 * MOW * 4 + 8 * TQ_MAX_SPLITS * 4);
+    float* qs = reinterpret_cast<float*>(&ring[0][0][0] + MEND + 8 * TQ_MAX_SPLITS * 4);
     float* ps = qs + 8 * D;           // [8][TQ_MAX_HOT] scores, then weights
     float* pw = ps + 8 * TQ_MAX_HOT;  // [8][D] the pages' part: sum over waves of f_w o_w
     const int64_t qh = ((int64_t)b * a.Hq + (int64_t)h * r) * D;
@@ -1027,7 +1042,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
         float o = 0.0f;
         if (hd < r) {
 #pragma unroll
-          for (int w = 0; w < NW; w++) o += mml[w][hd][0] * mo[w][hd][d];
+          for (int w = 0; w < NW; w++) o += mml[w][hd][0] * mo(w, hd)[d];
         }
         pw[i] = o;
         qs[i] = qx[k];
@@ -1109,7 +1124,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       if (j == 0) {
 #pragma unroll
         for (int hd = 0; hd < 8; hd++)
-          if (hd < r) *reinterpret_cast<f32x4*>(&mo[wv][hd][4 * c]) = f32x4{acc[hd][0], acc[hd][1], acc[hd][2], acc[hd][3]};
+          if (hd < r) *reinterpret_cast<f32x4*>(mo(wv, hd) + 4 * c) = f32x4{acc[hd][0], acc[hd][1], acc[hd][2], acc[hd][3]};
       }
     }
     __syncthreads();
@@ -1119,7 +1134,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       for (int k = 0; k < V; k++) {
         const int d = lane + 64 * k;
         float o = 0.0f;
-        for (int w = 0; w < NW; w++) o += mo[w][wv][d];
+        for (int w = 0; w < NW; w++) o += mo(w, wv)[d];
         x[k] = ((sgn_s[d >> 5] >> (d & 31)) & 1u) ? -o : o;
       }
       wave_fwht<V>(x, lane);
@@ -1130,7 +1145,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
       for (int k = 0; k < V; k++) {
         const int d = lane + 64 * k;
-        mo[0][wv][d] = cp * pw[wv * D + d] + ct * (x[k] * rho);
+        mo(0, wv)[d] = cp * pw[wv * D + d] + ct * (x[k] * rho);
       }
       if (lane == 0) {
         hml[wv][0] = M;
@@ -1142,7 +1157,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     __syncthreads();
   }
   // fin: [ngf][r][D] partial sums of the result (rotated basis), summed by the rotation below
-  float* fin = &mo[0][0][0];
+  float* fin = reinterpret_cast<float*>(&ring[0][0][0]);
   int ngf = 1;
   const int S = a.splits + a.hot_wg;  // partial rows per unit
   const int64_t prow = ((int64_t)u * S + srow) * r;  // partial rows of this (unit, split)
@@ -1156,7 +1171,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
         const int hd = i / D, d = i % D;
 #pragma unroll
         for (int w = 0; w < NW; w++)
-          if (w < nwsum) o += mml[w][hd][0] * mo[w][hd][d];
+          if (w < nwsum) o += mml[w][hd][0] * mo(w, hd)[d];
         o /= hml[hd][1];
       }
       ov[j] = o;
@@ -1171,7 +1186,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       float o = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; w++)
-        if (w < nwsum) o += mml[w][hd][0] * mo[w][hd][d];
+        if (w < nwsum) o += mml[w][hd][0] * mo(w, hd)[d];
       __hip_atomic_store(&a.part_o[(prow + hd) * D + d], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (d == 0) {
         __hip_atomic_store(&a.part_ml[2 * (prow + hd)], hml[hd][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1189,7 +1204,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     if (tid == 0) __hip_atomic_store(&a.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // ---- the last workgroup of unit u merges every split (coherent sc1 loads) ----------
     // thread = (split group grp, head hd, 4 dims d4); split group grp takes splits
-    // grp, grp + ngrp, ...; the first NLD of them are loaded before the weights are known
+    // grp, grp + ngrp, ...; the first NLD of them are loaded before the weights are known.
+    // Wave hd (< r) first loads the (m, l) of every split of head hd (lanes over splits), so
+    // that they arrive ahead of the partials and the weights 2^(m_t - M) / sum_t 2^(m_t - M) l_t
+    // are computed while the partials are still loading.
     const int64_t row0 = (int64_t)u * S * r;
     __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, (short)0, S * r * D * 4, 0x00020000);
     constexpr int D4 = D / 4;
@@ -1197,20 +1215,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     ngf = ngrp;
     const bool act = tid < ngrp * r * D4;
     const int grp = tid / (r * D4), hd = (tid / D4) % r, d4 = tid % D4;
-    constexpr int NLD = 16;  // split loads in flight per thread
-    f32x4 v[NLD];
-    if (act) {
-#pragma unroll
-      for (int k = 0; k < NLD; k++) {
-        const int t = min(grp + k * ngrp, ns - 1);
-        v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, ((t * r + hd) * D + 4 * d4) * 4, 0, 16));
-      }
-    }
-    // wave hd (< r) turns the (m, l) of every split of head hd into merge weights
-    // 2^(m_t - M) / sum_t 2^(m_t - M) l_t (lanes over splits), while the partials load
+    constexpr int TPL = TQ_MAX_SPLITS / 64;  // splits per lane
+    float m[TPL], l[TPL];
     if (wv < r) {
-      constexpr int TPL = TQ_MAX_SPLITS / 64;  // splits per lane
-      float m[TPL], l[TPL];
 #pragma unroll
       for (int q = 0; q < TPL; q++) {
         const int t = lane + 64 * q;
@@ -1221,6 +1228,19 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
           l[q] = __hip_atomic_load(&a.part_ml[2 * (row0 + (int64_t)t * r + wv) + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
+    }
+    // Partials of split t, or zero for t >= ns and inactive threads: an offset past the
+    // descriptor's range reads nothing and returns zeros. The loads stay unconditional, so
+    // that waiting for the (m, l) loads above does not wait for them too.
+    constexpr int NLD = 16;  // split loads in flight per thread
+    auto load_part = [&](int t) {
+      const uint32_t off = (act && t < ns) ? (uint32_t)(((t * r + hd) * D + 4 * d4) * 4) : 0x80000000u;
+      return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 16));
+    };
+    f32x4 v[NLD];
+#pragma unroll
+    for (int k = 0; k < NLD; k++) v[k] = load_part(grp + k * ngrp);
+    if (wv < r) {
       float M = m[0];
 #pragma unroll
       for (int q = 1; q < TPL; q++) M = fmaxf(M, m[q]);
@@ -1244,10 +1264,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
         if (grp + k * ngrp < ns) o4 += wsh[hd][grp + k * ngrp] * v[k];
       for (int t0 = grp + NLD * ngrp; t0 < ns; t0 += NLD * ngrp) {  // more splits per group
 #pragma unroll
-        for (int k = 0; k < NLD; k++) {
-          const int t = min(t0 + k * ngrp, ns - 1);
-          v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, ((t * r + hd) * D + 4 * d4) * 4, 0, 16));
-        }
+        for (int k = 0; k < NLD; k++) v[k] = load_part(t0 + k * ngrp);
 #pragma unroll
         for (int k = 0; k < NLD; k++)
           if (t0 + k * ngrp < ns) o4 += wsh[hd][t0 + k * ngrp] * v[k];
