@@ -6,7 +6,7 @@
 // Work unit u = (sequence b, kv head h); its pages are cut into S context splits, one
 // workgroup of NW wavefronts per (u, split). Workgroup order is XCD-aware: MI355X hands
 // consecutive workgroups to its 8 XCDs in turn, so all splits of unit u are placed on XCD
-// u mod 8 and the partials they exchange stay in that XCD's L2.
+// u mod 8, where one L2 holds the unit's query, block-table row and partials.
 //
 //  prologue  the r = Hq/Hkv queries of head h are rotated into the cache basis with the same
 //            fp32 butterfly as the keys (fp16 keys: not rotated), scaled by alpha*log2(e)
@@ -28,10 +28,12 @@
 //                    first rebuilt into the 4-bit layout); P' = p * s_V rounded once to
 //                    fp16 is the B operand, one 16x16x32 MFMA per group and dim parity for
 //                    both pages, and a second one with a constant A removes the offset.
-//  epilogue  the NW waves merge through LDS (an fp16 tail's slice joins here); with one
-//            split the workgroup finishes the head, otherwise it stores its partial
-//            (o', m, l), and the last workgroup of the unit to arrive (atomic counter, reset
-//            afterwards) merges all splits. The result is rotated back (fp32 butterfly,
+//  epilogue  each wave writes its (o', m, l) into its own ring slots as soon as its loop
+//            ends; after one barrier the NW waves merge through LDS (an fp16 tail's slice
+//            joins here). With one split the workgroup finishes the head, otherwise it
+//            stores its partial (o', m, l), and the last workgroup of the unit to arrive
+//            (atomic counter, reset afterwards) merges all splits: every split's (m, l)
+//            first, the partials behind them. The result is rotated back (fp32 butterfly,
 //            times rho, times sigma) and written.
 // Variants: the fused append of each sequence's newest token (knew/vnew), sparse values in
 // two passes (SPV), an fp16 tail (hot_k/hot_v).
