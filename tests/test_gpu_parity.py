@@ -321,6 +321,23 @@ def test_split_count_invariance():
         assert attn_err(o, ref).max() <= ATTN_TOL
 
 
+@pytest.mark.parametrize("D,r", [(128, 8), (256, 2), (64, 4)])
+def test_most_splits(D, r):
+    """The largest split count (128 splits of 2 pages): the last workgroup merges the
+    partials in several rounds of loads; within 2^-11 of one split and within the tolerance
+    of the oracle. A second sequence of 33 tokens (3 pages) uses 2 of the 128 splits."""
+    w = W.Workload("most_splits_d%d" % D, 2, 2 * r, 2, D, 4096, "bf16", 1.0 / math.sqrt(D),
+                   dist="lognormal_spikes")
+    _say("case most splits D", D, "r", r)
+    c = Case(w, seed=37, lens=[4096, 33])
+    c.fill()
+    one, most = c.decode_gpu(num_splits=1), c.decode_gpu(num_splits=128)
+    assert attn_err(most, one).max() < 2.0 ** -11
+    err = attn_err(most, c.decode_oracle())
+    _say("   max normwise err %.3e" % err.max())
+    assert np.all(np.isfinite(most)) and err.max() <= ATTN_TOL
+
+
 def test_negative_slots_and_untouched_bytes():
     w = W.WORKLOADS["llama8b_b16_8k"].scaled(context=64, batch=1)
     c = Case(w, seed=2)
