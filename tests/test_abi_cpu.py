@@ -208,6 +208,10 @@ def test_lut_constant_matches_product_generator():
     block = text[text.index("#define TQ_LUT16_BITS"):]
     bits = [int(x, 16) for x in re.findall(r"0x([0-9a-f]{4})u", block)[:16]]
     assert bits == gen_lloydmax.lut_bits()
+    # and the tabulated fp16 values of the scaled Gaussian codebook (positive half; the
+    # negative half is the same with the sign bit set)
+    pos = [0x25CF, 0x2C64, 0x2F6E, 0x3155, 0x331B, 0x3494, 0x35DA, 0x37BB]
+    assert bits == [b | 0x8000 for b in pos[::-1]] + pos
 
 
 def test_algorithmic_bytes_of_the_measured_workloads():

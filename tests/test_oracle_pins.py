@@ -212,9 +212,9 @@ def test_lloydmax_matches_textbook(orc):
     from scipy import integrate
     t = np.concatenate(([-np.inf], 0.5 * (m[1:] + m[:-1]), [np.inf]))
     pdf = lambda x: np.exp(-x * x / 2) / math.sqrt(2 * math.pi)
-    for j in (0, 5, 8, 15):
-        num = integrate.quad(lambda x: x * pdf(x), t[j], t[j + 1])[0]
-        den = integrate.quad(pdf, t[j], t[j + 1])[0]
+    for j in range(16):
+        num = integrate.quad(lambda x: x * pdf(x), t[j], t[j + 1], epsabs=1e-14, epsrel=1e-13)[0]
+        den = integrate.quad(pdf, t[j], t[j + 1], epsabs=1e-14, epsrel=1e-13)[0]
         assert abs(num / den - m[j]) < 1e-9
 
 
@@ -228,6 +228,32 @@ def test_lut_is_fp16_of_scaled_centroids(orc):
     lut = _lut_of(orc)
     assert np.array_equal(lut, (m / math.sqrt(32)).astype(np.float16))
     assert np.array_equal(lut[8:].astype(np.float64), -lut[7::-1].astype(np.float64))
+
+
+# fp16 bits of the positive codebook entries 8..15 (entries 0..7 are their negatives with
+# the sign bit set), as tabulated from an independent fp64 Lloyd iteration of the 16-level
+# Gaussian quantizer divided by sqrt(32) ("TurboQuant on AMD GPUs", section 2: keys by
+# rotation plus a lookup table).
+LUT16_POS_BITS = [0x25CF, 0x2C64, 0x2F6E, 0x3155, 0x331B, 0x3494, 0x35DA, 0x37BB]
+
+
+def test_lut_bits_are_the_tabulated_values(orc):
+    """The oracle's codebook, bit for bit, equals the tabulated fp16 values."""
+    bits = _lut_of(orc).view(np.uint16)
+    assert [int(b) for b in bits[8:]] == LUT16_POS_BITS
+    assert [int(b) for b in bits[:8]] == [b | 0x8000 for b in LUT16_POS_BITS[::-1]]
+
+
+def test_lut_bits_are_decided_by_the_pinned_levels(orc):
+    """Every scaled level sits far (> 1e-7 relative) from an fp16 rounding boundary, so the
+    1e-9 fixed-point pin above determines each fp16 entry: no plausible error in the
+    levels could flip a bit."""
+    m, _ = orc.lloydmax16()
+    for x in m[8:] / math.sqrt(32):
+        h = np.float16(x)
+        ulp = float(np.spacing(h))
+        frac = (x - float(h)) / ulp          # in (-0.5, 0.5) for round-to-nearest
+        assert abs(abs(frac) - 0.5) * ulp > 1e-7 * x
 
 
 def _lut_groups(orc, y):
