@@ -37,6 +37,8 @@
 //            times rho, times sigma) and written.
 // Variants: the fused append of each sequence's newest token (knew/vnew), sparse values in
 // two passes (SPV), an fp16 tail (hot_k/hot_v).
+#include <type_traits>
+
 #include "tq_codec.h"
 #include "tq_internal.h"
 
@@ -96,6 +98,29 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
                ::"v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory");
+}
+
+// NB bytes per lane (4, 8, 16 or 32, naturally aligned) into dwords w[0 .. NB/4), with
+// non-temporal loads: each page is read once, so it should not displace other data in the
+// caches (on MI355X a stream read this way runs ~15% faster than with default loads).
+template <int NB>
+__device__ __forceinline__ void ld_nt(const uint8_t* p, uint32_t* w) {
+  if constexpr (NB == 4) {
+    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  } else if constexpr (NB == 8) {
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    w[0] = x[0];
+    w[1] = x[1];
+  } else {
+#pragma unroll
+    for (int c = 0; c < NB / 16; c++) {
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + c);
+      w[4 * c] = x[0];
+      w[4 * c + 1] = x[1];
+      w[4 * c + 2] = x[2];
+      w[4 * c + 3] = x[3];
+    }
+  }
 }
 
 // Stage one page (one kv head's block) into an LDS slot:
@@ -289,6 +314,17 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   constexpr int NSLOT = (147456 / (NW * C::SLOT)) < 8 ? (147456 / (NW * C::SLOT)) : 8;
   static_assert(NSLOT >= 3, "ring too small");
   constexpr bool KSUB = (KCODEC == TQ_CODEC_ABSMAX);
+  // Register streaming: a page's K and V index dwords are loaded straight into the VGPRs
+  // that feed the MFMAs (lane l's bytes of each region are that lane's operand) and its
+  // scale block goes to a per-wave LDS slot; other variants stage whole pages in LDS by
+  // LDS-DMA. On MI355X the register path streams pages at ~6.2 TB/s, the LDS-DMA path at
+  // ~4.5 TB/s (same pages, no compute).
+  constexpr bool REG = !KF16 && !SPV && VB == 4 && D <= 128;
+  constexpr int SW = (C::SCB / 4 + 63) / 64;  // scale dwords per lane of a page (register path)
+  constexpr int RG = REG ? G : 1;             // index dwords per lane of a page region
+  constexpr int PPS = TQ_REG_PAGES_PER_STEP;  // register path: pages per step (2 or 4)
+  constexpr int NPR = PPS / 2;                // page pairs per step
+  static_assert(!REG || 2 * PPS * C::SCB <= C::SLOT, "the scale blocks of both page sets in one ring slot");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar page loads
   const int jq = lane >> 4, hr = lane & 15, hl = hr & 7;
@@ -380,16 +416,16 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   }
   const uint32_t sgn_word = tid < D / 32 ? a.sign_bits[tid] : 0u;
   constexpr int PPL = (TQ_MAX_SPLIT_PAGES / NW + 63) / 64;
-  int vpid[PPL];
+  static_assert(PPL <= 4, "page ids of a wave: at most four registers");
+  // held in a vector value, not an array: the selection below must stay in registers (as
+  // an array it was turned into an indexed access and the ids were moved to LDS, one
+  // waited-for load at a time)
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  i32x4 vpid = {0, 0, 0, 0};
 #pragma unroll
   for (int k = 0; k < PPL; k++) vpid[k] = (lane + 64 * k < npw) ? bt[p0 + wv + NW * (lane + 64 * k)] : 0;
   auto page_blk = [&](int n) {  // wave-uniform address of page n's block for head h
-    int id = vpid[0];
-    if constexpr (PPL > 1) {
-#pragma unroll
-      for (int k = 1; k < PPL; k++)
-        if ((n >> 6) == k) id = vpid[k];
-    }
+    const int id = PPL > 1 ? vpid[(n >> 6) & (PPL - 1)] : vpid[0];
     return hbase + (int64_t)__builtin_amdgcn_readlane(id, n & 63) * pstride;
   };
   // LDS byte address of ring slot k of this wave
@@ -460,6 +496,29 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       }
     }
   };
+  // Register path: two page sets of four pages, X (step st) and Y (step st + 1), one being
+  // computed while the other is in flight. A page n >= npw is a dummy load of one 16-byte
+  // line (every lane the same address in the wave's last page), so that every step issues
+  // the same loads and the compiler's vmcnt waits stay exact.
+  uint32_t xk[PPS][RG], xv[PPS][RG], xs[PPS][SW], yk[PPS][RG], yv[PPS][RG], ys[PPS][SW];
+  auto ldp = [&](int n, uint32_t (&k)[RG], uint32_t (&v)[RG], uint32_t (&sw)[SW]) {
+    if constexpr (REG) {
+      const bool real = n < npw;
+      const uint8_t* blk = page_blk(real ? n : npw - 1);
+      const uint32_t lo = real ? (uint32_t)lane * C::KB : 0u;
+      ld_nt<C::KB>(blk + lo, k);
+      ld_nt<C::KB>(blk + C::BV + lo, v);
+#pragma unroll
+      for (int i = 0; i < SW; i++) {
+        const int dw = real ? min(64 * i + lane, C::SCB / 4 - 1) : 0;
+        ld_nt<4>(blk + C::BS + 4 * dw, &sw[i]);
+      }
+    }
+  };
+  auto ldstep = [&](int st, uint32_t (&k)[PPS][RG], uint32_t (&v)[PPS][RG], uint32_t (&sw)[PPS][SW]) {
+#pragma unroll
+    for (int i = 0; i < PPS; i++) ldp(PPS * st + i, k[i], v[i], sw[i]);
+  };
   if (app && wv == wc && lane < 32) {  // quantize the appended token before this wave's
     uint32_t un[E];                     // first page loads, which may wait for queue space
     f16 scn;
@@ -472,7 +531,19 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       place_vector<D, KF16, VB>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
     }
   }
-  stage_first();  // (the query operands go to the last slot, which these loads do not use)
+  // Register path: only the first pages are requested before the query is prepared. A
+  // wave's loads issue in order, and more than the memory pipeline holds would stall it at
+  // the load instructions, holding back the rotation and the barriers behind them (all
+  // eight pages up front: the prologue ended 6 to 20 us into the launch instead of ~5).
+  constexpr int EARLY = TQ_REG_EARLY < PPS ? TQ_REG_EARLY : PPS;
+  if constexpr (REG) {
+    if (npw > 0) {
+#pragma unroll
+      for (int i = 0; i < EARLY; i++) ldp(i, xk[i], xv[i], xs[i]);
+    }
+  } else {
+    stage_first();  // (the query operands go to the last slot, which these loads do not use)
+  }
 
   // ---- prologue: rotate, scale, power-of-two prescale per head ----------------------------
   // Wave w (< r) holds query head w: after the butterflies and scaling it writes the fp16
@@ -530,6 +601,13 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     cinit[g] = KSUB ? -__builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, bq[g], zero4, 0, 0, 0)[0] : 0.0f;
   }
   __syncthreads();  // every wave holds its operands: the last ring slot is free again
+  if constexpr (REG) {  // the rest of the first two steps' pages
+    if (npw > 0) {
+#pragma unroll
+      for (int i = EARLY; i < PPS; i++) ldp(i, xk[i], xv[i], xs[i]);
+      ldstep(1, yk, yv, ys);
+    }
+  }
   uint32_t tlo[4] = {0, 0, 0, 0}, thi[4] = {0, 0, 0, 0};
   if constexpr (KCODEC == TQ_CODEC_LLOYDMAX) {
     const uint16_t lb[16] = TQ_LUT16_BITS;
@@ -632,21 +710,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   auto scale_of = [](const uint32_t (&st)[2 * G], int e, int g) {
     return (float)as_h2(st[(e * G + g) >> 1])[(e * G + g) & 1];
   };
-  // one page's partial scores in every lane (column hr: hi or lo part)
-  auto scores = [&](const uint8_t* slot, float (&sc)[4], int kso = C::SOFF) {  // kso: K scales
-    if constexpr (KF16) {  // fp16 keys are the A operand as staged; one accumulator
-      f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int g = 0; g < G; g++)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const f16x8*>(slot + 1024 * g + lane * 16),
-                                                    bq[g], c, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; e++) sc[e] = c[e];
-      return;
-    }
-    uint32_t kw[G], kst[2 * G];
-    load_idx(slot, kw, 0);
-    load_scales(slot, kst, 0, kso);
+  // one page's partial scores in every lane (column hr: hi or lo part), from its K index
+  // dwords and the K scales at sbase + kso
+  auto scores_w = [&](const uint32_t (&kw)[G], const uint8_t* sbase, int kso, float (&sc)[4]) {
+    uint32_t kst[2 * G];
+    load_scales(sbase, kst, 0, kso);
 #pragma unroll
     for (int e = 0; e < 4; e++) sc[e] = 0.0f;
 #pragma unroll
@@ -657,12 +725,28 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(scale_of(kst, e, g), c[e], sc[e]);
     }
   };
+  // the same for a page staged in an LDS slot (K scales at slot + kso)
+  auto scores = [&](const uint8_t* slot, float (&sc)[4], int kso = C::SOFF) {
+    if constexpr (KF16) {  // fp16 keys are the A operand as staged; one accumulator
+      f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int g = 0; g < G; g++)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const f16x8*>(slot + 1024 * g + lane * 16),
+                                                    bq[g], c, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; e++) sc[e] = c[e];
+      return;
+    }
+    uint32_t kw[G];
+    load_idx(slot, kw, 0);
+    scores_w(kw, slot, kso, sc);
+  };
 
-  auto step = [&](const uint8_t* slotA, const uint8_t* slotB, int pa, int pb) {
+  // One step over pages A and B from their partial scores (sA, sB); vidx(vwA, vwB) fetches
+  // their V index dwords, the V scales are read from svA / svB + svoff (the lane's own page).
+  auto step_core = [&](const float (&sA)[4], const float (&sB)[4], auto&& vidx, const uint8_t* svA,
+                       const uint8_t* svB, int svoff, int pa, int pb) {
     float sc[4];
-    float sA[4], sB[4];
-    scores(slotA, sA);
-    scores(slotB, sB);
     // own page's hi (or lo) part plus the partner lane's part of the same page
 #pragma unroll
     for (int e = 0; e < 4; e++) {
@@ -671,7 +755,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       sc[e] = own + dpp_ror8(sup);
     }
     uint32_t vst[2 * G];  // V scales of this lane's page
-    load_scales(hiLane ? slotA : slotB, vst, 1);
+    load_scales(hiLane ? svA : svB, vst, 1, svoff);
     if (pa == ptail || pb == ptail || pb >= p1) {  // wave-uniform: a partial or missing page
       const int pm = hiLane ? pa : pb;
       const int lim = (pm >= p1) ? 0 : (pm == ptail ? ltail : 16);
@@ -702,8 +786,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
     uint32_t vwA[G], vwB[G];
-    load_idx(slotA, vwA, 1);
-    load_idx(slotB, vwB, 1);
+    vidx(vwA, vwB);
     auto vsc = [&](int e, int g) { return (float)as_h2(vst[(e * G + g) >> 1])[(e * G + g) & 1]; };
 #pragma unroll
     for (int g = 0; g < G; g++) {
@@ -722,6 +805,96 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ceven, P, acc[2 * g], 0, 0, 0);
       acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, P, acc[2 * g + 1], 0, 0, 0);
       acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codd, P, acc[2 * g + 1], 0, 0, 0);
+    }
+  };
+  // a step over two pages staged in LDS slots
+  auto step = [&](const uint8_t* slotA, const uint8_t* slotB, int pa, int pb) {
+    float sA[4], sB[4];
+    scores(slotA, sA);
+    scores(slotB, sB);
+    step_core(sA, sB, [&](uint32_t (&wa)[G], uint32_t (&wb)[G]) {
+      load_idx(slotA, wa, 1);
+      load_idx(slotB, wb, 1);
+    }, slotA, slotB, C::SOFF, pa, pb);
+  };
+  // Register path, one step over PPS pages held in registers: pairs (0, 1), (2, 3), ...,
+  // each finished as in step_core (lanes with hr < 8 the first page of a pair, the others
+  // the second); the running max is updated once per step. ss: the pages' scale blocks in
+  // LDS, pa0: the global number of page 0 (pages pa0 + NW i).
+  auto stepN = [&](const uint32_t (&kk)[PPS][RG], const uint32_t (&vv)[PPS][RG], const uint8_t* ss, int pa0) {
+    if constexpr (REG) {
+      float s4[PPS][4];
+#pragma unroll
+      for (int i = 0; i < PPS; i++) scores_w(kk[i], ss + i * C::SCB, 0, s4[i]);
+      float sc[NPR][4];
+      uint32_t vst[NPR][2 * G];  // V scales of this lane's page of each pair
+#pragma unroll
+      for (int j = 0; j < NPR; j++) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float own = hiLane ? s4[2 * j][e] : s4[2 * j + 1][e];
+          const float sup = hiLane ? s4[2 * j + 1][e] : s4[2 * j][e];
+          sc[j][e] = own + dpp_ror8(sup);
+        }
+        load_scales(ss + (hiLane ? 2 * j : 2 * j + 1) * C::SCB, vst[j], 1, 0);
+      }
+      if (pa0 + (PPS - 1) * NW >= p1 || (ptail >= pa0 && ptail <= pa0 + (PPS - 1) * NW)) {  // wave-uniform
+#pragma unroll
+        for (int j = 0; j < NPR; j++) {
+          const int pm = pa0 + NW * (hiLane ? 2 * j : 2 * j + 1);
+          const int lim = (pm >= p1) ? 0 : (pm == ptail ? ltail : 16);
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (4 * jq + e >= lim) {
+              sc[j][e] = -INFINITY;
+#pragma unroll
+              for (int g = 0; g < G; g += 2) vst[j][(e * G + g) >> 1] = 0u;  // may hold garbage
+            }
+        }
+      }
+      float cm = vmax3(sc[0][0], sc[0][1], vmax(sc[0][2], sc[0][3]));
+#pragma unroll
+      for (int j = 1; j < NPR; j++) cm = vmax3(cm, vmax3(sc[j][0], sc[j][1], sc[j][2]), sc[j][3]);
+      cm = max_xor16(cm);
+      cm = max_xor32(cm);
+      cm = vmax(cm, dpp_ror8(cm));
+      if (__any(cm > m_run)) {
+        const float mn = fmaxf(m_run, cm);
+        const float f = __builtin_amdgcn_exp2f((m_run - mn) * down);  // 2^-inf = 0
+        l_run *= f;
+#pragma unroll
+        for (int t = 0; t < 2 * G; t++) acc[t] *= f;
+        m_run = mn;
+        nmd = -mn * down;
+      }
+      float pr[NPR][4];
+#pragma unroll
+      for (int j = 0; j < NPR; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) pr[j][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j][e], down, nmd));
+#pragma unroll
+      for (int j = 0; j < NPR; j++) l_run += (pr[j][0] + pr[j][1]) + (pr[j][2] + pr[j][3]);
+#pragma unroll
+      for (int j = 0; j < NPR; j++) {
+        auto vsc = [&](int e, int g) { return (float)as_h2(vst[j][(e * G + g) >> 1])[(e * G + g) & 1]; };
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+          // P' as in step_core: this lane's page in k-slots 0..3 (own) or 4..7 (partner)
+          const f16x4 own = {(f16)__builtin_fmaf(pr[j][0], vsc(0, g), 0.0f), (f16)__builtin_fmaf(pr[j][2], vsc(2, g), 0.0f),
+                             (f16)__builtin_fmaf(pr[j][1], vsc(1, g), 0.0f), (f16)__builtin_fmaf(pr[j][3], vsc(3, g), 0.0f)};
+          const u32x2 o2 = __builtin_bit_cast(u32x2, own);
+          const uint32_t x0 = __builtin_amdgcn_mov_dpp(o2[0], 0x128, 0xf, 0xf, true);
+          const uint32_t x1 = __builtin_amdgcn_mov_dpp(o2[1], 0x128, 0xf, 0xf, true);
+          const f16x8 P = __builtin_bit_cast(f16x8, u32x4{o2[0], o2[1], x0, x1});
+          const uint32_t a = vv[2 * j][g], a8 = a >> 8, bw = vv[2 * j + 1][g], b8 = bw >> 8;
+          const f16x8 Ae = __builtin_bit_cast(f16x8, u32x4{a & 0x000F000Fu, a8 & 0x000F000Fu, bw & 0x000F000Fu, b8 & 0x000F000Fu});
+          const f16x8 Ao = __builtin_bit_cast(f16x8, u32x4{a & 0x00F000F0u, a8 & 0x00F000F0u, bw & 0x00F000F0u, b8 & 0x00F000F0u});
+          acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, P, acc[2 * g], 0, 0, 0);
+          acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ceven, P, acc[2 * g], 0, 0, 0);
+          acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, P, acc[2 * g + 1], 0, 0, 0);
+          acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codd, P, acc[2 * g + 1], 0, 0, 0);
+        }
+      }
     }
   };
 
@@ -827,7 +1000,18 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // first steps (at most 4 issues per step) instead of in one burst that would stall the
   // prologue behind a full memory queue.
   int nis = min(npw, 2);
+  // Keep the waves abreast on long loops. The hardware lets the oldest waves issue first, so
+  // the youngest ones otherwise finish last, alone on their SIMDs and with too few pages in
+  // flight. A wave that lags the furthest one (by page-loop step) takes issue priority.
   const bool balance = npw >= 32;
+  auto balance_step = [&](int na) {
+    int lead = 0;
+    if (lane == 0) lead = atomicMax(&lead_n, na);
+    const int lag = __builtin_amdgcn_readfirstlane(lead) - na;
+    if (lag >= 4) __builtin_amdgcn_s_setprio(3);
+    else if (lag >= 2) __builtin_amdgcn_s_setprio(2);
+    else __builtin_amdgcn_s_setprio(0);
+  };
   if constexpr (SPV) {
     // Sparse values [mlxcel manual, sparse-V threshold]. Pass 1 streams the keys of every
     // page of this wave (exact running max and sum, page maxima). The workgroup's maximum
@@ -903,20 +1087,77 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     l_run = l_all;
     if (lane == 0 && nskip > 0) atomicAdd(&wskip, nskip);  // (one global add per workgroup below)
+  } else if constexpr (REG) {
+    // Register path: step st over the X set, step st + 1 over the Y set; each set is
+    // reloaded (two steps ahead) as soon as its step is done. Scale blocks: 2 PPS per wave
+    // (X first, then Y) in the wave's first ring slot.
+    uint8_t* const ssw = &ring[0][wv][0];
+    auto put_scales = [&](uint8_t* ss, const uint32_t (&sw)[PPS][SW]) {
+#pragma unroll
+      for (int i = 0; i < PPS; i++)
+#pragma unroll
+        for (int c = 0; c < SW; c++)
+          if (64 * c + lane < C::SCB / 4) reinterpret_cast<uint32_t*>(ss + i * C::SCB)[64 * c + lane] = sw[i][c];
+    };
+    // The appended token (block layout in tokblk) into the registers of the page that holds
+    // it: lane l holds the K index dwords of token l % 16, in byte e of each V index dword
+    // the token 4 (l / 16) + e, and scale dword l (and 64 + l) of the block, whose two
+    // halves belong to one token.
+    auto patch_regs = [&](uint32_t (&k)[RG], uint32_t (&v)[RG], uint32_t (&sw)[SW]) {
+      if ((lane & 15) == tnew) {
+#pragma unroll
+        for (int g = 0; g < RG; g++) k[g] = *reinterpret_cast<const uint32_t*>(tokblk + lane * 4 * G + 4 * g);
+      }
+      if ((lane >> 4) == (tnew >> 2)) {
+        const uint32_t m = 0xFFu << (8 * (tnew & 3));
+#pragma unroll
+        for (int g = 0; g < RG; g++)
+          v[g] = (v[g] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + lane * 4 * G + 4 * g) & m);
+      }
+#pragma unroll
+      for (int c = 0; c < SW; c++) {
+        const int d = 64 * c + lane;                 // scale dword: halves 2d, 2d + 1
+        const int hv = 2 * d - (2 * d >= 16 * G ? 16 * G : 0);  // half index inside K or V scales
+        if (d < C::SCB / 4 && hv / G == tnew)
+          sw[c] = *reinterpret_cast<const uint32_t*>(tokblk + C::BS + 4 * d);
+      }
+    };
+    // One step over a set. The last step of a wave is the only one that can hold the
+    // sequence's last page (pages ascend), so only it carries the fused append's patch.
+    auto run_step = [&](auto last, int st, uint32_t (&k)[PPS][RG], uint32_t (&v)[PPS][RG],
+                        uint32_t (&sw)[PPS][SW], uint8_t* ss) {
+      if (balance) balance_step(PPS * st);
+      const int pa0 = p0 + wv + NW * PPS * st;
+      if constexpr (decltype(last)::value) {
+        if (app && wv == wl) {  // wave-uniform
+#pragma unroll
+          for (int i = 0; i < PPS; i++)
+            if (pa0 + NW * i == plast) patch_regs(k[i], v[i], sw[i]);
+        }
+      }
+      put_scales(ss, sw);
+      stepN(k, v, ss, pa0);
+    };
+    const int nst = (npw + PPS - 1) / PPS;  // steps of this wave
+    // The loop runs the steps that are not the last; the last one or two run after it.
+    int st = 0;
+#pragma unroll 1
+    for (; st + 2 < nst; st += 2) {
+      run_step(std::false_type{}, st, xk, xv, xs, ssw);
+      ldstep(st + 2, xk, xv, xs);
+      run_step(std::false_type{}, st + 1, yk, yv, ys, ssw + PPS * C::SCB);
+      ldstep(st + 3, yk, yv, ys);
+    }
+    if (st + 1 < nst) {
+      run_step(std::false_type{}, st, xk, xv, xs, ssw);
+      run_step(std::true_type{}, st + 1, yk, yv, ys, ssw + PPS * C::SCB);
+    } else if (st < nst) {
+      run_step(std::true_type{}, st, xk, xv, xs, ssw);
+    }
   } else {
 #pragma unroll 1
   for (int na = 0; na < npw; na += 2) {
-    // Keep the waves abreast on long loops. The hardware lets the oldest waves issue first,
-    // so the youngest ones otherwise finish last, alone on their SIMDs and with too few
-    // pages in flight. A wave that lags the furthest one takes issue priority.
-    if (balance) {
-      int lead = 0;
-      if (lane == 0) lead = atomicMax(&lead_n, na);
-      const int lag = __builtin_amdgcn_readfirstlane(lead) - na;
-      if (lag >= 4) __builtin_amdgcn_s_setprio(3);
-      else if (lag >= 2) __builtin_amdgcn_s_setprio(2);
-      else __builtin_amdgcn_s_setprio(0);
-    }
+    if (balance) balance_step(na);
     const int nmax = min(npw, na + NSLOT);  // the slots of pages < na are free again
 #pragma unroll
     for (int k = 0; k < 4; k++)
@@ -1319,19 +1560,22 @@ __global__ __launch_bounds__(256) void lpt_order_kernel(const int32_t* __restric
   for (int p = t; p < B * Hkv; p += 256) order[p] = seq_of_rank[p / Hkv] * Hkv + p % Hkv;
 }
 
-template <int D, int VB, int NW, bool SPV>
+template <int D, int VB, bool SPV>
 hipError_t launch_dqs(const LaunchDecode& a, hipStream_t st, unsigned grid) {
+  constexpr int VC = VB == 4 ? TQ_CODEC_ABSMAX : (VB == 3 ? TQ_CODEC_ABSMAX3 : TQ_CODEC_ABSMAX2);
   if (a.k_codec == TQ_CODEC_FP16) {
     // fp16 keys: 8 waves; a staged page does not fit three times per wave at D = 256
     if constexpr (D <= 128) {
-      constexpr int NWF = tq_decode_waves(D, TQ_CODEC_FP16);
+      constexpr int NWF = tq_decode_waves(D, TQ_CODEC_FP16, VC, SPV);
       hipLaunchKernelGGL((decode_fused<D, TQ_CODEC_FP16, VB, NWF, SPV>), dim3(grid), dim3(64 * NWF), 0, st, a);
     } else {
       return hipErrorInvalidValue;
     }
   } else if (a.k_codec == TQ_CODEC_LLOYDMAX) {
+    constexpr int NW = tq_decode_waves(D, TQ_CODEC_LLOYDMAX, VC, SPV);
     hipLaunchKernelGGL((decode_fused<D, TQ_CODEC_LLOYDMAX, VB, NW, SPV>), dim3(grid), dim3(64 * NW), 0, st, a);
   } else {
+    constexpr int NW = tq_decode_waves(D, TQ_CODEC_ABSMAX, VC, SPV);
     hipLaunchKernelGGL((decode_fused<D, TQ_CODEC_ABSMAX, VB, NW, SPV>), dim3(grid), dim3(64 * NW), 0, st, a);
   }
   return hipGetLastError();
@@ -1339,7 +1583,6 @@ hipError_t launch_dqs(const LaunchDecode& a, hipStream_t st, unsigned grid) {
 
 template <int D>
 hipError_t launch_d(const LaunchDecode& a, hipStream_t st) {
-  constexpr int NW = tq_decode_waves(D);
   if (a.order) {
     if (a.B > TQ_LPT_MAX_BATCH) return hipErrorInvalidValue;
     hipLaunchKernelGGL(lpt_order_kernel, dim3(1), dim3(256), 0, st, a.context_lens, a.B, a.Hkv, a.order);
@@ -1349,11 +1592,11 @@ hipError_t launch_d(const LaunchDecode& a, hipStream_t st) {
   const int vb = tq_value_bits(a.v_codec);
   if (a.sparse_v) {
     if (vb != 4) return hipErrorInvalidValue;
-    return launch_dqs<D, 4, NW, true>(a, st, grid);
+    return launch_dqs<D, 4, true>(a, st, grid);
   }
-  if (vb == 3) return launch_dqs<D, 3, NW, false>(a, st, grid);
-  if (vb == 2) return launch_dqs<D, 2, NW, false>(a, st, grid);
-  return launch_dqs<D, 4, NW, false>(a, st, grid);
+  if (vb == 3) return launch_dqs<D, 3, false>(a, st, grid);
+  if (vb == 2) return launch_dqs<D, 2, false>(a, st, grid);
+  return launch_dqs<D, 4, false>(a, st, grid);
 }
 
 }  // namespace

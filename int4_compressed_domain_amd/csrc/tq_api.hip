@@ -68,9 +68,10 @@ Split make_split(int pages, int S) {
 
 // sparse: the two-pass sparse-value loop keeps at most TQ_SPARSE_PAGES_PER_WAVE pages per
 // wave, which sets a smallest split count.
-Split choose_split(int B, int Hkv, int D, int k_codec, int max_ctx, int requested, bool sparse = false) {
+Split choose_split(int B, int Hkv, int D, int k_codec, int v_codec, int max_ctx, int requested,
+                   bool sparse = false) {
   const int pages = (max_ctx + 15) / 16;
-  const int nw = tq_decode_waves(D, k_codec);
+  const int nw = tq_decode_waves(D, k_codec, v_codec, sparse);
   int min_s = (pages + TQ_MAX_SPLIT_PAGES - 1) / TQ_MAX_SPLIT_PAGES;  // page ids fit LDS
   if (sparse) {
     const int per = TQ_SPARSE_PAGES_PER_WAVE * nw;
@@ -108,8 +109,8 @@ size_t partial_bytes(int B, int Hq, int D, int splits) {
 }
 
 size_t workspace_bytes(const tq_layout* L, int B, int max_ctx, int requested) {
-  const Split f = choose_split(B, L->num_kv_heads, L->head_dim, L->k_codec, max_ctx, requested);
-  const Split sp = choose_split(B, L->num_kv_heads, L->head_dim, L->k_codec, max_ctx, requested, true);
+  const Split f = choose_split(B, L->num_kv_heads, L->head_dim, L->k_codec, L->v_codec, max_ctx, requested);
+  const Split sp = choose_split(B, L->num_kv_heads, L->head_dim, L->k_codec, L->v_codec, max_ctx, requested, true);
   const Split d = choose_split_dense(B, L->num_kv_heads, max_ctx, requested);
   int S = f.splits > d.splits ? f.splits : d.splits;
   if (sp.splits > S) S = sp.splits;
@@ -258,14 +259,14 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   if (L->k_codec == TQ_CODEC_FP16 && L->head_dim > 128) return TQ_EUNSUPPORTED;
   if (sparse_v && L->v_codec != TQ_CODEC_ABSMAX) return TQ_EUNSUPPORTED;
   if (sparse_v && (int64_t)max_context_len >
-                      16LL * TQ_MAX_SPLITS * TQ_SPARSE_PAGES_PER_WAVE * tq_decode_waves(L->head_dim, L->k_codec))
+                      16LL * TQ_MAX_SPLITS * TQ_SPARSE_PAGES_PER_WAVE * tq_decode_waves(L->head_dim, L->k_codec, L->v_codec, true))
     return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
   // with every context empty nothing is read from the pool or the block table (the outputs
   // are zeros, plus a tail's attention for tq_decode_attn_hotcold): they may be NULL then
   if (max_context_len > 0 && (!pool || !block_table)) return TQ_EINVAL;
-  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, max_context_len, num_splits,
-                         sparse_v != 0);
+  Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, L->v_codec, max_context_len,
+                         num_splits, sparse_v != 0);
   const int64_t resident = (int64_t)num_cus() * (L->head_dim >= 256 ? 2 : 1);
   // fp16 tail: with automatic splits, at least 8 of them per unit, a grid that fits the chip
   // and a tail of at most 256 tokens, one split is given up for a workgroup per unit that

@@ -58,14 +58,29 @@ struct LaunchDequant {
 };
 hipError_t tq_launch_dequant(const LaunchDequant& a, hipStream_t st);
 
-// Wavefronts per fused-decode workgroup; each workgroup owns one (sequence, kv head,
-// context split). 16 waves fill a CU when the kernel fits in 128 registers per lane.
-// fp16 keys: 8 waves (a staged page is 41*D bytes, three per wave fit the LDS ring).
-constexpr int tq_decode_waves(int D, int k_codec = TQ_CODEC_ABSMAX) {
-  return (D > 128 || k_codec == TQ_CODEC_FP16) ? 8 : 16;
-}
 // Bits per value index of a value codec.
 constexpr int tq_value_bits(int v_codec) { return TQ_VALUE_BITS(v_codec); }
+#ifndef TQ_REG_WAVES
+#define TQ_REG_WAVES 8
+#endif
+#ifndef TQ_REG_PAGES_PER_STEP
+#define TQ_REG_PAGES_PER_STEP 2
+#endif
+#ifndef TQ_REG_EARLY
+#define TQ_REG_EARLY 2
+#endif
+// Wavefronts per fused-decode workgroup; each workgroup owns one (sequence, kv head,
+// context split). Pages staged in LDS (fp16 keys, 3- and 2-bit values, sparse values):
+// 16 waves fill a CU when the kernel fits in 128 registers per lane; fp16 keys and D = 256
+// take 8 (a staged fp16-key page is 41*D bytes, three per wave fit the LDS ring). Pages
+// streamed through registers (4-bit keys and values, D <= 128): two sets of four pages per
+// wave, one computed while the other is in flight, need more than 128 registers, so 8
+// waves of up to 256.
+constexpr int tq_decode_waves(int D, int k_codec, int v_codec, bool sparse) {
+  if (D > 128 || k_codec == TQ_CODEC_FP16) return 8;
+  if (!sparse && tq_value_bits(v_codec) == 4) return TQ_REG_WAVES;
+  return 16;
+}
 // Bytes of one block (16 tokens of one kv head).
 constexpr int tq_block_bytes(int D, int k_codec, int v_codec = TQ_CODEC_ABSMAX) {
   return TQ_BLOCK_BYTES_KV(D, k_codec, v_codec);

@@ -87,15 +87,49 @@ class Case:
             c_oracle.append(self.opool, w.head_dim, w.kv_heads, k32, v32, slots, self.sb,
                             w.k_codec, w.v_codec)
 
-    def fill(self, chunk=4096):
-        for b in range(self.w.batch):
+    def fill(self, chunk=4096, keep_last=False):
+        """Append every sequence's tokens; keep_last: all but the last, which are returned
+        (the decode step's new tokens, [B][Hkv][D] fp32 values and storage, and slots)."""
+        w = self.w
+        last = None
+        if keep_last:
+            sdt = np.uint16 if w.dtype == "bf16" else np.float32
+            last = dict(k32=np.zeros((w.batch, w.kv_heads, w.head_dim), np.float32),
+                        kst=np.zeros((w.batch, w.kv_heads, w.head_dim), sdt),
+                        slots=np.full(w.batch, -1, np.int64))
+            last["v32"], last["vst"] = np.zeros_like(last["k32"]), np.zeros_like(last["kst"])
+        for b in range(w.batch):
             L = int(self.lens[b])
-            k32, v32, kst, vst = W.seq_tokens(self.w, b, L, self.seed, self.scales)
-            for t0 in range(0, L, chunk):
-                t1 = min(L, t0 + chunk)
+            k32, v32, kst, vst = W.seq_tokens(w, b, L, self.seed, self.scales)
+            n = L - 1 if keep_last and L > 0 else L
+            for t0 in range(0, n, chunk):
+                t1 = min(n, t0 + chunk)
                 self.append_raw(k32[t0:t1], v32[t0:t1], kst[t0:t1], vst[t0:t1],
                                 W.slots_for(self.bt, b, t0, t1))
+            if keep_last and L > 0:
+                last["k32"][b], last["v32"][b] = k32[L - 1], v32[L - 1]
+                last["kst"][b], last["vst"][b] = kst[L - 1], vst[L - 1]
+                last["slots"][b] = W.slots_for(self.bt, b, L - 1, L)[0]
         torch.cuda.synchronize()
+        return last
+
+    def append_decode_gpu(self, last, num_splits=0):
+        """The benchmark's call: tq_append_decode_attn of the new tokens over the whole
+        context (automatic split count unless given); the oracle pool gets the same tokens."""
+        w = self.w
+        maxc = int(self.lens.max())
+        ws = torch.zeros(max(tq.tq_decode_workspace_size(self.layout, w.batch, maxc, num_splits), 4) // 4,
+                         dtype=torch.float32, device=DEV)
+        out = torch.full((w.batch, w.q_heads, w.head_dim), float("nan"), dtype=torch.float32, device=DEV)
+        tq.tq_append_decode_attn(self.layout, self.pool, to_dev(last["kst"], w.dtype), to_dev(last["vst"], w.dtype),
+                                 self.q_dev, self.bt_dev, self.lens_dev, maxc, w.attn_scale, out, ws,
+                                 num_splits=num_splits)
+        torch.cuda.synchronize()
+        keep = last["slots"] >= 0
+        if self.opool is not None:
+            c_oracle.append(self.opool, w.head_dim, w.kv_heads, last["k32"][keep], last["v32"][keep],
+                            last["slots"][keep], self.sb, w.k_codec, w.v_codec)
+        return out.cpu().numpy()
 
     def pool_equal(self):
         return np.array_equal(self.pool.cpu().numpy(), self.opool)
