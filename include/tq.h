@@ -186,6 +186,28 @@ int tq_decode_attn(const tq_layout* layout, const void* pool, const void* q, int
                    int32_t num_splits, float* out, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Device scratch of tq_decode_attn_noalloc, per GPU, held until the process ends. */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* tq_decode_attn without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. It calls no allocating routine; its workspace is the library's own static
+ * device array of TQ_NOALLOC_SCRATCH_BYTES bytes on the current device (one per GPU,
+ * found on the first call on that device). Arguments, results and errors as
+ * tq_decode_attn, except:
+ *   - a call whose workspace (tq_decode_workspace_size(layout, batch, max_context_len,
+ *     num_splits)) exceeds TQ_NOALLOC_SCRATCH_BYTES returns TQ_ENOSPC before any launch;
+ *   - the arrival counters of the array are cleared by a fill kernel on `stream` at the
+ *     start of every call, so a call never depends on what an earlier one left there;
+ *   - calls that overlap on one GPU (on different streams, or from different threads)
+ *     share the array and race: the caller serializes them;
+ *   - TQ_VALIDATE does not apply (its checks synchronize and copy to host memory);
+ *   - TQ_EDEVICE if the device or the array's address cannot be obtained. */
+int tq_decode_attn_noalloc(const tq_layout* layout, const void* pool, const void* q, int32_t q_dtype,
+                           int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len, float attn_scale,
+                           int32_t num_splits, float* out, void* stream);
+
 /* Append the newest token of every sequence, then decode: the same result as
  *   tq_kv_append(k_last, v_last, slots = position context_lens[b] - 1 of each sequence)
  *   followed by tq_decode_attn(...), in one decode launch. The token of sequence b is the last one

@@ -37,6 +37,7 @@
 //            times rho, times sigma) and written.
 // Variants: the fused append of each sequence's newest token (knew/vnew), sparse values in
 // two passes (SPV), an fp16 tail (hot_k/hot_v).
+#include <algorithm>
 #include <type_traits>
 
 #include "tq_codec.h"
@@ -1536,6 +1537,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   }
 }
 
+// n int32 zeros from p (a plain fill kernel: usable where a memset node is not wanted).
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
 // Longest-first order of the units (b, h), for grids larger than the chip holds at once,
 // where a long sequence whose workgroups start last would finish alone: position p takes
 // head p % Hkv of the sequence ranked p / Hkv by context length (longest first, ties by
@@ -1600,6 +1606,13 @@ hipError_t launch_d(const LaunchDecode& a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t tq_launch_zero_i32(int32_t* p, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = std::min((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(blocks), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
 
 hipError_t tq_launch_decode(const LaunchDecode& a, hipStream_t st) {
   switch (a.D) {

@@ -7,6 +7,8 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "../../include/tq.h"
@@ -199,6 +201,34 @@ int check_decode_common(const tq_layout* L, const void* q, int q_dtype, int batc
 
 }  // namespace
 
+// ---- decode without allocation: the library's own device scratch -----------------------
+// One array per GPU (each device holds its own copy of a __device__ variable), looked up
+// with hipGetSymbolAddress on the first call on that device and kept per device: in host
+// code the array's name is not a device address.
+static __device__ __align__(256) uint8_t scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int TQ_MAX_DEVICES = 64;
+std::atomic<void*> scratch_dev[TQ_MAX_DEVICES];
+std::mutex scratch_mu;
+
+int scratch_of_current_device(void** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= TQ_MAX_DEVICES) return TQ_EDEVICE;
+  void* ptr = scratch_dev[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> g(scratch_mu);
+    ptr = scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TQ_EDEVICE;
+      scratch_dev[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *p = ptr;
+  return TQ_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* tq_status_str(int status) {
@@ -240,6 +270,9 @@ size_t tq_decode_workspace_size(const tq_layout* L, int32_t batch, int32_t max_c
   return workspace_bytes(L, batch, max_context_len, num_splits);
 }
 
+// no_alloc: the workspace is the library's static scratch (tq_decode_attn_noalloc): its
+// arrival counters are cleared by a fill kernel before the decode, and the TQ_VALIDATE
+// host checks (which synchronize and copy to host buffers) are not run.
 static int decode_impl(const tq_layout* L, const void* pool, const void* knew, const void* vnew,
                        int32_t new_dtype, const void* q, int32_t q_dtype, int32_t batch,
                        const int32_t* block_table, int32_t max_pages_per_seq,
@@ -248,7 +281,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
                        void* stream, int sparse_v = 0, float v_thr = 0.0f,
                        unsigned long long* v_skipped = nullptr, const void* hot_k = nullptr,
                        const void* hot_v = nullptr, const int32_t* hot_lens = nullptr,
-                       int hot_cap = 0) {
+                       int hot_cap = 0, bool no_alloc = false) {
   int rc = check_layout(L, true);
   if (rc != TQ_OK) return rc;
   rc = check_decode_common(L, q, q_dtype, batch, context_lens, max_context_len, attn_scale,
@@ -282,7 +315,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   }
   if (workspace_bytes_ < workspace_bytes(L, batch, max_context_len, num_splits)) return TQ_ENOSPC;
   if (!workspace) return TQ_EINVAL;
-  if (validating()) {
+  if (!no_alloc && validating()) {
     rc = validate_tables(L, batch, block_table, max_pages_per_seq, context_lens, max_context_len,
                          hot_k ? hot_lens : nullptr, hot_cap, static_cast<hipStream_t>(stream));
     if (rc != TQ_OK) return rc;
@@ -311,6 +344,10 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   if (batch > 1 && batch <= TQ_LPT_MAX_BATCH && (int64_t)batch * L->num_kv_heads * s.splits > resident)
     a.order = reinterpret_cast<int32_t*>(
         a.part_ml + (size_t)batch * L->num_q_heads * rows * 2);
+  if (no_alloc) {
+    rc = from_hip(tq_launch_zero_i32(a.counters, batch * L->num_kv_heads, static_cast<hipStream_t>(stream)));
+    if (rc != TQ_OK) return rc;
+  }
   return from_hip(tq_launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -322,6 +359,26 @@ int tq_decode_attn(const tq_layout* L, const void* pool, const void* q, int32_t 
   return decode_impl(L, pool, nullptr, nullptr, 0, q, q_dtype, batch, block_table,
                      max_pages_per_seq, context_lens, max_context_len, attn_scale, num_splits, out,
                      workspace, workspace_bytes_, stream);
+}
+
+int tq_decode_attn_noalloc(const tq_layout* L, const void* pool, const void* q, int32_t q_dtype,
+                           int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len, float attn_scale,
+                           int32_t num_splits, float* out, void* stream) {
+  int rc = check_layout(L, true);
+  if (rc != TQ_OK) return rc;
+  if (batch < 0 || max_context_len < 0 || num_splits < 0) return TQ_EINVAL;
+  if (batch > 0 && workspace_bytes(L, batch, max_context_len, num_splits) > TQ_NOALLOC_SCRATCH_BYTES)
+    return TQ_ENOSPC;
+  void* ws = nullptr;
+  if (batch > 0) {
+    rc = scratch_of_current_device(&ws);
+    if (rc != TQ_OK) return rc;
+  }
+  return decode_impl(L, pool, nullptr, nullptr, 0, q, q_dtype, batch, block_table, max_pages_per_seq,
+                     context_lens, max_context_len, attn_scale, num_splits, out, ws,
+                     TQ_NOALLOC_SCRATCH_BYTES, stream, 0, 0.0f, nullptr, nullptr, nullptr, nullptr, 0,
+                     true);
 }
 
 int tq_append_decode_attn(const tq_layout* L, void* pool, const void* k_last, const void* v_last,

@@ -16,7 +16,8 @@ F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("tq_status_str", "tq_page_bytes", "tq_kv_append", "tq_decode_workspace_size",
            "tq_decode_attn", "tq_append_decode_attn", "tq_decode_attn_sparse_v", "tq_dequant_ref",
-           "tq_dense_decode_attn", "tq_decode_attn_hotcold", "tq_stream_read_probe")
+           "tq_dense_decode_attn", "tq_decode_attn_hotcold", "tq_stream_read_probe",
+           "tq_decode_attn_noalloc")
 
 
 class TQError(RuntimeError):
@@ -70,6 +71,9 @@ def _lib():
             L.tq_stream_read_probe.argtypes = [P, sz, P, sz, P]
             L.tq_stream_read_probe.restype = ctypes.c_int
         L.tq_dense_decode_attn.argtypes = [LP, P, P, P, i32, i32, P, i32, f32, i32, P, P, sz, P]
+        if hasattr(L, "tq_decode_attn_noalloc"):
+            L.tq_decode_attn_noalloc.argtypes = [LP, P, P, i32, i32, P, i32, P, i32, f32, i32, P, P]
+            L.tq_decode_attn_noalloc.restype = ctypes.c_int
         for name in ("tq_kv_append", "tq_decode_attn", "tq_dequant_ref", "tq_dense_decode_attn"):
             getattr(L, name).restype = ctypes.c_int
         _L = L
@@ -132,6 +136,15 @@ def tq_decode_attn(layout, pool, q, block_table, context_lens, max_context_len, 
         block_table.shape[1], _ptr(context_lens), max_context_len, attn_scale, num_splits,
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)), "tq_decode_attn")
+
+
+def tq_decode_attn_noalloc(layout, pool, q, block_table, context_lens, max_context_len, attn_scale,
+                           out, num_splits=0, stream=None):
+    """tq_decode_attn on the library's own device scratch (no workspace argument)."""
+    _check(_lib().tq_decode_attn_noalloc(
+        ctypes.byref(layout), _ptr(pool), _ptr(q), _dtype_code(q), q.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(context_lens), max_context_len, attn_scale, num_splits,
+        _ptr(out), _stream(stream)), "tq_decode_attn_noalloc")
 
 
 def tq_append_decode_attn(layout, pool, k_last, v_last, q, block_table, context_lens,
