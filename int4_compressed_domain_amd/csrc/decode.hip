@@ -320,7 +320,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // scale block goes to a per-wave LDS slot; other variants stage whole pages in LDS by
   // LDS-DMA. On MI355X the register path streams pages at ~6.2 TB/s, the LDS-DMA path at
   // ~4.5 TB/s (same pages, no compute).
-  constexpr bool REG = !KF16 && !SPV && VB == 4 && D <= 128;
+  constexpr bool REG = tq_decode_reg_path(D, KCODEC, VB, SPV);
   constexpr int SW = (C::SCB / 4 + 63) / 64;  // scale dwords per lane of a page (register path)
   constexpr int RG = REG ? G : 1;             // index dwords per lane of a page region
   constexpr int PPS = TQ_REG_PAGES_PER_STEP;  // register path: pages per step (2 or 4)
@@ -340,9 +340,56 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   if (a.order) u = a.order[u];  // longest-first order (see lpt_order_kernel)
   const int b = u / a.Hkv, h = u - b * a.Hkv;
   const int r = a.Hq / a.Hkv;
+  const int pps = a.pages_per_split;
+  const bool hotwg = a.hot_wg && s == a.splits;
+  const int p0 = hotwg ? 0 : s * pps;
+
+  // ---- the prologue's small loads, issued together with the context length's -----------
+  // (one memory round trip): the query bits of this wave's head, the sign bits, and this
+  // wave's page ids p0 + wv + NW n. The ids are read up to the split's end in the block
+  // table's row, before the sequence's length is known; ids past its last page are never
+  // used. They are held across the lanes (page n in lane n % 64 of register n / 64) and read
+  // back with v_readlane when issued.
+  const int64_t qb = ((int64_t)b * a.Hq + (int64_t)h * r) * D;  // this unit's query elements
+  uint32_t qraw[V];  // wave w < r: bits of query head w, dims lane + 64k (widened below)
+  if (wv < r) {
+#pragma unroll
+    for (int k = 0; k < V; k++) qraw[k] = load_q_bits(a.q, a.q_dtype, qb + wv * D + lane + 64 * k);
+  }
+  const uint32_t sgn_word = tid < D / 32 ? a.sign_bits[tid] : 0u;
+  uint32_t qsgn[V];  // sign word of query dim lane + 64k: word 2k + lane / 32 (D >= 64)
+#pragma unroll
+  for (int k = 0; k < V; k++) qsgn[k] = a.sign_bits[2 * k + (lane >> 5)];
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  const int pcap = (hotwg || a.max_ctx == 0) ? 0 : min(p0 + pps, a.max_pages);
+  constexpr int PPL = (TQ_MAX_SPLIT_PAGES / NW + 63) / 64;
+  static_assert(PPL <= 4, "page ids of a wave: at most four registers");
+  // held in a vector value, not an array: the selection below must stay in registers (as
+  // an array it was turned into an indexed access and the ids were moved to LDS, one
+  // waited-for load at a time)
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  i32x4 vpid = {0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < PPL; k++) {
+    const int idx = p0 + wv + NW * (lane + 64 * k);
+    vpid[k] = idx < pcap ? bt[idx] : 0;
+  }
+  // Fused append: wave NW - 1 of every workgroup of the unit also loads the unit's new K/V
+  // token here (whether its split holds the sequence's last page is known only once the
+  // length has arrived); lanes 0..15 take K, 16..31 V, E elements each.
+  constexpr int E = CodecCfg<D>::E;
+  float ynew[E];
+  uint32_t swnew = 0;
+  if (!SPV && !hotwg && a.knew != nullptr && wv == NW - 1 && lane < 32) {
+    swnew = lane_signs<D>(a.sign_bits, lane & 15);
+    const int64_t off = ((int64_t)b * a.Hkv + h) * D + (lane & 15) * E;
+    const void* src = (lane < 16) ? a.knew : a.vnew;
+    if (a.new_dtype == TQ_F32) load_widen<float, E>(static_cast<const float*>(src) + off, ynew);
+    else if (a.new_dtype == TQ_BF16) load_widen<uint16_t, E>(static_cast<const uint16_t*>(src) + off, ynew);
+    else load_widen<f16, E>(static_cast<const f16*>(src) + off, ynew);
+  }
   const int L = a.context_lens[b];
   const int npages = (L + 15) >> 4;
-  const int pps = a.pages_per_split;
   // Hot/cold: an fp16 tail of Lh recent tokens besides the pool's L. Either every split of
   // the unit takes an equal slice [t0, t0 + tsl) of it after its pages (a unit with a tail
   // and no pool tokens has one split, holding the whole tail), or (a.hot_wg, when the grid
@@ -350,7 +397,6 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // tail and no pages and publishes partial row ns_cold.
   const int Lh = a.hot_k ? min(max(a.hot_lens[b], 0), a.hot_cap) : 0;
   const int ns_cold = (npages + pps - 1) / pps;
-  const bool hotwg = a.hot_wg && s == a.splits;
   const int ns = a.hot_wg ? ns_cold + (Lh > 0 ? 1 : 0)
                           : (ns_cold > 0 ? ns_cold : (Lh > 0 ? 1 : 0));  // partials merged for this unit
   float* outp = a.out + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
@@ -361,7 +407,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   }
   if (hotwg ? Lh == 0 : s >= (a.hot_wg ? ns_cold : ns)) return;
   const int srow = hotwg ? ns_cold : s;  // this workgroup's partial row
-  const int p0 = hotwg ? 0 : s * pps, p1 = hotwg ? 0 : min(p0 + pps, npages);
+  const int p1 = hotwg ? 0 : min(p0 + pps, npages);
   const int t0 = a.hot_wg ? 0 : (int)((int64_t)Lh * s / ns);
   const int tsl = a.hot_wg ? (hotwg ? Lh : 0) : (int)((int64_t)Lh * (s + 1) / ns) - t0;
 
@@ -373,6 +419,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   __shared__ float hml[8][2];                  // per head: max M and sum l of the workgroup
   __shared__ int last_flag;
   __shared__ int lead_n;                       // furthest page-loop step reached by a wave
+  __shared__ int tok_ready;                    // the appended token is in tokblk
   __shared__ int wskip;                        // sparse values: pages skipped by the workgroup
   __shared__ uint32_t sgn_s[D / 32];           // sigma bits, read once for the final un-rotation
   static_assert(NW >= 8, "one wave per query head in the rotations");
@@ -400,31 +447,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   };
   float (*wsh)[TQ_MAX_SPLITS] = reinterpret_cast<float (*)[TQ_MAX_SPLITS]>(&ring[0][0][0] + MEND);
 
-  // ---- page ids of this split and this wave's query head, loaded together ------------------
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  // ---- this wave's pages ----------------------------------------------------------------
   const uint8_t* hbase = a.pool + (int64_t)h * BB;
   const int64_t pstride = (int64_t)a.Hkv * BB;
-  // this wave's pages p0 + wv + NW n, n < npw: physical page ids held across the lanes
-  // (page n in lane n % 64 of register n / 64), read back with v_readlane when issued
-  const int npw = (p1 - p0 - wv + NW - 1) / NW;  // pages of this wave
-  // The small loads of the prologue (query bits, sign bits, page ids, an appended token)
-  // are issued back to back and waited for together: one memory round trip.
-  const int64_t qb = ((int64_t)b * a.Hq + (int64_t)h * r) * D;  // this unit's query elements
-  uint32_t qraw[V];  // wave w < r: bits of query head w, dims lane + 64k (widened below)
-  if (wv < r) {
-#pragma unroll
-    for (int k = 0; k < V; k++) qraw[k] = load_q_bits(a.q, a.q_dtype, qb + wv * D + lane + 64 * k);
-  }
-  const uint32_t sgn_word = tid < D / 32 ? a.sign_bits[tid] : 0u;
-  constexpr int PPL = (TQ_MAX_SPLIT_PAGES / NW + 63) / 64;
-  static_assert(PPL <= 4, "page ids of a wave: at most four registers");
-  // held in a vector value, not an array: the selection below must stay in registers (as
-  // an array it was turned into an indexed access and the ids were moved to LDS, one
-  // waited-for load at a time)
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  i32x4 vpid = {0, 0, 0, 0};
-#pragma unroll
-  for (int k = 0; k < PPL; k++) vpid[k] = (lane + 64 * k < npw) ? bt[p0 + wv + NW * (lane + 64 * k)] : 0;
+  const int npw = (p1 - p0 - wv + NW - 1) / NW;  // pages of this wave: p0 + wv + NW n, n < npw
   auto page_blk = [&](int n) {  // wave-uniform address of page n's block for head h
     const int id = PPL > 1 ? vpid[(n >> 6) & (PPL - 1)] : vpid[0];
     return hbase + (int64_t)__builtin_amdgcn_readlane(id, n & 63) * pstride;
@@ -433,43 +459,28 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ring[0][0][0]));
   auto slot_lds = [&](int k) { return ring_lds + (uint32_t)((k * NW + wv) * C::SLOT); };
   // Fused append: the split holding the sequence's last page also appends its last token
-  // (position L - 1) for head h. Wave wc quantizes it into tokblk (the block layout, only
-  // that token's bytes valid); wave wl, which owns the last page, patches its staged copy
-  // before computing it; wave wc stores the token to the pool after the page loop.
-  constexpr int E = CodecCfg<D>::E;
+  // (position L - 1) for head h. Wave wc (its token loaded above) quantizes it into tokblk
+  // (the block layout, only that token's bytes valid) once the prologue is over, so that the
+  // workgroup's start does not wait for it, and raises tok_ready; wave wl, which owns the
+  // last page, waits for the flag before it patches the token into that page; wave wc
+  // stores the token to the pool after the page loop.
   const bool app = !SPV && !hotwg && (a.knew != nullptr) && (s == ns_cold - 1);
   const int plast = npages - 1, tnew = (L - 1) & 15;
   const int wc = NW - 1, wl = (plast - p0) % NW;
-  float ynew[E];
-  uint32_t swnew = 0;
   int pid_last = 0;  // wave wc: physical id of the last page, for the token's store to the pool
   if (app && wv == wc) pid_last = bt[plast];
-  if (app && wv == wc && lane < 32) {
-    swnew = lane_signs<D>(a.sign_bits, lane & 15);
-    const int64_t off = ((int64_t)b * a.Hkv + h) * D + (lane & 15) * E;
-    const void* src = (lane < 16) ? a.knew : a.vnew;
-    if (a.new_dtype == TQ_F32) load_widen<float, E>(static_cast<const float*>(src) + off, ynew);
-    else if (a.new_dtype == TQ_BF16) load_widen<uint16_t, E>(static_cast<const uint16_t*>(src) + off, ynew);
-    else load_widen<f16, E>(static_cast<const f16*>(src) + off, ynew);
-#pragma unroll
-    for (int e = 0; e < E; e++) asm volatile("" ::"v"(ynew[e]));  // before any page load
-    asm volatile("" ::"v"(swnew));
-  }
-  if (app && wv == wc) asm volatile("" ::"v"(pid_last));
   // consume the page ids here, before any page is in flight: otherwise the compiler waits
   // for them (vmcnt(0), i.e. for every in-flight page too) where they are first read
 #pragma unroll
   for (int k = 0; k < PPL; k++) asm volatile("" ::"v"(vpid[k]));
-  if (tid < D / 32) sgn_s[tid] = sgn_word;
-  __syncthreads();
+  if (tid < D / 32) sgn_s[tid] = sgn_word;  // (read after later barriers: final rotation, tail)
   float qv[V];
   if (wv < r) {  // wave w rotates query head w: sign flip now, butterflies below
 #pragma unroll
     for (int k = 0; k < V; k++) {
-      const int d = lane + 64 * k;
       const float x = widen_q_bits(qraw[k], a.q_dtype);
       // fp16 keys are in the original basis: the query scores them unrotated
-      qv[k] = (!KF16 && ((sgn_s[d >> 5] >> (d & 31)) & 1u)) ? -x : x;
+      qv[k] = (!KF16 && ((qsgn[k] >> (lane & 31)) & 1u)) ? -x : x;
     }
   }
   // start streaming this wave's first pages; they land while the queries are prepared
@@ -520,18 +531,6 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int i = 0; i < PPS; i++) ldp(PPS * st + i, k[i], v[i], sw[i]);
   };
-  if (app && wv == wc && lane < 32) {  // quantize the appended token before this wave's
-    uint32_t un[E];                     // first page loads, which may wait for queue space
-    f16 scn;
-    if (KF16 && lane < 16) {
-      place_key_f16<D>(tokblk, tnew, lane, ynew);  // fp16 key, no rotation
-    } else {
-      if (lane >= 16) codec_vector<D, C::VC>(ynew, swnew, lane & 15, un, scn);
-      else if (KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, swnew, lane & 15, un, scn);
-      else codec_vector<D, TQ_CODEC_LLOYDMAX>(ynew, swnew, lane & 15, un, scn);
-      place_vector<D, KF16, VB>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
-    }
-  }
   // Register path: only the first pages are requested before the query is prepared. A
   // wave's loads issue in order, and more than the memory pipeline holds would stall it at
   // the load instructions, holding back the rotation and the barriers behind them (all
@@ -582,8 +581,32 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   if (tid == 0) {
     lead_n = 0;
     wskip = 0;
+    tok_ready = 0;
   }
   __syncthreads();
+  if (app && wv == wc) {  // the appended token, quantized into tokblk
+    if (lane < 32) {
+      uint32_t un[E];
+      f16 scn;
+      if (KF16 && lane < 16) {
+        place_key_f16<D>(tokblk, tnew, lane, ynew);  // fp16 key, no rotation
+      } else {
+        if (lane >= 16) codec_vector<D, C::VC>(ynew, swnew, lane & 15, un, scn);
+        else if (KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, swnew, lane & 15, un, scn);
+        else codec_vector<D, TQ_CODEC_LLOYDMAX>(ynew, swnew, lane & 15, un, scn);
+        place_vector<D, KF16, VB>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
+      }
+    }
+    __hip_atomic_store(&tok_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  // wave wl, before it reads tokblk: the flag is raised by wave wc right after the prologue,
+  // which waits for nothing else; the bound only guards against a wait that cannot end
+  auto wait_token = [&]() {
+    for (int i = 0; i < (1 << 22); i++) {
+      if (__hip_atomic_load(&tok_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  };
   const bool live = hl < r;
   const bool hiLane = hr < 8;  // lanes 0..7 of a row finish page A of each step, 8..15 page B
   const float down = live ? qdown[hl] : 1.0f;
@@ -601,7 +624,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     if (!live) bq[g] = f16x8{};
     cinit[g] = KSUB ? -__builtin_amdgcn_mfma_f32_16x16x32_f16(abeta, bq[g], zero4, 0, 0, 0)[0] : 0.0f;
   }
-  __syncthreads();  // every wave holds its operands: the last ring slot is free again
+  // every wave holds its operands: the last ring slot is free again (the register path
+  // never writes that slot: its scale blocks live in the first one)
+  if constexpr (!REG) __syncthreads();
   if constexpr (REG) {  // the rest of the first two steps' pages
     if (npw > 0) {
 #pragma unroll
@@ -1131,6 +1156,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       const int pa0 = p0 + wv + NW * PPS * st;
       if constexpr (decltype(last)::value) {
         if (app && wv == wl) {  // wave-uniform
+          wait_token();
 #pragma unroll
           for (int i = 0; i < PPS; i++)
             if (pa0 + NW * i == plast) patch_regs(k[i], v[i], sw[i]);
@@ -1170,6 +1196,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     wait_pages_in_flight<C::NDMA, NSLOT - 2>(younger);
     const int pa = p0 + wv + NW * na;
     if (app && wv == wl && (pa == plast || pa + NW == plast)) {  // wave-uniform
+      wait_token();
       copy_token(ring[(pa == plast ? na : na + 1) % NSLOT][wv], true);
       asm volatile("" ::: "memory");
     }

@@ -77,9 +77,17 @@ constexpr int tq_value_bits(int v_codec) { return TQ_VALUE_BITS(v_codec); }
 // streamed through registers (4-bit keys and values, D <= 128): two sets of four pages per
 // wave, one computed while the other is in flight, need more than 128 registers, so 8
 // waves of up to 256.
+#ifndef TQ_REG_LUT
+#define TQ_REG_LUT 0
+#endif
+// Variants whose pages stream through registers (the others stage pages in LDS).
+constexpr bool tq_decode_reg_path(int D, int k_codec, int value_bits, bool sparse) {
+  return D <= 128 && !sparse && value_bits == 4 &&
+         (k_codec == TQ_CODEC_ABSMAX || (TQ_REG_LUT && k_codec == TQ_CODEC_LLOYDMAX));
+}
 constexpr int tq_decode_waves(int D, int k_codec, int v_codec, bool sparse) {
   if (D > 128 || k_codec == TQ_CODEC_FP16) return 8;
-  if (!sparse && tq_value_bits(v_codec) == 4) return TQ_REG_WAVES;
+  if (tq_decode_reg_path(D, k_codec, tq_value_bits(v_codec), sparse)) return TQ_REG_WAVES;
   return 16;
 }
 // Bytes of one block (16 tokens of one kv head).
