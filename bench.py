@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+SPREAD_SAMPLES, SPREAD_LAUNCHES = 120, 32
 METRIC = "effective KV GB/s (fraction of HBM peak) + decode attn µs/token at 128K ctx"
 
 
@@ -53,6 +54,7 @@ def parse():
     ap.add_argument("--sparse-v", type=float, default=None, metavar="THR",
                     help="decode with sparse values at this weight threshold (the step is then the "
                          "new tokens' append + tq_decode_attn_sparse_v)")
+    ap.add_argument("--cpu-oracle-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--profile", type=int, default=0,
                     help="run this many eager steps and exit: for profilers")
     return ap.parse_args()
@@ -182,6 +184,13 @@ class Setup:
                                  self.lens_dev, self.max_ctx, self.w.attn_scale, self.out, self.ws,
                                  num_splits=self.splits)
 
+    def append_last(self, i):
+        """tq_kv_append alone: every decoding sequence's newest token (as the fused call
+        writes it, so the pool's contents do not change)."""
+        from int4_compressed_domain_amd import tq
+        tq.tq_kv_append(self.layout, self.pools[i % len(self.pools)], self.k_last, self.v_last,
+                        self.slots_last)
+
     def step(self, i):
         """The prefill chunk's append and the decode. They touch different pages (the chunk
         fills fresh ones), so the append runs on a second stream beside the decode and can
@@ -255,17 +264,29 @@ def time_steps(S, steps, warmup):
     dec_ms, _ = _time_replays(graphs[1], reps)
     pre_ms = _time_replays(graphs[2], reps)[0] if len(graphs) > 2 else 0.0
     K = reps * n
-    # spread: events around single replays of the decode graph (n launches each)
+    # spread: SPREAD_SAMPLES samples, each the mean per-launch time of one replay of a graph
+    # of SPREAD_LAUNCHES back-to-back decodes (the pool copies in turn), timed by events on
+    # the replay stream; the graph launch itself is spread over those launches
+    g32 = _graph(S.decode, SPREAD_LAUNCHES)
+    for _ in range(5):
+        g32.replay()
+    torch.cuda.synchronize()
     per = []
-    for _ in range(min(reps, 60)):
+    for _ in range(SPREAD_SAMPLES):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        graphs[1].replay()
+        g32.replay()
         e1.record()
         per.append((e0, e1))
     torch.cuda.synchronize()
-    us = np.array([a.elapsed_time(b) for a, b in per]) / n * 1e3
+    us = np.array([a.elapsed_time(b) for a, b in per]) / SPREAD_LAUNCHES * 1e3
     S.decode_pct = [round(float(x), 3) for x in np.percentile(us, [10, 50, 90])]
+    # the one-token append alone (the fused call does it inside the decode)
+    ga = _graph(S.append_last, n)
+    for _ in range(20):
+        ga.replay()
+    torch.cuda.synchronize()
+    S.append_one_us = _time_replays(ga, max(reps, 200 // n + 1))[0] / (max(reps, 200 // n + 1) * n) * 1e3
     return K, wall / K * 1e3, ev_ms / K, dec_ms / K * 1e3, pre_ms / K * 1e3
 
 
@@ -354,10 +375,11 @@ def profiled_traffic(workload):
         return None
 
 
-def cpu_baseline(w, min_seconds=10.0):
+def cpu_baseline(w, min_seconds=10.0, one_group=False):
     """The C oracle, as it stands, on the host cores: build its own pool (untimed), then time
-    its decode of a bounded sample (whole sequences, every q head over every cached token),
-    repeated until min_seconds have passed."""
+    its decode of a bounded sample (whole sequences, every q head over every cached token; with
+    one_group, only the q heads of the first sequence's first kv head), repeated until
+    min_seconds have passed."""
     from int4_compressed_domain_amd import workloads as W
     from oracle import c_oracle
     D, Hkv = w.head_dim, w.kv_heads
@@ -377,7 +399,11 @@ def cpu_baseline(w, min_seconds=10.0):
         c_oracle.append(opool, D, Hkv, k32, v32, W.slots_for(bt, b, 0, int(lens[b])), sb,
                         w.k_codec, w.v_codec)
     q32, _ = W.queries(w, 0)
-    pairs = np.array([(b, h) for b in range(nseq) for h in range(w.q_heads)], np.int32)
+    if one_group:
+        nseq = 1
+        pairs = np.array([(0, h) for h in range(w.gqa)], np.int32)
+    else:
+        pairs = np.array([(b, h) for b in range(nseq) for h in range(w.q_heads)], np.int32)
     # the sample's decode, repeated until at least min_seconds of host time are covered
     reps, dt = 0, 0.0
     while reps == 0 or dt < min_seconds:
@@ -386,12 +412,54 @@ def cpu_baseline(w, min_seconds=10.0):
                         k_codec=w.k_codec, v_codec=w.v_codec)
         dt += time.perf_counter() - t0
         reps += 1
+    # the KV bytes the sample's heads read: a q head group reads one kv head's share
     kv = reps * int(np.sum(lens[:nseq], dtype=np.int64)) * W.kv_bytes_per_token(w)
+    if one_group:
+        kv //= Hkv
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    heads = "%d q heads of kv head 0" % w.gqa if one_group else "%d q heads" % w.q_heads
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "seconds": dt,
-            "sample": "C oracle decode (fp64) of %d of %d sequences x %d q heads (%d tokens in "
-                      "the first), repeated %d times" % (nseq, w.batch, w.q_heads, int(lens[0]), reps)}
+            "sample": "C oracle decode (fp64) of %d of %d sequences x %s (%d tokens in "
+                      "the first), repeated %d times" % (nseq, w.batch, heads, int(lens[0]), reps)}
+
+
+def numpy_oracle_single_head(min_seconds=3.0):
+    """The NumPy oracle's decode on the single-head workload (1 head, D = 128, 1024 tokens),
+    repeated until min_seconds have passed (pool built untimed)."""
+    from int4_compressed_domain_amd import workloads as W
+    from oracle import np_oracle
+    w = W.WORKLOADS["single_head_1k"]
+    D, Hkv = w.head_dim, w.kv_heads
+    sb = W.sign_bits(D, 0)
+    lens = W.context_lens(w, 0)
+    bt, _, npages = W.page_tables(w, lens, 0)
+    pool = np_oracle.new_pool(npages, Hkv, D)
+    k32, v32, _, _ = W.seq_tokens(w, 0, int(lens[0]), 0, W.channel_scales(w, 0))
+    np_oracle.append(pool, D, Hkv, k32, v32, W.slots_for(bt, 0, 0, int(lens[0])), sb)
+    q32, _ = W.queries(w, 0)
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        np_oracle.decode(pool, D, w.q_heads, Hkv, sb, bt, lens, q32, w.attn_scale)
+        dt += time.perf_counter() - t0
+        reps += 1
+    kv = reps * int(lens[0]) * W.kv_bytes_per_token(w)
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle (NumPy)",
+            "seconds": dt, "sample": "NumPy oracle decode of single_head_1k (1024 tokens, "
+                                     "1 head), repeated %d times" % reps}
+
+
+def one_core_baselines(name):
+    """The C oracle on one core (one q head group of the workload) and the NumPy oracle on
+    the single-head workload, in a child process limited to one thread."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-oracle-child", "--workload", name],
+                       env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-400:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def main():
@@ -400,11 +468,15 @@ def main():
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)." % args.gpus, file=sys.stderr)
         sys.exit(2)
-    import torch
     from int4_compressed_domain_amd import workloads as W
-    dev = "cuda:0"
     name = args.workload or W.HEADLINE
     w = W.WORKLOADS[name]
+    if args.cpu_oracle_child:  # (one thread, no GPU)
+        print(json.dumps({"c_oracle_one_core": cpu_baseline(w, one_group=True),
+                          "numpy_oracle_single_head": numpy_oracle_single_head()}))
+        return
+    import torch
+    dev = "cuda:0"
     S = Setup(w, args, dev)
     if args.profile:
         for i in range(args.profile):
@@ -434,7 +506,20 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(name),
                      "kernel": "decode_fused", "mean_us": round(dec_mean, 3)},
         "decode_us_p10_p50_p90": S.decode_pct,
+        "decode_spread": "%d samples, each one graph replay of %d back-to-back decodes over the "
+                         "pool copies, timed with HIP events, divided by %d"
+                         % (SPREAD_SAMPLES, SPREAD_LAUNCHES, SPREAD_LAUNCHES),
+        # append cost per head_dim vector (K or V of one kv head of one token)
+        "append": {"vector": "one head_dim vector, K or V, of one kv head of one token",
+                   "one_token_us": round(S.append_one_us, 3),
+                   "one_token_vectors": 2 * w.kv_heads * int(np.count_nonzero(S.lens)),
+                   "one_token_ns_per_vector": round(S.append_one_us * 1e3 / max(
+                       1, 2 * w.kv_heads * int(np.count_nonzero(S.lens))), 3)},
     }
+    if w.prefill:
+        nv = 2 * w.kv_heads * w.prefill
+        rec["append"].update({"prefill_chunk_us": round(pre_mean, 3), "prefill_chunk_vectors": nv,
+                              "prefill_ns_per_vector": round(pre_mean * 1e3 / nv, 4)})
     if S.hot:
         rec["config"]["hot_tail"] = S.hot
         rec["roofline"].update({"traffic": None, "kernel": "decode_fused (hot/cold)"})
@@ -468,6 +553,7 @@ def main():
     rec["roofline"]["frac_of_measured_peak"] = round(rec["roofline"]["achieved"] / peak_meas, 4)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
+        rec["cpu_baseline"].update(one_core_baselines(name))
     print(json.dumps(rec), flush=True)
 
 
