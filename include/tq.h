@@ -79,7 +79,8 @@
  *    hot_cap, and slots outside the pool or given twice (a debugging aid: it costs a
  *    synchronization and host copies per call).
  *  - GPU support: head_dim in {64, 128, 256}, group_size 32, page_size 16,
- *    1 <= num_q_heads / num_kv_heads <= 8, batch * num_kv_heads <= 2^20; decode with fp16
+ *    1 <= num_q_heads / num_kv_heads <= 8, batch * num_kv_heads <= 2^20, appends with
+ *    num_kv_heads <= 65535; decode with fp16
  *    keys at head_dim 64 and 128; sparse values with 4-bit values only (TQ_EUNSUPPORTED
  *    otherwise).
  */

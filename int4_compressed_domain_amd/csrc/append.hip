@@ -7,11 +7,11 @@
 
 namespace {
 
-// Each 16-lane group takes VPT vectors (index vec = group * VPT + i; even vec: key, odd:
-// value, of token-head vec / 2): their slots and inputs are all loaded first, so one group
-// keeps several loads in flight and a large append needs few wavefronts.
-constexpr int VPT = 4;
-
+// One vector (the key or the value of one token and kv head) per 16-lane group, 16 per
+// workgroup: workgroup (x, y) takes kv head y of tokens 8x .. 8x + 7, waves 0 and 2 their
+// keys, waves 1 and 3 their values, so that every wave runs one codec. A vector's slot
+// and input are loaded together; one vector per group keeps each wave's dependent chain
+// short (a small append is one pass of latency) while a large one fills every SIMD.
 template <int D, typename TIn, int KCODEC, int VCODEC>
 __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
                                                      const TIn* __restrict__ kin,
@@ -23,47 +23,45 @@ __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
   constexpr int BB = tq_block_bytes(D, KCODEC, VCODEC);
   constexpr int VB = tq_value_bits(VCODEC);
   constexpr bool KF16 = KCODEC == TQ_CODEC_FP16;
-  const int lane = threadIdx.x & 15;
-  const int64_t nvec = (int64_t)n_tokens * Hkv * 2;
-  const int64_t vec0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * VPT;
-  if (vec0 >= nvec) return;  // whole 16-lane groups exit together
-  int64_t slot[VPT];
-  float y[VPT][E];
-#pragma unroll
-  for (int i = 0; i < VPT; i++) {
-    const int64_t vec = vec0 + i;
-    slot[i] = -1;
-    if (vec < nvec) {
-      const int64_t th = vec >> 1;  // token * Hkv + head
-      slot[i] = slots[th / Hkv];
-      load_widen<TIn, E>(((vec & 1) ? vin : kin) + th * D + lane * E, y[i]);
-    }
+  constexpr bool KLUT = KCODEC == TQ_CODEC_LLOYDMAX;
+  // sigma as a sign mask per coordinate (0 or the fp32 sign bit); the key codebook's
+  // bucket table
+  __shared__ uint32_t smask[D];
+  __shared__ u32x2 lut_tbl[KLUT ? tq_lutb::NB : 1];
+  const int cb = tq_blk16(threadIdx.x & 15);
+  const int wave = threadIdx.x >> 6;
+  const int h = blockIdx.y;
+  const int tok = blockIdx.x * 8 + (wave >> 1) * 4 + ((threadIdx.x >> 4) & 3);
+  const int tc = min(tok, n_tokens - 1);  // (a token past the end loads the last one's)
+  const int is_v = wave & 1;
+  // the vector's slot and input first, then the sign mask's words: one wait covers all
+  const int64_t slot_in = slots[tc];
+  float y[E];
+  load_widen<TIn, E>((is_v ? vin : kin) + ((size_t)tc * Hkv + h) * D + cb * E, y);
+  for (int i = threadIdx.x; i < D; i += 256) smask[i] = ((sign_bits[i >> 5] >> (i & 31)) & 1u) << 31;
+  if constexpr (KLUT) tq_lut_table_fill(lut_tbl, threadIdx.x);
+  __syncthreads();
+  const int64_t slot = tok < n_tokens ? slot_in : -1;
+  if (slot < 0) return;  // a skipped token, or past the end: the same for the 16 lanes
+  uint8_t* blk = pool + ((slot >> 4) * (int64_t)Hkv + h) * BB;
+  const int t = (int)(slot & 15);
+  if (KF16 && !is_v) {  // fp16 keys: stored as given, no rotation
+    place_key_f16<D>(blk, t, cb, y);
+    return;
   }
-  const uint32_t sw = lane_signs<D>(sign_bits, lane);
 #pragma unroll
-  for (int i = 0; i < VPT; i++) {
-    if (slot[i] < 0) continue;  // a skipped token, or past the end: the same for the group
-    const int64_t vec = vec0 + i;
-    const int is_v = (int)(vec & 1);
-    const int h = (int)((vec >> 1) % Hkv);
-    uint8_t* blk = pool + ((slot[i] >> 4) * (int64_t)Hkv + h) * BB;
-    if (KF16 && !is_v) {  // fp16 keys: stored as given, no rotation
-      place_key_f16<D>(blk, (int)(slot[i] & 15), lane, y[i]);
-      continue;
-    }
-    uint32_t u[E];
-    f16 scale;
-    if (is_v) codec_vector<D, VCODEC>(y[i], sw, lane, u, scale);
-    else if (KCODEC == TQ_CODEC_LLOYDMAX) codec_vector<D, TQ_CODEC_LLOYDMAX>(y[i], sw, lane, u, scale);
-    else codec_vector<D, TQ_CODEC_ABSMAX>(y[i], sw, lane, u, scale);
-    place_vector<D, KF16, VB>(blk, (int)(slot[i] & 15), lane, is_v != 0, u, scale);
-  }
+  for (int e = 0; e < E; e++) y[e] = __uint_as_float(__float_as_uint(y[e]) ^ smask[cb * E + e]);
+  uint32_t u[E];
+  f16 scale;
+  if (is_v) codec_vector<D, VCODEC>(y, cb, u, scale);
+  else if (KLUT) codec_vector<D, TQ_CODEC_LLOYDMAX>(y, cb, u, scale, lut_tbl);
+  else codec_vector<D, TQ_CODEC_ABSMAX>(y, cb, u, scale);
+  place_vector<D, KF16, VB>(blk, t, cb, is_v != 0, u, scale);
 }
 
 template <int D, typename T, int VC>
 hipError_t launch_v(const LaunchAppend& a, hipStream_t st) {
-  const int64_t nvec = (int64_t)a.n_tokens * a.Hkv * 2;
-  dim3 grid((unsigned)((nvec + 16 * VPT - 1) / (16 * VPT)));
+  const dim3 grid((unsigned)((a.n_tokens + 7) / 8), (unsigned)a.Hkv);
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
   if (a.k_codec == TQ_CODEC_LLOYDMAX)

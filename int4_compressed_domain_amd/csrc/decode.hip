@@ -381,8 +381,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   float ynew[E];
   uint32_t swnew = 0;
   if (!SPV && !hotwg && a.knew != nullptr && wv == NW - 1 && lane < 32) {
-    swnew = lane_signs<D>(a.sign_bits, lane & 15);
-    const int64_t off = ((int64_t)b * a.Hkv + h) * D + (lane & 15) * E;
+    swnew = lane_signs<D>(a.sign_bits, tq_blk16(lane & 15));
+    const int64_t off = ((int64_t)b * a.Hkv + h) * D + tq_blk16(lane & 15) * E;
     const void* src = (lane < 16) ? a.knew : a.vnew;
     if (a.new_dtype == TQ_F32) load_widen<float, E>(static_cast<const float*>(src) + off, ynew);
     else if (a.new_dtype == TQ_BF16) load_widen<uint16_t, E>(static_cast<const uint16_t*>(src) + off, ynew);
@@ -588,13 +588,15 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     if (lane < 32) {
       uint32_t un[E];
       f16 scn;
+      const int cb = tq_blk16(lane & 15);
       if (KF16 && lane < 16) {
-        place_key_f16<D>(tokblk, tnew, lane, ynew);  // fp16 key, no rotation
+        place_key_f16<D>(tokblk, tnew, cb, ynew);  // fp16 key, no rotation
       } else {
-        if (lane >= 16) codec_vector<D, C::VC>(ynew, swnew, lane & 15, un, scn);
-        else if (KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, swnew, lane & 15, un, scn);
-        else codec_vector<D, TQ_CODEC_LLOYDMAX>(ynew, swnew, lane & 15, un, scn);
-        place_vector<D, KF16, VB>(tokblk, tnew, lane & 15, lane >= 16, un, scn);
+        apply_signs<D>(ynew, swnew);
+        if (lane >= 16) codec_vector<D, C::VC>(ynew, cb, un, scn);
+        else if (KSUB) codec_vector<D, TQ_CODEC_ABSMAX>(ynew, cb, un, scn);
+        else codec_vector<D, TQ_CODEC_LLOYDMAX>(ynew, cb, un, scn);
+        place_vector<D, KF16, VB>(tokblk, tnew, cb, lane >= 16, un, scn);
       }
     }
     __hip_atomic_store(&tok_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);

@@ -254,7 +254,7 @@ int tq_kv_append(const tq_layout* L, void* pool, const void* k, const void* v, i
   if (n_tokens < 0 || !valid_dtype(in_dtype)) return TQ_EINVAL;
   if (n_tokens == 0) return TQ_OK;
   if (!pool || !k || !v || !slot_mapping) return TQ_EINVAL;
-  if ((int64_t)n_tokens * L->num_kv_heads * 2 > (int64_t)16 * 0x7fffffff) return TQ_EUNSUPPORTED;
+  if (L->num_kv_heads > 65535) return TQ_EUNSUPPORTED;  // (one grid row per kv head)
   if (validating()) {
     rc = validate_slots(L, n_tokens, slot_mapping, static_cast<hipStream_t>(stream));
     if (rc != TQ_OK) return rc;
