@@ -120,7 +120,14 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
 /* The first TQ_DECODE_COUNTER_BYTES bytes of a decode workspace hold per-(sequence,
  * kv head) arrival counters. They must be zero before the workspace is first used; every
- * tq_decode_attn call leaves them zero again. */
+ * tq_decode_attn call that completes leaves them zero again. A call whose kernel did not
+ * complete (a launch error, a device fault, a stream torn down mid-flight) can leave them
+ * non-zero, and later calls on that workspace would then merge at the wrong time and return
+ * wrong results without an error: clear the first TQ_DECODE_COUNTER_BYTES bytes again (or
+ * take a fresh zeroed workspace) after any failed call. How a split is published: its
+ * partial results are stored with device-coherent stores, the workgroup waits until the
+ * stores are complete, and only then increments the counter (a relaxed atomic); the
+ * workgroup that sees the final count reads the partials with device-coherent loads. */
 #define TQ_DECODE_COUNTER_BYTES ((size_t)4 << 20)
 
 typedef struct {
@@ -280,12 +287,6 @@ int tq_decode_attn_hotcold(const tq_layout* layout, const void* pool, const void
                            const int32_t* hot_lens, int32_t hot_cap, float attn_scale,
                            int32_t num_splits, float* out, void* workspace,
                            size_t workspace_bytes, void* stream);
-
-/* Measurement aid, not part of the method: reads bytes (a multiple of 16) of buf with a plain
- * streaming kernel, so that the decode's HBM rate can be set against the read rate a simple
- * kernel reaches on the same GPU. sink: device scratch of >= 8 * CUs * 256 * 4 bytes
- * (TQ_ENOSPC otherwise; 2 MiB always suffices), overwritten with the words' XOR per thread. */
-int tq_stream_read_probe(const void* buf, size_t bytes, void* sink, size_t sink_bytes, void* stream);
 
 /* Dequantize reference: dense K and V, [batch][num_kv_heads][max_context_len][head_dim]
  * of out_dtype (TQ_F32 or TQ_F16), rows at or past a sequence's length set to zero.

@@ -423,15 +423,6 @@ int tq_decode_attn_hotcold(const tq_layout* L, const void* pool, const void* q, 
                      hot_cap);
 }
 
-int tq_stream_read_probe(const void* buf, size_t bytes, void* sink, size_t sink_bytes, void* stream) {
-  if (bytes == 0) return TQ_OK;
-  if (!buf || !sink || bytes % 16 != 0) return TQ_EINVAL;
-  const int blocks = 8 * num_cus();
-  if (sink_bytes < (size_t)blocks * 256 * sizeof(uint32_t)) return TQ_ENOSPC;
-  return from_hip(tq_launch_stream_read(buf, bytes, static_cast<uint32_t*>(sink), blocks,
-                                        static_cast<hipStream_t>(stream)));
-}
-
 int tq_dequant_ref(const tq_layout* L, const void* pool, int32_t batch, const int32_t* block_table,
                    int32_t max_pages_per_seq, const int32_t* context_lens, int32_t max_context_len,
                    int32_t to_original_basis, int32_t out_dtype, void* k_out, void* v_out,

@@ -14,10 +14,12 @@ TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_ENOSPC, TQ_EDEVICE = 0, -1, -2, -3, -4
 CODEC_ABSMAX, CODEC_LLOYDMAX, CODEC_FP16, CODEC_ABSMAX3, CODEC_ABSMAX2 = 0, 1, 2, 3, 4
 F32, BF16, F16 = 0, 1, 2
 
+PROBE_LIB_PATH = os.path.join(HERE, "libtq_probe.so")  # measurement aid (include/tq_probe.h)
+
 EXPORTS = ("tq_status_str", "tq_page_bytes", "tq_kv_append", "tq_decode_workspace_size",
            "tq_decode_attn", "tq_append_decode_attn", "tq_decode_attn_sparse_v", "tq_dequant_ref",
-           "tq_dense_decode_attn", "tq_decode_attn_hotcold", "tq_stream_read_probe",
-           "tq_decode_attn_noalloc")
+           "tq_dense_decode_attn", "tq_decode_attn_hotcold", "tq_decode_attn_noalloc")
+PROBE_EXPORTS = ("tq_stream_read_probe",)
 
 
 class TQError(RuntimeError):
@@ -67,9 +69,6 @@ def _lib():
             L.tq_decode_attn_hotcold.argtypes = [LP, P, P, i32, i32, P, i32, P, i32, P, P, P, i32, f32,
                                                  i32, P, P, sz, P]
             L.tq_decode_attn_hotcold.restype = ctypes.c_int
-        if hasattr(L, "tq_stream_read_probe"):
-            L.tq_stream_read_probe.argtypes = [P, sz, P, sz, P]
-            L.tq_stream_read_probe.restype = ctypes.c_int
         L.tq_dense_decode_attn.argtypes = [LP, P, P, P, i32, i32, P, i32, f32, i32, P, P, sz, P]
         if hasattr(L, "tq_decode_attn_noalloc"):
             L.tq_decode_attn_noalloc.argtypes = [LP, P, P, i32, i32, P, i32, P, i32, f32, i32, P, P]
@@ -82,6 +81,24 @@ def _lib():
 
 def lib():
     return _lib()
+
+
+_PL = None
+
+
+def probe_lib():
+    """libtq_probe.so: the streaming-read probe."""
+    global _PL
+    if _PL is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise ImportError("libtq_probe.so is not built (run int4_compressed_domain_amd/build.py): "
+                              + PROBE_LIB_PATH)
+        L = ctypes.CDLL(PROBE_LIB_PATH)
+        L.tq_stream_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                           ctypes.c_size_t, ctypes.c_void_p]
+        L.tq_stream_read_probe.restype = ctypes.c_int
+        _PL = L
+    return _PL
 
 
 def make_layout(head_dim, num_q_heads, num_kv_heads, num_pages, sign_bits_ptr, k_codec=0,
@@ -187,8 +204,8 @@ def tq_dense_decode_attn(layout, k, v, q, context_lens, max_context_len, attn_sc
 
 def tq_stream_read_probe(buf, sink, stream=None):
     """Read every byte of buf (a device tensor) with the plain streaming kernel."""
-    _check(_lib().tq_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
-                                       sink.numel() * sink.element_size(), _stream(stream)),
+    _check(probe_lib().tq_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                            sink.numel() * sink.element_size(), _stream(stream)),
            "tq_stream_read_probe")
 
 

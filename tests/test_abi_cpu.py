@@ -11,8 +11,8 @@ from int4_compressed_domain_amd import tq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _header_functions():
-    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+def _header_functions(header="tq.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(tq_\w+)\s*\(", text, re.M)))
 
 
@@ -22,6 +22,12 @@ def test_library_exports_every_declared_function():
     lib = tq.lib()
     for n in names:
         assert hasattr(lib, n), n
+    # the measurement aid lives in a library of its own, not in the method's
+    pnames = _header_functions("tq_probe.h")
+    assert set(pnames) == set(tq.PROBE_EXPORTS), pnames
+    for n in pnames:
+        assert hasattr(tq.probe_lib(), n), n
+        assert not hasattr(lib, n), n
 
 
 def test_status_strings():
@@ -132,7 +138,7 @@ def test_sparse_v_argument_validation():
 
 
 def test_stream_read_probe_validation():
-    probe = tq.lib().tq_stream_read_probe
+    probe = tq.probe_lib().tq_stream_read_probe
     assert probe(FAKE, 0, None, 0, None) == tq.TQ_OK          # nothing to read
     assert probe(None, 64, FAKE, 1 << 21, None) == tq.TQ_EINVAL
     assert probe(FAKE, 60, FAKE, 1 << 21, None) == tq.TQ_EINVAL  # not a multiple of 16
