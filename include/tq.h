@@ -80,9 +80,9 @@
  *    synchronization and host copies per call).
  *  - GPU support: head_dim in {64, 128, 256}, group_size 32, page_size 16,
  *    1 <= num_q_heads / num_kv_heads <= 8, batch * num_kv_heads <= 2^20, appends with
- *    num_kv_heads <= 65535; decode with fp16
- *    keys at head_dim 64 and 128; sparse values with 4-bit values only (TQ_EUNSUPPORTED
- *    otherwise).
+ *    num_kv_heads <= 65535; decode with fp16 keys at head_dim 256 with
+ *    num_q_heads / num_kv_heads <= 4; sparse values with 4-bit values only
+ *    (TQ_EUNSUPPORTED otherwise).
  */
 #ifndef TQ_H
 #define TQ_H

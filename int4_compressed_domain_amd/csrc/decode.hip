@@ -362,7 +362,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   for (int k = 0; k < V; k++) qsgn[k] = a.sign_bits[2 * k + (lane >> 5)];
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int pcap = (hotwg || a.max_ctx == 0) ? 0 : min(p0 + pps, a.max_pages);
-  constexpr int PPL = (TQ_MAX_SPLIT_PAGES / NW + 63) / 64;
+  constexpr int PPL = (tq_max_split_pages(NW) / NW + 63) / 64;
   static_assert(PPL <= 4, "page ids of a wave: at most four registers");
   // held in a vector value, not an array: the selection below must stay in registers (as
   // an array it was turned into an indexed access and the ids were moved to LDS, one
@@ -422,7 +422,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   __shared__ int tok_ready;                    // the appended token is in tokblk
   __shared__ int wskip;                        // sparse values: pages skipped by the workgroup
   __shared__ uint32_t sgn_s[D / 32];           // sigma bits, read once for the final un-rotation
-  static_assert(NW >= 8, "one wave per query head in the rotations");
+  // one wave per query head in the rotations: the host admits r <= NW
+  static_assert(NW >= 4, "at least four waves");
   // Aliases of the ring: the query operands live in the last slot of every wave until the
   // page loop starts; after the loop, the per-wave results and the final-merge weights.
   static_assert(G * 64 * 8 * 2 <= NW * C::SLOT, "query operands must fit one ring slot row");
@@ -1599,13 +1600,9 @@ template <int D, int VB, bool SPV>
 hipError_t launch_dqs(const LaunchDecode& a, hipStream_t st, unsigned grid) {
   constexpr int VC = VB == 4 ? TQ_CODEC_ABSMAX : (VB == 3 ? TQ_CODEC_ABSMAX3 : TQ_CODEC_ABSMAX2);
   if (a.k_codec == TQ_CODEC_FP16) {
-    // fp16 keys: 8 waves; a staged page does not fit three times per wave at D = 256
-    if constexpr (D <= 128) {
-      constexpr int NWF = tq_decode_waves(D, TQ_CODEC_FP16, VC, SPV);
-      hipLaunchKernelGGL((decode_fused<D, TQ_CODEC_FP16, VB, NWF, SPV>), dim3(grid), dim3(64 * NWF), 0, st, a);
-    } else {
-      return hipErrorInvalidValue;
-    }
+    // fp16 keys: 8 waves, 4 at D = 256 (three staged pages per wave must fit the LDS ring)
+    constexpr int NWF = tq_decode_waves(D, TQ_CODEC_FP16, VC, SPV);
+    hipLaunchKernelGGL((decode_fused<D, TQ_CODEC_FP16, VB, NWF, SPV>), dim3(grid), dim3(64 * NWF), 0, st, a);
   } else if (a.k_codec == TQ_CODEC_LLOYDMAX) {
     constexpr int NW = tq_decode_waves(D, TQ_CODEC_LLOYDMAX, VC, SPV);
     hipLaunchKernelGGL((decode_fused<D, TQ_CODEC_LLOYDMAX, VB, NW, SPV>), dim3(grid), dim3(64 * NW), 0, st, a);

@@ -74,7 +74,8 @@ Split choose_split(int B, int Hkv, int D, int k_codec, int v_codec, int max_ctx,
                    bool sparse = false) {
   const int pages = (max_ctx + 15) / 16;
   const int nw = tq_decode_waves(D, k_codec, v_codec, sparse);
-  int min_s = (pages + TQ_MAX_SPLIT_PAGES - 1) / TQ_MAX_SPLIT_PAGES;  // page ids fit LDS
+  const int maxp = tq_max_split_pages(nw);
+  int min_s = (pages + maxp - 1) / maxp;  // page ids fit the waves' registers
   if (sparse) {
     const int per = TQ_SPARSE_PAGES_PER_WAVE * nw;
     if ((pages + per - 1) / per > min_s) min_s = (pages + per - 1) / per;
@@ -84,7 +85,7 @@ Split choose_split(int B, int Hkv, int D, int k_codec, int v_codec, int max_ctx,
     return make_split(pages, S > min_s ? S : min_s);
   }
   const int64_t units = (int64_t)B * Hkv;
-  const int64_t target = (int64_t)num_cus() * (D >= 256 ? 2 : 1);
+  const int64_t target = (int64_t)num_cus() * tq_decode_wgs_per_cu(D, k_codec);
   int64_t want = (target + units - 1) / units;
   // at least 4 pages per wave: below that the split merge costs more than the split saves
   // (1024 tokens, one head: 13.2 us with one split, 14.8 us with four)
@@ -288,8 +289,9 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
                            num_splits, out);
   if (rc != TQ_OK) return rc;
   if (max_pages_per_seq < 0 || (int64_t)max_context_len > 16LL * max_pages_per_seq) return TQ_EINVAL;
-  if ((int64_t)max_context_len > 16LL * TQ_MAX_SPLITS * TQ_MAX_SPLIT_PAGES) return TQ_EUNSUPPORTED;
-  if (L->k_codec == TQ_CODEC_FP16 && L->head_dim > 128) return TQ_EUNSUPPORTED;
+  const int nw = tq_decode_waves(L->head_dim, L->k_codec, L->v_codec, sparse_v != 0);
+  if ((int64_t)max_context_len > 16LL * TQ_MAX_SPLITS * tq_max_split_pages(nw)) return TQ_EUNSUPPORTED;
+  if (L->num_q_heads / L->num_kv_heads > nw) return TQ_EUNSUPPORTED;  // one wave per q head
   if (sparse_v && L->v_codec != TQ_CODEC_ABSMAX) return TQ_EUNSUPPORTED;
   if (sparse_v && (int64_t)max_context_len >
                       16LL * TQ_MAX_SPLITS * TQ_SPARSE_PAGES_PER_WAVE * tq_decode_waves(L->head_dim, L->k_codec, L->v_codec, true))
@@ -300,7 +302,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   if (max_context_len > 0 && (!pool || !block_table)) return TQ_EINVAL;
   Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, L->v_codec, max_context_len,
                          num_splits, sparse_v != 0);
-  const int64_t resident = (int64_t)num_cus() * (L->head_dim >= 256 ? 2 : 1);
+  const int64_t resident = (int64_t)num_cus() * tq_decode_wgs_per_cu(L->head_dim, L->k_codec);
   // fp16 tail: with automatic splits, at least 8 of them per unit, a grid that fits the chip
   // and a tail of at most 256 tokens, one split is given up for a workgroup per unit that
   // takes the whole tail and runs beside the pool's (its cost then hides behind theirs; a
@@ -309,7 +311,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   int hot_wg = 0;
   if (hot_k && num_splits == 0 && hot_cap <= 256 && s.splits >= 8 &&
       (int64_t)batch * L->num_kv_heads * s.splits <= resident &&
-      (int64_t)(s.splits - 1) * TQ_MAX_SPLIT_PAGES >= (max_context_len + 15) / 16) {
+      (int64_t)(s.splits - 1) * tq_max_split_pages(nw) >= (max_context_len + 15) / 16) {
     s = make_split((max_context_len + 15) / 16, s.splits - 1);
     hot_wg = 1;
   }

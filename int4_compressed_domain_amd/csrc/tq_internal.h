@@ -71,8 +71,10 @@ constexpr int tq_value_bits(int v_codec) { return TQ_VALUE_BITS(v_codec); }
 #endif
 // Wavefronts per fused-decode workgroup; each workgroup owns one (sequence, kv head,
 // context split). Pages staged in LDS (fp16 keys, 3- and 2-bit values, sparse values):
-// 16 waves fill a CU when the kernel fits in 128 registers per lane; fp16 keys and D = 256
-// take 8 (a staged fp16-key page is 41*D bytes, three per wave fit the LDS ring). Pages
+// 16 waves fill a CU when the kernel fits in 128 registers per lane; fp16 keys or D = 256
+// take 8 (a staged fp16-key page is 41*D bytes, three per wave fit the LDS ring), fp16 keys
+// at D = 256 (10.5 KB a page) 4, one workgroup per CU (the ring takes 123 KB), which limits
+// that variant to 4 query heads per kv head (one wave per head in the rotations). Pages
 // streamed through registers (4-bit keys and values, D <= 128): two sets of four pages per
 // wave, one computed while the other is in flight, need more than 128 registers, so 8
 // waves of up to 256.
@@ -85,6 +87,7 @@ constexpr bool tq_decode_reg_path(int D, int k_codec, int value_bits, bool spars
          (k_codec == TQ_CODEC_ABSMAX || (TQ_REG_LUT && k_codec == TQ_CODEC_LLOYDMAX));
 }
 constexpr int tq_decode_waves(int D, int k_codec, int v_codec, bool sparse) {
+  if (D > 128 && k_codec == TQ_CODEC_FP16) return 4;
   if (D > 128 || k_codec == TQ_CODEC_FP16) return 8;
   if (tq_decode_reg_path(D, k_codec, tq_value_bits(v_codec), sparse)) return TQ_REG_WAVES;
   return 16;
@@ -95,7 +98,15 @@ constexpr int tq_block_bytes(int D, int k_codec, int v_codec = TQ_CODEC_ABSMAX) 
 }
 constexpr int TQ_DECODE_WAVES = 4;   // dense baseline workgroups
 constexpr int TQ_MAX_SPLITS = 128;   // context splits per (sequence, kv head)
-constexpr int TQ_MAX_SPLIT_PAGES = 2048;  // pages per split (their ids are staged in LDS)
+constexpr int TQ_MAX_SPLIT_PAGES = 2048;  // pages per split (their ids are held in registers)
+// Pages per split of a variant with nw waves: every wave keeps the ids of its pages in at
+// most four registers (256 ids).
+constexpr int tq_max_split_pages(int nw) { return 256 * nw < TQ_MAX_SPLIT_PAGES ? 256 * nw : TQ_MAX_SPLIT_PAGES; }
+// Fused-decode workgroups resident per CU (LDS-bound): two at D = 256 with compact keys,
+// one otherwise.
+constexpr int tq_decode_wgs_per_cu(int D, int k_codec) {
+  return (D >= 256 && k_codec != TQ_CODEC_FP16) ? 2 : 1;
+}
 constexpr int TQ_LPT_MAX_BATCH = 256;    // longest-first workgroup order up to this batch
 constexpr int TQ_SPARSE_PAGES_PER_WAVE = 32;  // sparse values: page maxima kept per wave
 constexpr int TQ_MAX_HOT = 1024;         // fp16 tail tokens per (sequence, kv head)

@@ -6,7 +6,7 @@ CPU oracle can take their inputs from it. Every array comes from numpy's PCG64
 (``default_rng``) with a seed derived from (seed, purpose, sequence), so a sequence's
 tokens do not depend on how the caller chunks the generation.
 
-Six workloads, named by what they are:
+The workloads, named by what they are:
 
   single_head_1k     1 head, D=128, 1024 cached tokens, fp32, N(0,1) with 4 outlier
                      channels x20 on K and V (q not scaled)
@@ -21,7 +21,10 @@ Six workloads, named by what they are:
                      heads, D=128, keys by the LUT codec, values by abs-max
   llama70b_b1_128k_k16v4
                      the 128K workload with keys kept in fp16 and values in 4 bits (the
-                     asymmetric mode)
+                     asymmetric mode); _k16v3 with 3-bit values, _k4v2 with 4-bit keys and
+                     2-bit values
+  gemma_d256_32k_k16v4
+                     the D=256 workload with fp16 keys and 4-bit values
 
 Each step of a workload appends one new token per decoding sequence (its last token;
 the other L_b - 1 tokens are the resident cache) plus, for mixed_serving, the 2048-token
@@ -90,6 +93,9 @@ WORKLOADS = {
     "llama70b_b1_128k_k16v3": Workload("llama70b_b1_128k_k16v3", 1, 64, 8, 128, 131072, "bf16",
                                        1.0 / math.sqrt(128), k_codec=CODEC_FP16,
                                        v_codec=CODEC_ABSMAX3, dist="lognormal_spikes"),
+    # the D = 256 workload with fp16 keys and 4-bit values (the manual's recommended mode)
+    "gemma_d256_32k_k16v4": Workload("gemma_d256_32k_k16v4", 4, 16, 8, 256, 32768, "bf16", 1.0,
+                                     k_codec=CODEC_FP16, dist="lognormal_spikes"),
     # 4-bit keys + 2-bit values
     "llama70b_b1_128k_k4v2": Workload("llama70b_b1_128k_k4v2", 1, 64, 8, 128, 131072, "bf16",
                                       1.0 / math.sqrt(128), v_codec=CODEC_ABSMAX2,

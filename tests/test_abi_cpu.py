@@ -188,11 +188,15 @@ def test_page_bytes():
 
 
 def test_fp16_keys_decode_limits():
-    """fp16 keys decode at head_dim 64 and 128; 256 is rejected before any launch."""
-    L = _layout(head_dim=256, num_q_heads=16, num_kv_heads=8, k_codec=tq.CODEC_FP16)
+    """fp16 keys decode at every head_dim; at 256 (four-wave workgroups, one wave per query
+    head in the rotations) with at most 4 query heads per kv head: 8 is rejected before any
+    launch, 2 passes validation up to the workspace check."""
+    L = _layout(head_dim=256, num_q_heads=64, num_kv_heads=8, k_codec=tq.CODEC_FP16)
     assert _decode(L) == tq.TQ_EUNSUPPORTED
     assert _append_decode(L) == tq.TQ_EUNSUPPORTED
     assert _append(L, pool=None) == tq.TQ_EINVAL     # appending itself is supported
+    L2 = _layout(head_dim=256, num_q_heads=16, num_kv_heads=8, k_codec=tq.CODEC_FP16)
+    assert _decode(L2, wsb=16) == tq.TQ_ENOSPC
     assert _decode(_layout(k_codec=tq.CODEC_FP16), q=None) == tq.TQ_EINVAL
 
 

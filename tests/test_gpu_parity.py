@@ -90,8 +90,8 @@ def test_head_dims_and_gqa(D, r):
     _check_case(c)
 
 
-@pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("r", [1, 4, 8])
+@pytest.mark.parametrize("D,r", [(64, 1), (64, 4), (64, 8), (128, 1), (128, 4), (128, 8),
+                                 (256, 1), (256, 2), (256, 4)])
 def test_fp16_keys(D, r):
     """fp16 keys + 4-bit values: pool bytes equal the oracle's (keys as fp16 of the input,
     values rotated and quantized), attention within the tolerance, across split counts."""
@@ -110,7 +110,8 @@ V3, V2 = W.CODEC_ABSMAX3, W.CODEC_ABSMAX2
 
 @pytest.mark.parametrize("D,r,k_codec,v_codec", [(64, 4, 0, V3), (128, 8, 0, V3), (128, 8, 2, V3),
                                                  (256, 2, 0, V3), (128, 4, 1, V2), (128, 8, 0, V2),
-                                                 (64, 2, 2, V2), (256, 4, 1, V2)])
+                                                 (64, 2, 2, V2), (256, 4, 1, V2), (256, 2, 2, V3),
+                                                 (256, 4, 2, V2)])
 def test_low_bit_values(D, r, k_codec, v_codec):
     """3-bit and 2-bit values with each key codec: packed pool bytes equal the oracle's
     (appends of many tokens into shared pages), attention within the tolerance for edge
@@ -411,7 +412,8 @@ def _full_size_pairs(w):
 
 @pytest.mark.parametrize("name", ["single_head_1k", "llama8b_b16_8k", "llama70b_b1_128k",
                                   "gemma_d256_32k", "mixed_serving", "llama70b_b1_128k_k16v4",
-                                  "llama70b_b1_128k_k16v3", "llama70b_b1_128k_k4v2"])
+                                  "llama70b_b1_128k_k16v3", "llama70b_b1_128k_k4v2",
+                                  "gemma_d256_32k_k16v4"])
 def test_full_size_workloads(name):
     """The benchmark's step at full size: every token but each sequence's last is resident,
     the mixed-serving prefill chunk is appended with tq_kv_append, and one
