@@ -252,7 +252,11 @@ def time_steps(S, steps, warmup):
     for g in graphs[:2]:
         g.replay()
         torch.cuda.synchronize()
-        if not torch.equal(S.out, eager):
+        if S.sparse_v is None:
+            same = torch.equal(S.out, eager)
+        else:  # which value pages are skipped depends on the order the splits finish their keys
+            same = torch.allclose(S.out, eager, rtol=1e-4, atol=1e-5)
+        if not same:
             raise RuntimeError("graph replay output differs from the eager step")
     for g in graphs:  # untimed replays, ~0.3 s each: clocks ramp up and settle
         t0 = time.perf_counter()

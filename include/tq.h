@@ -81,7 +81,7 @@
  *  - GPU support: head_dim in {64, 128, 256}, group_size 32, page_size 16,
  *    1 <= num_q_heads / num_kv_heads <= 8, batch * num_kv_heads <= 2^20, appends with
  *    num_kv_heads <= 65535; decode with fp16 keys at head_dim 256 with
- *    num_q_heads / num_kv_heads <= 4; sparse values with 4-bit values only
+ *    num_q_heads / num_kv_heads <= 4; sparse values with batch * num_kv_heads <= 2^16
  *    (TQ_EUNSUPPORTED otherwise).
  */
 #ifndef TQ_H
@@ -242,14 +242,18 @@ int tq_append_decode_attn(const tq_layout* layout, void* pool, const void* k_las
  * sparse-V threshold: value dequantization is skipped where the attention weight is below
  * it, 1e-6 by default). Each context split first reads the keys of all its pages, then
  * the keys and values of the pages it keeps. The weight compared is exp(score - M), M the
- * largest score of the split, which bounds the token's final softmax weight from above; so
- * the result differs from tq_decode_attn only by dropped terms w_t * v_t with every
- * w_t < v_threshold (the softmax normalizer still counts every token). Which pages are
- * dropped depends on the split count; v_threshold = 0 drops none and is tq_decode_attn,
- * bit for bit. Keys are read twice for kept pages: this pays where attention is peaky.
- * The split count is at least the context's pages / (32 * waves per workgroup), which
+ * largest score the (sequence, kv head) has shown so far: the split's own largest, raised
+ * to the largest that the splits done with their keys before it have published (an atomic
+ * maximum in the workspace's counter area, cleared again by the split that merges). M never
+ * exceeds the final maximum, so exp(score - M) bounds the token's final softmax weight from
+ * above, and the result differs from tq_decode_attn only by dropped terms w_t * v_t with
+ * every w_t < v_threshold (the softmax normalizer still counts every token). Which pages
+ * are dropped depends on the split count and on the order in which splits finish their
+ * keys; v_threshold = 0 drops none and is tq_decode_attn, bit for bit. Keys are read twice
+ * for kept pages: this pays where attention is peaky. Any value width (4, 3, 2 bits). The
+ * split count is at least the context's pages / (32 * waves per workgroup), which
  * tq_decode_workspace_size includes.
- *   v_threshold     in [0, 1), TQ_EINVAL otherwise; 4-bit values only (TQ_EUNSUPPORTED)
+ *   v_threshold     in [0, 1), TQ_EINVAL otherwise
  *   v_pages_skipped optional device uint64: the number of (page, kv head) value blocks
  *                   skipped is added to it (NULL: not counted)
  *   other arguments, workspace and errors as tq_decode_attn.

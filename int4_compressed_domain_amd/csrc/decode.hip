@@ -159,17 +159,17 @@ __device__ __forceinline__ void stage_page(const uint8_t* blk, uint32_t base, in
 
 // Sparse values, first pass: the key part of a page ([K][K scales]) alone, into the same slot
 // layout as stage_page.
-template <int D, int KC>
+template <int D, int KC, int VB>
 struct SplitDma {
-  using C = Cfg<D, KC>;
+  using C = Cfg<D, KC, VB>;
   static constexpr int NSK = C::KF16 ? 0 : (8 * C::G + 63) / 64;  // dword DMAs, K scales
   static constexpr int NK_OPS = (C::KF16 ? C::G : C::NK) + NSK;
 };
 
 // The same, compact: K scales right after the K indices (a half slot, see Cfg::HS).
-template <int D, int KC>
+template <int D, int KC, int VB>
 __device__ __forceinline__ void stage_kc(const uint8_t* blk, uint32_t base, int lane) {
-  using C = Cfg<D, KC>;
+  using C = Cfg<D, KC, VB>;
   static_assert(C::HS, "compact key staging needs 4-bit keys");
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
   const uint32_t lo = (uint32_t)lane * C::KB;
@@ -179,13 +179,13 @@ __device__ __forceinline__ void stage_kc(const uint8_t* blk, uint32_t base, int 
     else dma4(r, lo + c * 4, 0u, base + c * 256);
   }
 #pragma unroll
-  for (int c = 0; c < SplitDma<D, KC>::NSK; c++)
+  for (int c = 0; c < SplitDma<D, KC, VB>::NSK; c++)
     if (c * 64 + lane < 8 * C::G) dma4(r, 4 * (c * 64 + lane), (uint32_t)C::BS, base + C::KREG + 256 * c);
 }
 
-template <int D, int KC>
+template <int D, int KC, int VB>
 __device__ __forceinline__ void stage_k(const uint8_t* blk, uint32_t base, int lane) {
-  using C = Cfg<D, KC>;
+  using C = Cfg<D, KC, VB>;
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, C::BB, 0x00020000);
   if constexpr (C::KF16) {
 #pragma unroll
@@ -198,7 +198,7 @@ __device__ __forceinline__ void stage_k(const uint8_t* blk, uint32_t base, int l
       else dma4(r, lo + c * 4, 0u, base + c * 256);
     }
 #pragma unroll
-    for (int c = 0; c < SplitDma<D, KC>::NSK; c++)
+    for (int c = 0; c < SplitDma<D, KC, VB>::NSK; c++)
       if (c * 64 + lane < 8 * C::G) dma4(r, 4 * (c * 64 + lane), (uint32_t)C::BS, base + C::SOFF + 256 * c);
   }
 }
@@ -308,7 +308,6 @@ __device__ __forceinline__ float widen_q_bits(uint32_t x, int dt) {
 template <int D, int KCODEC, int VB, int NW, bool SPV>
 __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   using C = Cfg<D, KCODEC, VB>;
-  static_assert(!SPV || VB == 4, "sparse values: 4-bit values only");
   constexpr int G = C::G, BB = C::BB, NT = 64 * NW, V = D / 64;
   constexpr bool KF16 = C::KF16;
   // ring slots per wave: as many as ~144 KB of LDS holds, at most 8 (NSLOT - 1 pages in flight)
@@ -421,6 +420,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   __shared__ int lead_n;                       // furthest page-loop step reached by a wave
   __shared__ int tok_ready;                    // the appended token is in tokblk
   __shared__ int wskip;                        // sparse values: pages skipped by the workgroup
+  __shared__ float mpub[8];                    // sparse values: the unit's maximum so far, per head
   __shared__ uint32_t sgn_s[D / 32];           // sigma bits, read once for the final un-rotation
   // one wave per query head in the rotations: the host admits r <= NW
   static_assert(NW >= 4, "at least four waves");
@@ -496,8 +496,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     else return ring[n % NSLOT][wv];
   };
   auto stage_keys = [&](int n) {
-    if constexpr (C::HS) stage_kc<D, KCODEC>(page_blk(n), k_lds(n), lane);
-    else stage_k<D, KCODEC>(page_blk(n), k_lds(n), lane);
+    if constexpr (C::HS) stage_kc<D, KCODEC, VB>(page_blk(n), k_lds(n), lane);
+    else stage_k<D, KCODEC, VB>(page_blk(n), k_lds(n), lane);
   };
   auto stage_first = [&]() {
 #pragma unroll
@@ -1059,7 +1059,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
           stage_keys(nis);
           nis++;
         }
-      wait_pages_in_flight<SplitDma<D, KCODEC>::NK_OPS, NR - 2>(max(0, min(NR - 2, nis - na - 2)));
+      wait_pages_in_flight<SplitDma<D, KCODEC, VB>::NK_OPS, NR - 2>(max(0, min(NR - 2, nis - na - 2)));
       const int pa = p0 + wv + NW * na;
       kstep(na, k_slot(na), k_slot(na + 1), pa, pa + NW);
     }
@@ -1069,7 +1069,20 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; w++) M = fmaxf(M, mml[w][hl][0]);
+    // The unit's maximum so far decides which pages are skipped: every split publishes its
+    // own per head (an atomic max on an order-preserving integer image, in the workspace's
+    // zeroed counter area) and reads the largest published. It is at most the unit's final
+    // maximum, so a page below the threshold relative to it is below it relative to the
+    // final one too; the last split to arrive clears the entries again.
+    if (ns > 1 && wv == 0 && lane < 8) {
+      const uint32_t bits = __float_as_uint(M);
+      const uint32_t e = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+      uint32_t* slot = reinterpret_cast<uint32_t*>(a.counters) + TQ_SPARSE_MAX_BASE + 8 * u + lane;
+      const uint32_t o = max(e, __hip_atomic_fetch_max(slot, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      mpub[lane] = __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+    }
     __syncthreads();  // (mml is written again in the epilogue)
+    const float Mu = ns > 1 ? mpub[hl] : M;
     const float l_all = (m_run == -INFINITY) ? 0.0f : l_run * __builtin_amdgcn_exp2f((m_run - M) * down);
     m_run = M;
     nmd = -M * down;
@@ -1079,7 +1092,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int k = 0; k < NPM; k++) {
       const int n = 8 * k + (lane >> 3);
-      const bool hit = live && n < npw && (pmreg[k] - M) * down >= l2t;
+      const bool hit = live && n < npw && (pmreg[k] - Mu) * down >= l2t;
       const uint64_t bal = __ballot(hit);
 #pragma unroll
       for (int q = 0; q < 8; q++)
@@ -1476,6 +1489,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     __syncthreads();
     if (!last_flag) return;
     if (tid == 0) __hip_atomic_store(&a.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (SPV && tid < 8)  // every split of the unit has read the published maxima
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(a.counters) + TQ_SPARSE_MAX_BASE + 8 * u + tid, 0u,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // ---- the last workgroup of unit u merges every split (coherent sc1 loads) ----------
     // thread = (split group grp, head hd, 4 dims d4); split group grp takes splits
     // grp, grp + ngrp, ...; the first NLD of them are loaded before the weights are known.
@@ -1623,7 +1639,8 @@ hipError_t launch_d(const LaunchDecode& a, hipStream_t st) {
   const unsigned grid = (unsigned)(8 * ((U + 7) / 8) * (a.splits + a.hot_wg));
   const int vb = tq_value_bits(a.v_codec);
   if (a.sparse_v) {
-    if (vb != 4) return hipErrorInvalidValue;
+    if (vb == 3) return launch_dqs<D, 3, true>(a, st, grid);
+    if (vb == 2) return launch_dqs<D, 2, true>(a, st, grid);
     return launch_dqs<D, 4, true>(a, st, grid);
   }
   if (vb == 3) return launch_dqs<D, 3, false>(a, st, grid);

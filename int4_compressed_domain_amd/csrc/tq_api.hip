@@ -271,6 +271,9 @@ size_t tq_decode_workspace_size(const tq_layout* L, int32_t batch, int32_t max_c
   return workspace_bytes(L, batch, max_context_len, num_splits);
 }
 
+static_assert(((size_t)TQ_SPARSE_MAX_BASE + 8 * (size_t)TQ_SPARSE_MAX_UNITS) * 4 <= TQ_DECODE_COUNTER_BYTES,
+              "the sparse maxima must fit the counter area");
+
 // no_alloc: the workspace is the library's static scratch (tq_decode_attn_noalloc): its
 // arrival counters are cleared by a fill kernel before the decode, and the TQ_VALIDATE
 // host checks (which synchronize and copy to host buffers) are not run.
@@ -292,7 +295,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   const int nw = tq_decode_waves(L->head_dim, L->k_codec, L->v_codec, sparse_v != 0);
   if ((int64_t)max_context_len > 16LL * TQ_MAX_SPLITS * tq_max_split_pages(nw)) return TQ_EUNSUPPORTED;
   if (L->num_q_heads / L->num_kv_heads > nw) return TQ_EUNSUPPORTED;  // one wave per q head
-  if (sparse_v && L->v_codec != TQ_CODEC_ABSMAX) return TQ_EUNSUPPORTED;
+  if (sparse_v && (int64_t)batch * L->num_kv_heads > TQ_SPARSE_MAX_UNITS) return TQ_EUNSUPPORTED;
   if (sparse_v && (int64_t)max_context_len >
                       16LL * TQ_MAX_SPLITS * TQ_SPARSE_PAGES_PER_WAVE * tq_decode_waves(L->head_dim, L->k_codec, L->v_codec, true))
     return TQ_EUNSUPPORTED;
@@ -403,7 +406,6 @@ int tq_decode_attn_sparse_v(const tq_layout* L, const void* pool, const void* q,
                             size_t workspace_bytes_, unsigned long long* v_pages_skipped,
                             void* stream) {
   if (!(v_threshold >= 0.0f && v_threshold < 1.0f)) return TQ_EINVAL;
-  if (check_layout(L, true) == TQ_OK && L->v_codec != TQ_CODEC_ABSMAX) return TQ_EUNSUPPORTED;
   // a zero threshold drops nothing: the dense decode, bit for bit
   return decode_impl(L, pool, nullptr, nullptr, 0, q, q_dtype, batch, block_table,
                      max_pages_per_seq, context_lens, max_context_len, attn_scale, num_splits, out,

@@ -109,5 +109,10 @@ constexpr int tq_decode_wgs_per_cu(int D, int k_codec) {
 }
 constexpr int TQ_LPT_MAX_BATCH = 256;    // longest-first workgroup order up to this batch
 constexpr int TQ_SPARSE_PAGES_PER_WAVE = 32;  // sparse values: page maxima kept per wave
+// Sparse values: per-(unit, head) published maxima, 8 words per unit from word 2^19 of the
+// workspace's counter area (zero between calls like the arrival counters), so at most
+// 2^16 units.
+constexpr int TQ_SPARSE_MAX_BASE = 1 << 19;
+constexpr int TQ_SPARSE_MAX_UNITS = 1 << 16;
 constexpr int TQ_MAX_HOT = 1024;         // fp16 tail tokens per (sequence, kv head)
 constexpr int TQ_MAX_UNITS = 1 << 20;  // sequences x kv heads per call

@@ -133,8 +133,11 @@ def test_sparse_v_argument_validation():
     assert _sparse(L, wsb=16) == tq.TQ_ENOSPC
     assert _sparse(L, batch=0, q=None, out=None) == tq.TQ_OK
     # sparse values are implemented for 4-bit values only
-    assert _sparse(_layout(v_codec=tq.CODEC_ABSMAX3)) == tq.TQ_EUNSUPPORTED
-    assert _sparse(_layout(v_codec=tq.CODEC_ABSMAX2)) == tq.TQ_EUNSUPPORTED
+    # every value width is accepted (up to the workspace check here)
+    assert _sparse(_layout(v_codec=tq.CODEC_ABSMAX3), wsb=16) == tq.TQ_ENOSPC
+    assert _sparse(_layout(v_codec=tq.CODEC_ABSMAX2), wsb=16) == tq.TQ_ENOSPC
+    # the published maxima take 8 words per (sequence, kv head) of the counter area
+    assert _sparse(_layout(), batch=(1 << 16) // 8 + 1) == tq.TQ_EUNSUPPORTED
 
 
 def test_stream_read_probe_validation():

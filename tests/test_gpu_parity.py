@@ -141,17 +141,19 @@ def _sparse_gpu(c, thr, num_splits=0):
     return out.cpu().numpy(), int(skipped.item())
 
 
-@pytest.mark.parametrize("name,k_codec", [("llama70b_b1_128k", 0), ("gemma_d256_32k", 0),
-                                          ("mixed_serving", 1), ("llama70b_b1_128k", 2)])
-def test_sparse_values(name, k_codec):
+@pytest.mark.parametrize("name,k_codec,v_codec", [("llama70b_b1_128k", 0, 0), ("gemma_d256_32k", 0, 0),
+                                                  ("mixed_serving", 1, 0), ("llama70b_b1_128k", 2, 0),
+                                                  ("llama70b_b1_128k", 2, V3), ("llama70b_b1_128k", 0, V2),
+                                                  ("gemma_d256_32k", 2, V3)])
+def test_sparse_values(name, k_codec, v_codec):
     """Sparse values: threshold 0 reproduces the dense decode bit for bit; at 1e-6 the
     result stays within the tolerance plus the oracle's bound on the dropped terms
     (sum of w_t |v_t| over weights below the threshold), for several split counts, and
-    spiky attention lets most value pages be skipped."""
+    spiky attention lets most value pages be skipped; 4-, 3- and 2-bit values."""
     base = W.WORKLOADS[name]
     w = W.Workload(name + "_sv", 3, base.q_heads, base.kv_heads, base.head_dim, 3000, base.dtype,
-                   base.attn_scale, k_codec=k_codec, dist="lognormal_spikes")
-    _say("case sparse values", name, "k_codec", k_codec)
+                   base.attn_scale, k_codec=k_codec, v_codec=v_codec, dist="lognormal_spikes")
+    _say("case sparse values", name, "k_codec", k_codec, "v_codec", v_codec)
     c = Case(w, seed=23, lens=[3000, 1234, 77])
     c.fill()
     dense = c.decode_gpu()
@@ -728,7 +730,7 @@ def test_pool_beyond_4gib(D, kv, k_codec, v_codec):
     err = attn_err(o, exact)
     _say("   decode: max normwise err %.3e" % err.max())
     assert np.all(np.isfinite(o)) and err.max() <= ATTN_TOL
-    if v_codec == 0:
+    if True:  # sparse values, every value width
         _, bound = c_oracle.decode_sparse_v(c.opool, D, w.q_heads, kv, c.sb, c.bt, c.lens, c.q32,
                                             w.attn_scale, 1e-6, k_codec=k_codec, v_codec=v_codec)
         so = torch.full_like(out, float("nan"))
