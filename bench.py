@@ -254,8 +254,10 @@ def time_steps(S, steps, warmup):
         torch.cuda.synchronize()
         if S.sparse_v is None:
             same = torch.equal(S.out, eager)
-        else:  # which value pages are skipped depends on the order the splits finish their keys
-            same = torch.allclose(S.out, eager, rtol=1e-4, atol=1e-5)
+        else:  # which value pages are skipped depends on the order the splits finish their
+            # keys: the two runs drop different terms below the threshold (normwise check)
+            diff = (S.out - eager).abs().amax(dim=2)
+            same = bool((diff <= 2e-3 * eager.abs().amax(dim=2) + 1e-6).all())
         if not same:
             raise RuntimeError("graph replay output differs from the eager step")
     for g in graphs:  # untimed replays, ~0.3 s each: clocks ramp up and settle
@@ -555,6 +557,13 @@ def main():
     peak_meas = stream_read_peak(dev)
     rec["roofline"]["measured_read_peak"] = round(peak_meas, 1)
     rec["roofline"]["frac_of_measured_peak"] = round(rec["roofline"]["achieved"] / peak_meas, 4)
+    if "fp16_dequant_then_attend" in rec:
+        # the same baseline's floor: its HBM bytes (packed pool read, dense fp16 K and V written
+        # then read) moved at the measured read peak, however fast its kernels were made
+        b = rec["fp16_dequant_then_attend"]
+        moved = rec["algorithmic_bytes"] + 2 * b["dense_kv_bytes"]
+        b["floor_us_at_measured_read_peak"] = round(moved / (peak_meas * 1e9) * 1e6, 2)
+        b["speedup_of_fused_vs_floor"] = round(b["floor_us_at_measured_read_peak"] / dec_mean, 2)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
         rec["cpu_baseline"].update(one_core_baselines(name))
