@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--cpu-oracle-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--profile", type=int, default=0,
                     help="run this many eager steps and exit: for profilers")
+    ap.add_argument("--profile-append", type=int, default=0,
+                    help="run this many appends of the prefill chunk (mixed_serving) alone and exit: "
+                         "for profilers")
     return ap.parse_args()
 
 
@@ -489,6 +492,14 @@ def main():
             S.step(i)
         torch.cuda.synchronize()
         log("profile mode: %d eager steps done" % args.profile)
+        return
+    if args.profile_append:
+        if S.k_pre is None:
+            sys.exit("--profile-append needs a workload with a prefill chunk")
+        for i in range(args.profile_append):
+            S.prefill(i)
+        torch.cuda.synchronize()
+        log("profile mode: %d prefill-chunk appends done" % args.profile_append)
         return
     K, ms, ev_ms, dec_mean, pre_mean = time_steps(S, args.steps, args.warmup)
     value = S.alg_bytes / (ms * 1e-3) / 1e9

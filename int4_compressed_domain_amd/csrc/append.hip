@@ -38,8 +38,13 @@ __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
   const int64_t slot_in = slots[tc];
   float y[E];
   load_widen<TIn, E>((is_v ? vin : kin) + ((size_t)tc * Hkv + h) * D + cb * E, y);
-  for (int i = threadIdx.x; i < D; i += 256) smask[i] = ((sign_bits[i >> 5] >> (i & 31)) & 1u) << 31;
-  if constexpr (KLUT) tq_lut_table_fill(lut_tbl, threadIdx.x);
+  // (both small loads issued before either is used: one wait covers them and the above)
+  const int tid = threadIdx.x;
+  const uint32_t sword = tid < D ? sign_bits[tid >> 5] : 0u;
+  u32x2 tent = {0u, 0u};
+  if constexpr (KLUT) tent = tq_lut_table_entry(tid);
+  if (tid < D) smask[tid] = ((sword >> (tid & 31)) & 1u) << 31;
+  if (KLUT && tid < tq_lutb::NB) lut_tbl[tid] = tent;
   __syncthreads();
   const int64_t slot = tok < n_tokens ? slot_in : -1;
   if (slot < 0) return;  // a skipped token, or past the end: the same for the 16 lanes

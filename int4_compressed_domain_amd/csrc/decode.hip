@@ -322,7 +322,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   constexpr bool REG = tq_decode_reg_path(D, KCODEC, VB, SPV);
   constexpr int SW = (C::SCB / 4 + 63) / 64;  // scale dwords per lane of a page (register path)
   constexpr int RG = REG ? G : 1;             // index dwords per lane of a page region
-  constexpr int PPS = TQ_REG_PAGES_PER_STEP;  // register path: pages per step (2 or 4)
+  // register path: pages per step (2 or 4; sparse values' first pass streams the keys
+  // alone, half a page's bytes, so it takes 4 to keep as many bytes in flight)
+  constexpr int PPS = SPV ? 4 : TQ_REG_PAGES_PER_STEP;
   constexpr int NPR = PPS / 2;                // page pairs per step
   static_assert(!REG || 2 * PPS * C::SCB <= C::SLOT, "the scale blocks of both page sets in one ring slot");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       }
     }
   };
-  // Register path: two page sets of four pages, X (step st) and Y (step st + 1), one being
+  // Register path: two page sets of PPS pages, X (step st) and Y (step st + 1), one being
   // computed while the other is in flight. A page n >= npw is a dummy load of one 16-byte
   // line (every lane the same address in the wave's last page), so that every step issues
   // the same loads and the compiler's vmcnt waits stay exact.
@@ -532,6 +534,24 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
     for (int i = 0; i < PPS; i++) ldp(PPS * st + i, k[i], v[i], sw[i]);
   };
+  // sparse values on the register path, first pass: a page's K indices and K scales only
+  // (the first half of its scale block), with the same dummy loads past the wave's end
+  auto ldk = [&](int n, uint32_t (&k)[RG], uint32_t (&sw)[SW]) {
+    if constexpr (REG) {
+      const bool real = n < npw;
+      const uint8_t* blk = page_blk(real ? n : npw - 1);
+      ld_nt<C::KB>(blk + (real ? (uint32_t)lane * C::KB : 0u), k);
+#pragma unroll
+      for (int i = 0; i < SW; i++) {
+        const int dw = real ? min(64 * i + lane, C::SCB / 8 - 1) : 0;
+        ld_nt<4>(blk + C::BS + 4 * dw, &sw[i]);
+      }
+    }
+  };
+  auto ldkstep = [&](int st, uint32_t (&k)[PPS][RG], uint32_t (&sw)[PPS][SW]) {
+#pragma unroll
+    for (int i = 0; i < PPS; i++) ldk(PPS * st + i, k[i], sw[i]);
+  };
   // Register path: only the first pages are requested before the query is prepared. A
   // wave's loads issue in order, and more than the memory pipeline holds would stall it at
   // the load instructions, holding back the rotation and the barriers behind them (all
@@ -540,7 +560,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   if constexpr (REG) {
     if (npw > 0) {
 #pragma unroll
-      for (int i = 0; i < EARLY; i++) ldp(i, xk[i], xv[i], xs[i]);
+      for (int i = 0; i < EARLY; i++) {
+        if constexpr (SPV) ldk(i, xk[i], xs[i]);
+        else ldp(i, xk[i], xv[i], xs[i]);
+      }
     }
   } else {
     stage_first();  // (the query operands go to the last slot, which these loads do not use)
@@ -632,9 +655,15 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   if constexpr (!REG) __syncthreads();
   if constexpr (REG) {  // the rest of the first two steps' pages
     if (npw > 0) {
+      if constexpr (SPV) {
 #pragma unroll
-      for (int i = EARLY; i < PPS; i++) ldp(i, xk[i], xv[i], xs[i]);
-      ldstep(1, yk, yv, ys);
+        for (int i = EARLY; i < PPS; i++) ldk(i, xk[i], xs[i]);
+        ldkstep(1, yk, ys);
+      } else {
+#pragma unroll
+        for (int i = EARLY; i < PPS; i++) ldp(i, xk[i], xv[i], xs[i]);
+        ldstep(1, yk, yv, ys);
+      }
     }
   }
   uint32_t tlo[4] = {0, 0, 0, 0}, thi[4] = {0, 0, 0, 0};
@@ -850,7 +879,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // each finished as in step_core (lanes with hr < 8 the first page of a pair, the others
   // the second); the running max is updated once per step. ss: the pages' scale blocks in
   // LDS, pa0: the global number of page 0 (pages pa0 + NW i).
-  auto stepN = [&](const uint32_t (&kk)[PPS][RG], const uint32_t (&vv)[PPS][RG], const uint8_t* ss, int pa0) {
+  auto stepN = [&](const uint32_t (&kk)[PPS][RG], const uint32_t (&vv)[PPS][RG], const uint8_t* ss,
+                   const int (&pg)[PPS]) {
     if constexpr (REG) {
       float s4[PPS][4];
 #pragma unroll
@@ -867,10 +897,13 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
         }
         load_scales(ss + (hiLane ? 2 * j : 2 * j + 1) * C::SCB, vst[j], 1, 0);
       }
-      if (pa0 + (PPS - 1) * NW >= p1 || (ptail >= pa0 && ptail <= pa0 + (PPS - 1) * NW)) {  // wave-uniform
+      bool edge = false;  // wave-uniform: a partial or missing page in the step
+#pragma unroll
+      for (int i = 0; i < PPS; i++) edge |= pg[i] >= p1 || pg[i] == ptail;
+      if (edge) {
 #pragma unroll
         for (int j = 0; j < NPR; j++) {
-          const int pm = pa0 + NW * (hiLane ? 2 * j : 2 * j + 1);
+          const int pm = hiLane ? pg[2 * j] : pg[2 * j + 1];
           const int lim = (pm >= p1) ? 0 : (pm == ptail ? ltail : 16);
 #pragma unroll
           for (int e = 0; e < 4; e++)
@@ -932,9 +965,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // entry 8n + h (wave page n, head h) in lane (8n + h) % 64 of register n / 8, which after
   // the reductions below is lane 16 ((n / 2) % 4) + hr of the step that scores page n.
   constexpr int NPM = TQ_SPARSE_PAGES_PER_WAVE / 8;  // registers of page maxima
-  float pmreg[NPM];
-#pragma unroll
-  for (int k = 0; k < NPM; k++) pmreg[k] = -INFINITY;
+  static_assert(NPM == 4, "four registers of page maxima");
+  // (a vector value, written by selects: as an array its updates became an indexed store
+  // that the compiler placed in scratch memory)
+  f32x4 pmreg = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   int nskip = 0;  // pages of this wave whose values were skipped
   auto kstep = [&](int na_, const uint8_t* slotA, const uint8_t* slotB, int pa, int pb) {
     float sc[4], sA[4], sB[4];
@@ -960,7 +994,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     const int kreg = na_ >> 3, kq = (na_ >> 1) & 3;
 #pragma unroll
     for (int k = 0; k < NPM; k++)
-      if (k == kreg && jq == kq) pmreg[k] = pmx;
+      pmreg[k] = (k == kreg && jq == kq) ? pmx : pmreg[k];
     const float cm = vmax(pmx, dpp_ror8(pmx));  // both pages
     if (__any(cm > m_run)) {
       const float mn = fmaxf(m_run, cm);
@@ -1041,6 +1075,61 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     else if (lag >= 2) __builtin_amdgcn_s_setprio(2);
     else __builtin_amdgcn_s_setprio(0);
   };
+  // Register path: a page set's scale blocks (PPS per set, X first, then Y) go to the
+  // wave's first ring slot, where the score and value steps read them.
+  uint8_t* const ssw = &ring[0][wv][0];
+  auto put_scales = [&](uint8_t* ss, const uint32_t (&sw)[PPS][SW]) {
+#pragma unroll
+    for (int i = 0; i < PPS; i++)
+#pragma unroll
+      for (int c = 0; c < SW; c++)
+        if (64 * c + lane < C::SCB / 4) reinterpret_cast<uint32_t*>(ss + i * C::SCB)[64 * c + lane] = sw[i][c];
+  };
+  // Sparse values, register path, first pass: the scores of a step's two pages (keys in
+  // registers, K scales in the set's scale blocks), each page's largest score per head
+  // into pmreg as kstep does, and the running max and sum.
+  auto kstepN = [&](const uint32_t (&kk)[PPS][RG], const uint8_t* ss, int na_, const int (&pg)[PPS]) {
+    if constexpr (REG && SPV) {
+      static_assert(PPS % 2 == 0, "the page maxima are kept per page pair");
+#pragma unroll
+      for (int j = 0; j < NPR; j++) {  // pair j: wave pages na_ + 2j (A) and na_ + 2j + 1 (B)
+        float sA[4], sB[4], sc[4];
+        scores_w(kk[2 * j], ss + 2 * j * C::SCB, 0, sA);
+        scores_w(kk[2 * j + 1], ss + (2 * j + 1) * C::SCB, 0, sB);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float own = hiLane ? sA[e] : sB[e];
+          const float sup = hiLane ? sB[e] : sA[e];
+          sc[e] = own + dpp_ror8(sup);
+        }
+        const int ga = pg[2 * j], gb = pg[2 * j + 1];
+        if (ga >= p1 || ga == ptail || gb >= p1 || gb == ptail) {  // wave-uniform
+          const int pm = hiLane ? ga : gb;
+          const int lim = (pm >= p1) ? 0 : (pm == ptail ? ltail : 16);
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (4 * jq + e >= lim) sc[e] = -INFINITY;
+        }
+        float pmx = vmax3(sc[0], sc[1], vmax(sc[2], sc[3]));
+        pmx = max_xor16(pmx);
+        pmx = max_xor32(pmx);  // this lane's page (A if hiLane), head hl: its largest score
+        const int na2 = na_ + 2 * j;
+        const int kreg = na2 >> 3, kq = (na2 >> 1) & 3;
+#pragma unroll
+        for (int k = 0; k < NPM; k++)
+          pmreg[k] = (k == kreg && jq == kq) ? pmx : pmreg[k];
+        const float cm = vmax(pmx, dpp_ror8(pmx));  // both pages
+        if (__any(cm > m_run)) {
+          const float mn = fmaxf(m_run, cm);
+          l_run *= __builtin_amdgcn_exp2f((m_run - mn) * down);  // 2^-inf = 0
+          m_run = mn;
+          nmd = -mn * down;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) l_run += __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], down, nmd));
+      }
+    }
+  };
   if constexpr (SPV) {
     // Sparse values [mlxcel manual, sparse-V threshold]. Pass 1 streams the keys of every
     // page of this wave (exact running max and sum, page maxima). The workgroup's maximum
@@ -1050,18 +1139,40 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     // keys and values of the kept pages through the dense step with the maximum fixed at M,
     // and the sum over every token comes from pass 1. (At most 32 pages per wave: the split
     // count is chosen for it.)
-#pragma unroll 1
-    for (int na = 0; na < npw; na += 2) {
-      const int nmax = min(npw, na + NR);
+    if constexpr (REG) {
+      // keys only, through registers: the X and Y sets alternate as in the dense loop
+      auto krun = [&](int st, uint32_t (&k)[PPS][RG], uint32_t (&sw)[PPS][SW], uint8_t* ss) {
+        put_scales(ss, sw);
+        int pg[PPS];
 #pragma unroll
-      for (int k = 0; k < 4; k++)
-        if (nis < nmax) {
-          stage_keys(nis);
-          nis++;
-        }
-      wait_pages_in_flight<SplitDma<D, KCODEC, VB>::NK_OPS, NR - 2>(max(0, min(NR - 2, nis - na - 2)));
-      const int pa = p0 + wv + NW * na;
-      kstep(na, k_slot(na), k_slot(na + 1), pa, pa + NW);
+        for (int i = 0; i < PPS; i++) pg[i] = p0 + wv + NW * (PPS * st + i);
+        kstepN(k, ss, PPS * st, pg);
+      };
+      const int nst = (npw + PPS - 1) / PPS;
+      int st = 0;
+#pragma unroll 1
+      for (; st + 2 < nst; st += 2) {
+        krun(st, xk, xs, ssw);
+        ldkstep(st + 2, xk, xs);
+        krun(st + 1, yk, ys, ssw + PPS * C::SCB);
+        ldkstep(st + 3, yk, ys);
+      }
+      if (st < nst) krun(st, xk, xs, ssw);
+      if (st + 1 < nst) krun(st + 1, yk, ys, ssw + PPS * C::SCB);
+    } else {
+#pragma unroll 1
+      for (int na = 0; na < npw; na += 2) {
+        const int nmax = min(npw, na + NR);
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+          if (nis < nmax) {
+            stage_keys(nis);
+            nis++;
+          }
+        wait_pages_in_flight<SplitDma<D, KCODEC, VB>::NK_OPS, NR - 2>(max(0, min(NR - 2, nis - na - 2)));
+        const int pa = p0 + wv + NW * na;
+        kstep(na, k_slot(na), k_slot(na + 1), pa, pa + NW);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (jq == 0 && hr < 8) mml[wv][hr][0] = m_run;
@@ -1111,36 +1222,44 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       }
     }
     auto kn = [&](int i) { return __builtin_amdgcn_readlane(klist, i); };
-    int nis2 = 0;
+    if constexpr (REG) {
+      // the kept pages, PPS at a time, keys and values into the X set (few: one wait each)
 #pragma unroll 1
-    for (int i = 0; i < nk; i += 2) {
-      const int nmax = min(nk, i + NSLOT);
+      for (int i = 0; i < nk; i += PPS) {
+        int pg[PPS];
 #pragma unroll
-      for (int k = 0; k < 4; k++)
-        if (nis2 < nmax) {
-          stage_page<D, KCODEC, VB>(page_blk(kn(nis2)), slot_lds(nis2 % NSLOT), lane);
-          nis2++;
+        for (int j = 0; j < PPS; j++) {
+          const bool kept = i + j < nk;
+          const int n = kept ? kn(i + j) : npw;  // past the end: a dummy load, masked below
+          ldp(n, xk[j], xv[j], xs[j]);
+          pg[j] = kept ? p0 + wv + NW * n : p1;
         }
-      wait_pages_in_flight<C::NDMA, NSLOT - 2>(max(0, min(NSLOT - 2, nis2 - i - 2)));
-      const int pa = p0 + wv + NW * kn(i);
-      const int pb = (i + 1 < nk) ? p0 + wv + NW * kn(i + 1) : p1;  // p1: no page B
-      step(ring[i % NSLOT][wv], ring[(i + 1) % NSLOT][wv], pa, pb);
+        put_scales(ssw, xs);
+        stepN(xk, xv, ssw, pg);
+      }
+    } else {
+      int nis2 = 0;
+#pragma unroll 1
+      for (int i = 0; i < nk; i += 2) {
+        const int nmax = min(nk, i + NSLOT);
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+          if (nis2 < nmax) {
+            stage_page<D, KCODEC, VB>(page_blk(kn(nis2)), slot_lds(nis2 % NSLOT), lane);
+            nis2++;
+          }
+        wait_pages_in_flight<C::NDMA, NSLOT - 2>(max(0, min(NSLOT - 2, nis2 - i - 2)));
+        const int pa = p0 + wv + NW * kn(i);
+        const int pb = (i + 1 < nk) ? p0 + wv + NW * kn(i + 1) : p1;  // p1: no page B
+        step(ring[i % NSLOT][wv], ring[(i + 1) % NSLOT][wv], pa, pb);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     l_run = l_all;
     if (lane == 0 && nskip > 0) atomicAdd(&wskip, nskip);  // (one global add per workgroup below)
   } else if constexpr (REG) {
     // Register path: step st over the X set, step st + 1 over the Y set; each set is
-    // reloaded (two steps ahead) as soon as its step is done. Scale blocks: 2 PPS per wave
-    // (X first, then Y) in the wave's first ring slot.
-    uint8_t* const ssw = &ring[0][wv][0];
-    auto put_scales = [&](uint8_t* ss, const uint32_t (&sw)[PPS][SW]) {
-#pragma unroll
-      for (int i = 0; i < PPS; i++)
-#pragma unroll
-        for (int c = 0; c < SW; c++)
-          if (64 * c + lane < C::SCB / 4) reinterpret_cast<uint32_t*>(ss + i * C::SCB)[64 * c + lane] = sw[i][c];
-    };
+    // reloaded (two steps ahead) as soon as its step is done.
     // The appended token (block layout in tokblk) into the registers of the page that holds
     // it: lane l holds the K index dwords of token l % 16, in byte e of each V index dword
     // the token 4 (l / 16) + e, and scale dword l (and 64 + l) of the block, whose two
@@ -1179,7 +1298,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
         }
       }
       put_scales(ss, sw);
-      stepN(k, v, ss, pa0);
+      int pg[PPS];
+#pragma unroll
+      for (int i = 0; i < PPS; i++) pg[i] = pa0 + NW * i;
+      stepN(k, v, ss, pg);
     };
     const int nst = (npw + PPS - 1) / PPS;  // steps of this wave
     // The loop runs the steps that are not the last; the last one or two run after it.

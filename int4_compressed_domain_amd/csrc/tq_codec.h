@@ -173,23 +173,23 @@ constexpr bool valid() {
 static_assert(valid(), "the key codebook thresholds do not fit the 1/32 buckets");
 }  // namespace tq_lutb
 
-// Fill the bucket table (NB entries of {lo + 1, bits of th}) into LDS, one entry per thread
-// i < NB; the caller synchronizes before codec_vector reads it.
-__device__ __forceinline__ void tq_lut_table_fill(u32x2* tbl, int i) {
+// Entry i of the bucket table ({lo + 1, bits of th}; zeros for i >= NB), for the caller to
+// write into LDS (NB entries) and synchronize before codec_vector reads it.
+__device__ __forceinline__ u32x2 tq_lut_table_entry(int i) {
   constexpr tq_lutb::Table T = tq_lutb::make_table();
+  u32x2 w = {0u, 0u};
   if (i < tq_lutb::NB) {
-    u32x2 w;
     w[0] = T.lo1[i];
     w[1] = __float_as_uint(T.th[i]);
-    tbl[i] = w;
   }
+  return w;
 }
 
 // y: this lane's E coordinates of the vector, widened to fp32 and already multiplied by
 // sigma; blk = tq_blk16(lane16) of the 16 lanes that hold the vector. Returns the lane's
 // E indices and its group's scale (abs-max scale, or the group norm for the LUT codec). The
 // abs-max codecs differ in their largest level QM: 7 (4 bits), 3 (3 bits), 1 (2 bits).
-// lut_tbl: the LUT codec's bucket table in LDS (tq_lut_table_fill), or null for the
+// lut_tbl: the LUT codec's bucket table in LDS (tq_lut_table_entry), or null for the
 // division-per-coordinate path alone.
 template <int D, int CODEC>
 __device__ __forceinline__ void codec_vector(float (&y)[D / 16], int blk, uint32_t (&u)[D / 16],

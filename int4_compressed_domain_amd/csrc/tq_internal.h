@@ -75,15 +75,16 @@ constexpr int tq_value_bits(int v_codec) { return TQ_VALUE_BITS(v_codec); }
 // take 8 (a staged fp16-key page is 41*D bytes, three per wave fit the LDS ring), fp16 keys
 // at D = 256 (10.5 KB a page) 4, one workgroup per CU (the ring takes 123 KB), which limits
 // that variant to 4 query heads per kv head (one wave per head in the rotations). Pages
-// streamed through registers (4-bit keys and values, D <= 128): two sets of four pages per
-// wave, one computed while the other is in flight, need more than 128 registers, so 8
-// waves of up to 256.
+// streamed through registers (4-bit keys and values, D <= 128): two sets of
+// TQ_REG_PAGES_PER_STEP pages per wave, one computed while the other is in flight, need
+// more than 128 registers, so 8 waves of up to 256.
 #ifndef TQ_REG_LUT
 #define TQ_REG_LUT 0
 #endif
-// Variants whose pages stream through registers (the others stage pages in LDS).
+// Variants whose pages stream through registers (the others stage pages in LDS); sparse
+// values included (the first pass streams the keys alone).
 constexpr bool tq_decode_reg_path(int D, int k_codec, int value_bits, bool sparse) {
-  return D <= 128 && !sparse && value_bits == 4 &&
+  return D <= 128 && value_bits == 4 &&
          (k_codec == TQ_CODEC_ABSMAX || (TQ_REG_LUT && k_codec == TQ_CODEC_LLOYDMAX));
 }
 constexpr int tq_decode_waves(int D, int k_codec, int v_codec, bool sparse) {

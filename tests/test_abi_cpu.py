@@ -165,8 +165,9 @@ def test_workspace_size_formula():
     L = _layout()
     for batch, ctx, splits in ((1, 131072, 5), (16, 8192, 1), (3, 100, 100)):
         pages = -(-ctx // 16)
-        # the sparse-value decode keeps at most 32 pages per wave (16 waves here)
-        splits = max(splits, -(-pages // (32 * 16)))
+        # the sparse-value decode keeps at most 32 pages per wave (8 waves here: 4-bit keys
+        # and values stream through registers)
+        splits = max(splits, -(-pages // (32 * 8)))
         pps = -(-pages // min(splits, pages))
         S = -(-pages // pps)
         want = (4 << 20) + batch * 32 * S * (128 + 2) * 4 + batch * 8 * 4  # counters + partials + order
