@@ -310,8 +310,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   using C = Cfg<D, KCODEC, VB>;
   constexpr int G = C::G, BB = C::BB, NT = 64 * NW, V = D / 64;
   constexpr bool KF16 = C::KF16;
-  // ring slots per wave: as many as ~144 KB of LDS holds, at most 8 (NSLOT - 1 pages in flight)
-  constexpr int NSLOT = (147456 / (NW * C::SLOT)) < 8 ? (147456 / (NW * C::SLOT)) : 8;
+  // ring slots per wave: as many as ~144 KB of LDS holds, at most 8 (NSLOT - 1 pages in
+  // flight), or 16 where pages stream through registers (there the ring holds only scale
+  // blocks and the merge's scratch, which with small pages needs more than 8 slots)
+  constexpr int NSMAX = tq_decode_reg_path(D, KCODEC, VB, SPV) ? 16 : 8;
+  constexpr int NSLOT = (147456 / (NW * C::SLOT)) < NSMAX ? (147456 / (NW * C::SLOT)) : NSMAX;
   static_assert(NSLOT >= 3, "ring too small");
   constexpr bool KSUB = (KCODEC == TQ_CODEC_ABSMAX);
   // Register streaming: a page's K and V index dwords are loaded straight into the VGPRs
@@ -326,7 +329,12 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // alone, half a page's bytes, so it takes 4 to keep as many bytes in flight)
   constexpr int PPS = SPV ? 4 : TQ_REG_PAGES_PER_STEP;
   constexpr int NPR = PPS / 2;                // page pairs per step
-  static_assert(!REG || 2 * PPS * C::SCB <= C::SLOT, "the scale blocks of both page sets in one ring slot");
+  static_assert(!REG || PPS * C::SCB <= C::SLOT, "a page set's scale blocks in one ring slot");
+  static_assert(!REG || G <= 4, "register path: D <= 128");
+  // register path, V index dwords of a page as loaded: 4-bit values G; packed values the G/2
+  // X dwords of the lane's row, then (3-bit) its Z dword (shared by a lane pair at D = 64)
+  constexpr int XD = G >= 2 ? G / 2 : 1;
+  constexpr int VRG = !REG ? 1 : (VB == 4 ? G : XD + (VB == 3 ? 1 : 0));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar page loads
   const int jq = lane >> 4, hr = lane & 15, hl = hr & 7;
@@ -515,14 +523,22 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // computed while the other is in flight. A page n >= npw is a dummy load of one 16-byte
   // line (every lane the same address in the wave's last page), so that every step issues
   // the same loads and the compiler's vmcnt waits stay exact.
-  uint32_t xk[PPS][RG], xv[PPS][RG], xs[PPS][SW], yk[PPS][RG], yv[PPS][RG], ys[PPS][SW];
-  auto ldp = [&](int n, uint32_t (&k)[RG], uint32_t (&v)[RG], uint32_t (&sw)[SW]) {
+  uint32_t xk[PPS][RG], xv[PPS][VRG], xs[PPS][SW], yk[PPS][RG], yv[PPS][VRG], ys[PPS][SW];
+  auto ldp = [&](int n, uint32_t (&k)[RG], uint32_t (&v)[VRG], uint32_t (&sw)[SW]) {
     if constexpr (REG) {
       const bool real = n < npw;
       const uint8_t* blk = page_blk(real ? n : npw - 1);
       const uint32_t lo = real ? (uint32_t)lane * C::KB : 0u;
       ld_nt<C::KB>(blk + lo, k);
-      ld_nt<C::KB>(blk + C::BV + lo, v);
+      if constexpr (VB == 4) {
+        ld_nt<C::KB>(blk + C::BV + lo, v);
+      } else {
+        ld_nt<4 * XD>(blk + C::BV + (real ? (uint32_t)lane * 4 * XD : 0u), v);
+        if constexpr (VB == 3) {
+          const uint32_t zo = real ? (uint32_t)(G == 2 ? lane >> 1 : lane) * 4 : 0u;
+          ld_nt<4>(blk + C::BV + 128 * G + zo, &v[XD]);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < SW; i++) {
         const int dw = real ? min(64 * i + lane, C::SCB / 4 - 1) : 0;
@@ -530,7 +546,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       }
     }
   };
-  auto ldstep = [&](int st, uint32_t (&k)[PPS][RG], uint32_t (&v)[PPS][RG], uint32_t (&sw)[PPS][SW]) {
+  auto ldstep = [&](int st, uint32_t (&k)[PPS][RG], uint32_t (&v)[PPS][VRG], uint32_t (&sw)[PPS][SW]) {
 #pragma unroll
     for (int i = 0; i < PPS; i++) ldp(PPS * st + i, k[i], v[i], sw[i]);
   };
@@ -879,7 +895,23 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // each finished as in step_core (lanes with hr < 8 the first page of a pair, the others
   // the second); the running max is updated once per step. ss: the pages' scale blocks in
   // LDS, pa0: the global number of page 0 (pages pa0 + NW i).
-  auto stepN = [&](const uint32_t (&kk)[PPS][RG], const uint32_t (&vv)[PPS][RG], const uint8_t* ss,
+  // a register page's V index dwords in the 4-bit layout (packed values unpacked as
+  // load_idx does for a staged page: X dword g/2 shifted by 2(g%2), Z bits into bit 2)
+  auto vregs = [&](const uint32_t (&raw)[VRG], uint32_t (&w)[G]) {
+    if constexpr (VB == 4 || !REG) {
+#pragma unroll
+      for (int g = 0; g < G; g++) w[g] = raw[VB == 4 ? g : 0];
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; g++) w[g] = (raw[g >> 1] >> (2 * (g & 1))) & 0x33333333u;
+      if constexpr (VB == 3) {
+        const uint32_t z = raw[XD] >> (G == 2 ? 2 * (lane & 1) : 0);
+#pragma unroll
+        for (int g = 0; g < G; g++) w[g] |= ((z >> g) & 0x11111111u) << 2;
+      }
+    }
+  };
+  auto stepN = [&](const uint32_t (&kk)[PPS][RG], const uint32_t (&vv)[PPS][VRG], const uint8_t* ss,
                    const int (&pg)[PPS]) {
     if constexpr (REG) {
       float s4[PPS][4];
@@ -939,6 +971,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 #pragma unroll
       for (int j = 0; j < NPR; j++) {
         auto vsc = [&](int e, int g) { return (float)as_h2(vst[j][(e * G + g) >> 1])[(e * G + g) & 1]; };
+        uint32_t wA[G], wB[G];
+        vregs(vv[2 * j], wA);
+        vregs(vv[2 * j + 1], wB);
 #pragma unroll
         for (int g = 0; g < G; g++) {
           // P' as in step_core: this lane's page in k-slots 0..3 (own) or 4..7 (partner)
@@ -948,7 +983,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
           const uint32_t x0 = __builtin_amdgcn_mov_dpp(o2[0], 0x128, 0xf, 0xf, true);
           const uint32_t x1 = __builtin_amdgcn_mov_dpp(o2[1], 0x128, 0xf, 0xf, true);
           const f16x8 P = __builtin_bit_cast(f16x8, u32x4{o2[0], o2[1], x0, x1});
-          const uint32_t a = vv[2 * j][g], a8 = a >> 8, bw = vv[2 * j + 1][g], b8 = bw >> 8;
+          const uint32_t a = wA[g], a8 = a >> 8, bw = wB[g], b8 = bw >> 8;
           const f16x8 Ae = __builtin_bit_cast(f16x8, u32x4{a & 0x000F000Fu, a8 & 0x000F000Fu, bw & 0x000F000Fu, b8 & 0x000F000Fu});
           const f16x8 Ao = __builtin_bit_cast(f16x8, u32x4{a & 0x00F000F0u, a8 & 0x00F000F0u, bw & 0x00F000F0u, b8 & 0x00F000F0u});
           acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, P, acc[2 * g], 0, 0, 0);
@@ -1075,9 +1110,12 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     else if (lag >= 2) __builtin_amdgcn_s_setprio(2);
     else __builtin_amdgcn_s_setprio(0);
   };
-  // Register path: a page set's scale blocks (PPS per set, X first, then Y) go to the
-  // wave's first ring slot, where the score and value steps read them.
+  // Register path: a page set's scale blocks (PPS per set) go to the wave's first ring slot,
+  // where the score and value steps read them: the X set's first, the Y set's after them,
+  // or, where both sets' do not fit one slot (sparse, 2-bit values), in the wave's second
+  // slot (until a wave writes its results, its slots are its own)
   uint8_t* const ssw = &ring[0][wv][0];
+  uint8_t* const ssy = 2 * PPS * C::SCB <= C::SLOT ? ssw + PPS * C::SCB : &ring[1][wv][0];
   auto put_scales = [&](uint8_t* ss, const uint32_t (&sw)[PPS][SW]) {
 #pragma unroll
     for (int i = 0; i < PPS; i++)
@@ -1154,11 +1192,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       for (; st + 2 < nst; st += 2) {
         krun(st, xk, xs, ssw);
         ldkstep(st + 2, xk, xs);
-        krun(st + 1, yk, ys, ssw + PPS * C::SCB);
+        krun(st + 1, yk, ys, ssy);
         ldkstep(st + 3, yk, ys);
       }
       if (st < nst) krun(st, xk, xs, ssw);
-      if (st + 1 < nst) krun(st + 1, yk, ys, ssw + PPS * C::SCB);
+      if (st + 1 < nst) krun(st + 1, yk, ys, ssy);
     } else {
 #pragma unroll 1
       for (int na = 0; na < npw; na += 2) {
@@ -1264,16 +1302,26 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     // it: lane l holds the K index dwords of token l % 16, in byte e of each V index dword
     // the token 4 (l / 16) + e, and scale dword l (and 64 + l) of the block, whose two
     // halves belong to one token.
-    auto patch_regs = [&](uint32_t (&k)[RG], uint32_t (&v)[RG], uint32_t (&sw)[SW]) {
+    auto patch_regs = [&](uint32_t (&k)[RG], uint32_t (&v)[VRG], uint32_t (&sw)[SW]) {
       if ((lane & 15) == tnew) {
 #pragma unroll
         for (int g = 0; g < RG; g++) k[g] = *reinterpret_cast<const uint32_t*>(tokblk + lane * 4 * G + 4 * g);
       }
       if ((lane >> 4) == (tnew >> 2)) {
         const uint32_t m = 0xFFu << (8 * (tnew & 3));
+        if constexpr (VB == 4) {
 #pragma unroll
-        for (int g = 0; g < RG; g++)
-          v[g] = (v[g] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + lane * 4 * G + 4 * g) & m);
+          for (int g = 0; g < RG; g++)
+            v[g] = (v[g] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + lane * 4 * G + 4 * g) & m);
+        } else {  // packed: byte tnew % 4 of the lane's X dwords (and of its Z dword)
+#pragma unroll
+          for (int i = 0; i < XD; i++)
+            v[i] = (v[i] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + 4 * (lane * XD + i)) & m);
+          if constexpr (VB == 3) {
+            const int zd = G == 2 ? lane >> 1 : lane;
+            v[XD] = (v[XD] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + 128 * G + 4 * zd) & m);
+          }
+        }
       }
 #pragma unroll
       for (int c = 0; c < SW; c++) {
@@ -1285,7 +1333,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     };
     // One step over a set. The last step of a wave is the only one that can hold the
     // sequence's last page (pages ascend), so only it carries the fused append's patch.
-    auto run_step = [&](auto last, int st, uint32_t (&k)[PPS][RG], uint32_t (&v)[PPS][RG],
+    auto run_step = [&](auto last, int st, uint32_t (&k)[PPS][RG], uint32_t (&v)[PPS][VRG],
                         uint32_t (&sw)[PPS][SW], uint8_t* ss) {
       if (balance) balance_step(PPS * st);
       const int pa0 = p0 + wv + NW * PPS * st;
@@ -1310,12 +1358,12 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     for (; st + 2 < nst; st += 2) {
       run_step(std::false_type{}, st, xk, xv, xs, ssw);
       ldstep(st + 2, xk, xv, xs);
-      run_step(std::false_type{}, st + 1, yk, yv, ys, ssw + PPS * C::SCB);
+      run_step(std::false_type{}, st + 1, yk, yv, ys, ssy);
       ldstep(st + 3, yk, yv, ys);
     }
     if (st + 1 < nst) {
       run_step(std::false_type{}, st, xk, xv, xs, ssw);
-      run_step(std::true_type{}, st + 1, yk, yv, ys, ssw + PPS * C::SCB);
+      run_step(std::true_type{}, st + 1, yk, yv, ys, ssy);
     } else if (st < nst) {
       run_step(std::true_type{}, st, xk, xv, xs, ssw);
     }

@@ -85,7 +85,10 @@ Split choose_split(int B, int Hkv, int D, int k_codec, int v_codec, int max_ctx,
     return make_split(pages, S > min_s ? S : min_s);
   }
   const int64_t units = (int64_t)B * Hkv;
-  const int64_t target = (int64_t)num_cus() * tq_decode_wgs_per_cu(D, k_codec);
+  // one workgroup per CU: the page ring takes ~147 KB of a CU's 160 KB of LDS, at every head
+  // size (at D = 256, batch 4, 8 kv heads, 32K tokens: 63.4 us against 70.6 us with splits
+  // sized for two workgroups per CU)
+  const int64_t target = (int64_t)num_cus();
   int64_t want = (target + units - 1) / units;
   // at least 4 pages per wave: below that the split merge costs more than the split saves
   // (1024 tokens, one head: 13.2 us with one split, 14.8 us with four)
@@ -305,7 +308,7 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   if (max_context_len > 0 && (!pool || !block_table)) return TQ_EINVAL;
   Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, L->v_codec, max_context_len,
                          num_splits, sparse_v != 0);
-  const int64_t resident = (int64_t)num_cus() * tq_decode_wgs_per_cu(L->head_dim, L->k_codec);
+  const int64_t resident = (int64_t)num_cus();  // fused-decode workgroups the chip holds at once
   // fp16 tail: with automatic splits, at least 8 of them per unit, a grid that fits the chip
   // and a tail of at most 256 tokens, one split is given up for a workgroup per unit that
   // takes the whole tail and runs beside the pool's (its cost then hides behind theirs; a

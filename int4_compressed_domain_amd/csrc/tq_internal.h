@@ -75,16 +75,20 @@ constexpr int tq_value_bits(int v_codec) { return TQ_VALUE_BITS(v_codec); }
 // take 8 (a staged fp16-key page is 41*D bytes, three per wave fit the LDS ring), fp16 keys
 // at D = 256 (10.5 KB a page) 4, one workgroup per CU (the ring takes 123 KB), which limits
 // that variant to 4 query heads per kv head (one wave per head in the rotations). Pages
-// streamed through registers (4-bit keys and values, D <= 128): two sets of
+// streamed through registers (abs-max keys, D <= 128): two sets of
 // TQ_REG_PAGES_PER_STEP pages per wave, one computed while the other is in flight, need
 // more than 128 registers, so 8 waves of up to 256.
 #ifndef TQ_REG_LUT
 #define TQ_REG_LUT 0
 #endif
-// Variants whose pages stream through registers (the others stage pages in LDS); sparse
-// values included (the first pass streams the keys alone).
+#ifndef TQ_REG_PACKED
+#define TQ_REG_PACKED 1
+#endif
+// Variants whose pages stream through registers (the others stage pages in LDS): abs-max
+// keys at D <= 128 with 4-bit values, or packed 3- and 2-bit ones; sparse values included
+// (the first pass streams the keys alone).
 constexpr bool tq_decode_reg_path(int D, int k_codec, int value_bits, bool sparse) {
-  return D <= 128 && value_bits == 4 &&
+  return D <= 128 && (value_bits == 4 || TQ_REG_PACKED) &&
          (k_codec == TQ_CODEC_ABSMAX || (TQ_REG_LUT && k_codec == TQ_CODEC_LLOYDMAX));
 }
 constexpr int tq_decode_waves(int D, int k_codec, int v_codec, bool sparse) {
@@ -103,11 +107,6 @@ constexpr int TQ_MAX_SPLIT_PAGES = 2048;  // pages per split (their ids are held
 // Pages per split of a variant with nw waves: every wave keeps the ids of its pages in at
 // most four registers (256 ids).
 constexpr int tq_max_split_pages(int nw) { return 256 * nw < TQ_MAX_SPLIT_PAGES ? 256 * nw : TQ_MAX_SPLIT_PAGES; }
-// Fused-decode workgroups resident per CU (LDS-bound): two at D = 256 with compact keys,
-// one otherwise.
-constexpr int tq_decode_wgs_per_cu(int D, int k_codec) {
-  return (D >= 256 && k_codec != TQ_CODEC_FP16) ? 2 : 1;
-}
 constexpr int TQ_LPT_MAX_BATCH = 256;    // longest-first workgroup order up to this batch
 constexpr int TQ_SPARSE_PAGES_PER_WAVE = 32;  // sparse values: page maxima kept per wave
 // Sparse values: per-(unit, head) published maxima, 8 words per unit from word 2^19 of the

@@ -111,7 +111,7 @@ V3, V2 = W.CODEC_ABSMAX3, W.CODEC_ABSMAX2
 @pytest.mark.parametrize("D,r,k_codec,v_codec", [(64, 4, 0, V3), (128, 8, 0, V3), (128, 8, 2, V3),
                                                  (256, 2, 0, V3), (128, 4, 1, V2), (128, 8, 0, V2),
                                                  (64, 2, 2, V2), (256, 4, 1, V2), (256, 2, 2, V3),
-                                                 (256, 4, 2, V2)])
+                                                 (256, 4, 2, V2), (64, 2, 0, V2)])
 def test_low_bit_values(D, r, k_codec, v_codec):
     """3-bit and 2-bit values with each key codec: packed pool bytes equal the oracle's
     (appends of many tokens into shared pages), attention within the tolerance for edge
@@ -144,7 +144,7 @@ def _sparse_gpu(c, thr, num_splits=0):
 @pytest.mark.parametrize("name,k_codec,v_codec", [("llama70b_b1_128k", 0, 0), ("gemma_d256_32k", 0, 0),
                                                   ("mixed_serving", 1, 0), ("llama70b_b1_128k", 2, 0),
                                                   ("llama70b_b1_128k", 2, V3), ("llama70b_b1_128k", 0, V2),
-                                                  ("gemma_d256_32k", 2, V3)])
+                                                  ("gemma_d256_32k", 2, V3), ("llama70b_b1_128k", 0, V3)])
 def test_sparse_values(name, k_codec, v_codec):
     """Sparse values: threshold 0 reproduces the dense decode bit for bit; at 1e-6 the
     result stays within the tolerance plus the oracle's bound on the dropped terms
@@ -458,7 +458,8 @@ def test_full_size_workloads(name):
                                                        (128, 8, 2, "bf16", 0), (64, 4, 2, "f32", 0),
                                                        (128, 8, 2, "bf16", V3), (128, 8, 0, "bf16", V2),
                                                        (64, 4, 2, "f32", V3), (256, 2, 0, "bf16", V3),
-                                                       (64, 2, 1, "bf16", V2)])
+                                                       (64, 2, 1, "bf16", V2), (128, 8, 0, "bf16", V3),
+                                                       (64, 2, 0, "f32", V3), (64, 4, 0, "bf16", V2)])
 def test_append_decode_equals_append_then_decode(D, r, k_codec, dtype, v_codec):
     """The fused entry point writes the same pool bytes as tq_kv_append of each sequence's
     last token and returns the same output, bit for bit, as tq_decode_attn afterwards."""
@@ -669,14 +670,16 @@ def test_validation_of_device_tables(monkeypatch):
     assert torch.equal(before, c.pool)
 
 
-@pytest.mark.parametrize("D,k_codec", [(64, 0), (128, 1)])
-def test_sparse_values_full_waves(D, k_codec):
+@pytest.mark.parametrize("D,k_codec,v_codec", [(64, 0, 0), (128, 1, 0), (128, 0, V2), (64, 0, V3), (64, 0, V2)])
+def test_sparse_values_full_waves(D, k_codec, v_codec):
     """Sparse values with one split over 8192 tokens (512 pages): each wave holds the most
-    pages the first pass keeps maxima for (32); D = 64 packs two key parts per ring slot
-    like D = 128. Within the tolerance plus the oracle's bound, value pages skipped."""
+    pages the first pass keeps maxima for (32). LUT keys stage two key parts per LDS ring
+    slot; abs-max keys stream through registers, where 2-bit values (D = 64 and 128) keep the
+    second page set's scale blocks in a second ring slot. Within the tolerance plus the
+    oracle's bound, value pages skipped."""
     w = W.Workload("sv_full_d%d" % D, 2, 8, 2, D, 8192, "bf16", 1.0 / math.sqrt(D), k_codec=k_codec,
-                   dist="lognormal_spikes")
-    _say("case sparse values, full waves, D", D, "k_codec", k_codec)
+                   v_codec=v_codec, dist="lognormal_spikes")
+    _say("case sparse values, full waves, D", D, "k_codec", k_codec, "v_codec", v_codec)
     c = Case(w, seed=29, lens=[8192, 5000])
     c.fill()
     exact = c.decode_oracle()
