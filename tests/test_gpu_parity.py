@@ -316,10 +316,15 @@ def test_split_count_invariance():
     c.fill()
     outs = [c.decode_gpu(num_splits=s) for s in (1, 2, 7, 0, 1000)]
     # P' = p * s_V is rounded to fp16 relative to the running max at the time its page is
-    # processed, which depends on the split count: results agree to about one fp16 unit
-    # roundoff (2^-11), not bit for bit.
+    # processed, which depends on the split count, so results differ by those roundings:
+    # at worst one fp16 unit roundoff (2^-11) of every weight, all in one direction. They
+    # are independent across the 3000 tokens and largely cancel: on MI355X the largest
+    # normwise difference of the four split counts is 6.1e-5 (~2^-14), rms ~7e-6, so the
+    # bar is 2^-13, twice the largest seen.
     for o in outs[1:]:
-        assert attn_err(o, outs[0]).max() < 2.0 ** -11
+        e = attn_err(o, outs[0])
+        _say("   split agreement: max %.3e, rms %.3e" % (e.max(), np.sqrt(np.mean(e ** 2))))
+        assert e.max() < 2.0 ** -13
     ref = c.decode_oracle()
     for o in outs:
         assert attn_err(o, ref).max() <= ATTN_TOL
