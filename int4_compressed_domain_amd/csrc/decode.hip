@@ -326,8 +326,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   constexpr int SW = (C::SCB / 4 + 63) / 64;  // scale dwords per lane of a page (register path)
   constexpr int RG = REG ? G : 1;             // index dwords per lane of a page region
   // register path: pages per step (2 or 4; sparse values' first pass streams the keys
-  // alone, half a page's bytes, so it takes 4 to keep as many bytes in flight)
-  constexpr int PPS = SPV ? 4 : TQ_REG_PAGES_PER_STEP;
+  // alone, half a page's bytes, and packed values' pages are smaller, so those take 4 to
+  // keep as many bytes in flight)
+  constexpr int PPS = SPV ? 4 : (VB < 4 ? TQ_REG_PPS_PACKED : TQ_REG_PAGES_PER_STEP);
   constexpr int NPR = PPS / 2;                // page pairs per step
   static_assert(!REG || PPS * C::SCB <= C::SLOT, "a page set's scale blocks in one ring slot");
   static_assert(!REG || G <= 4, "register path: D <= 128");

@@ -66,6 +66,11 @@ constexpr int tq_value_bits(int v_codec) { return TQ_VALUE_BITS(v_codec); }
 #ifndef TQ_REG_PAGES_PER_STEP
 #define TQ_REG_PAGES_PER_STEP 2
 #endif
+// Packed 3- and 2-bit values: 4 pages per step (their pages are ~28% smaller, so two sets
+// of 2 keep fewer bytes in flight; 128K with 2-bit values: 32.9 us against 33.7 with 2).
+#ifndef TQ_REG_PPS_PACKED
+#define TQ_REG_PPS_PACKED 4
+#endif
 #ifndef TQ_REG_EARLY
 #define TQ_REG_EARLY 2
 #endif
