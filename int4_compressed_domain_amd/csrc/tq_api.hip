@@ -90,9 +90,10 @@ Split choose_split(int B, int Hkv, int D, int k_codec, int v_codec, int max_ctx,
   // sized for two workgroups per CU)
   const int64_t target = (int64_t)num_cus();
   int64_t want = (target + units - 1) / units;
-  // at least 4 pages per wave: below that the split merge costs more than the split saves
-  // (1024 tokens, one head: 13.2 us with one split, 14.8 us with four)
-  const int64_t cap = pages / (4 * nw) > 1 ? pages / (4 * nw) : 1;
+  // at least ~1.5 pages per wave: below that the split merge costs more than the split
+  // saves (1024 tokens, one kv head, 8 waves: 11.2 us with 2 splits, 10.3 with 4, 10.1 with
+  // 5 or 6, 10.4 with 8)
+  const int64_t cap = 2 * (int64_t)pages / (3 * nw) > 1 ? 2 * (int64_t)pages / (3 * nw) : 1;
   if (want > cap) want = cap;
   if (want < min_s) want = min_s;
   if (want > TQ_MAX_SPLITS) want = TQ_MAX_SPLITS;
