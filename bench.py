@@ -168,8 +168,8 @@ class Setup:
                             self.slots_pre)
 
     def decode(self, i):
-        """One launch: append every decoding sequence's newest token, then attend (sparse
-        values: the append, then the sparse decode)."""
+        """One launch: append every decoding sequence's newest token, then attend (with
+        sparse values too)."""
         from int4_compressed_domain_amd import tq
         pool = self.pools[i % len(self.pools)]
         if self.hot:
@@ -178,10 +178,10 @@ class Setup:
                                       self.w.attn_scale, self.out, self.ws, num_splits=self.splits)
             return
         if self.sparse_v is not None:
-            tq.tq_kv_append(self.layout, pool, self.k_last, self.v_last, self.slots_last)
-            tq.tq_decode_attn_sparse_v(self.layout, pool, self.q, self.bt_dev, self.lens_dev,
-                                       self.max_ctx, self.w.attn_scale, self.sparse_v, self.out,
-                                       self.ws, num_splits=self.splits, v_pages_skipped=self.v_skipped)
+            tq.tq_append_decode_attn_sparse_v(self.layout, pool, self.k_last, self.v_last, self.q,
+                                              self.bt_dev, self.lens_dev, self.max_ctx,
+                                              self.w.attn_scale, self.sparse_v, self.out, self.ws,
+                                              num_splits=self.splits, v_pages_skipped=self.v_skipped)
             return
         tq.tq_append_decode_attn(self.layout, pool, self.k_last, self.v_last, self.q, self.bt_dev,
                                  self.lens_dev, self.max_ctx, self.w.attn_scale, self.out, self.ws,

@@ -266,6 +266,27 @@ int tq_decode_attn_sparse_v(const tq_layout* layout, const void* pool, const voi
                             size_t workspace_bytes, unsigned long long* v_pages_skipped,
                             void* stream);
 
+/* Sparse values with the newest token appended in the same launch: the same result as
+ *   tq_kv_append(k_last, v_last, slots = position context_lens[b] - 1 of each sequence)
+ *   followed by tq_decode_attn_sparse_v(...), as tq_append_decode_attn is to tq_decode_attn.
+ * Both passes of the split that holds a sequence's last page use the new token from on-chip
+ * memory: its key in the first (so its score counts in the page's maximum and in the
+ * normalizer), its key and value in the second if the page is kept. Which pages are dropped
+ * follows tq_decode_attn_sparse_v; v_threshold = 0 drops none and is tq_append_decode_attn,
+ * bit for bit.
+ *   pool, k_last, v_last, in_dtype   as tq_append_decode_attn
+ *   v_threshold, v_pages_skipped     as tq_decode_attn_sparse_v
+ *   other arguments, workspace and errors as tq_decode_attn_sparse_v.
+ * [mlxcel manual, sparse-V threshold; Open-TQ-Metal, card abstract: quantize on append] */
+int tq_append_decode_attn_sparse_v(const tq_layout* layout, void* pool, const void* k_last,
+                                   const void* v_last, int32_t in_dtype, const void* q,
+                                   int32_t q_dtype, int32_t batch, const int32_t* block_table,
+                                   int32_t max_pages_per_seq, const int32_t* context_lens,
+                                   int32_t max_context_len, float attn_scale, float v_threshold,
+                                   int32_t num_splits, float* out, void* workspace,
+                                   size_t workspace_bytes, unsigned long long* v_pages_skipped,
+                                   void* stream);
+
 /* Decode attention over a hot/cold cache: the packed pool holds each sequence's older
  * tokens and an fp16 tail its most recent ones [mlxcel "TurboQuant KV cache" manual,
  * delegated cache: recent tokens in fp16, older ones in the 4-bit form]. Sequence b attends

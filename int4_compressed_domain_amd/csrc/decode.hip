@@ -390,7 +390,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   constexpr int E = CodecCfg<D>::E;
   float ynew[E];
   uint32_t swnew = 0;
-  if (!SPV && !hotwg && a.knew != nullptr && wv == NW - 1 && lane < 32) {
+  if (!hotwg && a.knew != nullptr && wv == NW - 1 && lane < 32) {
     swnew = lane_signs<D>(a.sign_bits, tq_blk16(lane & 15));
     const int64_t off = ((int64_t)b * a.Hkv + h) * D + tq_blk16(lane & 15) * E;
     const void* src = (lane < 16) ? a.knew : a.vnew;
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // workgroup's start does not wait for it, and raises tok_ready; wave wl, which owns the
   // last page, waits for the flag before it patches the token into that page; wave wc
   // stores the token to the pool after the page loop.
-  const bool app = !SPV && !hotwg && (a.knew != nullptr) && (s == ns_cold - 1);
+  const bool app = !hotwg && (a.knew != nullptr) && (s == ns_cold - 1);
   const int plast = npages - 1, tnew = (L - 1) & 15;
   const int wc = NW - 1, wl = (plast - p0) % NW;
   int pid_last = 0;  // wave wc: physical id of the last page, for the token's store to the pool
@@ -1044,8 +1044,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
 
   // Copy the appended token's bytes (indices and scales of token tnew) from tokblk into a
   // block: the pool (to_lds = false), or the staged LDS copy of the last page, whose index
-  // regions are stored chunk by chunk as the page loads wrote them (see stage_page).
-  auto copy_token = [&](uint8_t* dst, bool to_lds) {
+  // regions are stored chunk by chunk as the page loads wrote them (see stage_page). With
+  // keys_only, only its key bytes and K scales, into a key-only staged copy of sparse
+  // values' first pass whose K scales start at kso (stage_k, stage_kc).
+  auto copy_token = [&](uint8_t* dst, bool to_lds, bool keys_only = false, int kso = C::SOFF) {
     constexpr int G_ = D / 32, KB = C::KB, DM = C::DMAK;
     // staged position of a 4-bit index byte w of an index region (page loads write each
     // region chunk by chunk: chunk w / DM of every lane, lane after lane)
@@ -1057,7 +1059,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       if (!to_lds) return o;
       if (o < C::BV) return KF16 ? o : staged(o);  // keys (fp16 keys are staged as stored)
       if (o < C::BS) return VB == 4 ? C::VOFF + staged(o - C::BV) : C::VOFF + (o - C::BV);
-      return C::SOFF + (o - C::BS);
+      return kso + (o - C::BS);
     };
     if constexpr (KF16) {
       for (int i = lane; i < 4 * G_; i += 64) {  // fp16 key: 8-dim run (g, j) = (i / 4, i % 4)
@@ -1069,6 +1071,13 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
         const int off = (16 * (i & 3) + tnew) * 4 * G_ + 4 * (i >> 2);
         *reinterpret_cast<uint32_t*>(dst + at(off)) = *reinterpret_cast<const uint32_t*>(tokblk + off);
       }
+    }
+    if (keys_only) {
+      if (!KF16 && lane < G_) {  // the token's K scales
+        const int off = C::BS + 2 * (tnew * G_ + lane);
+        *reinterpret_cast<f16*>(dst + at(off)) = *reinterpret_cast<const f16*>(tokblk + off);
+      }
+      return;
     }
     if constexpr (VB == 4) {
       for (int c = lane; c < D / 2; c += 64) {  // V index bytes: dim pair c = 16g + m
@@ -1169,6 +1178,54 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       }
     }
   };
+  // The appended token (block layout in tokblk) into the registers of the page that holds
+  // it: lane l holds the K index dwords of token l % 16, in byte e of each V index dword
+  // the token 4 (l / 16) + e, and scale dword l (and 64 + l) of the block, whose two
+  // halves belong to one token.
+  auto patch_regs = [&](uint32_t (&k)[RG], uint32_t (&v)[VRG], uint32_t (&sw)[SW]) {
+    if ((lane & 15) == tnew) {
+#pragma unroll
+      for (int g = 0; g < RG; g++) k[g] = *reinterpret_cast<const uint32_t*>(tokblk + lane * 4 * G + 4 * g);
+    }
+    if ((lane >> 4) == (tnew >> 2)) {
+      const uint32_t m = 0xFFu << (8 * (tnew & 3));
+      if constexpr (VB == 4) {
+#pragma unroll
+        for (int g = 0; g < RG; g++)
+          v[g] = (v[g] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + lane * 4 * G + 4 * g) & m);
+      } else {  // packed: byte tnew % 4 of the lane's X dwords (and of its Z dword)
+#pragma unroll
+        for (int i = 0; i < XD; i++)
+          v[i] = (v[i] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + 4 * (lane * XD + i)) & m);
+        if constexpr (VB == 3) {
+          const int zd = G == 2 ? lane >> 1 : lane;
+          v[XD] = (v[XD] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + 128 * G + 4 * zd) & m);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < SW; c++) {
+      const int d = 64 * c + lane;                 // scale dword: halves 2d, 2d + 1
+      const int hv = 2 * d - (2 * d >= 16 * G ? 16 * G : 0);  // half index inside K or V scales
+      if (d < C::SCB / 4 && hv / G == tnew)
+        sw[c] = *reinterpret_cast<const uint32_t*>(tokblk + C::BS + 4 * d);
+    }
+  };
+  // The same for sparse values' first pass, whose page registers hold only the K index
+  // dwords and K scale dwords l (and 64 + l) of the block (lanes past the K scales hold a
+  // copy of the last one)
+  auto patch_keys = [&](uint32_t (&k)[RG], uint32_t (&sw)[SW]) {
+    if ((lane & 15) == tnew) {
+#pragma unroll
+      for (int g = 0; g < RG; g++) k[g] = *reinterpret_cast<const uint32_t*>(tokblk + lane * 4 * G + 4 * g);
+    }
+#pragma unroll
+    for (int c = 0; c < SW; c++) {
+      const int d = 64 * c + lane;  // K scale dword: halves 2d, 2d + 1 of token 2d / G
+      if (d < C::SCB / 8 && (2 * d) / G == tnew)
+        sw[c] = *reinterpret_cast<const uint32_t*>(tokblk + C::BS + 4 * d);
+    }
+  };
   if constexpr (SPV) {
     // Sparse values [mlxcel manual, sparse-V threshold]. Pass 1 streams the keys of every
     // page of this wave (exact running max and sum, page maxima). The workgroup's maximum
@@ -1181,10 +1238,16 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
     if constexpr (REG) {
       // keys only, through registers: the X and Y sets alternate as in the dense loop
       auto krun = [&](int st, uint32_t (&k)[PPS][RG], uint32_t (&sw)[PPS][SW], uint8_t* ss) {
-        put_scales(ss, sw);
         int pg[PPS];
 #pragma unroll
         for (int i = 0; i < PPS; i++) pg[i] = p0 + wv + NW * (PPS * st + i);
+        if (app && wv == wl) {  // wave-uniform: the appended token's key into its page
+          wait_token();
+#pragma unroll
+          for (int i = 0; i < PPS; i++)
+            if (pg[i] == plast) patch_keys(k[i], sw[i]);
+        }
+        put_scales(ss, sw);
         kstepN(k, ss, PPS * st, pg);
       };
       const int nst = (npw + PPS - 1) / PPS;
@@ -1210,6 +1273,12 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
           }
         wait_pages_in_flight<SplitDma<D, KCODEC, VB>::NK_OPS, NR - 2>(max(0, min(NR - 2, nis - na - 2)));
         const int pa = p0 + wv + NW * na;
+        if (app && wv == wl && (pa == plast || pa + NW == plast)) {  // wave-uniform
+          wait_token();
+          copy_token(const_cast<uint8_t*>(k_slot(pa == plast ? na : na + 1)), true, true,
+                     C::HS ? C::KREG : C::SOFF);
+          asm volatile("" ::: "memory");
+        }
         kstep(na, k_slot(na), k_slot(na + 1), pa, pa + NW);
       }
     }
@@ -1273,6 +1342,12 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
           ldp(n, xk[j], xv[j], xs[j]);
           pg[j] = kept ? p0 + wv + NW * n : p1;
         }
+        if (app && wv == wl) {  // wave-uniform: the appended token into its page, if kept
+          wait_token();
+#pragma unroll
+          for (int j = 0; j < PPS; j++)
+            if (pg[j] == plast) patch_regs(xk[j], xv[j], xs[j]);
+        }
         put_scales(ssw, xs);
         stepN(xk, xv, ssw, pg);
       }
@@ -1290,6 +1365,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
         wait_pages_in_flight<C::NDMA, NSLOT - 2>(max(0, min(NSLOT - 2, nis2 - i - 2)));
         const int pa = p0 + wv + NW * kn(i);
         const int pb = (i + 1 < nk) ? p0 + wv + NW * kn(i + 1) : p1;  // p1: no page B
+        if (app && wv == wl && (pa == plast || pb == plast)) {  // wave-uniform
+          wait_token();
+          copy_token(ring[(pa == plast ? i : i + 1) % NSLOT][wv], true);
+          asm volatile("" ::: "memory");
+        }
         step(ring[i % NSLOT][wv], ring[(i + 1) % NSLOT][wv], pa, pb);
       }
     }
@@ -1299,39 +1379,6 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   } else if constexpr (REG) {
     // Register path: step st over the X set, step st + 1 over the Y set; each set is
     // reloaded (two steps ahead) as soon as its step is done.
-    // The appended token (block layout in tokblk) into the registers of the page that holds
-    // it: lane l holds the K index dwords of token l % 16, in byte e of each V index dword
-    // the token 4 (l / 16) + e, and scale dword l (and 64 + l) of the block, whose two
-    // halves belong to one token.
-    auto patch_regs = [&](uint32_t (&k)[RG], uint32_t (&v)[VRG], uint32_t (&sw)[SW]) {
-      if ((lane & 15) == tnew) {
-#pragma unroll
-        for (int g = 0; g < RG; g++) k[g] = *reinterpret_cast<const uint32_t*>(tokblk + lane * 4 * G + 4 * g);
-      }
-      if ((lane >> 4) == (tnew >> 2)) {
-        const uint32_t m = 0xFFu << (8 * (tnew & 3));
-        if constexpr (VB == 4) {
-#pragma unroll
-          for (int g = 0; g < RG; g++)
-            v[g] = (v[g] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + lane * 4 * G + 4 * g) & m);
-        } else {  // packed: byte tnew % 4 of the lane's X dwords (and of its Z dword)
-#pragma unroll
-          for (int i = 0; i < XD; i++)
-            v[i] = (v[i] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + 4 * (lane * XD + i)) & m);
-          if constexpr (VB == 3) {
-            const int zd = G == 2 ? lane >> 1 : lane;
-            v[XD] = (v[XD] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + 128 * G + 4 * zd) & m);
-          }
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < SW; c++) {
-        const int d = 64 * c + lane;                 // scale dword: halves 2d, 2d + 1
-        const int hv = 2 * d - (2 * d >= 16 * G ? 16 * G : 0);  // half index inside K or V scales
-        if (d < C::SCB / 4 && hv / G == tnew)
-          sw[c] = *reinterpret_cast<const uint32_t*>(tokblk + C::BS + 4 * d);
-      }
-    };
     // One step over a set. The last step of a wave is the only one that can hold the
     // sequence's last page (pages ascend), so only it carries the fused append's patch.
     auto run_step = [&](auto last, int st, uint32_t (&k)[PPS][RG], uint32_t (&v)[PPS][VRG],

@@ -417,6 +417,24 @@ int tq_decode_attn_sparse_v(const tq_layout* L, const void* pool, const void* q,
                      v_pages_skipped);
 }
 
+int tq_append_decode_attn_sparse_v(const tq_layout* L, void* pool, const void* k_last,
+                                   const void* v_last, int32_t in_dtype, const void* q,
+                                   int32_t q_dtype, int32_t batch, const int32_t* block_table,
+                                   int32_t max_pages_per_seq, const int32_t* context_lens,
+                                   int32_t max_context_len, float attn_scale, float v_threshold,
+                                   int32_t num_splits, float* out, void* workspace,
+                                   size_t workspace_bytes_, unsigned long long* v_pages_skipped,
+                                   void* stream) {
+  if (!(v_threshold >= 0.0f && v_threshold < 1.0f)) return TQ_EINVAL;
+  if (in_dtype != TQ_F32 && in_dtype != TQ_BF16 && in_dtype != TQ_F16) return TQ_EINVAL;
+  if (batch > 0 && (!k_last || !v_last)) return TQ_EINVAL;
+  // a zero threshold drops nothing: tq_append_decode_attn, bit for bit
+  return decode_impl(L, pool, k_last, v_last, in_dtype, q, q_dtype, batch, block_table,
+                     max_pages_per_seq, context_lens, max_context_len, attn_scale, num_splits, out,
+                     workspace, workspace_bytes_, stream, v_threshold > 0.0f ? 1 : 0, v_threshold,
+                     v_pages_skipped);
+}
+
 int tq_decode_attn_hotcold(const tq_layout* L, const void* pool, const void* q, int32_t q_dtype,
                            int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
                            const int32_t* cold_lens, int32_t max_cold_len, const void* hot_k,

@@ -18,7 +18,8 @@ PROBE_LIB_PATH = os.path.join(HERE, "libtq_probe.so")  # measurement aid (includ
 
 EXPORTS = ("tq_status_str", "tq_page_bytes", "tq_kv_append", "tq_decode_workspace_size",
            "tq_decode_attn", "tq_append_decode_attn", "tq_decode_attn_sparse_v", "tq_dequant_ref",
-           "tq_dense_decode_attn", "tq_decode_attn_hotcold", "tq_decode_attn_noalloc")
+           "tq_dense_decode_attn", "tq_decode_attn_hotcold", "tq_decode_attn_noalloc",
+           "tq_append_decode_attn_sparse_v")
 PROBE_EXPORTS = ("tq_stream_read_probe",)
 
 
@@ -64,6 +65,10 @@ def _lib():
             L.tq_decode_attn_sparse_v.argtypes = [LP, P, P, i32, i32, P, i32, P, i32, f32, f32, i32,
                                                   P, P, sz, P, P]
             L.tq_decode_attn_sparse_v.restype = ctypes.c_int
+        if hasattr(L, "tq_append_decode_attn_sparse_v"):
+            L.tq_append_decode_attn_sparse_v.argtypes = [LP, P, P, P, i32, P, i32, i32, P, i32, P, i32,
+                                                         f32, f32, i32, P, P, sz, P, P]
+            L.tq_append_decode_attn_sparse_v.restype = ctypes.c_int
         L.tq_dequant_ref.argtypes = [LP, P, i32, P, i32, P, i32, i32, i32, P, P, P]
         if hasattr(L, "tq_decode_attn_hotcold"):
             L.tq_decode_attn_hotcold.argtypes = [LP, P, P, i32, i32, P, i32, P, i32, P, P, P, i32, f32,
@@ -184,6 +189,18 @@ def tq_decode_attn_sparse_v(layout, pool, q, block_table, context_lens, max_cont
         block_table.shape[1], _ptr(context_lens), max_context_len, attn_scale, v_threshold,
         num_splits, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(v_pages_skipped), _stream(stream)), "tq_decode_attn_sparse_v")
+
+
+def tq_append_decode_attn_sparse_v(layout, pool, k_last, v_last, q, block_table, context_lens,
+                                   max_context_len, attn_scale, v_threshold, out, workspace,
+                                   num_splits=0, v_pages_skipped=None, stream=None):
+    """tq_append_decode_attn with sparse values (tq_decode_attn_sparse_v's threshold)."""
+    _check(_lib().tq_append_decode_attn_sparse_v(
+        ctypes.byref(layout), _ptr(pool), _ptr(k_last), _ptr(v_last), _dtype_code(k_last),
+        _ptr(q), _dtype_code(q), q.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(context_lens), max_context_len, attn_scale, v_threshold, num_splits, _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(v_pages_skipped),
+        _stream(stream)), "tq_append_decode_attn_sparse_v")
 
 
 def tq_dequant_ref(layout, pool, block_table, context_lens, max_context_len, k_out, v_out,

@@ -140,6 +140,29 @@ def test_sparse_v_argument_validation():
     assert _sparse(_layout(), batch=(1 << 16) // 8 + 1) == tq.TQ_EUNSUPPORTED
 
 
+def _append_sparse(L, thr=1e-6, batch=2, kl=FAKE, vl=FAKE, kd=tq.BF16, q=FAKE, wsb=1 << 30,
+                   out=FAKE, pool=FAKE):
+    return tq.lib().tq_append_decode_attn_sparse_v(ctypes.byref(L), pool, kl, vl, kd, q, tq.BF16, batch,
+                                                   FAKE, 4, FAKE, 64, 0.1, thr, 0, out, FAKE, wsb, None,
+                                                   None)
+
+
+def test_append_sparse_v_argument_validation():
+    L = _layout()
+    assert _append_sparse(L, thr=-1e-6) == tq.TQ_EINVAL
+    assert _append_sparse(L, thr=1.0) == tq.TQ_EINVAL
+    assert _append_sparse(L, thr=float("nan")) == tq.TQ_EINVAL
+    assert _append_sparse(L, kd=5) == tq.TQ_EINVAL              # bad k/v dtype
+    assert _append_sparse(L, kl=None) == tq.TQ_EINVAL
+    assert _append_sparse(L, vl=None) == tq.TQ_EINVAL
+    assert _append_sparse(L, q=None) == tq.TQ_EINVAL
+    assert _append_sparse(L, pool=None) == tq.TQ_EINVAL
+    assert _append_sparse(L, wsb=16) == tq.TQ_ENOSPC
+    assert _append_sparse(_layout(v_codec=tq.CODEC_ABSMAX2), wsb=16) == tq.TQ_ENOSPC
+    assert _append_sparse(L, batch=(1 << 16) // 8 + 1) == tq.TQ_EUNSUPPORTED
+    assert _append_sparse(L, batch=0, kl=None, vl=None, q=None, out=None) == tq.TQ_OK
+
+
 def test_stream_read_probe_validation():
     probe = tq.probe_lib().tq_stream_read_probe
     assert probe(FAKE, 0, None, 0, None) == tq.TQ_OK          # nothing to read

@@ -514,6 +514,78 @@ def test_append_decode_equals_append_then_decode(D, r, k_codec, dtype, v_codec):
     assert np.all(outs[0][0] == 0.0)
 
 
+@pytest.mark.parametrize("D,r,k_codec,v_codec", [(128, 8, 0, 0), (128, 4, 0, 0), (128, 2, 0, V2),
+                                                 (64, 4, 0, V3), (128, 4, 1, 0), (128, 4, 2, 0),
+                                                 (256, 2, 0, 0), (256, 2, 2, V3)])
+def test_append_sparse_v_equals_append_then_sparse_v(D, r, k_codec, v_codec):
+    """The fused sparse-value entry point writes the same pool bytes as tq_kv_append of each
+    sequence's last token; with one split (one published maximum per unit, so the pages
+    dropped do not depend on timing) it returns the same output and skip count, bit for
+    bit, as tq_decode_attn_sparse_v afterwards; with automatic splits it stays within the
+    tolerance plus the oracle's bound on the dropped terms."""
+    lens = [0, 1, 15, 16, 17, 33, 250, 1000]
+    w = W.Workload("appsv", len(lens), 2 * r, 2, D, max(lens), "bf16", 1.0 / math.sqrt(D),
+                   k_codec=k_codec, v_codec=v_codec, dist="lognormal_spikes")
+    _say("case append+sparse values D", D, "r", r, "k_codec", k_codec, "v_codec", v_codec)
+    fused = Case(w, seed=37, lens=lens)
+    split = Case(w, seed=37, lens=lens, oracle=False)
+    for c in (fused, split):  # every token but the last
+        for b, L in enumerate(c.lens):
+            if L > 1:
+                c.append_seq(b, 0, int(L) - 1)
+    k_last = np.zeros((w.batch, w.kv_heads, D), np.float32)
+    v_last = np.zeros_like(k_last)
+    kst = np.zeros(k_last.shape, np.uint16)
+    vst = np.zeros_like(kst)
+    slots = np.full(w.batch, -1, np.int64)
+    for b, L in enumerate(fused.lens):
+        if L > 0:
+            k32, v32, ks_, vs_ = W.seq_tokens(w, b, int(L), fused.seed, fused.scales)
+            k_last[b], v_last[b], kst[b], vst[b] = k32[-1], v32[-1], ks_[-1], vs_[-1]
+            slots[b] = W.slots_for(fused.bt, b, int(L) - 1, int(L))[0]
+    maxc = int(max(lens))
+    kd, vd = to_dev(kst, "bf16"), to_dev(vst, "bf16")
+
+    def run(c, use_fused, splits):
+        ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, w.batch, maxc, splits) // 4, dtype=torch.float32,
+                         device=DEV)
+        out = torch.full((w.batch, w.q_heads, D), float("nan"), dtype=torch.float32, device=DEV)
+        sk = torch.zeros(1, dtype=torch.int64, device=DEV)
+        if use_fused:
+            tq.tq_append_decode_attn_sparse_v(c.layout, c.pool, kd, vd, c.q_dev, c.bt_dev, c.lens_dev, maxc,
+                                              w.attn_scale, 1e-6, out, ws, num_splits=splits, v_pages_skipped=sk)
+        else:
+            tq.tq_kv_append(c.layout, c.pool, kd, vd, torch.from_numpy(slots).to(DEV))
+            tq.tq_decode_attn_sparse_v(c.layout, c.pool, c.q_dev, c.bt_dev, c.lens_dev, maxc, w.attn_scale,
+                                       1e-6, out, ws, num_splits=splits, v_pages_skipped=sk)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), int(sk.item())
+
+    of, skf = run(fused, True, 1)
+    os_, sks = run(split, False, 1)
+    keep = slots >= 0
+    c_oracle.append(fused.opool, D, w.kv_heads, k_last[keep], v_last[keep], slots[keep], fused.sb,
+                    w.k_codec, w.v_codec)
+    assert np.array_equal(fused.pool.cpu().numpy(), split.pool.cpu().numpy())
+    assert fused.pool_equal()
+    _say("   one split: skipped %d value pages (fused) and %d (separate append)" % (skf, sks))
+    assert skf == sks
+    if r <= 4:  # (with 8 q heads per kv head some head keeps nearly every page here)
+        assert skf > 0
+    assert np.array_equal(of, os_)
+    assert np.all(of[0] == 0.0)
+    exact = fused.decode_oracle()
+    _, bound = c_oracle.decode_sparse_v(fused.opool, D, w.q_heads, w.kv_heads, fused.sb, fused.bt,
+                                        fused.lens, fused.q32, w.attn_scale, 1e-6, k_codec=w.k_codec,
+                                        v_codec=w.v_codec)
+    lim = ATTN_TOL * np.max(np.abs(exact), axis=2) + bound
+    for out in (of, run(fused, True, 0)[0]):  # (the second call appends the same bytes again)
+        err = np.max(np.abs(out - exact), axis=2)
+        _say("   max err %.3e" % err.max())
+        assert np.all(np.isfinite(out)) and np.all(err <= lim)
+    assert fused.pool_equal()
+
+
 def test_workspace_reuse_across_calls():
     """The split-arrival counters in the workspace return to zero after every call, so one
     zero-filled workspace serves calls of any batch size and split count in sequence."""
