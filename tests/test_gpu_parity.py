@@ -603,14 +603,20 @@ def test_workspace_reuse_across_calls():
     assert int(ws[:(4 << 20) // 4].view(torch.int32).abs().sum().item()) == 0, "counters not reset"
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("mode", ["append_then_decode", "fused", "fused_sparse"])
+def test_graph_replay_matches_eager(mode):
     """append + decode captured in a HIP graph, replayed several times with eager work and
-    synchronizations in between; every replay must equal the eager result bit for bit."""
+    synchronizations in between; every replay must equal the eager result bit for bit. The
+    step is tq_kv_append then tq_decode_attn, or one tq_append_decode_attn, or one
+    tq_append_decode_attn_sparse_v with one split (whose dropped pages do not depend on
+    timing)."""
     w = W.WORKLOADS["llama8b_b16_8k"].scaled(context=900, batch=4)
     c = Case(w, seed=23, lens=[900, 899, 450, 17])
     c.fill()
     L = c.lens.copy()
-    ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, w.batch, int(L.max()), 0) // 4, dtype=torch.float32, device=DEV)
+    nsp = 1 if mode == "fused_sparse" else 0
+    ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, w.batch, int(L.max()), nsp) // 4, dtype=torch.float32,
+                     device=DEV)
     out = torch.zeros((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=DEV)
     # the step re-appends the last token of every sequence, then decodes
     k32, v32, kst, vst, sl = [], [], [], [], []
@@ -622,13 +628,28 @@ def test_graph_replay_matches_eager():
     sd = torch.from_numpy(np.concatenate(sl)).to(DEV)
 
     def step():
-        tq.tq_kv_append(c.layout, c.pool, kd, vd, sd)
-        tq.tq_decode_attn(c.layout, c.pool, c.q_dev, c.bt_dev, c.lens_dev, int(L.max()), w.attn_scale, out, ws)
+        if mode == "append_then_decode":
+            tq.tq_kv_append(c.layout, c.pool, kd, vd, sd)
+            tq.tq_decode_attn(c.layout, c.pool, c.q_dev, c.bt_dev, c.lens_dev, int(L.max()), w.attn_scale, out, ws)
+        elif mode == "fused":
+            tq.tq_append_decode_attn(c.layout, c.pool, kd, vd, c.q_dev, c.bt_dev, c.lens_dev, int(L.max()),
+                                     w.attn_scale, out, ws)
+        else:
+            tq.tq_append_decode_attn_sparse_v(c.layout, c.pool, kd, vd, c.q_dev, c.bt_dev, c.lens_dev,
+                                              int(L.max()), w.attn_scale, 1e-6, out, ws, num_splits=nsp)
 
     step()
     torch.cuda.synchronize()
     eager = out.clone()
-    assert attn_err(eager.cpu().numpy(), c.decode_oracle()).max() <= ATTN_TOL
+    assert c.pool_equal()
+    exact = c.decode_oracle()
+    if mode == "fused_sparse":  # within the tolerance plus the oracle's bound on the dropped terms
+        _, bound = c_oracle.decode_sparse_v(c.opool, w.head_dim, w.q_heads, w.kv_heads, c.sb, c.bt, c.lens,
+                                            c.q32, w.attn_scale, 1e-6, k_codec=w.k_codec, v_codec=w.v_codec)
+        err = np.max(np.abs(eager.cpu().numpy() - exact), axis=2)
+        assert np.all(err <= ATTN_TOL * np.max(np.abs(exact), axis=2) + bound)
+    else:
+        assert attn_err(eager.cpu().numpy(), exact).max() <= ATTN_TOL
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
