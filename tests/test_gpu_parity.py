@@ -707,6 +707,27 @@ def test_random_configurations(i):
     for b, L in enumerate(lens):
         if L == 0:
             assert np.all(out[b] == 0.0)
+    # sparse values with the last token re-appended in the launch (the same bytes again)
+    k_last = np.zeros((batch, kv, D), np.uint16)
+    v_last = np.zeros_like(k_last)
+    for b, L in enumerate(lens):
+        if L > 0:
+            _, _, ks_, vs_ = W.seq_tokens(w, b, L, c.seed, c.scales)
+            k_last[b], v_last[b] = ks_[-1], vs_[-1]
+    maxc = max(lens)
+    ws = torch.zeros(max(tq.tq_decode_workspace_size(c.layout, batch, maxc, splits), 4) // 4, dtype=torch.float32,
+                     device=DEV)
+    sp = torch.full((batch, kv * r, D), float("nan"), dtype=torch.float32, device=DEV)
+    tq.tq_append_decode_attn_sparse_v(c.layout, c.pool, to_dev(k_last, "bf16"), to_dev(v_last, "bf16"), c.q_dev,
+                                      c.bt_dev, c.lens_dev, maxc, w.attn_scale, 1e-6, sp, ws, num_splits=splits)
+    torch.cuda.synchronize()
+    assert c.pool_equal(), "the re-appended tokens changed the pool"
+    exact = c.decode_oracle()
+    _, bound = c_oracle.decode_sparse_v(c.opool, D, w.q_heads, kv, c.sb, c.bt, c.lens, c.q32, w.attn_scale, 1e-6,
+                                        k_codec=k_codec, v_codec=v_codec)
+    err = np.max(np.abs(sp.cpu().numpy() - exact), axis=2)
+    _say("   fused sparse values: max err %.3e" % err.max())
+    assert np.all(err <= ATTN_TOL * np.max(np.abs(exact), axis=2) + bound)
 
 
 @pytest.mark.parametrize("nbytes", [16, 16 * 12345, 8 << 20])
