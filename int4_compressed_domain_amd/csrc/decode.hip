@@ -1183,32 +1183,34 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   // the token 4 (l / 16) + e, and scale dword l (and 64 + l) of the block, whose two
   // halves belong to one token.
   auto patch_regs = [&](uint32_t (&k)[RG], uint32_t (&v)[VRG], uint32_t (&sw)[SW]) {
-    if ((lane & 15) == tnew) {
+    if constexpr (REG) {  // (register pages only)
+      if ((lane & 15) == tnew) {
 #pragma unroll
-      for (int g = 0; g < RG; g++) k[g] = *reinterpret_cast<const uint32_t*>(tokblk + lane * 4 * G + 4 * g);
-    }
-    if ((lane >> 4) == (tnew >> 2)) {
-      const uint32_t m = 0xFFu << (8 * (tnew & 3));
-      if constexpr (VB == 4) {
+        for (int g = 0; g < RG; g++) k[g] = *reinterpret_cast<const uint32_t*>(tokblk + lane * 4 * G + 4 * g);
+      }
+      if ((lane >> 4) == (tnew >> 2)) {
+        const uint32_t m = 0xFFu << (8 * (tnew & 3));
+        if constexpr (VB == 4) {
 #pragma unroll
-        for (int g = 0; g < RG; g++)
-          v[g] = (v[g] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + lane * 4 * G + 4 * g) & m);
-      } else {  // packed: byte tnew % 4 of the lane's X dwords (and of its Z dword)
+          for (int g = 0; g < RG; g++)
+            v[g] = (v[g] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + lane * 4 * G + 4 * g) & m);
+        } else {  // packed: byte tnew % 4 of the lane's X dwords (and of its Z dword)
 #pragma unroll
-        for (int i = 0; i < XD; i++)
-          v[i] = (v[i] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + 4 * (lane * XD + i)) & m);
-        if constexpr (VB == 3) {
-          const int zd = G == 2 ? lane >> 1 : lane;
-          v[XD] = (v[XD] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + 128 * G + 4 * zd) & m);
+          for (int i = 0; i < XD; i++)
+            v[i] = (v[i] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + 4 * (lane * XD + i)) & m);
+          if constexpr (VB == 3) {
+            const int zd = G == 2 ? lane >> 1 : lane;
+            v[XD] = (v[XD] & ~m) | (*reinterpret_cast<const uint32_t*>(tokblk + C::BV + 128 * G + 4 * zd) & m);
+          }
         }
       }
-    }
 #pragma unroll
-    for (int c = 0; c < SW; c++) {
-      const int d = 64 * c + lane;                 // scale dword: halves 2d, 2d + 1
-      const int hv = 2 * d - (2 * d >= 16 * G ? 16 * G : 0);  // half index inside K or V scales
-      if (d < C::SCB / 4 && hv / G == tnew)
-        sw[c] = *reinterpret_cast<const uint32_t*>(tokblk + C::BS + 4 * d);
+      for (int c = 0; c < SW; c++) {
+        const int d = 64 * c + lane;                 // scale dword: halves 2d, 2d + 1
+        const int hv = 2 * d - (2 * d >= 16 * G ? 16 * G : 0);  // half index inside K or V scales
+        if (d < C::SCB / 4 && hv / G == tnew)
+          sw[c] = *reinterpret_cast<const uint32_t*>(tokblk + C::BS + 4 * d);
+      }
     }
   };
   // The same for sparse values' first pass, whose page registers hold only the K index
