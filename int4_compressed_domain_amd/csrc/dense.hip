@@ -1,12 +1,14 @@
 // Dense fp16 decode attention: the "attend" half of the dequantize-then-attend baseline
-// [Open-TQ-Metal, arXiv abstract], plus the split merge it uses. Plain VALU fp32
-// arithmetic; this is the comparison path, not the product's hot path.
+// [Open-TQ-Metal, arXiv abstract], plus the split merge it uses. This is the comparison
+// path, not the product's hot path, but it is built to stream its fp16 K and V near the
+// memory rate: scores on the matrix cores (16 tokens x 16 columns per MFMA: 8 query heads
+// as fp16 hi parts, the same heads' lo parts), values on the VALU with fp32 accumulation.
 #include "tq_device.h"
 #include "tq_internal.h"
 
 namespace {
 // Merge of the context splits: m* = max m_s, o = sum_s 2^(m_s - m*) o_s / sum_s 2^(m_s - m*) l_s.
-template <int D, bool UNROTATE>
+template <int D>
 __global__ __launch_bounds__(64) void merge_splits(LaunchDecode a) {
   constexpr int PL = D / 64;
   const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
@@ -14,7 +16,6 @@ __global__ __launch_bounds__(64) void merge_splits(LaunchDecode a) {
   const int npages = (L + 15) >> 4;
   const int ns = (npages + a.pages_per_split - 1) / a.pages_per_split;
   const int64_t row0 = ((int64_t)b * a.Hq + hq) * a.splits;
-  __shared__ float buf[D];
   float M = -INFINITY;
   for (int s = 0; s < ns; s++) M = fmaxf(M, a.part_ml[2 * (row0 + s)]);
   float lsum = 0.0f, v[PL];
@@ -29,152 +30,210 @@ __global__ __launch_bounds__(64) void merge_splits(LaunchDecode a) {
     for (int k = 0; k < PL; k++) v[k] += f * a.part_o[(row0 + s) * D + lane + 64 * k];
   }
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-#pragma unroll
-  for (int k = 0; k < PL; k++) buf[lane + 64 * k] = v[k] * inv;
-  if constexpr (UNROTATE) {
-    for (int st = 1; st < D; st <<= 1) {
-      __syncthreads();
-      for (int pi = lane; pi < D / 2; pi += 64) {
-        const int lo = (pi / st) * 2 * st + (pi % st), hi = lo + st;
-        const float x0 = buf[lo], x1 = buf[hi];
-        buf[lo] = x0 + x1;
-        buf[hi] = x0 - x1;
-      }
-    }
-    __syncthreads();
-    const float rho = tq_rho(D);
-#pragma unroll
-    for (int k = 0; k < PL; k++) {
-      const int d = lane + 64 * k;
-      float x = buf[d] * rho;
-      if ((a.sign_bits[d >> 5] >> (d & 31)) & 1u) x = -x;
-      buf[d] = x;
-    }
-  }
-  __syncthreads();
   float* o = a.out + ((int64_t)b * a.Hq + hq) * D;
 #pragma unroll
-  for (int k = 0; k < PL; k++) o[lane + 64 * k] = buf[lane + 64 * k];
+  for (int k = 0; k < PL; k++) o[lane + 64 * k] = v[k] * inv;
 }
-}  // namespace
 
-namespace {
-
-// Dense fp16 decode attention, the "attend" half of the dequantize-then-attend baseline
-// [Open-TQ-Metal, arXiv abstract]. K, V fp16 [B][Hkv][max_ctx][D] in the original basis;
-// q is used unrotated. Plain VALU fp32 arithmetic on 64-token tiles staged in LDS; the
-// partial (o', m, l) layout is [B][Hq][S][D] and [B][Hq][S][2], merged by merge_splits.
-template <int D, typename TQ>
-__global__ __launch_bounds__(256) void dense_pass1(LaunchDecode a) {
-  constexpr int TT = 64, PD = D + 8, DPT = D / 32;
+// One workgroup of 4 waves per (split, kv head, sequence). The split's tokens are cut into
+// 16-token tiles dealt to the waves in turn; each wave keeps its own running max and sum.
+// Scores of a tile: A = 16 rows of K (lane l: row l%16, dims 32g + 8(l/16) .. +7, one
+// 16-byte load per group straight from the row), B = the query as fp16 hi (columns 0-7)
+// and lo (columns 8-15) parts, scaled per head by a power of two that keeps both parts
+// normal; lane l gets rows 4(l/16) .. +3 of column l%16, and the hi and lo columns are added
+// by a row rotation of 8 lanes. Values: lane l holds G chunks of 8 dims (chunk l % (D/8)) of
+// tokens (l + 64k) / (D/8), reads the tile's weights of all heads from LDS and accumulates
+// 8 dims x RP heads. The waves' (o', m, l) are merged in LDS into the split's partial.
+template <int D, int RP>
+__global__ __launch_bounds__(256) void dense_attn(LaunchDecode a) {
+  constexpr int G = D / 32, NC = D / 8;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = a.Hq / a.Hkv;
+  __shared__ __align__(16) float Pt[4][16][8];     // per wave: the tile's weights [token][head]
+  __shared__ float Ft[4][8];         // per wave: rescale factors of the heads
+  __shared__ float Ow[4][RP][D];     // per wave: o' of each head
+  __shared__ float MLw[4][RP][2];    // per wave: m, l of each head
   const int L = a.context_lens[b];
   const int npages = (L + 15) >> 4;
   const int p0 = s * a.pages_per_split;
   if (p0 >= npages) return;
   const int t0 = p0 * 16, t1 = min(min(p0 + a.pages_per_split, npages) * 16, L);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  __shared__ float qf[8][D];
-  __shared__ f16 kt[TT][PD];
-  __shared__ f16 vt[TT][PD];
-  __shared__ float pt[8][TT];
-  __shared__ float mrow[8], lrow[8], frow[8];
-
-  const TQ* qb = static_cast<const TQ*>(a.q) + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
-  const float qmul = a.attn_scale * TQ_LOG2E;
-  for (int i = tid; i < 8 * D; i += 256) {
-    const int hd = i / D, d = i % D;
-    qf[hd][d] = hd < r ? widen(qb[hd * D + d]) * qmul : 0.0f;
-  }
-  if (tid < 8) { mrow[tid] = -INFINITY; lrow[tid] = 0.0f; frow[tid] = 1.0f; }
-  const f16* kb = static_cast<const f16*>(static_cast<const void*>(a.pool)) +
-                  ((int64_t)b * a.Hkv + h) * (int64_t)a.max_ctx * D;
+  const int ntile = (t1 - t0 + 15) >> 4;
+  const f16* kb = reinterpret_cast<const f16*>(a.pool) + ((int64_t)b * a.Hkv + h) * (int64_t)a.max_ctx * D;
   const f16* vb = static_cast<const f16*>(a.dense_v) + ((int64_t)b * a.Hkv + h) * (int64_t)a.max_ctx * D;
-  const int phd = tid >> 5, pd0 = tid & 31;   // PV mapping: head phd, dims pd0 + 32 k
-  float o[DPT];
-#pragma unroll
-  for (int k = 0; k < DPT; k++) o[k] = 0.0f;
 
-  for (int t = t0; t < t1; t += TT) {
-    const int n = min(TT, t1 - t);
-    __syncthreads();
-    for (int i = tid; i < TT * (D / 8); i += 256) {
-      const int row = i / (D / 8), c8 = i % (D / 8);
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (row < n) {
-        kv = reinterpret_cast<const u32x4*>(kb + (int64_t)(t + row) * D)[c8];
-        vv = reinterpret_cast<const u32x4*>(vb + (int64_t)(t + row) * D)[c8];
-      }
-      *reinterpret_cast<u32x4*>(&kt[row][8 * c8]) = kv;
-      *reinterpret_cast<u32x4*>(&vt[row][8 * c8]) = vv;
+  // ---- query operand: column n = lane % 16 is head n % 8 (hi for n < 8, lo otherwise)
+  const int n = lane & 15, kq = lane >> 4, hd = n & 7;
+  const float qmul = a.attn_scale * TQ_LOG2E;
+  float qx[G][8];
+  const int64_t qoff = ((int64_t)b * a.Hq + (int64_t)h * r + (hd < r ? hd : 0)) * D + 8 * kq;
+  auto ldq = [&](const auto* qp) {
+#pragma unroll
+    for (int g = 0; g < G; g++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) qx[g][e] = hd < r ? widen(qp[qoff + 32 * g + e]) * qmul : 0.0f;
+  };
+  if (a.q_dtype == TQ_F32) ldq(static_cast<const float*>(a.q));
+  else if (a.q_dtype == TQ_BF16) ldq(static_cast<const uint16_t*>(a.q));
+  else ldq(static_cast<const f16*>(a.q));
+  float amax = 0.0f;
+#pragma unroll
+  for (int g = 0; g < G; g++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(qx[g][e]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  int ex = 0;
+  if (amax > 0.0f && amax <= 3.0e38f) (void)frexpf(amax, &ex);
+  const float up = ldexpf(1.0f, 15 - ex), down = ldexpf(1.0f, ex - 15);  // amax*up in [2^14, 2^15)
+  f16x8 bq[G];
+#pragma unroll
+  for (int g = 0; g < G; g++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const float x = qx[g][e] * up;
+      const f16 hi = (f16)x;
+      bq[g][e] = n < 8 ? hi : (f16)(x - (float)hi);
     }
-    __syncthreads();
-    for (int hd = wv; hd < r; hd += 4) {
-      float sc = -INFINITY;
-      if (lane < n) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int d = 0; d < D; d++) acc += qf[hd][d] * (float)kt[lane][d];
-        sc = acc;
-      }
-      float cm = sc;
+
+  float acc[RP][8];
 #pragma unroll
-      for (int o2 = 32; o2 >= 1; o2 >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o2, 64));
-      const float m_old = mrow[hd];
-      const float m_new = fmaxf(m_old, cm);
-      const float p = exp2f(sc - m_new);
-      float ps = p;
+  for (int k = 0; k < RP; k++)
 #pragma unroll
-      for (int o2 = 32; o2 >= 1; o2 >>= 1) ps += __shfl_xor(ps, o2, 64);
-      pt[hd][lane] = p;
-      if (lane == 0) {
-        const float f = exp2f(m_old - m_new);
-        frow[hd] = f;
-        lrow[hd] = lrow[hd] * f + ps;
-        mrow[hd] = m_new;
+    for (int e = 0; e < 8; e++) acc[k][e] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;  // of head hd; l_run is this lane's rows only
+
+  const int chunk = lane % NC;
+  auto load_tile = [&](int tile, f16x8* kA, f16x8* vv) {
+    const int tt = t0 + 16 * tile;
+    const int kr = min(tt + n, L - 1);
+#pragma unroll
+    for (int g = 0; g < G; g++) kA[g] = *reinterpret_cast<const f16x8*>(kb + (int64_t)kr * D + 32 * g + 8 * kq);
+#pragma unroll
+    for (int k = 0; k < G; k++) {
+      const int vr = min(tt + (lane + 64 * k) / NC, L - 1);
+      vv[k] = *reinterpret_cast<const f16x8*>(vb + (int64_t)vr * D + 8 * chunk);
+    }
+  };
+  f16x8 kA[G], vv[G], kN[G], vN[G];
+  if (w < ntile) load_tile(w, kA, vv);
+  for (int tile = w; tile < ntile; tile += 4) {
+    load_tile(min(tile + 4, ntile - 1), kN, vN);  // next tile (the last one again at the end)
+    const int tt = t0 + 16 * tile;
+    f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int g = 0; g < G; g++) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[g], bq[g], c, 0, 0, 0);
+    float sc[4], tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      sc[i] = tt + 4 * kq + i < t1 ? (c[i] + dpp_ror8(c[i])) * down : -INFINITY;
+      tmax = fmaxf(tmax, sc[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      sc[i] = exp2f(sc[i] - m_new);
+      ps += sc[i];
+    }
+    const bool grew = m_new > m_run;
+    const float f = exp2f(m_run - m_new);  // 1 where the max did not grow
+    l_run = l_run * f + ps;
+    m_run = m_new;
+    if (n < 8) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) Pt[w][4 * kq + i][n] = sc[i];
+      if (kq == 0) Ft[w][n] = f;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (__any(grew)) {
+#pragma unroll
+      for (int k = 0; k < RP; k++) {
+        const float fk = Ft[w][k];
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[k][e] *= fk;
       }
     }
-    __syncthreads();
-    if (phd < r) {
-      const float f = frow[phd];
 #pragma unroll
-      for (int k = 0; k < DPT; k++) o[k] *= f;
-      for (int tt = 0; tt < n; tt++) {
-        const float p = pt[phd][tt];
+    for (int k = 0; k < G; k++) {
+      const int tk = (lane + 64 * k) / NC;
+      const f32x4 p0v = *reinterpret_cast<const f32x4*>(&Pt[w][tk][0]);
+      const f32x4 p1v = *reinterpret_cast<const f32x4*>(&Pt[w][tk][4]);
+      const float pk[8] = {p0v[0], p0v[1], p0v[2], p0v[3], p1v[0], p1v[1], p1v[2], p1v[3]};
 #pragma unroll
-        for (int k = 0; k < DPT; k++) o[k] += p * (float)vt[tt][pd0 + 32 * k];
-      }
+      for (int hh = 0; hh < RP; hh++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[hh][e] = __builtin_fmaf((float)vv[k][e], pk[hh], acc[hh][e]);
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int g = 0; g < G; g++) { kA[g] = kN[g]; vv[g] = vN[g]; }
+  }
+  // ---- the wave's totals: o' summed over the lanes of each dim chunk, l over the row groups
+#pragma unroll
+  for (int x = NC; x < 64; x <<= 1)
+#pragma unroll
+    for (int k = 0; k < RP; k++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) acc[k][e] += __shfl_xor(acc[k][e], x, 64);
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (lane < NC)
+#pragma unroll
+    for (int k = 0; k < RP; k++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) Ow[w][k][8 * lane + e] = acc[k][e];
+  if (lane < RP) {
+    MLw[w][lane][0] = m_run;
+    MLw[w][lane][1] = l_run;
   }
   __syncthreads();
-  if (phd < r) {
-    const int64_t row = ((int64_t)b * a.Hq + (int64_t)h * r + phd) * a.splits + s;
+  // ---- merge of the 4 waves into the split's partial (o' relative to the split's max)
+  for (int i = tid; i < r * D; i += 256) {
+    const int k = i / D, d = i % D;
+    float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < DPT; k++) a.part_o[row * D + pd0 + 32 * k] = o[k];
-    if (pd0 == 0) {
-      a.part_ml[2 * row] = mrow[phd];
-      a.part_ml[2 * row + 1] = lrow[phd];
+    for (int v = 0; v < 4; v++) M = fmaxf(M, MLw[v][k][0]);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const float mv = MLw[v][k][0];
+      if (mv == -INFINITY) continue;
+      const float f = exp2f(mv - M);
+      o += f * Ow[v][k][d];
+      l += f * MLw[v][k][1];
+    }
+    const int64_t row = ((int64_t)b * a.Hq + (int64_t)h * r + k) * a.splits + s;
+    a.part_o[row * D + d] = o;
+    if (d == 0) {
+      a.part_ml[2 * row] = M;
+      a.part_ml[2 * row + 1] = l;
     }
   }
 }
 
-template <int D, typename TQ>
-hipError_t launch_dense_dq(const LaunchDecode& a, hipStream_t st) {
-  hipLaunchKernelGGL((dense_pass1<D, TQ>), dim3(a.splits, a.Hkv, a.B), dim3(256), 0, st, a);
+template <int D, int RP>
+hipError_t launch_dense_dr(const LaunchDecode& a, hipStream_t st) {
+  hipLaunchKernelGGL((dense_attn<D, RP>), dim3(a.splits, a.Hkv, a.B), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_splits<D, false>), dim3(a.Hq, a.B), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((merge_splits<D>), dim3(a.Hq, a.B), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_dense_d(const LaunchDecode& a, hipStream_t st) {
-  switch (a.q_dtype) {
-    case TQ_F32: return launch_dense_dq<D, float>(a, st);
-    case TQ_BF16: return launch_dense_dq<D, uint16_t>(a, st);
-    default: return launch_dense_dq<D, f16>(a, st);
-  }
+  const int r = a.Hq / a.Hkv;
+  if (r <= 1) return launch_dense_dr<D, 1>(a, st);
+  if (r <= 2) return launch_dense_dr<D, 2>(a, st);
+  if (r <= 4) return launch_dense_dr<D, 4>(a, st);
+  return launch_dense_dr<D, 8>(a, st);
 }
 
 }  // namespace

@@ -1,148 +1,297 @@
 // Dequantize reference: dense K and V from the packed pool, the first half of the
 // dequantize-then-attend baseline [Open-TQ-Metal, arXiv abstract].
-// 16 lanes per (sequence, kv head, token) vector, E = D/16 coordinates per lane; values
-// (u - 8)*s (4-bit), (u - 4)*s or (u - 2)*s (3- and 2-bit values) or LUT_u*n are exact in
-// fp32. The original-basis variant applies the fp32
-// inverse rotation diag(sigma)*rho*H with the forward rotation's stage order.
-// fp16 keys are copied as stored (they have no rotated form). Compiled with
-// -ffp-contract=off.
+// One wavefront per (sequence, kv head, page): it loads the page's block with one set of
+// coalesced vector loads, in the block's own lane order, and writes 16 rows of K and V.
+// K (4-bit codes): lane l = 16j + t holds token t, dims 32g + 8j + e (e = 0..7, g < D/32).
+// fp16 keys: the same lanes and dims, copied as stored (they have no rotated form).
+// V: lane l = 16j + m holds tokens 4j + e (e = 0..3), dims 32g + 2m + {0, 1}; packed 3- and
+// 2-bit values are first rebuilt into that 4-bit layout.
+// Values (u - 8)*s (4-bit), (u - 4)*s or (u - 2)*s (3- and 2-bit values) or LUT_u*n are
+// exact in fp32. The original-basis variant applies the fp32 inverse rotation
+// diag(sigma)*rho*H with the forward rotation's stage order: butterflies of stride 1, 2,
+// ..., D/2 (each an in-lane pair or a lane-xor pair, as the dims fall), then x rho, then the
+// signs. Compiled with -ffp-contract=off.
 #include "tq_device.h"
 #include "tq_internal.h"
 
 namespace {
 
-template <int D, typename TOut>
-__global__ __launch_bounds__(256) void dequant_kernel(LaunchDequant a) {
-  constexpr int E = D / 16, G = D / 32;
-  const bool kf16 = a.k_codec == TQ_CODEC_FP16;
-  const int BB = tq_block_bytes(D, a.k_codec, a.v_codec);
-  const int VB = tq_value_bits(a.v_codec);
-  const int QM = VB == 4 ? 7 : (VB == 3 ? 3 : 1);  // largest abs-max level of the values
-  const int vbase = kf16 ? 32 * D : 8 * D;
-  const int lane = threadIdx.x & 15;
-  const int64_t vec = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int64_t per_b = (int64_t)a.Hkv * a.max_ctx;
-  if (vec >= (int64_t)a.B * per_b * 2) return;
-  const int is_v = (int)(vec & 1);
-  const int64_t row = vec >> 1;  // (b * Hkv + h) * max_ctx + t
-  const int b = (int)(row / per_b);
-  const int h = (int)((row / a.max_ctx) % a.Hkv);
-  const int t = (int)(row % a.max_ctx);
-  float y[E];
-  if (t >= a.context_lens[b]) {
+// one butterfly stage across lanes: the lane whose dim has the stride bit clear keeps
+// own + partner, the other partner - own
+__device__ __forceinline__ float bfly_xor(float y, int lane, int m) {
+  const float o = __shfl_xor(y, m, 64);
+  return (lane & m) ? (o - y) : (y + o);
+}
+
+template <typename TOut>
+__device__ __forceinline__ void store8(TOut* p, const float* y) {
+  if constexpr (sizeof(TOut) == 2) {
+    f16x8 h;
 #pragma unroll
-    for (int e = 0; e < E; e++) y[e] = 0.0f;
+    for (int e = 0; e < 8; e++) h[e] = (f16)y[e];
+    *reinterpret_cast<f16x8*>(p) = h;
   } else {
-    const int64_t page = a.block_table[(int64_t)b * a.max_pages + (t >> 4)];
-    const uint8_t* blk = a.pool + (page * a.Hkv + h) * BB;
-    const int tt = t & 15;
-    uint32_t u[E];
-    if (!is_v && kf16) {  // fp16 key, dims lane*E + e: byte 1024g + 16(16j + t) + 2(d % 8)
+    *reinterpret_cast<f32x4*>(p) = f32x4{y[0], y[1], y[2], y[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{y[4], y[5], y[6], y[7]};
+  }
+}
+
+template <typename TOut>
+__device__ __forceinline__ void store2(TOut* p, float a, float b) {
+  if constexpr (sizeof(TOut) == 2) {
+    *reinterpret_cast<f16x2*>(p) = f16x2{(f16)a, (f16)b};
+  } else {
+    *reinterpret_cast<float2*>(p) = float2{a, b};
+  }
+}
+
+template <int D, typename TOut>
+__global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
+  constexpr int G = D / 32;
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) {
+    const uint16_t lb[16] = TQ_LUT16_BITS;
+    uint16_t v = lb[0];
 #pragma unroll
-      for (int e = 0; e < E; e++) {
-        const int d = lane * E + e;
-        y[e] = (float)*reinterpret_cast<const f16*>(blk + 1024 * (d >> 5) + 16 * (16 * ((d >> 3) & 3) + tt) + 2 * (d & 7));
+    for (int i = 1; i < 16; i++) v = threadIdx.x == i ? lb[i] : v;
+    lut[threadIdx.x] = (float)__builtin_bit_cast(f16, v);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int t0 = p * 16;
+  if (t0 >= a.max_ctx) return;
+  const int L = a.context_lens[b];
+  const int nt = min(16, a.max_ctx - t0);  // rows of this page inside the output
+  TOut* kout = static_cast<TOut*>(a.k_out) + (((int64_t)b * a.Hkv + h) * a.max_ctx + t0) * D;
+  TOut* vout = static_cast<TOut*>(a.v_out) + (((int64_t)b * a.Hkv + h) * a.max_ctx + t0) * D;
+  if (t0 >= L) {  // the whole page lies past the context: zero rows
+    const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = lane * 8; i < nt * D; i += 512) {
+      store8(kout + i, z);
+      store8(vout + i, z);
+    }
+    return;
+  }
+  const bool kf16 = a.k_codec == TQ_CODEC_FP16;
+  const bool lutk = a.k_codec == TQ_CODEC_LLOYDMAX;
+  const int VB = tq_value_bits(a.v_codec);
+  const int BB = tq_block_bytes(D, a.k_codec, a.v_codec);
+  const int vbase = kf16 ? 32 * D : 8 * D;
+  const int ksb = 8 * D + 2 * VB * D;                    // K scales (4-bit keys)
+  const int vsb = kf16 ? 32 * D + 2 * VB * D : ksb + D;  // V scales
+  const int64_t page = a.block_table[(int64_t)b * a.max_pages + p];
+  const uint8_t* blk = a.pool + (page * a.Hkv + h) * BB;
+  const bool rot = a.original_basis != 0;
+  const float rho = tq_rho(D);
+
+  // ---- keys: lane l = 16j + t, token t, dims 32g + 8j + e
+  {
+    const int j = lane >> 4, t = lane & 15;
+    float y[G][8];
+    if (kf16) {
+#pragma unroll
+      for (int g = 0; g < G; g++) {
+        const f16x8 w = *reinterpret_cast<const f16x8*>(blk + 1024 * g + 16 * lane);
+#pragma unroll
+        for (int e = 0; e < 8; e++) y[g][e] = (float)w[e];
       }
-    } else if (!is_v) {
-      if constexpr (E >= 8) {
-#pragma unroll
-        for (int c = 0; c < E / 8; c++) {
-          const int q = lane * (E / 8) + c;
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(blk + (16 * (q & 3) + tt) * 4 * G + 4 * (q >> 2));
-#pragma unroll
-          for (int e = 0; e < 8; e++) u[8 * c + e] = (w >> (4 * e)) & 15u;
-        }
+    } else {
+      uint32_t w[G];
+      f16 s[G];
+      if constexpr (G == 2) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(blk + 8 * lane);
+        w[0] = x[0]; w[1] = x[1];
+        const f16x2 sv = *reinterpret_cast<const f16x2*>(blk + ksb + 4 * t);
+        s[0] = sv[0]; s[1] = sv[1];
       } else {
-        const int q = lane >> 1;
-        const uint32_t w = *reinterpret_cast<const uint16_t*>(blk + (16 * (q & 3) + tt) * 4 * G + 4 * (q >> 2) + 2 * (lane & 1));
 #pragma unroll
-        for (int e = 0; e < 4; e++) u[e] = (w >> (4 * e)) & 15u;
-      }
-    } else if (VB == 4) {
+        for (int c = 0; c < G / 4; c++) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(blk + 4 * G * lane + 16 * c);
+          const f16x4 sv = *reinterpret_cast<const f16x4*>(blk + ksb + 2 * G * t + 8 * c);
 #pragma unroll
-      for (int k = 0; k < E / 2; k++) {
-        const int c = lane * (E / 2) + k;
-        const uint32_t byte = blk[vbase + (16 * (tt >> 2) + (c & 15)) * 4 * G + 4 * (c >> 4) + (tt & 3)];
-        u[2 * k] = byte & 15u;
-        u[2 * k + 1] = byte >> 4;
-      }
-    } else {
-      // packed b-bit values: dim pair c = 16g + m of token tt = 4j + e is row l = 16j + m,
-      // dword g of the 4-bit layout; its low bits are in byte e of X dword l*G/2 + g/2
-      // (nibble bits 2*(g%2)), its third bits (b = 3) in byte e of Z dword (l*G + g)/4
-      // (nibble bit (l*G + g)%4)
-      constexpr int XD = G >= 2 ? G / 2 : 1;
-#pragma unroll
-      for (int k = 0; k < E / 2; k++) {
-        const int c = lane * (E / 2) + k, gg = c >> 4;
-        const int l = 16 * (tt >> 2) + (c & 15), e = tt & 3;
-        const uint32_t xb = blk[vbase + 4 * (l * XD + (gg >> 1)) + e] >> (2 * (gg & 1));
-        uint32_t lo = xb & 3u, hi = (xb >> 4) & 3u;
-        if (VB == 3) {
-          const int z = l * G + gg;
-          const uint32_t zb = blk[vbase + 128 * G + 4 * (z >> 2) + e] >> (z & 3);
-          lo |= (zb & 1u) << 2;
-          hi |= ((zb >> 4) & 1u) << 2;
+          for (int k = 0; k < 4; k++) { w[4 * c + k] = x[k]; s[4 * c + k] = sv[k]; }
         }
-        u[2 * k] = lo;
-        u[2 * k + 1] = hi;
       }
-    }
-    const int g = (lane * E) / 32;
-    const int sbase = (kf16 ? 32 * D : 8 * D) + 2 * VB * D + ((is_v && !kf16) ? D : 0);
-    const float sc = (float)*reinterpret_cast<const f16*>(blk + sbase + 2 * (tt * G + g));
-    if (!is_v && kf16) {
-      // y holds the key already
-    } else if (!is_v && a.k_codec == TQ_CODEC_LLOYDMAX) {
-      const uint16_t lb[16] = TQ_LUT16_BITS;
 #pragma unroll
-      for (int e = 0; e < E; e++) y[e] = (float)__builtin_bit_cast(f16, lb[u[e]]) * sc;
-    } else {
-      const int off = is_v ? QM + 1 : 8;
+      for (int g = 0; g < G; g++) {
+        const float sc = (float)s[g];
 #pragma unroll
-      for (int e = 0; e < E; e++) y[e] = (float)((int)u[e] - off) * sc;
-    }
-    if (a.original_basis && (is_v || !kf16)) {
+        for (int e = 0; e < 8; e++) {
+          const uint32_t u = (w[g] >> (4 * e)) & 15u;
+          y[g][e] = lutk ? lut[u] * sc : (float)((int)u - 8) * sc;
+        }
+      }
+      if (rot) {
 #pragma unroll
-      for (int s = 1; s < E; s <<= 1)
+        for (int st = 1; st < 8; st <<= 1)
 #pragma unroll
-        for (int e = 0; e < E; e++)
-          if (!(e & s)) {
-            const float x0 = y[e], x1 = y[e + s];
-            y[e] = x0 + x1;
-            y[e + s] = x0 - x1;
+          for (int g = 0; g < G; g++)
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+              if (!(e & st)) {
+                const float x0 = y[g][e], x1 = y[g][e + st];
+                y[g][e] = x0 + x1;
+                y[g][e + st] = x0 - x1;
+              }
+#pragma unroll
+        for (int m = 16; m <= 32; m <<= 1)
+#pragma unroll
+          for (int g = 0; g < G; g++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) y[g][e] = bfly_xor(y[g][e], lane, m);
+#pragma unroll
+        for (int st = 1; st < G; st <<= 1)
+#pragma unroll
+          for (int g = 0; g < G; g++)
+            if (!(g & st))
+#pragma unroll
+              for (int e = 0; e < 8; e++) {
+                const float x0 = y[g][e], x1 = y[g + st][e];
+                y[g][e] = x0 + x1;
+                y[g + st][e] = x0 - x1;
+              }
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+          const uint32_t sw = a.sign_bits[g] >> (8 * j);
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float x = y[g][e] * rho;
+            y[g][e] = ((sw >> e) & 1u) ? -x : x;
           }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int e = 0; e < E; e++) {
-          const float o = __shfl_xor(y[e], m, 16);
-          y[e] = upper ? (o - y[e]) : (y[e] + o);
         }
       }
-      const float rho = tq_rho(D);
-      const uint32_t sw = a.sign_bits[(lane * E) >> 5] >> ((lane * E) & 31);
+    }
+    if (t < nt) {
+      const bool live = t0 + t < L;
 #pragma unroll
-      for (int e = 0; e < E; e++) {
-        const float x = y[e] * rho;
-        y[e] = ((sw >> e) & 1u) ? -x : x;
+      for (int g = 0; g < G; g++) {
+        if (!live)
+#pragma unroll
+          for (int e = 0; e < 8; e++) y[g][e] = 0.0f;
+        store8(kout + t * D + 32 * g + 8 * j, y[g]);
       }
     }
   }
-  TOut* out = static_cast<TOut*>(is_v ? a.v_out : a.k_out) + row * D + lane * E;
+
+  // ---- values: lane l = 16j + m, tokens 4j + e, dims 32g + 2m + {0, 1}
+  {
+    const int j = lane >> 4, m = lane & 15;
+    const int QM = VB == 4 ? 7 : (VB == 3 ? 3 : 1);  // largest abs-max level
+    uint32_t nw[G];                                    // the lane's nibble dwords
+    if (VB == 4) {
+      if constexpr (G == 2) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(blk + vbase + 8 * lane);
+        nw[0] = x[0]; nw[1] = x[1];
+      } else {
 #pragma unroll
-  for (int e = 0; e < E; e++) out[e] = (TOut)y[e];
+        for (int c = 0; c < G / 4; c++) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(blk + vbase + 4 * G * lane + 16 * c);
+#pragma unroll
+          for (int k = 0; k < 4; k++) nw[4 * c + k] = x[k];
+        }
+      }
+    } else {
+      // X dword i of row l holds the low two bits of nibble dwords 2i (bits 0-1 of every
+      // nibble) and 2i + 1 (bits 2-3); Z dword (l*G + g)/4 holds the third bit of nibble
+      // dword g at bit (l*G + g) % 4 of every nibble
+      constexpr int XD = G / 2;
+      uint32_t xw[XD];
+#pragma unroll
+      for (int i = 0; i < XD; i++) xw[i] = *reinterpret_cast<const uint32_t*>(blk + vbase + 4 * (lane * XD + i));
+#pragma unroll
+      for (int g = 0; g < G; g++) nw[g] = (xw[g >> 1] >> (2 * (g & 1))) & 0x33333333u;
+      if (VB == 3) {
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+          const int z = lane * G + g;
+          const uint32_t zw = *reinterpret_cast<const uint32_t*>(blk + vbase + 128 * G + 4 * (z >> 2));
+          nw[g] |= ((zw >> (z & 3)) & 0x11111111u) << 2;
+        }
+      }
+    }
+    // scales of tokens 4j .. 4j + 3, every group: 4G contiguous fp16
+    f16 s[4][G];
+#pragma unroll
+    for (int c = 0; c < G; c++) {
+      const f16x4 sv = *reinterpret_cast<const f16x4*>(blk + vsb + 2 * (4 * j * G) + 8 * c);
+#pragma unroll
+      for (int k = 0; k < 4; k++) s[(4 * c + k) / G][(4 * c + k) % G] = sv[k];
+    }
+    float y[4][G][2];
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+#pragma unroll
+      for (int g = 0; g < G; g++) {
+        const uint32_t byte = (nw[g] >> (8 * e)) & 0xFFu;
+        const float sc = (float)s[e][g];
+        y[e][g][0] = (float)((int)(byte & 15u) - (QM + 1)) * sc;
+        y[e][g][1] = (float)((int)(byte >> 4) - (QM + 1)) * sc;
+      }
+    if (rot) {
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+          const float x0 = y[e][g][0], x1 = y[e][g][1];
+          y[e][g][0] = x0 + x1;
+          y[e][g][1] = x0 - x1;
+        }
+#pragma unroll
+      for (int mm = 1; mm <= 8; mm <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+#pragma unroll
+          for (int g = 0; g < G; g++)
+#pragma unroll
+            for (int q = 0; q < 2; q++) y[e][g][q] = bfly_xor(y[e][g][q], lane, mm);
+#pragma unroll
+      for (int st = 1; st < G; st <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+#pragma unroll
+          for (int g = 0; g < G; g++)
+            if (!(g & st))
+#pragma unroll
+              for (int q = 0; q < 2; q++) {
+                const float x0 = y[e][g][q], x1 = y[e][g + st][q];
+                y[e][g][q] = x0 + x1;
+                y[e][g + st][q] = x0 - x1;
+              }
+#pragma unroll
+      for (int g = 0; g < G; g++) {
+        const uint32_t sw = a.sign_bits[g] >> (2 * m);
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+#pragma unroll
+          for (int q = 0; q < 2; q++) {
+            const float x = y[e][g][q] * rho;
+            y[e][g][q] = ((sw >> q) & 1u) ? -x : x;
+          }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int t = 4 * j + e;
+      if (t < nt) {
+        const bool live = t0 + t < L;
+#pragma unroll
+        for (int g = 0; g < G; g++)
+          store2(vout + t * D + 32 * g + 2 * m, live ? y[e][g][0] : 0.0f, live ? y[e][g][1] : 0.0f);
+      }
+    }
+  }
 }
 
 template <int D>
 hipError_t launch_d(const LaunchDequant& a, hipStream_t st) {
-  const int64_t nvec = (int64_t)a.B * a.Hkv * a.max_ctx * 2;
-  dim3 grid((unsigned)((nvec + 15) / 16));
+  const int pages = (a.max_ctx + 15) / 16;
+  dim3 grid((unsigned)((pages + 3) / 4), (unsigned)a.Hkv, (unsigned)a.B);
   if (a.out_dtype == TQ_F32)
-    hipLaunchKernelGGL((dequant_kernel<D, float>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dequant_page_kernel<D, float>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((dequant_kernel<D, f16>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dequant_page_kernel<D, f16>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -100,12 +100,13 @@ Split choose_split(int B, int Hkv, int D, int k_codec, int v_codec, int max_ctx,
   return make_split(pages, (int)want);
 }
 
-// The dense baseline uses 4-wave workgroups, about three per compute unit.
+// The dense baseline uses 4-wave workgroups, two per compute unit (its 8-head kernel at
+// head_dim 128 takes 166 registers a lane: two waves per SIMD).
 Split choose_split_dense(int B, int Hkv, int max_ctx, int requested) {
   const int pages = (max_ctx + 15) / 16;
   if (requested > 0) return make_split(pages, requested);
   const int64_t units = (int64_t)B * Hkv;
-  int64_t want = (3LL * num_cus() + units - 1) / units;
+  int64_t want = (2LL * num_cus() + units - 1) / units;
   const int64_t cap = (pages + TQ_DECODE_WAVES - 1) / TQ_DECODE_WAVES;
   if (want > cap) want = cap;
   return make_split(pages, (int)want);

@@ -362,51 +362,72 @@ def test_negative_slots_and_untouched_bytes():
     assert c.pool_equal()
 
 
-@pytest.mark.parametrize("k_codec,v_codec", [(0, 0), (1, 0), (2, 0), (0, V3), (2, V3), (1, V2)])
+DEQUANT_CASES = [(128, k, v) for k, v in [(0, 0), (1, 0), (2, 0), (0, V3), (2, V3), (1, V2)]] + \
+    [(64, 0, 0), (64, 1, V3), (64, 2, V2), (256, 0, 0), (256, 1, V2), (256, 2, V3), (256, 0, V3)]
+
+
+@pytest.mark.parametrize("D,k_codec,v_codec", DEQUANT_CASES)
 @pytest.mark.parametrize("basis", [0, 1])
-def test_dequant_reference(k_codec, v_codec, basis):
-    lens = [37, 0, 64]
-    w = W.Workload("dq", 3, 8, 2, 128, 64, "bf16", 0.1, k_codec=k_codec, v_codec=v_codec)
+def test_dequant_reference(D, k_codec, v_codec, basis):
+    lens = [37, 0, 50]
+    w = W.Workload("dq", 3, 8, 2, D, 50, "bf16", 0.1, k_codec=k_codec, v_codec=v_codec)
     c = Case(w, seed=13, lens=lens)
     c.fill()
-    Lmax = 64
+    Lmax = 60  # rows past each context (zeros), whole pages of them, a partial last page
     for dt in (torch.float32, torch.float16):
-        ko = torch.full((3, 2, Lmax, 128), 7.0, dtype=dt, device=DEV)
+        ko = torch.full((3, 2, Lmax, D), 7.0, dtype=dt, device=DEV)
         vo = torch.full_like(ko, 7.0)
         tq.tq_dequant_ref(c.layout, c.pool, c.bt_dev, c.lens_dev, Lmax, ko, vo, to_original_basis=basis)
         torch.cuda.synchronize()
-        rk, rv = c_oracle.dequant(c.opool, 128, 2, c.sb, c.bt, c.lens, Lmax, basis, k_codec, v_codec)
+        rk, rv = c_oracle.dequant(c.opool, D, 2, c.sb, c.bt, c.lens, Lmax, basis, k_codec, v_codec)
         if dt == torch.float16:
             rk, rv = rk.astype(np.float16), rv.astype(np.float16)
         assert np.array_equal(ko.cpu().numpy(), rk)
         assert np.array_equal(vo.cpu().numpy(), rv)
 
 
-def test_dense_fp16_baseline():
-    w = W.WORKLOADS["gemma_d256_32k"].scaled(context=500, batch=2)
-    c = Case(w, seed=17, lens=[500, 333])
+DENSE_CASES = [
+    # (head_dim, q heads, kv heads, lengths, splits, q dtype, key codec)
+    (256, 16, 8, [500, 333], 0, None, 0),      # the D = 256 workload's shape, r = 2
+    (128, 16, 2, [1000, 15, 16, 17], 3, None, 0),  # r = 8 (the 128K shape), edge lengths
+    (128, 4, 4, [257, 0, 1], 0, "f32", 1),      # r = 1, an empty and a one-token sequence
+    (64, 8, 1, [300, 33], 2, "f16", 0),         # r = 8 at D = 64
+    (256, 8, 1, [100, 31], 0, None, 2),         # r = 8 at D = 256, fp16 keys
+    (128, 12, 4, [129, 64], 5, None, 0),        # r = 3 (padded to 4 columns)
+]
+
+
+@pytest.mark.parametrize("D,hq,hkv,lens,splits,q_dtype,k_codec", DENSE_CASES)
+def test_dense_fp16_baseline(D, hq, hkv, lens, splits, q_dtype, k_codec):
+    w = W.Workload("dense", len(lens), hq, hkv, D, max(lens), "bf16", 1.0 if D == 256 else D ** -0.5,
+                   k_codec=k_codec)
+    c = Case(w, seed=17 + D + hq, lens=lens, q_dtype=q_dtype)
     c.fill()
-    Lmax = 500
-    ko = torch.zeros((2, w.kv_heads, Lmax, w.head_dim), dtype=torch.float16, device=DEV)
+    Lmax = max(lens)
+    B = len(lens)
+    ko = torch.zeros((B, hkv, Lmax, D), dtype=torch.float16, device=DEV)
     vo = torch.zeros_like(ko)
     tq.tq_dequant_ref(c.layout, c.pool, c.bt_dev, c.lens_dev, Lmax, ko, vo, to_original_basis=1)
-    ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, 2, Lmax, 0) // 4, dtype=torch.float32, device=DEV)
-    out = torch.zeros((2, w.q_heads, w.head_dim), dtype=torch.float32, device=DEV)
-    tq.tq_dense_decode_attn(c.layout, ko, vo, c.q_dev, c.lens_dev, Lmax, w.attn_scale, out, ws)
+    ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, B, Lmax, splits) // 4, dtype=torch.float32, device=DEV)
+    out = torch.full((B, hq, D), 7.0, dtype=torch.float32, device=DEV)
+    tq.tq_dense_decode_attn(c.layout, ko, vo, c.q_dev, c.lens_dev, Lmax, w.attn_scale, out, ws,
+                            num_splits=splits)
     torch.cuda.synchronize()
     # the reference is the oracle's: its own dequantization (original basis), rounded to
     # fp16 as the baseline stores it, then its fp64 attention
-    Ko, Vo = c_oracle.dequant(c.opool, w.head_dim, w.kv_heads, c.sb, c.bt, c.lens, Lmax, 1,
+    Ko, Vo = c_oracle.dequant(c.opool, D, hkv, c.sb, c.bt, c.lens, Lmax, 1,
                               k_codec=w.k_codec, v_codec=w.v_codec)
     assert np.array_equal(ko.cpu().numpy(), Ko.astype(np.float16))
     K16 = Ko.astype(np.float16).astype(np.float64)
     V16 = Vo.astype(np.float16).astype(np.float64)
-    ref = np.zeros((2, w.q_heads, w.head_dim))
-    for b in range(2):
+    ref = np.zeros((B, hq, D))
+    for b in range(B):
         L = int(c.lens[b])
-        for hq in range(w.q_heads):
-            h = hq // w.gqa
-            ref[b, hq] = c_oracle.attention_f64(c.q32[b, hq], K16[b, h, :L], V16[b, h, :L], w.attn_scale)
+        if L == 0:
+            continue
+        for h in range(hq):
+            ref[b, h] = c_oracle.attention_f64(c.q32[b, h], K16[b, h // w.gqa, :L], V16[b, h // w.gqa, :L],
+                                               w.attn_scale)
     got = out.cpu().numpy()
     assert attn_err(got, ref).max() <= ATTN_TOL
     # how far the baseline's fp16-rounded keys put it from the compressed-domain result
