@@ -575,6 +575,13 @@ def main():
         moved = rec["algorithmic_bytes"] + 2 * b["dense_kv_bytes"]
         b["floor_us_at_measured_read_peak"] = round(moved / (peak_meas * 1e9) * 1e6, 2)
         b["speedup_of_fused_vs_floor"] = round(b["floor_us_at_measured_read_peak"] / dec_mean, 2)
+        # the baseline's own roofline: dequant reads the packed pool and writes dense fp16 K and
+        # V; the attend reads them back
+        dq_bytes = rec["algorithmic_bytes"] + b["dense_kv_bytes"]
+        b["dequant_GBps"] = round(dq_bytes / (b["dequant_us"] * 1e-6) / 1e9, 1)
+        b["dequant_frac"] = round(b["dequant_GBps"] / HBM_PEAK_GBS, 4)
+        b["attend_frac"] = round(b["attend_GBps"] / HBM_PEAK_GBS, 4)
+        b["frac"] = round(moved / (b["total_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
         rec["cpu_baseline"].update(one_core_baselines(name))

@@ -8,6 +8,9 @@
 
 namespace {
 // Merge of the context splits: m* = max m_s, o = sum_s 2^(m_s - m*) o_s / sum_s 2^(m_s - m*) l_s.
+// One wave per (sequence, q head): the lanes take the splits' (m, l) 64 at a time, so the
+// loads of a round are in flight together, and the partial rows are summed with 8 loads in
+// flight per lane.
 template <int D>
 __global__ __launch_bounds__(64) void merge_splits(LaunchDecode a) {
   constexpr int PL = D / 64;
@@ -17,17 +20,43 @@ __global__ __launch_bounds__(64) void merge_splits(LaunchDecode a) {
   const int ns = (npages + a.pages_per_split - 1) / a.pages_per_split;
   const int64_t row0 = ((int64_t)b * a.Hq + hq) * a.splits;
   float M = -INFINITY;
-  for (int s = 0; s < ns; s++) M = fmaxf(M, a.part_ml[2 * (row0 + s)]);
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, a.part_ml[2 * (row0 + s)]);
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
   float lsum = 0.0f, v[PL];
 #pragma unroll
   for (int k = 0; k < PL; k++) v[k] = 0.0f;
-  for (int s = 0; s < ns; s++) {
-    const float m = a.part_ml[2 * (row0 + s)];
-    if (m == -INFINITY) continue;
-    const float f = exp2f(m - M);
-    lsum += f * a.part_ml[2 * (row0 + s) + 1];
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    float f = 0.0f, lw = 0.0f;
+    if (s0 + lane < ns) {
+      const float m = a.part_ml[2 * (row0 + s0 + lane)];
+      f = m == -INFINITY ? 0.0f : exp2f(m - M);
+      lw = f * a.part_ml[2 * (row0 + s0 + lane) + 1];
+    }
 #pragma unroll
-    for (int k = 0; k < PL; k++) v[k] += f * a.part_o[(row0 + s) * D + lane + 64 * k];
+    for (int x = 32; x >= 1; x >>= 1) lw += __shfl_xor(lw, x, 64);
+    lsum += lw;
+    const int cnt = min(64, ns - s0);
+    const float* po = a.part_o + (row0 + s0) * D + lane;
+    int i = 0;
+    for (; i + 8 <= cnt; i += 8) {  // eight partial rows loaded before any is used
+      float x[8][PL];
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+#pragma unroll
+        for (int k = 0; k < PL; k++) x[u][k] = po[(int64_t)(i + u) * D + 64 * k];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const float fi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), i + u));
+#pragma unroll
+        for (int k = 0; k < PL; k++) v[k] += fi * x[u][k];
+      }
+    }
+    for (; i < cnt; i++) {
+      const float fi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), i));
+#pragma unroll
+      for (int k = 0; k < PL; k++) v[k] += fi * po[(int64_t)i * D + 64 * k];
+    }
   }
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
   float* o = a.out + ((int64_t)b * a.Hq + hq) * D;
@@ -68,15 +97,35 @@ __global__ __launch_bounds__(256) void dense_attn(LaunchDecode a) {
   const float qmul = a.attn_scale * TQ_LOG2E;
   float qx[G][8];
   const int64_t qoff = ((int64_t)b * a.Hq + (int64_t)h * r + (hd < r ? hd : 0)) * D + 8 * kq;
-  auto ldq = [&](const auto* qp) {
+  // 8 consecutive elements per group with vector loads, all issued before any is used (the
+  // address is valid for every lane; heads past r are zeroed after the load)
+  const float keep = hd < r ? qmul : 0.0f;
+  if (a.q_dtype == TQ_F32) {
+    const float* qp = static_cast<const float*>(a.q) + qoff;
+    f32x4 raw[G][2];
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+      raw[g][0] = *reinterpret_cast<const f32x4*>(qp + 32 * g);
+      raw[g][1] = *reinterpret_cast<const f32x4*>(qp + 32 * g + 4);
+    }
 #pragma unroll
     for (int g = 0; g < G; g++)
 #pragma unroll
-      for (int e = 0; e < 8; e++) qx[g][e] = hd < r ? widen(qp[qoff + 32 * g + e]) * qmul : 0.0f;
-  };
-  if (a.q_dtype == TQ_F32) ldq(static_cast<const float*>(a.q));
-  else if (a.q_dtype == TQ_BF16) ldq(static_cast<const uint16_t*>(a.q));
-  else ldq(static_cast<const f16*>(a.q));
+      for (int e = 0; e < 8; e++) qx[g][e] = raw[g][e >> 2][e & 3] * keep;
+  } else {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qoff;
+    u32x4 raw[G];
+#pragma unroll
+    for (int g = 0; g < G; g++) raw[g] = *reinterpret_cast<const u32x4*>(qp + 32 * g);
+    const bool bf = a.q_dtype == TQ_BF16;
+#pragma unroll
+    for (int g = 0; g < G; g++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const uint16_t bits = (uint16_t)(raw[g][e >> 1] >> (16 * (e & 1)));
+        qx[g][e] = (bf ? widen(bits) : widen(__builtin_bit_cast(f16, bits))) * keep;
+      }
+  }
   float amax = 0.0f;
 #pragma unroll
   for (int g = 0; g < G; g++)
@@ -116,10 +165,11 @@ __global__ __launch_bounds__(256) void dense_attn(LaunchDecode a) {
       vv[k] = *reinterpret_cast<const f16x8*>(vb + (int64_t)vr * D + 8 * chunk);
     }
   };
-  f16x8 kA[G], vv[G], kN[G], vN[G];
-  if (w < ntile) load_tile(w, kA, vv);
-  for (int tile = w; tile < ntile; tile += 4) {
-    load_tile(min(tile + 4, ntile - 1), kN, vN);  // next tile (the last one again at the end)
+  // NB tiles in registers: the one being computed and NB - 1 in flight (3 at D <= 128, where
+  // the registers allow it; 2 at D = 256)
+  constexpr int NB = D <= 128 ? 3 : 2;
+  f16x8 kbuf[NB][G], vbuf[NB][G];
+  auto step = [&](int tile, const f16x8* kA, const f16x8* vv) {
     const int tt = t0 + 16 * tile;
     f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -172,8 +222,20 @@ __global__ __launch_bounds__(256) void dense_attn(LaunchDecode a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+  };
+  if (w < ntile) {
 #pragma unroll
-    for (int g = 0; g < G; g++) { kA[g] = kN[g]; vv[g] = vN[g]; }
+    for (int i = 0; i < NB; i++) load_tile(min(w + 4 * i, ntile - 1), kbuf[i], vbuf[i]);
+  }
+  for (int tile = w; tile < ntile; tile += 4 * NB) {
+    // the loads are issued whether or not their tile exists (the last tile again), so
+    // every buffer has the same loads outstanding on every path
+#pragma unroll
+    for (int i = 0; i < NB; i++) {
+      const int ti = tile + 4 * i;
+      if (ti < ntile) step(ti, kbuf[i], vbuf[i]);
+      load_tile(min(ti + 4 * NB, ntile - 1), kbuf[i], vbuf[i]);
+    }
   }
   // ---- the wave's totals: o' summed over the lanes of each dim chunk, l over the row groups
 #pragma unroll

@@ -45,7 +45,7 @@ __device__ __forceinline__ void store2(TOut* p, float a, float b) {
   }
 }
 
-template <int D, typename TOut>
+template <int D, typename TOut, int KC, int VB>
 __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
   constexpr int G = D / 32;
   __shared__ float lut[16];
@@ -58,11 +58,22 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int p = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.y, b = blockIdx.z;
   const int t0 = p * 16;
   if (t0 >= a.max_ctx) return;
+  // the length and the page id are loaded together: every page of the output (p < max_ctx/16
+  // rounded up <= max_pages) has a block-table entry, read whether or not it is used
   const int L = a.context_lens[b];
+  int page_id = a.block_table[(int64_t)b * a.max_pages + p];
+  uint32_t sgn[G];  // sign words of the rotation
+#pragma unroll
+  for (int g = 0; g < G; g++) sgn[g] = a.sign_bits[g];
+  // keeps these loads above the branch: one wait for all of them
+  asm volatile("" : "+s"(page_id));
+#pragma unroll
+  for (int g = 0; g < G; g++) asm volatile("" : "+s"(sgn[g]));
+  const int64_t page = page_id;
   const int nt = min(16, a.max_ctx - t0);  // rows of this page inside the output
   TOut* kout = static_cast<TOut*>(a.k_out) + (((int64_t)b * a.Hkv + h) * a.max_ctx + t0) * D;
   TOut* vout = static_cast<TOut*>(a.v_out) + (((int64_t)b * a.Hkv + h) * a.max_ctx + t0) * D;
@@ -74,54 +85,102 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
     }
     return;
   }
-  const bool kf16 = a.k_codec == TQ_CODEC_FP16;
-  const bool lutk = a.k_codec == TQ_CODEC_LLOYDMAX;
-  const int VB = tq_value_bits(a.v_codec);
-  const int BB = tq_block_bytes(D, a.k_codec, a.v_codec);
+  constexpr bool kf16 = KC == TQ_CODEC_FP16;
+  constexpr bool lutk = KC == TQ_CODEC_LLOYDMAX;
+  const int BB = tq_block_bytes(D, KC, a.v_codec);
   const int vbase = kf16 ? 32 * D : 8 * D;
   const int ksb = 8 * D + 2 * VB * D;                    // K scales (4-bit keys)
   const int vsb = kf16 ? 32 * D + 2 * VB * D : ksb + D;  // V scales
-  const int64_t page = a.block_table[(int64_t)b * a.max_pages + p];
   const uint8_t* blk = a.pool + (page * a.Hkv + h) * BB;
   const bool rot = a.original_basis != 0;
   const float rho = tq_rho(D);
+  const int j = lane >> 4, t = lane & 15, m = lane & 15;
 
-  // ---- keys: lane l = 16j + t, token t, dims 32g + 8j + e
+  // ---- every load of the page first (no store may come between them: the compiler cannot
+  // move a load of the pool above a store to the outputs)
+  // keys: lane l = 16j + t, token t, dims 32g + 8j + e
+  u32x4 k16[G];  // fp16 keys: 8 dims per group
+  uint32_t kw[G];
+  f16 ks[G];
+  if constexpr (kf16) {
+#pragma unroll
+    for (int g = 0; g < G; g++) k16[g] = *reinterpret_cast<const u32x4*>(blk + 1024 * g + 16 * lane);
+  } else if constexpr (G == 2) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(blk + 8 * lane);
+    kw[0] = x[0]; kw[1] = x[1];
+    const f16x2 sv = *reinterpret_cast<const f16x2*>(blk + ksb + 4 * t);
+    ks[0] = sv[0]; ks[1] = sv[1];
+  } else {
+#pragma unroll
+    for (int c = 0; c < G / 4; c++) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(blk + 4 * G * lane + 16 * c);
+      const f16x4 sv = *reinterpret_cast<const f16x4*>(blk + ksb + 2 * G * t + 8 * c);
+#pragma unroll
+      for (int k = 0; k < 4; k++) { kw[4 * c + k] = x[k]; ks[4 * c + k] = sv[k]; }
+    }
+  }
+  // values: lane l = 16j + m, tokens 4j + e, dims 32g + 2m + {0, 1}
+  uint32_t nw[G];  // the lane's nibble dwords
+  if constexpr (VB == 4) {
+    if constexpr (G == 2) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(blk + vbase + 8 * lane);
+      nw[0] = x[0]; nw[1] = x[1];
+    } else {
+#pragma unroll
+      for (int c = 0; c < G / 4; c++) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(blk + vbase + 4 * G * lane + 16 * c);
+#pragma unroll
+        for (int k = 0; k < 4; k++) nw[4 * c + k] = x[k];
+      }
+    }
+  } else {
+    // X dword i of row l holds the low two bits of nibble dwords 2i (bits 0-1 of every
+    // nibble) and 2i + 1 (bits 2-3); Z dword (l*G + g)/4 holds the third bit of nibble
+    // dword g at bit (l*G + g) % 4 of every nibble
+    constexpr int XD = G / 2;
+    uint32_t xw[XD], zw[G];
+#pragma unroll
+    for (int i = 0; i < XD; i++) xw[i] = *reinterpret_cast<const uint32_t*>(blk + vbase + 4 * (lane * XD + i));
+    if constexpr (VB == 3) {
+#pragma unroll
+      for (int g = 0; g < G; g++) zw[g] = *reinterpret_cast<const uint32_t*>(blk + vbase + 128 * G + 4 * ((lane * G + g) >> 2));
+    }
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+      nw[g] = (xw[g >> 1] >> (2 * (g & 1))) & 0x33333333u;
+      if constexpr (VB == 3) nw[g] |= ((zw[g] >> ((lane * G + g) & 3)) & 0x11111111u) << 2;
+    }
+  }
+  // scales of tokens 4j .. 4j + 3, every group: 4G contiguous fp16
+  f16 vs[4][G];
+#pragma unroll
+  for (int c = 0; c < G; c++) {
+    const f16x4 sv = *reinterpret_cast<const f16x4*>(blk + vsb + 2 * (4 * j * G) + 8 * c);
+#pragma unroll
+    for (int k = 0; k < 4; k++) vs[(4 * c + k) / G][(4 * c + k) % G] = sv[k];
+  }
+
+  // ---- keys
   {
-    const int j = lane >> 4, t = lane & 15;
     float y[G][8];
-    if (kf16) {
+    if constexpr (kf16) {
 #pragma unroll
       for (int g = 0; g < G; g++) {
-        const f16x8 w = *reinterpret_cast<const f16x8*>(blk + 1024 * g + 16 * lane);
+        const f16x8 w = __builtin_bit_cast(f16x8, k16[g]);
 #pragma unroll
         for (int e = 0; e < 8; e++) y[g][e] = (float)w[e];
       }
     } else {
-      uint32_t w[G];
-      f16 s[G];
-      if constexpr (G == 2) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(blk + 8 * lane);
-        w[0] = x[0]; w[1] = x[1];
-        const f16x2 sv = *reinterpret_cast<const f16x2*>(blk + ksb + 4 * t);
-        s[0] = sv[0]; s[1] = sv[1];
+      if constexpr (lutk) {
+#pragma unroll
+        for (int g = 0; g < G; g++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) y[g][e] = lut[(kw[g] >> (4 * e)) & 15u] * (float)ks[g];
       } else {
 #pragma unroll
-        for (int c = 0; c < G / 4; c++) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(blk + 4 * G * lane + 16 * c);
-          const f16x4 sv = *reinterpret_cast<const f16x4*>(blk + ksb + 2 * G * t + 8 * c);
+        for (int g = 0; g < G; g++)
 #pragma unroll
-          for (int k = 0; k < 4; k++) { w[4 * c + k] = x[k]; s[4 * c + k] = sv[k]; }
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < G; g++) {
-        const float sc = (float)s[g];
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const uint32_t u = (w[g] >> (4 * e)) & 15u;
-          y[g][e] = lutk ? lut[u] * sc : (float)((int)u - 8) * sc;
-        }
+          for (int e = 0; e < 8; e++) y[g][e] = (float)((int)((kw[g] >> (4 * e)) & 15u) - 8) * (float)ks[g];
       }
       if (rot) {
 #pragma unroll
@@ -136,11 +195,11 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
                 y[g][e + st] = x0 - x1;
               }
 #pragma unroll
-        for (int m = 16; m <= 32; m <<= 1)
+        for (int mm = 16; mm <= 32; mm <<= 1)
 #pragma unroll
           for (int g = 0; g < G; g++)
 #pragma unroll
-            for (int e = 0; e < 8; e++) y[g][e] = bfly_xor(y[g][e], lane, m);
+            for (int e = 0; e < 8; e++) y[g][e] = bfly_xor(y[g][e], lane, mm);
 #pragma unroll
         for (int st = 1; st < G; st <<= 1)
 #pragma unroll
@@ -154,7 +213,7 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
               }
 #pragma unroll
         for (int g = 0; g < G; g++) {
-          const uint32_t sw = a.sign_bits[g] >> (8 * j);
+          const uint32_t sw = sgn[g] >> (8 * j);
 #pragma unroll
           for (int e = 0; e < 8; e++) {
             const float x = y[g][e] * rho;
@@ -175,57 +234,16 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
     }
   }
 
-  // ---- values: lane l = 16j + m, tokens 4j + e, dims 32g + 2m + {0, 1}
+  // ---- values
   {
-    const int j = lane >> 4, m = lane & 15;
-    const int QM = VB == 4 ? 7 : (VB == 3 ? 3 : 1);  // largest abs-max level
-    uint32_t nw[G];                                    // the lane's nibble dwords
-    if (VB == 4) {
-      if constexpr (G == 2) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(blk + vbase + 8 * lane);
-        nw[0] = x[0]; nw[1] = x[1];
-      } else {
-#pragma unroll
-        for (int c = 0; c < G / 4; c++) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(blk + vbase + 4 * G * lane + 16 * c);
-#pragma unroll
-          for (int k = 0; k < 4; k++) nw[4 * c + k] = x[k];
-        }
-      }
-    } else {
-      // X dword i of row l holds the low two bits of nibble dwords 2i (bits 0-1 of every
-      // nibble) and 2i + 1 (bits 2-3); Z dword (l*G + g)/4 holds the third bit of nibble
-      // dword g at bit (l*G + g) % 4 of every nibble
-      constexpr int XD = G / 2;
-      uint32_t xw[XD];
-#pragma unroll
-      for (int i = 0; i < XD; i++) xw[i] = *reinterpret_cast<const uint32_t*>(blk + vbase + 4 * (lane * XD + i));
-#pragma unroll
-      for (int g = 0; g < G; g++) nw[g] = (xw[g >> 1] >> (2 * (g & 1))) & 0x33333333u;
-      if (VB == 3) {
-#pragma unroll
-        for (int g = 0; g < G; g++) {
-          const int z = lane * G + g;
-          const uint32_t zw = *reinterpret_cast<const uint32_t*>(blk + vbase + 128 * G + 4 * (z >> 2));
-          nw[g] |= ((zw >> (z & 3)) & 0x11111111u) << 2;
-        }
-      }
-    }
-    // scales of tokens 4j .. 4j + 3, every group: 4G contiguous fp16
-    f16 s[4][G];
-#pragma unroll
-    for (int c = 0; c < G; c++) {
-      const f16x4 sv = *reinterpret_cast<const f16x4*>(blk + vsb + 2 * (4 * j * G) + 8 * c);
-#pragma unroll
-      for (int k = 0; k < 4; k++) s[(4 * c + k) / G][(4 * c + k) % G] = sv[k];
-    }
+    constexpr int QM = VB == 4 ? 7 : (VB == 3 ? 3 : 1);  // largest abs-max level
     float y[4][G][2];
 #pragma unroll
     for (int e = 0; e < 4; e++)
 #pragma unroll
       for (int g = 0; g < G; g++) {
         const uint32_t byte = (nw[g] >> (8 * e)) & 0xFFu;
-        const float sc = (float)s[e][g];
+        const float sc = (float)vs[e][g];
         y[e][g][0] = (float)((int)(byte & 15u) - (QM + 1)) * sc;
         y[e][g][1] = (float)((int)(byte >> 4) - (QM + 1)) * sc;
       }
@@ -261,7 +279,7 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
               }
 #pragma unroll
       for (int g = 0; g < G; g++) {
-        const uint32_t sw = a.sign_bits[g] >> (2 * m);
+        const uint32_t sw = sgn[g] >> (2 * m);
 #pragma unroll
         for (int e = 0; e < 4; e++)
 #pragma unroll
@@ -273,14 +291,33 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
     }
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-      const int t = 4 * j + e;
-      if (t < nt) {
-        const bool live = t0 + t < L;
+      const int tv = 4 * j + e;
+      if (tv < nt) {
+        const bool live = t0 + tv < L;
 #pragma unroll
         for (int g = 0; g < G; g++)
-          store2(vout + t * D + 32 * g + 2 * m, live ? y[e][g][0] : 0.0f, live ? y[e][g][1] : 0.0f);
+          store2(vout + tv * D + 32 * g + 2 * m, live ? y[e][g][0] : 0.0f, live ? y[e][g][1] : 0.0f);
       }
     }
+  }
+}
+
+template <int D, typename TOut, int KC>
+hipError_t launch_k(const LaunchDequant& a, dim3 grid, hipStream_t st) {
+  switch (tq_value_bits(a.v_codec)) {
+    case 4: hipLaunchKernelGGL((dequant_page_kernel<D, TOut, KC, 4>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((dequant_page_kernel<D, TOut, KC, 3>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((dequant_page_kernel<D, TOut, KC, 2>), grid, dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int D, typename TOut>
+hipError_t launch_t(const LaunchDequant& a, dim3 grid, hipStream_t st) {
+  switch (a.k_codec) {
+    case TQ_CODEC_FP16: return launch_k<D, TOut, TQ_CODEC_FP16>(a, grid, st);
+    case TQ_CODEC_LLOYDMAX: return launch_k<D, TOut, TQ_CODEC_LLOYDMAX>(a, grid, st);
+    default: return launch_k<D, TOut, TQ_CODEC_ABSMAX>(a, grid, st);
   }
 }
 
@@ -288,11 +325,7 @@ template <int D>
 hipError_t launch_d(const LaunchDequant& a, hipStream_t st) {
   const int pages = (a.max_ctx + 15) / 16;
   dim3 grid((unsigned)((pages + 3) / 4), (unsigned)a.Hkv, (unsigned)a.B);
-  if (a.out_dtype == TQ_F32)
-    hipLaunchKernelGGL((dequant_page_kernel<D, float>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((dequant_page_kernel<D, f16>), grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+  return a.out_dtype == TQ_F32 ? launch_t<D, float>(a, grid, st) : launch_t<D, f16>(a, grid, st);
 }
 
 }  // namespace
