@@ -11,16 +11,23 @@
 // diag(sigma)*rho*H with the forward rotation's stage order: butterflies of stride 1, 2,
 // ..., D/2 (each an in-lane pair or a lane-xor pair, as the dims fall), then x rho, then the
 // signs. Compiled with -ffp-contract=off.
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 
 namespace {
 
-// one butterfly stage across lanes: the lane whose dim has the stride bit clear keeps
-// own + partner, the other partner - own
-__device__ __forceinline__ float bfly_xor(float y, int lane, int m) {
-  const float o = __shfl_xor(y, m, 64);
-  return (lane & m) ? (o - y) : (y + o);
+// One butterfly stage across lanes (stride bit = lane bit M): the lane whose dim has the
+// bit clear keeps own + partner, the other partner - own. Both are fma(s, own, partner) with
+// s = +1 or -1: s * own is exact, so the fma rounds once, as the addition it stands for.
+// The partner comes by DPP inside a row of 16 lanes, by ds_bpermute across rows.
+template <int M>
+__device__ __forceinline__ float bfly_lane(float y, int lane) {
+  float o;
+  if constexpr (M < 16) o = dpp_xor<M>(y, lane);
+  else o = __shfl_xor(y, M, 64);
+  return __builtin_fmaf((lane & M) ? -1.0f : 1.0f, y, o);
 }
 
 template <typename TOut>
@@ -195,11 +202,13 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
                 y[g][e + st] = x0 - x1;
               }
 #pragma unroll
-        for (int mm = 16; mm <= 32; mm <<= 1)
+        for (int g = 0; g < G; g++)
 #pragma unroll
-          for (int g = 0; g < G; g++)
+          for (int e = 0; e < 8; e++) y[g][e] = bfly_lane<16>(y[g][e], lane);
 #pragma unroll
-            for (int e = 0; e < 8; e++) y[g][e] = bfly_xor(y[g][e], lane, mm);
+        for (int g = 0; g < G; g++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) y[g][e] = bfly_lane<32>(y[g][e], lane);
 #pragma unroll
         for (int st = 1; st < G; st <<= 1)
 #pragma unroll
@@ -256,14 +265,19 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
           y[e][g][0] = x0 + x1;
           y[e][g][1] = x0 - x1;
         }
-#pragma unroll
-      for (int mm = 1; mm <= 8; mm <<= 1)
+      auto vstage = [&](auto mc) {
+        constexpr int M = decltype(mc)::value;
 #pragma unroll
         for (int e = 0; e < 4; e++)
 #pragma unroll
           for (int g = 0; g < G; g++)
 #pragma unroll
-            for (int q = 0; q < 2; q++) y[e][g][q] = bfly_xor(y[e][g][q], lane, mm);
+            for (int q = 0; q < 2; q++) y[e][g][q] = bfly_lane<M>(y[e][g][q], lane);
+      };
+      vstage(std::integral_constant<int, 1>{});
+      vstage(std::integral_constant<int, 2>{});
+      vstage(std::integral_constant<int, 4>{});
+      vstage(std::integral_constant<int, 8>{});
 #pragma unroll
       for (int st = 1; st < G; st <<= 1)
 #pragma unroll
