@@ -158,11 +158,12 @@ __global__ __launch_bounds__(256) void dense_attn(LaunchDecode a) {
     const int tt = t0 + 16 * tile;
     const int kr = min(tt + n, L - 1);
 #pragma unroll
-    for (int g = 0; g < G; g++) kA[g] = *reinterpret_cast<const f16x8*>(kb + (int64_t)kr * D + 32 * g + 8 * kq);
+    for (int g = 0; g < G; g++)
+      kA[g] = __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(kb + (int64_t)kr * D + 32 * g + 8 * kq));
 #pragma unroll
     for (int k = 0; k < G; k++) {
       const int vr = min(tt + (lane + 64 * k) / NC, L - 1);
-      vv[k] = *reinterpret_cast<const f16x8*>(vb + (int64_t)vr * D + 8 * chunk);
+      vv[k] = __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(vb + (int64_t)vr * D + 8 * chunk));
     }
   };
   // NB tiles in registers: the one being computed and NB - 1 in flight (3 at D <= 128, where

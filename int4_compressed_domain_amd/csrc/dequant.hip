@@ -30,25 +30,28 @@ __device__ __forceinline__ float bfly_lane(float y, int lane) {
   return __builtin_fmaf((lane & M) ? -1.0f : 1.0f, y, o);
 }
 
+// The dense outputs are written once and read back by another kernel, so stores are
+// non-temporal (streamed past the caches).
 template <typename TOut>
 __device__ __forceinline__ void store8(TOut* p, const float* y) {
   if constexpr (sizeof(TOut) == 2) {
     f16x8 h;
 #pragma unroll
     for (int e = 0; e < 8; e++) h[e] = (f16)y[e];
-    *reinterpret_cast<f16x8*>(p) = h;
+    __builtin_nontemporal_store(h, reinterpret_cast<f16x8*>(p));
   } else {
-    *reinterpret_cast<f32x4*>(p) = f32x4{y[0], y[1], y[2], y[3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{y[4], y[5], y[6], y[7]};
+    __builtin_nontemporal_store(f32x4{y[0], y[1], y[2], y[3]}, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(f32x4{y[4], y[5], y[6], y[7]}, reinterpret_cast<f32x4*>(p + 4));
   }
 }
 
 template <typename TOut>
 __device__ __forceinline__ void store2(TOut* p, float a, float b) {
   if constexpr (sizeof(TOut) == 2) {
-    *reinterpret_cast<f16x2*>(p) = f16x2{(f16)a, (f16)b};
+    __builtin_nontemporal_store(f16x2{(f16)a, (f16)b}, reinterpret_cast<f16x2*>(p));
   } else {
-    *reinterpret_cast<float2*>(p) = float2{a, b};
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(f32x2{a, b}, reinterpret_cast<f32x2*>(p));
   }
 }
 
