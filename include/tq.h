@@ -318,7 +318,8 @@ int tq_decode_attn_hotcold(const tq_layout* layout, const void* pool, const void
  * to_original_basis = 0: values (u-8)*s or LUT_u*n in the rotated basis (exact products,
  * rounded once to out_dtype); 1: times R^-1 = diag(sigma) * rho * H in fp32 (same stage
  * order as the forward rotation), then rounded to out_dtype. fp16 keys have no rotated
- * form: they are written as stored in both cases.
+ * form: they are written as stored in both cases. TQ_EUNSUPPORTED when batch *
+ * num_kv_heads * ceil(max_context_len / 64) (its workgroups) exceeds 2^31 - 1.
  * [Open-TQ-Metal, arXiv abstract: the dequantize-then-attend baseline] */
 int tq_dequant_ref(const tq_layout* layout, const void* pool, int32_t batch,
                    const int32_t* block_table, int32_t max_pages_per_seq,
@@ -330,6 +331,7 @@ int tq_dequant_ref(const tq_layout* layout, const void* pool, int32_t batch,
  * original basis), q as in tq_decode_attn but used unrotated; fp32 accumulation, same
  * split/merge scheme; out fp32 [batch][num_q_heads][head_dim]. Workspace as for
  * tq_decode_attn. Only head_dim, num_q_heads, num_kv_heads of the layout are used.
+ * TQ_EUNSUPPORTED when splits * num_kv_heads * batch (its workgroups) exceeds 2^31 - 1.
  * [Open-TQ-Metal, arXiv abstract: dequantize-then-attend] */
 int tq_dense_decode_attn(const tq_layout* layout, const void* k, const void* v, const void* q,
                          int32_t q_dtype, int32_t batch, const int32_t* context_lens,

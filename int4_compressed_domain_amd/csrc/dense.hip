@@ -14,7 +14,7 @@ namespace {
 template <int D>
 __global__ __launch_bounds__(64) void merge_splits(LaunchDecode a) {
   constexpr int PL = D / 64;
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int hq = (int)(blockIdx.x % (uint32_t)a.Hq), b = (int)(blockIdx.x / (uint32_t)a.Hq), lane = threadIdx.x;
   const int L = a.context_lens[b];
   const int npages = (L + 15) >> 4;
   const int ns = (npages + a.pages_per_split - 1) / a.pages_per_split;
@@ -76,7 +76,10 @@ __global__ __launch_bounds__(64) void merge_splits(LaunchDecode a) {
 template <int D, int RP>
 __global__ __launch_bounds__(256) void dense_attn(LaunchDecode a) {
   constexpr int G = D / 32, NC = D / 8;
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // one-dimensional grid: workgroup = (split s, kv head h, sequence b)
+  const uint32_t unit = blockIdx.x / (uint32_t)a.splits;
+  const int s = (int)(blockIdx.x % (uint32_t)a.splits);
+  const int h = (int)(unit % (uint32_t)a.Hkv), b = (int)(unit / (uint32_t)a.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = a.Hq / a.Hkv;
   __shared__ __align__(16) float Pt[4][16][8];     // per wave: the tile's weights [token][head]
@@ -283,10 +286,10 @@ __global__ __launch_bounds__(256) void dense_attn(LaunchDecode a) {
 
 template <int D, int RP>
 hipError_t launch_dense_dr(const LaunchDecode& a, hipStream_t st) {
-  hipLaunchKernelGGL((dense_attn<D, RP>), dim3(a.splits, a.Hkv, a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((dense_attn<D, RP>), dim3((unsigned)((int64_t)a.splits * a.Hkv * a.B)), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_splits<D>), dim3(a.Hq, a.B), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((merge_splits<D>), dim3((unsigned)((int64_t)a.Hq * a.B)), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

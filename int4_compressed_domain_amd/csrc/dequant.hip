@@ -68,8 +68,11 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int p = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = blockIdx.y, b = blockIdx.z;
+  // one-dimensional grid: workgroup = (sequence b, kv head h, 4 consecutive pages)
+  const uint32_t p4 = (uint32_t)(((a.max_ctx + 15) / 16 + 3) / 4);
+  const uint32_t unit = blockIdx.x / p4;
+  const int h = (int)(unit % (uint32_t)a.Hkv), b = (int)(unit / (uint32_t)a.Hkv);
+  const int p = (int)(blockIdx.x % p4) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = p * 16;
   if (t0 >= a.max_ctx) return;
   // the length and the page id are loaded together: every page of the output (p < max_ctx/16
@@ -340,8 +343,8 @@ hipError_t launch_t(const LaunchDequant& a, dim3 grid, hipStream_t st) {
 
 template <int D>
 hipError_t launch_d(const LaunchDequant& a, hipStream_t st) {
-  const int pages = (a.max_ctx + 15) / 16;
-  dim3 grid((unsigned)((pages + 3) / 4), (unsigned)a.Hkv, (unsigned)a.B);
+  const int64_t pages = (a.max_ctx + 15) / 16;
+  dim3 grid((unsigned)((int64_t)a.B * a.Hkv * ((pages + 3) / 4)));  // the caller keeps it < 2^31
   return a.out_dtype == TQ_F32 ? launch_t<D, float>(a, grid, st) : launch_t<D, f16>(a, grid, st);
 }
 

@@ -462,6 +462,8 @@ int tq_dequant_ref(const tq_layout* L, const void* pool, int32_t batch, const in
   if (to_original_basis != 0 && to_original_basis != 1) return TQ_EINVAL;
   if ((int64_t)batch * max_context_len == 0) return TQ_OK;
   if (!pool || !block_table || !context_lens || !k_out || !v_out) return TQ_EINVAL;
+  // one workgroup per (sequence, kv head, 4 pages), in a one-dimensional grid
+  if ((int64_t)batch * L->num_kv_heads * (((int64_t)max_context_len + 63) / 64) > INT32_MAX) return TQ_EUNSUPPORTED;
   if (validating()) {
     rc = validate_tables(L, batch, block_table, max_pages_per_seq, context_lens, max_context_len,
                          nullptr, 0, static_cast<hipStream_t>(stream));
@@ -485,6 +487,7 @@ int tq_dense_decode_attn(const tq_layout* L, const void* k, const void* v, const
   if (batch == 0) return TQ_OK;
   if (!k || !v) return TQ_EINVAL;
   Split s = choose_split_dense(batch, L->num_kv_heads, max_context_len, num_splits);
+  if ((int64_t)s.splits * L->num_kv_heads * batch > INT32_MAX) return TQ_EUNSUPPORTED;  // 1-D grid
   if (workspace_bytes_ < workspace_bytes(L, batch, max_context_len, num_splits)) return TQ_ENOSPC;
   if (!workspace) return TQ_EINVAL;
   float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + TQ_DECODE_COUNTER_BYTES);

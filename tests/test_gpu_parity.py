@@ -436,6 +436,34 @@ def test_dense_fp16_baseline(D, hq, hkv, lens, splits, q_dtype, k_codec):
     _say("   dense baseline vs the compressed-domain oracle: max normwise %.3e" % attn_err(got, exact).max())
 
 
+def test_baseline_batch_beyond_65535():
+    """70000 sequences (one kv head, one page each) through the dequant and the dense attend:
+    their workgroups fill a one-dimensional grid past 65535. The pool holds 4 filled
+    sequences; the block table repeats their rows, so every output row has a known answer."""
+    w = W.Workload("bigb", 4, 1, 1, 64, 16, "bf16", 0.125)
+    c = Case(w, seed=3, lens=[16, 16, 16, 16])
+    c.fill()
+    B = 70000
+    rep = np.arange(B) % 4
+    bt = torch.from_numpy(np.ascontiguousarray(c.bt[rep])).to(DEV)
+    lens = torch.full((B,), 16, dtype=torch.int32, device=DEV)
+    ko = torch.zeros((B, 1, 16, 64), dtype=torch.float16, device=DEV)
+    vo = torch.zeros_like(ko)
+    tq.tq_dequant_ref(c.layout, c.pool, bt, lens, 16, ko, vo, to_original_basis=1)
+    Ko, Vo = c_oracle.dequant(c.opool, 64, 1, c.sb, c.bt, c.lens, 16, 1)
+    K16, V16 = Ko.astype(np.float16), Vo.astype(np.float16)
+    assert np.array_equal(ko.cpu().numpy(), K16[rep])
+    assert np.array_equal(vo.cpu().numpy(), V16[rep])
+    q = c.q_dev[torch.from_numpy(rep).to(DEV)].contiguous()
+    ws = torch.zeros(tq.tq_decode_workspace_size(c.layout, B, 16, 0) // 4, dtype=torch.float32, device=DEV)
+    out = torch.full((B, 1, 64), 7.0, dtype=torch.float32, device=DEV)
+    tq.tq_dense_decode_attn(c.layout, ko, vo, q, lens, 16, w.attn_scale, out, ws)
+    torch.cuda.synchronize()
+    ref = np.stack([c_oracle.attention_f64(c.q32[b, 0], K16[b, 0].astype(np.float64),
+                                           V16[b, 0].astype(np.float64), w.attn_scale) for b in range(4)])
+    assert attn_err(out.cpu().numpy()[:, 0], ref[rep]).max() <= ATTN_TOL
+
+
 # ---- full-size workloads, through the call and launch configuration the benchmark times ----
 
 def _full_size_pairs(w):
