@@ -4,8 +4,9 @@
 // coalesced vector loads, in the block's own lane order, and writes 16 rows of K and V.
 // K (4-bit codes): lane l = 16j + t holds token t, dims 32g + 8j + e (e = 0..7, g < D/32).
 // fp16 keys: the same lanes and dims, copied as stored (they have no rotated form).
-// V: lane l = 16j + m holds tokens 4j + e (e = 0..3), dims 32g + 2m + {0, 1}; packed 3- and
-// 2-bit values are first rebuilt into that 4-bit layout.
+// V: lane 16j + i holds row 16j + m of the value region, m = i ^ 3*bit2(i) (so that every
+// cross-lane butterfly partner is one DPP move away): tokens 4j + e (e = 0..3), dims
+// 32g + 2m + {0, 1}; packed 3- and 2-bit values are first rebuilt into that 4-bit layout.
 // Values (u - 8)*s (4-bit), (u - 4)*s or (u - 2)*s (3- and 2-bit values) or LUT_u*n are
 // exact in fp32. The original-basis variant applies the fp32 inverse rotation
 // diag(sigma)*rho*H with the forward rotation's stage order: butterflies of stride 1, 2,
@@ -13,6 +14,7 @@
 // signs. Compiled with -ffp-contract=off.
 #include <type_traits>
 
+#include "tq_codec.h"
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -22,12 +24,16 @@ namespace {
 // bit clear keeps own + partner, the other partner - own. Both are fma(s, own, partner) with
 // s = +1 or -1: s * own is exact, so the fma rounds once, as the addition it stands for.
 // The partner comes by DPP inside a row of 16 lanes, by ds_bpermute across rows.
+// Keys: the stride bit is lane bit M (16 or 32), partner by ds_bpermute.
 template <int M>
 __device__ __forceinline__ float bfly_lane(float y, int lane) {
-  float o;
-  if constexpr (M < 16) o = dpp_xor<M>(y, lane);
-  else o = __shfl_xor(y, M, 64);
-  return __builtin_fmaf((lane & M) ? -1.0f : 1.0f, y, o);
+  return __builtin_fmaf((lane & M) ? -1.0f : 1.0f, y, __shfl_xor(y, M, 64));
+}
+// Values: lane 16j + i holds row 16j + tq_blk16(i), so the partner whose row differs in bit
+// M (1, 2, 4, 8) is one DPP move away (bxor<M>); the stride bit is that bit of the row.
+template <int M>
+__device__ __forceinline__ float bfly_row(float y, int row16) {
+  return __builtin_fmaf((row16 & M) ? -1.0f : 1.0f, y, bxor<M>(y));
 }
 
 // The dense outputs are written once and read back by another kernel, so stores are
@@ -107,7 +113,8 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
   const uint8_t* blk = a.pool + (page * a.Hkv + h) * BB;
   const bool rot = a.original_basis != 0;
   const float rho = tq_rho(D);
-  const int j = lane >> 4, t = lane & 15, m = lane & 15;
+  const int j = lane >> 4, t = lane & 15;
+  const int m = tq_blk16(lane & 15), vrow = 16 * j + m;  // values: the row this lane holds
 
   // ---- every load of the page first (no store may come between them: the compiler cannot
   // move a load of the pool above a store to the outputs)
@@ -132,16 +139,16 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
       for (int k = 0; k < 4; k++) { kw[4 * c + k] = x[k]; ks[4 * c + k] = sv[k]; }
     }
   }
-  // values: lane l = 16j + m, tokens 4j + e, dims 32g + 2m + {0, 1}
+  // values: lane 16j + i holds row 16j + m, m = tq_blk16(i): tokens 4j + e, dims 32g + 2m + {0, 1}
   uint32_t nw[G];  // the lane's nibble dwords
   if constexpr (VB == 4) {
     if constexpr (G == 2) {
-      const u32x2 x = *reinterpret_cast<const u32x2*>(blk + vbase + 8 * lane);
+      const u32x2 x = *reinterpret_cast<const u32x2*>(blk + vbase + 8 * vrow);
       nw[0] = x[0]; nw[1] = x[1];
     } else {
 #pragma unroll
       for (int c = 0; c < G / 4; c++) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(blk + vbase + 4 * G * lane + 16 * c);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(blk + vbase + 4 * G * vrow + 16 * c);
 #pragma unroll
         for (int k = 0; k < 4; k++) nw[4 * c + k] = x[k];
       }
@@ -153,15 +160,15 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
     constexpr int XD = G / 2;
     uint32_t xw[XD], zw[G];
 #pragma unroll
-    for (int i = 0; i < XD; i++) xw[i] = *reinterpret_cast<const uint32_t*>(blk + vbase + 4 * (lane * XD + i));
+    for (int i = 0; i < XD; i++) xw[i] = *reinterpret_cast<const uint32_t*>(blk + vbase + 4 * (vrow * XD + i));
     if constexpr (VB == 3) {
 #pragma unroll
-      for (int g = 0; g < G; g++) zw[g] = *reinterpret_cast<const uint32_t*>(blk + vbase + 128 * G + 4 * ((lane * G + g) >> 2));
+      for (int g = 0; g < G; g++) zw[g] = *reinterpret_cast<const uint32_t*>(blk + vbase + 128 * G + 4 * ((vrow * G + g) >> 2));
     }
 #pragma unroll
     for (int g = 0; g < G; g++) {
       nw[g] = (xw[g >> 1] >> (2 * (g & 1))) & 0x33333333u;
-      if constexpr (VB == 3) nw[g] |= ((zw[g] >> ((lane * G + g) & 3)) & 0x11111111u) << 2;
+      if constexpr (VB == 3) nw[g] |= ((zw[g] >> ((vrow * G + g) & 3)) & 0x11111111u) << 2;
     }
   }
   // scales of tokens 4j .. 4j + 3, every group: 4G contiguous fp16
@@ -190,10 +197,17 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
 #pragma unroll
           for (int e = 0; e < 8; e++) y[g][e] = lut[(kw[g] >> (4 * e)) & 15u] * (float)ks[g];
       } else {
+        // (u - 8) * s = fma(u, s, -8s): u*s and 8s are exact and so is their difference
 #pragma unroll
-        for (int g = 0; g < G; g++)
+        for (int g = 0; g < G; g++) {
+          const float sc = (float)ks[g], off = -8.0f * sc;
+          const uint32_t lo = kw[g] & 0x0F0F0F0Fu, hi = (kw[g] >> 4) & 0x0F0F0F0Fu;  // nibbles 2b, 2b + 1
 #pragma unroll
-          for (int e = 0; e < 8; e++) y[g][e] = (float)((int)((kw[g] >> (4 * e)) & 15u) - 8) * (float)ks[g];
+          for (int bb = 0; bb < 4; bb++) {
+            y[g][2 * bb] = __builtin_fmaf((float)((lo >> (8 * bb)) & 0xFFu), sc, off);
+            y[g][2 * bb + 1] = __builtin_fmaf((float)((hi >> (8 * bb)) & 0xFFu), sc, off);
+          }
+        }
       }
       if (rot) {
 #pragma unroll
@@ -254,14 +268,16 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
     constexpr int QM = VB == 4 ? 7 : (VB == 3 ? 3 : 1);  // largest abs-max level
     float y[4][G][2];
 #pragma unroll
-    for (int e = 0; e < 4; e++)
+    for (int g = 0; g < G; g++) {
+      const uint32_t lo = nw[g] & 0x0F0F0F0Fu, hi = (nw[g] >> 4) & 0x0F0F0F0Fu;  // byte e: token 4j + e
 #pragma unroll
-      for (int g = 0; g < G; g++) {
-        const uint32_t byte = (nw[g] >> (8 * e)) & 0xFFu;
-        const float sc = (float)vs[e][g];
-        y[e][g][0] = (float)((int)(byte & 15u) - (QM + 1)) * sc;
-        y[e][g][1] = (float)((int)(byte >> 4) - (QM + 1)) * sc;
+      for (int e = 0; e < 4; e++) {
+        // (u - (QM + 1)) * s = fma(u, s, -(QM + 1)s), exact as for the keys
+        const float sc = (float)vs[e][g], off = -(float)(QM + 1) * sc;
+        y[e][g][0] = __builtin_fmaf((float)((lo >> (8 * e)) & 0xFFu), sc, off);
+        y[e][g][1] = __builtin_fmaf((float)((hi >> (8 * e)) & 0xFFu), sc, off);
       }
+    }
     if (rot) {
 #pragma unroll
       for (int e = 0; e < 4; e++)
@@ -278,7 +294,7 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(LaunchDequant a) {
 #pragma unroll
           for (int g = 0; g < G; g++)
 #pragma unroll
-            for (int q = 0; q < 2; q++) y[e][g][q] = bfly_lane<M>(y[e][g][q], lane);
+            for (int q = 0; q < 2; q++) y[e][g][q] = bfly_row<M>(y[e][g][q], m);
       };
       vstage(std::integral_constant<int, 1>{});
       vstage(std::integral_constant<int, 2>{});
