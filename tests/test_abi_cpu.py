@@ -235,6 +235,13 @@ def test_dequant_and_dense_validation():
     assert lib.tq_dequant_ref(ctypes.byref(L), FAKE, 1, FAKE, 3, FAKE, 64, 1, tq.F32, FAKE, FAKE, None) == tq.TQ_EINVAL
     assert lib.tq_dense_decode_attn(ctypes.byref(L), FAKE, None, FAKE, tq.BF16, 1, FAKE, 64, 0.1, 0, FAKE, FAKE, 1 << 30, None) == tq.TQ_EINVAL
     assert lib.tq_dense_decode_attn(ctypes.byref(L), FAKE, FAKE, FAKE, tq.BF16, 1, FAKE, 64, 0.1, 0, FAKE, FAKE, 8, None) == tq.TQ_ENOSPC
+    # one-dimensional grids: more than 2^31 - 1 workgroups is refused before any launch
+    # (dequant: 65536 sequences x 8 kv heads x 2^20 tokens / 64 tokens per workgroup = 2^33)
+    assert lib.tq_dequant_ref(ctypes.byref(L), FAKE, 1 << 16, FAKE, 1 << 16, FAKE, 1 << 20, 1, tq.F16,
+                              FAKE, FAKE, None) == tq.TQ_EUNSUPPORTED
+    # (dense attend: 2^17 requested splits x 8 kv heads x 4096 sequences = 2^32)
+    assert lib.tq_dense_decode_attn(ctypes.byref(L), FAKE, FAKE, FAKE, tq.BF16, 4096, FAKE, 1 << 21, 0.1,
+                                    1 << 17, FAKE, FAKE, 1 << 62, None) == tq.TQ_EUNSUPPORTED
 
 
 def test_lut_constant_matches_product_generator():
