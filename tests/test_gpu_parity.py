@@ -394,6 +394,8 @@ DENSE_CASES = [
     (64, 8, 1, [300, 33], 2, "f16", 0),         # r = 8 at D = 64
     (256, 8, 1, [100, 31], 0, None, 2),         # r = 8 at D = 256, fp16 keys
     (128, 12, 4, [129, 64], 5, None, 0),        # r = 3 (padded to 4 columns)
+    (64, 12, 2, [1000, 77], 0, "f32", 1),       # r = 6 (padded to 8 columns)
+    (128, 8, 1, [2000, 1500, 0], 100, None, 0),  # 100 splits: the merge takes them in rounds of 64
 ]
 
 
