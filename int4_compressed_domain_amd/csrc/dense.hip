@@ -9,8 +9,8 @@
 namespace {
 // Merge of the context splits: m* = max m_s, o = sum_s 2^(m_s - m*) o_s / sum_s 2^(m_s - m*) l_s.
 // One wave per (sequence, q head): the lanes take the splits' (m, l) 64 at a time, so the
-// loads of a round are in flight together, and the partial rows are summed with 8 loads in
-// flight per lane.
+// loads of a round are in flight together, and the partial rows are summed eight rows at a
+// time, all of their loads issued before the first is used.
 template <int D>
 __global__ __launch_bounds__(64) void merge_splits(LaunchDecode a) {
   constexpr int PL = D / 64;
