@@ -293,8 +293,9 @@ int tq_append_decode_attn_sparse_v(const tq_layout* layout, void* pool, const vo
  * to its cold_lens[b] pool tokens and then to its hot_lens[b] tail tokens, one softmax over
  * both. Each split of the pool also takes an equal slice of the tail and joins it to its
  * partial, so the tail adds no workgroups and its work is spread over the splits; with
- * num_splits = 0, hot_cap <= 512 and few enough (sequence, kv head) pairs that the grid has
- * room, one workgroup per pair takes the whole tail instead, beside the pool's splits.
+ * num_splits = 0 and few enough (sequence, kv head) pairs that the grid has room (at least
+ * 8 splits per pair for every 512 tokens of hot_cap), workgroups of their own take the tail
+ * instead, one per 512 tokens of hot_cap, beside the pool's splits.
  *   cold_lens       device int32 [batch], as context_lens of tq_decode_attn (may be 0)
  *   max_cold_len    host, an upper bound of cold_lens
  *   hot_k, hot_v    device fp16 [batch][num_kv_heads][hot_cap][head_dim], original basis

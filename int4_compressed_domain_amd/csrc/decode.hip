@@ -351,7 +351,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int b = u / a.Hkv, h = u - b * a.Hkv;
   const int r = a.Hq / a.Hkv;
   const int pps = a.pages_per_split;
-  const bool hotwg = a.hot_wg && s == a.splits;
+  const bool hotwg = a.hot_wg && s >= a.splits;  // one of the unit's a.hot_wg tail workgroups
+  const int hwi = hotwg ? s - a.splits : 0;       // (which one)
   const int p0 = hotwg ? 0 : s * pps;
 
   // ---- the prologue's small loads, issued together with the context length's -----------
@@ -402,12 +403,15 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
   const int npages = (L + 15) >> 4;
   // Hot/cold: an fp16 tail of Lh recent tokens besides the pool's L. Either every split of
   // the unit takes an equal slice [t0, t0 + tsl) of it after its pages (a unit with a tail
-  // and no pool tokens has one split, holding the whole tail), or (a.hot_wg, when the grid
-  // has room for it) one more workgroup per unit, split index a.splits, takes the whole
-  // tail and no pages and publishes partial row ns_cold.
+  // and no pool tokens has one split, holding the whole tail), or (a.hot_wg > 0, when the
+  // grid has room for it) a.hot_wg more workgroups per unit, split indices a.splits + k,
+  // take the tail in pieces of csz tokens and no pages: piece k is [k csz, (k + 1) csz)
+  // (the non-empty pieces come first) and publishes partial row ns_cold + k.
   const int Lh = a.hot_k ? min(max(a.hot_lens[b], 0), a.hot_cap) : 0;
   const int ns_cold = (npages + pps - 1) / pps;
-  const int ns = a.hot_wg ? ns_cold + (Lh > 0 ? 1 : 0)
+  const int csz = a.hot_wg ? (Lh + a.hot_wg - 1) / a.hot_wg : 0;  // tail tokens per piece
+  const int nhot = csz > 0 ? (Lh + csz - 1) / csz : 0;             // non-empty pieces
+  const int ns = a.hot_wg ? ns_cold + nhot
                           : (ns_cold > 0 ? ns_cold : (Lh > 0 ? 1 : 0));  // partials merged for this unit
   float* outp = a.out + ((int64_t)b * a.Hq + (int64_t)h * r) * D;
   if (ns == 0) {  // empty sequence: zero output, written by split 0
@@ -415,11 +419,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused(LaunchDecode a) {
       for (int i = tid; i < r * D; i += NT) outp[i] = 0.0f;
     return;
   }
-  if (hotwg ? Lh == 0 : s >= (a.hot_wg ? ns_cold : ns)) return;
-  const int srow = hotwg ? ns_cold : s;  // this workgroup's partial row
+  if (hotwg ? hwi >= nhot : s >= (a.hot_wg ? ns_cold : ns)) return;
+  const int srow = hotwg ? ns_cold + hwi : s;  // this workgroup's partial row
   const int p1 = hotwg ? 0 : min(p0 + pps, npages);
-  const int t0 = a.hot_wg ? 0 : (int)((int64_t)Lh * s / ns);
-  const int tsl = a.hot_wg ? (hotwg ? Lh : 0) : (int)((int64_t)Lh * (s + 1) / ns) - t0;
+  const int t0 = a.hot_wg ? hwi * csz : (int)((int64_t)Lh * s / ns);
+  const int tsl = a.hot_wg ? (hotwg ? min(csz, Lh - t0) : 0) : (int)((int64_t)Lh * (s + 1) / ns) - t0;
 
   // page ring (per wave) -- reused after the page loop as the merge area
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT][NW][C::SLOT];

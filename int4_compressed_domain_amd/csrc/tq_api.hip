@@ -311,19 +311,21 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   Split s = choose_split(batch, L->num_kv_heads, L->head_dim, L->k_codec, L->v_codec, max_context_len,
                          num_splits, sparse_v != 0);
   const int64_t resident = (int64_t)num_cus();  // fused-decode workgroups the chip holds at once
-  // fp16 tail: with automatic splits, at least 8 of them per unit, a grid that fits the chip
-  // and a tail of at most 512 tokens, one split is given up for a workgroup per unit that
-  // takes the whole tail and runs beside the pool's (its cost then hides behind theirs);
-  // otherwise every split takes a slice of the tail after its pages. Measured at 128K (one
-  // sequence, 8 kv heads): tails of 512 / 640 / 768 / 1024 tokens 34.9 / 36.9 / 40.2 /
-  // 49.1 us in a workgroup of their own against 38.4 / 38.6 / 38.7 / 38.8 us in slices; at
-  // D = 256, 4 sequences of 32K: 512 tokens 62.8 against 72.2 us, 1024 101 against 77 us.
+  // fp16 tail: with automatic splits, a grid that fits the chip and at least 8 splits per
+  // unit for every 512 tokens of tail capacity, splits are given up for workgroups that take
+  // the tail in pieces of at most 512 tokens and run beside the pool's (their cost then
+  // hides behind theirs); otherwise every split takes a slice of the tail after its pages.
+  // Measured at 128K (one sequence, 8 kv heads, 32 splits): tails of 512 / 640 / 768 / 1024
+  // tokens in one workgroup 34.9 / 36.9 / 40.2 / 49.1 us against 38.4 / 38.6 / 38.7 / 38.8
+  // us in slices; at D = 256, 4 sequences of 32K (8 splits): 512 tokens 62.8 against 72.2
+  // us, 1024 tokens in one workgroup 101 against 77 us.
   int hot_wg = 0;
-  if (hot_k && num_splits == 0 && hot_cap <= 512 && s.splits >= 8 &&
+  const int hot_pieces = (hot_cap + 511) / 512;
+  if (hot_k && num_splits == 0 && s.splits >= 8 * hot_pieces &&
       (int64_t)batch * L->num_kv_heads * s.splits <= resident &&
-      (int64_t)(s.splits - 1) * tq_max_split_pages(nw) >= (max_context_len + 15) / 16) {
-    s = make_split((max_context_len + 15) / 16, s.splits - 1);
-    hot_wg = 1;
+      (int64_t)(s.splits - hot_pieces) * tq_max_split_pages(nw) >= (max_context_len + 15) / 16) {
+    s = make_split((max_context_len + 15) / 16, s.splits - hot_pieces);
+    hot_wg = hot_pieces;
   }
   if (workspace_bytes_ < workspace_bytes(L, batch, max_context_len, num_splits)) return TQ_ENOSPC;
   if (!workspace) return TQ_EINVAL;

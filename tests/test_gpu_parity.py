@@ -223,11 +223,12 @@ def test_hot_cold(D, r, k_codec, v_codec):
 
 
 @pytest.mark.parametrize("D,kv,cap", [(128, 2, 256), (256, 4, 256), (64, 1, 256), (128, 2, 512),
-                                      (256, 2, 512), (64, 1, 512)])
+                                      (256, 2, 512), (64, 1, 512), (128, 2, 1024), (64, 1, 1024)])
 def test_hot_cold_tail_workgroup(D, kv, cap):
-    """Few long sequences with automatic splits: the tail (capacity up to 512 tokens) gets a
-    workgroup of its own per (sequence, kv head) beside the pool's splits (one split fewer);
-    checked against the oracle with long, full, short and empty tails and pools."""
+    """Few long sequences with automatic splits: the tail gets workgroups of its own per
+    (sequence, kv head), one per 512 tokens of capacity (two at 1024: pieces of half the
+    tail each), beside the pool's splits (as many splits fewer); checked against the oracle
+    with long, full, short and empty tails and pools."""
     cold = [16384, 0, 9000, 100]
     hot = [200, cap, 0, 17] if cap == 256 else [cap, 333, 0, cap - 1]
     w_outs = _hot_cold_case(D, 4, 0, cold, hot, cap, (0,), 400 + D + cap, kv=kv)
