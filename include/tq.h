@@ -295,7 +295,8 @@ int tq_append_decode_attn_sparse_v(const tq_layout* layout, void* pool, const vo
  * partial, so the tail adds no workgroups and its work is spread over the splits; with
  * num_splits = 0 and few enough (sequence, kv head) pairs that the grid has room (at least
  * 8 splits per pair for every 512 tokens of hot_cap), workgroups of their own take the tail
- * instead, one per 512 tokens of hot_cap, beside the pool's splits.
+ * instead, one per 512 tokens of hot_cap (at least two with 16 splits or more), beside the
+ * pool's splits.
  *   cold_lens       device int32 [batch], as context_lens of tq_decode_attn (may be 0)
  *   max_cold_len    host, an upper bound of cold_lens
  *   hot_k, hot_v    device fp16 [batch][num_kv_heads][hot_cap][head_dim], original basis

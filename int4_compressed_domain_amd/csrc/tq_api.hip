@@ -318,9 +318,11 @@ static int decode_impl(const tq_layout* L, const void* pool, const void* knew, c
   // Measured at 128K (one sequence, 8 kv heads, 32 splits): tails of 512 / 640 / 768 / 1024
   // tokens in one workgroup 34.9 / 36.9 / 40.2 / 49.1 us against 38.4 / 38.6 / 38.7 / 38.8
   // us in slices; at D = 256, 4 sequences of 32K (8 splits): 512 tokens 62.8 against 72.2
-  // us, 1024 tokens in one workgroup 101 against 77 us.
+  // us, 1024 tokens in one workgroup 101 against 77 us. With 16 splits or more, two pieces
+  // even for short tails (128K: 256 tokens 34.83 against 35.05 us in one, 512 tokens 34.87
+  // against 34.97 us).
   int hot_wg = 0;
-  const int hot_pieces = (hot_cap + 511) / 512;
+  const int hot_pieces = (hot_cap + 511) / 512 < 2 && s.splits >= 16 ? 2 : (hot_cap + 511) / 512;
   if (hot_k && num_splits == 0 && s.splits >= 8 * hot_pieces &&
       (int64_t)batch * L->num_kv_heads * s.splits <= resident &&
       (int64_t)(s.splits - hot_pieces) * tq_max_split_pages(nw) >= (max_context_len + 15) / 16) {

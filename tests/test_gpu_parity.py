@@ -223,12 +223,14 @@ def test_hot_cold(D, r, k_codec, v_codec):
 
 
 @pytest.mark.parametrize("D,kv,cap", [(128, 2, 256), (256, 4, 256), (64, 1, 256), (128, 2, 512),
-                                      (256, 2, 512), (64, 1, 512), (128, 2, 1024), (64, 1, 1024)])
+                                      (256, 2, 512), (64, 1, 512), (128, 2, 1024), (64, 1, 1024),
+                                      (128, 8, 256), (128, 8, 512)])
 def test_hot_cold_tail_workgroup(D, kv, cap):
     """Few long sequences with automatic splits: the tail gets workgroups of its own per
-    (sequence, kv head), one per 512 tokens of capacity (two at 1024: pieces of half the
-    tail each), beside the pool's splits (as many splits fewer); checked against the oracle
-    with long, full, short and empty tails and pools."""
+    (sequence, kv head), one per 512 tokens of capacity and at least two where a unit has 16
+    splits or more (pieces of equal length), beside the pool's splits (as many splits fewer);
+    with 8 kv heads (8 splits per unit) one workgroup takes the whole tail. Checked against
+    the oracle with long, full, short and empty tails and pools."""
     cold = [16384, 0, 9000, 100]
     hot = [200, cap, 0, 17] if cap == 256 else [cap, 333, 0, cap - 1]
     w_outs = _hot_cold_case(D, 4, 0, cold, hot, cap, (0,), 400 + D + cap, kv=kv)
